@@ -1,0 +1,136 @@
+"""CPU oracle for the gated delta rule -- TEST INFRASTRUCTURE ONLY.
+
+Nothing on the product path imports this package: only ``tests/``, the smoke
+check in ``__graft_entry__.py`` and the CPU-baseline leg of ``bench.py`` do.
+It shares no code with the HIP library and never touches the GPU.
+
+Two independent fp64 implementations live here:
+
+* ``recurrent_forward`` / ``decode_step`` -- the token-by-token recurrence in
+  plain C (``gdr_oracle.c``), the definition the GPU path is judged against;
+* ``chunked.chunked_forward`` -- the per-chunk algorithm of "Linear Attention,
+  Visualized" (sections "Gated DeltaNet (GDN)" and "Reuse GLA and GDN"),
+  written in numpy, used only to cross-check the recurrence (every chunk size
+  gives the exact result, section "Cost").
+
+Both are pinned by ``tests/test_oracle_*.py`` against closed forms, limits and
+brute force that do not reuse them.  Parity of every function here is pinned;
+absolute values at the full workload sizes are pinned only through these
+functions themselves (the pages print no worked numbers).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gdr_oracle.c")
+_LIB = os.path.join(_HERE, "libgdr_oracle.so")
+_lock = threading.Lock()
+_lib = None
+
+GATE_SCALAR = 0
+GATE_CHANNEL = 1
+
+
+def build(force: bool = True) -> str:
+    """Compile the C oracle with gcc (host only, -O2, OpenMP, no fast-math)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.run(["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared",
+                        "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"], check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build(force=True)
+            lib = ctypes.CDLL(_LIB)
+            P = ctypes.c_void_p
+            lib.oracle_gdr_forward.argtypes = [ctypes.c_long, ctypes.c_long, ctypes.c_int, ctypes.c_int,
+                                               ctypes.c_int, P, P, P, P, P, P, P, P, ctypes.c_int]
+            lib.oracle_gdr_forward.restype = ctypes.c_int
+            lib.oracle_gdr_decode_step.argtypes = [ctypes.c_long, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                   P, P, P, P, P, P, P, ctypes.c_int]
+            lib.oracle_gdr_decode_step.restype = ctypes.c_int
+            lib.oracle_max_threads.restype = ctypes.c_int
+            _lib = lib
+    return _lib
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())
+
+
+def _f32(x):
+    return np.ascontiguousarray(x, dtype=np.float32)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def recurrent_forward(q, k, v, g, beta, S0=None, nthreads: int = 0):
+    """Token recurrence in fp64.
+
+    q, k [B,H,T,d_k]; v [B,H,T,d_v]; beta [B,H,T]; g [B,H,T] (scalar gate,
+    log-decay) or [B,H,T,d_k] (channel gate); S0 [B,H,d_v,d_k] or None.
+    Returns (o [B,H,T,d_v], S_T [B,H,d_v,d_k]) as float64.
+    """
+    q, k, v, g, beta = map(_f32, (q, k, v, g, beta))
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    assert k.shape == (B, H, T, dk) and v.shape == (B, H, T, dv) and beta.shape == (B, H, T)
+    if g.shape == (B, H, T):
+        gate = GATE_SCALAR
+    elif g.shape == (B, H, T, dk):
+        gate = GATE_CHANNEL
+    else:
+        raise ValueError(f"gate shape {g.shape} matches neither [B,H,T] nor [B,H,T,d_k]")
+    s0 = None
+    if S0 is not None:
+        s0 = np.ascontiguousarray(S0, dtype=np.float64)
+        assert s0.shape == (B, H, dv, dk)
+    o = np.empty((B, H, T, dv), dtype=np.float64)
+    S = np.empty((B, H, dv, dk), dtype=np.float64)
+    rc = _load().oracle_gdr_forward(B * H, T, dk, dv, gate, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                    _ptr(beta), _ptr(s0), _ptr(o), _ptr(S), int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_gdr_forward failed ({rc})")
+    return o, S
+
+
+def decode_step(q, k, v, g, beta, S, nthreads: int = 0):
+    """One recurrent step on resident states, fp64.
+
+    q, k [N,H,d_k]; v [N,H,d_v]; beta [N,H]; g [N,H] or [N,H,d_k];
+    S [N,H,d_v,d_k].  Returns (o [N,H,d_v], S_new) as float64 (S is not modified).
+    """
+    q, k, v, g, beta = map(_f32, (q, k, v, g, beta))
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    if g.shape == (N, H):
+        gate = GATE_SCALAR
+    elif g.shape == (N, H, dk):
+        gate = GATE_CHANNEL
+    else:
+        raise ValueError(f"gate shape {g.shape}")
+    Snew = np.array(S, dtype=np.float64, copy=True, order="C")
+    assert Snew.shape == (N, H, dv, dk)
+    o = np.empty((N, H, dv), dtype=np.float64)
+    rc = _load().oracle_gdr_decode_step(N * H, dk, dv, gate, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                        _ptr(beta), _ptr(Snew), _ptr(o), int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_gdr_decode_step failed ({rc})")
+    return o, Snew
+
+
+from .chunked import chunked_forward, chunk_transform  # noqa: E402,F401
