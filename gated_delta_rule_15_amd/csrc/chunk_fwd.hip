@@ -1,0 +1,441 @@
+// chunk_fwd.hip -- chunkwise-parallel forward pass of the gated delta rule on gfx950.
+//
+// The per-chunk algorithm of "Linear Attention, Visualized" (snowchord.com), section
+// "Gated DeltaNet (GDN)" -> "Complete per-chunk algorithm", in the library's column
+// convention (state S in R^{d_v x d_k}; the page's row-convention state is S^T).  With
+// C = 64 tokens per chunk, G_l the inclusive in-chunk cumulative log-decay and
+// Gam[l,m] = exp(G_l - G_m) for m <= l:
+//
+//   L = (K K^T (.) Gam) strictly lower,   (I + diag(beta) L) T = diag(beta)      [UT transform]
+//   A = (Q K^T) (.) Gam (lower, incl. the diagonal),  M = A T
+//   P = K S^T,  R = V - diag(e^G) P                                              [= U - W<- S^T, with
+//   Z = T R,    O = diag(e^G) Q S^T + M R                                         W<- = T diag(e^G) K]
+//   S^T <- e^{G_C} S^T + K^T diag(e^{G_C - G}) Z
+//
+// i.e. Z = U - W<- S^T and O = Q<- S^T + A Z of the page, regrouped so that U and W<- are
+// never formed (Z = T (V - K<- S^T)) and the local term uses M = A T computed before the
+// state is known.  Only P, R, Z, O and the state update depend on S; they form the
+// chunk-serial chain, everything else depends on the chunk alone.
+//
+// Mapping: one workgroup (4 waves) per (sequence, 32-column d_v tile); value channels are
+// independent because every transition acts on the key side, so tiles never communicate.
+// S^T for the tile lives in registers as fp32 MFMA accumulators (wave w owns d_k rows
+// 32w..32w+31).  Every product runs on 32x32x16 fp16 MFMA with fp32 accumulation (the
+// fp32-I/O instantiation uses fp32 MFMA instead); q and k are converted to fp16 on load.
+// The triangular solve is done in fp32 in LDS: the four 16x16 diagonal blocks by forward
+// substitution (one wave, lane = (block, column)), then the two block levels of the
+// inverse by block products.  A ragged last chunk is padded with identity tokens
+// (k = q = v = 0, beta = 0, g = 0), which leaves the state and the real outputs unchanged.
+#include "gdr_device.h"
+
+namespace gdr {
+
+struct ChunkArgs {
+    int64_t T;
+    int dv;        // full d_v (row stride of v, o and the state)
+    int ntiles;    // d_v / 32
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* g;
+    const float* beta;
+    const float* S0;   // may be null
+    void* o;
+    float* Sf;         // may be null
+};
+
+// LDS layout (bytes).  Padding keeps 16-byte alignment of every row and spreads rows
+// across banks.
+template <int DK, typename OpT>
+struct ChunkLds {
+    static constexpr int C = kChunk;
+    static constexpr int PAD = (sizeof(OpT) == 2) ? 8 : 4;
+    static constexpr int LDK = DK + PAD;   // rows of d_k elements (K, Q, S)
+    static constexpr int LDC = C + PAD;    // rows of C elements (K^T, T, T^T, A, M, R^T, Z^T)
+    static constexpr int LDF = C + 4;      // fp32 rows of C elements (N, X, V^T)
+    static constexpr int LDY = 32 + 4;     // fp32 32x32 scratch
+    static constexpr bool kKT = sizeof(OpT) == 2;  // keep a transposed K copy (fp16 only)
+    static constexpr int oKf = 0;
+    static constexpr int oQf = oKf + C * LDK * (int)sizeof(OpT);
+    static constexpr int oKT = oQf + C * LDK * (int)sizeof(OpT);
+    static constexpr int oTm = oKT + (kKT ? DK * LDC * (int)sizeof(OpT) : 0);
+    static constexpr int oMm = oTm + C * LDC * (int)sizeof(OpT);
+    static constexpr int oSm = oMm + C * LDC * (int)sizeof(OpT);
+    static constexpr int oRt = oSm + 32 * LDK * (int)sizeof(OpT);
+    static constexpr int oZt = oRt + 32 * LDC * (int)sizeof(OpT);
+    static constexpr int oVt = oZt + 32 * LDC * (int)sizeof(OpT);
+    static constexpr int oSmall = oVt + 32 * LDF * 4;   // G, e^G, e^{G_C-G}, beta, e^{G_C}
+    static constexpr int oU = oSmall + 5 * C * 4;       // union: only live inside a chunk's solve
+    static constexpr int oNm = oU;
+    static constexpr int oXm = oNm + C * LDF * 4;
+    static constexpr int oYb = oXm + C * LDF * 4;
+    static constexpr int oAm = oYb + 32 * LDY * 4;
+    static constexpr int oTt = oAm + C * LDC * (int)sizeof(OpT);
+    static constexpr int total = oTt + (kKT ? C * LDC * (int)sizeof(OpT) : 0);
+    static_assert(total <= 160 * 1024, "LDS budget of one gfx950 CU exceeded");
+};
+
+__device__ __forceinline__ int xcd_major_index(int wg, int nwg) {
+    // Workgroups are dispatched round-robin over the 8 XCDs; renumber them so that
+    // consecutive logical indices (the d_v tiles of one sequence, which read the same
+    // q/k chunks) land on the same XCD and share its L2.
+    const int xcd = wg & 7, slot = wg >> 3;
+    const int q8 = nwg >> 3, r8 = nwg & 7;
+    return xcd * q8 + (xcd < r8 ? xcd : r8) + slot;
+}
+
+template <int DK, typename IOT, typename OpT>
+__global__ __launch_bounds__(256, 1) void chunk_fwd_scalar_kernel(const ChunkArgs a) {
+    using L = ChunkLds<DK, OpT>;
+    constexpr int C = kChunk;
+    constexpr int NKT = DK / 32;   // 32-row d_k tiles of S^T
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    OpT* Kf = reinterpret_cast<OpT*>(smem + L::oKf);
+    OpT* Qf = reinterpret_cast<OpT*>(smem + L::oQf);
+    OpT* KT = reinterpret_cast<OpT*>(smem + L::oKT);
+    OpT* Tm = reinterpret_cast<OpT*>(smem + L::oTm);
+    OpT* Mm = reinterpret_cast<OpT*>(smem + L::oMm);
+    OpT* Sm = reinterpret_cast<OpT*>(smem + L::oSm);
+    OpT* Rt = reinterpret_cast<OpT*>(smem + L::oRt);
+    OpT* Zt = reinterpret_cast<OpT*>(smem + L::oZt);
+    float* Vt = reinterpret_cast<float*>(smem + L::oVt);
+    float* sG = reinterpret_cast<float*>(smem + L::oSmall);
+    float* seG = sG + C;
+    float* seGr = seG + C;
+    float* sB = seGr + C;
+    float* seGC = sB + C;
+    float* Nm = reinterpret_cast<float*>(smem + L::oNm);
+    float* Xm = reinterpret_cast<float*>(smem + L::oXm);
+    float* Yb = reinterpret_cast<float*>(smem + L::oYb);
+    OpT* Am = reinterpret_cast<OpT*>(smem + L::oAm);
+    OpT* Tt = reinterpret_cast<OpT*>(smem + L::oTt);
+
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, li = l & 31, g = l >> 5;
+    const int vi = xcd_major_index(blockIdx.x, gridDim.x);
+    const int64_t bh = vi / a.ntiles;
+    const int dv0 = (vi % a.ntiles) * 32;
+    const int64_t T = a.T;
+    const int DV = a.dv;
+    const IOT* qh = static_cast<const IOT*>(a.q) + bh * T * DK;
+    const IOT* kh = static_cast<const IOT*>(a.k) + bh * T * DK;
+    const IOT* vh = static_cast<const IOT*>(a.v) + bh * T * DV;
+    const float* gh = a.g + bh * T;
+    const float* bth = a.beta + bh * T;
+    IOT* oh = static_cast<IOT*>(a.o) + bh * T * DV;
+
+    // ---- initial state tile: S^T[dk][dv] accumulator of wave w (w < NKT)
+    float16v accS;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) accS[r] = 0.0f;
+    if (w < NKT && a.S0 != nullptr) {
+        const float* s0 = a.S0 + bh * (int64_t)DV * DK + (int64_t)(dv0 + li) * DK + 32 * w;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float4v x = *reinterpret_cast<const float4v*>(s0 + 8 * j + 4 * g);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) accS[4 * j + e] = x[e];
+        }
+    }
+
+    const int64_t nC = (T + C - 1) / C;
+    for (int64_t c = 0; c < nC; ++c) {
+        const int64_t t0 = c * C;
+        const int Cc = (T - t0) < C ? (int)(T - t0) : C;
+        __syncthreads();  // previous chunk's readers of K^T, Z^T, V^T are done
+
+        // ---- (1) stage the chunk: q, k -> operand type (row-major, plus K^T), V tile -> fp32 V^T
+        for (int i = tid; i < C * DK / 8; i += 256) {
+            const int row = i / (DK / 8), col = (i % (DK / 8)) * 8;
+            float kv[8], qv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                kv[e] = row < Cc ? IO<IOT>::load(kh, (t0 + row) * DK + col + e) : 0.0f;
+                qv[e] = row < Cc ? IO<IOT>::load(qh, (t0 + row) * DK + col + e) : 0.0f;
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                Kf[row * L::LDK + col + e] = (OpT)kv[e];
+                Qf[row * L::LDK + col + e] = (OpT)qv[e];
+                if constexpr (L::kKT) KT[(col + e) * L::LDC + row] = (OpT)kv[e];
+            }
+        }
+        {
+            const int row = tid >> 2, col = (tid & 3) * 8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                Vt[(col + e) * L::LDF + row] = row < Cc ? IO<IOT>::load(vh, (t0 + row) * DV + dv0 + col + e) : 0.0f;
+        }
+        if (w == 0) {
+            float x = l < Cc ? gh[t0 + l] : 0.0f;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float y = __shfl_up(x, off);
+                if (l >= off) x += y;
+            }
+            const float GC = __shfl(x, 63);
+            sG[l] = x;
+            seG[l] = fast_exp(x);
+            seGr[l] = fast_exp(GC - x);
+            sB[l] = l < Cc ? bth[t0 + l] : 0.0f;
+            if (l == 0) seGC[0] = fast_exp(GC);
+        }
+        __syncthreads();
+
+        // ---- (2) K K^T -> N = I + diag(beta) (K K^T (.) Gam) strict lower;  Q K^T -> A
+        {
+            // tiles (matrix, row block, col block): wave0 KK(1,0); wave1 QK(1,0);
+            // wave2 KK(0,0), KK(1,1); wave3 QK(0,0), QK(1,1)
+            const bool isQ = (w & 1);
+            const OpT* X = isQ ? Qf : Kf;
+            const int ntile = (w < 2) ? 1 : 2;
+            for (int tt = 0; tt < ntile; ++tt) {
+                const int ti = (w < 2) ? 1 : tt, tj = (w < 2) ? 0 : tt;
+                float16v acc;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+#pragma unroll
+                for (int kk = 0; kk < DK / 16; ++kk) {
+                    const Frag<OpT> fa = load_frag<OpT>(X + (32 * ti + li) * L::LDK + 16 * kk + 8 * g);
+                    const Frag<OpT> fb = load_frag<OpT>(Kf + (32 * tj + li) * L::LDK + 16 * kk + 8 * g);
+                    mma32(acc, fa, fb);
+                }
+                const int m = 32 * tj + li;
+                const float Gm = sG[m];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = 32 * ti + acc_row(r, l);
+                    const float dec = (m <= row) ? fast_exp(sG[row] - Gm) : 0.0f;
+                    if (isQ) {
+                        Am[row * L::LDC + m] = (OpT)(dec * acc[r]);
+                    } else {
+                        Nm[row * L::LDF + m] = (m < row) ? sB[row] * dec * acc[r] : (m == row ? 1.0f : 0.0f);
+                    }
+                }
+            }
+        }
+        __syncthreads();
+
+        // ---- (3) X = N^{-1}, then T = X diag(beta)
+        if (w == 0) {  // diagonal 16x16 blocks by forward substitution
+            const int blk = l >> 4, j = l & 15, base = 16 * blk;
+            float x[16];
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                float s = (t == j) ? 1.0f : 0.0f;
+                const float* nrow = Nm + (base + t) * L::LDF + base;
+#pragma unroll
+                for (int i = 0; i < t; ++i) s -= nrow[i] * x[i];
+                x[t] = s;
+            }
+#pragma unroll
+            for (int t = 0; t < 16; ++t) Xm[(base + t) * L::LDF + base + j] = x[t];
+        }
+        __syncthreads();
+        // level 2: X[i,i-1] = -X[i,i] N[i,i-1] X[i-1,i-1] for 16-blocks i = 1, 3
+        for (int o = tid; o < 512; o += 256) {
+            const int blk = o >> 8, rr = (o >> 4) & 15, cc = o & 15;
+            const int i = blk ? 3 : 1;
+            float s = 0.0f;
+#pragma unroll
+            for (int t = 0; t < 16; ++t)
+                s += Nm[(16 * i + rr) * L::LDF + 16 * (i - 1) + t] * Xm[(16 * (i - 1) + t) * L::LDF + 16 * (i - 1) + cc];
+            Yb[(16 * blk + rr) * L::LDY + cc] = s;
+        }
+        __syncthreads();
+        for (int o = tid; o < 512; o += 256) {
+            const int blk = o >> 8, rr = (o >> 4) & 15, cc = o & 15;
+            const int i = blk ? 3 : 1;
+            float s = 0.0f;
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                const float xd = (t <= rr) ? Xm[(16 * i + rr) * L::LDF + 16 * i + t] : 0.0f;
+                s += xd * Yb[(16 * blk + t) * L::LDY + cc];
+            }
+            Xm[(16 * i + rr) * L::LDF + 16 * (i - 1) + cc] = -s;
+        }
+        __syncthreads();
+        // level 3: X[32:64, 0:32] = -X[32:64,32:64] (N[32:64,0:32] X[0:32,0:32])
+        for (int o = tid; o < 1024; o += 256) {
+            const int rr = o >> 5, cc = o & 31;
+            float s = 0.0f;
+#pragma unroll 8
+            for (int t = 0; t < 32; ++t) {
+                const float xa = (t >= cc) ? Xm[t * L::LDF + cc] : 0.0f;
+                s += Nm[(32 + rr) * L::LDF + t] * xa;
+            }
+            Yb[rr * L::LDY + cc] = s;
+        }
+        __syncthreads();
+        for (int o = tid; o < 1024; o += 256) {
+            const int rr = o >> 5, cc = o & 31;
+            float s = 0.0f;
+#pragma unroll 8
+            for (int t = 0; t < 32; ++t) {
+                const float xd = (t <= rr) ? Xm[(32 + rr) * L::LDF + 32 + t] : 0.0f;
+                s += xd * Yb[t * L::LDY + cc];
+            }
+            Xm[(32 + rr) * L::LDF + cc] = -s;
+        }
+        __syncthreads();
+        for (int o = tid; o < C * C; o += 256) {
+            const int row = o >> 6, col = o & 63;
+            const float t = (col <= row) ? Xm[row * L::LDF + col] * sB[col] : 0.0f;
+            Tm[row * L::LDC + col] = (OpT)t;
+            if constexpr (L::kKT) Tt[col * L::LDC + row] = (OpT)t;
+        }
+        __syncthreads();
+
+        // ---- (4) M = A T (lower): tiles (0,0) k<32, (1,0) k<64, (1,1) 32<=k<64
+        if (w < 3) {
+            const int ti = (w == 0) ? 0 : 1, tj = (w == 2) ? 1 : 0;
+            const int k0 = (w == 2) ? 2 : 0, k1 = (w == 0) ? 2 : 4;
+            float16v acc;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+            for (int kk = k0; kk < k1; ++kk) {
+                const Frag<OpT> fa = load_frag<OpT>(Am + (32 * ti + li) * L::LDC + 16 * kk + 8 * g);
+                Frag<OpT> fb;
+                if constexpr (L::kKT) fb = load_frag<OpT>(Tt + (32 * tj + li) * L::LDC + 16 * kk + 8 * g);
+                else fb = gather_frag<OpT>(Tm + (16 * kk + 8 * g) * L::LDC + 32 * tj + li, L::LDC);
+                mma32(acc, fa, fb);
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) Mm[(32 * ti + acc_row(r, l)) * L::LDC + 32 * tj + li] = (OpT)acc[r];
+        }
+
+        // ---- (5a) S -> operand copy S[dv][dk]
+        if (w < NKT) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                store4_transposed<OpT>(Sm, L::LDK, li, 32 * w + 8 * j + 4 * g, accS[4 * j], accS[4 * j + 1],
+                                       accS[4 * j + 2], accS[4 * j + 3]);
+        }
+        __syncthreads();
+
+        // ---- (5b) [K; Q] S^T : wave w -> rows 32(w&1).. of K (w < 2) or Q (w >= 2)
+        float16v acc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+        {
+            const OpT* X = (w < 2) ? Kf : Qf;
+#pragma unroll
+            for (int kk = 0; kk < DK / 16; ++kk) {
+                const Frag<OpT> fa = load_frag<OpT>(X + (32 * (w & 1) + li) * L::LDK + 16 * kk + 8 * g);
+                const Frag<OpT> fb = load_frag<OpT>(Sm + li * L::LDK + 16 * kk + 8 * g);
+                mma32(acc, fa, fb);
+            }
+        }
+        // ---- (5c) R = V - e^G (K S^T)  (waves 0,1);  O_hist = e^G (Q S^T)  (waves 2,3)
+        if (w < 2) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int row0 = 32 * w + 8 * j + 4 * g;
+                const float4v vv = *reinterpret_cast<const float4v*>(Vt + li * L::LDF + row0);
+                float rv[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) rv[e] = vv[e] - seG[row0 + e] * acc[4 * j + e];
+                store4_transposed<OpT>(Rt, L::LDC, li, row0, rv[0], rv[1], rv[2], rv[3]);
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[r] *= seG[32 * (w - 2) + acc_row(r, l)];
+        }
+        __syncthreads();
+
+        // ---- (5d) Z = T R (waves 0,1);  O = O_hist + M R (waves 2,3)
+        {
+            const OpT* Y = (w < 2) ? Tm : Mm;
+            const int rb = w & 1;
+            float16v acc2;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc2[r] = 0.0f;
+            const int kmax = rb ? 4 : 2;   // T and M are lower triangular
+            for (int kk = 0; kk < kmax; ++kk) {
+                const Frag<OpT> fa = load_frag<OpT>(Y + (32 * rb + li) * L::LDC + 16 * kk + 8 * g);
+                const Frag<OpT> fb = load_frag<OpT>(Rt + li * L::LDC + 16 * kk + 8 * g);
+                mma32(acc2, fa, fb);
+            }
+            if (w < 2) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int row0 = 32 * w + 8 * j + 4 * g;
+                    store4_transposed<OpT>(Zt, L::LDC, li, row0, seGr[row0] * acc2[4 * j],
+                                           seGr[row0 + 1] * acc2[4 * j + 1], seGr[row0 + 2] * acc2[4 * j + 2],
+                                           seGr[row0 + 3] * acc2[4 * j + 3]);
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = 32 * rb + acc_row(r, l);
+                    if (row < Cc) IO<IOT>::store(oh, (t0 + row) * DV + dv0 + li, acc[r] + acc2[r]);
+                }
+            }
+        }
+        __syncthreads();
+
+        // ---- (5e) S^T <- e^{G_C} S^T + K^T Zs
+        if (w < NKT) {
+            const float eGC = seGC[0];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) accS[r] *= eGC;
+#pragma unroll
+            for (int kk = 0; kk < C / 16; ++kk) {
+                Frag<OpT> fa;
+                if constexpr (L::kKT) fa = load_frag<OpT>(KT + (32 * w + li) * L::LDC + 16 * kk + 8 * g);
+                else fa = gather_frag<OpT>(Kf + (16 * kk + 8 * g) * L::LDK + 32 * w + li, L::LDK);
+                const Frag<OpT> fb = load_frag<OpT>(Zt + li * L::LDC + 16 * kk + 8 * g);
+                mma32(accS, fa, fb);
+            }
+        }
+    }
+
+    if (w < NKT && a.Sf != nullptr) {
+        float* sf = a.Sf + bh * (int64_t)DV * DK + (int64_t)(dv0 + li) * DK + 32 * w;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float4v x = {accS[4 * j], accS[4 * j + 1], accS[4 * j + 2], accS[4 * j + 3]};
+            *reinterpret_cast<float4v*>(sf + 8 * j + 4 * g) = x;
+        }
+    }
+}
+
+template <int DK, typename IOT, typename OpT>
+static hipError_t launch_chunk_scalar(const ChunkArgs& a, int64_t nwg, hipStream_t st) {
+    using L = ChunkLds<DK, OpT>;
+    auto kern = chunk_fwd_scalar_kernel<DK, IOT, OpT>;
+    static bool attr_set = false;  // per instantiation
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, L::total);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(256), L::total, st, a);
+    return hipGetLastError();
+}
+
+hipError_t chunk_fwd_dispatch(int64_t BH, int64_t T, int dk, int dv, bool bf16, bool channel,
+                              const void* q, const void* k, const void* v, const float* g, const float* beta,
+                              const float* S0, void* o, float* Sf, hipStream_t st) {
+    (void)channel;
+    ChunkArgs a;
+    a.T = T;
+    a.dv = dv;
+    a.ntiles = dv / 32;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.g = g;
+    a.beta = beta;
+    a.S0 = S0;
+    a.o = o;
+    a.Sf = Sf;
+    const int64_t nwg = BH * a.ntiles;
+    if (bf16) {
+        if (dk == 128) return launch_chunk_scalar<128, uint16_t, _Float16>(a, nwg, st);
+        return launch_chunk_scalar<64, uint16_t, _Float16>(a, nwg, st);
+    }
+    return launch_chunk_scalar<64, float, float>(a, nwg, st);
+}
+
+}  // namespace gdr

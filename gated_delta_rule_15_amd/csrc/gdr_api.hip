@@ -1,0 +1,116 @@
+// gdr_api.hip -- host side of the libgdr C ABI: argument validation and kernel dispatch.
+// Declarations and the contract of every entry point are in include/gdr.h.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gdr.h"
+
+namespace gdr {
+hipError_t chunk_fwd_dispatch(int64_t BH, int64_t T, int dk, int dv, bool bf16, bool channel, const void* q,
+                              const void* k, const void* v, const float* g, const float* beta, const float* S0,
+                              void* o, float* Sf, hipStream_t st);
+hipError_t decode_dispatch(int64_t NH, int dk, int dv, bool bf16, bool channel, const void* q, const void* k,
+                           const void* v, const float* g, const float* beta, float* S, void* o, hipStream_t st);
+}  // namespace gdr
+
+namespace {
+
+constexpr int kVersion = 10000 * 0 + 100 * 1 + 0;
+constexpr int64_t kMaxGrid = 0x7fffffff;
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+    if (a < 0 || b < 0) return false;
+    if (a != 0 && b > INT64_MAX / a) return false;
+    *out = a * b;
+    return true;
+}
+
+// Byte ranges [p, p + n) and [q, q + m) overlap.
+bool overlaps(const void* p, int64_t n, const void* q, int64_t m) {
+    if (!p || !q || n <= 0 || m <= 0) return false;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+    return a < b + static_cast<uintptr_t>(m) && b < a + static_cast<uintptr_t>(n);
+}
+
+gdr_status check_common(int d_k, int d_v, int io_dtype, int gate) {
+    if (io_dtype != GDR_BF16 && io_dtype != GDR_F32) return GDR_ERR_DTYPE;
+    if (gate != GDR_GATE_SCALAR && gate != GDR_GATE_CHANNEL) return GDR_ERR_INVALID_ARG;
+    if (d_k != 64 && d_k != 128) return GDR_ERR_SHAPE;
+    if (d_v < 32 || d_v > 256 || (d_v % 32) != 0) return GDR_ERR_SHAPE;
+    return GDR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdr_version(void) { return kVersion; }
+
+const char* gdr_status_string(int status) {
+    switch (status) {
+        case GDR_OK: return "success";
+        case GDR_ERR_INVALID_ARG: return "invalid argument (null buffer, negative size or bad enum)";
+        case GDR_ERR_SHAPE: return "unsupported size (d_k must be 64 or 128, d_v a multiple of 32 in [32, 256])";
+        case GDR_ERR_DTYPE: return "unsupported io dtype (GDR_BF16 or GDR_F32)";
+        case GDR_ERR_UNSUPPORTED: return "valid but unsupported combination of arguments";
+        case GDR_ERR_HIP: return "HIP runtime error while enqueuing the kernel";
+        default: return "unknown gdr_status";
+    }
+}
+
+gdr_status gdr_chunk_fwd(int64_t B, int64_t H, int64_t T, int d_k, int d_v, int io_dtype, int gate,
+                         const void* q, const void* k, const void* v, const float* g, const float* beta,
+                         const float* initial_state, void* o, float* final_state, void* stream) {
+    if (B < 0 || H < 0 || T < 0) return GDR_ERR_INVALID_ARG;
+    gdr_status s = check_common(d_k, d_v, io_dtype, gate);
+    if (s != GDR_OK) return s;
+    int64_t BH, BHT, nq, nv, nstate, ng;
+    const int64_t esz = io_dtype == GDR_BF16 ? 2 : 4;
+    if (!mul_ok(B, H, &BH) || !mul_ok(BH, T, &BHT) || !mul_ok(BHT, d_k, &nq) || !mul_ok(BHT, d_v, &nv) ||
+        !mul_ok(BH, (int64_t)d_k * d_v, &nstate) || !mul_ok(BHT, gate == GDR_GATE_CHANNEL ? d_k : 1, &ng) ||
+        !mul_ok(nq, 4, &nq) || !mul_ok(nv, 4, &nv) || !mul_ok(nstate, 4, &nstate))
+        return GDR_ERR_SHAPE;
+    if (BHT > 0 && (!q || !k || !v || !g || !beta || !o)) return GDR_ERR_INVALID_ARG;
+    // o must not overlap an input; the final state may alias the initial state exactly.
+    const int64_t obytes = nv / 4 * esz, qbytes = nq / 4 * esz, vbytes = nv / 4 * esz;
+    if (overlaps(o, obytes, q, qbytes) || overlaps(o, obytes, k, qbytes) || overlaps(o, obytes, v, vbytes) ||
+        overlaps(o, obytes, initial_state, nstate) || overlaps(o, obytes, final_state, nstate))
+        return GDR_ERR_INVALID_ARG;
+    if (final_state && initial_state && final_state != initial_state &&
+        overlaps(final_state, nstate, initial_state, nstate))
+        return GDR_ERR_INVALID_ARG;
+    if (io_dtype == GDR_F32 && d_k != 64) return GDR_ERR_UNSUPPORTED;
+    if (gate == GDR_GATE_CHANNEL) return GDR_ERR_UNSUPPORTED;
+    if (BH == 0) return GDR_OK;
+    int64_t nwg;
+    if (!mul_ok(BH, d_v / 32, &nwg) || nwg > kMaxGrid) return GDR_ERR_SHAPE;
+    if (!final_state && BHT == 0) return GDR_OK;
+    hipError_t e = gdr::chunk_fwd_dispatch(BH, T, d_k, d_v, io_dtype == GDR_BF16, gate == GDR_GATE_CHANNEL, q, k,
+                                           v, g, beta, initial_state, o, final_state,
+                                           static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+}
+
+gdr_status gdr_decode_step(int64_t N, int64_t H, int d_k, int d_v, int io_dtype, int gate, const void* q,
+                           const void* k, const void* v, const float* g, const float* beta, float* state,
+                           void* o, void* stream) {
+    if (N < 0 || H < 0) return GDR_ERR_INVALID_ARG;
+    gdr_status s = check_common(d_k, d_v, io_dtype, gate);
+    if (s != GDR_OK) return s;
+    int64_t NH, nstate;
+    if (!mul_ok(N, H, &NH) || !mul_ok(NH, (int64_t)d_k * d_v, &nstate) || !mul_ok(nstate, 4, &nstate))
+        return GDR_ERR_SHAPE;
+    if (NH == 0) return GDR_OK;
+    if (!q || !k || !v || !g || !beta || !state || !o) return GDR_ERR_INVALID_ARG;
+    const int64_t esz = io_dtype == GDR_BF16 ? 2 : 4;
+    const int64_t obytes = NH * d_v * esz;
+    if (overlaps(o, obytes, state, nstate) || overlaps(o, obytes, q, NH * d_k * esz) ||
+        overlaps(o, obytes, k, NH * d_k * esz) || overlaps(o, obytes, v, NH * d_v * esz))
+        return GDR_ERR_INVALID_ARG;
+    if (NH > kMaxGrid) return GDR_ERR_SHAPE;
+    hipError_t e = gdr::decode_dispatch(NH, d_k, d_v, io_dtype == GDR_BF16, gate == GDR_GATE_CHANNEL, q, k, v, g,
+                                        beta, state, o, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,123 @@
+/*
+ * gdr.h -- C ABI of libgdr, the gated delta rule on AMD Instinct MI355X (gfx950).
+ *
+ * The recurrence (column vectors, state S in R^{d_v x d_k}, stored row-major as S[v][c]):
+ *
+ *   scalar gate (Gated DeltaNet):   S_t = a_t S_{t-1} (I - b_t k_t k_t^T) + b_t v_t k_t^T
+ *   channel gate (KDA-style):       S_t = S_{t-1} Diag(a_t) (I - b_t k_t k_t^T) + b_t v_t k_t^T
+ *   output:                         o_t = S_t q_t   (read after the write)
+ *
+ * with a_t = exp(g_t): the library takes the LOG-decay g (g <= 0 for a decay in (0, 1]),
+ * and b_t = beta_t.  Sources: "Linear Attention, Visualized" (snowchord.com), sections
+ * "Recurrent form", "Gated DeltaNet (GDN)" and "Kimi Delta Attention (KDA)"; "Gated
+ * DeltaNet: Householder Transitions and the Arithmetic of Forgetting" (mohakchugh.is-a.dev),
+ * section "The gated delta rule".  The channel gate decays channel by channel first and then
+ * applies the delta correction, as the KDA section states.
+ *
+ * No 1/sqrt(d) scale is applied (fold it into q), q and k are not normalised (the caller
+ * L2-normalises keys, as the pages do by convention), and beta and g are not clamped.
+ *
+ * Conventions shared by every entry point
+ *  - All tensor pointers are DEVICE pointers to contiguous row-major buffers owned by the
+ *    caller.  The library allocates nothing and keeps no state between calls.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only enqueue work and
+ *    return; faults during execution surface at the caller's next synchronisation.
+ *  - Every argument is validated on the host before anything is enqueued.  On any error the
+ *    call returns a non-zero gdr_status and enqueues nothing.
+ *  - io_dtype applies to q, k, v and o (GDR_BF16 or GDR_F32); g, beta and the state are
+ *    always float32.
+ *  - Supported sizes: d_k in {64, 128}; d_v a multiple of 32 in [32, 256].  With
+ *    io_dtype = GDR_F32 the chunked forward supports d_k = 64 only (GDR_ERR_UNSUPPORTED
+ *    otherwise); decode supports both.
+ *  - Numerics: bf16 inputs are widened exactly; the chunked forward multiplies on fp16 MFMA
+ *    (inputs with |x| >= 65504 overflow there) with fp32 accumulation, holds the state in
+ *    fp32, and rounds o to bf16 (RNE) once at the end.  The fp32-I/O forward and the
+ *    decode step compute in fp32 throughout.
+ */
+#ifndef GDR_H
+#define GDR_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gdr_status {
+    GDR_OK = 0,
+    GDR_ERR_INVALID_ARG = 1, /* NULL where a buffer is required, negative size, bad enum  */
+    GDR_ERR_SHAPE = 2,       /* a size outside the supported range                        */
+    GDR_ERR_DTYPE = 3,       /* io_dtype is not GDR_BF16 or GDR_F32                       */
+    GDR_ERR_UNSUPPORTED = 4, /* valid but not implemented combination                     */
+    GDR_ERR_HIP = 5          /* the HIP runtime rejected a launch                         */
+} gdr_status;
+
+typedef enum gdr_dtype { GDR_BF16 = 0, GDR_F32 = 1 } gdr_dtype;
+
+typedef enum gdr_gate {
+    GDR_GATE_SCALAR = 0,  /* g is [.., T] : one log-decay per token and head            */
+    GDR_GATE_CHANNEL = 1  /* g is [.., T, d_k] : one log-decay per key channel (KDA)    */
+} gdr_gate;
+
+/* Library version as 10000*major + 100*minor + patch. */
+int gdr_version(void);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char *gdr_status_string(int status);
+
+/*
+ * gdr_chunk_fwd -- chunkwise-parallel forward pass over whole sequences.
+ *
+ * Computes, for each of the B*H independent (batch, head) sequences, every output o_t of
+ * the recurrence above and the final state S_T, with the per-chunk algorithm of
+ * "Linear Attention, Visualized", section "Gated DeltaNet (GDN)", "Complete per-chunk
+ * algorithm" (scalar gate) and section "Reuse GLA and GDN" (channel gate), chunk size 64:
+ * the UT transform (I + B L) T = B inside each chunk, then the chunk-serial state pass.
+ *
+ *   q, k           [B, H, T, d_k]  io_dtype
+ *   v              [B, H, T, d_v]  io_dtype
+ *   g              [B, H, T] (GDR_GATE_SCALAR) or [B, H, T, d_k] (GDR_GATE_CHANNEL), float32
+ *   beta           [B, H, T]       float32
+ *   initial_state  [B, H, d_v, d_k] float32, or NULL for a zero state
+ *   o              [B, H, T, d_v]  io_dtype, written (must not alias an input)
+ *   final_state    [B, H, d_v, d_k] float32, written, or NULL to skip; may alias
+ *                  initial_state exactly (each state tile is read before it is written)
+ *
+ * T may be any value >= 0 (a ragged last chunk is handled exactly; T = 0 copies the
+ * initial state, or zeros, to final_state).  B*H*T*max(d_k, d_v) must fit in int64.
+ */
+gdr_status gdr_chunk_fwd(int64_t B, int64_t H, int64_t T, int d_k, int d_v,
+                         int io_dtype, int gate,
+                         const void *q, const void *k, const void *v,
+                         const float *g, const float *beta,
+                         const float *initial_state,
+                         void *o, float *final_state, void *stream);
+
+/*
+ * gdr_decode_step -- one recurrent token per sequence, state updated in place.
+ *
+ * One step of the recurrence ("Linear Attention, Visualized", section "Recurrent form",
+ * with the decay of section "Gated DeltaNet (GDN)" or "Kimi Delta Attention (KDA)") for
+ * N*H resident states, in a single pass over each state: decay, predict p = S k,
+ * u = beta (v - p), S += u k^T, o = S q.
+ *
+ *   q, k   [N, H, d_k]   io_dtype
+ *   v      [N, H, d_v]   io_dtype
+ *   g      [N, H] (GDR_GATE_SCALAR) or [N, H, d_k] (GDR_GATE_CHANNEL), float32
+ *   beta   [N, H]        float32
+ *   state  [N, H, d_v, d_k] float32, read and overwritten in place
+ *   o      [N, H, d_v]   io_dtype, written (must not alias the state or an input)
+ *
+ * N = 0 or H = 0 is a valid no-op.
+ */
+gdr_status gdr_decode_step(int64_t N, int64_t H, int d_k, int d_v,
+                           int io_dtype, int gate,
+                           const void *q, const void *k, const void *v,
+                           const float *g, const float *beta,
+                           float *state, void *o, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDR_H */
