@@ -1,0 +1,713 @@
+// chunk_fwd_pc.hip -- producer/consumer chunked forward of the gated delta rule (bf16 I/O,
+// fp16 MFMA operands, fp32 accumulation and state), gfx950.
+//
+// Same per-chunk algorithm and regrouping as chunk_fwd.hip ("Linear Attention, Visualized",
+// section "Gated DeltaNet (GDN)", "Complete per-chunk algorithm"; column convention):
+//
+//   N = I + diag(beta) (K K^T (.) Gam)_strict,  T = N^{-1} diag(beta),  A = (Q K^T) (.) Gam
+//   R = V - diag(e^G) K S^T,   Z = T R,   O = diag(e^G) Q S^T + A Z,
+//   S^T <- e^{G_C} S^T + K^T diag(e^{G_C - G}) Z.
+//
+// The page notes that the chunk-local quantities (here N, T, A) can be formed for all chunks
+// in parallel while the boundary pass threads the state through the chunks.  This kernel
+// runs the two concurrently inside one workgroup of four waves:
+//   * waves 0-1 (consumers) carry the state of 16 value channels each, run the whole
+//     S-dependent chain of chunk i, and stage the inputs of later chunks into LDS;
+//   * waves 2-3 (producers) form N, T and A of chunk i+1: the Gram tiles, the four 16x16
+//     diagonal blocks of N^{-1} by forward substitution in fp32, and the two block levels of
+//     the inverse on MFMA.
+// An iteration has three phases separated by workgroup barriers:
+//   phase 0  consumers: chain of chunk i          producers: Gram tiles, diagonal inverses,
+//                                                            first block level of chunk i+1
+//   phase 1  consumers: -                         producers: second block level
+//   phase 2  consumers: stage K, Q, g, beta of    producers: write T of chunk i+1
+//            chunk i+2 and V of chunk i+1
+// Every LDS buffer is written only in a phase where its previous contents are dead.
+//
+// MFMA 16x16x32 f16 conventions (l = lane, j = l & 15, g = l >> 4):
+//   accumulator register r of lane l holds element (row 4g + r, column j);
+//   an operand fragment of lane l is row/column j with the 8 reduction indices
+//   {32kb + 4g + r} U {32kb + 16 + 4g + r}, r = 0..3.
+// Every matrix used as an operand from LDS stores its reduction index permuted within each
+// 32-block (index 16h + 4gg + rr at position 8gg + 4h + rr), so a fragment is ONE 16-byte
+// read, and the accumulator of two vertically adjacent 16-row tiles IS the operand fragment
+// of the matrix whose rows are the reduction index: S^T, R and Z move between products in
+// registers only.  K^T fragments (reduction over tokens) come from the token-major K copy
+// through ds_read_b64_tr_b16, which hands lane i of each 16-lane group element (i & 3) of
+// the 4-element rows addressed by lanes (i >> 2) + 4e, e = 0..3.
+#include "gdr_device.h"
+
+namespace gdr {
+
+struct PcArgs {
+    int64_t T;
+    int dv;
+    int ntiles;  // d_v / 32
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const float* g;
+    const float* beta;
+    const float* S0;
+    uint16_t* o;
+    float* Sf;
+};
+
+// position of logical index m inside its row under the 32-block permutation
+__device__ __forceinline__ int pperm(int m) {
+    return (m & ~31) | (((m >> 2) & 3) << 3) | (((m >> 4) & 1) << 2) | (m & 3);
+}
+
+template <int DK>
+struct PcLds {
+    static constexpr int C = kChunk;
+    static constexpr int LDK = DK + 8;   // halfs, rows of K / Q
+    static constexpr int LDC = C + 8;    // halfs, rows of C-wide fp16 matrices
+    static constexpr int LDV = C + 4;    // floats, rows of V^T
+    static constexpr int LDN = 16 + 4;   // floats, rows of a 16x16 fp32 block
+    // per-chunk factor table (floats):
+    //   [0,64) G   [64,128) e^G   [128,192) e^{G_C - G}   [192,256) beta   [256] e^{G_C}
+    //   [272,336)  cf[m]     = e^{Gend(blk(m)) - G_m}           (<= 1)
+    //   [336,528)  rf[b][l]  = e^{G_l - Gend(b)}, b = 0..2        (<= 1 for blk(l) > b)
+    //   [528,720)  rb[b][l]  = beta_l rf[b][l]
+    // with Gend(b) = G at the last token of 16-token block b.
+    static constexpr int SG = 0, SEG = 64, SEGR = 128, SB = 192, SEGC = 256, SCF = 272, SRF = 336, SRB = 528;
+    static constexpr int NSM = 736;
+    static constexpr int szK = C * LDK * 2;
+    static constexpr int szC = C * LDC * 2;
+    static constexpr int oKb0 = 0;
+    static constexpr int oKb1 = oKb0 + szK;
+    static constexpr int oQb0 = oKb1 + szK;
+    static constexpr int oQb1 = oQb0 + szK;
+    static constexpr int oAt0 = oQb1 + szK;   // A^T (column-major A), two chunks
+    static constexpr int oAt1 = oAt0 + szC;
+    static constexpr int oSm0 = oAt1 + szC;
+    static constexpr int oSm1 = oSm0 + NSM * 4;
+    static constexpr int oVt = oSm1 + NSM * 4;
+    static constexpr int oTt = oVt + 32 * LDV * 4;  // T^T
+    static constexpr int oNt = oTt + szC;           // off-diagonal blocks of N^T (fp16)
+    static constexpr int oXt = oNt + szC;           // X^T, X = N^{-1} (fp16)
+    static constexpr int oNd = oXt + szC;           // diagonal blocks of N^T (fp32)
+    static constexpr int total = oNd + 4 * 16 * LDN * 4;
+    static_assert(total <= 160 * 1024, "LDS budget of one gfx950 CU exceeded");
+    static_assert((oAt0 | oAt1 | oSm0 | oSm1 | oVt | oTt | oNt | oXt | oNd) % 16 == 0, "alignment");
+};
+
+__device__ __forceinline__ void mma16(float4v& acc, const half8& a, const half8& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
+}
+__device__ __forceinline__ half8 ld8(const _Float16* p) { return *reinterpret_cast<const half8*>(p); }
+__device__ __forceinline__ half4 ldtr(const _Float16* p) {
+    typedef short short4v __attribute__((ext_vector_type(4)));
+    const short4v v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4v*)(p));
+    return __builtin_bit_cast(half4, v);
+}
+__device__ __forceinline__ half8 cat8(const half4& lo, const half4& hi) {
+    return half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+__device__ __forceinline__ half8 pack8(const float4v& lo, const float4v& hi) {
+    half8 h;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        h[r] = (_Float16)lo[r];
+        h[4 + r] = (_Float16)hi[r];
+    }
+    return h;
+}
+__device__ __forceinline__ float4v zero4() { return float4v{0.0f, 0.0f, 0.0f, 0.0f}; }
+__device__ __forceinline__ float4v ld4f(const float* p) { return *reinterpret_cast<const float4v*>(p); }
+// Wave-local ordering of LDS writes before later LDS reads of the same wave.
+__device__ __forceinline__ void lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+// Workgroup barrier for LDS traffic only.  Unlike __syncthreads() it does not wait for the
+// wave's outstanding global loads, so prefetches stay in flight across phases; no global
+// memory is exchanged between waves.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// 8 bf16 (one uint4) -> 8 fp16 written as two 4-element groups at permuted positions.
+__device__ __forceinline__ void stage8(_Float16* row, int m0, const uint4& u) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    half4 a, b;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        a[2 * e] = (_Float16)__uint_as_float(w[e] << 16);
+        a[2 * e + 1] = (_Float16)__uint_as_float(w[e] & 0xffff0000u);
+        b[2 * e] = (_Float16)__uint_as_float(w[2 + e] << 16);
+        b[2 * e + 1] = (_Float16)__uint_as_float(w[2 + e] & 0xffff0000u);
+    }
+    *reinterpret_cast<half4*>(row + pperm(m0)) = a;
+    *reinterpret_cast<half4*>(row + pperm(m0 + 4)) = b;
+}
+
+// Buffer resources: a load past the resource's byte range returns zeros and a store past it
+// is dropped, which pads the ragged last chunk with identity tokens (k = q = v = 0,
+// g = beta = 0) and clips its output rows without any branch.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 bld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return uint4{v[0], v[1], v[2], v[3]};
+}
+__device__ __forceinline__ float bld4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+__device__ __forceinline__ void bst_bf16(__amdgpu_buffer_rsrc_t r, uint32_t off, float x) {
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (__bf16)x), r, off, 0, 0);
+}
+
+template <int DK>
+__global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {
+    using L = PcLds<DK>;
+    constexpr int C = kChunk;
+    constexpr int NKB = DK / 32;      // 32-deep reduction blocks over d_k
+    constexpr int NST = DK / 16;      // 16-row tiles of S^T
+    constexpr int KVL = C * DK / 8 / 256;  // 16-byte vectors of one K chunk per lane
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    auto Kb = [&](int b) { return reinterpret_cast<_Float16*>(smem + (b ? L::oKb1 : L::oKb0)); };
+    auto Qb = [&](int b) { return reinterpret_cast<_Float16*>(smem + (b ? L::oQb1 : L::oQb0)); };
+    auto At = [&](int b) { return reinterpret_cast<_Float16*>(smem + (b ? L::oAt1 : L::oAt0)); };
+    auto Sm = [&](int b) { return reinterpret_cast<float*>(smem + (b ? L::oSm1 : L::oSm0)); };
+    float* Vt = reinterpret_cast<float*>(smem + L::oVt);
+    _Float16* Tt = reinterpret_cast<_Float16*>(smem + L::oTt);
+    _Float16* Nt = reinterpret_cast<_Float16*>(smem + L::oNt);
+    _Float16* Xt = reinterpret_cast<_Float16*>(smem + L::oXt);
+    float* Nd = reinterpret_cast<float*>(smem + L::oNd);
+
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, j = l & 15, g = l >> 4;
+    const bool consumer = w < 2;
+    const int p = w - 2;           // producer index (valid when !consumer)
+    const int vi = xcd_major_index(blockIdx.x, gridDim.x);
+    const int64_t bh = vi / a.ntiles;
+    const int dv0 = (vi % a.ntiles) * 32;
+    const int64_t T = a.T;
+    const int DV = a.dv;
+    const auto rq = make_rsrc(a.q + bh * T * DK, (uint32_t)(T * DK * 2));
+    const auto rk = make_rsrc(a.k + bh * T * DK, (uint32_t)(T * DK * 2));
+    const auto rv = make_rsrc(a.v + bh * T * DV, (uint32_t)(T * DV * 2));
+    const auto rg = make_rsrc(a.g + bh * T, (uint32_t)(T * 4));
+    const auto rb = make_rsrc(a.beta + bh * T, (uint32_t)(T * 4));
+    const auto ro = make_rsrc(a.o + bh * T * DV, (uint32_t)(T * DV * 2));
+    const int dvc = dv0 + 16 * w;  // consumer's first value channel
+    const int64_t nC = (T + C - 1) / C;
+
+    // operand fragment (rows 16*rt.., 8 reduction indices of block kb) of a row-major matrix
+    // whose reduction index runs along a column-major copy: transposing reads of the
+    // column-major matrix M^T at rows 32kb + 4g + (j >> 2) (+16) and columns col0 + 4(j & 3).
+    auto trfrag = [&](const _Float16* base, int ld, int kb, int col) {
+        const _Float16* p0 = base + (32 * kb + 4 * g + (j >> 2)) * ld + col;
+        return cat8(ldtr(p0), ldtr(p0 + 16 * ld));
+    };
+
+    // ---- zero the operand scratch whose never-written parts are read as structural zeros
+    for (int i = tid; i < (L::total - L::oAt0) / 16; i += 256)
+        reinterpret_cast<uint4*>(smem + L::oAt0)[i] = uint4{0u, 0u, 0u, 0u};
+
+    // ---- registers carried across phases.  A wave plays one role for the whole kernel, so
+    // the two roles share one array: consumers keep the state S^T (fp32 accumulators) and
+    // its fp16 operand copy; producers keep blocks of N^{-1}.
+    //   consumer: [0, 4*NST) S^T tiles   [4*NST, 4*NST + 4*NKB) fp16 copy of S^T
+    //   producer: [0,16) diagonal-block column of N^{-1}  [16,20) first level  [20,28) second
+    //   every wave: [oKR, NCARRY) its share of the prefetched K, Q, V, g, beta
+    constexpr int oSB = 4 * NST;
+    constexpr int oXD = 0, oX2 = 16, oXC = 20;
+    constexpr int oKR = (oSB + 4 * NKB) > 28 ? (oSB + 4 * NKB) : 28;
+    constexpr int oQR = oKR + 4 * KVL, oVR = oQR + 4 * KVL, oGR = oVR + 4;
+    constexpr int NCARRY = oGR + 2;
+    uint32_t cr[NCARRY];
+#pragma unroll
+    for (int i = 0; i < NCARRY; ++i) cr[i] = 0u;
+    auto getf4 = [&](int o) { return float4v{__uint_as_float(cr[o]), __uint_as_float(cr[o + 1]), __uint_as_float(cr[o + 2]), __uint_as_float(cr[o + 3])}; };
+    auto setf4 = [&](int o, const float4v& v) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) cr[o + e] = __float_as_uint(v[e]);
+    };
+    auto geth8 = [&](int o) { return __builtin_bit_cast(half8, uint4{cr[o], cr[o + 1], cr[o + 2], cr[o + 3]}); };
+    auto seth8 = [&](int o, const half8& h) {
+        const uint4 u = __builtin_bit_cast(uint4, h);
+        cr[o] = u.x; cr[o + 1] = u.y; cr[o + 2] = u.z; cr[o + 3] = u.w;
+    };
+    auto getu4 = [&](int o) { return uint4{cr[o], cr[o + 1], cr[o + 2], cr[o + 3]}; };
+    auto setu4 = [&](int o, const uint4& u) { cr[o] = u.x; cr[o + 1] = u.y; cr[o + 2] = u.z; cr[o + 3] = u.w; };
+
+    if (consumer) {
+        if (a.S0 != nullptr) {
+            const float* s0 = a.S0 + bh * (int64_t)DV * DK + (int64_t)(dvc + j) * DK;
+#pragma unroll
+            for (int t = 0; t < NST; ++t) setf4(4 * t, ld4f(s0 + 16 * t + 4 * g));
+        }
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) seth8(oSB + 4 * kb, pack8(getf4(8 * kb), getf4(8 * kb + 4)));
+    }
+
+    // ---- staging (all 256 lanes): global -> registers -> LDS.  Past the sequence end the
+    // buffer loads return zeros, i.e. identity tokens.
+    const int pt = tid;
+    auto issue_kq = [&](int64_t c) {
+        const uint32_t t0 = (uint32_t)(c * C);
+#pragma unroll
+        for (int u = 0; u < KVL; ++u) {
+            const int idx = pt + 256 * u, row = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
+            const uint32_t off = ((t0 + row) * DK + col) * 2;
+            setu4(oKR + 4 * u, bld16(rk, off));
+            setu4(oQR + 4 * u, bld16(rq, off));
+        }
+        if (w == 0) {
+            cr[oGR] = __float_as_uint(bld4(rg, (t0 + l) * 4));
+            cr[oGR + 1] = __float_as_uint(bld4(rb, (t0 + l) * 4));
+        }
+    };
+    auto issue_v = [&](int64_t c) {
+        const uint32_t t0 = (uint32_t)(c * C);
+        const int row = pt >> 2, col = (pt & 3) * 8;
+        setu4(oVR, bld16(rv, ((t0 + row) * DV + dv0 + col) * 2));
+    };
+    auto stage_kq = [&](int64_t c) {
+        const int buf = (int)(c & 1);
+#pragma unroll
+        for (int u = 0; u < KVL; ++u) {
+            const int idx = pt + 256 * u, row = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
+            stage8(Kb(buf) + row * L::LDK, col, getu4(oKR + 4 * u));
+            stage8(Qb(buf) + row * L::LDK, col, getu4(oQR + 4 * u));
+        }
+        if (w == 0) {  // in-chunk cumulative log-decay and the factor table
+            float x = __uint_as_float(cr[oGR]);
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float y = __shfl_up(x, off);
+                if (l >= off) x += y;
+            }
+            const float GC = __shfl(x, 63);
+            float ge[4];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) ge[b] = __shfl(x, 16 * b + 15);
+            const int blk = l >> 4;
+            const float beta = __uint_as_float(cr[oGR + 1]);
+            float* sm = Sm(buf);
+            sm[L::SG + l] = x;
+            sm[L::SEG + l] = fast_exp(x);
+            sm[L::SEGR + l] = fast_exp(GC - x);
+            sm[L::SB + l] = beta;
+            if (l == 0) sm[L::SEGC] = fast_exp(GC);
+            sm[L::SCF + l] = fast_exp(ge[blk] - x);
+#pragma unroll
+            for (int b = 0; b < 3; ++b) {
+                const float f = blk > b ? fast_exp(x - ge[b]) : 0.0f;
+                sm[L::SRF + 64 * b + l] = f;
+                sm[L::SRB + 64 * b + l] = beta * f;
+            }
+        }
+    };
+    auto stage_v = [&]() {  // V^T tile, fp32 [channel][token]
+        const int row = pt >> 2, col = (pt & 3) * 8;
+        const uint4 vr = getu4(oVR);
+        const uint32_t ww[4] = {vr.x, vr.y, vr.z, vr.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            Vt[(col + 2 * e) * L::LDV + row] = __uint_as_float(ww[e] << 16);
+            Vt[(col + 2 * e + 1) * L::LDV + row] = __uint_as_float(ww[e] & 0xffff0000u);
+        }
+    };
+
+    lds_barrier();  // zero-fill done
+    if (nC > 0) {
+        issue_kq(0);
+        stage_kq(0);
+    }
+    lds_barrier();
+
+    // Gram tiles of one producer wave.  Wave 2 forms KK {00,10,11,20,21,30,31} and
+    // QK {00,10,11}; wave 3 forms KK {22,32,33} and QK {20,21,22,30,31,32,33}.  Per
+    // reduction block each wave loads its 6 distinct row fragments once (K row tiles 0-3, Q
+    // row tiles 2P, 2P+1) one block ahead, then issues 10 independent MFMAs.  The epilogue
+    // applies the decay (factorised through the per-chunk table off the diagonal, exact on
+    // it) and beta, and stores each tile column-major: a lane's 4 accumulator rows are
+    // contiguous there.
+    auto gram_wave = [&](const _Float16* Kp, const _Float16* Qp, const float* sm, _Float16* Ap, const int P) {
+        constexpr int NT = 10;
+        const int tq[2][NT] = {{0, 0, 0, 0, 0, 0, 0, 1, 1, 1}, {0, 0, 0, 1, 1, 1, 1, 1, 1, 1}};
+        const int ti_[2][NT] = {{0, 1, 1, 2, 2, 3, 3, 0, 1, 1}, {2, 3, 3, 2, 2, 2, 3, 3, 3, 3}};
+        const int tj_[2][NT] = {{0, 0, 1, 0, 1, 0, 1, 0, 0, 1}, {2, 2, 3, 0, 1, 2, 0, 1, 2, 3}};
+        auto load6 = [&](half8* f, int kb) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) f[r] = ld8(Kp + (16 * r + j) * L::LDK + 32 * kb + 8 * g);
+#pragma unroll
+            for (int r = 0; r < 2; ++r) f[4 + r] = ld8(Qp + (16 * (2 * P + r) + j) * L::LDK + 32 * kb + 8 * g);
+        };
+        float4v acc[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t] = zero4();
+        half8 fa[6], fb[6];
+        load6(fa, 0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            half8* cur = (kb & 1) ? fb : fa;
+            half8* nxt = (kb & 1) ? fa : fb;
+            if (kb + 1 < NKB) load6(nxt, kb + 1);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const int ti = ti_[P][t], tj = tj_[P][t];
+                const half8 A = tq[P][t] ? cur[4 + (ti - 2 * P)] : cur[ti];
+                mma16(acc[t], A, cur[tj]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const int ti = ti_[P][t], tj = tj_[P][t];
+            const bool isQ = tq[P][t];
+            const int m = 16 * tj + j;            // this lane's column
+            const int l0 = 16 * ti + 4 * g;       // first of its 4 rows
+            float v[4];
+            if (ti != tj) {
+                // Gam[l][m] = rf[tj][l] cf[m] (both <= 1); beta folded into rb for N
+                const float cfm = sm[L::SCF + m];
+                const float4v rf = ld4f(sm + (isQ ? L::SRF : L::SRB) + 64 * tj + l0);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) v[r] = acc[t][r] * rf[r] * cfm;
+                _Float16* dst = (isQ ? Ap : Nt) + m * L::LDC + l0;
+                *reinterpret_cast<half4*>(dst) = half4{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+            } else {
+                const float Gm = sm[L::SG + m];
+                const float4v Gl = ld4f(sm + L::SG + l0);
+                if (isQ) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) v[r] = (m <= l0 + r) ? acc[t][r] * fast_exp(Gl[r] - Gm) : 0.0f;
+                    *reinterpret_cast<half4*>(Ap + m * L::LDC + l0) =
+                        half4{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+                } else {
+                    const float4v bl = ld4f(sm + L::SB + l0);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        v[r] = (m < l0 + r) ? bl[r] * acc[t][r] * fast_exp(Gl[r] - Gm) : (m == l0 + r ? 1.0f : 0.0f);
+                    // N^T diagonal block ti, column j: rows 4g..4g+3
+                    *reinterpret_cast<float4v*>(Nd + (ti * 16 + j) * L::LDN + 4 * g) = float4v{v[0], v[1], v[2], v[3]};
+                }
+            }
+        }
+    };
+
+    for (int64_t it = -1; it < nC; ++it) {
+        const int64_t cc = it;        // consumer chunk
+        const int64_t cp = it + 1;    // producer chunk (N, T, A)
+        const int64_t cs = it + 2;    // chunk whose K, Q are staged in phase 2
+        const int bc = (int)(cc & 1), bp = (int)(cp & 1);
+
+        // ======================= phase 0 =======================
+        // Unconditional: past the sequence end the buffer loads return zeros, and staging
+        // those zeros touches only buffers no later chunk reads.  (Conditional issue/stage
+        // pairs make the compiler wait for every outstanding load at the loop head.)
+        issue_kq(cs);
+        issue_v(cp);
+        if (consumer) {
+            if (cc >= 0) {
+                const _Float16* Kc = Kb(bc);
+                const _Float16* Qc = Qb(bc);
+                const _Float16* Ac = At(bc);
+                const float* sm = Sm(bc);
+                // The LDS operand fragments of each group of MFMAs are issued one group ahead
+                // (double-buffered registers), and sched_barrier pins that order: left alone,
+                // the scheduler serialises every ds_read with the MFMA that consumes it.
+                auto kfrag = [&](int ti, int kb) { return ld8(Kc + (16 * ti + j) * L::LDK + 32 * kb + 8 * g); };
+                auto qfrag = [&](int ti, int kb) { return ld8(Qc + (16 * ti + j) * L::LDK + 32 * kb + 8 * g); };
+                // P_K = K S^T, P_Q = Q S^T  (rows = tokens), reduction over d_k in NKB blocks
+                float4v PK[4], PQ[4];
+                half8 fa[8], fb[8];
+#pragma unroll
+                for (int ti = 0; ti < 4; ++ti) {
+                    PK[ti] = zero4();
+                    PQ[ti] = zero4();
+                    fa[ti] = kfrag(ti, 0);
+                    fa[4 + ti] = qfrag(ti, 0);
+                }
+                float4v eg[4], vv[4];
+#pragma unroll
+                for (int ti = 0; ti < 4; ++ti) {
+                    eg[ti] = ld4f(sm + L::SEG + 16 * ti + 4 * g);
+                    vv[ti] = ld4f(Vt + (16 * w + j) * L::LDV + 16 * ti + 4 * g);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) {
+                    half8* cur = (kb & 1) ? fb : fa;
+                    half8* nxt = (kb & 1) ? fa : fb;
+                    if (kb + 1 < NKB) {
+#pragma unroll
+                        for (int ti = 0; ti < 4; ++ti) {
+                            nxt[ti] = kfrag(ti, kb + 1);
+                            nxt[4 + ti] = qfrag(ti, kb + 1);
+                        }
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    const half8 sb = geth8(oSB + 4 * kb);
+#pragma unroll
+                    for (int ti = 0; ti < 4; ++ti) {
+                        mma16(PK[ti], cur[ti], sb);
+                        mma16(PQ[ti], cur[4 + ti], sb);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                // operands of the next products: rows of T and A (lower triangular, 6
+                // fragments each, from their column-major copies), e^{G_C - G}
+                half8 tf[6], af[6];
+                float4v er[4];
+#pragma unroll
+                for (int ti = 0, n = 0; ti < 4; ++ti) {
+#pragma unroll
+                    for (int kb = 0; kb <= (ti >> 1); ++kb, ++n) {
+                        tf[n] = trfrag(Tt, L::LDC, kb, 16 * ti + 4 * (j & 3));
+                        af[n] = trfrag(Ac, L::LDC, kb, 16 * ti + 4 * (j & 3));
+                    }
+                }
+#pragma unroll
+                for (int ti = 0; ti < 4; ++ti) er[ti] = ld4f(sm + L::SEGR + 16 * ti + 4 * g);
+                const float eGC = sm[L::SEGC];
+                __builtin_amdgcn_sched_barrier(0);
+                // R = V - e^G P_K ;  O_hist = e^G P_Q
+                float4v Rr[4], Oh[4];
+#pragma unroll
+                for (int ti = 0; ti < 4; ++ti) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        Rr[ti][r] = vv[ti][r] - eg[ti][r] * PK[ti][r];
+                        Oh[ti][r] = eg[ti][r] * PQ[ti][r];
+                    }
+                }
+                // Z = T R  (T lower triangular)
+                const half8 rB[2] = {pack8(Rr[0], Rr[1]), pack8(Rr[2], Rr[3])};
+                float4v Zz[4];
+#pragma unroll
+                for (int ti = 0, n = 0; ti < 4; ++ti) {
+                    Zz[ti] = zero4();
+#pragma unroll
+                    for (int kb = 0; kb <= (ti >> 1); ++kb, ++n) mma16(Zz[ti], tf[n], rB[kb]);
+                }
+                // A operand of the state update: K^T[16t + i][tokens] from the token-major K
+                // copy (d_k permuted).  First half of the tiles now.
+                auto ktfrag = [&](int t, int kb) { return trfrag(Kc, L::LDK, kb, pperm(16 * t + 4 * (j & 3))); };
+                half8 kt0[NST], kt1[NST];
+#pragma unroll
+                for (int t = 0; t < NST / 2; ++t) {
+                    kt0[t] = ktfrag(t, 0);
+                    kt1[t] = ktfrag(t, 1);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                // O = O_hist + A Z  -> o (bf16)
+                const half8 zB[2] = {pack8(Zz[0], Zz[1]), pack8(Zz[2], Zz[3])};
+                const uint32_t obase = ((uint32_t)(cc * C) * DV + dvc + j) * 2;
+#pragma unroll
+                for (int ti = 0, n = 0; ti < 4; ++ti) {
+                    float4v acc = Oh[ti];
+#pragma unroll
+                    for (int kb = 0; kb <= (ti >> 1); ++kb, ++n) mma16(acc, af[n], zB[kb]);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) bst_bf16(ro, obase + (16 * ti + 4 * g + r) * DV * 2, acc[r]);
+                }
+                // S^T <- e^{G_C} S^T + K^T diag(e^{G_C - G}) Z
+                float4v zs[4];
+#pragma unroll
+                for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) zs[ti][r] = er[ti][r] * Zz[ti][r];
+                const half8 sZ0 = pack8(zs[0], zs[1]), sZ1 = pack8(zs[2], zs[3]);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int t = NST / 2; t < NST; ++t) {
+                    kt0[t] = ktfrag(t, 0);
+                    kt1[t] = ktfrag(t, 1);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int t = 0; t < NST; ++t) {
+                    float4v st = getf4(4 * t);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) st[r] *= eGC;
+                    mma16(st, kt0[t], sZ0);
+                    mma16(st, kt1[t], sZ1);
+                    setf4(4 * t, st);
+                }
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) seth8(oSB + 4 * kb, pack8(getf4(8 * kb), getf4(8 * kb + 4)));
+            }
+        } else {
+          if (cp < nC) {
+            const _Float16* Kp = Kb(bp);
+            const _Float16* Qp = Qb(bp);
+            if (p == 0) gram_wave(Kp, Qp, Sm(bp), At(bp), 0);
+            else gram_wave(Kp, Qp, Sm(bp), At(bp), 1);
+            lds_fence();
+            // diagonal 16x16 blocks 2p, 2p+1 of X = N^{-1}, column-oriented forward
+            // substitution: lane (block, jc) builds column jc; after x[i] is final it is
+            // eliminated from the later rows, x[t] -= N[t][i] x[i] for t > i (column i of N
+            // is row i of the stored N^T block).
+            {
+                const int b = 2 * p + ((l >> 4) & 1), jc = j;
+                const float* nb = Nd + b * 16 * L::LDN;
+                float xd[16];
+#pragma unroll
+                for (int t = 0; t < 16; ++t) xd[t] = (t == jc) ? 1.0f : 0.0f;
+#pragma unroll
+                for (int i = 0; i < 15; ++i) {
+#pragma unroll
+                    for (int q4 = (i + 1) / 4; q4 < 4; ++q4) {
+                        const float4v nc = ld4f(nb + i * L::LDN + 4 * q4);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (4 * q4 + e > i) xd[4 * q4 + e] -= nc[e] * xd[i];
+                    }
+                }
+                // X^T row 16b + jc (= column jc of the block), natural order
+                if (l < 32) {
+                    half8 h0, h1;
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) {
+                        h0[t] = (_Float16)xd[t];
+                        h1[t] = (_Float16)xd[8 + t];
+                    }
+                    *reinterpret_cast<half8*>(Xt + (16 * b + jc) * L::LDC + 16 * b) = h0;
+                    *reinterpret_cast<half8*>(Xt + (16 * b + jc) * L::LDC + 16 * b + 8) = h1;
+                }
+#pragma unroll
+                for (int t = 0; t < 16; ++t) cr[oXD + t] = __float_as_uint(xd[t]);
+            }
+            lds_fence();
+            // first level: X[b1][b0] = -X[b1][b1] N[b1][b0] X[b0][b0], b0 = 2p, b1 = 2p + 1.
+            // 16-deep reductions: fragment elements 0-3 carry k = 4g + r, elements 4-7 zero.
+            {
+                const int b0 = 2 * p, b1 = 2 * p + 1;
+                const half4 z4 = {(_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f};
+                // A: N[16b1 + i][16b0 + 4g + e] from N^T rows 16b0 + 4g + e
+                const half8 fa = cat8(ldtr(Nt + (16 * b0 + 4 * g + (j >> 2)) * L::LDC + 16 * b1 + 4 * (j & 3)), z4);
+                // B: X[16b0 + 4g + r][16b0 + j] = X^T[16b0 + j][16b0 + 4g + r]
+                const half8 fb = cat8(*reinterpret_cast<const half4*>(Xt + (16 * b0 + j) * L::LDC + 16 * b0 + 4 * g), z4);
+                float4v y = zero4();
+                mma16(y, fa, fb);
+                // A: X[16b1 + i][16b1 + 4g + e] = X^T[16b1 + 4g + e][16b1 + i];  B: y
+                const half8 fx = cat8(ldtr(Xt + (16 * b1 + 4 * g + (j >> 2)) * L::LDC + 16 * b1 + 4 * (j & 3)), z4);
+                const half8 fy = cat8(half4{(_Float16)y[0], (_Float16)y[1], (_Float16)y[2], (_Float16)y[3]}, z4);
+                float4v x2 = zero4();
+                mma16(x2, fx, fy);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) x2[r] = -x2[r];
+                // X^T row 16b0 + j, columns 16b1 + 4g .. +3
+                *reinterpret_cast<half4*>(Xt + (16 * b0 + j) * L::LDC + 16 * b1 + 4 * g) =
+                    half4{(_Float16)x2[0], (_Float16)x2[1], (_Float16)x2[2], (_Float16)x2[3]};
+                setf4(oX2, x2);
+            }
+          }
+        }
+        lds_barrier();
+
+        // ======================= phase 1 =======================
+        if (!consumer && cp < nC) {
+            // second level: X[32:64][16p:16p+16] = -X[32:64][32:64] (N[32:64][0:32] X[0:32][16p:16p+16])
+            const int n = 16 * p + j;
+            // B: X[m][n] for m in {4g + r, 16 + 4g + r} = X^T[n][...]
+            const half8 fxa = cat8(*reinterpret_cast<const half4*>(Xt + n * L::LDC + 4 * g),
+                                   *reinterpret_cast<const half4*>(Xt + n * L::LDC + 16 + 4 * g));
+            float4v y3[2];
+#pragma unroll
+            for (int ti = 0; ti < 2; ++ti) {
+                y3[ti] = zero4();
+                mma16(y3[ti], trfrag(Nt, L::LDC, 0, 32 + 16 * ti + 4 * (j & 3)), fxa);
+            }
+            const half8 fy = pack8(y3[0], y3[1]);
+#pragma unroll
+            for (int ti = 0; ti < 2; ++ti) {
+                float4v xc = zero4();
+                mma16(xc, trfrag(Xt, L::LDC, 1, 32 + 16 * ti + 4 * (j & 3)), fy);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) xc[r] = -xc[r];
+                setf4(oXC + 4 * ti, xc);
+            }
+        }
+        lds_barrier();
+
+        // ======================= phase 2 =======================
+        if (!consumer && cp < nC) {
+            // T = X diag(beta), stored column-major: T^T[m][l] = X^T[m][l] beta_m
+            const float* sm = Sm(bp);
+            if (l < 32) {
+                const int b = 2 * p + (l >> 4), m = 16 * b + j;
+                const float bm = sm[L::SB + m];
+                half8 h0, h1;
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    h0[t] = (_Float16)(__uint_as_float(cr[oXD + t]) * bm);
+                    h1[t] = (_Float16)(__uint_as_float(cr[oXD + 8 + t]) * bm);
+                }
+                *reinterpret_cast<half8*>(Tt + m * L::LDC + 16 * b) = h0;
+                *reinterpret_cast<half8*>(Tt + m * L::LDC + 16 * b + 8) = h1;
+            }
+            {
+                const int m = 32 * p + j;  // block column 2p; rows 32p + 16 + 4g ..
+                const float bm = sm[L::SB + m];
+                const float4v x2 = getf4(oX2);
+                *reinterpret_cast<half4*>(Tt + m * L::LDC + 32 * p + 16 + 4 * g) =
+                    half4{(_Float16)(x2[0] * bm), (_Float16)(x2[1] * bm), (_Float16)(x2[2] * bm), (_Float16)(x2[3] * bm)};
+            }
+            {
+                const int m = 16 * p + j;
+                const float bm = sm[L::SB + m];
+#pragma unroll
+                for (int ti = 0; ti < 2; ++ti) {
+                    const float4v xc = getf4(oXC + 4 * ti);
+                    *reinterpret_cast<half4*>(Tt + m * L::LDC + 32 + 16 * ti + 4 * g) =
+                        half4{(_Float16)(xc[0] * bm), (_Float16)(xc[1] * bm), (_Float16)(xc[2] * bm), (_Float16)(xc[3] * bm)};
+                }
+            }
+        }
+        stage_kq(cs);
+        stage_v();
+        lds_barrier();
+    }
+
+    if (consumer && a.Sf != nullptr) {
+        float* sf = a.Sf + bh * (int64_t)DV * DK + (int64_t)(dvc + j) * DK;
+#pragma unroll
+        for (int t = 0; t < NST; ++t) *reinterpret_cast<float4v*>(sf + 16 * t + 4 * g) = getf4(4 * t);
+    }
+}
+
+template <int DK>
+static hipError_t launch_pc(const PcArgs& a, int64_t nwg, hipStream_t st) {
+    using L = PcLds<DK>;
+    auto kern = chunk_fwd_pc_kernel<DK>;
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, L::total);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(256), L::total, st, a);
+    return hipGetLastError();
+}
+
+hipError_t chunk_fwd_pc_dispatch(int64_t BH, int64_t T, int dk, int dv, const void* q, const void* k, const void* v,
+                                 const float* g, const float* beta, const float* S0, void* o, float* Sf,
+                                 hipStream_t st) {
+    PcArgs a;
+    a.T = T;
+    a.dv = dv;
+    a.ntiles = dv / 32;
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k);
+    a.v = static_cast<const uint16_t*>(v);
+    a.g = g;
+    a.beta = beta;
+    a.S0 = S0;
+    a.o = static_cast<uint16_t*>(o);
+    a.Sf = Sf;
+    const int64_t nwg = BH * a.ntiles;
+    if (dk == 128) return launch_pc<128>(a, nwg, st);
+    return launch_pc<64>(a, nwg, st);
+}
+
+}  // namespace gdr

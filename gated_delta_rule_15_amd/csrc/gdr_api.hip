@@ -9,6 +9,9 @@ namespace gdr {
 hipError_t chunk_fwd_dispatch(int64_t BH, int64_t T, int dk, int dv, bool bf16, bool channel, const void* q,
                               const void* k, const void* v, const float* g, const float* beta, const float* S0,
                               void* o, float* Sf, hipStream_t st);
+hipError_t chunk_fwd_pc_dispatch(int64_t BH, int64_t T, int dk, int dv, const void* q, const void* k, const void* v,
+                                 const float* g, const float* beta, const float* S0, void* o, float* Sf,
+                                 hipStream_t st);
 hipError_t decode_dispatch(int64_t NH, int dk, int dv, bool bf16, bool channel, const void* q, const void* k,
                            const void* v, const float* g, const float* beta, float* S, void* o, hipStream_t st);
 }  // namespace gdr
@@ -85,9 +88,13 @@ gdr_status gdr_chunk_fwd(int64_t B, int64_t H, int64_t T, int d_k, int d_v, int 
     int64_t nwg;
     if (!mul_ok(BH, d_v / 32, &nwg) || nwg > kMaxGrid) return GDR_ERR_SHAPE;
     if (!final_state && BHT == 0) return GDR_OK;
-    hipError_t e = gdr::chunk_fwd_dispatch(BH, T, d_k, d_v, io_dtype == GDR_BF16, gate == GDR_GATE_CHANNEL, q, k,
-                                           v, g, beta, initial_state, o, final_state,
-                                           static_cast<hipStream_t>(stream));
+    hipError_t e;
+    if (io_dtype == GDR_BF16)  // fp16-MFMA producer/consumer kernel
+        e = gdr::chunk_fwd_pc_dispatch(BH, T, d_k, d_v, q, k, v, g, beta, initial_state, o, final_state,
+                                       static_cast<hipStream_t>(stream));
+    else  // fp32 operands throughout
+        e = gdr::chunk_fwd_dispatch(BH, T, d_k, d_v, false, gate == GDR_GATE_CHANNEL, q, k, v, g, beta,
+                                    initial_state, o, final_state, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
 }
 

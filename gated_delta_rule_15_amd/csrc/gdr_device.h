@@ -109,4 +109,13 @@ __device__ __forceinline__ void store4_transposed(OpT* base, int ld, int col, in
 
 __device__ __forceinline__ float fast_exp(float x) { return __expf(x); }
 
+// Workgroups are dispatched round-robin over the 8 XCDs; renumber them so that consecutive
+// logical indices (the d_v tiles of one sequence, which read the same q/k chunks) land on
+// the same XCD and share its L2.  A bijection of [0, nwg) for any nwg.
+__device__ __forceinline__ int xcd_major_index(int wg, int nwg) {
+    const int xcd = wg & 7, slot = wg >> 3;
+    const int q8 = nwg >> 3, r8 = nwg & 7;
+    return xcd * q8 + (xcd < r8 ? xcd : r8) + slot;
+}
+
 }  // namespace gdr
