@@ -65,6 +65,7 @@ struct PcLds {
     static constexpr int LDC = C + 8;    // halfs, rows of C-wide fp16 matrices
     static constexpr int LDV = C + 4;    // floats, rows of V^T
     static constexpr int LDN = 16 + 4;   // floats, rows of a 16x16 fp32 block
+    static constexpr int LDO = C + 8;    // bf16, rows of the output tile O^T
     // per-chunk factor table (floats):
     //   [0,64) G   [64,128) e^G   [128,192) e^{G_C - G}   [192,256) beta   [256] e^{G_C}
     //   [272,336)  cf[m]     = e^{Gend(blk(m)) - G_m}           (<= 1)
@@ -88,9 +89,10 @@ struct PcLds {
     static constexpr int oNt = oTt + szC;           // off-diagonal blocks of N^T (fp16)
     static constexpr int oXt = oNt + szC;           // X^T, X = N^{-1} (fp16)
     static constexpr int oNd = oXt + szC;           // diagonal blocks of N^T (fp32)
-    static constexpr int total = oNd + 4 * 16 * LDN * 4;
+    static constexpr int oOt = oNd + 4 * 16 * LDN * 4;  // O^T of the consumer chunk (bf16)
+    static constexpr int total = oOt + 32 * LDO * 2;
     static_assert(total <= 160 * 1024, "LDS budget of one gfx950 CU exceeded");
-    static_assert((oAt0 | oAt1 | oSm0 | oSm1 | oVt | oTt | oNt | oXt | oNd) % 16 == 0, "alignment");
+    static_assert((oAt0 | oAt1 | oSm0 | oSm1 | oVt | oTt | oNt | oXt | oNd | oOt) % 16 == 0, "alignment");
 };
 
 __device__ __forceinline__ void mma16(float4v& acc, const half8& a, const half8& b) {
@@ -142,6 +144,29 @@ __device__ __forceinline__ void stage8(_Float16* row, int m0, const uint4& u) {
     *reinterpret_cast<half4*>(row + pperm(m0 + 4)) = b;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP lane moves (no LDS traffic):
+// shifts by 1, 2, 4, 8 within each 16-lane row, then the row totals are broadcast into the
+// following rows.  Lanes whose source falls outside the row receive 0.
+__device__ __forceinline__ float dpp_add(float x, int y_bits) { return x + __int_as_float(y_bits); }
+__device__ __forceinline__ float wave_inclusive_scan(float x) {
+    int b = __float_as_int(x);
+    x = dpp_add(x, __builtin_amdgcn_update_dpp(0, b, 0x111, 0xf, 0xf, false));  // row_shr:1
+    b = __float_as_int(x);
+    x = dpp_add(x, __builtin_amdgcn_update_dpp(0, b, 0x112, 0xf, 0xf, false));  // row_shr:2
+    b = __float_as_int(x);
+    x = dpp_add(x, __builtin_amdgcn_update_dpp(0, b, 0x114, 0xf, 0xf, false));  // row_shr:4
+    b = __float_as_int(x);
+    x = dpp_add(x, __builtin_amdgcn_update_dpp(0, b, 0x118, 0xf, 0xf, false));  // row_shr:8
+    b = __float_as_int(x);
+    x = dpp_add(x, __builtin_amdgcn_update_dpp(0, b, 0x142, 0xa, 0xf, false));  // row_bcast:15
+    b = __float_as_int(x);
+    x = dpp_add(x, __builtin_amdgcn_update_dpp(0, b, 0x143, 0xc, 0xf, false));  // row_bcast:31
+    return x;
+}
+__device__ __forceinline__ float lane_value(float x, int lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
+}
+
 // Buffer resources: a load past the resource's byte range returns zeros and a store past it
 // is dropped, which pads the ragged last chunk with identity tokens (k = q = v = 0,
 // g = beta = 0) and clips its output rows without any branch.
@@ -156,8 +181,13 @@ __device__ __forceinline__ uint4 bld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
 __device__ __forceinline__ float bld4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
-__device__ __forceinline__ void bst_bf16(__amdgpu_buffer_rsrc_t r, uint32_t off, float x) {
-    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (__bf16)x), r, off, 0, 0);
+__device__ __forceinline__ void bst16(__amdgpu_buffer_rsrc_t r, uint32_t off, const uint4& u) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4{u.x, u.y, u.z, u.w}, r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return (uint32_t)__builtin_bit_cast(unsigned short, (__bf16)lo) |
+           ((uint32_t)__builtin_bit_cast(unsigned short, (__bf16)hi) << 16);
 }
 
 template <int DK>
@@ -177,6 +207,7 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {
     _Float16* Nt = reinterpret_cast<_Float16*>(smem + L::oNt);
     _Float16* Xt = reinterpret_cast<_Float16*>(smem + L::oXt);
     float* Nd = reinterpret_cast<float*>(smem + L::oNd);
+    _Float16* Ot = reinterpret_cast<_Float16*>(smem + L::oOt);  // holds bf16 bit patterns
 
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, j = l & 15, g = l >> 4;
     const bool consumer = w < 2;
@@ -274,32 +305,30 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {
             stage8(Kb(buf) + row * L::LDK, col, getu4(oKR + 4 * u));
             stage8(Qb(buf) + row * L::LDK, col, getu4(oQR + 4 * u));
         }
-        if (w == 0) {  // in-chunk cumulative log-decay and the factor table
-            float x = __uint_as_float(cr[oGR]);
+    };
+    // In-chunk cumulative log-decay G and the per-chunk factor table of chunk c (wave 0,
+    // from the g and beta values its issue_kq(c) loaded).
+    auto scan = [&](int64_t c) {
+        const int buf = (int)(c & 1);
+        const float x = wave_inclusive_scan(__uint_as_float(cr[oGR]));
+        const float GC = lane_value(x, 63);
+        float ge[4];
 #pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float y = __shfl_up(x, off);
-                if (l >= off) x += y;
-            }
-            const float GC = __shfl(x, 63);
-            float ge[4];
+        for (int b = 0; b < 4; ++b) ge[b] = lane_value(x, 16 * b + 15);
+        const int blk = l >> 4;
+        const float beta = __uint_as_float(cr[oGR + 1]);
+        float* sm = Sm(buf);
+        sm[L::SG + l] = x;
+        sm[L::SEG + l] = fast_exp(x);
+        sm[L::SEGR + l] = fast_exp(GC - x);
+        sm[L::SB + l] = beta;
+        if (l == 0) sm[L::SEGC] = fast_exp(GC);
+        sm[L::SCF + l] = fast_exp(ge[blk] - x);
 #pragma unroll
-            for (int b = 0; b < 4; ++b) ge[b] = __shfl(x, 16 * b + 15);
-            const int blk = l >> 4;
-            const float beta = __uint_as_float(cr[oGR + 1]);
-            float* sm = Sm(buf);
-            sm[L::SG + l] = x;
-            sm[L::SEG + l] = fast_exp(x);
-            sm[L::SEGR + l] = fast_exp(GC - x);
-            sm[L::SB + l] = beta;
-            if (l == 0) sm[L::SEGC] = fast_exp(GC);
-            sm[L::SCF + l] = fast_exp(ge[blk] - x);
-#pragma unroll
-            for (int b = 0; b < 3; ++b) {
-                const float f = blk > b ? fast_exp(x - ge[b]) : 0.0f;
-                sm[L::SRF + 64 * b + l] = f;
-                sm[L::SRB + 64 * b + l] = beta * f;
-            }
+        for (int b = 0; b < 3; ++b) {
+            const float f = blk > b ? fast_exp(x - ge[b]) : 0.0f;
+            sm[L::SRF + 64 * b + l] = f;
+            sm[L::SRB + 64 * b + l] = beta * f;
         }
     };
     auto stage_v = [&]() {  // V^T tile, fp32 [channel][token]
@@ -317,6 +346,7 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {
     if (nC > 0) {
         issue_kq(0);
         stage_kq(0);
+        if (w == 0) scan(0);
     }
     lds_barrier();
 
@@ -338,6 +368,32 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {
 #pragma unroll
             for (int r = 0; r < 2; ++r) f[4 + r] = ld8(Qp + (16 * (2 * P + r) + j) * L::LDK + 32 * kb + 8 * g);
         };
+        // Per-tile scale factors, formed before the products so that their LDS reads and
+        // exponentials overlap the MFMAs: element (l0 + r, m) of tile t is acc * fr[t][r] * fc[t]
+        // off the diagonal; on it fr already holds the exact decay (and beta for N) with the
+        // causal mask applied.
+        float4v fr[NT];
+        float fc[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const int ti = ti_[P][t], tj = tj_[P][t];
+            const bool isQ = tq[P][t];
+            const int m = 16 * tj + j, l0 = 16 * ti + 4 * g;
+            if (ti != tj) {
+                fr[t] = ld4f(sm + (isQ ? L::SRF : L::SRB) + 64 * tj + l0);
+                fc[t] = sm[L::SCF + m];
+            } else {
+                const float Gm = sm[L::SG + m];
+                const float4v Gl = ld4f(sm + L::SG + l0);
+                const float4v bl = isQ ? float4v{1.0f, 1.0f, 1.0f, 1.0f} : ld4f(sm + L::SB + l0);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const bool keep = isQ ? (m <= l0 + r) : (m < l0 + r);
+                    fr[t][r] = keep ? bl[r] * fast_exp(Gl[r] - Gm) : 0.0f;
+                }
+                fc[t] = 1.0f;
+            }
+        }
         float4v acc[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t) acc[t] = zero4();
@@ -365,30 +421,17 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {
             const int m = 16 * tj + j;            // this lane's column
             const int l0 = 16 * ti + 4 * g;       // first of its 4 rows
             float v[4];
-            if (ti != tj) {
-                // Gam[l][m] = rf[tj][l] cf[m] (both <= 1); beta folded into rb for N
-                const float cfm = sm[L::SCF + m];
-                const float4v rf = ld4f(sm + (isQ ? L::SRF : L::SRB) + 64 * tj + l0);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) v[r] = acc[t][r] * rf[r] * cfm;
+            for (int r = 0; r < 4; ++r) v[r] = acc[t][r] * fr[t][r] * fc[t];
+            if (ti == tj && !isQ) {
+                // N^T diagonal block ti, column j: rows 4g..4g+3, unit diagonal
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (m == l0 + r) v[r] = 1.0f;
+                *reinterpret_cast<float4v*>(Nd + (ti * 16 + j) * L::LDN + 4 * g) = float4v{v[0], v[1], v[2], v[3]};
+            } else {
                 _Float16* dst = (isQ ? Ap : Nt) + m * L::LDC + l0;
                 *reinterpret_cast<half4*>(dst) = half4{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
-            } else {
-                const float Gm = sm[L::SG + m];
-                const float4v Gl = ld4f(sm + L::SG + l0);
-                if (isQ) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) v[r] = (m <= l0 + r) ? acc[t][r] * fast_exp(Gl[r] - Gm) : 0.0f;
-                    *reinterpret_cast<half4*>(Ap + m * L::LDC + l0) =
-                        half4{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
-                } else {
-                    const float4v bl = ld4f(sm + L::SB + l0);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        v[r] = (m < l0 + r) ? bl[r] * acc[t][r] * fast_exp(Gl[r] - Gm) : (m == l0 + r ? 1.0f : 0.0f);
-                    // N^T diagonal block ti, column j: rows 4g..4g+3
-                    *reinterpret_cast<float4v*>(Nd + (ti * 16 + j) * L::LDN + 4 * g) = float4v{v[0], v[1], v[2], v[3]};
-                }
             }
         }
     };
@@ -498,16 +541,26 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {
                     kt1[t] = ktfrag(t, 1);
                 }
                 __builtin_amdgcn_sched_barrier(0);
-                // O = O_hist + A Z  -> o (bf16)
+                // O = O_hist + A Z, rounded to bf16 into this wave's rows of O^T; read back
+                // transposed (a lane gets 8 consecutive channels of one token) for 16-byte
+                // stores of o.
                 const half8 zB[2] = {pack8(Zz[0], Zz[1]), pack8(Zz[2], Zz[3])};
-                const uint32_t obase = ((uint32_t)(cc * C) * DV + dvc + j) * 2;
 #pragma unroll
                 for (int ti = 0, n = 0; ti < 4; ++ti) {
                     float4v acc = Oh[ti];
 #pragma unroll
                     for (int kb = 0; kb <= (ti >> 1); ++kb, ++n) mma16(acc, af[n], zB[kb]);
+                    *reinterpret_cast<uint2*>(Ot + (16 * w + j) * L::LDO + 16 * ti + 4 * g) =
+                        uint2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+                }
+                lds_fence();
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) bst_bf16(ro, obase + (16 * ti + 4 * g + r) * DV * 2, acc[r]);
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    const int tb = 32 * s2 + 16 * (g >> 1), d = 16 * w + 8 * (g & 1);
+                    const _Float16* rp = Ot + (d + (j >> 2)) * L::LDO + tb + 4 * (j & 3);
+                    const uint2 lo = __builtin_bit_cast(uint2, ldtr(rp));
+                    const uint2 hi = __builtin_bit_cast(uint2, ldtr(rp + 4 * L::LDO));
+                    bst16(ro, ((uint32_t)(cc * C + tb + j) * DV + dv0 + d) * 2, uint4{lo.x, lo.y, hi.x, hi.y});
                 }
                 // S^T <- e^{G_C} S^T + K^T diag(e^{G_C - G}) Z
                 float4v zs[4];
@@ -549,6 +602,13 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {
             {
                 const int b = 2 * p + ((l >> 4) & 1), jc = j;
                 const float* nb = Nd + b * 16 * L::LDN;
+                // all rows first: the substitution is a chain of dependent FMAs, and waiting
+                // for each row's LDS read inside it would serialise the latencies
+                float4v nr[15][4];
+#pragma unroll
+                for (int i = 0; i < 15; ++i)
+#pragma unroll
+                    for (int q4 = (i + 1) / 4; q4 < 4; ++q4) nr[i][q4] = ld4f(nb + i * L::LDN + 4 * q4);
                 float xd[16];
 #pragma unroll
                 for (int t = 0; t < 16; ++t) xd[t] = (t == jc) ? 1.0f : 0.0f;
@@ -556,10 +616,9 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {
                 for (int i = 0; i < 15; ++i) {
 #pragma unroll
                     for (int q4 = (i + 1) / 4; q4 < 4; ++q4) {
-                        const float4v nc = ld4f(nb + i * L::LDN + 4 * q4);
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
-                            if (4 * q4 + e > i) xd[4 * q4 + e] -= nc[e] * xd[i];
+                            if (4 * q4 + e > i) xd[4 * q4 + e] -= nr[i][q4][e] * xd[i];
                     }
                 }
                 // X^T row 16b + jc (= column jc of the block), natural order
@@ -605,6 +664,8 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {
         lds_barrier();
 
         // ======================= phase 1 =======================
+        // The consumer is done with Sm(cs & 1) = Sm(cc & 1); wave 0 fills it for chunk cs.
+        if (w == 0) scan(cs);
         if (!consumer && cp < nC) {
             // second level: X[32:64][16p:16p+16] = -X[32:64][32:64] (N[32:64][0:32] X[0:32][16p:16p+16])
             const int n = 16 * p + j;
