@@ -6,6 +6,7 @@ decode step's HBM GB/s (256 sequences x 32 heads, d=128, 64 steps on a 512 MiB s
 and the long-context workload (B=1, H=32, T=65536, carried state).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extra]
+    python bench.py --pmc-run      # kernels only, for rocprofv3 counter passes
 
 Prints ONE JSON line.  Inputs are seeded synthetic tensors (gdr_synth) resident in HBM
 before timing starts; two input sets alternate so the 256 MB last-level cache cannot
@@ -27,6 +28,29 @@ sys.path.insert(0, os.path.join(ROOT, "tests"))
 
 PEAK_MFMA_F16 = 2500.0  # TFLOP/s, MI355X dense fp16/bf16
 PEAK_HBM = 8000.0       # GB/s, MI355X HBM3E
+CHUNK_KERNEL = "chunk_fwd_pc_kernel<128>"
+CHUNK_SOURCE = os.path.join(ROOT, "gated_delta_rule_15_amd", "csrc", "chunk_fwd_pc.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "chunk_fwd_pc_gdn_bf16_B4_H16_T4096_traffic.json")
+COPY_BYTES = 256 << 20  # calibration copy for the HBM byte counters
+
+
+def source_digest(path):
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the chunk kernel from the committed counter summary, or None
+    when the summary is missing or was taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256_16") != source_digest(CHUNK_SOURCE):
+        return None
+    return rec.get("hbm_bytes_per_launch")
 
 
 def chunk_flops(B, H, T, dk, dv, C=64):
@@ -157,6 +181,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="headline workload only")
+    ap.add_argument("--pmc-run", action="store_true",
+                    help="launch the headline chunk kernel --steps times and one 256 MiB device copy, print nothing")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path shards by "
@@ -170,12 +196,23 @@ def main():
     gdr.load_library()
     w = gdr_synth.WORKLOADS[2]
     sets = make_chunk_sets(torch, gdr_synth, w)
+    if args.pmc_run:
+        # Counter passes: the chunk kernel on the headline workload, then a plain copy of
+        # known size whose FETCH_SIZE / WRITE_SIZE calibrate the counters' byte units.
+        time_chunk(torch, gdr, sets, args.steps, 0)
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        return
     ms_mean, ms_med, wall, o, S = time_chunk(torch, gdr, sets, args.steps, args.warmup)
     flops = chunk_flops(w.B, w.H, w.T, w.d_k, w.d_v)
     nbytes = chunk_bytes(w.B, w.H, w.T, w.d_k, w.d_v)
     tflops = flops / (ms_mean * 1e-3) / 1e12
     gbs = nbytes / (ms_mean * 1e-3) / 1e9
-    tokens_per_s = w.B * w.T / (ms_mean * 1e-3)
+    ms_step = wall / args.steps * 1e3  # timed region: K launches between two synchronizations
+    tokens_per_s = w.B * w.T / (ms_step * 1e-3)
     result = {
         "metric": "gated-delta chunk_fwd tokens/s (H=16,T=4096,d=128) + % MFMA peak; decode GB/s",
         "value": round(tokens_per_s, 1),
@@ -183,18 +220,20 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_mean, 5),
+        "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16 MFMA operands, f32 accumulate/state (bf16 I/O)",
+        "dtype": "f16",
         "data": "synthetic (seeded gdr_synth; two alternating input sets)",
-        "config": {"workload": "gdn_bf16_train: chunk_fwd B=4 H=16 T=4096 d_k=d_v=128 chunk=64 bf16, zero S0",
-                   "B": w.B, "H": w.H, "T": w.T, "d_k": w.d_k, "d_v": w.d_v, "chunk": 64, "gate": "scalar"},
+        "config": {"workload": "gdn_bf16_train: chunk_fwd B=4 H=16 T=4096 d_k=d_v=128 chunk=64 bf16 I/O, "
+                               "fp32 gate/beta/state, zero S0",
+                   "B": w.B, "H": w.H, "T": w.T, "d_k": w.d_k, "d_v": w.d_v, "chunk": 64, "gate": "scalar",
+                   "compute": "f16 MFMA operands, f32 accumulation and state"},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_MFMA_F16, "unit": "TFLOP/s",
-                     "frac": round(tflops / PEAK_MFMA_F16, 4), "traffic": None,
-                     "flops_per_launch": flops, "kernel": "chunk_fwd_scalar_kernel<128, bf16, f16>",
-                     "ms_per_launch_median": round(ms_med, 5)},
+                     "frac": round(tflops / PEAK_MFMA_F16, 4), "traffic": measured_traffic(),
+                     "flops_per_launch": flops, "kernel": CHUNK_KERNEL,
+                     "ms_per_launch_mean": round(ms_mean, 5), "ms_per_launch_median": round(ms_med, 5)},
         "roofline_hbm": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM, 4), "bytes_per_launch": nbytes},
         "wall_s_timed_region": round(wall, 4),
