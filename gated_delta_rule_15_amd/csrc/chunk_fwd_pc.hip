@@ -35,7 +35,7 @@
 // registers only.  K^T fragments (reduction over tokens) come from the token-major K copy
 // through ds_read_b64_tr_b16, which hands lane i of each 16-lane group element (i & 3) of
 // the 4-element rows addressed by lanes (i >> 2) + 4e, e = 0..3.
-#include "gdr_device.h"
+#include "chunk_common.h"
 
 namespace gdr {
 
@@ -52,11 +52,6 @@ struct PcArgs {
     uint16_t* o;
     float* Sf;
 };
-
-// position of logical index m inside its row under the 32-block permutation
-__device__ __forceinline__ int pperm(int m) {
-    return (m & ~31) | (((m >> 2) & 3) << 3) | (((m >> 4) & 1) << 2) | (m & 3);
-}
 
 template <int DK>
 struct PcLds {
@@ -94,101 +89,6 @@ struct PcLds {
     static_assert(total <= 160 * 1024, "LDS budget of one gfx950 CU exceeded");
     static_assert((oAt0 | oAt1 | oSm0 | oSm1 | oVt | oTt | oNt | oXt | oNd | oOt) % 16 == 0, "alignment");
 };
-
-__device__ __forceinline__ void mma16(float4v& acc, const half8& a, const half8& b) {
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
-}
-__device__ __forceinline__ half8 ld8(const _Float16* p) { return *reinterpret_cast<const half8*>(p); }
-__device__ __forceinline__ half4 ldtr(const _Float16* p) {
-    typedef short short4v __attribute__((ext_vector_type(4)));
-    const short4v v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4v*)(p));
-    return __builtin_bit_cast(half4, v);
-}
-__device__ __forceinline__ half8 cat8(const half4& lo, const half4& hi) {
-    return half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-}
-__device__ __forceinline__ half8 pack8(const float4v& lo, const float4v& hi) {
-    half8 h;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        h[r] = (_Float16)lo[r];
-        h[4 + r] = (_Float16)hi[r];
-    }
-    return h;
-}
-__device__ __forceinline__ float4v zero4() { return float4v{0.0f, 0.0f, 0.0f, 0.0f}; }
-__device__ __forceinline__ float4v ld4f(const float* p) { return *reinterpret_cast<const float4v*>(p); }
-// Wave-local ordering of LDS writes before later LDS reads of the same wave.
-__device__ __forceinline__ void lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-// Workgroup barrier for LDS traffic only.  Unlike __syncthreads() it does not wait for the
-// wave's outstanding global loads, so prefetches stay in flight across phases; no global
-// memory is exchanged between waves.
-__device__ __forceinline__ void lds_barrier() {
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
-// 8 bf16 (one uint4) -> 8 fp16 written as two 4-element groups at permuted positions.
-__device__ __forceinline__ void stage8(_Float16* row, int m0, const uint4& u) {
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-    half4 a, b;
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-        a[2 * e] = (_Float16)__uint_as_float(w[e] << 16);
-        a[2 * e + 1] = (_Float16)__uint_as_float(w[e] & 0xffff0000u);
-        b[2 * e] = (_Float16)__uint_as_float(w[2 + e] << 16);
-        b[2 * e + 1] = (_Float16)__uint_as_float(w[2 + e] & 0xffff0000u);
-    }
-    *reinterpret_cast<half4*>(row + pperm(m0)) = a;
-    *reinterpret_cast<half4*>(row + pperm(m0 + 4)) = b;
-}
-
-// Inclusive prefix sum over the 64 lanes of a wave with DPP lane moves (no LDS traffic):
-// shifts by 1, 2, 4, 8 within each 16-lane row, then the row totals are broadcast into the
-// following rows.  Lanes whose source falls outside the row receive 0.
-__device__ __forceinline__ float dpp_add(float x, int y_bits) { return x + __int_as_float(y_bits); }
-__device__ __forceinline__ float wave_inclusive_scan(float x) {
-    int b = __float_as_int(x);
-    x = dpp_add(x, __builtin_amdgcn_update_dpp(0, b, 0x111, 0xf, 0xf, false));  // row_shr:1
-    b = __float_as_int(x);
-    x = dpp_add(x, __builtin_amdgcn_update_dpp(0, b, 0x112, 0xf, 0xf, false));  // row_shr:2
-    b = __float_as_int(x);
-    x = dpp_add(x, __builtin_amdgcn_update_dpp(0, b, 0x114, 0xf, 0xf, false));  // row_shr:4
-    b = __float_as_int(x);
-    x = dpp_add(x, __builtin_amdgcn_update_dpp(0, b, 0x118, 0xf, 0xf, false));  // row_shr:8
-    b = __float_as_int(x);
-    x = dpp_add(x, __builtin_amdgcn_update_dpp(0, b, 0x142, 0xa, 0xf, false));  // row_bcast:15
-    b = __float_as_int(x);
-    x = dpp_add(x, __builtin_amdgcn_update_dpp(0, b, 0x143, 0xc, 0xf, false));  // row_bcast:31
-    return x;
-}
-__device__ __forceinline__ float lane_value(float x, int lane) {
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
-}
-
-// Buffer resources: a load past the resource's byte range returns zeros and a store past it
-// is dropped, which pads the ragged last chunk with identity tokens (k = q = v = 0,
-// g = beta = 0) and clips its output rows without any branch.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
-}
-__device__ __forceinline__ uint4 bld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-    return uint4{v[0], v[1], v[2], v[3]};
-}
-__device__ __forceinline__ float bld4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
-}
-__device__ __forceinline__ void bst16(__amdgpu_buffer_rsrc_t r, uint32_t off, const uint4& u) {
-    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-    __builtin_amdgcn_raw_buffer_store_b128(u32x4{u.x, u.y, u.z, u.w}, r, off, 0, 0);
-}
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return (uint32_t)__builtin_bit_cast(unsigned short, (__bf16)lo) |
-           ((uint32_t)__builtin_bit_cast(unsigned short, (__bf16)hi) << 16);
-}
 
 template <int DK>
 __global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {

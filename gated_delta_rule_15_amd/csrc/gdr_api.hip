@@ -12,6 +12,8 @@ hipError_t chunk_fwd_dispatch(int64_t BH, int64_t T, int dk, int dv, bool bf16, 
 hipError_t chunk_fwd_pc_dispatch(int64_t BH, int64_t T, int dk, int dv, const void* q, const void* k, const void* v,
                                  const float* g, const float* beta, const float* S0, void* o, float* Sf,
                                  hipStream_t st);
+hipError_t chunk_kda_dispatch(int64_t BH, int64_t T, int dk, int dv, const void* q, const void* k, const void* v,
+                              const float* g, const float* beta, const float* S0, void* o, float* Sf, hipStream_t st);
 hipError_t decode_dispatch(int64_t NH, int dk, int dv, bool bf16, bool channel, const void* q, const void* k,
                            const void* v, const float* g, const float* beta, float* S, void* o, hipStream_t st);
 }  // namespace gdr
@@ -20,6 +22,8 @@ namespace {
 
 constexpr int kVersion = 10000 * 0 + 100 * 1 + 0;
 constexpr int64_t kMaxGrid = 0x7fffffff;
+// The kernels address one sequence with 32-bit byte offsets: T * d * 4 stays below 2^32.
+constexpr int64_t kMaxT = int64_t(1) << 22;
 
 bool mul_ok(int64_t a, int64_t b, int64_t* out) {
     if (a < 0 || b < 0) return false;
@@ -67,6 +71,7 @@ gdr_status gdr_chunk_fwd(int64_t B, int64_t H, int64_t T, int d_k, int d_v, int 
     if (B < 0 || H < 0 || T < 0) return GDR_ERR_INVALID_ARG;
     gdr_status s = check_common(d_k, d_v, io_dtype, gate);
     if (s != GDR_OK) return s;
+    if (T > kMaxT) return GDR_ERR_SHAPE;
     int64_t BH, BHT, nq, nv, nstate, ng;
     const int64_t esz = io_dtype == GDR_BF16 ? 2 : 4;
     if (!mul_ok(B, H, &BH) || !mul_ok(BH, T, &BHT) || !mul_ok(BHT, d_k, &nq) || !mul_ok(BHT, d_v, &nv) ||
@@ -82,14 +87,16 @@ gdr_status gdr_chunk_fwd(int64_t B, int64_t H, int64_t T, int d_k, int d_v, int 
     if (final_state && initial_state && final_state != initial_state &&
         overlaps(final_state, nstate, initial_state, nstate))
         return GDR_ERR_INVALID_ARG;
-    if (io_dtype == GDR_F32 && d_k != 64) return GDR_ERR_UNSUPPORTED;
-    if (gate == GDR_GATE_CHANNEL) return GDR_ERR_UNSUPPORTED;
+    if (io_dtype == GDR_F32 && (d_k != 64 || gate == GDR_GATE_CHANNEL)) return GDR_ERR_UNSUPPORTED;
     if (BH == 0) return GDR_OK;
     int64_t nwg;
     if (!mul_ok(BH, d_v / 32, &nwg) || nwg > kMaxGrid) return GDR_ERR_SHAPE;
     if (!final_state && BHT == 0) return GDR_OK;
     hipError_t e;
-    if (io_dtype == GDR_BF16)  // fp16-MFMA producer/consumer kernel
+    if (io_dtype == GDR_BF16 && gate == GDR_GATE_CHANNEL)  // per-channel gate, fp16 MFMA
+        e = gdr::chunk_kda_dispatch(BH, T, d_k, d_v, q, k, v, g, beta, initial_state, o, final_state,
+                                    static_cast<hipStream_t>(stream));
+    else if (io_dtype == GDR_BF16)  // fp16-MFMA producer/consumer kernel
         e = gdr::chunk_fwd_pc_dispatch(BH, T, d_k, d_v, q, k, v, g, beta, initial_state, o, final_state,
                                        static_cast<hipStream_t>(stream));
     else  // fp32 operands throughout

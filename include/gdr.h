@@ -27,8 +27,8 @@
  *  - io_dtype applies to q, k, v and o (GDR_BF16 or GDR_F32); g, beta and the state are
  *    always float32.
  *  - Supported sizes: d_k in {64, 128}; d_v a multiple of 32 in [32, 256].  With
- *    io_dtype = GDR_F32 the chunked forward supports d_k = 64 only (GDR_ERR_UNSUPPORTED
- *    otherwise); decode supports both.
+ *    io_dtype = GDR_F32 the chunked forward supports d_k = 64 and the scalar gate only
+ *    (GDR_ERR_UNSUPPORTED otherwise); decode supports every combination.
  *  - Numerics: bf16 inputs are widened exactly; the chunked forward multiplies on fp16 MFMA
  *    (inputs with |x| >= 65504 overflow there) with fp32 accumulation, holds the state in
  *    fp32, and rounds o to bf16 (RNE) once at the end.  The fp32-I/O forward and the
@@ -83,8 +83,15 @@ const char *gdr_status_string(int status);
  *   final_state    [B, H, d_v, d_k] float32, written, or NULL to skip; may alias
  *                  initial_state exactly (each state tile is read before it is written)
  *
- * T may be any value >= 0 (a ragged last chunk is handled exactly; T = 0 copies the
- * initial state, or zeros, to final_state).  B*H*T*max(d_k, d_v) must fit in int64.
+ * T may be any value in [0, 2^22] (a ragged last chunk is handled exactly; T = 0 copies
+ * the initial state, or zeros, to final_state); a longer sequence returns GDR_ERR_SHAPE
+ * (split it and carry the state).  B*H*T*max(d_k, d_v) must fit in int64.
+ *
+ * Per-channel gate: bf16 I/O only (GDR_ERR_UNSUPPORTED for GDR_F32).  Inside each 16-token
+ * block the decay is factored through the block's 9th token; the fast path covers a
+ * log-decay spread of up to 6 from that token in every channel, a wider block is
+ * recomputed on a bf16 path that holds while every per-token log-decay is >= -10 (a
+ * decay factor of at least 4.5e-5 per token).
  */
 gdr_status gdr_chunk_fwd(int64_t B, int64_t H, int64_t T, int d_k, int d_v,
                          int io_dtype, int gate,

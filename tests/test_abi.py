@@ -68,7 +68,9 @@ def decode(lib, N=1, H=1, dk=128, dv=128, io=0, gate=0, q=FAKE, k=FAKE, v=FAKE, 
     (dict(beta=None), INVALID), (dict(o=None), INVALID),
     (dict(o=FAKE), INVALID),                                   # o overlaps q
     (dict(io=1, dk=128), UNSUP),                               # fp32 chunk path is d_k = 64 only
+    (dict(io=1, dk=64, dv=64, gate=1), UNSUP),                 # per-channel gate needs bf16 I/O
     (dict(B=1 << 40, H=1 << 30), SHAPE),                       # size overflow
+    (dict(T=(1 << 22) + 1), SHAPE),                            # 32-bit per-sequence offsets
 ])
 def test_chunk_fwd_rejects(lib, kw, status):
     assert chunk(lib, **kw) == status

@@ -161,6 +161,62 @@ def test_chunk_workload4_full_size_sampled():
     check("workload 4 full size (2 sampled heads)", o, S, o_ref, S_ref, True)
 
 
+# ----------------------------------------------------------------------------- chunk_fwd, per-channel gate
+@pytest.mark.parametrize("T", [1, 37, 64, 65, 200])
+@pytest.mark.parametrize("dk,dv", [(128, 128), (128, 32), (64, 64)])
+@pytest.mark.parametrize("with_s0", [False, True])
+def test_chunk_kda_small(T, dk, dv, with_s0):
+    w = variant(3, d_k=dk, d_v=dv)
+    x = gdr_synth.make_inputs(w, B=2, H=2, T=T)
+    S0 = (np.random.default_rng(T).standard_normal((2, 2, dv, dk)) * 0.05).astype(np.float32) if with_s0 else None
+    o, S = run_chunk(x, True, S0)
+    o_ref, S_ref = oracle.recurrent_forward(x["q"], x["k"], x["v"], x["g"], x["beta"], S0)
+    check(f"chunk kda T={T} dk={dk} dv={dv} s0={with_s0}", o, S, o_ref, S_ref, True)
+
+
+@pytest.mark.parametrize("lo,hi", [(-3.0, -0.5), (-8.0, -0.01)])
+def test_chunk_kda_strong_decay(lo, hi):
+    """Per-channel log-decays far beyond the fp16 range of the in-block factors (the
+    diagonal tiles take the bf16 path); mixed with weak channels so both paths meet."""
+    w = variant(3, g_dist=("uniform", lo, hi))
+    x = gdr_synth.make_inputs(w, B=1, H=2, T=200)
+    x["g"][..., ::3] = x["g"][..., ::3] * 0.01  # every third channel decays slowly
+    o, S = run_chunk(x, True)
+    o_ref, S_ref = oracle.recurrent_forward(x["q"], x["k"], x["v"], x["g"], x["beta"])
+    check(f"chunk kda strong decay U({lo},{hi})", o, S, o_ref, S_ref, True)
+
+
+def test_chunk_kda_uniform_gate_matches_scalar_gate():
+    """P9 on the GPU: a per-channel gate equal across channels gives the scalar-gate result."""
+    x = gdr_synth.make_inputs(gdr_synth.WORKLOADS[2], B=1, H=2, T=300)
+    o1, S1 = run_chunk(x, True)
+    xc = dict(x)
+    xc["g"] = np.repeat(x["g"][..., None], x["q"].shape[-1], axis=-1).copy()
+    o2, S2 = run_chunk(xc, True)
+    o_ref, S_ref = oracle.recurrent_forward(x["q"], x["k"], x["v"], x["g"], x["beta"])
+    check("kda with a uniform gate", o2, S2, o_ref, S_ref, True)
+    check("scalar gate", o1, S1, o_ref, S_ref, True)
+
+
+def test_chunk_workload3_full_size_sampled():
+    """B=2, H=16, T=8192, d=128 bf16, per-channel gate; 2 of the 32 sequences checked."""
+    o, S, o_ref, S_ref = _sampled_full(3, 2, 3)
+    check("workload 3 full size (2 sampled heads)", o, S, o_ref, S_ref, True)
+
+
+def test_chunk_kda_carried_state_split():
+    w = variant(3, s0_std=0.02)
+    x = gdr_synth.make_inputs(w, B=1, H=2, T=300)
+    o_ref, S_ref = oracle.recurrent_forward(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"])
+    t0 = 140
+    a = {kk: (vv if kk == "S0" else vv[:, :, :t0]) for kk, vv in x.items()}
+    b = {kk: (None if kk == "S0" else vv[:, :, t0:]) for kk, vv in x.items()}
+    oa, Sa = run_chunk(a, True, x["S0"])
+    ob, Sb = gdr.chunk_fwd(dev(b["q"], True), dev(b["k"], True), dev(b["v"], True), dev(b["g"]), dev(b["beta"]), Sa)
+    torch.cuda.synchronize()
+    check(f"kda split at {t0}", torch.cat([oa, ob], dim=2), Sb, o_ref, S_ref, True)
+
+
 def test_chunk_deterministic():
     x = gdr_synth.make_inputs(gdr_synth.WORKLOADS[2], B=1, H=4, T=300)
     o1, S1 = run_chunk(x, True)
