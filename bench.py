@@ -249,6 +249,18 @@ def main():
             "ms_per_call": round(m4, 4), "tokens_per_s": round(w4.B * w4.T / (m4 * 1e-3), 1),
             "mfma_frac": round(chunk_flops(w4.B, w4.H, w4.T, 128, 128) / (m4 * 1e-3) / 1e12 / PEAK_MFMA_F16, 4)}
         del sets4
+        w3 = gdr_synth.WORKLOADS[3]
+        sets3 = make_chunk_sets(torch, gdr_synth, w3, nsets=2)
+        m3, _, _, _, _ = time_chunk(torch, gdr, sets3, 10, 2)
+        f3 = chunk_flops(w3.B, w3.H, w3.T, 128, 128)
+        b3 = chunk_bytes(w3.B, w3.H, w3.T, 128, 128, gate_per_channel=True)
+        result["kda"] = {
+            "workload": "per-channel gate B=2 H=16 T=8192 d=128 bf16, fp32 gate [B,H,T,128]",
+            "kernel": "chunk_kda_kernel<128>", "ms_per_call": round(m3, 4),
+            "tokens_per_s": round(w3.B * w3.T / (m3 * 1e-3), 1),
+            "mfma_frac": round(f3 / (m3 * 1e-3) / 1e12 / PEAK_MFMA_F16, 4),
+            "hbm_frac": round(b3 / (m3 * 1e-3) / 1e9 / PEAK_HBM, 4)}
+        del sets3
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(w, sets[0]["host"])
     print(json.dumps(result))

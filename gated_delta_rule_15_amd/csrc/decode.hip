@@ -26,7 +26,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(int dv, const IOT* __r
                                                           float* __restrict__ S, IOT* __restrict__ o) {
     constexpr int LPR = DK / 4;          // lanes per state row
     constexpr int RPI = kWave / LPR;     // rows per wave per instruction
-    constexpr int BATCH = 8;             // row-loads in flight per lane
+    constexpr int BATCH = 4;             // row-loads in flight per lane (8 waves per SIMD fit)
     const int64_t nh = blockIdx.x;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
