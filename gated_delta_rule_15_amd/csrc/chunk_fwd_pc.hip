@@ -19,9 +19,10 @@
 // An iteration has three phases separated by workgroup barriers:
 //   phase 0  consumers: chain of chunk i          producers: Gram tiles, diagonal inverses,
 //                                                            first block level of chunk i+1
-//   phase 1  consumers: -                         producers: second block level
-//   phase 2  consumers: stage K, Q, g, beta of    producers: write T of chunk i+1
-//            chunk i+2 and V of chunk i+1
+//   phase 1  wave 0: G scan of chunk i+2          producers: second block level, T of i+1
+//   phase 2  all waves: stage K, Q of chunk i+2 and V of chunk i+1
+// The global loads of chunk i+2 (and V of i+1) are issued in phase 0, interleaved with each
+// wave's main MFMA loop.
 // Every LDS buffer is written only in a phase where its previous contents are dead.
 //
 // MFMA 16x16x32 f16 conventions (l = lane, j = l & 15, g = l >> 4):
@@ -178,24 +179,28 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {
     // ---- staging (all 256 lanes): global -> registers -> LDS.  Past the sequence end the
     // buffer loads return zeros, i.e. identity tokens.
     const int pt = tid;
-    auto issue_kq = [&](int64_t c) {
-        const uint32_t t0 = (uint32_t)(c * C);
-#pragma unroll
-        for (int u = 0; u < KVL; ++u) {
-            const int idx = pt + 256 * u, row = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
-            const uint32_t off = ((t0 + row) * DK + col) * 2;
-            setu4(oKR + 4 * u, bld16(rk, off));
-            setu4(oQR + 4 * u, bld16(rq, off));
-        }
-        if (w == 0) {
-            cr[oGR] = __float_as_uint(bld4(rg, (t0 + l) * 4));
-            cr[oGR + 1] = __float_as_uint(bld4(rb, (t0 + l) * 4));
+    // Global loads of one iteration, in KVL parts: part u brings the lane's u-th 16-byte
+    // pieces of K and Q of chunk cs; part 0 also V of chunk cv and (wave 0) g, beta of cs.
+    // The parts are issued between the MFMAs of each wave's main product loop, so the
+    // vector-memory queue drains while the matrix pipe is busy.
+    auto issue_part = [&](int u, int64_t cs_, int64_t cv_) {
+        const uint32_t t0 = (uint32_t)(cs_ * C);
+        const int idx = pt + 256 * u, row = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
+        const uint32_t off = ((t0 + row) * DK + col) * 2;
+        setu4(oKR + 4 * u, bld16(rk, off));
+        setu4(oQR + 4 * u, bld16(rq, off));
+        if (u == 0) {
+            const uint32_t tv = (uint32_t)(cv_ * C);
+            setu4(oVR, bld16(rv, ((tv + (pt >> 2)) * DV + dv0 + (pt & 3) * 8) * 2));
+            if (w == 0) {
+                cr[oGR] = __float_as_uint(bld4(rg, (t0 + l) * 4));
+                cr[oGR + 1] = __float_as_uint(bld4(rb, (t0 + l) * 4));
+            }
         }
     };
-    auto issue_v = [&](int64_t c) {
-        const uint32_t t0 = (uint32_t)(c * C);
-        const int row = pt >> 2, col = (pt & 3) * 8;
-        setu4(oVR, bld16(rv, ((t0 + row) * DV + dv0 + col) * 2));
+    auto issue_all = [&](int64_t cs_, int64_t cv_) {
+#pragma unroll
+        for (int u = 0; u < KVL; ++u) issue_part(u, cs_, cv_);
     };
     auto stage_kq = [&](int64_t c) {
         const int buf = (int)(c & 1);
@@ -207,7 +212,7 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {
         }
     };
     // In-chunk cumulative log-decay G and the per-chunk factor table of chunk c (wave 0,
-    // from the g and beta values its issue_kq(c) loaded).
+    // from the g and beta values its issue_part(0, c, ..) loaded).
     auto scan = [&](int64_t c) {
         const int buf = (int)(c & 1);
         const float x = wave_inclusive_scan(__uint_as_float(cr[oGR]));
@@ -244,7 +249,7 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {
 
     lds_barrier();  // zero-fill done
     if (nC > 0) {
-        issue_kq(0);
+        issue_all(0, 0);
         stage_kq(0);
         if (w == 0) scan(0);
     }
@@ -257,7 +262,8 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {
     // applies the decay (factorised through the per-chunk table off the diagonal, exact on
     // it) and beta, and stores each tile column-major: a lane's 4 accumulator rows are
     // contiguous there.
-    auto gram_wave = [&](const _Float16* Kp, const _Float16* Qp, const float* sm, _Float16* Ap, const int P) {
+    auto gram_wave = [&](const _Float16* Kp, const _Float16* Qp, const float* sm, _Float16* Ap, const int P,
+                         int64_t cs_, int64_t cv_) {
         constexpr int NT = 10;
         const int tq[2][NT] = {{0, 0, 0, 0, 0, 0, 0, 1, 1, 1}, {0, 0, 0, 1, 1, 1, 1, 1, 1, 1}};
         const int ti_[2][NT] = {{0, 1, 1, 2, 2, 3, 3, 0, 1, 1}, {2, 3, 3, 2, 2, 2, 3, 3, 3, 3}};
@@ -311,6 +317,7 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {
                 const int ti = ti_[P][t], tj = tj_[P][t];
                 const half8 A = tq[P][t] ? cur[4 + (ti - 2 * P)] : cur[ti];
                 mma16(acc[t], A, cur[tj]);
+                if (t == 1) issue_part(kb, cs_, cv_);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -346,9 +353,8 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {
         // Unconditional: past the sequence end the buffer loads return zeros, and staging
         // those zeros touches only buffers no later chunk reads.  (Conditional issue/stage
         // pairs make the compiler wait for every outstanding load at the loop head.)
-        issue_kq(cs);
-        issue_v(cp);
         if (consumer) {
+            if (cc < 0) issue_all(cs, cp);
             if (cc >= 0) {
                 const _Float16* Kc = Kb(bc);
                 const _Float16* Qc = Qb(bc);
@@ -393,6 +399,7 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {
                     for (int ti = 0; ti < 4; ++ti) {
                         mma16(PK[ti], cur[ti], sb);
                         mma16(PQ[ti], cur[4 + ti], sb);
+                        if (ti == 0) issue_part(kb, cs, cp);
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
@@ -489,11 +496,12 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {
                 for (int kb = 0; kb < NKB; ++kb) seth8(oSB + 4 * kb, pack8(getf4(8 * kb), getf4(8 * kb + 4)));
             }
         } else {
+          if (cp >= nC) issue_all(cs, cp);
           if (cp < nC) {
             const _Float16* Kp = Kb(bp);
             const _Float16* Qp = Qb(bp);
-            if (p == 0) gram_wave(Kp, Qp, Sm(bp), At(bp), 0);
-            else gram_wave(Kp, Qp, Sm(bp), At(bp), 1);
+            if (p == 0) gram_wave(Kp, Qp, Sm(bp), At(bp), 0, cs, cp);
+            else gram_wave(Kp, Qp, Sm(bp), At(bp), 1, cs, cp);
             lds_fence();
             // diagonal 16x16 blocks 2p, 2p+1 of X = N^{-1}, column-oriented forward
             // substitution: lane (block, jc) builds column jc; after x[i] is final it is
@@ -587,11 +595,7 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {
                 for (int r = 0; r < 4; ++r) xc[r] = -xc[r];
                 setf4(oXC + 4 * ti, xc);
             }
-        }
-        lds_barrier();
-
-        // ======================= phase 2 =======================
-        if (!consumer && cp < nC) {
+            // The consumer read T^T of its chunk in phase 0; T of chunk cp replaces it now.
             // T = X diag(beta), stored column-major: T^T[m][l] = X^T[m][l] beta_m
             const float* sm = Sm(bp);
             if (l < 32) {
@@ -624,6 +628,9 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {
                 }
             }
         }
+        lds_barrier();
+
+        // ======================= phase 2 =======================
         stage_kq(cs);
         stage_v();
         lds_barrier();
