@@ -50,6 +50,17 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// 8 bf16 (one uint4, element order preserved) -> 8 fp16.
+__device__ __forceinline__ half8 bf16x8_to_half8(const uint4& u) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    half8 h;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        h[2 * e] = (_Float16)__uint_as_float(w[e] << 16);
+        h[2 * e + 1] = (_Float16)__uint_as_float(w[e] & 0xffff0000u);
+    }
+    return h;
+}
 // 8 bf16 (one uint4) -> 8 fp16 written as two 4-element groups at permuted positions.
 __device__ __forceinline__ void stage8(_Float16* row, int m0, const uint4& u) {
     const uint32_t w[4] = {u.x, u.y, u.z, u.w};

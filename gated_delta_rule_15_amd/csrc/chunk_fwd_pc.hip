@@ -13,14 +13,13 @@
 // runs the two concurrently inside one workgroup of four waves:
 //   * waves 0-1 (consumers) carry the state of 16 value channels each, run the whole
 //     S-dependent chain of chunk i, and stage the inputs of later chunks into LDS;
-//   * waves 2-3 (producers) form N, T and A of chunk i+1: the Gram tiles, the four 16x16
-//     diagonal blocks of N^{-1} by forward substitution in fp32, and the two block levels of
-//     the inverse on MFMA.
-// An iteration has three phases separated by workgroup barriers:
-//   phase 0  consumers: chain of chunk i          producers: Gram tiles, diagonal inverses,
-//                                                            first block level of chunk i+1
-//   phase 1  wave 0: G scan of chunk i+2          producers: second block level, T of i+1
-//   phase 2  all waves: stage K, Q of chunk i+2 and V of chunk i+1
+//   * waves 2-3 (producers) form, for chunk i+1, A, the blocks of N below the diagonal and
+//     the inverses of its four 16x16 diagonal blocks (forward substitution in fp32); the
+//     consumer then applies N^{-1} diag(beta) by blocked forward substitution on MFMA.
+// An iteration has two phases separated by workgroup barriers:
+//   phase 0  consumers: chain of chunk i;         producers: Gram tiles and diagonal
+//            G scan of chunk i+2 (wave 0)                    inverses of chunk i+1
+//   phase 1  consumers: write o of chunk i; all waves: stage K, Q of chunk i+2 and V of i+1
 // The global loads of chunk i+2 (and V of i+1) are issued in phase 0, interleaved with each
 // wave's main MFMA loop.
 // Every LDS buffer is written only in a phase where its previous contents are dead.
@@ -29,13 +28,15 @@
 //   accumulator register r of lane l holds element (row 4g + r, column j);
 //   an operand fragment of lane l is row/column j with the 8 reduction indices
 //   {32kb + 4g + r} U {32kb + 16 + 4g + r}, r = 0..3.
-// Every matrix used as an operand from LDS stores its reduction index permuted within each
-// 32-block (index 16h + 4gg + rr at position 8gg + 4h + rr), so a fragment is ONE 16-byte
-// read, and the accumulator of two vertically adjacent 16-row tiles IS the operand fragment
-// of the matrix whose rows are the reduction index: S^T, R and Z move between products in
-// registers only.  K^T fragments (reduction over tokens) come from the token-major K copy
+// K and Q sit in LDS in natural channel order, so a fragment of 8 consecutive channels is
+// ONE 16-byte read.  The state S^T is kept with its row index permuted within each 32-block
+// (row 16h + 4gg + rr holds channel 8gg + 4h + rr, pperm below): then the accumulator of two
+// vertically adjacent 16-row tiles of S^T IS the B fragment that pairs with those 8
+// consecutive channels, and S^T, R and Z move between products in registers only.  K^T
+// fragments (reduction over tokens) for the state update come from the token-major K copy
 // through ds_read_b64_tr_b16, which hands lane i of each 16-lane group element (i & 3) of
-// the 4-element rows addressed by lanes (i >> 2) + 4e, e = 0..3.
+// the 4-element rows addressed by lanes (i >> 2) + 4e, e = 0..3; reading channel columns
+// pperm(16t + 4(i & 3)) gives S^T's permuted row order.
 #include "chunk_common.h"
 
 namespace gdr {
@@ -57,7 +58,10 @@ struct PcArgs {
 template <int DK>
 struct PcLds {
     static constexpr int C = kChunk;
-    static constexpr int LDK = DK + 8;   // halfs, rows of K / Q
+    // halfs, rows of K / Q: a stride of 16 mod 128 halfs keeps both the 16-byte fragment
+    // reads (row j, 8 channels at 8g) and the transposing reads (rows 4g + j/4) free of
+    // LDS bank conflicts on gfx950
+    static constexpr int LDK = DK + 16;
     static constexpr int LDC = C + 8;    // halfs, rows of C-wide fp16 matrices
     static constexpr int LDV = C + 4;    // floats, rows of V^T
     static constexpr int LDN = 16 + 4;   // floats, rows of a 16x16 fp32 block
@@ -78,17 +82,19 @@ struct PcLds {
     static constexpr int oQb1 = oQb0 + szK;
     static constexpr int oAt0 = oQb1 + szK;   // A^T (column-major A), two chunks
     static constexpr int oAt1 = oAt0 + szC;
-    static constexpr int oSm0 = oAt1 + szC;
-    static constexpr int oSm1 = oSm0 + NSM * 4;
-    static constexpr int oVt = oSm1 + NSM * 4;
-    static constexpr int oTt = oVt + 32 * LDV * 4;  // T^T
-    static constexpr int oNt = oTt + szC;           // off-diagonal blocks of N^T (fp16)
-    static constexpr int oXt = oNt + szC;           // X^T, X = N^{-1} (fp16)
-    static constexpr int oNd = oXt + szC;           // diagonal blocks of N^T (fp32)
+    static constexpr int oSm = oAt1 + szC;            // factor tables of three chunks
+    static constexpr int LDX = 16 + 8;   // halfs, rows of a 16x16 fp16 block
+    static constexpr int szX = 4 * 16 * LDX * 2;
+    static constexpr int oVt = oSm + 3 * NSM * 4;
+    static constexpr int oNt0 = oVt + 32 * LDV * 4;  // off-diagonal blocks of N^T (fp16), two chunks
+    static constexpr int oNt1 = oNt0 + szC;
+    static constexpr int oXd0 = oNt1 + szC;          // X_bb^T, the diagonal blocks of N^{-1} (fp16), two chunks
+    static constexpr int oXd1 = oXd0 + szX;
+    static constexpr int oNd = oXd1 + szX;           // diagonal blocks of N^T (fp32)
     static constexpr int oOt = oNd + 4 * 16 * LDN * 4;  // O^T of the consumer chunk (bf16)
     static constexpr int total = oOt + 32 * LDO * 2;
     static_assert(total <= 160 * 1024, "LDS budget of one gfx950 CU exceeded");
-    static_assert((oAt0 | oAt1 | oSm0 | oSm1 | oVt | oTt | oNt | oXt | oNd | oOt) % 16 == 0, "alignment");
+    static_assert((oAt0 | oAt1 | oSm | oVt | oNt0 | oNt1 | oXd0 | oXd1 | oNd | oOt) % 16 == 0, "alignment");
 };
 
 template <int DK>
@@ -102,11 +108,12 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {
     auto Kb = [&](int b) { return reinterpret_cast<_Float16*>(smem + (b ? L::oKb1 : L::oKb0)); };
     auto Qb = [&](int b) { return reinterpret_cast<_Float16*>(smem + (b ? L::oQb1 : L::oQb0)); };
     auto At = [&](int b) { return reinterpret_cast<_Float16*>(smem + (b ? L::oAt1 : L::oAt0)); };
-    auto Sm = [&](int b) { return reinterpret_cast<float*>(smem + (b ? L::oSm1 : L::oSm0)); };
+    // factor table of chunk c: buffer c mod 3, so the scan of chunk c+2 never meets the
+    // tables that the consumer (chunk c) and the producers (chunk c+1) are reading
+    auto Sm = [&](int64_t c) { return reinterpret_cast<float*>(smem + L::oSm + (int)(c % 3) * L::NSM * 4); };
     float* Vt = reinterpret_cast<float*>(smem + L::oVt);
-    _Float16* Tt = reinterpret_cast<_Float16*>(smem + L::oTt);
-    _Float16* Nt = reinterpret_cast<_Float16*>(smem + L::oNt);
-    _Float16* Xt = reinterpret_cast<_Float16*>(smem + L::oXt);
+    auto Ntb = [&](int b) { return reinterpret_cast<_Float16*>(smem + (b ? L::oNt1 : L::oNt0)); };
+    auto Xdb = [&](int b) { return reinterpret_cast<_Float16*>(smem + (b ? L::oXd1 : L::oXd0)); };
     float* Nd = reinterpret_cast<float*>(smem + L::oNd);
     _Float16* Ot = reinterpret_cast<_Float16*>(smem + L::oOt);  // holds bf16 bit patterns
 
@@ -127,6 +134,10 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {
     const int dvc = dv0 + 16 * w;  // consumer's first value channel
     const int64_t nC = (T + C - 1) / C;
 
+    // 16-deep product: lane (j, g) gives A[j][4g..4g+3] and B[4g..4g+3][j]
+    auto mma16k16 = [](float4v& acc, const half4& a4, const half4& b4) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x16f16(a4, b4, acc, 0, 0, 0);
+    };
     // operand fragment (rows 16*rt.., 8 reduction indices of block kb) of a row-major matrix
     // whose reduction index runs along a column-major copy: transposing reads of the
     // column-major matrix M^T at rows 32kb + 4g + (j >> 2) (+16) and columns col0 + 4(j & 3).
@@ -143,11 +154,9 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {
     // the two roles share one array: consumers keep the state S^T (fp32 accumulators) and
     // its fp16 operand copy; producers keep blocks of N^{-1}.
     //   consumer: [0, 4*NST) S^T tiles   [4*NST, 4*NST + 4*NKB) fp16 copy of S^T
-    //   producer: [0,16) diagonal-block column of N^{-1}  [16,20) first level  [20,28) second
     //   every wave: [oKR, NCARRY) its share of the prefetched K, Q, V, g, beta
     constexpr int oSB = 4 * NST;
-    constexpr int oXD = 0, oX2 = 16, oXC = 20;
-    constexpr int oKR = (oSB + 4 * NKB) > 28 ? (oSB + 4 * NKB) : 28;
+    constexpr int oKR = oSB + 4 * NKB;
     constexpr int oQR = oKR + 4 * KVL, oVR = oQR + 4 * KVL, oGR = oVR + 4;
     constexpr int NCARRY = oGR + 2;
     uint32_t cr[NCARRY];
@@ -170,7 +179,7 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {
         if (a.S0 != nullptr) {
             const float* s0 = a.S0 + bh * (int64_t)DV * DK + (int64_t)(dvc + j) * DK;
 #pragma unroll
-            for (int t = 0; t < NST; ++t) setf4(4 * t, ld4f(s0 + 16 * t + 4 * g));
+            for (int t = 0; t < NST; ++t) setf4(4 * t, ld4f(s0 + pperm(16 * t + 4 * g)));
         }
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) seth8(oSB + 4 * kb, pack8(getf4(8 * kb), getf4(8 * kb + 4)));
@@ -207,14 +216,13 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {
 #pragma unroll
         for (int u = 0; u < KVL; ++u) {
             const int idx = pt + 256 * u, row = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
-            stage8(Kb(buf) + row * L::LDK, col, getu4(oKR + 4 * u));
-            stage8(Qb(buf) + row * L::LDK, col, getu4(oQR + 4 * u));
+            *reinterpret_cast<half8*>(Kb(buf) + row * L::LDK + col) = bf16x8_to_half8(getu4(oKR + 4 * u));
+            *reinterpret_cast<half8*>(Qb(buf) + row * L::LDK + col) = bf16x8_to_half8(getu4(oQR + 4 * u));
         }
     };
     // In-chunk cumulative log-decay G and the per-chunk factor table of chunk c (wave 0,
     // from the g and beta values its issue_part(0, c, ..) loaded).
     auto scan = [&](int64_t c) {
-        const int buf = (int)(c & 1);
         const float x = wave_inclusive_scan(__uint_as_float(cr[oGR]));
         const float GC = lane_value(x, 63);
         float ge[4];
@@ -222,7 +230,7 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {
         for (int b = 0; b < 4; ++b) ge[b] = lane_value(x, 16 * b + 15);
         const int blk = l >> 4;
         const float beta = __uint_as_float(cr[oGR + 1]);
-        float* sm = Sm(buf);
+        float* sm = Sm(c);
         sm[L::SG + l] = x;
         sm[L::SEG + l] = fast_exp(x);
         sm[L::SEGR + l] = fast_exp(GC - x);
@@ -262,8 +270,8 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {
     // applies the decay (factorised through the per-chunk table off the diagonal, exact on
     // it) and beta, and stores each tile column-major: a lane's 4 accumulator rows are
     // contiguous there.
-    auto gram_wave = [&](const _Float16* Kp, const _Float16* Qp, const float* sm, _Float16* Ap, const int P,
-                         int64_t cs_, int64_t cv_) {
+    auto gram_wave = [&](const _Float16* Kp, const _Float16* Qp, const float* sm, _Float16* Ap, _Float16* Np,
+                         const int P, int64_t cs_, int64_t cv_) {
         constexpr int NT = 10;
         const int tq[2][NT] = {{0, 0, 0, 0, 0, 0, 0, 1, 1, 1}, {0, 0, 0, 1, 1, 1, 1, 1, 1, 1}};
         const int ti_[2][NT] = {{0, 1, 1, 2, 2, 3, 3, 0, 1, 1}, {2, 3, 3, 2, 2, 2, 3, 3, 3, 3}};
@@ -337,7 +345,7 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {
                     if (m == l0 + r) v[r] = 1.0f;
                 *reinterpret_cast<float4v*>(Nd + (ti * 16 + j) * L::LDN + 4 * g) = float4v{v[0], v[1], v[2], v[3]};
             } else {
-                _Float16* dst = (isQ ? Ap : Nt) + m * L::LDC + l0;
+                _Float16* dst = (isQ ? Ap : Np) + m * L::LDC + l0;
                 *reinterpret_cast<half4*>(dst) = half4{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
             }
         }
@@ -345,21 +353,22 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {
 
     for (int64_t it = -1; it < nC; ++it) {
         const int64_t cc = it;        // consumer chunk
-        const int64_t cp = it + 1;    // producer chunk (N, T, A)
-        const int64_t cs = it + 2;    // chunk whose K, Q are staged in phase 2
+        const int64_t cp = it + 1;    // producer chunk (N blocks, diagonal inverses, A)
+        const int64_t cs = it + 2;    // chunk whose K, Q are staged in phase 1
         const int bc = (int)(cc & 1), bp = (int)(cp & 1);
 
         // ======================= phase 0 =======================
-        // Unconditional: past the sequence end the buffer loads return zeros, and staging
-        // those zeros touches only buffers no later chunk reads.  (Conditional issue/stage
-        // pairs make the compiler wait for every outstanding load at the loop head.)
+        // Loads are unconditional: past the sequence end the buffer loads return zeros, and
+        // staging those zeros touches only buffers no later chunk reads.
         if (consumer) {
             if (cc < 0) issue_all(cs, cp);
             if (cc >= 0) {
                 const _Float16* Kc = Kb(bc);
                 const _Float16* Qc = Qb(bc);
                 const _Float16* Ac = At(bc);
-                const float* sm = Sm(bc);
+                const _Float16* Nc = Ntb(bc);
+                const _Float16* Xc = Xdb(bc);
+                const float* sm = Sm(cc);
                 // The LDS operand fragments of each group of MFMAs are issued one group ahead
                 // (double-buffered registers), and sched_barrier pins that order: left alone,
                 // the scheduler serialises every ds_read with the MFMA that consumes it.
@@ -375,11 +384,12 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {
                     fa[ti] = kfrag(ti, 0);
                     fa[4 + ti] = qfrag(ti, 0);
                 }
-                float4v eg[4], vv[4];
+                float4v eg[4], vv[4], bt[4];
 #pragma unroll
                 for (int ti = 0; ti < 4; ++ti) {
                     eg[ti] = ld4f(sm + L::SEG + 16 * ti + 4 * g);
                     vv[ti] = ld4f(Vt + (16 * w + j) * L::LDV + 16 * ti + 4 * g);
+                    bt[ti] = ld4f(sm + L::SB + 16 * ti + 4 * g);
                 }
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -403,41 +413,61 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
-                // operands of the next products: rows of T and A (lower triangular, 6
-                // fragments each, from their column-major copies), e^{G_C - G}
-                half8 tf[6], af[6];
-                float4v er[4];
+                // operands of the block substitution: X_bb (diagonal inverses) and the N blocks
+                // below the diagonal, as A fragments from their column-major copies; rows of A
+                half4 xf[4];
+#pragma unroll
+                for (int b = 0; b < 4; ++b) xf[b] = ldtr(Xc + (16 * b + 4 * g + (j >> 2)) * L::LDX + 4 * (j & 3));
+                const half4 n10 = ldtr(Nc + (4 * g + (j >> 2)) * L::LDC + 16 + 4 * (j & 3));
+                const half8 n2x = trfrag(Nc, L::LDC, 0, 32 + 4 * (j & 3));   // [N20 N21]
+                const half8 n3x = trfrag(Nc, L::LDC, 0, 48 + 4 * (j & 3));   // [N30 N31]
+                const half4 n32 = ldtr(Nc + (32 + 4 * g + (j >> 2)) * L::LDC + 48 + 4 * (j & 3));
+                half8 af[6];
 #pragma unroll
                 for (int ti = 0, n = 0; ti < 4; ++ti) {
 #pragma unroll
-                    for (int kb = 0; kb <= (ti >> 1); ++kb, ++n) {
-                        tf[n] = trfrag(Tt, L::LDC, kb, 16 * ti + 4 * (j & 3));
-                        af[n] = trfrag(Ac, L::LDC, kb, 16 * ti + 4 * (j & 3));
-                    }
+                    for (int kb = 0; kb <= (ti >> 1); ++kb, ++n) af[n] = trfrag(Ac, L::LDC, kb, 16 * ti + 4 * (j & 3));
                 }
+                float4v er[4];
 #pragma unroll
                 for (int ti = 0; ti < 4; ++ti) er[ti] = ld4f(sm + L::SEGR + 16 * ti + 4 * g);
                 const float eGC = sm[L::SEGC];
                 __builtin_amdgcn_sched_barrier(0);
-                // R = V - e^G P_K ;  O_hist = e^G P_Q
-                float4v Rr[4], Oh[4];
+                // R' = diag(beta) (V - e^G P_K) ;  O_hist = e^G P_Q
+                float4v Rb[4], Oh[4];
 #pragma unroll
                 for (int ti = 0; ti < 4; ++ti) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        Rr[ti][r] = vv[ti][r] - eg[ti][r] * PK[ti][r];
+                        Rb[ti][r] = bt[ti][r] * (vv[ti][r] - eg[ti][r] * PK[ti][r]);
                         Oh[ti][r] = eg[ti][r] * PQ[ti][r];
                     }
                 }
-                // Z = T R  (T lower triangular)
-                const half8 rB[2] = {pack8(Rr[0], Rr[1]), pack8(Rr[2], Rr[3])};
-                float4v Zz[4];
+                // Z = N^{-1} R' by blocked forward substitution over the 16-token blocks:
+                //   Z_b = X_bb (R'_b - sum_{b' < b} N_{b b'} Z_{b'})
+                auto h4 = [](const float4v& x) { return half4{(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3]}; };
+                auto sub4 = [](float4v a4, const float4v& b4) {
 #pragma unroll
-                for (int ti = 0, n = 0; ti < 4; ++ti) {
-                    Zz[ti] = zero4();
-#pragma unroll
-                    for (int kb = 0; kb <= (ti >> 1); ++kb, ++n) mma16(Zz[ti], tf[n], rB[kb]);
-                }
+                    for (int r = 0; r < 4; ++r) a4[r] -= b4[r];
+                    return a4;
+                };
+                float4v Zz[4], y;
+                Zz[0] = zero4();
+                mma16k16(Zz[0], xf[0], h4(Rb[0]));
+                y = zero4();
+                mma16k16(y, n10, h4(Zz[0]));
+                Zz[1] = zero4();
+                mma16k16(Zz[1], xf[1], h4(sub4(Rb[1], y)));
+                const half8 z01 = pack8(Zz[0], Zz[1]);
+                y = zero4();
+                mma16(y, n2x, z01);
+                Zz[2] = zero4();
+                mma16k16(Zz[2], xf[2], h4(sub4(Rb[2], y)));
+                y = zero4();
+                mma16(y, n3x, z01);
+                mma16k16(y, n32, h4(Zz[2]));
+                Zz[3] = zero4();
+                mma16k16(Zz[3], xf[3], h4(sub4(Rb[3], y)));
                 // A operand of the state update: K^T[16t + i][tokens] from the token-major K
                 // copy (d_k permuted).  First half of the tiles now.
                 auto ktfrag = [&](int t, int kb) { return trfrag(Kc, L::LDK, kb, pperm(16 * t + 4 * (j & 3))); };
@@ -448,10 +478,9 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {
                     kt1[t] = ktfrag(t, 1);
                 }
                 __builtin_amdgcn_sched_barrier(0);
-                // O = O_hist + A Z, rounded to bf16 into this wave's rows of O^T; read back
-                // transposed (a lane gets 8 consecutive channels of one token) for 16-byte
-                // stores of o.
-                const half8 zB[2] = {pack8(Zz[0], Zz[1]), pack8(Zz[2], Zz[3])};
+                // O = O_hist + A Z, rounded to bf16 into this wave's rows of O^T (written to
+                // o in phase 1).
+                const half8 zB[2] = {z01, pack8(Zz[2], Zz[3])};
 #pragma unroll
                 for (int ti = 0, n = 0; ti < 4; ++ti) {
                     float4v acc = Oh[ti];
@@ -459,15 +488,6 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {
                     for (int kb = 0; kb <= (ti >> 1); ++kb, ++n) mma16(acc, af[n], zB[kb]);
                     *reinterpret_cast<uint2*>(Ot + (16 * w + j) * L::LDO + 16 * ti + 4 * g) =
                         uint2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
-                }
-                lds_fence();
-#pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2) {
-                    const int tb = 32 * s2 + 16 * (g >> 1), d = 16 * w + 8 * (g & 1);
-                    const _Float16* rp = Ot + (d + (j >> 2)) * L::LDO + tb + 4 * (j & 3);
-                    const uint2 lo = __builtin_bit_cast(uint2, ldtr(rp));
-                    const uint2 hi = __builtin_bit_cast(uint2, ldtr(rp + 4 * L::LDO));
-                    bst16(ro, ((uint32_t)(cc * C + tb + j) * DV + dv0 + d) * 2, uint4{lo.x, lo.y, hi.x, hi.y});
                 }
                 // S^T <- e^{G_C} S^T + K^T diag(e^{G_C - G}) Z
                 float4v zs[4];
@@ -495,18 +515,19 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb) seth8(oSB + 4 * kb, pack8(getf4(8 * kb), getf4(8 * kb + 4)));
             }
+            if (w == 0) scan(cs);
         } else {
           if (cp >= nC) issue_all(cs, cp);
           if (cp < nC) {
             const _Float16* Kp = Kb(bp);
             const _Float16* Qp = Qb(bp);
-            if (p == 0) gram_wave(Kp, Qp, Sm(bp), At(bp), 0, cs, cp);
-            else gram_wave(Kp, Qp, Sm(bp), At(bp), 1, cs, cp);
+            if (p == 0) gram_wave(Kp, Qp, Sm(cp), At(bp), Ntb(bp), 0, cs, cp);
+            else gram_wave(Kp, Qp, Sm(cp), At(bp), Ntb(bp), 1, cs, cp);
             lds_fence();
             // diagonal 16x16 blocks 2p, 2p+1 of X = N^{-1}, column-oriented forward
             // substitution: lane (block, jc) builds column jc; after x[i] is final it is
             // eliminated from the later rows, x[t] -= N[t][i] x[i] for t > i (column i of N
-            // is row i of the stored N^T block).
+            // is row i of the stored N^T block).  Stored as X_bb^T (row jc = column jc of X_bb).
             {
                 const int b = 2 * p + ((l >> 4) & 1), jc = j;
                 const float* nb = Nd + b * 16 * L::LDN;
@@ -529,7 +550,6 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {
                             if (4 * q4 + e > i) xd[4 * q4 + e] -= nr[i][q4][e] * xd[i];
                     }
                 }
-                // X^T row 16b + jc (= column jc of the block), natural order
                 if (l < 32) {
                     half8 h0, h1;
 #pragma unroll
@@ -537,100 +557,29 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {
                         h0[t] = (_Float16)xd[t];
                         h1[t] = (_Float16)xd[8 + t];
                     }
-                    *reinterpret_cast<half8*>(Xt + (16 * b + jc) * L::LDC + 16 * b) = h0;
-                    *reinterpret_cast<half8*>(Xt + (16 * b + jc) * L::LDC + 16 * b + 8) = h1;
+                    _Float16* xr = Xdb(bp) + (16 * b + jc) * L::LDX;
+                    *reinterpret_cast<half8*>(xr) = h0;
+                    *reinterpret_cast<half8*>(xr + 8) = h1;
                 }
-#pragma unroll
-                for (int t = 0; t < 16; ++t) cr[oXD + t] = __float_as_uint(xd[t]);
-            }
-            lds_fence();
-            // first level: X[b1][b0] = -X[b1][b1] N[b1][b0] X[b0][b0], b0 = 2p, b1 = 2p + 1.
-            // 16-deep reductions: fragment elements 0-3 carry k = 4g + r, elements 4-7 zero.
-            {
-                const int b0 = 2 * p, b1 = 2 * p + 1;
-                const half4 z4 = {(_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f};
-                // A: N[16b1 + i][16b0 + 4g + e] from N^T rows 16b0 + 4g + e
-                const half8 fa = cat8(ldtr(Nt + (16 * b0 + 4 * g + (j >> 2)) * L::LDC + 16 * b1 + 4 * (j & 3)), z4);
-                // B: X[16b0 + 4g + r][16b0 + j] = X^T[16b0 + j][16b0 + 4g + r]
-                const half8 fb = cat8(*reinterpret_cast<const half4*>(Xt + (16 * b0 + j) * L::LDC + 16 * b0 + 4 * g), z4);
-                float4v y = zero4();
-                mma16(y, fa, fb);
-                // A: X[16b1 + i][16b1 + 4g + e] = X^T[16b1 + 4g + e][16b1 + i];  B: y
-                const half8 fx = cat8(ldtr(Xt + (16 * b1 + 4 * g + (j >> 2)) * L::LDC + 16 * b1 + 4 * (j & 3)), z4);
-                const half8 fy = cat8(half4{(_Float16)y[0], (_Float16)y[1], (_Float16)y[2], (_Float16)y[3]}, z4);
-                float4v x2 = zero4();
-                mma16(x2, fx, fy);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) x2[r] = -x2[r];
-                // X^T row 16b0 + j, columns 16b1 + 4g .. +3
-                *reinterpret_cast<half4*>(Xt + (16 * b0 + j) * L::LDC + 16 * b1 + 4 * g) =
-                    half4{(_Float16)x2[0], (_Float16)x2[1], (_Float16)x2[2], (_Float16)x2[3]};
-                setf4(oX2, x2);
             }
           }
         }
         lds_barrier();
 
         // ======================= phase 1 =======================
-        // The consumer is done with Sm(cs & 1) = Sm(cc & 1); wave 0 fills it for chunk cs.
-        if (w == 0) scan(cs);
-        if (!consumer && cp < nC) {
-            // second level: X[32:64][16p:16p+16] = -X[32:64][32:64] (N[32:64][0:32] X[0:32][16p:16p+16])
-            const int n = 16 * p + j;
-            // B: X[m][n] for m in {4g + r, 16 + 4g + r} = X^T[n][...]
-            const half8 fxa = cat8(*reinterpret_cast<const half4*>(Xt + n * L::LDC + 4 * g),
-                                   *reinterpret_cast<const half4*>(Xt + n * L::LDC + 16 + 4 * g));
-            float4v y3[2];
+        // o of chunk cc: each consumer wave reads its rows of O^T back transposed (a lane gets
+        // 8 consecutive channels of one token) and writes them with 16-byte stores.
+        if (consumer && cc >= 0) {
 #pragma unroll
-            for (int ti = 0; ti < 2; ++ti) {
-                y3[ti] = zero4();
-                mma16(y3[ti], trfrag(Nt, L::LDC, 0, 32 + 16 * ti + 4 * (j & 3)), fxa);
-            }
-            const half8 fy = pack8(y3[0], y3[1]);
-#pragma unroll
-            for (int ti = 0; ti < 2; ++ti) {
-                float4v xc = zero4();
-                mma16(xc, trfrag(Xt, L::LDC, 1, 32 + 16 * ti + 4 * (j & 3)), fy);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) xc[r] = -xc[r];
-                setf4(oXC + 4 * ti, xc);
-            }
-            // The consumer read T^T of its chunk in phase 0; T of chunk cp replaces it now.
-            // T = X diag(beta), stored column-major: T^T[m][l] = X^T[m][l] beta_m
-            const float* sm = Sm(bp);
-            if (l < 32) {
-                const int b = 2 * p + (l >> 4), m = 16 * b + j;
-                const float bm = sm[L::SB + m];
-                half8 h0, h1;
-#pragma unroll
-                for (int t = 0; t < 8; ++t) {
-                    h0[t] = (_Float16)(__uint_as_float(cr[oXD + t]) * bm);
-                    h1[t] = (_Float16)(__uint_as_float(cr[oXD + 8 + t]) * bm);
-                }
-                *reinterpret_cast<half8*>(Tt + m * L::LDC + 16 * b) = h0;
-                *reinterpret_cast<half8*>(Tt + m * L::LDC + 16 * b + 8) = h1;
-            }
-            {
-                const int m = 32 * p + j;  // block column 2p; rows 32p + 16 + 4g ..
-                const float bm = sm[L::SB + m];
-                const float4v x2 = getf4(oX2);
-                *reinterpret_cast<half4*>(Tt + m * L::LDC + 32 * p + 16 + 4 * g) =
-                    half4{(_Float16)(x2[0] * bm), (_Float16)(x2[1] * bm), (_Float16)(x2[2] * bm), (_Float16)(x2[3] * bm)};
-            }
-            {
-                const int m = 16 * p + j;
-                const float bm = sm[L::SB + m];
-#pragma unroll
-                for (int ti = 0; ti < 2; ++ti) {
-                    const float4v xc = getf4(oXC + 4 * ti);
-                    *reinterpret_cast<half4*>(Tt + m * L::LDC + 32 + 16 * ti + 4 * g) =
-                        half4{(_Float16)(xc[0] * bm), (_Float16)(xc[1] * bm), (_Float16)(xc[2] * bm), (_Float16)(xc[3] * bm)};
-                }
+            for (int s2 = 0; s2 < 2; ++s2) {
+                const int tb = 32 * s2 + 16 * (g >> 1), d = 16 * w + 8 * (g & 1);
+                const _Float16* rp = Ot + (d + (j >> 2)) * L::LDO + tb + 4 * (j & 3);
+                const uint2 lo = __builtin_bit_cast(uint2, ldtr(rp));
+                const uint2 hi = __builtin_bit_cast(uint2, ldtr(rp + 4 * L::LDO));
+                bst16(ro, ((uint32_t)(cc * C + tb + j) * DV + dv0 + d) * 2, uint4{lo.x, lo.y, hi.x, hi.y});
             }
         }
-        lds_barrier();
-
-        // ======================= phase 2 =======================
+        // The consumer is done with K, Q of chunk cc (= cs mod 2) and with V of cc.
         stage_kq(cs);
         stage_v();
         lds_barrier();
@@ -639,7 +588,7 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {
     if (consumer && a.Sf != nullptr) {
         float* sf = a.Sf + bh * (int64_t)DV * DK + (int64_t)(dvc + j) * DK;
 #pragma unroll
-        for (int t = 0; t < NST; ++t) *reinterpret_cast<float4v*>(sf + 16 * t + 4 * g) = getf4(4 * t);
+        for (int t = 0; t < NST; ++t) *reinterpret_cast<float4v*>(sf + pperm(16 * t + 4 * g)) = getf4(4 * t);
     }
 }
 
