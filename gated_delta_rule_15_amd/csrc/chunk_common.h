@@ -118,8 +118,9 @@ __device__ __forceinline__ void bst16(__amdgpu_buffer_rsrc_t r, uint32_t off, co
     __builtin_amdgcn_raw_buffer_store_b128(u32x4{u.x, u.y, u.z, u.w}, r, off, 0, 0);
 }
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return (uint32_t)__builtin_bit_cast(unsigned short, (__bf16)lo) |
-           ((uint32_t)__builtin_bit_cast(unsigned short, (__bf16)hi) << 16);
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    typedef float float2v __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{lo, hi}, bf16x2));  // one RNE cvt_pk
 }
 
 }  // namespace gdr

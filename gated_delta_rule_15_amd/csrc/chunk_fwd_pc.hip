@@ -63,7 +63,8 @@ struct PcLds {
     // LDS bank conflicts on gfx950
     static constexpr int LDK = DK + 16;
     static constexpr int LDC = C + 8;    // halfs, rows of C-wide fp16 matrices
-    static constexpr int LDV = C + 4;    // floats, rows of V^T
+    static constexpr int LDV = 80;       // bf16, rows (tokens) of the 32-channel V tile; a
+                                         // transposing-read-friendly stride
     static constexpr int LDN = 16 + 4;   // floats, rows of a 16x16 fp32 block
     static constexpr int LDO = C + 8;    // bf16, rows of the output tile O^T
     // per-chunk factor table (floats):
@@ -86,7 +87,7 @@ struct PcLds {
     static constexpr int LDX = 16 + 8;   // halfs, rows of a 16x16 fp16 block
     static constexpr int szX = 4 * 16 * LDX * 2;
     static constexpr int oVt = oSm + 3 * NSM * 4;
-    static constexpr int oNt0 = oVt + 32 * LDV * 4;  // off-diagonal blocks of N^T (fp16), two chunks
+    static constexpr int oNt0 = oVt + C * LDV * 2;   // off-diagonal blocks of N^T (fp16), two chunks
     static constexpr int oNt1 = oNt0 + szC;
     static constexpr int oXd0 = oNt1 + szC;          // X_bb^T, the diagonal blocks of N^{-1} (fp16), two chunks
     static constexpr int oXd1 = oXd0 + szX;
@@ -110,8 +111,9 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {
     auto At = [&](int b) { return reinterpret_cast<_Float16*>(smem + (b ? L::oAt1 : L::oAt0)); };
     // factor table of chunk c: buffer c mod 3, so the scan of chunk c+2 never meets the
     // tables that the consumer (chunk c) and the producers (chunk c+1) are reading
-    auto Sm = [&](int64_t c) { return reinterpret_cast<float*>(smem + L::oSm + (int)(c % 3) * L::NSM * 4); };
-    float* Vt = reinterpret_cast<float*>(smem + L::oVt);
+    // (the buffer index is passed in, kept by rotation: no 64-bit division in the loop)
+    auto Sm = [&](int m3) { return reinterpret_cast<float*>(smem + L::oSm + m3 * L::NSM * 4); };
+    uint16_t* Vt = reinterpret_cast<uint16_t*>(smem + L::oVt);  // V tile, bf16 [token][channel]
     auto Ntb = [&](int b) { return reinterpret_cast<_Float16*>(smem + (b ? L::oNt1 : L::oNt0)); };
     auto Xdb = [&](int b) { return reinterpret_cast<_Float16*>(smem + (b ? L::oXd1 : L::oXd0)); };
     float* Nd = reinterpret_cast<float*>(smem + L::oNd);
@@ -222,7 +224,7 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {
     };
     // In-chunk cumulative log-decay G and the per-chunk factor table of chunk c (wave 0,
     // from the g and beta values its issue_part(0, c, ..) loaded).
-    auto scan = [&](int64_t c) {
+    auto scan = [&](int m3) {
         const float x = wave_inclusive_scan(__uint_as_float(cr[oGR]));
         const float GC = lane_value(x, 63);
         float ge[4];
@@ -230,7 +232,7 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {
         for (int b = 0; b < 4; ++b) ge[b] = lane_value(x, 16 * b + 15);
         const int blk = l >> 4;
         const float beta = __uint_as_float(cr[oGR + 1]);
-        float* sm = Sm(c);
+        float* sm = Sm(m3);
         sm[L::SG + l] = x;
         sm[L::SEG + l] = fast_exp(x);
         sm[L::SEGR + l] = fast_exp(GC - x);
@@ -244,22 +246,15 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {
             sm[L::SRB + 64 * b + l] = beta * f;
         }
     };
-    auto stage_v = [&]() {  // V^T tile, fp32 [channel][token]
-        const int row = pt >> 2, col = (pt & 3) * 8;
-        const uint4 vr = getu4(oVR);
-        const uint32_t ww[4] = {vr.x, vr.y, vr.z, vr.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            Vt[(col + 2 * e) * L::LDV + row] = __uint_as_float(ww[e] << 16);
-            Vt[(col + 2 * e + 1) * L::LDV + row] = __uint_as_float(ww[e] & 0xffff0000u);
-        }
+    auto stage_v = [&]() {  // V tile as loaded: bf16 [token][32 channels]
+        *reinterpret_cast<uint4*>(Vt + (pt >> 2) * L::LDV + (pt & 3) * 8) = getu4(oVR);
     };
 
     lds_barrier();  // zero-fill done
     if (nC > 0) {
         issue_all(0, 0);
         stage_kq(0);
-        if (w == 0) scan(0);
+        if (w == 0) scan(0);  // chunk 0 -> buffer 0
     }
     lds_barrier();
 
@@ -282,14 +277,13 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {
 #pragma unroll
             for (int r = 0; r < 2; ++r) f[4 + r] = ld8(Qp + (16 * (2 * P + r) + j) * L::LDK + 32 * kb + 8 * g);
         };
-        // Per-tile scale factors, formed before the products so that their LDS reads and
+        // Per-tile scale factors, formed between the products so that their LDS reads and
         // exponentials overlap the MFMAs: element (l0 + r, m) of tile t is acc * fr[t][r] * fc[t]
         // off the diagonal; on it fr already holds the exact decay (and beta for N) with the
         // causal mask applied.
         float4v fr[NT];
         float fc[NT];
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
+        auto factors = [&](const int t) {
             const int ti = ti_[P][t], tj = tj_[P][t];
             const bool isQ = tq[P][t];
             const int m = 16 * tj + j, l0 = 16 * ti + 4 * g;
@@ -307,7 +301,7 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {
                 }
                 fc[t] = 1.0f;
             }
-        }
+        };
         float4v acc[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t) acc[t] = zero4();
@@ -326,6 +320,11 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {
                 const half8 A = tq[P][t] ? cur[4 + (ti - 2 * P)] : cur[ti];
                 mma16(acc[t], A, cur[tj]);
                 if (t == 1) issue_part(kb, cs_, cv_);
+            }
+            // the epilogue's factors, computed while the matrix pipe works through this block
+            if (kb < 2) {
+#pragma unroll
+                for (int t = 5 * kb; t < 5 * kb + 5; ++t) factors(t);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -351,7 +350,9 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {
         }
     };
 
-    for (int64_t it = -1; it < nC; ++it) {
+    // factor-table buffers (chunk mod 3) of the consumer, producer and scanned chunks
+    int mc = 2, mp = 0, ms = 1;
+    for (int64_t it = -1; it < nC; ++it, mc = mp, mp = ms, ms = (ms == 2 ? 0 : ms + 1)) {
         const int64_t cc = it;        // consumer chunk
         const int64_t cp = it + 1;    // producer chunk (N blocks, diagonal inverses, A)
         const int64_t cs = it + 2;    // chunk whose K, Q are staged in phase 1
@@ -368,7 +369,7 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {
                 const _Float16* Ac = At(bc);
                 const _Float16* Nc = Ntb(bc);
                 const _Float16* Xc = Xdb(bc);
-                const float* sm = Sm(cc);
+                const float* sm = Sm(mc);
                 // The LDS operand fragments of each group of MFMAs are issued one group ahead
                 // (double-buffered registers), and sched_barrier pins that order: left alone,
                 // the scheduler serialises every ds_read with the MFMA that consumes it.
@@ -388,7 +389,12 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {
 #pragma unroll
                 for (int ti = 0; ti < 4; ++ti) {
                     eg[ti] = ld4f(sm + L::SEG + 16 * ti + 4 * g);
-                    vv[ti] = ld4f(Vt + (16 * w + j) * L::LDV + 16 * ti + 4 * g);
+                    // V[16ti + 4g + r][16w + j] through a transposing read, widened from bf16
+                    const uint2 vb = __builtin_bit_cast(
+                        uint2, ldtr(reinterpret_cast<const _Float16*>(Vt) + (16 * ti + 4 * g + (j >> 2)) * L::LDV +
+                                    16 * w + 4 * (j & 3)));
+                    vv[ti] = float4v{__uint_as_float(vb.x << 16), __uint_as_float(vb.x & 0xffff0000u),
+                                     __uint_as_float(vb.y << 16), __uint_as_float(vb.y & 0xffff0000u)};
                     bt[ti] = ld4f(sm + L::SB + 16 * ti + 4 * g);
                 }
                 __builtin_amdgcn_sched_barrier(0);
@@ -515,14 +521,14 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb) seth8(oSB + 4 * kb, pack8(getf4(8 * kb), getf4(8 * kb + 4)));
             }
-            if (w == 0) scan(cs);
+            if (w == 0) scan(ms);
         } else {
           if (cp >= nC) issue_all(cs, cp);
           if (cp < nC) {
             const _Float16* Kp = Kb(bp);
             const _Float16* Qp = Qb(bp);
-            if (p == 0) gram_wave(Kp, Qp, Sm(cp), At(bp), Ntb(bp), 0, cs, cp);
-            else gram_wave(Kp, Qp, Sm(cp), At(bp), Ntb(bp), 1, cs, cp);
+            if (p == 0) gram_wave(Kp, Qp, Sm(mp), At(bp), Ntb(bp), 0, cs, cp);
+            else gram_wave(Kp, Qp, Sm(mp), At(bp), Ntb(bp), 1, cs, cp);
             lds_fence();
             // diagonal 16x16 blocks 2p, 2p+1 of X = N^{-1}, column-oriented forward
             // substitution: lane (block, jc) builds column jc; after x[i] is final it is
