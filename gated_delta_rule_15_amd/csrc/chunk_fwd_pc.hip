@@ -122,6 +122,9 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, j = l & 15, g = l >> 4;
     const bool consumer = w < 2;
     const int p = w - 2;           // producer index (valid when !consumer)
+    // the producers' work per chunk is the longer of the two roles: let them win arbitration
+    // for the CU's shared LDS and memory pipelines
+    if (!consumer) __builtin_amdgcn_s_setprio(2);
     const int vi = xcd_major_index(blockIdx.x, gridDim.x);
     const int64_t bh = vi / a.ntiles;
     const int dv0 = (vi % a.ntiles) * 32;
