@@ -27,9 +27,12 @@
 // K (.) e^{G_C - G} for the state pass (per-block, per-channel factors <= 1).
 //
 // One workgroup (four waves) per (batch*head, 32-wide d_v tile) walks the chunks in order;
-// each chunk runs stage by stage with all waves: scan, staging, Gram, the blocked inverse
-// (as in the scalar kernel), then the state pass on waves 0-1.  Loads of chunk c+1 are in
-// flight while chunk c is processed.
+// each chunk runs stage by stage with all waves: scan, staging, Gram, the inverses of the
+// four 16x16 diagonal blocks of N, then the state pass on waves 0-1, which applies
+// N^{-1} diag(beta) by blocked forward substitution (as in the scalar kernel).  Loads of
+// chunk c+1 are in flight while chunk c is processed.
+#include <type_traits>
+
 #include "chunk_common.h"
 
 namespace gdr {
@@ -53,7 +56,9 @@ struct KdaArgs {
 template <int DK>
 struct KdaLds {
     static constexpr int C = kChunk;
-    static constexpr int LDK = DK + 8;   // halfs, rows of the K / Q operand copies
+    static constexpr int LDK = DK + 16;  // halfs, rows of the K / Q operand copies (bank-conflict
+                                         // free for fragment and transposing reads)
+    static constexpr int LDX = 16 + 8;   // halfs, rows of a 16x16 fp16 block
     static constexpr int LDC = C + 8;    // halfs, rows of C-wide fp16 matrices
     static constexpr int LDV = C + 4;    // floats, rows of V^T
     static constexpr int LDN = 16 + 4;   // floats, rows of a 16x16 fp32 block
@@ -65,27 +70,25 @@ struct KdaLds {
     static constexpr int oQr = oKr + szK;             // Q e^{G - G_start(blk)}, then Q e^G
     static constexpr int oKc = oQr + szK;             // K e^{G_end(blk) - G}, then K e^{G_C - G}
     static constexpr int oAt = oKc + szK;             // A^T
-    static constexpr int oTt = oAt + szC;             // T^T
-    static constexpr int oNt = oTt + szC;             // off-diagonal blocks of N^T (fp16)
-    static constexpr int oXt = oNt + szC;             // X^T, X = N^{-1} (fp16)
-    static constexpr int oNd = oXt + szC;             // diagonal blocks of N^T (fp32)
+    static constexpr int oNt = oAt + szC;             // off-diagonal blocks of N^T (fp16)
+    static constexpr int oXd = oNt + szC;             // X_bb^T, diagonal blocks of N^{-1} (fp16)
+    static constexpr int oNd = oXd + 4 * 16 * LDX * 2;  // diagonal blocks of N^T (fp32)
     static constexpr int oGl = oNd + 4 * 16 * LDN * 4;  // block-local cumulative log-decay [C][LDG]
     static constexpr int oVt = oGl + C * LDG * 4;     // V^T fp32 [32][LDV]
     static constexpr int oOt = oVt + 32 * LDV * 4;    // O^T bf16 [32][LDO]
     // per-chunk tables (fp32 natural channel order unless noted)
     static constexpr int oFB = oOt + 32 * LDO * 2;    // beta [C]
     static constexpr int oFDl = oFB + C * 4;          // Delta_b = G_loc(15) of block b [4][DK]
-    static constexpr int oFGm = oFDl + 4 * DK * 4;    // G_loc(8) of block b [4][DK]
-    static constexpr int oFE = oFGm + 4 * DK * 4;     // e^{G_C} [DK]
-    static constexpr int oHD = oFE + DK * 4;          // fp16, permuted order: d-factors [3][DK]
-    static constexpr int oHMR = oHD + 3 * DK * 2;     // fp16 permuted: e^{-G_loc(8)} [4][DK]
-    static constexpr int oHMC = oHMR + 4 * DK * 2;    // fp16 permuted: e^{G_loc(8) - Delta_b} [4][DK]
-    static constexpr int oHP = oHMC + 4 * DK * 2;     // fp16 permuted: e^{G_start(b)} [4][DK]
-    static constexpr int oHS = oHP + 4 * DK * 2;      // fp16 permuted: e^{G_C - G_end(b)} [4][DK]
+    static constexpr int oFE = oFDl + 4 * DK * 4;     // e^{G_C} [DK]
+    static constexpr int oHD = oFE + DK * 4;          // fp16: d-factors [3][DK]
+    static constexpr int oHMR = oHD + 3 * DK * 2;     // fp16: e^{-G_loc(8)} [4][DK]
+    static constexpr int oHMC = oHMR + 4 * DK * 2;    // fp16: e^{G_loc(8) - Delta_b} [4][DK]
+    static constexpr int oHP = oHMC + 4 * DK * 2;     // fp16: e^{G_start(b)} [4][DK]
+    static constexpr int oHS = oHP + 4 * DK * 2;      // fp16: e^{G_C - G_end(b)} [4][DK]
     static constexpr int oFlag = oHS + 4 * DK * 2;    // int [4]: block needs the bf16 diagonal path
     static constexpr int total = oFlag + 16;
     static_assert(total <= 160 * 1024, "LDS budget of one gfx950 CU exceeded");
-    static_assert((oAt | oTt | oNt | oXt | oNd | oGl | oVt | oOt | oFB | oFDl | oFGm | oFE | oHD | oHMR | oHMC |
+    static_assert((oAt | oNt | oXd | oNd | oGl | oVt | oOt | oFB | oFDl | oFE | oHD | oHMR | oHMC |
                    oHP | oHS | oFlag) % 16 == 0,
                   "alignment");
 };
@@ -106,23 +109,19 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
     constexpr int C = kChunk;
     constexpr int NKB = DK / 32;
     constexpr int NST = DK / 16;
-    constexpr int KVL = C * DK / 8 / 256;  // 16-byte vectors of one K chunk per lane
-    constexpr int CPL = DK / 64;           // channels per lane in the scan
     extern __shared__ __attribute__((aligned(16))) char smem[];
     _Float16* Kr = reinterpret_cast<_Float16*>(smem + L::oKr);
     _Float16* Qr = reinterpret_cast<_Float16*>(smem + L::oQr);
     _Float16* Kc = reinterpret_cast<_Float16*>(smem + L::oKc);
     _Float16* At = reinterpret_cast<_Float16*>(smem + L::oAt);
-    _Float16* Tt = reinterpret_cast<_Float16*>(smem + L::oTt);
     _Float16* Nt = reinterpret_cast<_Float16*>(smem + L::oNt);
-    _Float16* Xt = reinterpret_cast<_Float16*>(smem + L::oXt);
+    _Float16* Xd = reinterpret_cast<_Float16*>(smem + L::oXd);
     float* Nd = reinterpret_cast<float*>(smem + L::oNd);
     float* Gl = reinterpret_cast<float*>(smem + L::oGl);
     float* Vt = reinterpret_cast<float*>(smem + L::oVt);
     _Float16* Ot = reinterpret_cast<_Float16*>(smem + L::oOt);  // bf16 bit patterns
     float* FB = reinterpret_cast<float*>(smem + L::oFB);
     float* FDl = reinterpret_cast<float*>(smem + L::oFDl);
-    float* FGm = reinterpret_cast<float*>(smem + L::oFGm);
     float* FE = reinterpret_cast<float*>(smem + L::oFE);
     _Float16* HD = reinterpret_cast<_Float16*>(smem + L::oHD);
     _Float16* HMR = reinterpret_cast<_Float16*>(smem + L::oHMR);
@@ -152,7 +151,7 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
     };
 
     // structural zeros of the triangular operands (never written afterwards)
-    for (int i = tid; i < (L::oNd + 4 * 16 * L::LDN * 4 - L::oAt) / 16; i += 256)
+    for (int i = tid; i < (L::oGl - L::oAt) / 16; i += 256)
         reinterpret_cast<uint4*>(smem + L::oAt)[i] = uint4{0u, 0u, 0u, 0u};
 
     // ---- state of consumer waves 0-1: S^T tiles (fp32) and their fp16 operand copy
@@ -163,62 +162,59 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
     if (w < 2 && a.S0 != nullptr) {
         const float* s0 = a.S0 + bh * (int64_t)DV * DK + (int64_t)(dvc + j) * DK;
 #pragma unroll
-        for (int t = 0; t < NST; ++t) St[t] = ld4f(s0 + 16 * t + 4 * g);
+        for (int t = 0; t < NST; ++t) St[t] = ld4f(s0 + pperm(16 * t + 4 * g));
     }
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) Sb[kb] = pack8(St[2 * kb], St[2 * kb + 1]);
 
-    // ---- prefetch registers for one chunk
-    float2 gp[16];  // g of tokens 16w + t, channels CPL*l (+1)
-    uint4 kp[KVL], qp[KVL], vp;
+    // ---- prefetch registers for one chunk, in the layout of the scan: wave w holds the
+    // 16-token block w, lane l the channel pair ch2 = 2 (l mod DK/2) (for DK = 64 the upper
+    // half of the wave loads duplicates and stores nothing)
+    const int ch2 = 2 * (l % (DK / 2));
+    const bool own = 2 * l < DK;
+    float2 gp[16];
+    uint32_t kp[16], qp[16];
+    uint4 vp;
     float bp = 0.0f;
+    // token t of the lane's block (g, k, q of its channel pair); t = 0 also brings V, beta.
+    // Past the sequence end the loads return zeros (identity tokens).
+    auto issue_tok = [&](int64_t c, int t) {
+        const uint32_t t0 = (uint32_t)(c * C) + 16 * w;
+        const uint2 u = bld8(rg, ((t0 + t) * DK + ch2) * 4);
+        gp[t] = float2{__uint_as_float(u.x), __uint_as_float(u.y)};
+        kp[t] = __builtin_amdgcn_raw_buffer_load_b32(rk, ((t0 + t) * DK + ch2) * 2, 0, 0);
+        qp[t] = __builtin_amdgcn_raw_buffer_load_b32(rq, ((t0 + t) * DK + ch2) * 2, 0, 0);
+        if (t == 0) {
+            const uint32_t tc = (uint32_t)(c * C);
+            vp = bld16(rv, ((tc + (tid >> 2)) * DV + dv0 + (tid & 3) * 8) * 2);
+            if (w == 0) bp = bld4(rb, (tc + l) * 4);
+        }
+    };
     auto issue = [&](int64_t c) {
-        const uint32_t t0 = (uint32_t)(c * C);
 #pragma unroll
-        for (int t = 0; t < 16; ++t) {
-            const uint32_t off = ((t0 + 16 * w + t) * DK + CPL * l) * 4;
-            if constexpr (CPL == 2) {
-                const uint2 u = bld8(rg, off);
-                gp[t] = float2{__uint_as_float(u.x), __uint_as_float(u.y)};
-            } else {
-                gp[t] = float2{bld4(rg, off), 0.0f};
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < KVL; ++u) {
-            const int idx = tid + 256 * u, row = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
-            const uint32_t off = ((t0 + row) * DK + col) * 2;
-            kp[u] = bld16(rk, off);
-            qp[u] = bld16(rq, off);
-        }
-        vp = bld16(rv, ((t0 + (tid >> 2)) * DV + dv0 + (tid & 3) * 8) * 2);
-        if (w == 0) bp = bld4(rb, (t0 + l) * 4);
+        for (int t = 0; t < 16; ++t) issue_tok(c, t);
     };
 
     // Operand fragments (row j of tile ti, reduction block kb) of the Gram products.
     auto rfrag = [&](const _Float16* M, int ti, int kb) { return ld8(M + (16 * ti + j) * L::LDK + 32 * kb + 8 * g); };
     auto hfrag = [&](const _Float16* H, int row, int kb) { return ld8(H + row * DK + 32 * kb + 8 * g); };
     // Diagonal-tile operand of block b built afresh in fp32 from the bf16 input (lane row or
-    // column j = token 16b + j; the fragment's channels are 32kb + 4g + e and 32kb + 16 + 4g
-    // + e): x e^{G_loc(tok) - G_loc(8)} for the row side, x e^{G_loc(8) - G_loc(tok)} for
-    // the column side, rounded to bf16.
+    // column j = token 16b + j; the fragment's channels are 32kb + 8g .. +7):
+    // x e^{G_loc(tok) - G_loc(8)} for the row side, x e^{G_loc(8) - G_loc(tok)} for the
+    // column side, rounded to bf16.
     auto diag_bf16 = [&](const __amdgpu_buffer_rsrc_t& rs, int64_t c, int b, int kb, bool row_side) {
-        const int tok = 16 * b + j, ch = 32 * kb + 4 * g;
-        const uint32_t off = ((uint32_t)(c * C + tok) * DK + ch) * 2;
-        const uint2 lo = bld8(rs, off), hi = bld8(rs, off + 32);
-        const uint32_t wv[4] = {lo.x, lo.y, hi.x, hi.y};
+        const int tok = 16 * b + j, ch = 32 * kb + 8 * g;
+        const uint4 u = bld16(rs, ((uint32_t)(c * C + tok) * DK + ch) * 2);
+        const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
         const float* gt = Gl + tok * L::LDG + ch;
         const float* gm = Gl + (16 * b + 8) * L::LDG + ch;
-        const float4v t0 = ld4f(gt), t1 = ld4f(gt + 16), m0 = ld4f(gm), m1 = ld4f(gm + 16);
+        const float4v t0 = ld4f(gt), t1 = ld4f(gt + 4), m0 = ld4f(gm), m1 = ld4f(gm + 4);
         bf16x8 r;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float d0 = row_side ? t0[e] - m0[e] : m0[e] - t0[e];
-            const float d1 = row_side ? t1[e] - m1[e] : m1[e] - t1[e];
-            const float x0 = __uint_as_float(e & 1 ? (wv[e >> 1] & 0xffff0000u) : (wv[e >> 1] << 16));
-            const float x1 = __uint_as_float(e & 1 ? (wv[2 + (e >> 1)] & 0xffff0000u) : (wv[2 + (e >> 1)] << 16));
-            r[e] = (__bf16)(x0 * fast_exp(d0));
-            r[4 + e] = (__bf16)(x1 * fast_exp(d1));
+        for (int e = 0; e < 8; ++e) {
+            const float te = e < 4 ? t0[e] : t1[e - 4], me = e < 4 ? m0[e] : m1[e - 4];
+            const float x = __uint_as_float(e & 1 ? (wv[e >> 1] & 0xffff0000u) : (wv[e >> 1] << 16));
+            r[e] = (__bf16)(x * fast_exp(row_side ? te - me : me - te));
         }
         return r;
     };
@@ -227,39 +223,61 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
     if (nC > 0) issue(0);
 
     for (int64_t c = 0; c < nC; ++c) {
-        // ================= S1: block-local scan of the log-decay; V and beta =================
+        // ====== S1: block-local scan of the log-decay and the decayed copies of K and Q ======
+        // Per channel pair and 16-token block: a_t = e^{g_t}, E_t = e^{G_loc(t)} (forward
+        // product), Ec_t = e^{G_loc(15) - G_loc(t)} (backward product);
+        // Kr = K E, Qr = Q E, Kc = K Ec.
         {
-            float G[16][CPL];
-            float run[CPL];
-#pragma unroll
-            for (int e = 0; e < CPL; ++e) run[e] = 0.0f;
-            bool unsafe = false;
+            float G[16][2], E[16][2], Ec[16][2];
+            float run[2] = {0.0f, 0.0f}, pe[2] = {1.0f, 1.0f}, pc[2] = {1.0f, 1.0f};
+            float av[16][2];
 #pragma unroll
             for (int t = 0; t < 16; ++t) {
                 const float gv[2] = {gp[t].x, gp[t].y};
 #pragma unroll
-                for (int e = 0; e < CPL; ++e) {
+                for (int e = 0; e < 2; ++e) {
                     run[e] += gv[e];
                     G[t][e] = run[e];
+                    av[t][e] = fast_exp(gv[e]);
+                    pe[e] *= av[t][e];
+                    E[t][e] = pe[e];
                 }
             }
 #pragma unroll
-            for (int e = 0; e < CPL; ++e) {
+            for (int t = 15; t >= 0; --t) {
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    Ec[t][e] = pc[e];
+                    pc[e] *= av[t][e];
+                }
+            }
+            bool unsafe = false;
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
                 const float gm = G[8][e];
                 unsafe |= fabsf(gm) > 6.0f;  // the block start, G_loc = 0
 #pragma unroll
                 for (int t = 0; t < 16; ++t) unsafe |= fabsf(G[t][e] - gm) > 6.0f;
             }
+            if (own) {
 #pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                float* dst = Gl + (16 * w + t) * L::LDG + CPL * l;
-                if constexpr (CPL == 2) *reinterpret_cast<float2*>(dst) = float2{G[t][0], G[t][1]};
-                else dst[0] = G[t][0];
-            }
+                for (int t = 0; t < 16; ++t) {
+                    const int row = 16 * w + t;
+                    *reinterpret_cast<float2*>(Gl + row * L::LDG + ch2) = float2{G[t][0], G[t][1]};
+                    const float k0 = __uint_as_float(kp[t] << 16), k1 = __uint_as_float(kp[t] & 0xffff0000u);
+                    const float q0 = __uint_as_float(qp[t] << 16), q1 = __uint_as_float(qp[t] & 0xffff0000u);
+                    typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+                    *reinterpret_cast<half2v*>(Kr + row * L::LDK + ch2) = half2v{(_Float16)(k0 * E[t][0]), (_Float16)(k1 * E[t][1])};
+                    *reinterpret_cast<half2v*>(Qr + row * L::LDK + ch2) = half2v{(_Float16)(q0 * E[t][0]), (_Float16)(q1 * E[t][1])};
+                    *reinterpret_cast<half2v*>(Kc + row * L::LDK + ch2) = half2v{(_Float16)(k0 * Ec[t][0]), (_Float16)(k1 * Ec[t][1])};
+                }
 #pragma unroll
-            for (int e = 0; e < CPL; ++e) {
-                FDl[w * DK + CPL * l + e] = G[15][e];
-                FGm[w * DK + CPL * l + e] = G[8][e];
+                for (int e = 0; e < 2; ++e) {
+                    FDl[w * DK + ch2 + e] = G[15][e];
+                    // diagonal-tile factors of this block: e^{-G_loc(8)}, e^{G_loc(8) - G_loc(15)}
+                    HMR[w * DK + ch2 + e] = (_Float16)fast_exp(-G[8][e]);
+                    HMC[w * DK + ch2 + e] = (_Float16)fast_exp(G[8][e] - G[15][e]);
+                }
             }
             const bool any_unsafe = __any(unsafe);
             if (l == 0) Flag[w] = any_unsafe ? 1 : 0;
@@ -275,114 +293,76 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
         }
         lds_barrier();
 
-        // ================= S2: per-channel tables; scaled operand copies =================
-        if (tid < DK) {
-            const int ch = tid, pc = pperm(ch);
-            float D[4], Gm[4];
+        // ================= S2: per-channel tables across the blocks =================
+        {
+            // spread over all threads: channel tid % DK, a share of the blocks
+            const int ch = tid % DK, hb = tid / DK;  // hb in [0, 256 / DK)
+            float D[4];
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                D[b] = FDl[b * DK + ch];
-                Gm[b] = FGm[b * DK + ch];
-            }
+            for (int b = 0; b < 4; ++b) D[b] = FDl[b * DK + ch];
             const float P[4] = {0.0f, D[0], D[0] + D[1], D[0] + D[1] + D[2]};
             const float GC = P[3] + D[3];
-            FE[ch] = fast_exp(GC);
+            constexpr int NH = 256 / DK, BPH = 4 / NH;  // thread groups per channel, blocks each
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                HMR[b * DK + pc] = (_Float16)fast_exp(-Gm[b]);
-                HMC[b * DK + pc] = (_Float16)fast_exp(Gm[b] - D[b]);
-                HP[b * DK + pc] = (_Float16)fast_exp(P[b]);
-                HS[b * DK + pc] = (_Float16)fast_exp(GC - P[b] - D[b]);
+            for (int bb = 0; bb < BPH; ++bb) {
+                const int b = hb * BPH + bb;
+                HP[b * DK + ch] = (_Float16)fast_exp(P[b]);
+                HS[b * DK + ch] = (_Float16)fast_exp(GC - P[b] - D[b]);
             }
-            // column factors of the tiles two or three blocks below the diagonal:
-            // (2,0): e^{Delta_1}, (3,1): e^{Delta_2}, (3,0): e^{Delta_1 + Delta_2}
-            HD[0 * DK + pc] = (_Float16)fast_exp(D[1]);
-            HD[1 * DK + pc] = (_Float16)fast_exp(D[2]);
-            HD[2 * DK + pc] = (_Float16)fast_exp(D[1] + D[2]);
+            if (hb == 0) {
+                FE[ch] = fast_exp(GC);
+                // column factors of the tiles two or three blocks below the diagonal:
+                // (2,0): e^{Delta_1}, (3,1): e^{Delta_2}, (3,0): e^{Delta_1 + Delta_2}
+                HD[0 * DK + ch] = (_Float16)fast_exp(D[1]);
+                HD[1 * DK + ch] = (_Float16)fast_exp(D[2]);
+                HD[2 * DK + ch] = (_Float16)fast_exp(D[1] + D[2]);
+            }
         }
-#pragma unroll
-        for (int u = 0; u < KVL; ++u) {
-            const int idx = tid + 256 * u, row = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
-            const float* gr = Gl + row * L::LDG + col;
-            const float* dl = FDl + (row >> 4) * DK + col;
-            const float4v g0 = ld4f(gr), g1 = ld4f(gr + 4), d0 = ld4f(dl), d1 = ld4f(dl + 4);
-            float er[8], ec[8];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                er[e] = fast_exp(g0[e]);
-                er[4 + e] = fast_exp(g1[e]);
-                ec[e] = fast_exp(d0[e] - g0[e]);
-                ec[4 + e] = fast_exp(d1[e] - g1[e]);
-            }
-            const uint32_t kw[4] = {kp[u].x, kp[u].y, kp[u].z, kp[u].w};
-            const uint32_t qw[4] = {qp[u].x, qp[u].y, qp[u].z, qp[u].w};
-            half4 kr0, kr1, qr0, qr1, kc0, kc1;
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const float k0 = __uint_as_float(kw[e] << 16), k1 = __uint_as_float(kw[e] & 0xffff0000u);
-                const float k2 = __uint_as_float(kw[2 + e] << 16), k3 = __uint_as_float(kw[2 + e] & 0xffff0000u);
-                const float q0 = __uint_as_float(qw[e] << 16), q1 = __uint_as_float(qw[e] & 0xffff0000u);
-                const float q2 = __uint_as_float(qw[2 + e] << 16), q3 = __uint_as_float(qw[2 + e] & 0xffff0000u);
-                kr0[2 * e] = (_Float16)(k0 * er[2 * e]);
-                kr0[2 * e + 1] = (_Float16)(k1 * er[2 * e + 1]);
-                kr1[2 * e] = (_Float16)(k2 * er[4 + 2 * e]);
-                kr1[2 * e + 1] = (_Float16)(k3 * er[4 + 2 * e + 1]);
-                qr0[2 * e] = (_Float16)(q0 * er[2 * e]);
-                qr0[2 * e + 1] = (_Float16)(q1 * er[2 * e + 1]);
-                qr1[2 * e] = (_Float16)(q2 * er[4 + 2 * e]);
-                qr1[2 * e + 1] = (_Float16)(q3 * er[4 + 2 * e + 1]);
-                kc0[2 * e] = (_Float16)(k0 * ec[2 * e]);
-                kc0[2 * e + 1] = (_Float16)(k1 * ec[2 * e + 1]);
-                kc1[2 * e] = (_Float16)(k2 * ec[4 + 2 * e]);
-                kc1[2 * e + 1] = (_Float16)(k3 * ec[4 + 2 * e + 1]);
-            }
-            const int p0 = row * L::LDK + pperm(col), p1 = row * L::LDK + pperm(col + 4);
-            *reinterpret_cast<half4*>(Kr + p0) = kr0;
-            *reinterpret_cast<half4*>(Kr + p1) = kr1;
-            *reinterpret_cast<half4*>(Qr + p0) = qr0;
-            *reinterpret_cast<half4*>(Qr + p1) = qr1;
-            *reinterpret_cast<half4*>(Kc + p0) = kc0;
-            *reinterpret_cast<half4*>(Kc + p1) = kc1;
-        }
-        // the next chunk's loads fly during the rest of this one
-        if (c + 1 < nC) issue(c + 1);
         lds_barrier();
 
         // ================= S3: Gram tiles =================
         // waves 0-1: K rows (N), waves 2-3: Q rows (A); half 0 tiles {00,10,11,20,30}, half 1
         // {21,22,31,32,33}.  Column factor code: -1 none, 0..2 d-factor pair, 3 diagonal.
-        {
-            const bool isQ = w >= 2;
-            const int h = w & 1;
+        // Each wave runs its own compile-time instance, so every tile's path is static.
+        // The next chunk's loads are issued between this stage's MFMAs (a token of the block
+        // per step), so the memory queue drains while the matrix pipe works.
+        const int64_t cn = c + 1 < nC ? c + 1 : c;  // reloading the last chunk is harmless
+        auto gram_kda = [&](auto hc, auto qc) {
+            constexpr int h = decltype(hc)::value;
+            constexpr bool isQ = decltype(qc)::value;
             const _Float16* Rs = isQ ? Qr : Kr;
             constexpr int NT = 5;
-            const int ti_[2][NT] = {{0, 1, 1, 2, 3}, {2, 2, 3, 3, 3}};
-            const int tj_[2][NT] = {{0, 0, 1, 0, 0}, {1, 2, 1, 2, 3}};
-            const int cf_[2][NT] = {{3, -1, 3, 0, 2}, {-1, 3, 1, -1, 3}};
+            constexpr int ti_[2][NT] = {{0, 1, 1, 2, 3}, {2, 2, 3, 3, 3}};
+            constexpr int tj_[2][NT] = {{0, 0, 1, 0, 0}, {1, 2, 1, 2, 3}};
+            constexpr int cf_[2][NT] = {{3, -1, 3, 0, 2}, {-1, 3, 1, -1, 3}};
             float4v acc[NT];
 #pragma unroll
             for (int t = 0; t < NT; ++t) acc[t] = zero4();
+            // the bf16 path of a diagonal block is chosen per block for the whole wave
             int fl[4];
 #pragma unroll
-            for (int b = 0; b < 4; ++b) fl[b] = Flag[b];
+            for (int b = 0; b < 4; ++b) fl[b] = __builtin_amdgcn_readfirstlane(Flag[b]);
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
                 for (int t = 0; t < NT; ++t) {
                     const int ti = ti_[h][t], tj = tj_[h][t], cf = cf_[h][t];
-                    half8 A = rfrag(Rs, ti, kb), B = rfrag(Kc, tj, kb);
+                    const half8 A = rfrag(Rs, ti, kb);
+                    half8 B = rfrag(Kc, tj, kb);
                     if (cf == 3) {
-                        const int b = ti;
-                        if (fl[b]) {
-                            mma16_bf16(acc[t], diag_bf16(isQ ? rq : rk, c, b, kb, true), diag_bf16(rk, c, b, kb, false));
+                        if (fl[ti]) {
+                            mma16_bf16(acc[t], diag_bf16(isQ ? rq : rk, c, ti, kb, true), diag_bf16(rk, c, ti, kb, false));
                         } else {
-                            mma16(acc[t], hmul8(A, hfrag(HMR, b, kb)), hmul8(B, hfrag(HMC, b, kb)));
+                            mma16(acc[t], hmul8(A, hfrag(HMR, ti, kb)), hmul8(B, hfrag(HMC, ti, kb)));
                         }
                     } else {
                         if (cf >= 0) B = hmul8(B, hfrag(HD, cf, kb));
                         mma16(acc[t], A, B);
                     }
+                    if (t < 16 / NKB) issue_tok(cn, kb * (16 / NKB) + t);
                 }
+#pragma unroll
+                for (int u = NT; u < 16 / NKB; ++u) issue_tok(cn, kb * (16 / NKB) + u);
             }
             // epilogue: beta of the row for N, causal masks on the diagonal
 #pragma unroll
@@ -413,19 +393,26 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
                     *reinterpret_cast<half4*>(dst) = half4{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
                 }
             }
-        }
+        };
+        if (w == 0) gram_kda(std::integral_constant<int, 0>{}, std::false_type{});
+        else if (w == 1) gram_kda(std::integral_constant<int, 1>{}, std::false_type{});
+        else if (w == 2) gram_kda(std::integral_constant<int, 0>{}, std::true_type{});
+        else gram_kda(std::integral_constant<int, 1>{}, std::true_type{});
         lds_barrier();
 
-        // ================= S4: diagonal inverses (block w per wave) =================
-        float xd[16];
-        {
-            const int b = w, jc = j;
+        // ============ S4: diagonal inverses (waves 0-1, two blocks each); the copies are
+        // rescaled in place for the state pass (waves 2-3) ============
+        if (w < 2) {
+            // column-oriented forward substitution: lane (block, jc) builds column jc of
+            // X_bb = N_bb^{-1}; stored as X_bb^T (row jc = column jc)
+            const int b = 2 * w + ((l >> 4) & 1), jc = j;
             const float* nb = Nd + b * 16 * L::LDN;
             float4v nr[15][4];
 #pragma unroll
             for (int i = 0; i < 15; ++i)
 #pragma unroll
                 for (int q4 = (i + 1) / 4; q4 < 4; ++q4) nr[i][q4] = ld4f(nb + i * L::LDN + 4 * q4);
+            float xd[16];
 #pragma unroll
             for (int t = 0; t < 16; ++t) xd[t] = (t == jc) ? 1.0f : 0.0f;
 #pragma unroll
@@ -437,40 +424,25 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
                         if (4 * q4 + e > i) xd[4 * q4 + e] -= nr[i][q4][e] * xd[i];
                 }
             }
-            if (l < 16) {
+            if (l < 32) {
                 half8 h0, h1;
 #pragma unroll
                 for (int t = 0; t < 8; ++t) {
                     h0[t] = (_Float16)xd[t];
                     h1[t] = (_Float16)xd[8 + t];
                 }
-                *reinterpret_cast<half8*>(Xt + (16 * b + jc) * L::LDC + 16 * b) = h0;
-                *reinterpret_cast<half8*>(Xt + (16 * b + jc) * L::LDC + 16 * b + 8) = h1;
+                *reinterpret_cast<half8*>(Xd + (16 * b + jc) * L::LDX) = h0;
+                *reinterpret_cast<half8*>(Xd + (16 * b + jc) * L::LDX + 8) = h1;
             }
         }
-        lds_barrier();
-
-        // ================= S5: first block level (waves 0-1); rescale the copies (2-3) ======
-        float4v x2 = zero4();
-        if (w < 2) {
-            const int p = w, b0 = 2 * p, b1 = 2 * p + 1;
-            const half4 z4 = {(_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f};
-            const half8 fa = cat8(ldtr(Nt + (16 * b0 + 4 * g + (j >> 2)) * L::LDC + 16 * b1 + 4 * (j & 3)), z4);
-            const half8 fb = cat8(*reinterpret_cast<const half4*>(Xt + (16 * b0 + j) * L::LDC + 16 * b0 + 4 * g), z4);
-            float4v y = zero4();
-            mma16(y, fa, fb);
-            const half8 fx = cat8(ldtr(Xt + (16 * b1 + 4 * g + (j >> 2)) * L::LDC + 16 * b1 + 4 * (j & 3)), z4);
-            const half8 fy = cat8(half4{(_Float16)y[0], (_Float16)y[1], (_Float16)y[2], (_Float16)y[3]}, z4);
-            mma16(x2, fx, fy);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) x2[r] = -x2[r];
-            *reinterpret_cast<half4*>(Xt + (16 * b0 + j) * L::LDC + 16 * b1 + 4 * g) =
-                half4{(_Float16)x2[0], (_Float16)x2[1], (_Float16)x2[2], (_Float16)x2[3]};
-        } else {
+        {
             // Kr -> K e^G, Qr -> Q e^G (factor e^{G_start(blk)}), Kc -> K e^{G_C - G}
-            // (factor e^{G_C - G_end(blk)}); 16-byte groups of the permuted rows.
+            // (factor e^{G_C - G_end(blk)}); 16-byte groups of the rows.  Waves 2-3 take the
+            // first three quarters, waves 0-1 (after their inverses) the last quarter.
             constexpr int NG = C * (DK / 8);  // 16-byte groups per copy
-            for (int i = tid - 128; i < NG; i += 128) {
+            const int i0 = w >= 2 ? tid - 128 : 3 * NG / 4 + tid;
+            const int i1 = w >= 2 ? 3 * NG / 4 : NG;
+            for (int i = i0; i < i1; i += 128) {
                 const int row = i / (DK / 8), col = (i % (DK / 8)) * 8, blk = row >> 4;
                 const half8 fp = ld8(HP + blk * DK + col), fs = ld8(HS + blk * DK + col);
                 half8* pk = reinterpret_cast<half8*>(Kr + row * L::LDK + col);
@@ -483,65 +455,7 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
         }
         lds_barrier();
 
-        // ================= S6: second block level (waves 0-1) =================
-        float4v xc[2] = {zero4(), zero4()};
-        if (w < 2) {
-            const int p = w, n = 16 * p + j;
-            const half8 fxa = cat8(*reinterpret_cast<const half4*>(Xt + n * L::LDC + 4 * g),
-                                   *reinterpret_cast<const half4*>(Xt + n * L::LDC + 16 + 4 * g));
-            float4v y3[2];
-#pragma unroll
-            for (int ti = 0; ti < 2; ++ti) {
-                y3[ti] = zero4();
-                mma16(y3[ti], trfrag(Nt, L::LDC, 0, 32 + 16 * ti + 4 * (j & 3)), fxa);
-            }
-            const half8 fy = pack8(y3[0], y3[1]);
-#pragma unroll
-            for (int ti = 0; ti < 2; ++ti) {
-                mma16(xc[ti], trfrag(Xt, L::LDC, 1, 32 + 16 * ti + 4 * (j & 3)), fy);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) xc[ti][r] = -xc[ti][r];
-            }
-        }
-        lds_barrier();
-
-        // ================= S7: T = X diag(beta), column-major =================
-        {
-            const int b = w;
-            if (l < 16) {
-                const int m = 16 * b + j;
-                const float bm = FB[m];
-                half8 h0, h1;
-#pragma unroll
-                for (int t = 0; t < 8; ++t) {
-                    h0[t] = (_Float16)(xd[t] * bm);
-                    h1[t] = (_Float16)(xd[8 + t] * bm);
-                }
-                *reinterpret_cast<half8*>(Tt + m * L::LDC + 16 * b) = h0;
-                *reinterpret_cast<half8*>(Tt + m * L::LDC + 16 * b + 8) = h1;
-            }
-            if (w < 2) {
-                const int p = w;
-                {
-                    const int m = 32 * p + j;
-                    const float bm = FB[m];
-                    *reinterpret_cast<half4*>(Tt + m * L::LDC + 32 * p + 16 + 4 * g) =
-                        half4{(_Float16)(x2[0] * bm), (_Float16)(x2[1] * bm), (_Float16)(x2[2] * bm), (_Float16)(x2[3] * bm)};
-                }
-                {
-                    const int m = 16 * p + j;
-                    const float bm = FB[m];
-#pragma unroll
-                    for (int ti = 0; ti < 2; ++ti)
-                        *reinterpret_cast<half4*>(Tt + m * L::LDC + 32 + 16 * ti + 4 * g) =
-                            half4{(_Float16)(xc[ti][0] * bm), (_Float16)(xc[ti][1] * bm), (_Float16)(xc[ti][2] * bm),
-                                  (_Float16)(xc[ti][3] * bm)};
-                }
-            }
-        }
-        lds_barrier();
-
-        // ================= S8: state pass of chunk c (waves 0-1) =================
+        // ================= S5: state pass of chunk c (waves 0-1) =================
         if (w < 2) {
             // P_K = (K e^G) S^T, P_Q = (Q e^G) S^T
             float4v PK[4], PQ[4];
@@ -556,9 +470,12 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
                 fa[ti] = rfrag(Kr, ti, 0);
                 fa[4 + ti] = rfrag(Qr, ti, 0);
             }
-            float4v vv[4];
+            float4v vv[4], bt[4];
 #pragma unroll
-            for (int ti = 0; ti < 4; ++ti) vv[ti] = ld4f(Vt + (16 * w + j) * L::LDV + 16 * ti + 4 * g);
+            for (int ti = 0; ti < 4; ++ti) {
+                vv[ti] = ld4f(Vt + (16 * w + j) * L::LDV + 16 * ti + 4 * g);
+                bt[ti] = ld4f(FB + 16 * ti + 4 * g);
+            }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
@@ -579,32 +496,56 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
-            half8 tf[6], af[6];
+            // operands of the block substitution and of A Z
+            half4 xf[4];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) xf[b] = ldtr(Xd + (16 * b + 4 * g + (j >> 2)) * L::LDX + 4 * (j & 3));
+            const half4 n10 = ldtr(Nt + (4 * g + (j >> 2)) * L::LDC + 16 + 4 * (j & 3));
+            const half8 n2x = trfrag(Nt, L::LDC, 0, 32 + 4 * (j & 3));
+            const half8 n3x = trfrag(Nt, L::LDC, 0, 48 + 4 * (j & 3));
+            const half4 n32 = ldtr(Nt + (32 + 4 * g + (j >> 2)) * L::LDC + 48 + 4 * (j & 3));
+            half8 af[6];
 #pragma unroll
             for (int ti = 0, n = 0; ti < 4; ++ti) {
 #pragma unroll
-                for (int kb = 0; kb <= (ti >> 1); ++kb, ++n) {
-                    tf[n] = trfrag(Tt, L::LDC, kb, 16 * ti + 4 * (j & 3));
-                    af[n] = trfrag(At, L::LDC, kb, 16 * ti + 4 * (j & 3));
-                }
+                for (int kb = 0; kb <= (ti >> 1); ++kb, ++n) af[n] = trfrag(At, L::LDC, kb, 16 * ti + 4 * (j & 3));
             }
             float4v ed[NST];
 #pragma unroll
-            for (int t = 0; t < NST; ++t) ed[t] = ld4f(FE + 16 * t + 4 * g);
+            for (int t = 0; t < NST; ++t) ed[t] = ld4f(FE + pperm(16 * t + 4 * g));
             __builtin_amdgcn_sched_barrier(0);
-            float4v Rr[4];
+            // R' = diag(beta) (V - P_K);  Z = N^{-1} R' by blocked forward substitution
+            float4v Rb[4];
 #pragma unroll
             for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) Rr[ti][r] = vv[ti][r] - PK[ti][r];
-            const half8 rB[2] = {pack8(Rr[0], Rr[1]), pack8(Rr[2], Rr[3])};
-            float4v Zz[4];
+                for (int r = 0; r < 4; ++r) Rb[ti][r] = bt[ti][r] * (vv[ti][r] - PK[ti][r]);
+            auto mma16k16 = [](float4v& acc, const half4& a4, const half4& b4) {
+                acc = __builtin_amdgcn_mfma_f32_16x16x16f16(a4, b4, acc, 0, 0, 0);
+            };
+            auto h4 = [](const float4v& x) { return half4{(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3]}; };
+            auto sub4 = [](float4v a4, const float4v& b4) {
 #pragma unroll
-            for (int ti = 0, n = 0; ti < 4; ++ti) {
-                Zz[ti] = zero4();
-#pragma unroll
-                for (int kb = 0; kb <= (ti >> 1); ++kb, ++n) mma16(Zz[ti], tf[n], rB[kb]);
-            }
+                for (int r = 0; r < 4; ++r) a4[r] -= b4[r];
+                return a4;
+            };
+            float4v Zz[4], y;
+            Zz[0] = zero4();
+            mma16k16(Zz[0], xf[0], h4(Rb[0]));
+            y = zero4();
+            mma16k16(y, n10, h4(Zz[0]));
+            Zz[1] = zero4();
+            mma16k16(Zz[1], xf[1], h4(sub4(Rb[1], y)));
+            const half8 z01 = pack8(Zz[0], Zz[1]);
+            y = zero4();
+            mma16(y, n2x, z01);
+            Zz[2] = zero4();
+            mma16k16(Zz[2], xf[2], h4(sub4(Rb[2], y)));
+            y = zero4();
+            mma16(y, n3x, z01);
+            mma16k16(y, n32, h4(Zz[2]));
+            Zz[3] = zero4();
+            mma16k16(Zz[3], xf[3], h4(sub4(Rb[3], y)));
             auto ktfrag = [&](int t, int kb) { return trfrag(Kc, L::LDK, kb, pperm(16 * t + 4 * (j & 3))); };
             half8 kt0[NST], kt1[NST];
 #pragma unroll
@@ -612,7 +553,7 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
                 kt0[t] = ktfrag(t, 0);
                 kt1[t] = ktfrag(t, 1);
             }
-            const half8 zB[2] = {pack8(Zz[0], Zz[1]), pack8(Zz[2], Zz[3])};
+            const half8 zB[2] = {z01, pack8(Zz[2], Zz[3])};
 #pragma unroll
             for (int ti = 0, n = 0; ti < 4; ++ti) {
                 float4v acc = PQ[ti];
@@ -647,7 +588,7 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
     if (w < 2 && a.Sf != nullptr) {
         float* sf = a.Sf + bh * (int64_t)DV * DK + (int64_t)(dvc + j) * DK;
 #pragma unroll
-        for (int t = 0; t < NST; ++t) *reinterpret_cast<float4v*>(sf + 16 * t + 4 * g) = St[t];
+        for (int t = 0; t < NST; ++t) *reinterpret_cast<float4v*>(sf + pperm(16 * t + 4 * g)) = St[t];
     }
 }
 
