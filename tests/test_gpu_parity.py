@@ -105,7 +105,7 @@ def test_decode_full_size_64_steps_sampled():
 
 # ----------------------------------------------------------------------------- chunk_fwd
 @pytest.mark.parametrize("T", [1, 37, 64, 65, 200])
-@pytest.mark.parametrize("dk,dv", [(128, 128), (128, 32), (64, 64)])
+@pytest.mark.parametrize("dk,dv", [(128, 128), (128, 32), (64, 64), (128, 256), (64, 96)])
 @pytest.mark.parametrize("with_s0", [False, True])
 def test_chunk_small_bf16(T, dk, dv, with_s0):
     w = variant(2, d_k=dk, d_v=dv)
@@ -163,7 +163,7 @@ def test_chunk_workload4_full_size_sampled():
 
 # ----------------------------------------------------------------------------- chunk_fwd, per-channel gate
 @pytest.mark.parametrize("T", [1, 37, 64, 65, 200])
-@pytest.mark.parametrize("dk,dv", [(128, 128), (128, 32), (64, 64)])
+@pytest.mark.parametrize("dk,dv", [(128, 128), (128, 32), (64, 64), (128, 256), (64, 96)])
 @pytest.mark.parametrize("with_s0", [False, True])
 def test_chunk_kda_small(T, dk, dv, with_s0):
     w = variant(3, d_k=dk, d_v=dv)
