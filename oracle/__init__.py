@@ -12,6 +12,10 @@ Two independent fp64 implementations live here:
   Visualized" (sections "Gated DeltaNet (GDN)" and "Reuse GLA and GDN"),
   written in numpy, used only to cross-check the recurrence (every chunk size
   gives the exact result, section "Cost").
+* ``gdp_forward`` -- Gated Delta Product token by token (section "Gated Delta
+  Product (GDP)"), with the explicit n_h-substep update in the page's row
+  notation, in C; and ``gdp_as_virtual_gdn``, the input mapping of section
+  "GDP as GDN over a virtual sequence" that turns a GDP problem into a GDN one.
 
 Both are pinned by ``tests/test_oracle_*.py`` against closed forms, limits and
 brute force that do not reuse them.  Parity of every function here is pinned;
@@ -61,6 +65,9 @@ def _load():
             lib.oracle_gdr_decode_step.argtypes = [ctypes.c_long, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                                    P, P, P, P, P, P, P, ctypes.c_int]
             lib.oracle_gdr_decode_step.restype = ctypes.c_int
+            lib.oracle_gdp_forward.argtypes = [ctypes.c_long, ctypes.c_long, ctypes.c_int, ctypes.c_int,
+                                               ctypes.c_int, P, P, P, P, P, P, P, P, ctypes.c_int]
+            lib.oracle_gdp_forward.restype = ctypes.c_int
             lib.oracle_max_threads.restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -131,6 +138,59 @@ def decode_step(q, k, v, g, beta, S, nthreads: int = 0):
     if rc != 0:
         raise RuntimeError(f"oracle_gdr_decode_step failed ({rc})")
     return o, Snew
+
+
+def gdp_forward(q, k, v, g, beta, S0=None, nthreads: int = 0):
+    """Gated Delta Product, token by token, fp64 ("Linear Attention, Visualized",
+    section "Gated Delta Product (GDP)").
+
+    q [B,H,T,d_k]; k [B,H,T,n_h,d_k]; v [B,H,T,n_h,d_v]; beta [B,H,T,n_h];
+    g [B,H,T] (one log-decay per real token); S0 [B,H,d_v,d_k] or None.
+    Returns (o [B,H,T,d_v], S_T [B,H,d_v,d_k]) as float64.
+    """
+    q, k, v, g, beta = map(_f32, (q, k, v, g, beta))
+    B, H, T, dk = q.shape
+    nh = k.shape[3]
+    dv = v.shape[-1]
+    assert k.shape == (B, H, T, nh, dk) and v.shape == (B, H, T, nh, dv)
+    assert beta.shape == (B, H, T, nh) and g.shape == (B, H, T)
+    s0 = None
+    if S0 is not None:
+        s0 = np.ascontiguousarray(S0, dtype=np.float64)
+        assert s0.shape == (B, H, dv, dk)
+    o = np.empty((B, H, T, dv), dtype=np.float64)
+    S = np.empty((B, H, dv, dk), dtype=np.float64)
+    rc = _load().oracle_gdp_forward(B * H, T, nh, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                    _ptr(s0), _ptr(o), _ptr(S), int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_gdp_forward failed ({rc})")
+    return o, S
+
+
+def gdp_as_virtual_gdn(q, k, v, g, beta):
+    """The mapping of section "GDP as GDN over a virtual sequence".
+
+    Real token t and substep j (both 1-based on the page) become virtual step
+    m = n_h (t - 1) + j, carrying (k, v, beta)_{t,j}; the decay a_t sits on the
+    first substep (a = 1, i.e. log-decay 0, on the others) and the query q_t on
+    the last (zero query on the others).  The GDN outputs to keep are those of
+    virtual steps m = t n_h, i.e. indices n_h - 1, 2 n_h - 1, ... (0-based).
+
+    Inputs as ``gdp_forward``; returns (q~, k~, v~, g~, beta~) of GDN shapes over
+    T n_h steps and the 0-based indices of the kept outputs.
+    """
+    q, k, v, g, beta = map(_f32, (q, k, v, g, beta))
+    B, H, T, nh, dk = k.shape
+    dv = v.shape[-1]
+    kt = k.reshape(B, H, T * nh, dk)
+    vt = v.reshape(B, H, T * nh, dv)
+    bt = beta.reshape(B, H, T * nh)
+    gt = np.zeros((B, H, T, nh), dtype=np.float32)
+    gt[..., 0] = g
+    qt = np.zeros((B, H, T, nh, dk), dtype=np.float32)
+    qt[..., nh - 1, :] = q
+    keep = np.arange(T) * nh + (nh - 1)
+    return qt.reshape(B, H, T * nh, dk), kt, vt, gt.reshape(B, H, T * nh), bt, keep
 
 
 from .chunked import chunked_forward, chunk_transform  # noqa: E402,F401

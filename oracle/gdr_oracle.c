@@ -145,6 +145,83 @@ int oracle_gdr_decode_step(long NH, int dk, int dv, int gate,
     return failed ? -2 : 0;
 }
 
+/*
+ * Gated Delta Product, token by token, in the page's own (row-vector) notation:
+ * "Linear Attention, Visualized", section "Gated Delta Product (GDP)".
+ *
+ * The page keeps the state as P = S^T in R^{d_k x d_v} (rows = key channels).  Each real
+ * token t carries n_h substeps j with their own k_{t,j}, v_{t,j}, beta_{t,j}; with
+ *     A_{t,j} = I - beta_{t,j} k_{t,j}^T k_{t,j}      (d_k x d_k, formed explicitly here)
+ *     X_{t,j} = beta_{t,j} k_{t,j}^T v_{t,j}          (d_k x d_v)
+ * the token update is
+ *     P_{t,0} = a_t P_{t-1},   P_{t,j} = A_{t,j} P_{t,j-1} + X_{t,j} (j = 1..n_h),
+ *     P_t = P_{t,n_h},         o_t = q_t P_t.
+ * The decay acts once, before the first substep; the query reads after the last.
+ *
+ * Layouts (row-major, contiguous):
+ *   q [BH][T][d_k]   k [BH][T][n_h][d_k]   v [BH][T][n_h][d_v]   beta [BH][T][n_h]
+ *   g [BH][T] (log-decay, a_t = exp(g_t))
+ *   S0, S_final [BH][d_v][d_k] (double; the library's S = P^T), S0 may be NULL
+ *   o [BH][T][d_v] (double)
+ * Returns 0 on success, -1 on bad arguments, -2 on allocation failure.
+ */
+int oracle_gdp_forward(long BH, long T, int nh, int dk, int dv,
+                       const float *q, const float *k, const float *v,
+                       const float *g, const float *beta, const double *S0,
+                       double *o, double *S_final, int nthreads)
+{
+    if (BH < 0 || T < 0 || nh <= 0 || dk <= 0 || dv <= 0 || !S_final) return -1;
+    if (T > 0 && (!q || !k || !v || !g || !beta || !o)) return -1;
+    int failed = 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : failed)
+#endif
+    for (long bh = 0; bh < BH; ++bh) {
+        double *P = (double *)malloc(sizeof(double) * (size_t)dk * dv);   /* P[c][r]  */
+        double *Pn = (double *)malloc(sizeof(double) * (size_t)dk * dv);
+        double *A = (double *)malloc(sizeof(double) * (size_t)dk * dk);   /* A[c][c'] */
+        if (!P || !Pn || !A) { free(P); free(Pn); free(A); failed |= 1; continue; }
+        double *Sf = S_final + bh * (long)dv * dk;
+        for (int c = 0; c < dk; ++c)
+            for (int r = 0; r < dv; ++r)
+                P[c * dv + r] = S0 ? S0[bh * (long)dv * dk + (long)r * dk + c] : 0.0;
+        for (long t = 0; t < T; ++t) {
+            const long tok = bh * T + t;
+            /* P_{t,0} = a_t P_{t-1} */
+            const double a = exp((double)g[tok]);
+            for (int i = 0; i < dk * dv; ++i) P[i] *= a;
+            for (int jj = 0; jj < nh; ++jj) {
+                const long sub = tok * nh + jj;
+                const float *kk = k + sub * dk, *vv = v + sub * dv;
+                const double b = (double)beta[sub];
+                /* A_{t,j} = I - b k^T k */
+                for (int c = 0; c < dk; ++c)
+                    for (int c2 = 0; c2 < dk; ++c2)
+                        A[c * dk + c2] = (c == c2 ? 1.0 : 0.0) - b * (double)kk[c] * (double)kk[c2];
+                /* P <- A P + b k^T v */
+                for (int c = 0; c < dk; ++c)
+                    for (int r = 0; r < dv; ++r) {
+                        double acc = b * (double)kk[c] * (double)vv[r];
+                        for (int c2 = 0; c2 < dk; ++c2) acc += A[c * dk + c2] * P[c2 * dv + r];
+                        Pn[c * dv + r] = acc;
+                    }
+                double *sw = P; P = Pn; Pn = sw;
+            }
+            /* o_t = q_t P_t */
+            for (int r = 0; r < dv; ++r) {
+                double acc = 0.0;
+                for (int c = 0; c < dk; ++c) acc += (double)q[tok * dk + c] * P[c * dv + r];
+                o[tok * dv + r] = acc;
+            }
+        }
+        for (int c = 0; c < dk; ++c)
+            for (int r = 0; r < dv; ++r) Sf[(long)r * dk + c] = P[c * dv + r];
+        free(P); free(Pn); free(A);
+    }
+    return failed ? -2 : 0;
+}
+
 int oracle_max_threads(void)
 {
 #ifdef _OPENMP
