@@ -28,7 +28,7 @@ sys.path.insert(0, os.path.join(ROOT, "tests"))
 
 PEAK_MFMA_F16 = 2500.0  # TFLOP/s, MI355X dense fp16/bf16
 PEAK_HBM = 8000.0       # GB/s, MI355X HBM3E
-CHUNK_KERNEL = "chunk_fwd_pc_kernel<128>"
+CHUNK_KERNEL = "chunk_fwd_pc_kernel<128, false>"
 CHUNK_SOURCE = os.path.join(ROOT, "gated_delta_rule_15_amd", "csrc", "chunk_fwd_pc.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "chunk_fwd_pc_gdn_bf16_B4_H16_T4096_traffic.json")
 COPY_BYTES = 256 << 20  # calibration copy for the HBM byte counters
@@ -83,15 +83,17 @@ def to_dev(torch, a, bf16=False):
     return t.to(torch.bfloat16) if bf16 else t
 
 
-def time_chunk(torch, gdr, sets, steps, warmup):
-    """Per-launch HIP-event durations of chunk_fwd, alternating input sets."""
-    outs = [torch.empty_like(s["v"]) for s in sets]
+def time_chunk(torch, gdr, sets, steps, warmup, fn=None):
+    """Per-launch HIP-event durations of chunk_fwd (or ``fn``, same signature), alternating
+    input sets."""
+    fn = gdr.chunk_fwd if fn is None else fn
+    outs = [torch.empty(s["o_shape"], dtype=torch.bfloat16, device="cuda") for s in sets]
     fin = [torch.empty(s["S_shape"], dtype=torch.float32, device="cuda") for s in sets]
 
     def launch(i):
         s = sets[i % len(sets)]
-        gdr.chunk_fwd(s["q"], s["k"], s["v"], s["g"], s["beta"], s["S0"], out=outs[i % len(sets)],
-                      final_state=fin[i % len(sets)])
+        fn(s["q"], s["k"], s["v"], s["g"], s["beta"], s["S0"], out=outs[i % len(sets)],
+           final_state=fin[i % len(sets)])
 
     for i in range(warmup):
         launch(i)
@@ -115,7 +117,8 @@ def make_chunk_sets(torch, gdr_synth, w, nsets=2):
         sets.append({"q": to_dev(torch, x["q"], True), "k": to_dev(torch, x["k"], True),
                      "v": to_dev(torch, x["v"], True), "g": to_dev(torch, x["g"]), "beta": to_dev(torch, x["beta"]),
                      "S0": None if x["S0"] is None else to_dev(torch, x["S0"]),
-                     "S_shape": (w.B, w.H, w.d_v, w.d_k), "host": x if salt == 0 else None})
+                     "S_shape": (w.B, w.H, w.d_v, w.d_k), "o_shape": (w.B, w.H, w.T, w.d_v),
+                     "host": x if salt == 0 else None})
     return sets
 
 
@@ -146,6 +149,39 @@ def bench_decode(torch, gdr, gdr_synth, steps=64):
             "tokens_per_s": round(w.B / (ms.mean() * 1e-3), 1),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM, 4), "traffic": None, "bytes_per_step": nbytes}}
+
+
+def bench_gdp(torch, gdr, gdr_synth, steps=10):
+    """Gated Delta Product forward on B=4, H=16, T=2048, n_h=2, d=128 (4096 substeps per
+    sequence).  Algorithmic work is that of the chunked GDN over the T n_h virtual steps;
+    bytes: q, g and o per token, k, v and beta per substep, the final state."""
+    w = gdr_synth.WORKLOADS[6]
+    sets = make_chunk_sets(torch, gdr_synth, w, nsets=2)
+    ms, med, _, o, S = time_chunk(torch, gdr, sets, steps, 2, fn=gdr.gdp_chunk_fwd)
+    Tv = w.T * w.nh
+    flops = chunk_flops(w.B, w.H, Tv, w.d_k, w.d_v)
+    nbytes = (w.B * w.H * (w.T * (2 * w.d_k + 2 * w.d_v + 4) + Tv * (2 * w.d_k + 2 * w.d_v + 4))
+              + w.B * w.H * w.d_k * w.d_v * 4)
+    # parity on one sampled sequence (GDN over the virtual sequence, the CPU-pinned oracle route)
+    import oracle
+    from parity import err_bf16_out, err_literal
+    x = sets[0]["host"]
+    sub = {k: x[k][:1, :1] for k in ("q", "k", "v", "g", "beta")}
+    qt, kt, vt, gt, bt, keep = oracle.gdp_as_virtual_gdn(sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"])
+    o_ref, S_ref = oracle.recurrent_forward(qt, kt, vt, gt, bt)
+    res = {"workload": "gdp_bf16: Gated Delta Product B=4 H=16 T=2048 n_h=2 d_k=d_v=128 bf16, zero S0",
+           "kernel": "chunk_fwd_pc_kernel<128, true>", "ms_per_call": round(ms, 4),
+           "ms_per_call_median": round(med, 4),
+           "tokens_per_s": round(w.B * w.T / (ms * 1e-3), 1),
+           "substeps_per_s": round(w.B * Tv / (ms * 1e-3), 1),
+           "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_MFMA_F16, 4),
+           "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM, 4),
+           "flops_per_launch": flops, "bytes_per_launch": nbytes,
+           "parity_sampled": {"heads_checked": 1,
+                              "e_o": round(err_bf16_out(o[:1, :1].float().cpu().numpy().astype(np.float64),
+                                                        o_ref[:, :, keep]), 6),
+                              "e_S": round(err_literal(S[:1, :1].cpu().numpy().astype(np.float64), S_ref), 6)}}
+    return res
 
 
 def cpu_baseline(w, host_inputs, max_heads=None):
@@ -261,6 +297,7 @@ def main():
             "mfma_frac": round(f3 / (m3 * 1e-3) / 1e12 / PEAK_MFMA_F16, 4),
             "hbm_frac": round(b3 / (m3 * 1e-3) / 1e9 / PEAK_HBM, 4)}
         del sets3
+        result["gdp"] = bench_gdp(torch, gdr, gdr_synth)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(w, sets[0]["host"])
     print(json.dumps(result))

@@ -37,12 +37,24 @@
 // through ds_read_b64_tr_b16, which hands lane i of each 16-lane group element (i & 3) of
 // the 4-element rows addressed by lanes (i >> 2) + 4e, e = 0..3; reading channel columns
 // pperm(16t + 4(i & 3)) gives S^T's permuted row order.
+//
+// Gated Delta Product ("Linear Attention, Visualized", sections "Gated Delta Product (GDP)"
+// and "GDP as GDN over a virtual sequence"): the VIRT instantiation runs the same chain over
+// the T n_h virtual steps m = n_h t + j of a GDP sequence (0-based t, j).  Keys, values and
+// betas are stored per substep, so they already form the virtual sequence.  The query, the
+// log-decay and the output are stored per real token: step m reads q_t only when
+// j = n_h - 1 and g_t only when j = 0, and writes o only when j = n_h - 1.  On the other
+// steps the buffer offset is set past the end of the real-token buffer, so the load returns
+// zero (a zero query; log-decay 0, i.e. a = 1) and the store is dropped.
 #include "chunk_common.h"
 
 namespace gdr {
 
 struct PcArgs {
-    int64_t T;
+    int64_t T;         // steps per sequence (virtual steps T_real * nh for the VIRT kernel)
+    int64_t Treal;     // tokens per sequence of q, g and o (= T unless VIRT)
+    uint32_t nh;       // substeps per token (VIRT)
+    uint32_t nh_magic; // ceil(2^32 / nh): m / nh = umulhi(m, nh_magic) for m < 2^23 (VIRT)
     int dv;
     int ntiles;  // d_v / 32
     const uint16_t* q;
@@ -98,7 +110,7 @@ struct PcLds {
     static_assert((oAt0 | oAt1 | oSm | oVt | oNt0 | oNt1 | oXd0 | oXd1 | oNd | oOt) % 16 == 0, "alignment");
 };
 
-template <int DK>
+template <int DK, bool VIRT>
 __global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {
     using L = PcLds<DK>;
     constexpr int C = kChunk;
@@ -130,12 +142,16 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {
     const int dv0 = (vi % a.ntiles) * 32;
     const int64_t T = a.T;
     const int DV = a.dv;
-    const auto rq = make_rsrc(a.q + bh * T * DK, (uint32_t)(T * DK * 2));
+    const int64_t Tr = VIRT ? a.Treal : T;  // rows of q, g and o per sequence
+    const uint32_t qbytes = (uint32_t)(Tr * DK * 2), gbytes = (uint32_t)(Tr * 4), obytes = (uint32_t)(Tr * DV * 2);
+    const auto rq = make_rsrc(a.q + bh * Tr * DK, qbytes);
     const auto rk = make_rsrc(a.k + bh * T * DK, (uint32_t)(T * DK * 2));
     const auto rv = make_rsrc(a.v + bh * T * DV, (uint32_t)(T * DV * 2));
-    const auto rg = make_rsrc(a.g + bh * T, (uint32_t)(T * 4));
+    const auto rg = make_rsrc(a.g + bh * Tr, gbytes);
     const auto rb = make_rsrc(a.beta + bh * T, (uint32_t)(T * 4));
-    const auto ro = make_rsrc(a.o + bh * T * DV, (uint32_t)(T * DV * 2));
+    const auto ro = make_rsrc(a.o + bh * Tr * DV, obytes);
+    // virtual step m -> (real token, substep) of a Gated Delta Product sequence
+    auto vtok = [&](uint32_t m) { return __umulhi(m, a.nh_magic); };
     const int dvc = dv0 + 16 * w;  // consumer's first value channel
     const int64_t nC = (T + C - 1) / C;
 
@@ -201,13 +217,23 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {
         const uint32_t t0 = (uint32_t)(cs_ * C);
         const int idx = pt + 256 * u, row = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
         const uint32_t off = ((t0 + row) * DK + col) * 2;
+        uint32_t offq = off;
+        if constexpr (VIRT) {  // q_t on the last substep of token t, zero elsewhere
+            const uint32_t m = t0 + row, tr = vtok(m);
+            offq = m - tr * a.nh == a.nh - 1 ? (tr * DK + col) * 2 : qbytes;
+        }
         setu4(oKR + 4 * u, bld16(rk, off));
-        setu4(oQR + 4 * u, bld16(rq, off));
+        setu4(oQR + 4 * u, bld16(rq, offq));
         if (u == 0) {
             const uint32_t tv = (uint32_t)(cv_ * C);
             setu4(oVR, bld16(rv, ((tv + (pt >> 2)) * DV + dv0 + (pt & 3) * 8) * 2));
             if (w == 0) {
-                cr[oGR] = __float_as_uint(bld4(rg, (t0 + l) * 4));
+                uint32_t offg = (t0 + l) * 4;
+                if constexpr (VIRT) {  // log-decay g_t on the first substep, 0 elsewhere
+                    const uint32_t m = t0 + l, tr = vtok(m);
+                    offg = m - tr * a.nh == 0 ? tr * 4 : gbytes;
+                }
+                cr[oGR] = __float_as_uint(bld4(rg, offg));
                 cr[oGR + 1] = __float_as_uint(bld4(rb, (t0 + l) * 4));
             }
         }
@@ -585,7 +611,12 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {
                 const _Float16* rp = Ot + (d + (j >> 2)) * L::LDO + tb + 4 * (j & 3);
                 const uint2 lo = __builtin_bit_cast(uint2, ldtr(rp));
                 const uint2 hi = __builtin_bit_cast(uint2, ldtr(rp + 4 * L::LDO));
-                bst16(ro, ((uint32_t)(cc * C + tb + j) * DV + dv0 + d) * 2, uint4{lo.x, lo.y, hi.x, hi.y});
+                uint32_t offo = ((uint32_t)(cc * C + tb + j) * DV + dv0 + d) * 2;
+                if constexpr (VIRT) {  // only the last substep of a token has an output
+                    const uint32_t m = (uint32_t)(cc * C + tb + j), tr = vtok(m);
+                    offo = m - tr * a.nh == a.nh - 1 ? (tr * DV + dv0 + d) * 2 : obytes;
+                }
+                bst16(ro, offo, uint4{lo.x, lo.y, hi.x, hi.y});
             }
         }
         // The consumer is done with K, Q of chunk cc (= cs mod 2) and with V of cc.
@@ -601,10 +632,10 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {
     }
 }
 
-template <int DK>
+template <int DK, bool VIRT>
 static hipError_t launch_pc(const PcArgs& a, int64_t nwg, hipStream_t st) {
     using L = PcLds<DK>;
-    auto kern = chunk_fwd_pc_kernel<DK>;
+    auto kern = chunk_fwd_pc_kernel<DK, VIRT>;
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -616,11 +647,16 @@ static hipError_t launch_pc(const PcArgs& a, int64_t nwg, hipStream_t st) {
     return hipGetLastError();
 }
 
-hipError_t chunk_fwd_pc_dispatch(int64_t BH, int64_t T, int dk, int dv, const void* q, const void* k, const void* v,
-                                 const float* g, const float* beta, const float* S0, void* o, float* Sf,
-                                 hipStream_t st) {
+// T counts real tokens; nh > 1 runs a Gated Delta Product over the T * nh virtual steps
+// (k, v, beta hold T * nh rows per sequence; q, g, o hold T).
+hipError_t chunk_fwd_pc_dispatch(int64_t BH, int64_t T, int nh, int dk, int dv, const void* q, const void* k,
+                                 const void* v, const float* g, const float* beta, const float* S0, void* o,
+                                 float* Sf, hipStream_t st) {
     PcArgs a;
-    a.T = T;
+    a.T = T * nh;
+    a.Treal = T;
+    a.nh = (uint32_t)nh;
+    a.nh_magic = nh > 1 ? (uint32_t)(((uint64_t(1) << 32) + nh - 1) / nh) : 0u;
     a.dv = dv;
     a.ntiles = dv / 32;
     a.q = static_cast<const uint16_t*>(q);
@@ -632,8 +668,12 @@ hipError_t chunk_fwd_pc_dispatch(int64_t BH, int64_t T, int dk, int dv, const vo
     a.o = static_cast<uint16_t*>(o);
     a.Sf = Sf;
     const int64_t nwg = BH * a.ntiles;
-    if (dk == 128) return launch_pc<128>(a, nwg, st);
-    return launch_pc<64>(a, nwg, st);
+    if (nh > 1) {
+        if (dk == 128) return launch_pc<128, true>(a, nwg, st);
+        return launch_pc<64, true>(a, nwg, st);
+    }
+    if (dk == 128) return launch_pc<128, false>(a, nwg, st);
+    return launch_pc<64, false>(a, nwg, st);
 }
 
 }  // namespace gdr

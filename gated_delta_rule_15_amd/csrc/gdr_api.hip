@@ -9,9 +9,9 @@ namespace gdr {
 hipError_t chunk_fwd_dispatch(int64_t BH, int64_t T, int dk, int dv, bool bf16, bool channel, const void* q,
                               const void* k, const void* v, const float* g, const float* beta, const float* S0,
                               void* o, float* Sf, hipStream_t st);
-hipError_t chunk_fwd_pc_dispatch(int64_t BH, int64_t T, int dk, int dv, const void* q, const void* k, const void* v,
-                                 const float* g, const float* beta, const float* S0, void* o, float* Sf,
-                                 hipStream_t st);
+hipError_t chunk_fwd_pc_dispatch(int64_t BH, int64_t T, int nh, int dk, int dv, const void* q, const void* k,
+                                 const void* v, const float* g, const float* beta, const float* S0, void* o,
+                                 float* Sf, hipStream_t st);
 hipError_t chunk_kda_dispatch(int64_t BH, int64_t T, int dk, int dv, const void* q, const void* k, const void* v,
                               const float* g, const float* beta, const float* S0, void* o, float* Sf, hipStream_t st);
 hipError_t decode_dispatch(int64_t NH, int dk, int dv, bool bf16, bool channel, const void* q, const void* k,
@@ -24,6 +24,8 @@ constexpr int kVersion = 10000 * 0 + 100 * 1 + 0;
 constexpr int64_t kMaxGrid = 0x7fffffff;
 // The kernels address one sequence with 32-bit byte offsets: T * d * 4 stays below 2^32.
 constexpr int64_t kMaxT = int64_t(1) << 22;
+// Substeps per token of the Gated Delta Product forward.
+constexpr int kMaxNh = 16;
 
 bool mul_ok(int64_t a, int64_t b, int64_t* out) {
     if (a < 0 || b < 0) return false;
@@ -97,11 +99,45 @@ gdr_status gdr_chunk_fwd(int64_t B, int64_t H, int64_t T, int d_k, int d_v, int 
         e = gdr::chunk_kda_dispatch(BH, T, d_k, d_v, q, k, v, g, beta, initial_state, o, final_state,
                                     static_cast<hipStream_t>(stream));
     else if (io_dtype == GDR_BF16)  // fp16-MFMA producer/consumer kernel
-        e = gdr::chunk_fwd_pc_dispatch(BH, T, d_k, d_v, q, k, v, g, beta, initial_state, o, final_state,
+        e = gdr::chunk_fwd_pc_dispatch(BH, T, 1, d_k, d_v, q, k, v, g, beta, initial_state, o, final_state,
                                        static_cast<hipStream_t>(stream));
     else  // fp32 operands throughout
         e = gdr::chunk_fwd_dispatch(BH, T, d_k, d_v, false, gate == GDR_GATE_CHANNEL, q, k, v, g, beta,
                                     initial_state, o, final_state, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+}
+
+gdr_status gdr_gdp_chunk_fwd(int64_t B, int64_t H, int64_t T, int n_h, int d_k, int d_v, int io_dtype,
+                             const void* q, const void* k, const void* v, const float* g, const float* beta,
+                             const float* initial_state, void* o, float* final_state, void* stream) {
+    if (B < 0 || H < 0 || T < 0 || n_h < 1) return GDR_ERR_INVALID_ARG;
+    gdr_status s = check_common(d_k, d_v, io_dtype, GDR_GATE_SCALAR);
+    if (s != GDR_OK) return s;
+    if (n_h > kMaxNh) return GDR_ERR_SHAPE;
+    int64_t BH, BHT, BHTN, nq, nk, nv, no, nstate;
+    if (!mul_ok(B, H, &BH) || !mul_ok(BH, T, &BHT) || !mul_ok(BHT, n_h, &BHTN) || !mul_ok(BHT, d_k, &nq) ||
+        !mul_ok(BHTN, d_k, &nk) || !mul_ok(BHTN, d_v, &nv) || !mul_ok(BHT, d_v, &no) ||
+        !mul_ok(BH, (int64_t)d_k * d_v, &nstate) || !mul_ok(nk, 4, &nk) || !mul_ok(nv, 4, &nv) ||
+        !mul_ok(nstate, 4, &nstate))
+        return GDR_ERR_SHAPE;
+    if (T * n_h > kMaxT) return GDR_ERR_SHAPE;  // T <= kMaxT here, so the product fits
+    if (BHT > 0 && (!q || !k || !v || !g || !beta || !o)) return GDR_ERR_INVALID_ARG;
+    if (io_dtype != GDR_BF16) return GDR_ERR_UNSUPPORTED;
+    // o must not overlap an input; the final state may alias the initial state exactly.
+    const int64_t obytes = no * 2, qbytes = nq * 2, kbytes = nk / 2, vbytes = nv / 2;
+    if (overlaps(o, obytes, q, qbytes) || overlaps(o, obytes, k, kbytes) || overlaps(o, obytes, v, vbytes) ||
+        overlaps(o, obytes, g, BHT * 4) || overlaps(o, obytes, beta, BHTN * 4) ||
+        overlaps(o, obytes, initial_state, nstate) || overlaps(o, obytes, final_state, nstate))
+        return GDR_ERR_INVALID_ARG;
+    if (final_state && initial_state && final_state != initial_state &&
+        overlaps(final_state, nstate, initial_state, nstate))
+        return GDR_ERR_INVALID_ARG;
+    if (BH == 0) return GDR_OK;
+    int64_t nwg;
+    if (!mul_ok(BH, d_v / 32, &nwg) || nwg > kMaxGrid) return GDR_ERR_SHAPE;
+    if (!final_state && BHT == 0) return GDR_OK;
+    hipError_t e = gdr::chunk_fwd_pc_dispatch(BH, T, n_h, d_k, d_v, q, k, v, g, beta, initial_state, o,
+                                              final_state, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
 }
 

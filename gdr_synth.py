@@ -16,9 +16,9 @@ tensor_index, tensor order q, k, v, beta, g, S0):
 * beta = sigmoid(N(0,1)); the gate is the log-decay g = log(alpha) in float32;
 * the state is always float32.
 
-The five workloads mirror the shapes the pages use for their 1.3B training setup
-(16 heads, d_k = d_v = 128, 4K sequence) plus a per-channel-decay, a long-context
-and a decode shape.  Every array is returned as float32 holding values that are
+The workloads mirror the shapes the pages use for their 1.3B training setup
+(16 heads, d_k = d_v = 128, 4K sequence) plus a per-channel-decay, a long-context,
+a decode and a Gated Delta Product shape (keys, values and betas per substep).  Every array is returned as float32 holding values that are
 exactly representable in the I/O dtype; ``to_bf16_bits`` gives the raw bf16 bit
 pattern for upload.
 """
@@ -48,6 +48,7 @@ class Workload:
     s0_std: float  # 0.0 means a zero initial state
     decode: bool = False
     steps: int = 1
+    nh: int = 1  # substeps per token (Gated Delta Product); 1 = Gated DeltaNet
     note: str = field(default="", compare=False)
 
     @property
@@ -66,6 +67,8 @@ WORKLOADS = {
                 note="long single sequence with carried state"),
     5: Workload(5, "decode", 256, 32, 1, 128, 128, "bf16", "scalar", ("uniform", -0.1, -0.001), 0.02,
                 decode=True, steps=64, note="recurrent decode step, 64 steps"),
+    6: Workload(6, "gdp_bf16", 4, 16, 2048, 128, 128, "bf16", "scalar", ("neg_softplus", 0.05), 0.0,
+                nh=2, note="Gated Delta Product, 2 substeps per token (4096 substeps per sequence)"),
 }
 
 
@@ -122,15 +125,18 @@ def make_inputs(w: Workload, *, B=None, H=None, T=None, salt: int = 0) -> dict:
 
     Returns float32 arrays: q, k [B,H,T,d_k]; v [B,H,T,d_v]; beta [B,H,T];
     g [B,H,T] (scalar gate) or [B,H,T,d_k] (channel gate); S0 [B,H,d_v,d_k] or None.
+    With ``w.nh > 1`` (Gated Delta Product) k, v and beta carry a substep axis:
+    k [B,H,T,n_h,d_k], v [B,H,T,n_h,d_v], beta [B,H,T,n_h]; q and g stay per token.
     """
     B = w.B if B is None else B
     H = w.H if H is None else H
     T = w.T if T is None else T
     dk, dv = w.d_k, w.d_v
+    sub = (B, H, T) if w.nh == 1 else (B, H, T, w.nh)
     q = _rng(w.wid, 0, salt).standard_normal(size=(B, H, T, dk), dtype=np.float32)
-    k = _rng(w.wid, 1, salt).standard_normal(size=(B, H, T, dk), dtype=np.float32)
-    v = _rng(w.wid, 2, salt).standard_normal(size=(B, H, T, dv), dtype=np.float32)
-    beta = _sigmoid(_rng(w.wid, 3, salt).standard_normal(size=(B, H, T), dtype=np.float32))
+    k = _rng(w.wid, 1, salt).standard_normal(size=sub + (dk,), dtype=np.float32)
+    v = _rng(w.wid, 2, salt).standard_normal(size=sub + (dv,), dtype=np.float32)
+    beta = _sigmoid(_rng(w.wid, 3, salt).standard_normal(size=sub, dtype=np.float32))
     gshape = (B, H, T) if w.gate == "scalar" else (B, H, T, dk)
     g = _gate(_rng(w.wid, 4, salt), gshape, w.g_dist)
     S0 = None

@@ -101,6 +101,38 @@ gdr_status gdr_chunk_fwd(int64_t B, int64_t H, int64_t T, int d_k, int d_v,
                          void *o, float *final_state, void *stream);
 
 /*
+ * gdr_gdp_chunk_fwd -- chunkwise forward pass of the Gated Delta Product.
+ *
+ * "Linear Attention, Visualized", section "Gated Delta Product (GDP)": each token t carries
+ * n_h substeps with their own key, value and beta.  The state decays once, by a_t = exp(g_t),
+ * then takes the n_h updates in order,
+ *     S <- S (I - b_{t,j} k_{t,j} k_{t,j}^T) + b_{t,j} v_{t,j} k_{t,j}^T,   j = 1..n_h,
+ * and o_t = S q_t is read after the last one.  Computed, as that page's section "GDP as GDN
+ * over a virtual sequence" describes, by the scalar-gate chunked forward of gdr_chunk_fwd run
+ * over the T * n_h substeps in order (decay on each token's first substep, query and output
+ * on its last), with the same numerics.  n_h = 1 is exactly gdr_chunk_fwd.
+ *
+ *   q              [B, H, T, d_k]         bf16
+ *   k              [B, H, T, n_h, d_k]    bf16
+ *   v              [B, H, T, n_h, d_v]    bf16
+ *   g              [B, H, T]              float32, one log-decay per token
+ *   beta           [B, H, T, n_h]         float32
+ *   initial_state  [B, H, d_v, d_k] float32, or NULL for a zero state
+ *   o              [B, H, T, d_v]         bf16, written (must not alias an input)
+ *   final_state    [B, H, d_v, d_k] float32, written, or NULL; may alias initial_state exactly
+ *
+ * n_h in [1, 16] (n_h < 1: GDR_ERR_INVALID_ARG, n_h > 16: GDR_ERR_SHAPE); T * n_h <= 2^22
+ * (GDR_ERR_SHAPE otherwise); io_dtype must be GDR_BF16 (GDR_F32 returns
+ * GDR_ERR_UNSUPPORTED).  Sizes and every other error as for gdr_chunk_fwd.
+ */
+gdr_status gdr_gdp_chunk_fwd(int64_t B, int64_t H, int64_t T, int n_h, int d_k, int d_v,
+                             int io_dtype,
+                             const void *q, const void *k, const void *v,
+                             const float *g, const float *beta,
+                             const float *initial_state,
+                             void *o, float *final_state, void *stream);
+
+/*
  * gdr_decode_step -- one recurrent token per sequence, state updated in place.
  *
  * One step of the recurrence ("Linear Attention, Visualized", section "Recurrent form",

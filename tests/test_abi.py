@@ -89,6 +89,46 @@ def test_chunk_fwd_empty_batch_is_a_noop(lib):
     assert chunk(lib, H=0, q=None, k=None, v=None, g=None, beta=None, o=None) == OK
 
 
+def gdp(lib, B=1, H=1, T=64, nh=2, dk=128, dv=128, io=0, q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE,
+        s0=None, o=FAKE2, sf=None):
+    return lib.gdr_gdp_chunk_fwd(B, H, T, nh, dk, dv, io, q, k, v, g, beta, s0, o, sf, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), INVALID), (dict(T=-1), INVALID), (dict(nh=0), INVALID), (dict(nh=-3), INVALID),
+    (dict(nh=17), SHAPE), (dict(dk=96), SHAPE), (dict(dv=16), SHAPE), (dict(io=7), DTYPE),
+    (dict(io=1), UNSUP),                                        # bf16 I/O only
+    (dict(q=None), INVALID), (dict(k=None), INVALID), (dict(v=None), INVALID), (dict(g=None), INVALID),
+    (dict(beta=None), INVALID), (dict(o=None), INVALID),
+    (dict(o=FAKE), INVALID),                                    # o overlaps q
+    (dict(T=1 << 21, nh=3), SHAPE),                             # T * n_h above 2^22
+    (dict(T=(1 << 22) + 1, nh=1), SHAPE),
+    (dict(B=1 << 40, H=1 << 30), SHAPE),                        # size overflow
+])
+def test_gdp_chunk_fwd_rejects(lib, kw, status):
+    assert gdp(lib, **kw) == status
+
+
+def test_gdp_chunk_fwd_empty_batch_is_a_noop(lib):
+    assert gdp(lib, B=0) == OK
+    assert gdp(lib, H=0, q=None, k=None, v=None, g=None, beta=None, o=None) == OK
+
+
+def test_gdp_partial_state_overlap_rejected(lib):
+    s = ctypes.c_void_p(0x30000000)
+    assert gdp(lib, s0=s, sf=ctypes.c_void_p(0x30000000 + 4)) == INVALID
+
+
+@pytest.mark.parametrize("nh", range(2, 17))
+def test_virtual_step_division(nh):
+    """The GDP kernel splits virtual step m into (m // n_h, m % n_h) as umulhi(m, ceil(2^32 / n_h)),
+    exact for every m below 2^23 (T * n_h <= 2^22 plus a chunk of overhang)."""
+    import numpy as np
+    magic = np.uint64(((1 << 32) + nh - 1) // nh)
+    m = np.arange(1 << 23, dtype=np.uint64)
+    assert np.array_equal((m * magic) >> np.uint64(32), m // np.uint64(nh))
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(N=-1), INVALID), (dict(dk=32), SHAPE), (dict(dv=100), SHAPE), (dict(io=9), DTYPE),
     (dict(gate=2), INVALID), (dict(q=None), INVALID), (dict(S=None), INVALID), (dict(o=None), INVALID),
@@ -107,6 +147,8 @@ def test_python_binding_refuses_cpu_tensors(lib):
     x = torch.zeros(1, 1, 4, 64)
     with pytest.raises(ValueError):
         gdr.chunk_fwd(x, x, x, torch.zeros(1, 1, 4), torch.zeros(1, 1, 4))
+    with pytest.raises(ValueError):
+        gdr.gdp_chunk_fwd(x, x[:, :, :, None], x[:, :, :, None], torch.zeros(1, 1, 4), torch.zeros(1, 1, 4, 1))
     with pytest.raises(ValueError):
         gdr.decode_step(x[:, :, 0], x[:, :, 0], x[:, :, 0], torch.zeros(1, 1), torch.zeros(1, 1),
                         torch.zeros(1, 1, 64, 64))
