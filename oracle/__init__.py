@@ -16,6 +16,10 @@ Two independent fp64 implementations live here:
   Product (GDP)"), with the explicit n_h-substep update in the page's row
   notation, in C; and ``gdp_as_virtual_gdn``, the input mapping of section
   "GDP as GDN over a virtual sequence" that turns a GDP problem into a GDN one.
+* ``gdn2_forward`` -- Gated DeltaNet-2 token by token ("Gated DeltaNet-2, and the
+  gate that was doing two jobs", section 2 "What decoupling actually means here"):
+  KDA's decay with the scalar beta split into a key-side erase gate and a
+  value-side write gate, in C.
 
 Both are pinned by ``tests/test_oracle_*.py`` against closed forms, limits and
 brute force that do not reuse them.  Parity of every function here is pinned;
@@ -68,6 +72,9 @@ def _load():
             lib.oracle_gdp_forward.argtypes = [ctypes.c_long, ctypes.c_long, ctypes.c_int, ctypes.c_int,
                                                ctypes.c_int, P, P, P, P, P, P, P, P, ctypes.c_int]
             lib.oracle_gdp_forward.restype = ctypes.c_int
+            lib.oracle_gdn2_forward.argtypes = [ctypes.c_long, ctypes.c_long, ctypes.c_int, ctypes.c_int,
+                                                P, P, P, P, P, P, P, P, P, ctypes.c_int]
+            lib.oracle_gdn2_forward.restype = ctypes.c_int
             lib.oracle_max_threads.restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -164,6 +171,29 @@ def gdp_forward(q, k, v, g, beta, S0=None, nthreads: int = 0):
                                     _ptr(s0), _ptr(o), _ptr(S), int(nthreads))
     if rc != 0:
         raise RuntimeError(f"oracle_gdp_forward failed ({rc})")
+    return o, S
+
+
+def gdn2_forward(q, k, v, g, b, w, S0=None, nthreads: int = 0):
+    """Gated DeltaNet-2 token recurrence, fp64.
+
+    q, k, g, b [B,H,T,d_k] (g the per-channel log-decay, b the erase gate); v, w [B,H,T,d_v]
+    (w the write gate); S0 [B,H,d_v,d_k] or None.  Returns (o [B,H,T,d_v], S_T) as float64.
+    """
+    q, k, v, g, b, w = map(_f32, (q, k, v, g, b, w))
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    assert k.shape == g.shape == b.shape == (B, H, T, dk) and w.shape == v.shape == (B, H, T, dv)
+    s0 = None
+    if S0 is not None:
+        s0 = np.ascontiguousarray(S0, dtype=np.float64)
+        assert s0.shape == (B, H, dv, dk)
+    o = np.empty((B, H, T, dv), dtype=np.float64)
+    S = np.empty((B, H, dv, dk), dtype=np.float64)
+    rc = _load().oracle_gdn2_forward(B * H, T, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), _ptr(w),
+                                     _ptr(s0), _ptr(o), _ptr(S), int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_gdn2_forward failed ({rc})")
     return o, S
 
 

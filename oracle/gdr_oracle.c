@@ -222,6 +222,70 @@ int oracle_gdp_forward(long BH, long T, int nh, int dk, int dv,
     return failed ? -2 : 0;
 }
 
+/*
+ * Gated DeltaNet-2, token by token: "Gated DeltaNet-2, and the gate that was doing two jobs"
+ * (aigenapps.com), section 2 "What decoupling actually means here".  The scalar beta of the delta rule is split into a key-side erase gate
+ * b_t in [0,1]^{d_k} and a value-side write gate w_t in [0,1]^{d_v}; with e_t = b_t (.) k_t and
+ * z_t = w_t (.) v_t the page's update (row notation, state P in R^{d_k x d_v}) is
+ *     P_t = (I - k_t e_t^T) D_t P_{t-1} + k_t z_t^T,       D_t = Diag(a_t) (KDA's decay),
+ * i.e. in this file's column convention S = P^T:
+ *     S_t = S_{t-1} D_t (I - e_t k_t^T) + z_t k_t^T.
+ * Steps per token, as that formula orders them:
+ *   1. decay        S <- S D_t              (column c scaled by a_t[c] = exp(g_t[c]))
+ *   2. erase read   p = S e_t               (the decayed state read along e_t)
+ *   3. correction   u = z_t - p
+ *   4. write        S <- S + u k_t^T        (written along k_t)
+ *   5. read         o_t = S q_t
+ * Layouts: q, k, g, b [BH][T][d_k]; v, w [BH][T][d_v]; S0, S_final [BH][d_v][d_k] (double,
+ * S0 may be NULL); o [BH][T][d_v] (double).  Returns 0, -1 on bad arguments, -2 on
+ * allocation failure.
+ */
+int oracle_gdn2_forward(long BH, long T, int dk, int dv,
+                        const float *q, const float *k, const float *v,
+                        const float *g, const float *b, const float *w,
+                        const double *S0, double *o, double *S_final, int nthreads)
+{
+    if (BH < 0 || T < 0 || dk <= 0 || dv <= 0 || !S_final) return -1;
+    if (T > 0 && (!q || !k || !v || !g || !b || !w || !o)) return -1;
+    int failed = 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : failed)
+#endif
+    for (long bh = 0; bh < BH; ++bh) {
+        double *S = S_final + bh * (long)dv * dk;
+        double *u = (double *)malloc(sizeof(double) * (size_t)dv);
+        double *e = (double *)malloc(sizeof(double) * (size_t)dk);
+        if (!u || !e) { free(u); free(e); failed |= 1; continue; }
+        if (S0) memcpy(S, S0 + bh * (long)dv * dk, sizeof(double) * (size_t)dv * dk);
+        else memset(S, 0, sizeof(double) * (size_t)dv * dk);
+        for (long t = 0; t < T; ++t) {
+            const long tok = bh * T + t;
+            const float *qt = q + tok * dk, *kt = k + tok * dk, *gt = g + tok * dk, *bt = b + tok * dk;
+            const float *vt = v + tok * dv, *wt = w + tok * dv;
+            for (int c = 0; c < dk; ++c) {               /* 1. decay */
+                const double a = exp((double)gt[c]);
+                for (int r = 0; r < dv; ++r) S[r * dk + c] *= a;
+            }
+            for (int c = 0; c < dk; ++c) e[c] = (double)bt[c] * (double)kt[c];
+            for (int r = 0; r < dv; ++r) {                /* 2-3. erase read, correction */
+                double p = 0.0;
+                for (int c = 0; c < dk; ++c) p += S[r * dk + c] * e[c];
+                u[r] = (double)wt[r] * (double)vt[r] - p;
+            }
+            for (int r = 0; r < dv; ++r)                  /* 4. write along k */
+                for (int c = 0; c < dk; ++c) S[r * dk + c] += u[r] * (double)kt[c];
+            for (int r = 0; r < dv; ++r) {                /* 5. read */
+                double acc = 0.0;
+                for (int c = 0; c < dk; ++c) acc += S[r * dk + c] * (double)qt[c];
+                o[tok * dv + r] = acc;
+            }
+        }
+        free(u); free(e);
+    }
+    return failed ? -2 : 0;
+}
+
 int oracle_max_threads(void)
 {
 #ifdef _OPENMP
