@@ -2,8 +2,9 @@
 
 Headline: chunk_fwd tokens/s on the GDN bf16 training shape (B=4, H=16, T=4096,
 d_k=d_v=128, chunk 64), with its MFMA and HBM roofline fractions; alongside it the
-decode step's HBM GB/s (256 sequences x 32 heads, d=128, 64 steps on a 512 MiB state)
-and the long-context workload (B=1, H=32, T=65536, carried state).
+decode step's HBM GB/s (256 sequences x 32 heads, d=128, 64 steps on a 512 MiB state),
+the long-context workload (B=1, H=32, T=65536, carried state), the per-channel-gate
+(KDA) workload, the Gated Delta Product and the Gated DeltaNet-2 workloads.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extra]
     python bench.py --pmc-run      # kernels only, for rocprofv3 counter passes
@@ -184,6 +185,56 @@ def bench_gdp(torch, gdr, gdr_synth, steps=10):
     return res
 
 
+def bench_gdn2(torch, gdr, gdr_synth, steps=10):
+    """Gated DeltaNet-2 forward on B=2, H=16, T=8192, d=128 (per-channel decay, erase gate b,
+    write gate w).  Algorithmic flops as the chunked forward; bytes: q, k, v, o in bf16, g and
+    b [T, d_k] and w [T, d_v] in fp32, the final state."""
+    w = gdr_synth.WORKLOADS[7]
+    sets = []
+    for salt in range(2):
+        x = gdr_synth.make_inputs(w, salt=salt)
+        sets.append({kk: to_dev(torch, x[kk], kk in ("q", "k", "v")) for kk in ("q", "k", "v", "g", "b", "w")})
+        sets[-1]["host"] = x if salt == 0 else None
+    outs = [torch.empty((w.B, w.H, w.T, w.d_v), dtype=torch.bfloat16, device="cuda") for _ in sets]
+    fin = [torch.empty((w.B, w.H, w.d_v, w.d_k), dtype=torch.float32, device="cuda") for _ in sets]
+
+    def launch(i):
+        s = sets[i % 2]
+        gdr.gdn2_chunk_fwd(s["q"], s["k"], s["v"], s["g"], s["b"], s["w"], out=outs[i % 2], final_state=fin[i % 2])
+
+    for i in range(2):
+        launch(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record()
+        launch(i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    flops = chunk_flops(w.B, w.H, w.T, w.d_k, w.d_v)
+    n = w.B * w.H * w.T
+    nbytes = n * (2 * w.d_k + 2 * w.d_v) * 2 + n * (2 * w.d_k + w.d_v) * 4 + w.B * w.H * w.d_k * w.d_v * 4
+    import oracle
+    from parity import err_bf16_out, err_literal
+    x = sets[0]["host"]
+    sub = {kk: x[kk][:1, :1] for kk in ("q", "k", "v", "g", "b", "w")}
+    o_ref, S_ref = oracle.gdn2_forward(sub["q"], sub["k"], sub["v"], sub["g"], sub["b"], sub["w"])
+    launch(0)
+    torch.cuda.synchronize()
+    return {"workload": "gdn2_bf16: Gated DeltaNet-2 B=2 H=16 T=8192 d_k=d_v=128 bf16, fp32 g, b [B,H,T,128], "
+                        "w [B,H,T,128], zero S0",
+            "kernel": "chunk_kda_kernel<128, true>", "ms_per_call": round(ms, 4),
+            "tokens_per_s": round(w.B * w.T / (ms * 1e-3), 1),
+            "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_MFMA_F16, 4),
+            "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM, 4),
+            "flops_per_launch": flops, "bytes_per_launch": nbytes,
+            "parity_sampled": {"heads_checked": 1,
+                               "e_o": round(err_bf16_out(outs[0][:1, :1].float().cpu().numpy().astype(np.float64),
+                                                         o_ref), 6),
+                               "e_S": round(err_literal(fin[0][:1, :1].cpu().numpy().astype(np.float64), S_ref), 6)}}
+
+
 def cpu_baseline(w, host_inputs, max_heads=None):
     import oracle
     x = host_inputs
@@ -292,12 +343,13 @@ def main():
         b3 = chunk_bytes(w3.B, w3.H, w3.T, 128, 128, gate_per_channel=True)
         result["kda"] = {
             "workload": "per-channel gate B=2 H=16 T=8192 d=128 bf16, fp32 gate [B,H,T,128]",
-            "kernel": "chunk_kda_kernel<128>", "ms_per_call": round(m3, 4),
+            "kernel": "chunk_kda_kernel<128, false>", "ms_per_call": round(m3, 4),
             "tokens_per_s": round(w3.B * w3.T / (m3 * 1e-3), 1),
             "mfma_frac": round(f3 / (m3 * 1e-3) / 1e12 / PEAK_MFMA_F16, 4),
             "hbm_frac": round(b3 / (m3 * 1e-3) / 1e9 / PEAK_HBM, 4)}
         del sets3
         result["gdp"] = bench_gdp(torch, gdr, gdr_synth)
+        result["gdn2"] = bench_gdn2(torch, gdr, gdr_synth)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(w, sets[0]["host"])
     print(json.dumps(result))

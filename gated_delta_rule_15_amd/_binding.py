@@ -18,7 +18,8 @@ GDR_BF16, GDR_F32 = 0, 1
 GDR_GATE_SCALAR, GDR_GATE_CHANNEL = 0, 1
 
 # every entry point include/gdr.h declares
-EXPORTED_SYMBOLS = ("gdr_version", "gdr_status_string", "gdr_chunk_fwd", "gdr_gdp_chunk_fwd", "gdr_decode_step")
+EXPORTED_SYMBOLS = ("gdr_version", "gdr_status_string", "gdr_chunk_fwd", "gdr_gdp_chunk_fwd", "gdr_gdn2_chunk_fwd",
+                    "gdr_decode_step")
 
 _lock = threading.Lock()
 _lib = None
@@ -48,6 +49,8 @@ def load_library():
         lib.gdr_chunk_fwd.argtypes = [i64, i64, i64, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P]
         lib.gdr_gdp_chunk_fwd.restype = i32
         lib.gdr_gdp_chunk_fwd.argtypes = [i64, i64, i64, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P]
+        lib.gdr_gdn2_chunk_fwd.restype = i32
+        lib.gdr_gdn2_chunk_fwd.argtypes = [i64, i64, i64, i32, i32, i32, P, P, P, P, P, P, P, P, P, P]
         lib.gdr_decode_step.restype = i32
         lib.gdr_decode_step.argtypes = [i64, i64, i32, i32, i32, i32, P, P, P, P, P, P, P, P]
         _lib = lib
@@ -169,6 +172,44 @@ def gdp_chunk_fwd(q, k, v, g, beta, initial_state=None, *, output_final_state=Tr
                                           _stream(stream, dev))
     if st != GDR_OK:
         raise GdrError(st, "gdr_gdp_chunk_fwd")
+    return o, final_state
+
+
+def gdn2_chunk_fwd(q, k, v, g, b, w, initial_state=None, *, output_final_state=True, out=None,
+                   final_state=None, stream=None):
+    """gdr_gdn2_chunk_fwd (Gated DeltaNet-2) on torch tensors.
+
+    q, k [B,H,T,d_k]; v [B,H,T,d_v] (bf16); g [B,H,T,d_k] fp32 (per-channel log-decay);
+    b [B,H,T,d_k] fp32 (erase gate); w [B,H,T,d_v] fp32 (write gate); initial_state
+    [B,H,d_v,d_k] fp32 or None.  Returns (o, final_state); final_state is None when
+    output_final_state is False.
+    """
+    import torch
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("gdn2_chunk_fwd needs GPU tensors")
+    io = _io_dtype(q)
+    _check(q, "q", (B, H, T, dk), q.dtype, dev)
+    _check(k, "k", (B, H, T, dk), q.dtype, dev)
+    _check(v, "v", (B, H, T, dv), q.dtype, dev)
+    _check(g, "g", (B, H, T, dk), torch.float32, dev)
+    _check(b, "b", (B, H, T, dk), torch.float32, dev)
+    _check(w, "w", (B, H, T, dv), torch.float32, dev)
+    if initial_state is not None:
+        _check(initial_state, "initial_state", (B, H, dv, dk), torch.float32, dev)
+    o = torch.empty((B, H, T, dv), dtype=q.dtype, device=dev) if out is None else out
+    _check(o, "out", (B, H, T, dv), q.dtype, dev)
+    if output_final_state and final_state is None:
+        final_state = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+    if final_state is not None:
+        _check(final_state, "final_state", (B, H, dv, dk), torch.float32, dev)
+    st = load_library().gdr_gdn2_chunk_fwd(B, H, T, dk, dv, io, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b),
+                                           _ptr(w), _ptr(initial_state), _ptr(o), _ptr(final_state),
+                                           _stream(stream, dev))
+    if st != GDR_OK:
+        raise GdrError(st, "gdr_gdn2_chunk_fwd")
     return o, final_state
 
 

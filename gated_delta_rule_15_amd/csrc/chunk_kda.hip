@@ -31,6 +31,16 @@
 // four 16x16 diagonal blocks of N, then the state pass on waves 0-1, which applies
 // N^{-1} diag(beta) by blocked forward substitution (as in the scalar kernel).  Loads of
 // chunk c+1 are in flight while chunk c is processed.
+//
+// Gated DeltaNet-2 ("Gated DeltaNet-2, and the gate that was doing two jobs", section 2) is
+// the GD2 instantiation.  The scalar beta is replaced by a key-side erase gate b_t and a
+// value-side write gate w_t: S_t = S_{t-1} D_t (I - e_t k_t^T) + z_t k_t^T, with e = b (.) k
+// and z = w (.) v.  Per chunk, the same derivation gives
+//   L[l][m] = sum_c e_lc k_mc e^{G_lc - G_mc} (m < l),   N = I + L,   Z = N^{-1} R,
+//   R = Z_in - (E (.) e^G) S^T   (Z_in the rows z_l),
+// and O, A and the state update unchanged: only the row operand of N and of the prediction
+// product changes from beta k to e, and the right-hand side from beta v to z.  So the "Kr"
+// copy holds E e^{G - G_start(blk)} (then E e^G), V^T holds z, and beta is not used.
 #include <type_traits>
 
 #include "chunk_common.h"
@@ -48,6 +58,8 @@ struct KdaArgs {
     const uint16_t* v;
     const float* g;  // [.., T, DK]
     const float* beta;
+    const float* eg;  // erase gate b [.., T, DK] (GD2)
+    const float* wg;  // write gate w [.., T, d_v] (GD2)
     const float* S0;
     uint16_t* o;
     float* Sf;
@@ -103,7 +115,7 @@ __device__ __forceinline__ uint2 bld8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return uint2{v[0], v[1]};
 }
 
-template <int DK>
+template <int DK, bool GD2>
 __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
     using L = KdaLds<DK>;
     constexpr int C = kChunk;
@@ -140,7 +152,9 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
     const auto rk = make_rsrc(a.k + bh * T * DK, (uint32_t)(T * DK * 2));
     const auto rv = make_rsrc(a.v + bh * T * DV, (uint32_t)(T * DV * 2));
     const auto rg = make_rsrc(a.g + bh * T * DK, (uint32_t)(T * DK * 4));
-    const auto rb = make_rsrc(a.beta + bh * T, (uint32_t)(T * 4));
+    const auto rb = make_rsrc(GD2 ? nullptr : a.beta + bh * T, GD2 ? 0u : (uint32_t)(T * 4));
+    const auto re = make_rsrc(GD2 ? a.eg + bh * T * DK : nullptr, GD2 ? (uint32_t)(T * DK * 4) : 0u);
+    const auto rw = make_rsrc(GD2 ? a.wg + bh * T * DV : nullptr, GD2 ? (uint32_t)(T * DV * 4) : 0u);
     const auto ro = make_rsrc(a.o + bh * T * DV, (uint32_t)(T * DV * 2));
     const int dvc = dv0 + 16 * w;  // first value channel of consumer wave w (w < 2)
     const int64_t nC = (T + C - 1) / C;
@@ -172,9 +186,9 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
     // half of the wave loads duplicates and stores nothing)
     const int ch2 = 2 * (l % (DK / 2));
     const bool own = 2 * l < DK;
-    float2 gp[16];
+    float2 gp[16], ep[16];  // ep: erase gate b (GD2)
     uint32_t kp[16], qp[16];
-    uint4 vp;
+    uint4 vp, wp0, wp1;     // wp: write gate w of the lane's 8 V values (GD2)
     float bp = 0.0f;
     // token t of the lane's block (g, k, q of its channel pair); t = 0 also brings V, beta.
     // Past the sequence end the loads return zeros (identity tokens).
@@ -184,10 +198,20 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
         gp[t] = float2{__uint_as_float(u.x), __uint_as_float(u.y)};
         kp[t] = __builtin_amdgcn_raw_buffer_load_b32(rk, ((t0 + t) * DK + ch2) * 2, 0, 0);
         qp[t] = __builtin_amdgcn_raw_buffer_load_b32(rq, ((t0 + t) * DK + ch2) * 2, 0, 0);
+        if constexpr (GD2) {
+            const uint2 ue = bld8(re, ((t0 + t) * DK + ch2) * 4);
+            ep[t] = float2{__uint_as_float(ue.x), __uint_as_float(ue.y)};
+        }
         if (t == 0) {
             const uint32_t tc = (uint32_t)(c * C);
-            vp = bld16(rv, ((tc + (tid >> 2)) * DV + dv0 + (tid & 3) * 8) * 2);
-            if (w == 0) bp = bld4(rb, (tc + l) * 4);
+            const uint32_t vidx = (tc + (tid >> 2)) * DV + dv0 + (tid & 3) * 8;
+            vp = bld16(rv, vidx * 2);
+            if constexpr (GD2) {
+                wp0 = bld16(rw, vidx * 4);
+                wp1 = bld16(rw, vidx * 4 + 16);
+            } else {
+                if (w == 0) bp = bld4(rb, (tc + l) * 4);
+            }
         }
     };
     auto issue = [&](int64_t c) {
@@ -201,11 +225,21 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
     // Diagonal-tile operand of block b built afresh in fp32 from the bf16 input (lane row or
     // column j = token 16b + j; the fragment's channels are 32kb + 8g .. +7):
     // x e^{G_loc(tok) - G_loc(8)} for the row side, x e^{G_loc(8) - G_loc(tok)} for the
-    // column side, rounded to bf16.
-    auto diag_bf16 = [&](const __amdgpu_buffer_rsrc_t& rs, int64_t c, int b, int kb, bool row_side) {
+    // column side, rounded to bf16.  With gate set (GD2, row side of N) x is b (.) k.
+    auto diag_bf16 = [&](const __amdgpu_buffer_rsrc_t& rs, int64_t c, int b, int kb, bool row_side, bool gate) {
         const int tok = 16 * b + j, ch = 32 * kb + 8 * g;
-        const uint4 u = bld16(rs, ((uint32_t)(c * C + tok) * DK + ch) * 2);
+        const uint32_t gidx = (uint32_t)(c * C + tok) * DK + ch;
+        const uint4 u = bld16(rs, gidx * 2);
         const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
+        float gb[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) gb[e] = 1.0f;
+        if (gate) {
+            const uint4 b0 = bld16(re, gidx * 4), b1 = bld16(re, gidx * 4 + 16);
+            const uint32_t bw[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) gb[e] = __uint_as_float(bw[e]);
+        }
         const float* gt = Gl + tok * L::LDG + ch;
         const float* gm = Gl + (16 * b + 8) * L::LDG + ch;
         const float4v t0 = ld4f(gt), t1 = ld4f(gt + 4), m0 = ld4f(gm), m1 = ld4f(gm + 4);
@@ -214,7 +248,7 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
         for (int e = 0; e < 8; ++e) {
             const float te = e < 4 ? t0[e] : t1[e - 4], me = e < 4 ? m0[e] : m1[e - 4];
             const float x = __uint_as_float(e & 1 ? (wv[e >> 1] & 0xffff0000u) : (wv[e >> 1] << 16));
-            r[e] = (__bf16)(x * fast_exp(row_side ? te - me : me - te));
+            r[e] = (__bf16)(gb[e] * x * fast_exp(row_side ? te - me : me - te));
         }
         return r;
     };
@@ -266,8 +300,10 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
                     *reinterpret_cast<float2*>(Gl + row * L::LDG + ch2) = float2{G[t][0], G[t][1]};
                     const float k0 = __uint_as_float(kp[t] << 16), k1 = __uint_as_float(kp[t] & 0xffff0000u);
                     const float q0 = __uint_as_float(qp[t] << 16), q1 = __uint_as_float(qp[t] & 0xffff0000u);
+                    // row operand of N and of the prediction: beta k (KDA, beta applied later) or e = b k
+                    const float r0 = GD2 ? ep[t].x * k0 : k0, r1 = GD2 ? ep[t].y * k1 : k1;
                     typedef _Float16 half2v __attribute__((ext_vector_type(2)));
-                    *reinterpret_cast<half2v*>(Kr + row * L::LDK + ch2) = half2v{(_Float16)(k0 * E[t][0]), (_Float16)(k1 * E[t][1])};
+                    *reinterpret_cast<half2v*>(Kr + row * L::LDK + ch2) = half2v{(_Float16)(r0 * E[t][0]), (_Float16)(r1 * E[t][1])};
                     *reinterpret_cast<half2v*>(Qr + row * L::LDK + ch2) = half2v{(_Float16)(q0 * E[t][0]), (_Float16)(q1 * E[t][1])};
                     *reinterpret_cast<half2v*>(Kc + row * L::LDK + ch2) = half2v{(_Float16)(k0 * Ec[t][0]), (_Float16)(k1 * Ec[t][1])};
                 }
@@ -281,14 +317,20 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
             }
             const bool any_unsafe = __any(unsafe);
             if (l == 0) Flag[w] = any_unsafe ? 1 : 0;
-            if (w == 0) FB[l] = bp;
-            // V^T tile, fp32 [channel][token]
+            if (!GD2 && w == 0) FB[l] = bp;
+            // V^T tile, fp32 [channel][token] (GD2: z = w (.) v)
             const int row = tid >> 2, col = (tid & 3) * 8;
             const uint32_t ww[4] = {vp.x, vp.y, vp.z, vp.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                Vt[(col + 2 * e) * L::LDV + row] = __uint_as_float(ww[e] << 16);
-                Vt[(col + 2 * e + 1) * L::LDV + row] = __uint_as_float(ww[e] & 0xffff0000u);
+                float v0 = __uint_as_float(ww[e] << 16), v1 = __uint_as_float(ww[e] & 0xffff0000u);
+                if constexpr (GD2) {
+                    const uint32_t wgt[8] = {wp0.x, wp0.y, wp0.z, wp0.w, wp1.x, wp1.y, wp1.z, wp1.w};
+                    v0 *= __uint_as_float(wgt[2 * e]);
+                    v1 *= __uint_as_float(wgt[2 * e + 1]);
+                }
+                Vt[(col + 2 * e) * L::LDV + row] = v0;
+                Vt[(col + 2 * e + 1) * L::LDV + row] = v1;
             }
         }
         lds_barrier();
@@ -351,7 +393,8 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
                     half8 B = rfrag(Kc, tj, kb);
                     if (cf == 3) {
                         if (fl[ti]) {
-                            mma16_bf16(acc[t], diag_bf16(isQ ? rq : rk, c, ti, kb, true), diag_bf16(rk, c, ti, kb, false));
+                            mma16_bf16(acc[t], diag_bf16(isQ ? rq : rk, c, ti, kb, true, GD2 && !isQ),
+                                       diag_bf16(rk, c, ti, kb, false, false));
                         } else {
                             mma16(acc[t], hmul8(A, hfrag(HMR, ti, kb)), hmul8(B, hfrag(HMC, ti, kb)));
                         }
@@ -364,13 +407,13 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
 #pragma unroll
                 for (int u = NT; u < 16 / NKB; ++u) issue_tok(cn, kb * (16 / NKB) + u);
             }
-            // epilogue: beta of the row for N, causal masks on the diagonal
+            // epilogue: beta of the row for N (not for GD2: e carries the gate), causal masks
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
                 const int ti = ti_[h][t], tj = tj_[h][t];
                 const int m = 16 * tj + j, l0 = 16 * ti + 4 * g;
                 float v[4];
-                if (!isQ) {
+                if (!isQ && !GD2) {
                     const float4v bl = ld4f(FB + l0);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) v[r] = acc[t][r] * bl[r];
@@ -474,7 +517,7 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
 #pragma unroll
             for (int ti = 0; ti < 4; ++ti) {
                 vv[ti] = ld4f(Vt + (16 * w + j) * L::LDV + 16 * ti + 4 * g);
-                bt[ti] = ld4f(FB + 16 * ti + 4 * g);
+                bt[ti] = GD2 ? float4v{1.0f, 1.0f, 1.0f, 1.0f} : ld4f(FB + 16 * ti + 4 * g);
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -514,7 +557,7 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
 #pragma unroll
             for (int t = 0; t < NST; ++t) ed[t] = ld4f(FE + pperm(16 * t + 4 * g));
             __builtin_amdgcn_sched_barrier(0);
-            // R' = diag(beta) (V - P_K);  Z = N^{-1} R' by blocked forward substitution
+            // R' = diag(beta) (V - P_K) (GD2: z - P_E);  Z = N^{-1} R' by blocked forward substitution
             float4v Rb[4];
 #pragma unroll
             for (int ti = 0; ti < 4; ++ti)
@@ -592,10 +635,10 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
     }
 }
 
-template <int DK>
+template <int DK, bool GD2>
 static hipError_t launch_kda(const KdaArgs& a, int64_t nwg, hipStream_t st) {
     using L = KdaLds<DK>;
-    auto kern = chunk_kda_kernel<DK>;
+    auto kern = chunk_kda_kernel<DK, GD2>;
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -619,12 +662,38 @@ hipError_t chunk_kda_dispatch(int64_t BH, int64_t T, int dk, int dv, const void*
     a.v = static_cast<const uint16_t*>(v);
     a.g = g;
     a.beta = beta;
+    a.eg = nullptr;
+    a.wg = nullptr;
     a.S0 = S0;
     a.o = static_cast<uint16_t*>(o);
     a.Sf = Sf;
     const int64_t nwg = BH * a.ntiles;
-    if (dk == 128) return launch_kda<128>(a, nwg, st);
-    return launch_kda<64>(a, nwg, st);
+    if (dk == 128) return launch_kda<128, false>(a, nwg, st);
+    return launch_kda<64, false>(a, nwg, st);
+}
+
+// Gated DeltaNet-2: per-channel log-decay g [.., T, dk], erase gate b [.., T, dk], write gate
+// w [.., T, dv], all fp32.
+hipError_t chunk_gdn2_dispatch(int64_t BH, int64_t T, int dk, int dv, const void* q, const void* k, const void* v,
+                               const float* g, const float* b, const float* w, const float* S0, void* o, float* Sf,
+                               hipStream_t st) {
+    KdaArgs a;
+    a.T = T;
+    a.dv = dv;
+    a.ntiles = dv / 32;
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k);
+    a.v = static_cast<const uint16_t*>(v);
+    a.g = g;
+    a.beta = nullptr;
+    a.eg = b;
+    a.wg = w;
+    a.S0 = S0;
+    a.o = static_cast<uint16_t*>(o);
+    a.Sf = Sf;
+    const int64_t nwg = BH * a.ntiles;
+    if (dk == 128) return launch_kda<128, true>(a, nwg, st);
+    return launch_kda<64, true>(a, nwg, st);
 }
 
 }  // namespace gdr

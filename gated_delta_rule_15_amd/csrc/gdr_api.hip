@@ -14,6 +14,9 @@ hipError_t chunk_fwd_pc_dispatch(int64_t BH, int64_t T, int nh, int dk, int dv, 
                                  float* Sf, hipStream_t st);
 hipError_t chunk_kda_dispatch(int64_t BH, int64_t T, int dk, int dv, const void* q, const void* k, const void* v,
                               const float* g, const float* beta, const float* S0, void* o, float* Sf, hipStream_t st);
+hipError_t chunk_gdn2_dispatch(int64_t BH, int64_t T, int dk, int dv, const void* q, const void* k, const void* v,
+                               const float* g, const float* b, const float* w, const float* S0, void* o, float* Sf,
+                               hipStream_t st);
 hipError_t decode_dispatch(int64_t NH, int dk, int dv, bool bf16, bool channel, const void* q, const void* k,
                            const void* v, const float* g, const float* beta, float* S, void* o, hipStream_t st);
 }  // namespace gdr
@@ -138,6 +141,39 @@ gdr_status gdr_gdp_chunk_fwd(int64_t B, int64_t H, int64_t T, int n_h, int d_k, 
     if (!final_state && BHT == 0) return GDR_OK;
     hipError_t e = gdr::chunk_fwd_pc_dispatch(BH, T, n_h, d_k, d_v, q, k, v, g, beta, initial_state, o,
                                               final_state, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+}
+
+gdr_status gdr_gdn2_chunk_fwd(int64_t B, int64_t H, int64_t T, int d_k, int d_v, int io_dtype, const void* q,
+                              const void* k, const void* v, const float* g, const float* b, const float* w,
+                              const float* initial_state, void* o, float* final_state, void* stream) {
+    if (B < 0 || H < 0 || T < 0) return GDR_ERR_INVALID_ARG;
+    gdr_status s = check_common(d_k, d_v, io_dtype, GDR_GATE_CHANNEL);
+    if (s != GDR_OK) return s;
+    // the fp32 write gate is addressed with 32-bit byte offsets, one chunk past the end included
+    if (T > kMaxT || (T + 64) * d_v > (int64_t(1) << 30)) return GDR_ERR_SHAPE;
+    int64_t BH, BHT, nq, nv, nstate;
+    if (!mul_ok(B, H, &BH) || !mul_ok(BH, T, &BHT) || !mul_ok(BHT, d_k, &nq) || !mul_ok(BHT, d_v, &nv) ||
+        !mul_ok(BH, (int64_t)d_k * d_v, &nstate) || !mul_ok(nq, 4, &nq) || !mul_ok(nv, 4, &nv) ||
+        !mul_ok(nstate, 4, &nstate))
+        return GDR_ERR_SHAPE;
+    if (BHT > 0 && (!q || !k || !v || !g || !b || !w || !o)) return GDR_ERR_INVALID_ARG;
+    if (io_dtype != GDR_BF16) return GDR_ERR_UNSUPPORTED;
+    // o must not overlap an input; the final state may alias the initial state exactly.
+    const int64_t obytes = nv / 2, qbytes = nq / 2;
+    if (overlaps(o, obytes, q, qbytes) || overlaps(o, obytes, k, qbytes) || overlaps(o, obytes, v, obytes) ||
+        overlaps(o, obytes, g, nq) || overlaps(o, obytes, b, nq) || overlaps(o, obytes, w, nv) ||
+        overlaps(o, obytes, initial_state, nstate) || overlaps(o, obytes, final_state, nstate))
+        return GDR_ERR_INVALID_ARG;
+    if (final_state && initial_state && final_state != initial_state &&
+        overlaps(final_state, nstate, initial_state, nstate))
+        return GDR_ERR_INVALID_ARG;
+    if (BH == 0) return GDR_OK;
+    int64_t nwg;
+    if (!mul_ok(BH, d_v / 32, &nwg) || nwg > kMaxGrid) return GDR_ERR_SHAPE;
+    if (!final_state && BHT == 0) return GDR_OK;
+    hipError_t e = gdr::chunk_gdn2_dispatch(BH, T, d_k, d_v, q, k, v, g, b, w, initial_state, o, final_state,
+                                            static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
 }
 

@@ -14,6 +14,8 @@ tensor_index, tensor order q, k, v, beta, g, S0):
   Transitions..." explainer and the video-delta-rule post, Preliminaries);
 * q, k, v are then rounded to the I/O dtype with round-to-nearest-even;
 * beta = sigmoid(N(0,1)); the gate is the log-decay g = log(alpha) in float32;
+* Gated DeltaNet-2 workloads add an erase gate b [B,H,T,d_k] and a write gate
+  w [B,H,T,d_v], each sigmoid(N(0,1)) (tensor indices 6 and 7; beta is then unused);
 * the state is always float32.
 
 The workloads mirror the shapes the pages use for their 1.3B training setup
@@ -43,7 +45,7 @@ class Workload:
     d_k: int
     d_v: int
     io_dtype: str  # "f32" or "bf16"
-    gate: str  # "scalar" or "channel"
+    gate: str  # "scalar", "channel" or "gdn2" (channel decay, erase gate b and write gate w)
     g_dist: tuple  # ("uniform", lo, hi) or ("neg_softplus", scale)
     s0_std: float  # 0.0 means a zero initial state
     decode: bool = False
@@ -69,6 +71,8 @@ WORKLOADS = {
                 decode=True, steps=64, note="recurrent decode step, 64 steps"),
     6: Workload(6, "gdp_bf16", 4, 16, 2048, 128, 128, "bf16", "scalar", ("neg_softplus", 0.05), 0.0,
                 nh=2, note="Gated Delta Product, 2 substeps per token (4096 substeps per sequence)"),
+    7: Workload(7, "gdn2_bf16", 2, 16, 8192, 128, 128, "bf16", "gdn2", ("neg_softplus", 0.05), 0.0,
+                note="Gated DeltaNet-2: per-channel decay, erase gate b and write gate w"),
 }
 
 
@@ -139,6 +143,10 @@ def make_inputs(w: Workload, *, B=None, H=None, T=None, salt: int = 0) -> dict:
     beta = _sigmoid(_rng(w.wid, 3, salt).standard_normal(size=sub, dtype=np.float32))
     gshape = (B, H, T) if w.gate == "scalar" else (B, H, T, dk)
     g = _gate(_rng(w.wid, 4, salt), gshape, w.g_dist)
+    extra = {}
+    if w.gate == "gdn2":  # erase gate b [B,H,T,d_k], write gate w [B,H,T,d_v], both sigmoid(N(0,1))
+        extra["b"] = _sigmoid(_rng(w.wid, 6, salt).standard_normal(size=(B, H, T, dk), dtype=np.float32))
+        extra["w"] = _sigmoid(_rng(w.wid, 7, salt).standard_normal(size=(B, H, T, dv), dtype=np.float32))
     S0 = None
     if w.s0_std > 0.0:
         S0 = (_rng(w.wid, 5, salt).standard_normal(size=(B, H, dv, dk), dtype=np.float32)
@@ -146,7 +154,9 @@ def make_inputs(w: Workload, *, B=None, H=None, T=None, salt: int = 0) -> dict:
     q = _cast_io(_l2_normalise(q), w.io_dtype)
     k = _cast_io(_l2_normalise(k), w.io_dtype)
     v = _cast_io(v, w.io_dtype)
-    return {"q": q, "k": k, "v": v, "beta": beta, "g": g, "S0": S0}
+    out = {"q": q, "k": k, "v": v, "beta": beta, "g": g, "S0": S0}
+    out.update(extra)
+    return out
 
 
 def make_decode_inputs(w: Workload, step: int, *, N=None, H=None) -> dict:

@@ -133,6 +133,39 @@ gdr_status gdr_gdp_chunk_fwd(int64_t B, int64_t H, int64_t T, int n_h, int d_k, 
                              void *o, float *final_state, void *stream);
 
 /*
+ * gdr_gdn2_chunk_fwd -- chunkwise forward pass of Gated DeltaNet-2.
+ *
+ * "Gated DeltaNet-2, and the gate that was doing two jobs" (aigenapps.com), section 2: the
+ * scalar beta of the delta rule splits into a key-side erase gate b_t and a value-side write
+ * gate w_t, with KDA's per-channel decay a_t = exp(g_t):
+ *     e_t = b_t (.) k_t,   z_t = w_t (.) v_t,
+ *     S_t = S_{t-1} Diag(a_t) (I - e_t k_t^T) + z_t k_t^T,     o_t = S_t q_t
+ * (the page's P_t = (I - k_t e_t^T) D_t P_{t-1} + k_t z_t^T for P = S^T): the decayed state is
+ * read along e_t and the correction z_t - S Diag(a_t) e_t is written along k_t.  b = w = beta
+ * on every channel is exactly gdr_chunk_fwd with GDR_GATE_CHANNEL.  Computed by the
+ * per-channel-gate chunk kernel with the same numerics and the same decay range limits.
+ *
+ *   q, k           [B, H, T, d_k]  bf16
+ *   v              [B, H, T, d_v]  bf16
+ *   g              [B, H, T, d_k]  float32, per-channel log-decay
+ *   b              [B, H, T, d_k]  float32, erase gate (the page uses [0, 1]; not clamped)
+ *   w              [B, H, T, d_v]  float32, write gate (the page uses [0, 1]; not clamped)
+ *   initial_state  [B, H, d_v, d_k] float32, or NULL for a zero state
+ *   o              [B, H, T, d_v]  bf16, written (must not alias an input)
+ *   final_state    [B, H, d_v, d_k] float32, written, or NULL; may alias initial_state exactly
+ *
+ * io_dtype must be GDR_BF16 (GDR_F32 returns GDR_ERR_UNSUPPORTED).  (T + 64) * d_v <= 2^30
+ * (the fp32 write gate's 32-bit offsets; GDR_ERR_SHAPE otherwise).  Sizes, the rest of the T
+ * range and every other error as for gdr_chunk_fwd.
+ */
+gdr_status gdr_gdn2_chunk_fwd(int64_t B, int64_t H, int64_t T, int d_k, int d_v,
+                              int io_dtype,
+                              const void *q, const void *k, const void *v,
+                              const float *g, const float *b, const float *w,
+                              const float *initial_state,
+                              void *o, float *final_state, void *stream);
+
+/*
  * gdr_decode_step -- one recurrent token per sequence, state updated in place.
  *
  * One step of the recurrence ("Linear Attention, Visualized", section "Recurrent form",

@@ -119,6 +119,30 @@ def test_gdp_partial_state_overlap_rejected(lib):
     assert gdp(lib, s0=s, sf=ctypes.c_void_p(0x30000000 + 4)) == INVALID
 
 
+def gdn2(lib, B=1, H=1, T=64, dk=128, dv=128, io=0, q=FAKE, k=FAKE, v=FAKE, g=FAKE, b=FAKE, w=FAKE,
+         s0=None, o=FAKE2, sf=None):
+    return lib.gdr_gdn2_chunk_fwd(B, H, T, dk, dv, io, q, k, v, g, b, w, s0, o, sf, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), INVALID), (dict(T=-1), INVALID), (dict(dk=96), SHAPE), (dict(dv=48), SHAPE),
+    (dict(io=5), DTYPE), (dict(io=1), UNSUP),
+    (dict(q=None), INVALID), (dict(k=None), INVALID), (dict(v=None), INVALID), (dict(g=None), INVALID),
+    (dict(b=None), INVALID), (dict(w=None), INVALID), (dict(o=None), INVALID),
+    (dict(o=FAKE), INVALID),                                    # o overlaps q
+    (dict(T=(1 << 22) + 1), SHAPE),
+    (dict(T=1 << 22, dv=256), SHAPE),                           # fp32 write gate past 32-bit offsets
+    (dict(B=1 << 40, H=1 << 30), SHAPE),
+])
+def test_gdn2_chunk_fwd_rejects(lib, kw, status):
+    assert gdn2(lib, **kw) == status
+
+
+def test_gdn2_chunk_fwd_empty_batch_is_a_noop(lib):
+    assert gdn2(lib, B=0) == OK
+    assert gdn2(lib, H=0, q=None, k=None, v=None, g=None, b=None, w=None, o=None) == OK
+
+
 @pytest.mark.parametrize("nh", range(2, 17))
 def test_virtual_step_division(nh):
     """The GDP kernel splits virtual step m into (m // n_h, m % n_h) as umulhi(m, ceil(2^32 / n_h)),
@@ -149,6 +173,8 @@ def test_python_binding_refuses_cpu_tensors(lib):
         gdr.chunk_fwd(x, x, x, torch.zeros(1, 1, 4), torch.zeros(1, 1, 4))
     with pytest.raises(ValueError):
         gdr.gdp_chunk_fwd(x, x[:, :, :, None], x[:, :, :, None], torch.zeros(1, 1, 4), torch.zeros(1, 1, 4, 1))
+    with pytest.raises(ValueError):
+        gdr.gdn2_chunk_fwd(x, x, x, x, x, x)
     with pytest.raises(ValueError):
         gdr.decode_step(x[:, :, 0], x[:, :, 0], x[:, :, 0], torch.zeros(1, 1), torch.zeros(1, 1),
                         torch.zeros(1, 1, 64, 64))

@@ -1,0 +1,169 @@
+"""GPU parity of the Gated DeltaNet-2 forward (gdr_gdn2_chunk_fwd) against the fp64 oracle.
+
+Every case compares element by element with ``oracle.gdn2_forward`` (the token recurrence
+of "Gated DeltaNet-2, and the gate that was doing two jobs", section 2), except the
+full-size workload (B=2, H=16, T=8192, d=128), which runs in the launch configuration the
+bench times and is compared on sampled sequences.  Bars: tests/parity.py.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import gdr_synth
+import oracle
+from parity import TOL_BF16, err_bf16_out, report
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import gated_delta_rule_15_amd as gdr  # noqa: E402
+
+DEV = torch.device("cuda:0")
+
+
+def dev(a, bf16=False):
+    if a is None:
+        return None
+    t = torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    return t.to(torch.bfloat16) if bf16 else t
+
+
+def host(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def variant(**kw):
+    return dataclasses.replace(gdr_synth.WORKLOADS[7], **kw)
+
+
+def run(x, S0=None, **kw):
+    o, S = gdr.gdn2_chunk_fwd(dev(x["q"], True), dev(x["k"], True), dev(x["v"], True), dev(x["g"]), dev(x["b"]),
+                              dev(x["w"]), dev(S0), **kw)
+    torch.cuda.synchronize()
+    return o, S
+
+
+def ref(x, S0=None):
+    return oracle.gdn2_forward(x["q"], x["k"], x["v"], x["g"], x["b"], x["w"], S0)
+
+
+def check(name, o, S, o_ref, S_ref):
+    eo, es, msg = report(name, host(o), o_ref, None if S is None else host(S), S_ref, True)
+    print(msg)
+    assert eo <= TOL_BF16 and es <= TOL_BF16, msg
+
+
+def state(seed, B, H, dv, dk, std=0.05):
+    return (np.random.default_rng(seed).standard_normal((B, H, dv, dk)) * std).astype(np.float32)
+
+
+@pytest.mark.parametrize("T", [1, 37, 64, 65, 200])
+@pytest.mark.parametrize("dk,dv", [(128, 128), (128, 32), (64, 64), (128, 256), (64, 96)])
+@pytest.mark.parametrize("with_s0", [False, True])
+def test_gdn2_small(T, dk, dv, with_s0):
+    x = gdr_synth.make_inputs(variant(d_k=dk, d_v=dv), B=2, H=2, T=T)
+    S0 = state(T, 2, 2, dv, dk) if with_s0 else None
+    o, S = run(x, S0)
+    o_ref, S_ref = ref(x, S0)
+    check(f"gdn2 T={T} dk={dk} dv={dv} s0={with_s0}", o, S, o_ref, S_ref)
+
+
+@pytest.mark.parametrize("lo,hi", [(-3.0, -0.5), (-8.0, -0.01)])
+def test_gdn2_strong_decay(lo, hi):
+    """Per-channel decays beyond the fp16 range of the in-block factors: the diagonal tiles
+    take the bf16 path, which rebuilds e = b (.) k from the inputs."""
+    x = gdr_synth.make_inputs(variant(g_dist=("uniform", lo, hi)), B=1, H=2, T=200)
+    x["g"][..., ::3] = x["g"][..., ::3] * 0.01
+    o, S = run(x)
+    o_ref, S_ref = ref(x)
+    check(f"gdn2 strong decay U({lo},{hi})", o, S, o_ref, S_ref)
+
+
+@pytest.mark.parametrize("case", ["no_erase", "no_write", "full_erase", "erase_up_to_2"])
+def test_gdn2_gate_extremes(case):
+    x = gdr_synth.make_inputs(variant(), B=1, H=2, T=150)
+    if case == "no_erase":
+        x["b"][:] = 0.0
+    elif case == "no_write":
+        x["w"][:] = 0.0
+    elif case == "full_erase":
+        x["b"][:] = 1.0
+    else:
+        x["b"] = (2.0 * x["b"]).astype(np.float32)
+    S0 = state(5, 1, 2, 128, 128, std=0.5)
+    o, S = run(x, S0)
+    o_ref, S_ref = ref(x, S0)
+    check(f"gdn2 {case}", o, S, o_ref, S_ref)
+
+
+def test_gdn2_equal_gates_match_kda():
+    """b = w = beta on every channel is KDA (the page's collapse): both kernels against the
+    oracle, and against each other."""
+    x = gdr_synth.make_inputs(gdr_synth.WORKLOADS[3], B=1, H=2, T=300)
+    x["b"] = np.repeat(x["beta"][..., None], 128, axis=-1).copy()
+    x["w"] = np.repeat(x["beta"][..., None], 128, axis=-1).copy()
+    o2, S2 = run(x)
+    o1, S1 = gdr.chunk_fwd(dev(x["q"], True), dev(x["k"], True), dev(x["v"], True), dev(x["g"]), dev(x["beta"]))
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.recurrent_forward(x["q"], x["k"], x["v"], x["g"], x["beta"])
+    check("gdn2 with b = w = beta", o2, S2, o_ref, S_ref)
+    check("kda", o1, S1, o_ref, S_ref)
+    # both outputs are rounded to bf16: charge their difference only beyond that rounding
+    assert err_bf16_out(host(o2), host(o1)) <= TOL_BF16
+
+
+def test_gdn2_full_size_sampled():
+    """B=2, H=16, T=8192, d=128 bf16; 2 of the 32 sequences checked."""
+    w = gdr_synth.WORKLOADS[7]
+    x = gdr_synth.make_inputs(w)
+    o, S = run(x)
+    pick = np.array([5, 26])
+    bi, hi = pick // w.H, pick % w.H
+    sub = {kk: x[kk][bi, hi][None] for kk in ("q", "k", "v", "g", "b", "w")}
+    o_ref, S_ref = ref(sub)
+    o_s = o[torch.from_numpy(bi), torch.from_numpy(hi)][None]
+    S_s = S[torch.from_numpy(bi), torch.from_numpy(hi)][None]
+    check("gdn2 full size (2 sampled heads)", o_s, S_s, o_ref, S_ref)
+
+
+def test_gdn2_carried_state_split():
+    x = gdr_synth.make_inputs(variant(), B=1, H=2, T=300)
+    S0 = state(7, 1, 2, 128, 128, std=0.02)
+    o_ref, S_ref = ref(x, S0)
+    t0 = 140
+    a = {kk: vv[:, :, :t0] for kk, vv in x.items() if vv is not None}
+    b = {kk: vv[:, :, t0:] for kk, vv in x.items() if vv is not None}
+    oa, Sa = run(a, S0)
+    ob, Sb = gdr.gdn2_chunk_fwd(dev(b["q"], True), dev(b["k"], True), dev(b["v"], True), dev(b["g"]), dev(b["b"]),
+                                dev(b["w"]), Sa)
+    torch.cuda.synchronize()
+    check(f"gdn2 split at {t0}", torch.cat([oa, ob], dim=2), Sb, o_ref, S_ref)
+
+
+def test_gdn2_final_state_may_alias_initial_state():
+    x = gdr_synth.make_inputs(variant(), B=1, H=2, T=130)
+    S0 = state(8, 1, 2, 128, 128)
+    s = dev(S0)
+    o, _ = gdr.gdn2_chunk_fwd(dev(x["q"], True), dev(x["k"], True), dev(x["v"], True), dev(x["g"]), dev(x["b"]),
+                              dev(x["w"]), s, final_state=s)
+    torch.cuda.synchronize()
+    o_ref, S_ref = ref(x, S0)
+    check("gdn2 aliased state", o, s, o_ref, S_ref)
+
+
+def test_gdn2_empty_sequence_copies_state():
+    x = gdr_synth.make_inputs(variant(), B=1, H=2, T=0)
+    S0 = state(9, 1, 2, 128, 128)
+    o, S = run(x, S0)
+    assert o.numel() == 0 and torch.equal(S.cpu(), torch.from_numpy(S0))
+
+
+def test_gdn2_deterministic():
+    x = gdr_synth.make_inputs(variant(), B=1, H=3, T=190)
+    o1, S1 = run(x)
+    o2, S2 = run(x)
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
