@@ -159,6 +159,36 @@ def make_inputs(w: Workload, *, B=None, H=None, T=None, salt: int = 0) -> dict:
     return out
 
 
+def make_raw_inputs(w: Workload, *, B=None, H=None, T=None, salt: int = 0, head_params: str = "plain") -> dict:
+    """The raw draws that ``make_inputs`` turns into q, k, beta and g, for a scalar-gate
+    workload with the ("neg_softplus", scale) gate: q_raw, k_raw [B,H,T,d_k] (N(0,1),
+    rounded to the I/O dtype but NOT normalised), v [B,H,T,d_v], dt and beta_logit [B,H,T]
+    (N(0,1)), and per-head A_log, dt_bias [H].  The same generators as ``make_inputs``.
+
+    head_params "plain": A_log = log(scale), dt_bias = 0, so that -exp(A_log) softplus(dt +
+    dt_bias) is the workload's g; "varied": A_log = log(scale) + U(-1, 1) and dt_bias ~
+    N(0, 0.5^2) per head (tensor index 8).
+    """
+    assert w.gate == "scalar" and w.g_dist[0] == "neg_softplus" and w.nh == 1
+    B = w.B if B is None else B
+    H = w.H if H is None else H
+    T = w.T if T is None else T
+    dk, dv = w.d_k, w.d_v
+    q = _rng(w.wid, 0, salt).standard_normal(size=(B, H, T, dk), dtype=np.float32)
+    k = _rng(w.wid, 1, salt).standard_normal(size=(B, H, T, dk), dtype=np.float32)
+    v = _rng(w.wid, 2, salt).standard_normal(size=(B, H, T, dv), dtype=np.float32)
+    beta_logit = _rng(w.wid, 3, salt).standard_normal(size=(B, H, T), dtype=np.float32)
+    dt = _rng(w.wid, 4, salt).standard_normal(size=(B, H, T), dtype=np.float32)
+    A_log = np.full(H, np.log(w.g_dist[1]), dtype=np.float32)
+    dt_bias = np.zeros(H, dtype=np.float32)
+    if head_params == "varied":
+        r = _rng(w.wid, 8, salt)
+        A_log = (A_log + r.uniform(-1.0, 1.0, size=H)).astype(np.float32)
+        dt_bias = (0.5 * r.standard_normal(size=H)).astype(np.float32)
+    return {"q_raw": _cast_io(q, w.io_dtype), "k_raw": _cast_io(k, w.io_dtype), "v": _cast_io(v, w.io_dtype),
+            "dt": dt, "beta_logit": beta_logit, "A_log": A_log, "dt_bias": dt_bias}
+
+
 def make_decode_inputs(w: Workload, step: int, *, N=None, H=None) -> dict:
     """Fresh per-step decode inputs (q, k [N,H,d_k]; v [N,H,d_v]; beta, g [N,H]
     or g [N,H,d_k]).  Step ``s`` uses salt ``s + 1``; the initial state comes

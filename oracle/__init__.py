@@ -16,6 +16,10 @@ Two independent fp64 implementations live here:
   Product (GDP)"), with the explicit n_h-substep update in the page's row
   notation, in C; and ``gdp_as_virtual_gdn``, the input mapping of section
   "GDP as GDN over a virtual sequence" that turns a GDP problem into a GDN one.
+* ``prepare_inputs`` -- the step upstream of the path: unit-norm q and k (the
+  pages' convention), beta = sigmoid(logit) in (0, 1), and Mamba-2's decay gate
+  g = log a = -exp(A_log) softplus(dt + dt_bias) ("Linear Attention, Visualized",
+  "Optional: Constructing the decay gate"), in numpy fp64.
 * ``gdn2_forward`` -- Gated DeltaNet-2 token by token ("Gated DeltaNet-2, and the
   gate that was doing two jobs", section 2 "What decoupling actually means here"):
   KDA's decay with the scalar beta split into a key-side erase gate and a
@@ -195,6 +199,39 @@ def gdn2_forward(q, k, v, g, b, w, S0=None, nthreads: int = 0):
     if rc != 0:
         raise RuntimeError(f"oracle_gdn2_forward failed ({rc})")
     return o, S
+
+
+def prepare_inputs(q_raw, k_raw, dt, A_log, dt_bias, beta_logit, eps: float = 1e-6):
+    """Inputs of the gated delta rule from raw projections, fp64.
+
+    * q = q_raw / max(||q_raw||_2, eps), k likewise, per token over d_k: the pages take
+      keys (and queries) L2-normalised by convention ("Gated DeltaNet: Householder
+      Transitions...", video-delta-rule post, Preliminaries); eps only keeps a zero vector
+      at zero.
+    * beta = 1 / (1 + exp(-beta_logit)): the pages require 0 < beta <= 1; the logistic map
+      is the plain way to get there.
+    * g = log a = -exp(A_log[h]) * softplus(dt + dt_bias[h]), softplus(x) = log(1 + e^x):
+      "Linear Attention, Visualized", section "Mamba-2: input-dependent scalar decay",
+      "Optional: Constructing the decay gate" (a_t = exp(-lambda Delta_t), lambda =
+      e^{A_log}, Delta_t = softplus(dt_t + b_Delta)).
+
+    q_raw, k_raw [B,H,T,d_k]; dt, beta_logit [B,H,T]; A_log, dt_bias [H].
+    Returns (q, k, g, beta) as float64.
+    """
+    q_raw, k_raw, dt, beta_logit = (np.asarray(x, dtype=np.float64) for x in (q_raw, k_raw, dt, beta_logit))
+    A_log = np.asarray(A_log, dtype=np.float64)
+    dt_bias = np.asarray(dt_bias, dtype=np.float64)
+
+    def unit(x):
+        n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+        return x / np.maximum(n, eps)
+
+    lam = np.exp(A_log)[None, :, None]
+    z = dt + dt_bias[None, :, None]
+    softplus = np.logaddexp(0.0, z)
+    g = -lam * softplus
+    beta = 1.0 / (1.0 + np.exp(-beta_logit))
+    return unit(q_raw), unit(k_raw), g, beta
 
 
 def gdp_as_virtual_gdn(q, k, v, g, beta):
