@@ -4,7 +4,8 @@ Headline: chunk_fwd tokens/s on the GDN bf16 training shape (B=4, H=16, T=4096,
 d_k=d_v=128, chunk 64), with its MFMA and HBM roofline fractions; alongside it the
 decode step's HBM GB/s (256 sequences x 32 heads, d=128, 64 steps on a 512 MiB state),
 the long-context workload (B=1, H=32, T=65536, carried state), the per-channel-gate
-(KDA) workload, the Gated Delta Product and the Gated DeltaNet-2 workloads.
+(KDA) workload, the Gated Delta Product and the Gated DeltaNet-2 workloads, and the
+headline workload from raw projections with the input preparation fused in.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extra]
     python bench.py --pmc-run      # kernels only, for rocprofv3 counter passes
@@ -29,7 +30,7 @@ sys.path.insert(0, os.path.join(ROOT, "tests"))
 
 PEAK_MFMA_F16 = 2500.0  # TFLOP/s, MI355X dense fp16/bf16
 PEAK_HBM = 8000.0       # GB/s, MI355X HBM3E
-CHUNK_KERNEL = "chunk_fwd_pc_kernel<128, false>"
+CHUNK_KERNEL = "chunk_fwd_pc_kernel<128, 0>"
 CHUNK_SOURCE = os.path.join(ROOT, "gated_delta_rule_15_amd", "csrc", "chunk_fwd_pc.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "chunk_fwd_pc_gdn_bf16_B4_H16_T4096_traffic.json")
 COPY_BYTES = 256 << 20  # calibration copy for the HBM byte counters
@@ -171,7 +172,7 @@ def bench_gdp(torch, gdr, gdr_synth, steps=10):
     qt, kt, vt, gt, bt, keep = oracle.gdp_as_virtual_gdn(sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"])
     o_ref, S_ref = oracle.recurrent_forward(qt, kt, vt, gt, bt)
     res = {"workload": "gdp_bf16: Gated Delta Product B=4 H=16 T=2048 n_h=2 d_k=d_v=128 bf16, zero S0",
-           "kernel": "chunk_fwd_pc_kernel<128, true>", "ms_per_call": round(ms, 4),
+           "kernel": "chunk_fwd_pc_kernel<128, 1>", "ms_per_call": round(ms, 4),
            "ms_per_call_median": round(med, 4),
            "tokens_per_s": round(w.B * w.T / (ms * 1e-3), 1),
            "substeps_per_s": round(w.B * Tv / (ms * 1e-3), 1),
@@ -183,6 +184,44 @@ def bench_gdp(torch, gdr, gdr_synth, steps=10):
                                                         o_ref[:, :, keep]), 6),
                               "e_S": round(err_literal(S[:1, :1].cpu().numpy().astype(np.float64), S_ref), 6)}}
     return res
+
+
+def bench_prep(torch, gdr, gdr_synth, steps=20):
+    """The headline workload from raw projections (gdr_chunk_fwd_fused_prep): q, k
+    normalised, beta and the Mamba-2 gate formed inside the chunk kernel.  Reported beside
+    the HBM floor of doing the same preparation as a separate pass (read q_raw, k_raw, dt,
+    beta_logit; write q, k, g, beta)."""
+    w = gdr_synth.WORKLOADS[2]
+    sets = []
+    for salt in range(2):
+        r = gdr_synth.make_raw_inputs(w, salt=salt, head_params="varied")
+        sets.append({kk: to_dev(torch, r[kk], kk in ("q_raw", "k_raw", "v")) for kk in r})
+    outs = [torch.empty((w.B, w.H, w.T, w.d_v), dtype=torch.bfloat16, device="cuda") for _ in sets]
+    fin = [torch.empty((w.B, w.H, w.d_v, w.d_k), dtype=torch.float32, device="cuda") for _ in sets]
+
+    def launch(i):
+        s = sets[i % 2]
+        gdr.chunk_fwd_fused_prep(s["q_raw"], s["k_raw"], s["v"], s["dt"], s["A_log"], s["dt_bias"], s["beta_logit"],
+                                 out=outs[i % 2], final_state=fin[i % 2])
+
+    for i in range(2):
+        launch(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record()
+        launch(i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    n = w.B * w.H * w.T
+    separate_pass = n * w.d_k * 2 * 2 * 2 + n * 4 * 4   # q, k read and written (bf16); dt, logit read, g, beta written
+    flops = chunk_flops(w.B, w.H, w.T, w.d_k, w.d_v)
+    return {"workload": "gdn_bf16_train from raw projections: B=4 H=16 T=4096 d=128, per-head A_log, dt_bias",
+            "kernel": "chunk_fwd_pc_kernel<128, 2>", "ms_per_call": round(ms, 4),
+            "tokens_per_s": round(w.B * w.T / (ms * 1e-3), 1),
+            "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_MFMA_F16, 4),
+            "separate_prep_pass_hbm_floor_ms": round(separate_pass / (PEAK_HBM * 1e9) * 1e3, 4)}
 
 
 def bench_gdn2(torch, gdr, gdr_synth, steps=10):
@@ -350,6 +389,7 @@ def main():
         del sets3
         result["gdp"] = bench_gdp(torch, gdr, gdr_synth)
         result["gdn2"] = bench_gdn2(torch, gdr, gdr_synth)
+        result["fused_prep"] = bench_prep(torch, gdr, gdr_synth)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(w, sets[0]["host"])
     print(json.dumps(result))

@@ -18,8 +18,8 @@ GDR_BF16, GDR_F32 = 0, 1
 GDR_GATE_SCALAR, GDR_GATE_CHANNEL = 0, 1
 
 # every entry point include/gdr.h declares
-EXPORTED_SYMBOLS = ("gdr_version", "gdr_status_string", "gdr_chunk_fwd", "gdr_gdp_chunk_fwd", "gdr_gdn2_chunk_fwd",
-                    "gdr_decode_step")
+EXPORTED_SYMBOLS = ("gdr_version", "gdr_status_string", "gdr_chunk_fwd", "gdr_chunk_fwd_fused_prep",
+                    "gdr_gdp_chunk_fwd", "gdr_gdn2_chunk_fwd", "gdr_decode_step")
 
 _lock = threading.Lock()
 _lib = None
@@ -47,6 +47,8 @@ def load_library():
         lib.gdr_status_string.argtypes = [i32]
         lib.gdr_chunk_fwd.restype = i32
         lib.gdr_chunk_fwd.argtypes = [i64, i64, i64, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P]
+        lib.gdr_chunk_fwd_fused_prep.restype = i32
+        lib.gdr_chunk_fwd_fused_prep.argtypes = [i64, i64, i64, i32, i32, i32, P, P, P, P, P, P, P, P, P, P, P]
         lib.gdr_gdp_chunk_fwd.restype = i32
         lib.gdr_gdp_chunk_fwd.argtypes = [i64, i64, i64, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P]
         lib.gdr_gdn2_chunk_fwd.restype = i32
@@ -133,6 +135,46 @@ def chunk_fwd(q, k, v, g, beta, initial_state=None, *, output_final_state=True, 
                                       _ptr(initial_state), _ptr(o), _ptr(final_state), _stream(stream, dev))
     if st != GDR_OK:
         raise GdrError(st, "gdr_chunk_fwd")
+    return o, final_state
+
+
+def chunk_fwd_fused_prep(q_raw, k_raw, v, dt, A_log, dt_bias, beta_logit, initial_state=None, *,
+                         output_final_state=True, out=None, final_state=None, stream=None):
+    """gdr_chunk_fwd_fused_prep on torch tensors: the scalar-gate chunked forward from raw
+    projections (q, k normalised, beta = sigmoid(beta_logit), g = -exp(A_log) softplus(dt +
+    dt_bias) inside the kernel).
+
+    q_raw, k_raw [B,H,T,d_k], v [B,H,T,d_v] (bf16); dt, beta_logit [B,H,T] fp32;
+    A_log, dt_bias [H] fp32; initial_state [B,H,d_v,d_k] fp32 or None.
+    Returns (o, final_state); final_state is None when output_final_state is False.
+    """
+    import torch
+    B, H, T, dk = q_raw.shape
+    dv = v.shape[-1]
+    dev = q_raw.device
+    if dev.type != "cuda":
+        raise ValueError("chunk_fwd_fused_prep needs GPU tensors")
+    io = _io_dtype(q_raw)
+    _check(k_raw, "k_raw", (B, H, T, dk), q_raw.dtype, dev)
+    _check(q_raw, "q_raw", (B, H, T, dk), q_raw.dtype, dev)
+    _check(v, "v", (B, H, T, dv), q_raw.dtype, dev)
+    _check(dt, "dt", (B, H, T), torch.float32, dev)
+    _check(beta_logit, "beta_logit", (B, H, T), torch.float32, dev)
+    _check(A_log, "A_log", (H,), torch.float32, dev)
+    _check(dt_bias, "dt_bias", (H,), torch.float32, dev)
+    if initial_state is not None:
+        _check(initial_state, "initial_state", (B, H, dv, dk), torch.float32, dev)
+    o = torch.empty((B, H, T, dv), dtype=q_raw.dtype, device=dev) if out is None else out
+    _check(o, "out", (B, H, T, dv), q_raw.dtype, dev)
+    if output_final_state and final_state is None:
+        final_state = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+    if final_state is not None:
+        _check(final_state, "final_state", (B, H, dv, dk), torch.float32, dev)
+    st = load_library().gdr_chunk_fwd_fused_prep(B, H, T, dk, dv, io, _ptr(q_raw), _ptr(k_raw), _ptr(v), _ptr(dt),
+                                                 _ptr(A_log), _ptr(dt_bias), _ptr(beta_logit), _ptr(initial_state),
+                                                 _ptr(o), _ptr(final_state), _stream(stream, dev))
+    if st != GDR_OK:
+        raise GdrError(st, "gdr_chunk_fwd_fused_prep")
     return o, final_state
 
 

@@ -46,9 +46,21 @@
 // j = n_h - 1 and g_t only when j = 0, and writes o only when j = n_h - 1.  On the other
 // steps the buffer offset is set past the end of the real-token buffer, so the load returns
 // zero (a zero query; log-decay 0, i.e. a = 1) and the store is dropped.
+//
+// The PREP instantiation fuses the step upstream of the chain: it takes raw projections and
+// forms the rule's inputs on the fly, q = q_raw / ||q_raw||, k likewise (the pages' unit-norm
+// convention), beta = sigmoid(beta_logit) and the Mamba-2 gate g = -e^{A_log[h]} softplus(dt +
+// dt_bias[h]) ("Linear Attention, Visualized", "Optional: Constructing the decay gate").  The
+// norms come from the staged 16-byte pieces (one K or Q row spans DK/8 consecutive lanes, so a
+// DPP reduction inside each 16-lane row gives the row's sum of squares); each piece is scaled
+// before its fp16 conversion.  The gate and beta are transformed where the scan reads them.
 #include "chunk_common.h"
 
 namespace gdr {
+
+// Instantiations of the kernel: plain Gated DeltaNet, Gated Delta Product over virtual steps,
+// Gated DeltaNet with fused input preparation.
+constexpr int kPcPlain = 0, kPcGdp = 1, kPcPrep = 2;
 
 struct PcArgs {
     int64_t T;         // steps per sequence (virtual steps T_real * nh for the VIRT kernel)
@@ -57,6 +69,9 @@ struct PcArgs {
     uint32_t nh_magic; // ceil(2^32 / nh): m / nh = umulhi(m, nh_magic) for m < 2^23 (VIRT)
     int dv;
     int ntiles;  // d_v / 32
+    int H;                  // heads (PREP: per-head gate parameters)
+    const float* A_log;     // [H] (PREP)
+    const float* dt_bias;   // [H] (PREP)
     const uint16_t* q;
     const uint16_t* k;
     const uint16_t* v;
@@ -110,8 +125,9 @@ struct PcLds {
     static_assert((oAt0 | oAt1 | oSm | oVt | oNt0 | oNt1 | oXd0 | oXd1 | oNd | oOt) % 16 == 0, "alignment");
 };
 
-template <int DK, bool VIRT>
+template <int DK, int MODE>
 __global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {
+    constexpr bool VIRT = MODE == kPcGdp, PREP = MODE == kPcPrep;
     using L = PcLds<DK>;
     constexpr int C = kChunk;
     constexpr int NKB = DK / 32;      // 32-deep reduction blocks over d_k
@@ -152,6 +168,13 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {
     const auto ro = make_rsrc(a.o + bh * Tr * DV, obytes);
     // virtual step m -> (real token, substep) of a Gated Delta Product sequence
     auto vtok = [&](uint32_t m) { return __umulhi(m, a.nh_magic); };
+    // gate parameters of this head (PREP): lambda = e^{A_log}, the bias of dt
+    float lam = 0.0f, dtb = 0.0f;
+    if constexpr (PREP) {
+        const int h = (int)(bh % a.H);
+        lam = fast_exp(a.A_log[h]);
+        dtb = a.dt_bias[h];
+    }
     const int dvc = dv0 + 16 * w;  // consumer's first value channel
     const int64_t nC = (T + C - 1) / C;
 
@@ -242,25 +265,63 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {
 #pragma unroll
         for (int u = 0; u < KVL; ++u) issue_part(u, cs_, cv_);
     };
+    // PREP: a row piece of 8 bf16 values divided by its row's L2 norm, in fp16.  The row's
+    // DK/8 pieces sit in consecutive lanes of one 16-lane DPP row; quad_perm xor 1, xor 2,
+    // row_half_mirror (and row_mirror for 16 lanes) leave the row sum in every lane.
+    auto unit_half8 = [&](const uint4& u) {
+        const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
+        float x[8], ss = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            x[2 * e] = __uint_as_float(wv[e] << 16);
+            x[2 * e + 1] = __uint_as_float(wv[e] & 0xffff0000u);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
+        ss += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(ss), 0xB1, 0xf, 0xf, false));
+        ss += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(ss), 0x4E, 0xf, 0xf, false));
+        ss += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(ss), 0x141, 0xf, 0xf, false));
+        if constexpr (DK == 128)
+            ss += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(ss), 0x140, 0xf, 0xf, false));
+        const float inv = __builtin_amdgcn_rsqf(fmaxf(ss, 1e-12f));  // 1 / max(||x||, 1e-6)
+        half8 h;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h[e] = (_Float16)(x[e] * inv);
+        return h;
+    };
     auto stage_kq = [&](int64_t c) {
         const int buf = (int)(c & 1);
 #pragma unroll
         for (int u = 0; u < KVL; ++u) {
             const int idx = pt + 256 * u, row = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
-            *reinterpret_cast<half8*>(Kb(buf) + row * L::LDK + col) = bf16x8_to_half8(getu4(oKR + 4 * u));
-            *reinterpret_cast<half8*>(Qb(buf) + row * L::LDK + col) = bf16x8_to_half8(getu4(oQR + 4 * u));
+            if constexpr (PREP) {
+                *reinterpret_cast<half8*>(Kb(buf) + row * L::LDK + col) = unit_half8(getu4(oKR + 4 * u));
+                *reinterpret_cast<half8*>(Qb(buf) + row * L::LDK + col) = unit_half8(getu4(oQR + 4 * u));
+            } else {
+                *reinterpret_cast<half8*>(Kb(buf) + row * L::LDK + col) = bf16x8_to_half8(getu4(oKR + 4 * u));
+                *reinterpret_cast<half8*>(Qb(buf) + row * L::LDK + col) = bf16x8_to_half8(getu4(oQR + 4 * u));
+            }
         }
     };
     // In-chunk cumulative log-decay G and the per-chunk factor table of chunk c (wave 0,
     // from the g and beta values its issue_part(0, c, ..) loaded).
-    auto scan = [&](int m3) {
-        const float x = wave_inclusive_scan(__uint_as_float(cr[oGR]));
+    // PREP: past the sequence end the raw loads are zeros, which the transforms would turn
+    // into g = -lambda softplus(b) and beta = 1/2; such tokens are set back to identity tokens.
+    auto scan = [&](int m3, int64_t chunk) {
+        float gl = __uint_as_float(cr[oGR]);
+        const bool live = !PREP || chunk * C + l < T;
+        if constexpr (PREP) {  // g = -lambda softplus(dt + b), softplus(z) = max(z, 0) + log(1 + e^{-|z|})
+            const float z = gl + dtb;
+            gl = live ? -lam * (fmaxf(z, 0.0f) + __logf(1.0f + fast_exp(-fabsf(z)))) : 0.0f;
+        }
+        const float x = wave_inclusive_scan(gl);
         const float GC = lane_value(x, 63);
         float ge[4];
 #pragma unroll
         for (int b = 0; b < 4; ++b) ge[b] = lane_value(x, 16 * b + 15);
         const int blk = l >> 4;
-        const float beta = __uint_as_float(cr[oGR + 1]);
+        float beta = __uint_as_float(cr[oGR + 1]);
+        if constexpr (PREP) beta = live ? 1.0f / (1.0f + fast_exp(-beta)) : 0.0f;
         float* sm = Sm(m3);
         sm[L::SG + l] = x;
         sm[L::SEG + l] = fast_exp(x);
@@ -283,7 +344,7 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {
     if (nC > 0) {
         issue_all(0, 0);
         stage_kq(0);
-        if (w == 0) scan(0);  // chunk 0 -> buffer 0
+        if (w == 0) scan(0, 0);  // chunk 0 -> buffer 0
     }
     lds_barrier();
 
@@ -550,7 +611,7 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb) seth8(oSB + 4 * kb, pack8(getf4(8 * kb), getf4(8 * kb + 4)));
             }
-            if (w == 0) scan(ms);
+            if (w == 0) scan(ms, cs);
         } else {
           if (cp >= nC) issue_all(cs, cp);
           if (cp < nC) {
@@ -632,10 +693,10 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_pc_kernel(const PcArgs a) {
     }
 }
 
-template <int DK, bool VIRT>
+template <int DK, int MODE>
 static hipError_t launch_pc(const PcArgs& a, int64_t nwg, hipStream_t st) {
     using L = PcLds<DK>;
-    auto kern = chunk_fwd_pc_kernel<DK, VIRT>;
+    auto kern = chunk_fwd_pc_kernel<DK, MODE>;
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -657,6 +718,9 @@ hipError_t chunk_fwd_pc_dispatch(int64_t BH, int64_t T, int nh, int dk, int dv, 
     a.Treal = T;
     a.nh = (uint32_t)nh;
     a.nh_magic = nh > 1 ? (uint32_t)(((uint64_t(1) << 32) + nh - 1) / nh) : 0u;
+    a.H = 1;
+    a.A_log = nullptr;
+    a.dt_bias = nullptr;
     a.dv = dv;
     a.ntiles = dv / 32;
     a.q = static_cast<const uint16_t*>(q);
@@ -669,11 +733,40 @@ hipError_t chunk_fwd_pc_dispatch(int64_t BH, int64_t T, int nh, int dk, int dv, 
     a.Sf = Sf;
     const int64_t nwg = BH * a.ntiles;
     if (nh > 1) {
-        if (dk == 128) return launch_pc<128, true>(a, nwg, st);
-        return launch_pc<64, true>(a, nwg, st);
+        if (dk == 128) return launch_pc<128, kPcGdp>(a, nwg, st);
+        return launch_pc<64, kPcGdp>(a, nwg, st);
     }
-    if (dk == 128) return launch_pc<128, false>(a, nwg, st);
-    return launch_pc<64, false>(a, nwg, st);
+    if (dk == 128) return launch_pc<128, kPcPlain>(a, nwg, st);
+    return launch_pc<64, kPcPlain>(a, nwg, st);
+}
+
+// Gated DeltaNet from raw projections: q_raw, k_raw [BH][T][dk] bf16 (normalised here),
+// dt and beta_logit [BH][T], A_log and dt_bias [H] (bh mod H is the head).
+hipError_t chunk_fwd_pc_prep_dispatch(int64_t BH, int64_t H, int64_t T, int dk, int dv, const void* q_raw,
+                                      const void* k_raw, const void* v, const float* dt, const float* A_log,
+                                      const float* dt_bias, const float* beta_logit, const float* S0, void* o,
+                                      float* Sf, hipStream_t st) {
+    PcArgs a;
+    a.T = T;
+    a.Treal = T;
+    a.nh = 1;
+    a.nh_magic = 0u;
+    a.dv = dv;
+    a.ntiles = dv / 32;
+    a.H = (int)H;
+    a.A_log = A_log;
+    a.dt_bias = dt_bias;
+    a.q = static_cast<const uint16_t*>(q_raw);
+    a.k = static_cast<const uint16_t*>(k_raw);
+    a.v = static_cast<const uint16_t*>(v);
+    a.g = dt;
+    a.beta = beta_logit;
+    a.S0 = S0;
+    a.o = static_cast<uint16_t*>(o);
+    a.Sf = Sf;
+    const int64_t nwg = BH * a.ntiles;
+    if (dk == 128) return launch_pc<128, kPcPrep>(a, nwg, st);
+    return launch_pc<64, kPcPrep>(a, nwg, st);
 }
 
 }  // namespace gdr

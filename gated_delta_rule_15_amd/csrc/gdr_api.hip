@@ -14,6 +14,10 @@ hipError_t chunk_fwd_pc_dispatch(int64_t BH, int64_t T, int nh, int dk, int dv, 
                                  float* Sf, hipStream_t st);
 hipError_t chunk_kda_dispatch(int64_t BH, int64_t T, int dk, int dv, const void* q, const void* k, const void* v,
                               const float* g, const float* beta, const float* S0, void* o, float* Sf, hipStream_t st);
+hipError_t chunk_fwd_pc_prep_dispatch(int64_t BH, int64_t H, int64_t T, int dk, int dv, const void* q_raw,
+                                      const void* k_raw, const void* v, const float* dt, const float* A_log,
+                                      const float* dt_bias, const float* beta_logit, const float* S0, void* o,
+                                      float* Sf, hipStream_t st);
 hipError_t chunk_gdn2_dispatch(int64_t BH, int64_t T, int dk, int dv, const void* q, const void* k, const void* v,
                                const float* g, const float* b, const float* w, const float* S0, void* o, float* Sf,
                                hipStream_t st);
@@ -141,6 +145,41 @@ gdr_status gdr_gdp_chunk_fwd(int64_t B, int64_t H, int64_t T, int n_h, int d_k, 
     if (!final_state && BHT == 0) return GDR_OK;
     hipError_t e = gdr::chunk_fwd_pc_dispatch(BH, T, n_h, d_k, d_v, q, k, v, g, beta, initial_state, o,
                                               final_state, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+}
+
+gdr_status gdr_chunk_fwd_fused_prep(int64_t B, int64_t H, int64_t T, int d_k, int d_v, int io_dtype,
+                                    const void* q_raw, const void* k_raw, const void* v, const float* dt,
+                                    const float* A_log, const float* dt_bias, const float* beta_logit,
+                                    const float* initial_state, void* o, float* final_state, void* stream) {
+    if (B < 0 || H < 0 || T < 0) return GDR_ERR_INVALID_ARG;
+    gdr_status s = check_common(d_k, d_v, io_dtype, GDR_GATE_SCALAR);
+    if (s != GDR_OK) return s;
+    if (T > kMaxT) return GDR_ERR_SHAPE;
+    int64_t BH, BHT, nq, nv, nstate;
+    if (!mul_ok(B, H, &BH) || !mul_ok(BH, T, &BHT) || !mul_ok(BHT, d_k, &nq) || !mul_ok(BHT, d_v, &nv) ||
+        !mul_ok(BH, (int64_t)d_k * d_v, &nstate) || !mul_ok(nq, 2, &nq) || !mul_ok(nv, 2, &nv) ||
+        !mul_ok(nstate, 4, &nstate))
+        return GDR_ERR_SHAPE;
+    if (BHT > 0 && (!q_raw || !k_raw || !v || !dt || !beta_logit || !o)) return GDR_ERR_INVALID_ARG;
+    if (BH > 0 && (!A_log || !dt_bias)) return GDR_ERR_INVALID_ARG;
+    if (io_dtype != GDR_BF16) return GDR_ERR_UNSUPPORTED;
+    // o must not overlap an input; the final state may alias the initial state exactly.
+    if (overlaps(o, nv, q_raw, nq) || overlaps(o, nv, k_raw, nq) || overlaps(o, nv, v, nv) ||
+        overlaps(o, nv, dt, BHT * 4) || overlaps(o, nv, beta_logit, BHT * 4) || overlaps(o, nv, A_log, H * 4) ||
+        overlaps(o, nv, dt_bias, H * 4) || overlaps(o, nv, initial_state, nstate) ||
+        overlaps(o, nv, final_state, nstate))
+        return GDR_ERR_INVALID_ARG;
+    if (final_state && initial_state && final_state != initial_state &&
+        overlaps(final_state, nstate, initial_state, nstate))
+        return GDR_ERR_INVALID_ARG;
+    if (BH == 0) return GDR_OK;
+    int64_t nwg;
+    if (!mul_ok(BH, d_v / 32, &nwg) || nwg > kMaxGrid) return GDR_ERR_SHAPE;
+    if (!final_state && BHT == 0) return GDR_OK;
+    hipError_t e = gdr::chunk_fwd_pc_prep_dispatch(BH, H, T, d_k, d_v, q_raw, k_raw, v, dt, A_log, dt_bias,
+                                                   beta_logit, initial_state, o, final_state,
+                                                   static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
 }
 

@@ -101,6 +101,39 @@ gdr_status gdr_chunk_fwd(int64_t B, int64_t H, int64_t T, int d_k, int d_v,
                          void *o, float *final_state, void *stream);
 
 /*
+ * gdr_chunk_fwd_fused_prep -- gdr_chunk_fwd (scalar gate) from raw projections, with the
+ * input preparation fused into the chunk kernel.
+ *
+ * Forms, per token and head, the inputs the recurrence assumes and runs the chunked forward
+ * on them without writing them out:
+ *   q = q_raw / max(||q_raw||_2, 1e-6),  k = k_raw / max(||k_raw||_2, 1e-6)   (over d_k; the
+ *       pages take keys L2-normalised by convention, and queries are treated the same way)
+ *   beta = 1 / (1 + exp(-beta_logit))                                        (0 < beta < 1)
+ *   g = log a = -exp(A_log[h]) * softplus(dt + dt_bias[h]),  softplus(x) = log(1 + e^x)
+ * The gate is Mamba-2's construction ("Linear Attention, Visualized", section "Mamba-2:
+ * input-dependent scalar decay", "Optional: Constructing the decay gate"): a decay rate
+ * lambda = e^{A_log} per head times a positive step Delta_t = softplus(dt_t + b_Delta).
+ *
+ *   q_raw, k_raw     [B, H, T, d_k]  bf16 (not normalised)
+ *   v                [B, H, T, d_v]  bf16
+ *   dt, beta_logit   [B, H, T]       float32
+ *   A_log, dt_bias   [H]             float32, one per head
+ *   initial_state, o, final_state    as gdr_chunk_fwd
+ *
+ * Equivalent to computing q, k, g, beta as above and calling gdr_chunk_fwd with
+ * GDR_GATE_SCALAR, except that q and k enter the fp16 MFMA operands unrounded to bf16.
+ * io_dtype must be GDR_BF16 (GDR_F32 returns GDR_ERR_UNSUPPORTED).  Sizes, T range and every
+ * other error as for gdr_chunk_fwd.
+ */
+gdr_status gdr_chunk_fwd_fused_prep(int64_t B, int64_t H, int64_t T, int d_k, int d_v,
+                                    int io_dtype,
+                                    const void *q_raw, const void *k_raw, const void *v,
+                                    const float *dt, const float *A_log, const float *dt_bias,
+                                    const float *beta_logit,
+                                    const float *initial_state,
+                                    void *o, float *final_state, void *stream);
+
+/*
  * gdr_gdp_chunk_fwd -- chunkwise forward pass of the Gated Delta Product.
  *
  * "Linear Attention, Visualized", section "Gated Delta Product (GDP)": each token t carries

@@ -143,6 +143,29 @@ def test_gdn2_chunk_fwd_empty_batch_is_a_noop(lib):
     assert gdn2(lib, H=0, q=None, k=None, v=None, g=None, b=None, w=None, o=None) == OK
 
 
+def prep(lib, B=1, H=1, T=64, dk=128, dv=128, io=0, q=FAKE, k=FAKE, v=FAKE, dt=FAKE, A=FAKE, bias=FAKE,
+         bl=FAKE, s0=None, o=FAKE2, sf=None):
+    return lib.gdr_chunk_fwd_fused_prep(B, H, T, dk, dv, io, q, k, v, dt, A, bias, bl, s0, o, sf, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), INVALID), (dict(H=-1), INVALID), (dict(T=-1), INVALID), (dict(dk=32), SHAPE),
+    (dict(dv=40), SHAPE), (dict(io=3), DTYPE), (dict(io=1), UNSUP),
+    (dict(q=None), INVALID), (dict(k=None), INVALID), (dict(v=None), INVALID), (dict(dt=None), INVALID),
+    (dict(A=None), INVALID), (dict(bias=None), INVALID), (dict(bl=None), INVALID), (dict(o=None), INVALID),
+    (dict(o=FAKE), INVALID),                                    # o overlaps q_raw
+    (dict(T=(1 << 22) + 1), SHAPE),
+    (dict(B=1 << 40, H=1 << 30), SHAPE),
+])
+def test_fused_prep_rejects(lib, kw, status):
+    assert prep(lib, **kw) == status
+
+
+def test_fused_prep_empty_batch_is_a_noop(lib):
+    assert prep(lib, B=0) == OK
+    assert prep(lib, T=0, q=None, k=None, v=None, dt=None, bl=None, o=None) == OK
+
+
 @pytest.mark.parametrize("nh", range(2, 17))
 def test_virtual_step_division(nh):
     """The GDP kernel splits virtual step m into (m // n_h, m % n_h) as umulhi(m, ceil(2^32 / n_h)),
@@ -175,6 +198,8 @@ def test_python_binding_refuses_cpu_tensors(lib):
         gdr.gdp_chunk_fwd(x, x[:, :, :, None], x[:, :, :, None], torch.zeros(1, 1, 4), torch.zeros(1, 1, 4, 1))
     with pytest.raises(ValueError):
         gdr.gdn2_chunk_fwd(x, x, x, x, x, x)
+    with pytest.raises(ValueError):
+        gdr.chunk_fwd_fused_prep(x, x, x, torch.zeros(1, 1, 4), torch.zeros(1), torch.zeros(1), torch.zeros(1, 1, 4))
     with pytest.raises(ValueError):
         gdr.decode_step(x[:, :, 0], x[:, :, 0], x[:, :, 0], torch.zeros(1, 1), torch.zeros(1, 1),
                         torch.zeros(1, 1, 64, 64))
