@@ -30,9 +30,11 @@ sys.path.insert(0, os.path.join(ROOT, "tests"))
 
 PEAK_MFMA_F16 = 2500.0  # TFLOP/s, MI355X dense fp16/bf16
 PEAK_HBM = 8000.0       # GB/s, MI355X HBM3E
-CHUNK_KERNEL = "chunk_fwd_pc_kernel<128, 0>"
-CHUNK_SOURCE = os.path.join(ROOT, "gated_delta_rule_15_amd", "csrc", "chunk_fwd_pc.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "chunk_fwd_pc_gdn_bf16_B4_H16_T4096_traffic.json")
+# the headline step: one gdr_chunk_fwd_ws call = the UT kernel over all chunks, then the
+# chunk-serial state kernel
+CHUNK_KERNEL = "chunk_ut_kernel<128> + chunk_state_kernel<128>"
+CHUNK_SOURCE = os.path.join(ROOT, "gated_delta_rule_15_amd", "csrc", "chunk_split.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "chunk_split_gdn_bf16_B4_H16_T4096_traffic.json")
 COPY_BYTES = 256 << 20  # calibration copy for the HBM byte counters
 
 
@@ -88,9 +90,14 @@ def to_dev(torch, a, bf16=False):
 def time_chunk(torch, gdr, sets, steps, warmup, fn=None):
     """Per-launch HIP-event durations of chunk_fwd (or ``fn``, same signature), alternating
     input sets."""
-    fn = gdr.chunk_fwd if fn is None else fn
     outs = [torch.empty(s["o_shape"], dtype=torch.bfloat16, device="cuda") for s in sets]
     fin = [torch.empty(s["S_shape"], dtype=torch.float32, device="cuda") for s in sets]
+    if fn is None:  # the chunked forward with a workspace allocated once, outside the timing
+        B, H, T, dk = sets[0]["q"].shape
+        gate = 0 if sets[0]["g"].dim() == 3 else 1
+        need = gdr.chunk_fwd_workspace_size(B, H, T, dk, sets[0]["v"].shape[-1], 0, gate)
+        wsb = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+        fn = lambda *args, **kw: gdr.chunk_fwd(*args, workspace=wsb, **kw)  # noqa: E731
 
     def launch(i):
         s = sets[i % len(sets)]
@@ -323,8 +330,8 @@ def main():
     w = gdr_synth.WORKLOADS[2]
     sets = make_chunk_sets(torch, gdr_synth, w)
     if args.pmc_run:
-        # Counter passes: the chunk kernel on the headline workload, then a plain copy of
-        # known size whose FETCH_SIZE / WRITE_SIZE calibrate the counters' byte units.
+        # Counter passes: the headline step's kernels on the headline workload, then a plain
+        # copy of known size whose FETCH_SIZE / WRITE_SIZE calibrate the counters' byte units.
         time_chunk(torch, gdr, sets, args.steps, 0)
         src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
         dst = torch.empty_like(src)
@@ -359,12 +366,18 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_MFMA_F16, "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_MFMA_F16, 4), "traffic": measured_traffic(),
                      "flops_per_launch": flops, "kernel": CHUNK_KERNEL,
-                     "ms_per_launch_mean": round(ms_mean, 5), "ms_per_launch_median": round(ms_med, 5)},
+                     "ms_per_launch_mean": round(ms_mean, 5), "ms_per_launch_median": round(ms_med, 5),
+                     "note": "one launch = one gdr_chunk_fwd_ws call (both kernels), HIP events around it"},
         "roofline_hbm": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM, 4), "bytes_per_launch": nbytes},
         "wall_s_timed_region": round(wall, 4),
     }
     result["parity_sampled"] = sampled_parity(gdr_synth, w, sets[0]["host"], o, S)
+    # the single-kernel path (gdr_chunk_fwd, no workspace) on the same inputs
+    m1, _, _, _, _ = time_chunk(torch, gdr, sets, 20, 3,
+                                fn=lambda *a_, **kw: gdr.chunk_fwd(*a_, workspace=None, **kw))
+    result["single_kernel"] = {"kernel": "chunk_fwd_pc_kernel<128, 0>", "ms_per_launch_mean": round(m1, 5),
+                               "mfma_frac": round(flops / (m1 * 1e-3) / 1e12 / PEAK_MFMA_F16, 4)}
     if not args.no_extra:
         result["decode"] = bench_decode(torch, gdr, gdr_synth)
         w4 = gdr_synth.WORKLOADS[4]

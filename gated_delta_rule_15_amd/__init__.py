@@ -1,7 +1,8 @@
 """libgdr: the gated delta rule on AMD Instinct MI355X (gfx950).
 
 Python face of the C ABI in include/gdr.h.  ``chunk_fwd`` runs the chunkwise
-forward pass and returns (o, final_state); ``chunk_fwd_fused_prep`` runs it from raw
+forward pass and returns (o, final_state) (by default on the two-kernel path with a
+torch-allocated workspace); ``chunk_fwd_fused_prep`` runs it from raw
 projections (normalisation and gates fused in); ``gdp_chunk_fwd`` is the same pass
 for the Gated Delta Product (n_h key/value/beta substeps per token) and
 ``gdn2_chunk_fwd`` for Gated DeltaNet-2 (separate erase and write gates);
@@ -9,8 +10,9 @@ for the Gated Delta Product (n_h key/value/beta substeps per token) and
 library is loaded on first use and its absence is an error: there is no CPU
 fallback.
 """
-from ._binding import (EXPORTED_SYMBOLS, LIBRARY_PATH, GdrError, chunk_fwd, chunk_fwd_fused_prep, decode_step,
-                       gdn2_chunk_fwd, gdp_chunk_fwd, load_library, status_string, version)
+from ._binding import (EXPORTED_SYMBOLS, LIBRARY_PATH, GdrError, chunk_fwd, chunk_fwd_fused_prep,
+                       chunk_fwd_workspace_size, decode_step, gdn2_chunk_fwd, gdp_chunk_fwd, load_library,
+                       status_string, version)
 
-__all__ = ["chunk_fwd", "chunk_fwd_fused_prep", "gdp_chunk_fwd", "gdn2_chunk_fwd", "decode_step", "GdrError", "load_library", "version", "status_string",
+__all__ = ["chunk_fwd", "chunk_fwd_workspace_size", "chunk_fwd_fused_prep", "gdp_chunk_fwd", "gdn2_chunk_fwd", "decode_step", "GdrError", "load_library", "version", "status_string",
            "LIBRARY_PATH", "EXPORTED_SYMBOLS"]

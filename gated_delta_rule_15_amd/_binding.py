@@ -14,12 +14,14 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIBRARY_PATH = os.path.join(_PKG, "libgdr.so")
 
 GDR_OK = 0
+GDR_ERR_SHAPE = 2
 GDR_BF16, GDR_F32 = 0, 1
 GDR_GATE_SCALAR, GDR_GATE_CHANNEL = 0, 1
 
 # every entry point include/gdr.h declares
-EXPORTED_SYMBOLS = ("gdr_version", "gdr_status_string", "gdr_chunk_fwd", "gdr_chunk_fwd_fused_prep",
-                    "gdr_gdp_chunk_fwd", "gdr_gdn2_chunk_fwd", "gdr_decode_step")
+EXPORTED_SYMBOLS = ("gdr_version", "gdr_status_string", "gdr_chunk_fwd", "gdr_chunk_fwd_workspace_size",
+                    "gdr_chunk_fwd_ws", "gdr_chunk_fwd_fused_prep", "gdr_gdp_chunk_fwd", "gdr_gdn2_chunk_fwd",
+                    "gdr_decode_step")
 
 _lock = threading.Lock()
 _lib = None
@@ -47,6 +49,10 @@ def load_library():
         lib.gdr_status_string.argtypes = [i32]
         lib.gdr_chunk_fwd.restype = i32
         lib.gdr_chunk_fwd.argtypes = [i64, i64, i64, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P]
+        lib.gdr_chunk_fwd_workspace_size.restype = i64
+        lib.gdr_chunk_fwd_workspace_size.argtypes = [i64, i64, i64, i32, i32, i32, i32]
+        lib.gdr_chunk_fwd_ws.restype = i32
+        lib.gdr_chunk_fwd_ws.argtypes = [i64, i64, i64, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, i64, P]
         lib.gdr_chunk_fwd_fused_prep.restype = i32
         lib.gdr_chunk_fwd_fused_prep.argtypes = [i64, i64, i64, i32, i32, i32, P, P, P, P, P, P, P, P, P, P, P]
         lib.gdr_gdp_chunk_fwd.restype = i32
@@ -97,12 +103,23 @@ def _check(t, name, shape, dtype, device):
         raise ValueError(f"{name}: must be contiguous")
 
 
+def chunk_fwd_workspace_size(B, H, T, d_k, d_v, io_dtype=GDR_BF16, gate=GDR_GATE_SCALAR) -> int:
+    """gdr_chunk_fwd_workspace_size: bytes of workspace the two-kernel path needs (0: none)."""
+    n = int(load_library().gdr_chunk_fwd_workspace_size(B, H, T, d_k, d_v, io_dtype, gate))
+    if n < 0:
+        raise GdrError(GDR_ERR_SHAPE, "gdr_chunk_fwd_workspace_size")
+    return n
+
+
 def chunk_fwd(q, k, v, g, beta, initial_state=None, *, output_final_state=True, out=None,
-              final_state=None, stream=None):
-    """gdr_chunk_fwd on torch tensors.
+              final_state=None, stream=None, workspace="auto"):
+    """The chunked forward on torch tensors.
 
     q, k [B,H,T,d_k]; v [B,H,T,d_v] (bf16 or fp32); g [B,H,T] or [B,H,T,d_k] fp32
     (log-decay); beta [B,H,T] fp32; initial_state [B,H,d_v,d_k] fp32 or None.
+    workspace: "auto" (default) allocates the two-kernel path's workspace with torch and
+    calls gdr_chunk_fwd_ws; a uint8 CUDA tensor is used as that workspace; None calls
+    gdr_chunk_fwd (one kernel, no workspace).
     Returns (o, final_state); final_state is None when output_final_state is False.
     """
     import torch
@@ -131,10 +148,26 @@ def chunk_fwd(q, k, v, g, beta, initial_state=None, *, output_final_state=True, 
         final_state = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
     if final_state is not None:
         _check(final_state, "final_state", (B, H, dv, dk), torch.float32, dev)
-    st = load_library().gdr_chunk_fwd(B, H, T, dk, dv, io, gate, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                                      _ptr(initial_state), _ptr(o), _ptr(final_state), _stream(stream, dev))
+    if workspace is None:
+        st = load_library().gdr_chunk_fwd(B, H, T, dk, dv, io, gate, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                          _ptr(beta), _ptr(initial_state), _ptr(o), _ptr(final_state),
+                                          _stream(stream, dev))
+        if st != GDR_OK:
+            raise GdrError(st, "gdr_chunk_fwd")
+        return o, final_state
+    need = chunk_fwd_workspace_size(B, H, T, dk, dv, io, gate)
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError(f"workspace: expected 'auto', None or a tensor, got {workspace!r}")
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace: must be a contiguous tensor on the inputs' device")
+    nbytes = workspace.numel() * workspace.element_size()
+    st = load_library().gdr_chunk_fwd_ws(B, H, T, dk, dv, io, gate, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                         _ptr(initial_state), _ptr(o), _ptr(final_state), _ptr(workspace), nbytes,
+                                         _stream(stream, dev))
     if st != GDR_OK:
-        raise GdrError(st, "gdr_chunk_fwd")
+        raise GdrError(st, "gdr_chunk_fwd_ws")
     return o, final_state
 
 

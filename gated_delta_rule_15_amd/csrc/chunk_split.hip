@@ -1,0 +1,707 @@
+// chunk_split.hip -- chunked forward of the gated delta rule (scalar gate, bf16 I/O) as two
+// kernels: the chunk-local UT transform for every chunk at once, then the chunk-serial state
+// pass.  gfx950, fp16 MFMA operands, fp32 accumulation and state.
+//
+// "Linear Attention, Visualized", section "Gated DeltaNet (GDN)", "Complete per-chunk
+// algorithm" (column convention): within a chunk,
+//   N = I + diag(beta) (K K^T (.) Gam)_strict,   T = N^{-1} diag(beta),   A = (Q K^T) (.) Gam
+// depend on the chunk's own inputs only, and the page notes that they can be formed for all
+// chunks in parallel before the boundary pass threads the state through the chunks.  So:
+//
+//   chunk_ut_kernel     one workgroup per (sequence, chunk), all chunks at once: the decay scan,
+//                       the Gram tiles of K K^T and Q K^T, the four 16x16 diagonal blocks of
+//                       N^{-1} by fp32 forward substitution, the blocks below the diagonal by
+//                       16x16 MFMA products (M_bc = -X_bb sum_{c<=d<b} N_bd M_dc), and T and A
+//                       written to a workspace as fp16 (16 KiB per chunk and sequence);
+//   chunk_state_kernel  one workgroup per (sequence, 32 value channels), chunks in order:
+//                       R = V - diag(e^G) K S^T,  Z = T R,  O = diag(e^G) Q S^T + A Z,
+//                       S^T <- e^{G_C} S^T + K^T diag(e^{G_C - G}) Z.
+//
+// With T formed in advance, the serial chain of a chunk is three dependent product groups
+// (K S^T, T R, the state update) instead of a blocked substitution, and the UT work is done
+// once per chunk instead of once per value-channel tile.  The price is the workspace traffic
+// (T and A written once and read by every value-channel tile) and a second read of K and Q.
+//
+// Workspace layout, per (sequence, chunk): A^T [64][64] (row m holds A[l][m], l = 0..63), then
+// T [64][64] (row l; column m stored at position pperm(m), so one operand fragment is one
+// 16-byte read).  Upper triangles are stored as zeros.
+#include <type_traits>
+
+#include "chunk_common.h"
+
+namespace gdr {
+
+// per-chunk factor table of the UT kernel (floats), as the single-kernel path:
+//   [0,64) G   [192,256) beta   [272,336) cf[m] = e^{Gend(blk(m)) - G_m}
+//   [336,528) rf[b][l] = e^{G_l - Gend(b)}   [528,720) rb[b][l] = beta_l rf[b][l]
+struct UtTab {
+    static constexpr int SG = 0, SB = 192, SCF = 272, SRF = 336, SRB = 528, NSM = 736;
+};
+
+struct UtArgs {
+    int64_t T;
+    int64_t nC;
+    const uint16_t* q;
+    const uint16_t* k;
+    const float* g;
+    const float* beta;
+    uint16_t* ws;
+};
+
+template <int DK>
+struct UtLds {
+    static constexpr int C = kChunk;
+    static constexpr int LDK = DK + 16;  // halfs, rows of K / Q (conflict-free fragment reads)
+    static constexpr int LDC = C + 8;    // halfs, rows of C-wide fp16 matrices
+    static constexpr int LDN = 16 + 4;   // floats, rows of a 16x16 fp32 block
+    static constexpr int LDX = 16 + 8;   // halfs, rows of a 16x16 fp16 block
+    static constexpr int szK = C * LDK * 2;
+    static constexpr int szC = C * LDC * 2;
+    // K and Q during the Gram products; afterwards the same bytes hold N^T, A^T and T
+    static constexpr int oK = 0, oQ = szK;
+    static constexpr int oNt = 0, oAt = szC, oTt = 2 * szC;
+    static constexpr int szAlias = (2 * szK > 3 * szC ? 2 * szK : 3 * szC);
+    static constexpr int oSm = (szAlias + 15) / 16 * 16;
+    static constexpr int oNd = oSm + UtTab::NSM * 4;          // diagonal blocks of N^T (fp32)
+    static constexpr int oXd = oNd + 4 * 16 * LDN * 4;        // X_bb^T (fp16)
+    static constexpr int total = oXd + 4 * 16 * LDX * 2;
+    static_assert(total <= 64 * 1024, "the UT kernel is sized for several workgroups per CU");
+    static_assert((oSm | oNd | oXd | oAt | oTt) % 16 == 0, "alignment");
+};
+
+template <int DK>
+__global__ __launch_bounds__(128) void chunk_ut_kernel(const UtArgs a) {
+    using L = UtLds<DK>;
+    using S = UtTab;
+    constexpr int C = kChunk;
+    constexpr int NKB = DK / 32;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    _Float16* Kb = reinterpret_cast<_Float16*>(smem + L::oK);
+    _Float16* Qb = reinterpret_cast<_Float16*>(smem + L::oQ);
+    _Float16* Nt = reinterpret_cast<_Float16*>(smem + L::oNt);
+    _Float16* At = reinterpret_cast<_Float16*>(smem + L::oAt);
+    _Float16* Tt = reinterpret_cast<_Float16*>(smem + L::oTt);
+    float* sm = reinterpret_cast<float*>(smem + L::oSm);
+    float* Nd = reinterpret_cast<float*>(smem + L::oNd);
+    _Float16* Xd = reinterpret_cast<_Float16*>(smem + L::oXd);
+
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, j = l & 15, g = l >> 4;
+    const int64_t bh = blockIdx.x / a.nC;
+    const int64_t c = blockIdx.x - bh * a.nC;
+    const int64_t T = a.T;
+    const uint32_t t0 = (uint32_t)(c * C);
+    const auto rq = make_rsrc(a.q + bh * T * DK, (uint32_t)(T * DK * 2));
+    const auto rk = make_rsrc(a.k + bh * T * DK, (uint32_t)(T * DK * 2));
+    const auto rg = make_rsrc(a.g + bh * T, (uint32_t)(T * 4));
+    const auto rb = make_rsrc(a.beta + bh * T, (uint32_t)(T * 4));
+
+    // ---- K and Q of the chunk into LDS (fp16, natural channel order); past the sequence end
+    // the loads return zeros, i.e. identity tokens
+    constexpr int NP = C * DK / 8 / 128;  // 16-byte pieces per thread and matrix
+    {
+        uint4 kr[NP], qr[NP];
+#pragma unroll
+        for (int u = 0; u < NP; ++u) {
+            const int idx = tid + 128 * u, row = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
+            const uint32_t off = ((t0 + row) * DK + col) * 2;
+            kr[u] = bld16(rk, off);
+            qr[u] = bld16(rq, off);
+        }
+        float gl = 0.0f, bt = 0.0f;
+        if (w == 0) {
+            gl = bld4(rg, (t0 + l) * 4);
+            bt = bld4(rb, (t0 + l) * 4);
+        }
+#pragma unroll
+        for (int u = 0; u < NP; ++u) {
+            const int idx = tid + 128 * u, row = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
+            *reinterpret_cast<half8*>(Kb + row * L::LDK + col) = bf16x8_to_half8(kr[u]);
+            *reinterpret_cast<half8*>(Qb + row * L::LDK + col) = bf16x8_to_half8(qr[u]);
+        }
+        // in-chunk cumulative log-decay and the factor table (wave 0, lane = token)
+        if (w == 0) {
+            const float x = wave_inclusive_scan(gl);
+            float ge[4];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) ge[b] = lane_value(x, 16 * b + 15);
+            const int blk = l >> 4;
+            sm[S::SG + l] = x;
+            sm[S::SB + l] = bt;
+            sm[S::SCF + l] = fast_exp(ge[blk] - x);
+#pragma unroll
+            for (int b = 0; b < 3; ++b) {
+                const float f = blk > b ? fast_exp(x - ge[b]) : 0.0f;
+                sm[S::SRF + 64 * b + l] = f;
+                sm[S::SRB + 64 * b + l] = bt * f;
+            }
+        }
+    }
+    lds_barrier();
+
+    // ---- Gram tiles.  Wave 0 forms KK {00,10,11,20,21,30,31} and QK {00,10,11}; wave 1 forms
+    // KK {22,32,33} and QK {20,21,22,30,31,32,33}.  Off the diagonal the decay is factorised
+    // through the 16-token block ends (both factors <= 1); on it it is exact.
+    // The tile lists are indexed by the wave's role, so the role is a compile-time constant.
+    auto gram = [&](auto pc) {
+    constexpr int P = decltype(pc)::value;
+    constexpr int NT = 10;
+    constexpr int tq[2][NT] = {{0, 0, 0, 0, 0, 0, 0, 1, 1, 1}, {0, 0, 0, 1, 1, 1, 1, 1, 1, 1}};
+    constexpr int ti_[2][NT] = {{0, 1, 1, 2, 2, 3, 3, 0, 1, 1}, {2, 3, 3, 2, 2, 2, 3, 3, 3, 3}};
+    constexpr int tj_[2][NT] = {{0, 0, 1, 0, 1, 0, 1, 0, 0, 1}, {2, 2, 3, 0, 1, 2, 0, 1, 2, 3}};
+    float4v acc[NT];
+    float4v fr[NT];
+    float fc[NT];
+    {
+        auto load6 = [&](half8* f, int kb) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) f[r] = ld8(Kb + (16 * r + j) * L::LDK + 32 * kb + 8 * g);
+#pragma unroll
+            for (int r = 0; r < 2; ++r) f[4 + r] = ld8(Qb + (16 * (2 * P + r) + j) * L::LDK + 32 * kb + 8 * g);
+        };
+        auto factors = [&](const int t) {
+            const int ti = ti_[P][t], tj = tj_[P][t];
+            const bool isQ = tq[P][t];
+            const int m = 16 * tj + j, l0 = 16 * ti + 4 * g;
+            if (ti != tj) {
+                fr[t] = ld4f(sm + (isQ ? S::SRF : S::SRB) + 64 * tj + l0);
+                fc[t] = sm[S::SCF + m];
+            } else {
+                const float Gm = sm[S::SG + m];
+                const float4v Gl = ld4f(sm + S::SG + l0);
+                const float4v bl = isQ ? float4v{1.0f, 1.0f, 1.0f, 1.0f} : ld4f(sm + S::SB + l0);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const bool keep = isQ ? (m <= l0 + r) : (m < l0 + r);
+                    fr[t][r] = keep ? bl[r] * fast_exp(Gl[r] - Gm) : 0.0f;
+                }
+                fc[t] = 1.0f;
+            }
+        };
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t] = zero4();
+        half8 fa[6], fb[6];
+        load6(fa, 0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            half8* cur = (kb & 1) ? fb : fa;
+            half8* nxt = (kb & 1) ? fa : fb;
+            if (kb + 1 < NKB) load6(nxt, kb + 1);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const int ti = ti_[P][t], tj = tj_[P][t];
+                const half8 A = tq[P][t] ? cur[4 + (ti - 2 * P)] : cur[ti];
+                mma16(acc[t], A, cur[tj]);
+            }
+            if (kb < 2) {
+#pragma unroll
+                for (int t = 5 * kb; t < 5 * kb + 5; ++t) factors(t);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    lds_barrier();  // every read of K and Q is done: their bytes become N^T, A^T and T
+    for (int i = tid; i < 3 * L::szC / 16; i += 128)
+        reinterpret_cast<uint4*>(smem + L::oNt)[i] = uint4{0u, 0u, 0u, 0u};
+    lds_barrier();
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const int ti = ti_[P][t], tj = tj_[P][t];
+        const bool isQ = tq[P][t];
+        const int m = 16 * tj + j, l0 = 16 * ti + 4 * g;
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = acc[t][r] * fr[t][r] * fc[t];
+        if (ti == tj && !isQ) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (m == l0 + r) v[r] = 1.0f;
+            *reinterpret_cast<float4v*>(Nd + (ti * 16 + j) * L::LDN + 4 * g) = float4v{v[0], v[1], v[2], v[3]};
+        } else {
+            _Float16* dst = (isQ ? At : Nt) + m * L::LDC + l0;
+            *reinterpret_cast<half4*>(dst) = half4{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+        }
+    }
+    };
+    if (w == 0) gram(std::integral_constant<int, 0>{});
+    else gram(std::integral_constant<int, 1>{});
+    lds_barrier();
+
+    // ---- diagonal blocks X_bb = N_bb^{-1}: wave w takes blocks 2w, 2w+1, lane (block, jc)
+    // builds column jc by forward substitution in fp32.  Stored as X_bb^T (fp16) for the
+    // products below, and as the diagonal blocks of T = N^{-1} diag(beta).
+    {
+        const int b = 2 * w + ((l >> 4) & 1), jc = j;
+        const float* nb = Nd + b * 16 * L::LDN;
+        float4v nr[15][4];
+#pragma unroll
+        for (int i = 0; i < 15; ++i)
+#pragma unroll
+            for (int q4 = (i + 1) / 4; q4 < 4; ++q4) nr[i][q4] = ld4f(nb + i * L::LDN + 4 * q4);
+        float xd[16];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) xd[t] = (t == jc) ? 1.0f : 0.0f;
+#pragma unroll
+        for (int i = 0; i < 15; ++i) {
+#pragma unroll
+            for (int q4 = (i + 1) / 4; q4 < 4; ++q4) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (4 * q4 + e > i) xd[4 * q4 + e] -= nr[i][q4][e] * xd[i];
+            }
+        }
+        if (l < 32) {
+            half8 h0, h1;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                h0[t] = (_Float16)xd[t];
+                h1[t] = (_Float16)xd[8 + t];
+            }
+            *reinterpret_cast<half8*>(Xd + (16 * b + jc) * L::LDX) = h0;
+            *reinterpret_cast<half8*>(Xd + (16 * b + jc) * L::LDX + 8) = h1;
+            const float bc = sm[S::SB + 16 * b + jc];
+            const int pc = pperm(16 * b + jc);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) Tt[(16 * b + i) * L::LDC + pc] = (_Float16)(xd[i] * bc);
+        }
+    }
+    lds_barrier();
+
+    // ---- blocks below the diagonal, column block by column block:
+    //   M_bc = -X_bb sum_{d = c}^{b-1} N_bd M_dc   (M_cc = X_cc),   T_bc = M_bc diag(beta_c).
+    // Wave 0 takes column 0 (three blocks), wave 1 columns 1 and 2.
+    {
+        auto mma16k16 = [](float4v& acc4, const half4& a4, const half4& b4) {
+            acc4 = __builtin_amdgcn_mfma_f32_16x16x16f16(a4, b4, acc4, 0, 0, 0);
+        };
+        auto h4 = [](const float4v& x) { return half4{(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3]}; };
+        // A operands (rows = lane j): X_bb from its transposed copy, N_bd from N^T
+        auto xA = [&](int b) { return ldtr(Xd + (16 * b + 4 * g + (j >> 2)) * L::LDX + 4 * (j & 3)); };
+        auto nA = [&](int b, int d) { return ldtr(Nt + (16 * d + 4 * g + (j >> 2)) * L::LDC + 16 * b + 4 * (j & 3)); };
+        auto column = [&](auto cc) {
+            constexpr int cb = decltype(cc)::value;
+            half4 mb[4];
+            mb[cb] = *reinterpret_cast<const half4*>(Xd + (16 * cb + j) * L::LDX + 4 * g);  // B operand X_cc
+            const float bcol = sm[S::SB + 16 * cb + j];
+            const int pc = pperm(16 * cb + j);
+#pragma unroll
+            for (int b = cb + 1; b < 4; ++b) {
+                float4v y = zero4();
+#pragma unroll
+                for (int d = cb; d < b; ++d) mma16k16(y, nA(b, d), mb[d]);
+                float4v m = zero4();
+                mma16k16(m, xA(b), h4(y));
+#pragma unroll
+                for (int r = 0; r < 4; ++r) m[r] = -m[r];
+                mb[b] = h4(m);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Tt[(16 * b + 4 * g + r) * L::LDC + pc] = (_Float16)(m[r] * bcol);
+            }
+        };
+        if (w == 0) {
+            column(std::integral_constant<int, 0>{});
+        } else {
+            column(std::integral_constant<int, 1>{});
+            column(std::integral_constant<int, 2>{});
+        }
+    }
+    lds_barrier();
+
+    // ---- A^T and T to the workspace, 16-byte pieces
+    uint16_t* dst = a.ws + (bh * a.nC + c) * (2 * C * C);
+#pragma unroll
+    for (int u = 0; u < C * C / 8 / 128; ++u) {
+        const int idx = tid + 128 * u, row = idx / (C / 8), col = (idx % (C / 8)) * 8;
+        *reinterpret_cast<uint4*>(dst + row * C + col) = *reinterpret_cast<const uint4*>(At + row * L::LDC + col);
+        *reinterpret_cast<uint4*>(dst + C * C + row * C + col) = *reinterpret_cast<const uint4*>(Tt + row * L::LDC + col);
+    }
+}
+
+// ============================================================================ state pass
+
+struct StArgs {
+    int64_t T;
+    int64_t nC;
+    int dv;
+    int ntiles;  // d_v / 32
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const float* g;
+    const uint16_t* ws;
+    const float* S0;
+    uint16_t* o;
+    float* Sf;
+};
+
+template <int DK>
+struct StLds {
+    static constexpr int C = kChunk;
+    static constexpr int LDK = DK + 16;
+    static constexpr int LDC = C + 8;
+    static constexpr int LDV = 80;     // bf16, rows (tokens) of the 32-channel V tile
+    static constexpr int LDO = C + 8;  // bf16, rows of O^T
+    // factor table: [0,64) e^G   [64,128) e^{G_C - G}   [128] e^{G_C}
+    static constexpr int FEG = 0, FER = 64, FEC = 128, NF = 144;
+    static constexpr int szK = C * LDK * 2;
+    static constexpr int szC = C * LDC * 2;
+    static constexpr int szV = C * LDV * 2;
+    static constexpr int oK = 0;                    // two buffers each
+    static constexpr int oQ = oK + 2 * szK;
+    static constexpr int oA = oQ + 2 * szK;
+    static constexpr int oT = oA + 2 * szC;
+    static constexpr int oV = oT + 2 * szC;
+    static constexpr int oF = oV + 2 * szV;
+    static constexpr int oOt = oF + 2 * NF * 4;  // O^T of a chunk, two buffers
+    static constexpr int szO = 32 * LDO * 2;
+    static constexpr int total = oOt + 2 * szO;
+    static_assert(total <= 160 * 1024, "LDS budget of one gfx950 CU exceeded");
+    static_assert((oQ | oA | oT | oV | oF | oOt) % 16 == 0, "alignment");
+};
+
+template <int DK>
+__global__ __launch_bounds__(256, 1) void chunk_state_kernel(const StArgs a) {
+    using L = StLds<DK>;
+    constexpr int C = kChunk;
+    constexpr int NKB = DK / 32;
+    constexpr int NST = DK / 16;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    auto Kb = [&](int b) { return reinterpret_cast<_Float16*>(smem + L::oK + b * L::szK); };
+    auto Qb = [&](int b) { return reinterpret_cast<_Float16*>(smem + L::oQ + b * L::szK); };
+    auto Ab = [&](int b) { return reinterpret_cast<_Float16*>(smem + L::oA + b * L::szC); };
+    auto Tb = [&](int b) { return reinterpret_cast<_Float16*>(smem + L::oT + b * L::szC); };
+    auto Vb = [&](int b) { return reinterpret_cast<uint16_t*>(smem + L::oV + b * L::szV); };
+    auto Fb = [&](int b) { return reinterpret_cast<float*>(smem + L::oF + b * L::NF * 4); };
+    auto Ob = [&](int b) { return reinterpret_cast<_Float16*>(smem + L::oOt + b * L::szO); };  // bf16 bits
+
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, j = l & 15, g = l >> 4;
+    const bool consumer = w < 2;
+    // the consumers' chain is the critical path: let them win issue and LDS arbitration
+    if (consumer) __builtin_amdgcn_s_setprio(2);
+    const int vi = xcd_major_index(blockIdx.x, gridDim.x);
+    const int64_t bh = vi / a.ntiles;
+    const int dv0 = (vi % a.ntiles) * 32;
+    const int dvc = dv0 + 16 * w;
+    const int64_t T = a.T, nC = a.nC;
+    const int DV = a.dv;
+    const auto rq = make_rsrc(a.q + bh * T * DK, (uint32_t)(T * DK * 2));
+    const auto rk = make_rsrc(a.k + bh * T * DK, (uint32_t)(T * DK * 2));
+    const auto rv = make_rsrc(a.v + bh * T * DV, (uint32_t)(T * DV * 2));
+    const auto rg = make_rsrc(a.g + bh * T, (uint32_t)(T * 4));
+    const auto rw = make_rsrc(a.ws + bh * nC * (2 * C * C), (uint32_t)(nC * (2 * C * C) * 2));
+    const auto ro = make_rsrc(a.o + bh * T * DV, (uint32_t)(T * DV * 2));
+
+    auto trfrag = [&](const _Float16* base, int ld, int kb, int col) {
+        const _Float16* p0 = base + (32 * kb + 4 * g + (j >> 2)) * ld + col;
+        return cat8(ldtr(p0), ldtr(p0 + 16 * ld));
+    };
+
+    // ---- loader waves (2, 3): registers for one chunk, staged into LDS one chunk ahead
+    const int lt = tid - 128;  // loader thread in [0, 128)
+    constexpr int NPK = C * DK / 8 / 128;  // K (and Q) pieces per loader thread
+    constexpr int NPW = C * C / 8 / 128;   // A^T (and T) pieces per loader thread
+    uint4 kr[NPK], qr[NPK], ar[NPW], tr[NPW], vr[2];
+    float gr = 0.0f;
+    auto issue = [&](int64_t c) {
+        const uint32_t t0 = (uint32_t)(c * C);
+#pragma unroll
+        for (int u = 0; u < NPK; ++u) {
+            const int idx = lt + 128 * u, row = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
+            const uint32_t off = ((t0 + row) * DK + col) * 2;
+            kr[u] = bld16(rk, off);
+            qr[u] = bld16(rq, off);
+        }
+        const uint32_t wb = (uint32_t)(c * (2 * C * C));
+#pragma unroll
+        for (int u = 0; u < NPW; ++u) {
+            const int idx = lt + 128 * u;
+            ar[u] = bld16(rw, (wb + idx * 8) * 2);
+            tr[u] = bld16(rw, (wb + C * C + idx * 8) * 2);
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int idx = lt + 128 * u, row = idx >> 2, col = (idx & 3) * 8;
+            vr[u] = bld16(rv, ((t0 + row) * DV + dv0 + col) * 2);
+        }
+        if (w == 2) gr = bld4(rg, (t0 + l) * 4);
+    };
+    // o of chunk c from its O^T buffer: loader wave lw takes rows (value channels) 16 lw ..,
+    // a lane reads 8 consecutive channels of one token back transposed and stores 16 bytes
+    auto store_o = [&](int64_t c) {
+        const int lw = w - 2;
+        const _Float16* Ot = Ob((int)(c & 1));
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            const int tb = 32 * s2 + 16 * (g >> 1), d = 16 * lw + 8 * (g & 1);
+            const _Float16* rp = Ot + (d + (j >> 2)) * L::LDO + tb + 4 * (j & 3);
+            const uint2 lo = __builtin_bit_cast(uint2, ldtr(rp));
+            const uint2 hi = __builtin_bit_cast(uint2, ldtr(rp + 4 * L::LDO));
+            bst16(ro, ((uint32_t)(c * C + tb + j) * DV + dv0 + d) * 2, uint4{lo.x, lo.y, hi.x, hi.y});
+        }
+    };
+    // K and Q to fp16 in the registers (while the consumers' first products read LDS)
+    auto convert = [&]() {
+#pragma unroll
+        for (int u = 0; u < NPK; ++u) {
+            kr[u] = __builtin_bit_cast(uint4, bf16x8_to_half8(kr[u]));
+            qr[u] = __builtin_bit_cast(uint4, bf16x8_to_half8(qr[u]));
+        }
+    };
+    auto stage = [&](int64_t c) {
+        const int b = (int)(c & 1);
+#pragma unroll
+        for (int u = 0; u < NPK; ++u) {
+            const int idx = lt + 128 * u, row = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
+            *reinterpret_cast<uint4*>(Kb(b) + row * L::LDK + col) = kr[u];
+            *reinterpret_cast<uint4*>(Qb(b) + row * L::LDK + col) = qr[u];
+        }
+#pragma unroll
+        for (int u = 0; u < NPW; ++u) {
+            const int idx = lt + 128 * u, row = idx / (C / 8), col = (idx % (C / 8)) * 8;
+            *reinterpret_cast<uint4*>(Ab(b) + row * L::LDC + col) = ar[u];
+            *reinterpret_cast<uint4*>(Tb(b) + row * L::LDC + col) = tr[u];
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int idx = lt + 128 * u, row = idx >> 2, col = (idx & 3) * 8;
+            *reinterpret_cast<uint4*>(Vb(b) + row * L::LDV + col) = vr[u];
+        }
+        if (w == 2) {  // in-chunk cumulative log-decay (lane = token) and its factors
+            const float x = wave_inclusive_scan(gr);
+            const float GC = lane_value(x, 63);
+            float* F = Fb(b);
+            F[L::FEG + l] = fast_exp(x);
+            F[L::FER + l] = fast_exp(GC - x);
+            if (l == 0) F[L::FEC] = fast_exp(GC);
+        }
+    };
+
+    // ---- consumer waves (0, 1): the state S^T of 16 value channels (fp32 accumulators, rows
+    // permuted by pperm) and its fp16 operand copy
+    float4v St[NST];
+    half8 Sb[NKB];
+#pragma unroll
+    for (int t = 0; t < NST; ++t) St[t] = zero4();
+    if (consumer && a.S0 != nullptr) {
+        const float* s0 = a.S0 + bh * (int64_t)DV * DK + (int64_t)(dvc + j) * DK;
+#pragma unroll
+        for (int t = 0; t < NST; ++t) St[t] = ld4f(s0 + pperm(16 * t + 4 * g));
+    }
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) Sb[kb] = pack8(St[2 * kb], St[2 * kb + 1]);
+
+    if (!consumer && nC > 0) {
+        issue(0);
+        convert();
+        stage(0);
+        if (nC > 1) issue(1);
+    }
+    lds_barrier();
+
+    for (int64_t c = 0; c < nC; ++c) {
+        const int bc = (int)(c & 1);
+        if (consumer) {
+            const _Float16* Kc = Kb(bc);
+            const _Float16* Qc = Qb(bc);
+            const _Float16* Ac = Ab(bc);
+            const _Float16* Tc = Tb(bc);
+            const uint16_t* Vc = Vb(bc);
+            const float* F = Fb(bc);
+            auto kfrag = [&](int ti, int kb) { return ld8(Kc + (16 * ti + j) * L::LDK + 32 * kb + 8 * g); };
+            auto qfrag = [&](int ti, int kb) { return ld8(Qc + (16 * ti + j) * L::LDK + 32 * kb + 8 * g); };
+            // P_K = K S^T, P_Q = Q S^T (rows = tokens)
+            float4v PK[4], PQ[4];
+            half8 fa[8], fb[8];
+#pragma unroll
+            for (int ti = 0; ti < 4; ++ti) {
+                PK[ti] = zero4();
+                PQ[ti] = zero4();
+                fa[ti] = kfrag(ti, 0);
+                fa[4 + ti] = qfrag(ti, 0);
+            }
+            // fragments that do not depend on the state (T, A, K^T) are loaded while the
+            // first products run
+            half8 tf[6], af[6];
+            auto ktfrag = [&](int t, int kb) { return trfrag(Kc, L::LDK, kb, pperm(16 * t + 4 * (j & 3))); };
+            half8 kt0[NST], kt1[NST];
+            auto prefetch = [&](int kb) {
+                if (kb == 0) {
+#pragma unroll
+                    for (int ti = 0, n = 0; ti < 4; ++ti) {
+#pragma unroll
+                        for (int k2 = 0; k2 <= (ti >> 1); ++k2, ++n) {
+                            tf[n] = ld8(Tc + (16 * ti + j) * L::LDC + 32 * k2 + 8 * g);
+                            af[n] = trfrag(Ac, L::LDC, k2, 16 * ti + 4 * (j & 3));
+                        }
+                    }
+                } else {
+                    // K^T fragments: NST / (NKB - 1) tiles per later block
+                    constexpr int PER = (NST + NKB - 2) / (NKB - 1);
+#pragma unroll
+                    for (int t = (kb - 1) * PER; t < kb * PER && t < NST; ++t) {
+                        kt0[t] = ktfrag(t, 0);
+                        kt1[t] = ktfrag(t, 1);
+                    }
+                }
+            };
+            float4v eg[4], vv[4];
+#pragma unroll
+            for (int ti = 0; ti < 4; ++ti) {
+                eg[ti] = ld4f(F + L::FEG + 16 * ti + 4 * g);
+                const uint2 vb = __builtin_bit_cast(
+                    uint2, ldtr(reinterpret_cast<const _Float16*>(Vc) + (16 * ti + 4 * g + (j >> 2)) * L::LDV +
+                                16 * w + 4 * (j & 3)));
+                vv[ti] = float4v{__uint_as_float(vb.x << 16), __uint_as_float(vb.x & 0xffff0000u),
+                                 __uint_as_float(vb.y << 16), __uint_as_float(vb.y & 0xffff0000u)};
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                half8* cur = (kb & 1) ? fb : fa;
+                half8* nxt = (kb & 1) ? fa : fb;
+                if (kb + 1 < NKB) {
+#pragma unroll
+                    for (int ti = 0; ti < 4; ++ti) {
+                        nxt[ti] = kfrag(ti, kb + 1);
+                        nxt[4 + ti] = qfrag(ti, kb + 1);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int ti = 0; ti < 4; ++ti) {
+                    mma16(PK[ti], cur[ti], Sb[kb]);
+                    mma16(PQ[ti], cur[4 + ti], Sb[kb]);
+                }
+                prefetch(kb);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            float4v er[4];
+#pragma unroll
+            for (int ti = 0; ti < 4; ++ti) er[ti] = ld4f(F + L::FER + 16 * ti + 4 * g);
+            const float eGC = F[L::FEC];
+            __builtin_amdgcn_sched_barrier(0);
+            // R = V - e^G P_K,  O_hist = e^G P_Q
+            float4v Rr[4], Oh[4];
+#pragma unroll
+            for (int ti = 0; ti < 4; ++ti) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    Rr[ti][r] = vv[ti][r] - eg[ti][r] * PK[ti][r];
+                    Oh[ti][r] = eg[ti][r] * PQ[ti][r];
+                }
+            }
+            // Z = T R (T lower triangular: block column kb only for row tiles ti >= 2 kb)
+            const half8 rB[2] = {pack8(Rr[0], Rr[1]), pack8(Rr[2], Rr[3])};
+            float4v Zz[4];
+#pragma unroll
+            for (int ti = 0, n = 0; ti < 4; ++ti) {
+                Zz[ti] = zero4();
+#pragma unroll
+                for (int kb = 0; kb <= (ti >> 1); ++kb, ++n) mma16(Zz[ti], tf[n], rB[kb]);
+            }
+            // O = O_hist + A Z  and  S^T <- e^{G_C} S^T + K^T diag(e^{G_C - G}) Z: both groups
+            // of products are issued before any of their results is used
+            const half8 zB[2] = {pack8(Zz[0], Zz[1]), pack8(Zz[2], Zz[3])};
+            float4v zs[4];
+#pragma unroll
+            for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) zs[ti][r] = er[ti][r] * Zz[ti][r];
+            const half8 sZ0 = pack8(zs[0], zs[1]), sZ1 = pack8(zs[2], zs[3]);
+            float4v Oa[4];
+#pragma unroll
+            for (int ti = 0, n = 0; ti < 4; ++ti) {
+                Oa[ti] = Oh[ti];
+#pragma unroll
+                for (int kb = 0; kb <= (ti >> 1); ++kb, ++n) mma16(Oa[ti], af[n], zB[kb]);
+            }
+#pragma unroll
+            for (int t = 0; t < NST; ++t) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) St[t][r] *= eGC;
+                mma16(St[t], kt0[t], sZ0);
+                mma16(St[t], kt1[t], sZ1);
+            }
+            // O rounded to bf16 into this wave's rows of O^T (the loaders store it)
+#pragma unroll
+            for (int ti = 0; ti < 4; ++ti)
+                *reinterpret_cast<uint2*>(Ob(bc) + (16 * w + j) * L::LDO + 16 * ti + 4 * g) =
+                    uint2{pack_bf16x2(Oa[ti][0], Oa[ti][1]), pack_bf16x2(Oa[ti][2], Oa[ti][3])};
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) Sb[kb] = pack8(St[2 * kb], St[2 * kb + 1]);
+        } else {
+            // loaders: o of the previous chunk, the next chunk into LDS, then the loads of the
+            // one after
+            if (c > 0) store_o(c - 1);
+            if (c + 1 < nC) convert();
+            if (c + 1 < nC) {
+                stage(c + 1);
+                if (c + 2 < nC) issue(c + 2);
+            }
+        }
+        lds_barrier();
+    }
+    if (!consumer && nC > 0) store_o(nC - 1);
+
+    if (consumer && a.Sf != nullptr) {
+        float* sf = a.Sf + bh * (int64_t)DV * DK + (int64_t)(dvc + j) * DK;
+#pragma unroll
+        for (int t = 0; t < NST; ++t) *reinterpret_cast<float4v*>(sf + pperm(16 * t + 4 * g)) = St[t];
+    }
+}
+
+template <int DK>
+static hipError_t launch_split(const UtArgs& u, const StArgs& s, int64_t BH, hipStream_t st) {
+    using LU = UtLds<DK>;
+    using LS = StLds<DK>;
+    auto ku = chunk_ut_kernel<DK>;
+    auto ks = chunk_state_kernel<DK>;
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(ks),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, LS::total);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    if (u.nC > 0) hipLaunchKernelGGL(ku, dim3((unsigned)(BH * u.nC)), dim3(128), LU::total, st, u);
+    hipLaunchKernelGGL(ks, dim3((unsigned)(BH * s.ntiles)), dim3(256), LS::total, st, s);
+    return hipGetLastError();
+}
+
+// Bytes of workspace the two-kernel path needs: 16 KiB per (sequence, chunk).
+int64_t chunk_split_workspace_bytes(int64_t BH, int64_t T) {
+    const int64_t nC = (T + kChunk - 1) / kChunk;
+    return BH * nC * (2 * kChunk * kChunk) * 2;
+}
+
+hipError_t chunk_split_dispatch(int64_t BH, int64_t T, int dk, int dv, const void* q, const void* k, const void* v,
+                                const float* g, const float* beta, const float* S0, void* o, float* Sf, void* ws,
+                                hipStream_t st) {
+    const int64_t nC = (T + kChunk - 1) / kChunk;
+    UtArgs u;
+    u.T = T;
+    u.nC = nC;
+    u.q = static_cast<const uint16_t*>(q);
+    u.k = static_cast<const uint16_t*>(k);
+    u.g = g;
+    u.beta = beta;
+    u.ws = static_cast<uint16_t*>(ws);
+    StArgs s;
+    s.T = T;
+    s.nC = nC;
+    s.dv = dv;
+    s.ntiles = dv / 32;
+    s.q = u.q;
+    s.k = u.k;
+    s.v = static_cast<const uint16_t*>(v);
+    s.g = g;
+    s.ws = u.ws;
+    s.S0 = S0;
+    s.o = static_cast<uint16_t*>(o);
+    s.Sf = Sf;
+    if (dk == 128) return launch_split<128>(u, s, BH, st);
+    return launch_split<64>(u, s, BH, st);
+}
+
+}  // namespace gdr

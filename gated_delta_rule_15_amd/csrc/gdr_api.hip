@@ -14,6 +14,10 @@ hipError_t chunk_fwd_pc_dispatch(int64_t BH, int64_t T, int nh, int dk, int dv, 
                                  float* Sf, hipStream_t st);
 hipError_t chunk_kda_dispatch(int64_t BH, int64_t T, int dk, int dv, const void* q, const void* k, const void* v,
                               const float* g, const float* beta, const float* S0, void* o, float* Sf, hipStream_t st);
+hipError_t chunk_split_dispatch(int64_t BH, int64_t T, int dk, int dv, const void* q, const void* k, const void* v,
+                                const float* g, const float* beta, const float* S0, void* o, float* Sf, void* ws,
+                                hipStream_t st);
+int64_t chunk_split_workspace_bytes(int64_t BH, int64_t T);
 hipError_t chunk_fwd_pc_prep_dispatch(int64_t BH, int64_t H, int64_t T, int dk, int dv, const void* q_raw,
                                       const void* k_raw, const void* v, const float* dt, const float* A_log,
                                       const float* dt_bias, const float* beta_logit, const float* S0, void* o,
@@ -31,6 +35,8 @@ constexpr int kVersion = 10000 * 0 + 100 * 1 + 0;
 constexpr int64_t kMaxGrid = 0x7fffffff;
 // The kernels address one sequence with 32-bit byte offsets: T * d * 4 stays below 2^32.
 constexpr int64_t kMaxT = int64_t(1) << 22;
+// Chunk length of the chunked kernels.
+constexpr int64_t kChunkLen = 64;
 // Substeps per token of the Gated Delta Product forward.
 constexpr int kMaxNh = 16;
 
@@ -74,9 +80,16 @@ const char* gdr_status_string(int status) {
     }
 }
 
-gdr_status gdr_chunk_fwd(int64_t B, int64_t H, int64_t T, int d_k, int d_v, int io_dtype, int gate,
-                         const void* q, const void* k, const void* v, const float* g, const float* beta,
-                         const float* initial_state, void* o, float* final_state, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation shared by gdr_chunk_fwd and gdr_chunk_fwd_ws.  On success *launch tells whether
+// there is work to enqueue and *BH is B * H.
+gdr_status check_chunk(int64_t B, int64_t H, int64_t T, int d_k, int d_v, int io_dtype, int gate, const void* q,
+                       const void* k, const void* v, const float* g, const float* beta, const float* initial_state,
+                       const void* o, const float* final_state, int64_t* BHout, bool* launch) {
+    *launch = false;
     if (B < 0 || H < 0 || T < 0) return GDR_ERR_INVALID_ARG;
     gdr_status s = check_common(d_k, d_v, io_dtype, gate);
     if (s != GDR_OK) return s;
@@ -97,20 +110,86 @@ gdr_status gdr_chunk_fwd(int64_t B, int64_t H, int64_t T, int d_k, int d_v, int 
         overlaps(final_state, nstate, initial_state, nstate))
         return GDR_ERR_INVALID_ARG;
     if (io_dtype == GDR_F32 && (d_k != 64 || gate == GDR_GATE_CHANNEL)) return GDR_ERR_UNSUPPORTED;
+    *BHout = BH;
     if (BH == 0) return GDR_OK;
     int64_t nwg;
     if (!mul_ok(BH, d_v / 32, &nwg) || nwg > kMaxGrid) return GDR_ERR_SHAPE;
-    if (!final_state && BHT == 0) return GDR_OK;
-    hipError_t e;
+    *launch = final_state != nullptr || BHT > 0;
+    return GDR_OK;
+}
+
+hipError_t chunk_single_kernel(int64_t BH, int64_t T, int d_k, int d_v, int io_dtype, int gate, const void* q,
+                               const void* k, const void* v, const float* g, const float* beta,
+                               const float* initial_state, void* o, float* final_state, hipStream_t st) {
     if (io_dtype == GDR_BF16 && gate == GDR_GATE_CHANNEL)  // per-channel gate, fp16 MFMA
-        e = gdr::chunk_kda_dispatch(BH, T, d_k, d_v, q, k, v, g, beta, initial_state, o, final_state,
-                                    static_cast<hipStream_t>(stream));
-    else if (io_dtype == GDR_BF16)  // fp16-MFMA producer/consumer kernel
-        e = gdr::chunk_fwd_pc_dispatch(BH, T, 1, d_k, d_v, q, k, v, g, beta, initial_state, o, final_state,
-                                       static_cast<hipStream_t>(stream));
-    else  // fp32 operands throughout
-        e = gdr::chunk_fwd_dispatch(BH, T, d_k, d_v, false, gate == GDR_GATE_CHANNEL, q, k, v, g, beta,
-                                    initial_state, o, final_state, static_cast<hipStream_t>(stream));
+        return gdr::chunk_kda_dispatch(BH, T, d_k, d_v, q, k, v, g, beta, initial_state, o, final_state, st);
+    if (io_dtype == GDR_BF16)  // fp16-MFMA producer/consumer kernel
+        return gdr::chunk_fwd_pc_dispatch(BH, T, 1, d_k, d_v, q, k, v, g, beta, initial_state, o, final_state, st);
+    // fp32 operands throughout
+    return gdr::chunk_fwd_dispatch(BH, T, d_k, d_v, false, gate == GDR_GATE_CHANNEL, q, k, v, g, beta, initial_state,
+                                   o, final_state, st);
+}
+
+// The two-kernel path serves the scalar gate with bf16 I/O.
+bool uses_workspace(int io_dtype, int gate) { return io_dtype == GDR_BF16 && gate == GDR_GATE_SCALAR; }
+
+}  // namespace
+
+extern "C" {
+
+gdr_status gdr_chunk_fwd(int64_t B, int64_t H, int64_t T, int d_k, int d_v, int io_dtype, int gate,
+                         const void* q, const void* k, const void* v, const float* g, const float* beta,
+                         const float* initial_state, void* o, float* final_state, void* stream) {
+    int64_t BH = 0;
+    bool launch = false;
+    gdr_status s = check_chunk(B, H, T, d_k, d_v, io_dtype, gate, q, k, v, g, beta, initial_state, o, final_state,
+                               &BH, &launch);
+    if (s != GDR_OK || !launch) return s;
+    hipError_t e = chunk_single_kernel(BH, T, d_k, d_v, io_dtype, gate, q, k, v, g, beta, initial_state, o,
+                                       final_state, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+}
+
+int64_t gdr_chunk_fwd_workspace_size(int64_t B, int64_t H, int64_t T, int d_k, int d_v, int io_dtype, int gate) {
+    if (B < 0 || H < 0 || T < 0 || T > kMaxT) return -1;
+    if (check_common(d_k, d_v, io_dtype, gate) != GDR_OK) return -1;
+    int64_t BH, BHT, bytes;
+    if (!mul_ok(B, H, &BH) || !mul_ok(BH, T + kChunkLen, &BHT) || !mul_ok(BHT, 4 * kChunkLen, &bytes)) return -1;
+    if (!uses_workspace(io_dtype, gate)) return 0;
+    return gdr::chunk_split_workspace_bytes(BH, T);
+}
+
+gdr_status gdr_chunk_fwd_ws(int64_t B, int64_t H, int64_t T, int d_k, int d_v, int io_dtype, int gate,
+                            const void* q, const void* k, const void* v, const float* g, const float* beta,
+                            const float* initial_state, void* o, float* final_state, void* workspace,
+                            int64_t workspace_bytes, void* stream) {
+    int64_t BH = 0;
+    bool launch = false;
+    gdr_status s = check_chunk(B, H, T, d_k, d_v, io_dtype, gate, q, k, v, g, beta, initial_state, o, final_state,
+                               &BH, &launch);
+    if (s != GDR_OK) return s;
+    if (workspace_bytes < 0) return GDR_ERR_INVALID_ARG;
+    const int64_t need = gdr_chunk_fwd_workspace_size(B, H, T, d_k, d_v, io_dtype, gate);
+    if (need < 0) return GDR_ERR_SHAPE;
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return GDR_ERR_INVALID_ARG;
+    if (need > 0) {
+        // the workspace is written by the first kernel: it may overlap no input and no output
+        const int64_t esz = 2, BHT = BH * T;
+        if (overlaps(workspace, need, q, BHT * d_k * esz) || overlaps(workspace, need, k, BHT * d_k * esz) ||
+            overlaps(workspace, need, v, BHT * d_v * esz) || overlaps(workspace, need, g, BHT * 4) ||
+            overlaps(workspace, need, beta, BHT * 4) || overlaps(workspace, need, o, BHT * d_v * esz) ||
+            overlaps(workspace, need, initial_state, BH * d_k * d_v * 4) ||
+            overlaps(workspace, need, final_state, BH * d_k * d_v * 4))
+            return GDR_ERR_INVALID_ARG;
+    }
+    if (!launch) return GDR_OK;
+    hipError_t e;
+    if (need > 0)
+        e = gdr::chunk_split_dispatch(BH, T, d_k, d_v, q, k, v, g, beta, initial_state, o, final_state, workspace,
+                                      static_cast<hipStream_t>(stream));
+    else
+        e = chunk_single_kernel(BH, T, d_k, d_v, io_dtype, gate, q, k, v, g, beta, initial_state, o, final_state,
+                                static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
 }
 

@@ -19,7 +19,8 @@
  *
  * Conventions shared by every entry point
  *  - All tensor pointers are DEVICE pointers to contiguous row-major buffers owned by the
- *    caller.  The library allocates nothing and keeps no state between calls.
+ *    caller.  The library allocates nothing and keeps no state between calls; the one entry
+ *    point that needs scratch memory (gdr_chunk_fwd_ws) takes it from the caller.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only enqueue work and
  *    return; faults during execution surface at the caller's next synchronisation.
  *  - Every argument is validated on the host before anything is enqueued.  On any error the
@@ -99,6 +100,44 @@ gdr_status gdr_chunk_fwd(int64_t B, int64_t H, int64_t T, int d_k, int d_v,
                          const float *g, const float *beta,
                          const float *initial_state,
                          void *o, float *final_state, void *stream);
+
+/*
+ * gdr_chunk_fwd_workspace_size -- bytes of device workspace gdr_chunk_fwd_ws needs.
+ *
+ * Returns 0 for configurations that use no workspace (GDR_F32 I/O, GDR_GATE_CHANNEL), the
+ * size in bytes otherwise (16 KiB per sequence and 64-token chunk: B*H*ceil(T/64)*16384),
+ * and -1 for sizes or enums gdr_chunk_fwd would reject.
+ */
+int64_t gdr_chunk_fwd_workspace_size(int64_t B, int64_t H, int64_t T, int d_k, int d_v,
+                                     int io_dtype, int gate);
+
+/*
+ * gdr_chunk_fwd_ws -- gdr_chunk_fwd with a caller-provided device workspace.
+ *
+ * Same inputs, outputs, numerics and errors as gdr_chunk_fwd.  With bf16 I/O and the scalar
+ * gate it runs the per-chunk algorithm as two kernels: the first forms, for every chunk at
+ * once, T = N^{-1} diag(beta) (the UT transform) and the decayed score matrix A, and writes
+ * them to the workspace; the second walks the chunks in order with
+ * Z = T (V - diag(e^G) K S^T).  ("Linear Attention, Visualized", section "Gated DeltaNet
+ * (GDN)", "Complete per-chunk algorithm": the chunk-local quantities can be formed for all
+ * chunks in parallel.)  Other configurations ignore the workspace and behave exactly like
+ * gdr_chunk_fwd.
+ *
+ *   workspace        device buffer of at least gdr_chunk_fwd_workspace_size(...) bytes, owned
+ *                    by the caller; contents on entry are ignored and on return undefined; it
+ *                    must not overlap any input or output (GDR_ERR_INVALID_ARG)
+ *   workspace_bytes  its size; smaller than required (or a NULL workspace when one is
+ *                    required) returns GDR_ERR_INVALID_ARG
+ *
+ * Calls that share a workspace must be ordered on one stream.
+ */
+gdr_status gdr_chunk_fwd_ws(int64_t B, int64_t H, int64_t T, int d_k, int d_v,
+                            int io_dtype, int gate,
+                            const void *q, const void *k, const void *v,
+                            const float *g, const float *beta,
+                            const float *initial_state,
+                            void *o, float *final_state,
+                            void *workspace, int64_t workspace_bytes, void *stream);
 
 /*
  * gdr_chunk_fwd_fused_prep -- gdr_chunk_fwd (scalar gate) from raw projections, with the

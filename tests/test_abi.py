@@ -89,6 +89,43 @@ def test_chunk_fwd_empty_batch_is_a_noop(lib):
     assert chunk(lib, H=0, q=None, k=None, v=None, g=None, beta=None, o=None) == OK
 
 
+def test_workspace_size(lib):
+    n = lib.gdr_chunk_fwd_workspace_size
+    assert n(4, 16, 4096, 128, 128, 0, 0) == 64 * 64 * 16384        # 16 KiB per (sequence, chunk)
+    assert n(1, 1, 65, 64, 32, 0, 0) == 2 * 16384                    # ragged tail counts as a chunk
+    assert n(1, 1, 0, 128, 128, 0, 0) == 0
+    assert n(2, 2, 100, 64, 64, 1, 0) == 0                           # fp32 I/O: single kernel
+    assert n(2, 2, 100, 128, 128, 0, 1) == 0                         # channel gate: single kernel
+    assert n(1, 1, 64, 96, 128, 0, 0) == -1 and n(-1, 1, 64, 128, 128, 0, 0) == -1
+    assert n(1, 1, (1 << 22) + 1, 128, 128, 0, 0) == -1
+    assert gdr.chunk_fwd_workspace_size(1, 2, 128, 128, 128) == 2 * 2 * 16384
+
+
+def ws(lib, B=1, H=1, T=64, dk=128, dv=128, io=0, gate=0, q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, s0=None,
+       o=FAKE2, sf=None, w=ctypes.c_void_p(0x50000000), nbytes=1 << 20):
+    return lib.gdr_chunk_fwd_ws(B, H, T, dk, dv, io, gate, q, k, v, g, beta, s0, o, sf, w, nbytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), INVALID), (dict(dk=96), SHAPE), (dict(io=2), DTYPE), (dict(q=None), INVALID),
+    (dict(o=FAKE), INVALID),                                    # o overlaps q
+    (dict(w=None), INVALID),                                    # a workspace is required
+    (dict(nbytes=16383), INVALID),                              # one chunk needs 16 KiB
+    (dict(nbytes=-1), INVALID),
+    (dict(w=FAKE), INVALID),                                    # workspace overlaps q
+    (dict(w=FAKE2), INVALID),                                   # workspace overlaps o
+    (dict(T=(1 << 22) + 1), SHAPE),
+    (dict(io=1, dk=128), UNSUP),
+])
+def test_chunk_fwd_ws_rejects(lib, kw, status):
+    assert ws(lib, **kw) == status
+
+
+def test_chunk_fwd_ws_noops(lib):
+    assert ws(lib, B=0) == OK
+    assert ws(lib, T=0, q=None, k=None, v=None, g=None, beta=None, o=None, w=None, nbytes=0) == OK
+
+
 def gdp(lib, B=1, H=1, T=64, nh=2, dk=128, dv=128, io=0, q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE,
         s0=None, o=FAKE2, sf=None):
     return lib.gdr_gdp_chunk_fwd(B, H, T, nh, dk, dv, io, q, k, v, g, beta, s0, o, sf, None)

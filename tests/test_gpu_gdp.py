@@ -84,13 +84,14 @@ def test_gdp_many_substeps(nh, T):
 
 def test_gdp_equals_chunk_fwd_on_the_virtual_sequence():
     """The GDP kernel reads q, g and writes o through the substep mapping; fed the expanded
-    virtual sequence, the plain chunked forward must give the same bits."""
+    virtual sequence, the single-kernel chunked forward (the same kernel body) must give the
+    same bits."""
     w = variant(nh=3)
     x = gdr_synth.make_inputs(w, B=2, H=3, T=150)
     S0 = state(3, 2, 3, 128, 128)
     o, S = run_gdp(x, S0)
     qt, kt, vt, gt, bt, keep = oracle.gdp_as_virtual_gdn(x["q"], x["k"], x["v"], x["g"], x["beta"])
-    ov, Sv = gdr.chunk_fwd(dev(qt, True), dev(kt, True), dev(vt, True), dev(gt), dev(bt), dev(S0))
+    ov, Sv = gdr.chunk_fwd(dev(qt, True), dev(kt, True), dev(vt, True), dev(gt), dev(bt), dev(S0), workspace=None)
     torch.cuda.synchronize()
     assert torch.equal(o, ov[:, :, torch.from_numpy(keep).to(DEV)])
     assert torch.equal(S, Sv)
@@ -101,7 +102,8 @@ def test_gdp_one_substep_is_chunk_fwd():
     x = gdr_synth.make_inputs(w, B=1, H=4, T=200)
     o, S = gdr.gdp_chunk_fwd(dev(x["q"], True), dev(x["k"][:, :, :, None], True), dev(x["v"][:, :, :, None], True),
                              dev(x["g"]), dev(x["beta"][:, :, :, None]))
-    o2, S2 = gdr.chunk_fwd(dev(x["q"], True), dev(x["k"], True), dev(x["v"], True), dev(x["g"]), dev(x["beta"]))
+    o2, S2 = gdr.chunk_fwd(dev(x["q"], True), dev(x["k"], True), dev(x["v"], True), dev(x["g"]), dev(x["beta"]),
+                           workspace=None)
     torch.cuda.synchronize()
     assert torch.equal(o, o2) and torch.equal(S, S2)
 

@@ -104,16 +104,45 @@ def test_decode_full_size_64_steps_sampled():
 
 
 # ----------------------------------------------------------------------------- chunk_fwd
+# "split": gdr_chunk_fwd_ws (UT kernel for all chunks, then the state pass); "single":
+# gdr_chunk_fwd (one producer/consumer kernel)
+PATHS = {"split": "auto", "single": None}
+
+
 @pytest.mark.parametrize("T", [1, 37, 64, 65, 200])
 @pytest.mark.parametrize("dk,dv", [(128, 128), (128, 32), (64, 64), (128, 256), (64, 96)])
 @pytest.mark.parametrize("with_s0", [False, True])
-def test_chunk_small_bf16(T, dk, dv, with_s0):
+@pytest.mark.parametrize("path", sorted(PATHS))
+def test_chunk_small_bf16(T, dk, dv, with_s0, path):
     w = variant(2, d_k=dk, d_v=dv)
     x = gdr_synth.make_inputs(w, B=2, H=2, T=T)
     S0 = (np.random.default_rng(T).standard_normal((2, 2, dv, dk)) * 0.05).astype(np.float32) if with_s0 else None
-    o, S = run_chunk(x, True, S0)
+    o, S = run_chunk(x, True, S0, workspace=PATHS[path])
     o_ref, S_ref = oracle.recurrent_forward(x["q"], x["k"], x["v"], x["g"], x["beta"], S0)
-    check(f"chunk bf16 T={T} dk={dk} dv={dv} s0={with_s0}", o, S, o_ref, S_ref, True)
+    check(f"chunk bf16 {path} T={T} dk={dk} dv={dv} s0={with_s0}", o, S, o_ref, S_ref, True)
+
+
+def test_chunk_split_equals_single_closely():
+    """The two paths compute the same algebra with different roundings (T formed densely in
+    the split path, blockwise substitution in the single kernel): they agree within the
+    outputs' bf16 rounding."""
+    x = gdr_synth.make_inputs(gdr_synth.WORKLOADS[2], B=2, H=4, T=333)
+    o1, S1 = run_chunk(x, True, None, workspace="auto")
+    o2, S2 = run_chunk(x, True, None, workspace=None)
+    assert err_bf16_out(host(o1), host(o2)) <= TOL_BF16
+    assert err_literal(host(S1), host(S2)) <= TOL_BF16
+
+
+def test_chunk_split_explicit_workspace_reused():
+    """A caller-owned workspace, reused across calls of different sizes (its contents on
+    entry do not matter)."""
+    need = gdr.chunk_fwd_workspace_size(2, 2, 300, 128, 128)
+    wsb = torch.full((need,), 0xFF, dtype=torch.uint8, device=DEV)
+    for T in (300, 70, 5):
+        x = gdr_synth.make_inputs(gdr_synth.WORKLOADS[2], B=2, H=2, T=T, salt=T)
+        o, S = run_chunk(x, True, None, workspace=wsb)
+        o_ref, S_ref = oracle.recurrent_forward(x["q"], x["k"], x["v"], x["g"], x["beta"])
+        check(f"chunk split, reused workspace T={T}", o, S, o_ref, S_ref, True)
 
 
 @pytest.mark.parametrize("T", [1, 63, 100, 256])
@@ -135,10 +164,10 @@ def test_chunk_workload1_tiny_f32():
     check("workload 1 (tiny fp32)", o, S, o_ref, S_ref, False)
 
 
-def _sampled_full(wid, nsample, seed):
+def _sampled_full(wid, nsample, seed, **kw):
     w = gdr_synth.WORKLOADS[wid]
     x = gdr_synth.make_inputs(w)
-    o, S = run_chunk(x, True, x["S0"])
+    o, S = run_chunk(x, True, x["S0"], **kw)
     rng = np.random.default_rng(seed)
     pick = np.sort(rng.choice(w.B * w.H, size=nsample, replace=False))
     bi, hi = pick // w.H, pick % w.H
@@ -149,16 +178,18 @@ def _sampled_full(wid, nsample, seed):
     return o_s, S_s, o_ref, S_ref
 
 
-def test_chunk_workload2_full_size_sampled():
+@pytest.mark.parametrize("path", sorted(PATHS))
+def test_chunk_workload2_full_size_sampled(path):
     """B=4, H=16, T=4096, d=128 bf16; 8 of the 64 sequences checked."""
-    o, S, o_ref, S_ref = _sampled_full(2, 8, 2)
-    check("workload 2 full size (8 sampled heads)", o, S, o_ref, S_ref, True)
+    o, S, o_ref, S_ref = _sampled_full(2, 8, 2, workspace=PATHS[path])
+    check(f"workload 2 full size, {path} (8 sampled heads)", o, S, o_ref, S_ref, True)
 
 
-def test_chunk_workload4_full_size_sampled():
+@pytest.mark.parametrize("path", sorted(PATHS))
+def test_chunk_workload4_full_size_sampled(path):
     """B=1, H=32, T=65536, d=128 bf16 with a carried initial state; 2 heads checked."""
-    o, S, o_ref, S_ref = _sampled_full(4, 2, 4)
-    check("workload 4 full size (2 sampled heads)", o, S, o_ref, S_ref, True)
+    o, S, o_ref, S_ref = _sampled_full(4, 2, 4, workspace=PATHS[path])
+    check(f"workload 4 full size, {path} (2 sampled heads)", o, S, o_ref, S_ref, True)
 
 
 # ----------------------------------------------------------------------------- chunk_fwd, per-channel gate
