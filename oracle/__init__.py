@@ -20,6 +20,9 @@ Two independent fp64 implementations live here:
   pages' convention), beta = sigmoid(logit) in (0, 1), and Mamba-2's decay gate
   g = log a = -exp(A_log) softplus(dt + dt_bias) ("Linear Attention, Visualized",
   "Optional: Constructing the decay gate"), in numpy fp64.
+* ``frame.frame_forward`` -- the frame-level implicit update of the video
+  delta-rule post ("A Different Route"): per frame, S_t (I + G_t) = S_{t-1} D_t + C_t
+  by a Cholesky factorisation and triangular solves, in numpy fp64.
 * ``gdn2_forward`` -- Gated DeltaNet-2 token by token ("Gated DeltaNet-2, and the
   gate that was doing two jobs", section 2 "What decoupling actually means here"):
   KDA's decay with the scalar beta split into a key-side erase gate and a
@@ -261,3 +264,4 @@ def gdp_as_virtual_gdn(q, k, v, g, beta):
 
 
 from .chunked import chunked_forward, chunk_transform  # noqa: E402,F401
+from .frame import frame_forward  # noqa: E402,F401
