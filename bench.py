@@ -231,6 +231,62 @@ def bench_prep(torch, gdr, gdr_synth, steps=20):
             "separate_prep_pass_hbm_floor_ms": round(separate_pass / (PEAK_HBM * 1e9) * 1e3, 4)}
 
 
+def bench_frame(torch, gdr, gdr_synth, steps=10):
+    """Frame-level implicit update on B=1, H=16, T=16384 as 16 frames of 1024 tokens, d=128,
+    per-channel frame gate.  Algorithmic flops per (frame, head): the lower triangle of
+    G = K^T Gamma K (n d_k^2), C = V^T Gamma K (2 n d_k d_v), the inverse of I + G (2 d_k^3),
+    the state step (2 d_k^2 d_v) and the outputs (2 n d_k d_v)."""
+    wf = gdr_synth.FRAME_WORKLOAD
+    n, dk, dv = wf["frame_len"], wf["d_k"], wf["d_v"]
+    sets = []
+    for salt in range(2):
+        x = gdr_synth.make_frame_inputs(B=wf["B"], H=wf["H"], T=wf["T"], frame_len=n, d_k=dk, d_v=dv, salt=salt)
+        sets.append({kk: to_dev(torch, x[kk], kk in ("q", "k", "v")) for kk in ("q", "k", "v", "gamma", "g")})
+        if salt == 0:
+            host = x
+    need = gdr.frame_fwd_workspace_size(wf["B"], wf["H"], wf["T"], n, dk, dv)
+    wsb = torch.empty(need, dtype=torch.uint8, device="cuda")
+    outs = [torch.empty((wf["B"], wf["H"], wf["T"], dv), dtype=torch.bfloat16, device="cuda") for _ in sets]
+    fin = [torch.empty((wf["B"], wf["H"], dv, dk), dtype=torch.float32, device="cuda") for _ in sets]
+
+    def launch(i):
+        s_ = sets[i % 2]
+        gdr.frame_fwd(s_["q"], s_["k"], s_["v"], s_["gamma"], s_["g"], n, out=outs[i % 2], final_state=fin[i % 2],
+                      workspace=wsb)
+
+    for i in range(2):
+        launch(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record()
+        launch(i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    F = wf["T"] // n
+    per = n * dk * dk + 2 * n * dk * dv + 2 * dk ** 3 + 2 * dk * dk * dv + 2 * n * dk * dv
+    flops = wf["B"] * wf["H"] * F * per
+    nbytes = wf["B"] * wf["H"] * wf["T"] * ((2 * dk + 2 * dv) * 2 + 4) + wf["B"] * wf["H"] * F * dk * 4
+    from oracle.frame import frame_forward
+    from parity import err_bf16_out, err_literal
+    sub = {kk: (None if host[kk] is None else host[kk][:, :1]) for kk in host}
+    o_ref, S_ref = frame_forward(sub["q"], sub["k"], sub["v"], sub["gamma"], sub["g"], n)
+    launch(0)
+    torch.cuda.synchronize()
+    return {"workload": "frame_bf16: frame-level implicit update B=1 H=16 T=16384 (16 frames x 1024 tokens) "
+                        "d_k=d_v=128 bf16, per-channel frame gate",
+            "kernels": "frame_gram_kernel<128,128> + frame_state_kernel<128,128> + frame_out_kernel<128,128>",
+            "ms_per_call": round(ms, 4), "tokens_per_s": round(wf["B"] * wf["T"] / (ms * 1e-3), 1),
+            "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_MFMA_F16, 4),
+            "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM, 4),
+            "flops_per_launch": flops, "bytes_per_launch": nbytes,
+            "parity_sampled": {"heads_checked": 1,
+                               "e_o": round(err_bf16_out(outs[0][:, :1].float().cpu().numpy().astype(np.float64),
+                                                         o_ref), 6),
+                               "e_S": round(err_literal(fin[0][:, :1].cpu().numpy().astype(np.float64), S_ref), 6)}}
+
+
 def bench_gdn2(torch, gdr, gdr_synth, steps=10):
     """Gated DeltaNet-2 forward on B=2, H=16, T=8192, d=128 (per-channel decay, erase gate b,
     write gate w).  Algorithmic flops as the chunked forward; bytes: q, k, v, o in bf16, g and
@@ -403,6 +459,7 @@ def main():
         result["gdp"] = bench_gdp(torch, gdr, gdr_synth)
         result["gdn2"] = bench_gdn2(torch, gdr, gdr_synth)
         result["fused_prep"] = bench_prep(torch, gdr, gdr_synth)
+        result["frame"] = bench_frame(torch, gdr, gdr_synth)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(w, sets[0]["host"])
     print(json.dumps(result))

@@ -6,13 +6,14 @@ torch-allocated workspace); ``chunk_fwd_fused_prep`` runs it from raw
 projections (normalisation and gates fused in); ``gdp_chunk_fwd`` is the same pass
 for the Gated Delta Product (n_h key/value/beta substeps per token) and
 ``gdn2_chunk_fwd`` for Gated DeltaNet-2 (separate erase and write gates);
+``frame_fwd`` runs the frame-level implicit update (tokens in unordered frames);
 ``decode_step`` advances resident states by one token in place.  The HIP
 library is loaded on first use and its absence is an error: there is no CPU
 fallback.
 """
 from ._binding import (EXPORTED_SYMBOLS, LIBRARY_PATH, GdrError, chunk_fwd, chunk_fwd_fused_prep,
-                       chunk_fwd_workspace_size, decode_step, gdn2_chunk_fwd, gdp_chunk_fwd, load_library,
-                       status_string, version)
+                       chunk_fwd_workspace_size, decode_step, frame_fwd, frame_fwd_workspace_size, gdn2_chunk_fwd,
+                       gdp_chunk_fwd, load_library, status_string, version)
 
-__all__ = ["chunk_fwd", "chunk_fwd_workspace_size", "chunk_fwd_fused_prep", "gdp_chunk_fwd", "gdn2_chunk_fwd", "decode_step", "GdrError", "load_library", "version", "status_string",
+__all__ = ["chunk_fwd", "chunk_fwd_workspace_size", "chunk_fwd_fused_prep", "frame_fwd", "frame_fwd_workspace_size", "gdp_chunk_fwd", "gdn2_chunk_fwd", "decode_step", "GdrError", "load_library", "version", "status_string",
            "LIBRARY_PATH", "EXPORTED_SYMBOLS"]

@@ -21,7 +21,7 @@ GDR_GATE_SCALAR, GDR_GATE_CHANNEL = 0, 1
 # every entry point include/gdr.h declares
 EXPORTED_SYMBOLS = ("gdr_version", "gdr_status_string", "gdr_chunk_fwd", "gdr_chunk_fwd_workspace_size",
                     "gdr_chunk_fwd_ws", "gdr_chunk_fwd_fused_prep", "gdr_gdp_chunk_fwd", "gdr_gdn2_chunk_fwd",
-                    "gdr_decode_step")
+                    "gdr_frame_fwd_workspace_size", "gdr_frame_fwd", "gdr_decode_step")
 
 _lock = threading.Lock()
 _lib = None
@@ -59,6 +59,10 @@ def load_library():
         lib.gdr_gdp_chunk_fwd.argtypes = [i64, i64, i64, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P]
         lib.gdr_gdn2_chunk_fwd.restype = i32
         lib.gdr_gdn2_chunk_fwd.argtypes = [i64, i64, i64, i32, i32, i32, P, P, P, P, P, P, P, P, P, P]
+        lib.gdr_frame_fwd_workspace_size.restype = i64
+        lib.gdr_frame_fwd_workspace_size.argtypes = [i64, i64, i64, i32, i32, i32]
+        lib.gdr_frame_fwd.restype = i32
+        lib.gdr_frame_fwd.argtypes = [i64, i64, i64, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, i64, P]
         lib.gdr_decode_step.restype = i32
         lib.gdr_decode_step.argtypes = [i64, i64, i32, i32, i32, i32, P, P, P, P, P, P, P, P]
         _lib = lib
@@ -285,6 +289,60 @@ def gdn2_chunk_fwd(q, k, v, g, b, w, initial_state=None, *, output_final_state=T
                                            _stream(stream, dev))
     if st != GDR_OK:
         raise GdrError(st, "gdr_gdn2_chunk_fwd")
+    return o, final_state
+
+
+def frame_fwd_workspace_size(B, H, T, frame_len, d_k, d_v) -> int:
+    n = int(load_library().gdr_frame_fwd_workspace_size(B, H, T, frame_len, d_k, d_v))
+    if n < 0:
+        raise GdrError(GDR_ERR_SHAPE, "gdr_frame_fwd_workspace_size")
+    return n
+
+
+def frame_fwd(q, k, v, gamma, g, frame_len, initial_state=None, *, output_final_state=True, out=None,
+              final_state=None, workspace=None, stream=None):
+    """gdr_frame_fwd (frame-level implicit update) on torch tensors.
+
+    q, k [B,H,T,d_k]; v [B,H,T,d_v] (bf16); gamma [B,H,T] fp32; g [B,H,F] or [B,H,F,d_k]
+    fp32 (log forget gate per frame, F = ceil(T / frame_len)); initial_state [B,H,d_v,d_k]
+    fp32 or None; workspace: a uint8 CUDA tensor or None (allocated with torch).
+    Returns (o, final_state); final_state is None when output_final_state is False.
+    """
+    import torch
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("frame_fwd needs GPU tensors")
+    io = _io_dtype(q)
+    F = (T + frame_len - 1) // frame_len
+    _check(k, "k", (B, H, T, dk), q.dtype, dev)
+    _check(v, "v", (B, H, T, dv), q.dtype, dev)
+    _check(gamma, "gamma", (B, H, T), torch.float32, dev)
+    if g.shape == (B, H, F):
+        gate = GDR_GATE_SCALAR
+    elif g.shape == (B, H, F, dk):
+        gate = GDR_GATE_CHANNEL
+    else:
+        raise ValueError(f"g: expected [B,H,F] or [B,H,F,d_k] with F={F}, got {tuple(g.shape)}")
+    _check(g, "g", tuple(g.shape), torch.float32, dev)
+    if initial_state is not None:
+        _check(initial_state, "initial_state", (B, H, dv, dk), torch.float32, dev)
+    o = torch.empty((B, H, T, dv), dtype=q.dtype, device=dev) if out is None else out
+    _check(o, "out", (B, H, T, dv), q.dtype, dev)
+    if output_final_state and final_state is None:
+        final_state = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+    if final_state is not None:
+        _check(final_state, "final_state", (B, H, dv, dk), torch.float32, dev)
+    if workspace is None:
+        workspace = torch.empty(max(frame_fwd_workspace_size(B, H, T, frame_len, dk, dv), 1), dtype=torch.uint8,
+                                device=dev)
+    nbytes = workspace.numel() * workspace.element_size()
+    st = load_library().gdr_frame_fwd(B, H, T, frame_len, dk, dv, io, gate, _ptr(q), _ptr(k), _ptr(v), _ptr(gamma),
+                                      _ptr(g), _ptr(initial_state), _ptr(o), _ptr(final_state), _ptr(workspace),
+                                      nbytes, _stream(stream, dev))
+    if st != GDR_OK:
+        raise GdrError(st, "gdr_frame_fwd")
     return o, final_state
 
 

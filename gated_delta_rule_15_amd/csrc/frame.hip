@@ -1,0 +1,485 @@
+// frame.hip -- the frame-level implicit delta-rule update, bf16 I/O, gfx950.
+//
+// The video delta-rule post (haoyizhu.site, "video-delta-rule"), section "A Different Route":
+// tokens come in frames of n with no order inside a frame, and one frame moves the state by
+// one implicit (backward-Euler) gradient step on the frame's total loss.  Column convention,
+// S in R^{d_v x d_k}:
+//   G_t = K_t^T Gamma_t K_t,   C_t = V_t^T Gamma_t K_t,   S_t (I + G_t) = S_{t-1} D_t + C_t,
+//   o_{t,i} = S_t q_{t,i}  for every token of frame t,
+// with Gamma_t the per-token writing strengths and D_t the frame's forget gate (scalar or per
+// key channel) applied to the old state first.  I + G_t does not depend on the state, so
+// everything but one product per frame runs for all frames at once:
+//
+//   frame_gram_kernel   one workgroup per (sequence, frame): G and C by fp16 MFMA over the
+//                       frame's tokens (operands sqrt(gamma) k and sqrt(gamma) v, fp32
+//                       accumulation), then W = (I + G)^{-1} by in-place Gauss-Jordan
+//                       elimination in fp32 registers (I + G is symmetric positive definite
+//                       with eigenvalues >= 1, so no pivoting is needed), written as a pair of
+//                       fp16 matrices W = W_hi + W_lo, and C in fp32;
+//   frame_state_kernel  one workgroup per (sequence, 64 value channels), frames in order:
+//                       S_t^T = W_t (D_t S_{t-1}^T + C_t^T) on fp16 MFMA with both factors split
+//                       into high and low halves (three products: hi.hi + hi.lo + lo.hi), which
+//                       keeps the chained state at fp32-class accuracy; S_t is written in fp16
+//                       for the outputs;
+//   frame_out_kernel    one workgroup per (sequence, 64 tokens): O = Q S_t^T.
+// The post solves the system by a Cholesky factorisation; forming the inverse once per frame
+// instead keeps the serial pass to one product per frame (the same solution in exact
+// arithmetic; I + G is well conditioned, its eigenvalues lying in [1, 1 + tr G]).
+#include "chunk_common.h"
+
+namespace gdr {
+
+struct FrArgs {
+    int64_t T;
+    int64_t F;       // frames per sequence, ceil(T / n)
+    int n;           // tokens per frame (a multiple of 16)
+    int channel;     // gate per key channel (1) or scalar (0)
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const float* gamma;
+    const float* g;  // log forget gate, [.., F] or [.., F, DK]
+    const float* S0;
+    uint16_t* o;
+    float* Sf;
+    // workspace, per (sequence, frame): W_hi, W_lo [DK][DK] fp16, C [DV][DK] fp32, S [DV][DK] fp16
+    uint16_t* Wh;
+    uint16_t* Wl;
+    float* Cw;
+    uint16_t* Sw;
+};
+
+// ============================================================================ Gram + inverse
+
+template <int DK, int DV>
+struct FrGramLds {
+    static constexpr int LDK = DK + 16;   // halfs, token rows of sqrt(gamma) k
+    static constexpr int LDV = DV + 16;   // halfs, token rows of sqrt(gamma) v
+    static constexpr int LDA = DK + 4;    // floats, rows of I + G
+    static constexpr int oK = 0;
+    static constexpr int oV = oK + 64 * LDK * 2;
+    static constexpr int oA = oV + 64 * LDV * 2;
+    static constexpr int oRow = oA + DK * LDA * 4;   // pivot row, two buffers
+    static constexpr int oCol = oRow + 2 * DK * 4;   // pivot column, two buffers
+    static constexpr int total = oCol + 2 * DK * 4;
+    static_assert(total <= 160 * 1024, "LDS budget");
+};
+
+template <int DK, int DV>
+__global__ __launch_bounds__(256, 1) void frame_gram_kernel(const FrArgs a) {
+    using L = FrGramLds<DK, DV>;
+    constexpr int NT = DK / 16, NV = DV / 16;
+    constexpr int NSG = (NT + 3) / 4, NSC = (NV + 3) / 4;  // row tiles per wave
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    _Float16* Kp = reinterpret_cast<_Float16*>(smem + L::oK);
+    _Float16* Vp = reinterpret_cast<_Float16*>(smem + L::oV);
+    float* Am = reinterpret_cast<float*>(smem + L::oA);
+    float* rowb = reinterpret_cast<float*>(smem + L::oRow);
+    float* colb = reinterpret_cast<float*>(smem + L::oCol);
+
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, j = l & 15, g = l >> 4;
+    const int64_t bh = blockIdx.x / a.F;
+    const int64_t f = blockIdx.x - bh * a.F;
+    const int64_t T = a.T;
+    const int64_t t_beg = f * a.n;
+    const int64_t t_end = (t_beg + a.n < T) ? t_beg + a.n : T;
+    const auto rk = make_rsrc(a.k + bh * T * DK, (uint32_t)(T * DK * 2));
+    const auto rv = make_rsrc(a.v + bh * T * DV, (uint32_t)(T * DV * 2));
+    const auto rgm = make_rsrc(a.gamma + bh * T, (uint32_t)(T * 4));
+
+    auto trfrag = [&](const _Float16* base, int ld, int kb, int col) {
+        const _Float16* p0 = base + (32 * kb + 4 * g + (j >> 2)) * ld + col;
+        return cat8(ldtr(p0), ldtr(p0 + 16 * ld));
+    };
+
+    // accumulators: G row tiles ti = w + 4s (tiles tj <= ti), C row tiles vi = w + 4s
+    float4v accG[NSG][NT], accC[NSC][NT];
+#pragma unroll
+    for (int s = 0; s < NSG; ++s)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) accG[s][t] = zero4();
+#pragma unroll
+    for (int s = 0; s < NSC; ++s)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) accC[s][t] = zero4();
+
+    // ---- G and C over the frame's tokens, 64 at a time
+    for (int64_t t0 = t_beg; t0 < t_end; t0 += 64) {
+        // stage sqrt(gamma) k and sqrt(gamma) v (fp16); tokens outside the frame are zeros
+        constexpr int PK = 64 * DK / 8, PV = 64 * DV / 8;
+        for (int idx = tid; idx < PK + PV; idx += 256) {
+            const bool isk = idx < PK;
+            const int id2 = isk ? idx : idx - PK;
+            const int D = isk ? DK : DV;
+            const int row = id2 / (D / 8), col = (id2 % (D / 8)) * 8;
+            const int64_t tok = t0 + row;
+            uint4 u = uint4{0u, 0u, 0u, 0u};
+            float sg = 0.0f;
+            if (tok < t_end) {
+                u = isk ? bld16(rk, (uint32_t)((tok * DK + col) * 2)) : bld16(rv, (uint32_t)((tok * DV + col) * 2));
+                sg = sqrtf(bld4(rgm, (uint32_t)(tok * 4)));
+            }
+            const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
+            half8 h;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                h[2 * e] = (_Float16)(sg * __uint_as_float(wv[e] << 16));
+                h[2 * e + 1] = (_Float16)(sg * __uint_as_float(wv[e] & 0xffff0000u));
+            }
+            _Float16* dst = isk ? Kp + row * L::LDK + col : Vp + row * L::LDV + col;
+            *reinterpret_cast<half8*>(dst) = h;
+        }
+        lds_barrier();
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            half8 kf[NT];
+#pragma unroll
+            for (int t = 0; t < NT; ++t) kf[t] = trfrag(Kp, L::LDK, kb, 16 * t + 4 * (j & 3));
+#pragma unroll
+            for (int s = 0; s < NSG; ++s) {
+                const int ti = w + 4 * s;
+                if (ti < NT) {
+                    const half8 kr = trfrag(Kp, L::LDK, kb, 16 * ti + 4 * (j & 3));
+#pragma unroll
+                    for (int tj = 0; tj < NT; ++tj)
+                        if (tj <= ti) mma16(accG[s][tj], kr, kf[tj]);
+                }
+            }
+#pragma unroll
+            for (int s = 0; s < NSC; ++s) {
+                const int vi = w + 4 * s;
+                if (vi < NV) {
+                    const half8 vr = trfrag(Vp, L::LDV, kb, 16 * vi + 4 * (j & 3));
+#pragma unroll
+                    for (int tj = 0; tj < NT; ++tj) mma16(accC[s][tj], vr, kf[tj]);
+                }
+            }
+        }
+        lds_barrier();
+    }
+
+    // ---- I + G into LDS (both triangles), C to the workspace
+    const int64_t fi = bh * a.F + f;
+#pragma unroll
+    for (int s = 0; s < NSG; ++s) {
+        const int ti = w + 4 * s;
+        if (ti < NT) {
+#pragma unroll
+            for (int tj = 0; tj < NT; ++tj) {
+                if (tj <= ti) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int row = 16 * ti + 4 * g + r, col = 16 * tj + j;
+                        const float x = accG[s][tj][r] + (row == col ? 1.0f : 0.0f);
+                        Am[row * L::LDA + col] = x;
+                        Am[col * L::LDA + row] = x;
+                    }
+                }
+            }
+        }
+    }
+    float* cdst = a.Cw + fi * (int64_t)(DV * DK);
+#pragma unroll
+    for (int s = 0; s < NSC; ++s) {
+        const int vi = w + 4 * s;
+        if (vi < NV) {
+#pragma unroll
+            for (int tj = 0; tj < NT; ++tj)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) cdst[(16 * vi + 4 * g + r) * DK + 16 * tj + j] = accC[s][tj][r];
+        }
+    }
+    lds_barrier();
+
+    // ---- W = (I + G)^{-1}: in-place Gauss-Jordan.  Thread t holds CPT consecutive entries of
+    // row i; for pivot p every entry off row p and column p takes x -= (A[i][p] / A[p][p]) A[p][j],
+    // row p is divided by the pivot, column p becomes -A[i][p] / A[p][p], the pivot 1 / A[p][p].
+    constexpr int TPR = 256 / DK, CPT = DK / TPR;
+    const int ri = tid / TPR, c0 = (tid % TPR) * CPT;
+    float x[CPT];
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) x[c] = Am[ri * L::LDA + c0 + c];
+    for (int pb = 0; pb < TPR; ++pb) {
+        const bool owns_col = c0 == pb * CPT;
+        // fully unrolled, so that x[pp] is a register and not a scratch access
+#pragma clang loop unroll(full)
+        for (int pp = 0; pp < CPT; ++pp) {
+            const int p = pb * CPT + pp;
+            float* rb = rowb + (p & 1) * DK;
+            float* cb = colb + (p & 1) * DK;
+            if (owns_col) cb[ri] = x[pp];
+            if (ri == p) {
+#pragma unroll
+                for (int c = 0; c < CPT; c += 4)
+                    *reinterpret_cast<float4v*>(rb + c0 + c) = float4v{x[c], x[c + 1], x[c + 2], x[c + 3]};
+            }
+            lds_barrier();
+            const float rp = 1.0f / rb[p];
+            const float fac = cb[ri] * rp;
+            const bool prow = ri == p;
+            // row p: x = A[p][j] / piv; other rows: x -= fac * A[p][j]
+            const float keep = prow ? 0.0f : 1.0f;
+            const float cf = prow ? rp : -fac;
+#pragma unroll
+            for (int c = 0; c < CPT; c += 4) {
+                const float4v rv4 = *reinterpret_cast<const float4v*>(rb + c0 + c);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[c + e] = fmaf(rv4[e], cf, x[c + e] * keep);
+            }
+            if (owns_col) x[pp] = prow ? rp : -fac;
+        }
+    }
+    // W as W_hi + W_lo (fp16 each), rows natural
+    uint16_t* wh = a.Wh + fi * (int64_t)(DK * DK) + ri * DK + c0;
+    uint16_t* wl = a.Wl + fi * (int64_t)(DK * DK) + ri * DK + c0;
+#pragma unroll
+    for (int c = 0; c < CPT; c += 8) {
+        half8 hh, hl;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            hh[e] = (_Float16)x[c + e];
+            hl[e] = (_Float16)(x[c + e] - (float)hh[e]);
+        }
+        *reinterpret_cast<half8*>(wh + c) = hh;
+        *reinterpret_cast<half8*>(wl + c) = hl;
+    }
+}
+
+// ============================================================================ state pass
+
+template <int DK>
+struct FrStateLds {
+    static constexpr int LDW = DK + 8;  // halfs, rows of W_hi / W_lo
+    static constexpr int oWh = 0;
+    static constexpr int oWl = oWh + DK * LDW * 2;
+    static constexpr int total = oWl + DK * LDW * 2;
+};
+
+template <int DK, int DV>
+__global__ __launch_bounds__(256, 1) void frame_state_kernel(const FrArgs a) {
+    using L = FrStateLds<DK>;
+    constexpr int NKB = DK / 32, NST = DK / 16;
+    constexpr int NPW = DK * DK / 8 / 256;  // 16-byte pieces of one W matrix per thread
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    _Float16* Whs = reinterpret_cast<_Float16*>(smem + L::oWh);
+    _Float16* Wls = reinterpret_cast<_Float16*>(smem + L::oWl);
+
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, j = l & 15, g = l >> 4;
+    constexpr int NDT = DV / 64;  // workgroups per sequence
+    const int64_t bh = blockIdx.x / NDT;
+    const int dvc = (int)(blockIdx.x % NDT) * 64 + 16 * w;  // this wave's first value channel
+    const int64_t F = a.F;
+
+    // S^T of 16 value channels, rows permuted by pperm (row P holds key channel pperm(P))
+    float4v St[NST];
+#pragma unroll
+    for (int t = 0; t < NST; ++t) St[t] = zero4();
+    if (a.S0 != nullptr) {
+        const float* s0 = a.S0 + bh * (int64_t)DV * DK + (int64_t)(dvc + j) * DK;
+#pragma unroll
+        for (int t = 0; t < NST; ++t) St[t] = ld4f(s0 + pperm(16 * t + 4 * g));
+    }
+
+    // W of the next frame, prefetched into registers one frame ahead (buffer loads: the
+    // offsets stay below 2^31 per sequence)
+    const auto rwh = make_rsrc(a.Wh + bh * F * (int64_t)(DK * DK), (uint32_t)(F * DK * DK * 2));
+    const auto rwl = make_rsrc(a.Wl + bh * F * (int64_t)(DK * DK), (uint32_t)(F * DK * DK * 2));
+    uint4 wph[NPW], wpl[NPW];
+#pragma unroll
+    for (int u = 0; u < NPW; ++u) {
+        wph[u] = bld16(rwh, (uint32_t)((tid + 256 * u) * 16));
+        wpl[u] = bld16(rwl, (uint32_t)((tid + 256 * u) * 16));
+    }
+    for (int64_t f = 0; f < F; ++f) {
+        const int64_t fi = bh * F + f;
+        // W of this frame into LDS (the previous frame's readers are past the barrier below)
+#pragma unroll
+        for (int u = 0; u < NPW; ++u) {
+            const int idx = tid + 256 * u, row = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
+            *reinterpret_cast<uint4*>(Whs + row * L::LDW + col) = wph[u];
+            *reinterpret_cast<uint4*>(Wls + row * L::LDW + col) = wpl[u];
+        }
+        lds_barrier();
+        {
+            const uint32_t nb = (uint32_t)((f + 1) * DK * DK * 2);  // past the end: zeros, unused
+#pragma unroll
+            for (int u = 0; u < NPW; ++u) {
+                wph[u] = bld16(rwh, nb + (uint32_t)((tid + 256 * u) * 16));
+                wpl[u] = bld16(rwl, nb + (uint32_t)((tid + 256 * u) * 16));
+            }
+        }
+        // rhs^T = D S^T + C^T (rows permuted as S^T)
+        const float* cs = a.Cw + fi * (int64_t)(DV * DK) + (int64_t)(dvc + j) * DK;
+        const float* gf = a.g + (a.channel ? fi * DK : fi);
+        float4v rh[NST];
+#pragma unroll
+        for (int t = 0; t < NST; ++t) {
+            const int ch = pperm(16 * t + 4 * g);
+            const float4v c4 = ld4f(cs + ch);
+            float4v d4;
+            if (a.channel) {
+                const float4v g4 = ld4f(gf + ch);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) d4[r] = fast_exp(g4[r]);
+            } else {
+                const float d = fast_exp(gf[0]);
+                d4 = float4v{d, d, d, d};
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) rh[t][r] = fmaf(d4[r], St[t][r], c4[r]);
+        }
+        // operand halves: rhs = hi + lo
+        half8 bh8[NKB], bl8[NKB];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            bh8[kb] = pack8(rh[2 * kb], rh[2 * kb + 1]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float full = e < 4 ? rh[2 * kb][e] : rh[2 * kb + 1][e - 4];
+                bl8[kb][e] = (_Float16)(full - (float)bh8[kb][e]);
+            }
+        }
+        // S^T = W rhs^T: row tile t uses W rows pperm(16 t + j), 8 consecutive key channels
+#pragma unroll
+        for (int t = 0; t < NST; ++t) {
+            float4v acc = zero4();
+            const int wr = pperm(16 * t + j);
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                const half8 ah = ld8(Whs + wr * L::LDW + 32 * kb + 8 * g);
+                const half8 al = ld8(Wls + wr * L::LDW + 32 * kb + 8 * g);
+                mma16(acc, ah, bh8[kb]);
+                mma16(acc, ah, bl8[kb]);
+                mma16(acc, al, bh8[kb]);
+            }
+            St[t] = acc;
+        }
+        // S_t in fp16, [value channel][key channel], for the outputs
+        uint16_t* sd = a.Sw + fi * (int64_t)(DV * DK) + (int64_t)(dvc + j) * DK;
+#pragma unroll
+        for (int t = 0; t < NST; ++t) {
+            const half4 h = half4{(_Float16)St[t][0], (_Float16)St[t][1], (_Float16)St[t][2], (_Float16)St[t][3]};
+            *reinterpret_cast<half4*>(sd + pperm(16 * t + 4 * g)) = h;
+        }
+        lds_barrier();
+    }
+    if (a.Sf != nullptr) {
+        float* sf = a.Sf + bh * (int64_t)DV * DK + (int64_t)(dvc + j) * DK;
+#pragma unroll
+        for (int t = 0; t < NST; ++t) *reinterpret_cast<float4v*>(sf + pperm(16 * t + 4 * g)) = St[t];
+    }
+}
+
+// ============================================================================ outputs
+
+template <int DV>
+struct FrOutLds {
+    static constexpr int LDO = DV + 8;  // bf16, token rows of the output tile
+    static constexpr int total = 64 * LDO * 2;
+};
+
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void frame_out_kernel(const FrArgs a, int64_t nblk) {
+    using L = FrOutLds<DV>;
+    constexpr int NKB = DK / 32, NV = DV / 16;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    uint16_t* Ot = reinterpret_cast<uint16_t*>(smem);
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, j = l & 15, g = l >> 4;
+    const int64_t bh = blockIdx.x / nblk;
+    const int64_t blk = blockIdx.x - bh * nblk;
+    const int64_t T = a.T;
+    const int64_t tb = blk * 64 + 16 * w;  // this wave's 16 tokens, all in one frame
+    const auto rq = make_rsrc(a.q + bh * T * DK, (uint32_t)(T * DK * 2));
+    const auto ro = make_rsrc(a.o + bh * T * DV, (uint32_t)(T * DV * 2));
+    const int64_t f = (tb < T ? tb : T - 1) / a.n;
+    const uint16_t* S = a.Sw + (bh * a.F + f) * (int64_t)(DV * DK);
+
+    half8 qa[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+        qa[kb] = bf16x8_to_half8(bld16(rq, (uint32_t)(((tb + j) * DK + 32 * kb + 8 * g) * 2)));
+#pragma unroll
+    for (int vi = 0; vi < NV; ++vi) {
+        float4v acc = zero4();
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            const half8 sb = *reinterpret_cast<const half8*>(S + (16 * vi + j) * DK + 32 * kb + 8 * g);
+            mma16(acc, qa[kb], sb);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const uint32_t b2 = pack_bf16x2(acc[r], 0.0f);
+            Ot[(16 * w + 4 * g + r) * L::LDO + 16 * vi + j] = (uint16_t)(b2 & 0xffffu);
+        }
+    }
+    lds_fence();
+    // this wave's 16 token rows back as 16-byte pieces
+    constexpr int PPR = DV / 8;  // pieces per row
+#pragma unroll
+    for (int u = 0; u < 16 * PPR / 64; ++u) {
+        const int idx = l + 64 * u, row = idx / PPR, col = (idx % PPR) * 8;
+        const uint4 val = *reinterpret_cast<const uint4*>(Ot + (16 * w + row) * L::LDO + col);
+        bst16(ro, (uint32_t)(((tb + row) * DV + col) * 2), val);
+    }
+}
+
+// ============================================================================ host side
+
+int64_t frame_workspace_bytes(int64_t BH, int64_t T, int n, int dk, int dv) {
+    const int64_t F = (T + n - 1) / n;
+    return BH * F * ((int64_t)dk * dk * 2 * 2 + (int64_t)dv * dk * 4 + (int64_t)dv * dk * 2);
+}
+
+template <int DK, int DV>
+static hipError_t launch_frame(const FrArgs& a, int64_t BH, hipStream_t st) {
+    constexpr int lds_gram = FrGramLds<DK, DV>::total, lds_state = FrStateLds<DK>::total;
+    constexpr int lds_out = FrOutLds<DV>::total;
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(frame_gram_kernel<DK, DV>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, lds_gram);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    if (a.F > 0) {
+        hipLaunchKernelGGL((frame_gram_kernel<DK, DV>), dim3((unsigned)(BH * a.F)), dim3(256), lds_gram, st, a);
+    }
+    hipLaunchKernelGGL((frame_state_kernel<DK, DV>), dim3((unsigned)(BH * (DV / 64))), dim3(256), lds_state, st,
+                       a);
+    const int64_t nblk = (a.T + 63) / 64;
+    if (nblk > 0) {
+        hipLaunchKernelGGL((frame_out_kernel<DK, DV>), dim3((unsigned)(BH * nblk)), dim3(256), lds_out, st, a,
+                           nblk);
+    }
+    return hipGetLastError();
+}
+
+hipError_t frame_dispatch(int64_t BH, int64_t T, int n, int dk, int dv, bool channel, const void* q, const void* k,
+                          const void* v, const float* gamma, const float* g, const float* S0, void* o, float* Sf,
+                          void* ws, hipStream_t st) {
+    FrArgs a;
+    a.T = T;
+    a.F = (T + n - 1) / n;
+    a.n = n;
+    a.channel = channel ? 1 : 0;
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k);
+    a.v = static_cast<const uint16_t*>(v);
+    a.gamma = gamma;
+    a.g = g;
+    a.S0 = S0;
+    a.o = static_cast<uint16_t*>(o);
+    a.Sf = Sf;
+    const int64_t nf = BH * a.F;
+    char* base = static_cast<char*>(ws);
+    a.Wh = reinterpret_cast<uint16_t*>(base);
+    a.Wl = reinterpret_cast<uint16_t*>(base + nf * (int64_t)dk * dk * 2);
+    a.Cw = reinterpret_cast<float*>(base + nf * (int64_t)dk * dk * 4);
+    a.Sw = reinterpret_cast<uint16_t*>(base + nf * ((int64_t)dk * dk * 4 + (int64_t)dv * dk * 4));
+    if (dk == 128 && dv == 128) return launch_frame<128, 128>(a, BH, st);
+    if (dk == 128 && dv == 64) return launch_frame<128, 64>(a, BH, st);
+    if (dk == 64 && dv == 128) return launch_frame<64, 128>(a, BH, st);
+    return launch_frame<64, 64>(a, BH, st);
+}
+
+}  // namespace gdr

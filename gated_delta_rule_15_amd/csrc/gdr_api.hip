@@ -22,6 +22,10 @@ hipError_t chunk_fwd_pc_prep_dispatch(int64_t BH, int64_t H, int64_t T, int dk, 
                                       const void* k_raw, const void* v, const float* dt, const float* A_log,
                                       const float* dt_bias, const float* beta_logit, const float* S0, void* o,
                                       float* Sf, hipStream_t st);
+hipError_t frame_dispatch(int64_t BH, int64_t T, int n, int dk, int dv, bool channel, const void* q, const void* k,
+                          const void* v, const float* gamma, const float* g, const float* S0, void* o, float* Sf,
+                          void* ws, hipStream_t st);
+int64_t frame_workspace_bytes(int64_t BH, int64_t T, int n, int dk, int dv);
 hipError_t chunk_gdn2_dispatch(int64_t BH, int64_t T, int dk, int dv, const void* q, const void* k, const void* v,
                                const float* g, const float* b, const float* w, const float* S0, void* o, float* Sf,
                                hipStream_t st);
@@ -292,6 +296,58 @@ gdr_status gdr_gdn2_chunk_fwd(int64_t B, int64_t H, int64_t T, int d_k, int d_v,
     if (!final_state && BHT == 0) return GDR_OK;
     hipError_t e = gdr::chunk_gdn2_dispatch(BH, T, d_k, d_v, q, k, v, g, b, w, initial_state, o, final_state,
                                             static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+}
+
+int64_t gdr_frame_fwd_workspace_size(int64_t B, int64_t H, int64_t T, int frame_len, int d_k, int d_v) {
+    if (B < 0 || H < 0 || T < 0 || T > kMaxT || frame_len < 16 || frame_len % 16 != 0) return -1;
+    if ((d_k != 64 && d_k != 128) || (d_v != 64 && d_v != 128)) return -1;
+    int64_t BH, x;
+    const int64_t F = (T + frame_len - 1) / frame_len;
+    if (!mul_ok(B, H, &BH) || !mul_ok(BH, F + 1, &x) || !mul_ok(x, 4 * 128 * 128 * 2, &x)) return -1;
+    return gdr::frame_workspace_bytes(BH, T, frame_len, d_k, d_v);
+}
+
+gdr_status gdr_frame_fwd(int64_t B, int64_t H, int64_t T, int frame_len, int d_k, int d_v, int io_dtype, int gate,
+                         const void* q, const void* k, const void* v, const float* gamma, const float* g,
+                         const float* initial_state, void* o, float* final_state, void* workspace,
+                         int64_t workspace_bytes, void* stream) {
+    if (B < 0 || H < 0 || T < 0 || frame_len < 1) return GDR_ERR_INVALID_ARG;
+    gdr_status s = check_common(d_k, d_v, io_dtype, gate);
+    if (s != GDR_OK) return s;
+    if (T > kMaxT || frame_len % 16 != 0) return GDR_ERR_SHAPE;
+    if (io_dtype != GDR_BF16 || d_v == 32 || d_v > 128 || d_v == 96) return GDR_ERR_UNSUPPORTED;
+    const int64_t F = (T + frame_len - 1) / frame_len;
+    // the state pass addresses one sequence's W matrices with 32-bit byte offsets
+    if ((F + 1) * d_k * d_k * 2 > (int64_t(1) << 31)) return GDR_ERR_SHAPE;
+    int64_t BH, BHT, BHF, nq, nv, nstate, ng;
+    if (!mul_ok(B, H, &BH) || !mul_ok(BH, T, &BHT) || !mul_ok(BH, F, &BHF) || !mul_ok(BHT, d_k * 2, &nq) ||
+        !mul_ok(BHT, d_v * 2, &nv) || !mul_ok(BH, (int64_t)d_k * d_v * 4, &nstate) ||
+        !mul_ok(BHF, gate == GDR_GATE_CHANNEL ? d_k * 4 : 4, &ng))
+        return GDR_ERR_SHAPE;
+    if (BHT > 0 && (!q || !k || !v || !gamma || !g || !o)) return GDR_ERR_INVALID_ARG;
+    const int64_t need = gdr_frame_fwd_workspace_size(B, H, T, frame_len, d_k, d_v);
+    if (need < 0) return GDR_ERR_SHAPE;
+    if (workspace_bytes < 0 || (need > 0 && (!workspace || workspace_bytes < need))) return GDR_ERR_INVALID_ARG;
+    if (overlaps(o, nv, q, nq) || overlaps(o, nv, k, nq) || overlaps(o, nv, v, nv) ||
+        overlaps(o, nv, gamma, BHT * 4) || overlaps(o, nv, g, ng) || overlaps(o, nv, initial_state, nstate) ||
+        overlaps(o, nv, final_state, nstate))
+        return GDR_ERR_INVALID_ARG;
+    if (final_state && initial_state && final_state != initial_state &&
+        overlaps(final_state, nstate, initial_state, nstate))
+        return GDR_ERR_INVALID_ARG;
+    if (need > 0 &&
+        (overlaps(workspace, need, q, nq) || overlaps(workspace, need, k, nq) || overlaps(workspace, need, v, nv) ||
+         overlaps(workspace, need, gamma, BHT * 4) || overlaps(workspace, need, g, ng) ||
+         overlaps(workspace, need, o, nv) || overlaps(workspace, need, initial_state, nstate) ||
+         overlaps(workspace, need, final_state, nstate)))
+        return GDR_ERR_INVALID_ARG;
+    if (BH == 0) return GDR_OK;
+    int64_t nwg;
+    if (!mul_ok(BH, F > (T + 63) / 64 ? F : (T + 63) / 64, &nwg) || nwg > kMaxGrid) return GDR_ERR_SHAPE;
+    if (!final_state && BHT == 0) return GDR_OK;
+    hipError_t e = gdr::frame_dispatch(BH, T, frame_len, d_k, d_v, gate == GDR_GATE_CHANNEL, q, k, v, gamma, g,
+                                       initial_state, o, final_state, workspace, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
 }
 

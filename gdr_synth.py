@@ -189,6 +189,34 @@ def make_raw_inputs(w: Workload, *, B=None, H=None, T=None, salt: int = 0, head_
             "dt": dt, "beta_logit": beta_logit, "A_log": A_log, "dt_bias": dt_bias}
 
 
+FRAME_WORKLOAD = dict(wid=8, name="frame_bf16", B=1, H=16, T=16384, frame_len=1024, d_k=128, d_v=128,
+                      note="frame-level implicit update: 16 frames of 1024 tokens (video-like)")
+
+
+def make_frame_inputs(*, B=1, H=16, T=16384, frame_len=1024, d_k=128, d_v=128, channel=True, salt: int = 0,
+                      s0_std: float = 0.0) -> dict:
+    """Inputs of the frame-level implicit update (wid 8): q, k ~ N(0,1) L2-normalised and v ~
+    N(0,1), all rounded to bf16; writing strengths gamma = s e^z with s = d_k / frame_len (the
+    post's suggested scale, old state and frame about equal) and z ~ N(0, 0.5^2); the log
+    forget gate of each frame ~ U(-0.2, -0.01), per key channel (or one per frame).
+    Returns float32 arrays: q, k [B,H,T,d_k]; v [B,H,T,d_v]; gamma [B,H,T]; g [B,H,F(,d_k)];
+    S0 [B,H,d_v,d_k] or None."""
+    wid = 8
+    F = (T + frame_len - 1) // frame_len
+    q = _rng(wid, 0, salt).standard_normal(size=(B, H, T, d_k), dtype=np.float32)
+    k = _rng(wid, 1, salt).standard_normal(size=(B, H, T, d_k), dtype=np.float32)
+    v = _rng(wid, 2, salt).standard_normal(size=(B, H, T, d_v), dtype=np.float32)
+    z = _rng(wid, 3, salt).standard_normal(size=(B, H, T), dtype=np.float32)
+    gamma = (np.float32(d_k / frame_len) * np.exp(np.float32(0.5) * z)).astype(np.float32)
+    g = _rng(wid, 4, salt).uniform(-0.2, -0.01, size=(B, H, F, d_k) if channel else (B, H, F)).astype(np.float32)
+    S0 = None
+    if s0_std > 0.0:
+        S0 = (_rng(wid, 5, salt).standard_normal(size=(B, H, d_v, d_k), dtype=np.float32)
+              * np.float32(s0_std)).astype(np.float32)
+    return {"q": round_to_bf16(_l2_normalise(q)), "k": round_to_bf16(_l2_normalise(k)), "v": round_to_bf16(v),
+            "gamma": gamma, "g": g, "S0": S0}
+
+
 def make_decode_inputs(w: Workload, step: int, *, N=None, H=None) -> dict:
     """Fresh per-step decode inputs (q, k [N,H,d_k]; v [N,H,d_v]; beta, g [N,H]
     or g [N,H,d_k]).  Step ``s`` uses salt ``s + 1``; the initial state comes

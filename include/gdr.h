@@ -238,6 +238,47 @@ gdr_status gdr_gdn2_chunk_fwd(int64_t B, int64_t H, int64_t T, int d_k, int d_v,
                               void *o, float *final_state, void *stream);
 
 /*
+ * gdr_frame_fwd -- the frame-level implicit update (tokens in unordered frames).
+ *
+ * The video delta-rule post (haoyizhu.site, "video-delta-rule"), section "A Different Route":
+ * the sequence is cut into frames of frame_len tokens (the last frame may be shorter), and a
+ * frame moves the state by one implicit gradient step on its total loss,
+ *     G_t = K_t^T Gamma_t K_t,   C_t = V_t^T Gamma_t K_t,
+ *     S_t (I + G_t) = S_{t-1} D_t + C_t,      o_i = S_t q_i for every token i of frame t,
+ * with Gamma_t = diag(gamma) the tokens' writing strengths (gamma >= 0; the post's gamma =
+ * s e^z) and D_t = exp(g_t) the frame's forget gate (scalar or per key channel), applied to
+ * the old state first.  Every query of a frame reads the frame's final state, so the result
+ * does not depend on the order of the tokens inside a frame.  With frame_len = 1 this is the
+ * delta rule with beta = gamma / (1 + gamma) (but frame_len must be a multiple of 16 here).
+ *
+ *   q, k           [B, H, T, d_k]   bf16 (keys unit-norm by the pages' convention; not checked)
+ *   v              [B, H, T, d_v]   bf16
+ *   gamma          [B, H, T]        float32, >= 0
+ *   g              [B, H, F] (GDR_GATE_SCALAR) or [B, H, F, d_k] (GDR_GATE_CHANNEL), float32,
+ *                  F = ceil(T / frame_len): the log forget gate of each frame
+ *   initial_state, o, final_state   as gdr_chunk_fwd
+ *   workspace      device buffer of at least gdr_frame_fwd_workspace_size(...) bytes (per
+ *                  sequence and frame: (I + G)^{-1} as two fp16 matrices, C in fp32 and the
+ *                  frame's state in fp16), owned by the caller, overlapping nothing else
+ *
+ * Supported: bf16 I/O, d_k and d_v in {64, 128} (GDR_ERR_UNSUPPORTED otherwise); frame_len a
+ * positive multiple of 16 and (ceil(T / frame_len) + 1) * d_k * d_k * 2 <= 2^31
+ * (GDR_ERR_SHAPE otherwise); T in [0, 2^22].  Numerics: G and C from fp16 MFMA operands
+ * sqrt(gamma) k, sqrt(gamma) v with fp32 accumulation; (I + G)^{-1} by Gauss-Jordan
+ * elimination in fp32; the state chained in fp32 with split-fp16 products; o from an fp16
+ * copy of each frame's state, rounded to bf16.
+ */
+int64_t gdr_frame_fwd_workspace_size(int64_t B, int64_t H, int64_t T, int frame_len, int d_k,
+                                     int d_v);
+gdr_status gdr_frame_fwd(int64_t B, int64_t H, int64_t T, int frame_len, int d_k, int d_v,
+                         int io_dtype, int gate,
+                         const void *q, const void *k, const void *v,
+                         const float *gamma, const float *g,
+                         const float *initial_state,
+                         void *o, float *final_state,
+                         void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
  * gdr_decode_step -- one recurrent token per sequence, state updated in place.
  *
  * One step of the recurrence ("Linear Attention, Visualized", section "Recurrent form",

@@ -203,6 +203,32 @@ def test_fused_prep_empty_batch_is_a_noop(lib):
     assert prep(lib, T=0, q=None, k=None, v=None, dt=None, bl=None, o=None) == OK
 
 
+def frame(lib, B=1, H=1, T=64, n=16, dk=128, dv=128, io=0, gate=0, q=FAKE, k=FAKE, v=FAKE, gm=FAKE, g=FAKE,
+          s0=None, o=FAKE2, sf=None, w=ctypes.c_void_p(0x50000000), nbytes=1 << 24):
+    return lib.gdr_frame_fwd(B, H, T, n, dk, dv, io, gate, q, k, v, gm, g, s0, o, sf, w, nbytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), INVALID), (dict(n=0), INVALID), (dict(n=24), SHAPE), (dict(dk=96), SHAPE),
+    (dict(dv=32), UNSUP), (dict(dv=256), UNSUP), (dict(io=1, dk=64, dv=64), UNSUP), (dict(io=3), DTYPE),
+    (dict(gate=2), INVALID), (dict(q=None), INVALID), (dict(gm=None), INVALID), (dict(g=None), INVALID),
+    (dict(o=FAKE), INVALID), (dict(w=None), INVALID), (dict(nbytes=100), INVALID), (dict(w=FAKE), INVALID),
+    (dict(T=(1 << 22) + 1), SHAPE),
+    (dict(T=1 << 22, n=16), SHAPE),                             # frames' W past 32-bit offsets
+])
+def test_frame_fwd_rejects(lib, kw, status):
+    assert frame(lib, **kw) == status
+
+
+def test_frame_workspace_size(lib):
+    n = lib.gdr_frame_fwd_workspace_size
+    per = 128 * 128 * 4 + 128 * 128 * 4 + 128 * 128 * 2             # W hi+lo, C, S per frame
+    assert n(1, 2, 1000, 256, 128, 128) == 2 * 4 * per
+    assert n(1, 1, 0, 16, 64, 64) == 0
+    assert n(1, 1, 64, 24, 128, 128) == -1 and n(1, 1, 64, 16, 128, 32) == -1
+    assert frame(lib, B=0) == OK
+
+
 @pytest.mark.parametrize("nh", range(2, 17))
 def test_virtual_step_division(nh):
     """The GDP kernel splits virtual step m into (m // n_h, m % n_h) as umulhi(m, ceil(2^32 / n_h)),
@@ -235,6 +261,8 @@ def test_python_binding_refuses_cpu_tensors(lib):
         gdr.gdp_chunk_fwd(x, x[:, :, :, None], x[:, :, :, None], torch.zeros(1, 1, 4), torch.zeros(1, 1, 4, 1))
     with pytest.raises(ValueError):
         gdr.gdn2_chunk_fwd(x, x, x, x, x, x)
+    with pytest.raises(ValueError):
+        gdr.frame_fwd(x, x, x, torch.zeros(1, 1, 4), torch.zeros(1, 1, 1), 16)
     with pytest.raises(ValueError):
         gdr.chunk_fwd_fused_prep(x, x, x, torch.zeros(1, 1, 4), torch.zeros(1), torch.zeros(1), torch.zeros(1, 1, 4))
     with pytest.raises(ValueError):
