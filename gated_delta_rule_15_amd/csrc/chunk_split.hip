@@ -499,9 +499,12 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const StArgs a) {
     }
     lds_barrier();
 
+    // The two roles run separate loops with the same barrier sequence, so that the loaders'
+    // prefetch registers are not live in the consumers' code (and the other way round).
+    if (consumer) {
     for (int64_t c = 0; c < nC; ++c) {
         const int bc = (int)(c & 1);
-        if (consumer) {
+        {
             const _Float16* Kc = Kb(bc);
             const _Float16* Qc = Qb(bc);
             const _Float16* Ac = Ab(bc);
@@ -630,19 +633,23 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const StArgs a) {
                     uint2{pack_bf16x2(Oa[ti][0], Oa[ti][1]), pack_bf16x2(Oa[ti][2], Oa[ti][3])};
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) Sb[kb] = pack8(St[2 * kb], St[2 * kb + 1]);
-        } else {
-            // loaders: o of the previous chunk, the next chunk into LDS, then the loads of the
-            // one after
-            if (c > 0) store_o(c - 1);
-            if (c + 1 < nC) convert();
-            if (c + 1 < nC) {
-                stage(c + 1);
-                if (c + 2 < nC) issue(c + 2);
-            }
         }
         lds_barrier();
     }
-    if (!consumer && nC > 0) store_o(nC - 1);
+    } else {
+    for (int64_t c = 0; c < nC; ++c) {
+        // loaders: o of the previous chunk, the next chunk into LDS, then the loads of the one
+        // after
+        if (c > 0) store_o(c - 1);
+        if (c + 1 < nC) {
+            convert();
+            stage(c + 1);
+            if (c + 2 < nC) issue(c + 2);
+        }
+        lds_barrier();
+    }
+    if (nC > 0) store_o(nC - 1);
+    }
 
     if (consumer && a.Sf != nullptr) {
         float* sf = a.Sf + bh * (int64_t)DV * DK + (int64_t)(dvc + j) * DK;
