@@ -32,7 +32,7 @@ PEAK_MFMA_F16 = 2500.0  # TFLOP/s, MI355X dense fp16/bf16
 PEAK_HBM = 8000.0       # GB/s, MI355X HBM3E
 # the headline step: one gdr_chunk_fwd_ws call = the UT kernel over all chunks, then the
 # chunk-serial state kernel
-CHUNK_KERNEL = "chunk_ut_kernel<128> + chunk_state_kernel<128>"
+CHUNK_KERNEL = "chunk_ut_kernel<128> + chunk_state_kernel<128, false, 2>"
 CHUNK_SOURCE = os.path.join(ROOT, "gated_delta_rule_15_amd", "csrc", "chunk_split.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "chunk_split_gdn_bf16_B4_H16_T4096_traffic.json")
 COPY_BYTES = 256 << 20  # calibration copy for the HBM byte counters
@@ -326,7 +326,7 @@ def bench_gdn2(torch, gdr, gdr_synth, steps=10):
     torch.cuda.synchronize()
     return {"workload": "gdn2_bf16: Gated DeltaNet-2 B=2 H=16 T=8192 d_k=d_v=128 bf16, fp32 g, b [B,H,T,128], "
                         "w [B,H,T,128], zero S0",
-            "kernel": "chunk_kda_kernel<128, true>", "ms_per_call": round(ms, 4),
+            "kernel": "chunk_kda_kernel<128, true, false>", "ms_per_call": round(ms, 4),
             "tokens_per_s": round(w.B * w.T / (ms * 1e-3), 1),
             "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_MFMA_F16, 4),
             "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM, 4),
@@ -447,14 +447,18 @@ def main():
         w3 = gdr_synth.WORKLOADS[3]
         sets3 = make_chunk_sets(torch, gdr_synth, w3, nsets=2)
         m3, _, _, _, _ = time_chunk(torch, gdr, sets3, 10, 2)
+        m3s, _, _, _, _ = time_chunk(torch, gdr, sets3, 10, 2,
+                                     fn=lambda *a_, **kw: gdr.chunk_fwd(*a_, workspace=None, **kw))
         f3 = chunk_flops(w3.B, w3.H, w3.T, 128, 128)
         b3 = chunk_bytes(w3.B, w3.H, w3.T, 128, 128, gate_per_channel=True)
         result["kda"] = {
             "workload": "per-channel gate B=2 H=16 T=8192 d=128 bf16, fp32 gate [B,H,T,128]",
-            "kernel": "chunk_kda_kernel<128, false>", "ms_per_call": round(m3, 4),
+            "kernel": "chunk_kda_kernel<128, false, true> + chunk_state_kernel<128, true, 1>",
+            "ms_per_call": round(m3, 4),
             "tokens_per_s": round(w3.B * w3.T / (m3 * 1e-3), 1),
             "mfma_frac": round(f3 / (m3 * 1e-3) / 1e12 / PEAK_MFMA_F16, 4),
-            "hbm_frac": round(b3 / (m3 * 1e-3) / 1e9 / PEAK_HBM, 4)}
+            "hbm_frac": round(b3 / (m3 * 1e-3) / 1e9 / PEAK_HBM, 4),
+            "single_kernel": {"kernel": "chunk_kda_kernel<128, false, false>", "ms_per_call": round(m3s, 4)}}
         del sets3
         result["gdp"] = bench_gdp(torch, gdr, gdr_synth)
         result["gdn2"] = bench_gdn2(torch, gdr, gdr_synth)

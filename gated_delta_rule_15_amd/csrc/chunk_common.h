@@ -11,6 +11,12 @@
 
 namespace gdr {
 
+// Workspace of the per-channel-gate two-kernel path, per (sequence, chunk), in halfs:
+// A^T [C][C], T [C][C] (columns pperm'd), K e^G [C][DK], Q e^G [C][DK], K e^{G_C - G} [C][DK]
+// (fp16), then e^{G_C} [DK] (fp32, natural channel order).
+template <int DK>
+constexpr int kda_ws_stride() { return 2 * kChunk * kChunk + 3 * kChunk * DK + 2 * DK; }
+
 // position of logical index m inside its row under the 32-block permutation
 __device__ __forceinline__ int pperm(int m) {
     return (m & ~31) | (((m >> 2) & 3) << 3) | (((m >> 4) & 1) << 2) | (m & 3);

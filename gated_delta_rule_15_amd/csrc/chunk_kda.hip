@@ -32,6 +32,12 @@
 // N^{-1} diag(beta) by blocked forward substitution (as in the scalar kernel).  Loads of
 // chunk c+1 are in flight while chunk c is processed.
 //
+// The UT instantiation runs stages S1-S4 for one chunk per workgroup, all chunks at once, adds
+// the blocks of N^{-1} below the diagonal (M_bc = -X_bb sum_{c<=d<b} N_bd M_dc) and writes, per
+// (sequence, chunk), the operands of the two-kernel state pass to a workspace: A^T and
+// T = N^{-1} diag(beta) (fp16, T's columns pperm'd), the decayed copies K e^G, Q e^G and
+// K e^{G_C - G} (fp16) and e^{G_C} per key channel (fp32).
+//
 // Gated DeltaNet-2 ("Gated DeltaNet-2, and the gate that was doing two jobs", section 2) is
 // the GD2 instantiation.  The scalar beta is replaced by a key-side erase gate b_t and a
 // value-side write gate w_t: S_t = S_{t-1} D_t (I - e_t k_t^T) + z_t k_t^T, with e = b (.) k
@@ -63,6 +69,8 @@ struct KdaArgs {
     const float* S0;
     uint16_t* o;
     float* Sf;
+    uint16_t* ws;     // UT: workspace, kda_ws_stride<DK>() halfs per (sequence, chunk)
+    int cpw;          // UT: chunks per workgroup
 };
 
 template <int DK>
@@ -115,7 +123,7 @@ __device__ __forceinline__ uint2 bld8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return uint2{v[0], v[1]};
 }
 
-template <int DK, bool GD2>
+template <int DK, bool GD2, bool UT>
 __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
     using L = KdaLds<DK>;
     constexpr int C = kChunk;
@@ -143,10 +151,16 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
     int* Flag = reinterpret_cast<int*>(smem + L::oFlag);
 
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, j = l & 15, g = l >> 4;
-    const int vi = xcd_major_index(blockIdx.x, gridDim.x);
-    const int64_t bh = vi / a.ntiles;
-    const int dv0 = (vi % a.ntiles) * 32;
     const int64_t T = a.T;
+    const int64_t nC = (T + C - 1) / C;
+    // state pass: one group per (sequence, 32 value channels) over all chunks; UT: one group per
+    // (sequence, run of cpw consecutive chunks)
+    const int64_t runs = UT ? (nC + a.cpw - 1) / a.cpw : 1;
+    const int vi = UT ? 0 : xcd_major_index(blockIdx.x, gridDim.x);
+    const int64_t bh = UT ? blockIdx.x / runs : vi / a.ntiles;
+    const int64_t c_first = UT ? (blockIdx.x - bh * runs) * a.cpw : 0;
+    const int64_t c_last = UT ? (c_first + a.cpw < nC ? c_first + a.cpw : nC) : nC;
+    const int dv0 = (vi % a.ntiles) * 32;
     const int DV = a.dv;
     const auto rq = make_rsrc(a.q + bh * T * DK, (uint32_t)(T * DK * 2));
     const auto rk = make_rsrc(a.k + bh * T * DK, (uint32_t)(T * DK * 2));
@@ -157,7 +171,6 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
     const auto rw = make_rsrc(GD2 ? a.wg + bh * T * DV : nullptr, GD2 ? (uint32_t)(T * DV * 4) : 0u);
     const auto ro = make_rsrc(a.o + bh * T * DV, (uint32_t)(T * DV * 2));
     const int dvc = dv0 + 16 * w;  // first value channel of consumer wave w (w < 2)
-    const int64_t nC = (T + C - 1) / C;
 
     auto trfrag = [&](const _Float16* base, int ld, int kb, int col) {
         const _Float16* p0 = base + (32 * kb + 4 * g + (j >> 2)) * ld + col;
@@ -205,7 +218,7 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
         if (t == 0) {
             const uint32_t tc = (uint32_t)(c * C);
             const uint32_t vidx = (tc + (tid >> 2)) * DV + dv0 + (tid & 3) * 8;
-            vp = bld16(rv, vidx * 2);
+            if (!UT) vp = bld16(rv, vidx * 2);
             if constexpr (GD2) {
                 wp0 = bld16(rw, vidx * 4);
                 wp1 = bld16(rw, vidx * 4 + 16);
@@ -254,9 +267,9 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
     };
 
     lds_barrier();
-    if (nC > 0) issue(0);
+    if (nC > 0) issue(c_first);
 
-    for (int64_t c = 0; c < nC; ++c) {
+    for (int64_t c = c_first; c < c_last; ++c) {
         // ====== S1: block-local scan of the log-decay and the decayed copies of K and Q ======
         // Per channel pair and 16-token block: a_t = e^{g_t}, E_t = e^{G_loc(t)} (forward
         // product), Ec_t = e^{G_loc(15) - G_loc(t)} (backward product);
@@ -318,7 +331,8 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
             const bool any_unsafe = __any(unsafe);
             if (l == 0) Flag[w] = any_unsafe ? 1 : 0;
             if (!GD2 && w == 0) FB[l] = bp;
-            // V^T tile, fp32 [channel][token] (GD2: z = w (.) v)
+            // V^T tile, fp32 [channel][token] (GD2: z = w (.) v); the UT pass has no V
+            if (!UT) {
             const int row = tid >> 2, col = (tid & 3) * 8;
             const uint32_t ww[4] = {vp.x, vp.y, vp.z, vp.w};
 #pragma unroll
@@ -331,6 +345,7 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
                 }
                 Vt[(col + 2 * e) * L::LDV + row] = v0;
                 Vt[(col + 2 * e + 1) * L::LDV + row] = v1;
+            }
             }
         }
         lds_barrier();
@@ -368,7 +383,7 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
         // Each wave runs its own compile-time instance, so every tile's path is static.
         // The next chunk's loads are issued between this stage's MFMAs (a token of the block
         // per step), so the memory queue drains while the matrix pipe works.
-        const int64_t cn = c + 1 < nC ? c + 1 : c;  // reloading the last chunk is harmless
+        const int64_t cn = c + 1 < c_last ? c + 1 : c;  // reloading the last chunk is harmless
         auto gram_kda = [&](auto hc, auto qc) {
             constexpr int h = decltype(hc)::value;
             constexpr bool isQ = decltype(qc)::value;
@@ -443,6 +458,13 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
         else gram_kda(std::integral_constant<int, 1>{}, std::true_type{});
         lds_barrier();
 
+        // UT: T is staged where the block-local log-decay was (dead after the Gram tiles)
+        _Float16* Tt = reinterpret_cast<_Float16*>(smem + L::oGl);
+        if (UT) {
+            for (int i = tid; i < C * L::LDC / 8; i += 256)
+                reinterpret_cast<uint4*>(Tt)[i] = uint4{0u, 0u, 0u, 0u};
+            lds_barrier();
+        }
         // ============ S4: diagonal inverses (waves 0-1, two blocks each); the copies are
         // rescaled in place for the state pass (waves 2-3) ============
         if (w < 2) {
@@ -476,6 +498,12 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
                 }
                 *reinterpret_cast<half8*>(Xd + (16 * b + jc) * L::LDX) = h0;
                 *reinterpret_cast<half8*>(Xd + (16 * b + jc) * L::LDX + 8) = h1;
+                if (UT) {  // diagonal block of T = N^{-1} diag(beta)
+                    const float bc = FB[16 * b + jc];
+                    const int pc = pperm(16 * b + jc);
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) Tt[(16 * b + i) * L::LDC + pc] = (_Float16)(xd[i] * bc);
+                }
             }
         }
         {
@@ -498,6 +526,60 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
         }
         lds_barrier();
 
+        if constexpr (UT) {
+            // blocks of N^{-1} below the diagonal, column block by column block (wave 0: column
+            // 0, wave 1: columns 1 and 2): M_bc = -X_bb sum_{d=c}^{b-1} N_bd M_dc, then
+            // T_bc = M_bc diag(beta_c)
+            auto mma16k16 = [](float4v& acc4, const half4& a4, const half4& b4) {
+                acc4 = __builtin_amdgcn_mfma_f32_16x16x16f16(a4, b4, acc4, 0, 0, 0);
+            };
+            auto h4 = [](const float4v& x) { return half4{(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3]}; };
+            auto xA = [&](int b) { return ldtr(Xd + (16 * b + 4 * g + (j >> 2)) * L::LDX + 4 * (j & 3)); };
+            auto nA = [&](int b, int d) { return ldtr(Nt + (16 * d + 4 * g + (j >> 2)) * L::LDC + 16 * b + 4 * (j & 3)); };
+            auto column = [&](auto cc) {
+                constexpr int cb = decltype(cc)::value;
+                half4 mb[4];
+                mb[cb] = *reinterpret_cast<const half4*>(Xd + (16 * cb + j) * L::LDX + 4 * g);
+                const float bcol = FB[16 * cb + j];
+                const int pc = pperm(16 * cb + j);
+#pragma unroll
+                for (int b = cb + 1; b < 4; ++b) {
+                    float4v y = zero4();
+#pragma unroll
+                    for (int d = cb; d < b; ++d) mma16k16(y, nA(b, d), mb[d]);
+                    float4v m = zero4();
+                    mma16k16(m, xA(b), h4(y));
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) m[r] = -m[r];
+                    mb[b] = h4(m);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) Tt[(16 * b + 4 * g + r) * L::LDC + pc] = (_Float16)(m[r] * bcol);
+                }
+            };
+            if (w == 0) {
+                column(std::integral_constant<int, 0>{});
+            } else if (w == 1) {
+                column(std::integral_constant<int, 1>{});
+                column(std::integral_constant<int, 2>{});
+            }
+            lds_barrier();
+            // the chunk's operands to the workspace, 16-byte pieces
+            uint16_t* dst = a.ws + (bh * nC + c) * (int64_t)kda_ws_stride<DK>();
+            for (int i = tid; i < C * C / 8; i += 256) {
+                const int row = i / (C / 8), col = (i % (C / 8)) * 8;
+                *reinterpret_cast<uint4*>(dst + row * C + col) = *reinterpret_cast<const uint4*>(At + row * L::LDC + col);
+                *reinterpret_cast<uint4*>(dst + C * C + row * C + col) =
+                    *reinterpret_cast<const uint4*>(Tt + row * L::LDC + col);
+            }
+            for (int i = tid; i < C * DK / 8; i += 256) {
+                const int row = i / (DK / 8), col = (i % (DK / 8)) * 8;
+                uint16_t* d0 = dst + 2 * C * C + row * DK + col;
+                *reinterpret_cast<uint4*>(d0) = *reinterpret_cast<const uint4*>(Kr + row * L::LDK + col);
+                *reinterpret_cast<uint4*>(d0 + C * DK) = *reinterpret_cast<const uint4*>(Qr + row * L::LDK + col);
+                *reinterpret_cast<uint4*>(d0 + 2 * C * DK) = *reinterpret_cast<const uint4*>(Kc + row * L::LDK + col);
+            }
+            if (tid < DK) reinterpret_cast<float*>(dst + 2 * C * C + 3 * C * DK)[tid] = FE[tid];
+        } else {
         // ================= S5: state pass of chunk c (waves 0-1) =================
         if (w < 2) {
             // P_K = (K e^G) S^T, P_Q = (Q e^G) S^T
@@ -625,20 +707,21 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) Sb[kb] = pack8(St[2 * kb], St[2 * kb + 1]);
         }
+        }  // state pass
         lds_barrier();
     }
 
-    if (w < 2 && a.Sf != nullptr) {
+    if (!UT && w < 2 && a.Sf != nullptr) {
         float* sf = a.Sf + bh * (int64_t)DV * DK + (int64_t)(dvc + j) * DK;
 #pragma unroll
         for (int t = 0; t < NST; ++t) *reinterpret_cast<float4v*>(sf + pperm(16 * t + 4 * g)) = St[t];
     }
 }
 
-template <int DK, bool GD2>
+template <int DK, bool GD2, bool UT = false>
 static hipError_t launch_kda(const KdaArgs& a, int64_t nwg, hipStream_t st) {
     using L = KdaLds<DK>;
-    auto kern = chunk_kda_kernel<DK, GD2>;
+    auto kern = chunk_kda_kernel<DK, GD2, UT>;
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -667,10 +750,51 @@ hipError_t chunk_kda_dispatch(int64_t BH, int64_t T, int dk, int dv, const void*
     a.S0 = S0;
     a.o = static_cast<uint16_t*>(o);
     a.Sf = Sf;
+    a.ws = nullptr;
+    a.cpw = 1;
     const int64_t nwg = BH * a.ntiles;
     if (dk == 128) return launch_kda<128, false>(a, nwg, st);
     return launch_kda<64, false>(a, nwg, st);
 }
+
+// UT pass of the per-channel-gate two-kernel path: one group per (sequence, run of chunks), the
+// runs sized so the grid about fills the chip once (a group walks its chunks with the next
+// chunk's loads in flight).
+hipError_t chunk_kda_ut_dispatch(int64_t BH, int64_t T, int dk, const void* q, const void* k, const float* g,
+                                 const float* beta, void* ws, hipStream_t st) {
+    KdaArgs a;
+    a.T = T;
+    a.dv = 32;
+    a.ntiles = 1;
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k);
+    a.v = nullptr;
+    a.g = g;
+    a.beta = beta;
+    a.eg = nullptr;
+    a.wg = nullptr;
+    a.S0 = nullptr;
+    a.o = nullptr;
+    a.Sf = nullptr;
+    a.ws = static_cast<uint16_t*>(ws);
+    const int64_t nC = (T + kChunk - 1) / kChunk;
+    if (BH * nC == 0) return hipSuccess;
+    static int ncu = 0;
+    if (ncu == 0) {
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        if (ncu < 1) ncu = 1;
+    }
+    const int64_t cpw = (BH * nC + ncu - 1) / ncu;
+    a.cpw = (int)(cpw < nC ? cpw : nC);
+    const int64_t nwg = BH * ((nC + a.cpw - 1) / a.cpw);
+    if (dk == 128) return launch_kda<128, false, true>(a, nwg, st);
+    return launch_kda<64, false, true>(a, nwg, st);
+}
+
+int64_t chunk_kda_ws_halfs(int dk) { return dk == 128 ? kda_ws_stride<128>() : kda_ws_stride<64>(); }
 
 // Gated DeltaNet-2: per-channel log-decay g [.., T, dk], erase gate b [.., T, dk], write gate
 // w [.., T, dv], all fp32.
@@ -691,6 +815,8 @@ hipError_t chunk_gdn2_dispatch(int64_t BH, int64_t T, int dk, int dv, const void
     a.S0 = S0;
     a.o = static_cast<uint16_t*>(o);
     a.Sf = Sf;
+    a.ws = nullptr;
+    a.cpw = 1;
     const int64_t nwg = BH * a.ntiles;
     if (dk == 128) return launch_kda<128, true>(a, nwg, st);
     return launch_kda<64, true>(a, nwg, st);

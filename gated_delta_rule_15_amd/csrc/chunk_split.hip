@@ -25,6 +25,14 @@
 // Workspace layout, per (sequence, chunk): A^T [64][64] (row m holds A[l][m], l = 0..63), then
 // T [64][64] (row l; column m stored at position pperm(m), so one operand fragment is one
 // 16-byte read).  Upper triangles are stored as zeros.
+//
+// The per-channel gate ("Kimi Delta Attention (KDA)" section of the same page) takes the same
+// state kernel in its KDA instantiation: the UT pass (chunk_kda.hip) also writes the decayed
+// copies K e^G, Q e^G, K e^{G_C - G} and e^{G_C} per channel, so the state pass scales
+// nothing itself:  R = V - (K e^G) S^T,  Z = T R,  O = (Q e^G) S^T + A Z,
+// S^T <- Diag(e^{G_C}) S^T + (K e^{G_C - G})^T Z.  The loaders stage K e^G in the K buffer and
+// K e^{G_C - G} in the Q buffer; the consumers read their Q e^G fragments straight from the
+// workspace, one chunk ahead, and take the Q e^G S^T products after Z, off the serial chain.
 #include <type_traits>
 
 #include "chunk_common.h"
@@ -324,7 +332,7 @@ struct StArgs {
     int64_t T;
     int64_t nC;
     int dv;
-    int ntiles;  // d_v / 32
+    int ntiles;  // d_v / (16 NCW)
     const uint16_t* q;
     const uint16_t* k;
     const uint16_t* v;
@@ -360,8 +368,10 @@ struct StLds {
     static_assert((oQ | oA | oT | oV | oF | oOt) % 16 == 0, "alignment");
 };
 
-template <int DK>
-__global__ __launch_bounds__(256, 1) void chunk_state_kernel(const StArgs a) {
+// NCW consumer waves of 16 value channels each (a value tile of 16 NCW channels) and two loader
+// waves.  NCW = 1 doubles the workgroups of a grid that would leave compute units idle.
+template <int DK, bool KDA, int NCW>
+__global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const StArgs a) {
     using L = StLds<DK>;
     constexpr int C = kChunk;
     constexpr int NKB = DK / 32;
@@ -376,20 +386,23 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const StArgs a) {
     auto Ob = [&](int b) { return reinterpret_cast<_Float16*>(smem + L::oOt + b * L::szO); };  // bf16 bits
 
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, j = l & 15, g = l >> 4;
-    const bool consumer = w < 2;
+    const bool consumer = w < NCW;
     // the consumers' chain is the critical path: let them win issue and LDS arbitration
     if (consumer) __builtin_amdgcn_s_setprio(2);
     const int vi = xcd_major_index(blockIdx.x, gridDim.x);
     const int64_t bh = vi / a.ntiles;
-    const int dv0 = (vi % a.ntiles) * 32;
+    const int dv0 = (vi % a.ntiles) * (16 * NCW);
     const int dvc = dv0 + 16 * w;
     const int64_t T = a.T, nC = a.nC;
     const int DV = a.dv;
     const auto rq = make_rsrc(a.q + bh * T * DK, (uint32_t)(T * DK * 2));
     const auto rk = make_rsrc(a.k + bh * T * DK, (uint32_t)(T * DK * 2));
     const auto rv = make_rsrc(a.v + bh * T * DV, (uint32_t)(T * DV * 2));
-    const auto rg = make_rsrc(a.g + bh * T, (uint32_t)(T * 4));
-    const auto rw = make_rsrc(a.ws + bh * nC * (2 * C * C), (uint32_t)(nC * (2 * C * C) * 2));
+    const auto rg = make_rsrc(KDA ? nullptr : a.g + bh * T, KDA ? 0u : (uint32_t)(T * 4));
+    constexpr int WS = KDA ? kda_ws_stride<DK>() : 2 * C * C;  // workspace halfs per chunk
+    // offsets (halfs) inside a chunk's workspace record of the per-channel gate
+    constexpr int WKG = 2 * C * C, WQG = WKG + C * DK, WKC = WQG + C * DK, WFE = WKC + C * DK;
+    const auto rw = make_rsrc(a.ws + bh * nC * WS, (uint32_t)(nC * WS * 2));
     const auto ro = make_rsrc(a.o + bh * T * DV, (uint32_t)(T * DV * 2));
 
     auto trfrag = [&](const _Float16* base, int ld, int kb, int col) {
@@ -398,21 +411,28 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const StArgs a) {
     };
 
     // ---- loader waves (2, 3): registers for one chunk, staged into LDS one chunk ahead
-    const int lt = tid - 128;  // loader thread in [0, 128)
+    const int lt = tid - 64 * NCW;  // loader thread in [0, 128)
+    constexpr int NPV = NCW;        // 16-byte pieces of the V tile per loader thread
     constexpr int NPK = C * DK / 8 / 128;  // K (and Q) pieces per loader thread
     constexpr int NPW = C * C / 8 / 128;   // A^T (and T) pieces per loader thread
-    uint4 kr[NPK], qr[NPK], ar[NPW], tr[NPW], vr[2];
+    // (KDA: kr holds K e^G, qr K e^{G_C - G}, gr e^{G_C} of channel lt)
+    uint4 kr[NPK], qr[NPK], ar[NPW], tr[NPW], vr[NPV];
     float gr = 0.0f;
     auto issue = [&](int64_t c) {
         const uint32_t t0 = (uint32_t)(c * C);
+        const uint32_t wb = (uint32_t)(c * WS);
 #pragma unroll
         for (int u = 0; u < NPK; ++u) {
             const int idx = lt + 128 * u, row = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
-            const uint32_t off = ((t0 + row) * DK + col) * 2;
-            kr[u] = bld16(rk, off);
-            qr[u] = bld16(rq, off);
+            if constexpr (KDA) {
+                kr[u] = bld16(rw, (wb + WKG + idx * 8) * 2);
+                qr[u] = bld16(rw, (wb + WKC + idx * 8) * 2);
+            } else {
+                const uint32_t off = ((t0 + row) * DK + col) * 2;
+                kr[u] = bld16(rk, off);
+                qr[u] = bld16(rq, off);
+            }
         }
-        const uint32_t wb = (uint32_t)(c * (2 * C * C));
 #pragma unroll
         for (int u = 0; u < NPW; ++u) {
             const int idx = lt + 128 * u;
@@ -420,16 +440,21 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const StArgs a) {
             tr[u] = bld16(rw, (wb + C * C + idx * 8) * 2);
         }
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int idx = lt + 128 * u, row = idx >> 2, col = (idx & 3) * 8;
+        for (int u = 0; u < NPV; ++u) {
+            const int idx = lt + 128 * u, row = idx / (2 * NCW), col = (idx % (2 * NCW)) * 8;
             vr[u] = bld16(rv, ((t0 + row) * DV + dv0 + col) * 2);
         }
-        if (w == 2) gr = bld4(rg, (t0 + l) * 4);
+        if constexpr (KDA) {
+            if (lt < DK) gr = bld4(rw, (wb + WFE) * 2 + lt * 4);
+        } else {
+            if (w == NCW) gr = bld4(rg, (t0 + l) * 4);
+        }
     };
     // o of chunk c from its O^T buffer: loader wave lw takes rows (value channels) 16 lw ..,
     // a lane reads 8 consecutive channels of one token back transposed and stores 16 bytes
     auto store_o = [&](int64_t c) {
-        const int lw = w - 2;
+        const int lw = w - NCW;
+        if (lw >= NCW) return;
         const _Float16* Ot = Ob((int)(c & 1));
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
@@ -442,6 +467,7 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const StArgs a) {
     };
     // K and Q to fp16 in the registers (while the consumers' first products read LDS)
     auto convert = [&]() {
+        if constexpr (KDA) return;  // the UT pass wrote fp16
 #pragma unroll
         for (int u = 0; u < NPK; ++u) {
             kr[u] = __builtin_bit_cast(uint4, bf16x8_to_half8(kr[u]));
@@ -463,11 +489,13 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const StArgs a) {
             *reinterpret_cast<uint4*>(Tb(b) + row * L::LDC + col) = tr[u];
         }
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int idx = lt + 128 * u, row = idx >> 2, col = (idx & 3) * 8;
+        for (int u = 0; u < NPV; ++u) {
+            const int idx = lt + 128 * u, row = idx / (2 * NCW), col = (idx % (2 * NCW)) * 8;
             *reinterpret_cast<uint4*>(Vb(b) + row * L::LDV + col) = vr[u];
         }
-        if (w == 2) {  // in-chunk cumulative log-decay (lane = token) and its factors
+        if constexpr (KDA) {
+            if (lt < DK) Fb(b)[lt] = gr;
+        } else if (w == NCW) {  // in-chunk cumulative log-decay (lane = token) and its factors
             const float x = wave_inclusive_scan(gr);
             const float GC = lane_value(x, 63);
             float* F = Fb(b);
@@ -502,6 +530,20 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const StArgs a) {
     // The two roles run separate loops with the same barrier sequence, so that the loaders'
     // prefetch registers are not live in the consumers' code (and the other way round).
     if (consumer) {
+    // KDA: the chunk's Q e^G fragments (row 16 ti + j, channels 32 kb + 8 g ..), from the
+    // workspace one chunk ahead
+    half8 qg[KDA ? 4 : 1][KDA ? NKB : 1];
+    auto issue_qg = [&](int64_t c) {
+        if constexpr (KDA) {
+            const uint32_t base = (uint32_t)(c * WS) + WQG;
+#pragma unroll
+            for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb)
+                    qg[ti][kb] = __builtin_bit_cast(half8, bld16(rw, (base + (16 * ti + j) * DK + 32 * kb + 8 * g) * 2));
+        }
+    };
+    if (nC > 0) issue_qg(0);
     for (int64_t c = 0; c < nC; ++c) {
         const int bc = (int)(c & 1);
         {
@@ -521,12 +563,13 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const StArgs a) {
                 PK[ti] = zero4();
                 PQ[ti] = zero4();
                 fa[ti] = kfrag(ti, 0);
-                fa[4 + ti] = qfrag(ti, 0);
+                if (!KDA) fa[4 + ti] = qfrag(ti, 0);
             }
             // fragments that do not depend on the state (T, A, K^T) are loaded while the
             // first products run
             half8 tf[6], af[6];
-            auto ktfrag = [&](int t, int kb) { return trfrag(Kc, L::LDK, kb, pperm(16 * t + 4 * (j & 3))); };
+            // K^T fragments (KDA: of K e^{G_C - G}, staged in the Q buffer)
+            auto ktfrag = [&](int t, int kb) { return trfrag(KDA ? Qc : Kc, L::LDK, kb, pperm(16 * t + 4 * (j & 3))); };
             half8 kt0[NST], kt1[NST];
             auto prefetch = [&](int kb) {
                 if (kb == 0) {
@@ -551,7 +594,7 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const StArgs a) {
             float4v eg[4], vv[4];
 #pragma unroll
             for (int ti = 0; ti < 4; ++ti) {
-                eg[ti] = ld4f(F + L::FEG + 16 * ti + 4 * g);
+                eg[ti] = KDA ? float4v{1.0f, 1.0f, 1.0f, 1.0f} : ld4f(F + L::FEG + 16 * ti + 4 * g);
                 const uint2 vb = __builtin_bit_cast(
                     uint2, ldtr(reinterpret_cast<const _Float16*>(Vc) + (16 * ti + 4 * g + (j >> 2)) * L::LDV +
                                 16 * w + 4 * (j & 3)));
@@ -567,22 +610,29 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const StArgs a) {
 #pragma unroll
                     for (int ti = 0; ti < 4; ++ti) {
                         nxt[ti] = kfrag(ti, kb + 1);
-                        nxt[4 + ti] = qfrag(ti, kb + 1);
+                        if (!KDA) nxt[4 + ti] = qfrag(ti, kb + 1);
                     }
                 }
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int ti = 0; ti < 4; ++ti) {
                     mma16(PK[ti], cur[ti], Sb[kb]);
-                    mma16(PQ[ti], cur[4 + ti], Sb[kb]);
+                    if (!KDA) mma16(PQ[ti], cur[4 + ti], Sb[kb]);
                 }
                 prefetch(kb);
                 __builtin_amdgcn_sched_barrier(0);
             }
             float4v er[4];
+            float4v ed[KDA ? NST : 1];  // KDA: e^{G_C} of the state rows
+            float eGC = 1.0f;
+            if constexpr (KDA) {
 #pragma unroll
-            for (int ti = 0; ti < 4; ++ti) er[ti] = ld4f(F + L::FER + 16 * ti + 4 * g);
-            const float eGC = F[L::FEC];
+                for (int t = 0; t < NST; ++t) ed[t] = ld4f(F + pperm(16 * t + 4 * g));
+            } else {
+#pragma unroll
+                for (int ti = 0; ti < 4; ++ti) er[ti] = ld4f(F + L::FER + 16 * ti + 4 * g);
+                eGC = F[L::FEC];
+            }
             __builtin_amdgcn_sched_barrier(0);
             // R = V - e^G P_K,  O_hist = e^G P_Q
             float4v Rr[4], Oh[4];
@@ -606,12 +656,22 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const StArgs a) {
             // O = O_hist + A Z  and  S^T <- e^{G_C} S^T + K^T diag(e^{G_C - G}) Z: both groups
             // of products are issued before any of their results is used
             const half8 zB[2] = {pack8(Zz[0], Zz[1]), pack8(Zz[2], Zz[3])};
-            float4v zs[4];
+            half8 sZ0 = zB[0], sZ1 = zB[1];
+            if constexpr (!KDA) {
+                float4v zs[4];
 #pragma unroll
-            for (int ti = 0; ti < 4; ++ti)
+                for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) zs[ti][r] = er[ti][r] * Zz[ti][r];
-            const half8 sZ0 = pack8(zs[0], zs[1]), sZ1 = pack8(zs[2], zs[3]);
+                    for (int r = 0; r < 4; ++r) zs[ti][r] = er[ti][r] * Zz[ti][r];
+                sZ0 = pack8(zs[0], zs[1]);
+                sZ1 = pack8(zs[2], zs[3]);
+            } else {
+                // P_Q = (Q e^G) S^T with the state of the chunk start
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                    for (int ti = 0; ti < 4; ++ti) mma16(Oh[ti], qg[ti][kb], Sb[kb]);
+            }
             float4v Oa[4];
 #pragma unroll
             for (int ti = 0, n = 0; ti < 4; ++ti) {
@@ -622,10 +682,11 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const StArgs a) {
 #pragma unroll
             for (int t = 0; t < NST; ++t) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) St[t][r] *= eGC;
+                for (int r = 0; r < 4; ++r) St[t][r] *= KDA ? ed[t][r] : eGC;
                 mma16(St[t], kt0[t], sZ0);
                 mma16(St[t], kt1[t], sZ1);
             }
+            if (c + 1 < nC) issue_qg(c + 1);
             // O rounded to bf16 into this wave's rows of O^T (the loaders store it)
 #pragma unroll
             for (int ti = 0; ti < 4; ++ti)
@@ -658,12 +719,10 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const StArgs a) {
     }
 }
 
-template <int DK>
-static hipError_t launch_split(const UtArgs& u, const StArgs& s, int64_t BH, hipStream_t st) {
-    using LU = UtLds<DK>;
+template <int DK, bool KDA, int NCW>
+static hipError_t launch_state_ncw(StArgs s, int64_t BH, hipStream_t st) {
     using LS = StLds<DK>;
-    auto ku = chunk_ut_kernel<DK>;
-    auto ks = chunk_state_kernel<DK>;
+    auto ks = chunk_state_kernel<DK, KDA, NCW>;
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(ks),
@@ -671,9 +730,35 @@ static hipError_t launch_split(const UtArgs& u, const StArgs& s, int64_t BH, hip
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    if (u.nC > 0) hipLaunchKernelGGL(ku, dim3((unsigned)(BH * u.nC)), dim3(128), LU::total, st, u);
-    hipLaunchKernelGGL(ks, dim3((unsigned)(BH * s.ntiles)), dim3(256), LS::total, st, s);
+    s.ntiles = s.dv / (16 * NCW);
+    hipLaunchKernelGGL(ks, dim3((unsigned)(BH * s.ntiles)), dim3(64 * (NCW + 2)), LS::total, st, s);
     return hipGetLastError();
+}
+
+// Value tiles of 32 channels, or of 16 when 32-channel tiles would leave compute units idle
+// (one workgroup fills a compute unit's LDS).
+template <int DK, bool KDA>
+static hipError_t launch_state(const StArgs& s, int64_t BH, hipStream_t st) {
+    static int ncu = 0;
+    if (ncu == 0) {
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        if (ncu < 1) ncu = 1;
+    }
+    if (BH * (s.dv / 32) < ncu) return launch_state_ncw<DK, KDA, 1>(s, BH, st);
+    return launch_state_ncw<DK, KDA, 2>(s, BH, st);
+}
+
+template <int DK>
+static hipError_t launch_split(const UtArgs& u, const StArgs& s, int64_t BH, hipStream_t st) {
+    using LU = UtLds<DK>;
+    auto ku = chunk_ut_kernel<DK>;
+    if (u.nC > 0) hipLaunchKernelGGL(ku, dim3((unsigned)(BH * u.nC)), dim3(128), LU::total, st, u);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_state<DK, false>(s, BH, st);
 }
 
 // Bytes of workspace the two-kernel path needs: 16 KiB per (sequence, chunk).
@@ -709,6 +794,27 @@ hipError_t chunk_split_dispatch(int64_t BH, int64_t T, int dk, int dv, const voi
     s.Sf = Sf;
     if (dk == 128) return launch_split<128>(u, s, BH, st);
     return launch_split<64>(u, s, BH, st);
+}
+
+// State pass of the per-channel-gate two-kernel path, over a workspace the KDA UT pass has
+// filled (chunk_kda_ut_dispatch): kda_ws_stride<dk>() halfs per (sequence, chunk).
+hipError_t chunk_state_kda_dispatch(int64_t BH, int64_t T, int dk, int dv, const void* v, const float* S0, void* o,
+                                    float* Sf, const void* ws, hipStream_t st) {
+    StArgs s;
+    s.T = T;
+    s.nC = (T + kChunk - 1) / kChunk;
+    s.dv = dv;
+    s.ntiles = dv / 32;
+    s.q = nullptr;
+    s.k = nullptr;
+    s.v = static_cast<const uint16_t*>(v);
+    s.g = nullptr;
+    s.ws = static_cast<const uint16_t*>(ws);
+    s.S0 = S0;
+    s.o = static_cast<uint16_t*>(o);
+    s.Sf = Sf;
+    if (dk == 128) return launch_state<128, true>(s, BH, st);
+    return launch_state<64, true>(s, BH, st);
 }
 
 }  // namespace gdr

@@ -18,6 +18,11 @@ hipError_t chunk_split_dispatch(int64_t BH, int64_t T, int dk, int dv, const voi
                                 const float* g, const float* beta, const float* S0, void* o, float* Sf, void* ws,
                                 hipStream_t st);
 int64_t chunk_split_workspace_bytes(int64_t BH, int64_t T);
+hipError_t chunk_kda_ut_dispatch(int64_t BH, int64_t T, int dk, const void* q, const void* k, const float* g,
+                                 const float* beta, void* ws, hipStream_t st);
+int64_t chunk_kda_ws_halfs(int dk);
+hipError_t chunk_state_kda_dispatch(int64_t BH, int64_t T, int dk, int dv, const void* v, const float* S0, void* o,
+                                    float* Sf, const void* ws, hipStream_t st);
 hipError_t chunk_fwd_pc_prep_dispatch(int64_t BH, int64_t H, int64_t T, int dk, int dv, const void* q_raw,
                                       const void* k_raw, const void* v, const float* dt, const float* A_log,
                                       const float* dt_bias, const float* beta_logit, const float* S0, void* o,
@@ -134,8 +139,19 @@ hipError_t chunk_single_kernel(int64_t BH, int64_t T, int d_k, int d_v, int io_d
                                    o, final_state, st);
 }
 
-// The two-kernel path serves the scalar gate with bf16 I/O.
-bool uses_workspace(int io_dtype, int gate) { return io_dtype == GDR_BF16 && gate == GDR_GATE_SCALAR; }
+// Workspace bytes of one sequence for the per-channel gate: the state kernel addresses it with
+// 32-bit byte offsets.
+int64_t kda_ws_bytes_per_seq(int64_t T, int d_k) {
+    return (T + kChunkLen - 1) / kChunkLen * gdr::chunk_kda_ws_halfs(d_k) * 2;
+}
+
+// The two-kernel path serves bf16 I/O: the scalar gate always, the per-channel gate while one
+// sequence's workspace stays below 4 GiB (T below about four million tokens).
+bool uses_workspace(int64_t T, int d_k, int io_dtype, int gate) {
+    if (io_dtype != GDR_BF16) return false;
+    if (gate == GDR_GATE_SCALAR) return true;
+    return kda_ws_bytes_per_seq(T, d_k) <= int64_t(0xffffffff);
+}
 
 }  // namespace
 
@@ -159,7 +175,8 @@ int64_t gdr_chunk_fwd_workspace_size(int64_t B, int64_t H, int64_t T, int d_k, i
     if (check_common(d_k, d_v, io_dtype, gate) != GDR_OK) return -1;
     int64_t BH, BHT, bytes;
     if (!mul_ok(B, H, &BH) || !mul_ok(BH, T + kChunkLen, &BHT) || !mul_ok(BHT, 4 * kChunkLen, &bytes)) return -1;
-    if (!uses_workspace(io_dtype, gate)) return 0;
+    if (!uses_workspace(T, d_k, io_dtype, gate)) return 0;
+    if (gate == GDR_GATE_CHANNEL) return BH * kda_ws_bytes_per_seq(T, d_k);
     return gdr::chunk_split_workspace_bytes(BH, T);
 }
 
@@ -178,9 +195,9 @@ gdr_status gdr_chunk_fwd_ws(int64_t B, int64_t H, int64_t T, int d_k, int d_v, i
     if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return GDR_ERR_INVALID_ARG;
     if (need > 0) {
         // the workspace is written by the first kernel: it may overlap no input and no output
-        const int64_t esz = 2, BHT = BH * T;
+        const int64_t esz = 2, BHT = BH * T, gw = gate == GDR_GATE_CHANNEL ? d_k : 1;
         if (overlaps(workspace, need, q, BHT * d_k * esz) || overlaps(workspace, need, k, BHT * d_k * esz) ||
-            overlaps(workspace, need, v, BHT * d_v * esz) || overlaps(workspace, need, g, BHT * 4) ||
+            overlaps(workspace, need, v, BHT * d_v * esz) || overlaps(workspace, need, g, BHT * gw * 4) ||
             overlaps(workspace, need, beta, BHT * 4) || overlaps(workspace, need, o, BHT * d_v * esz) ||
             overlaps(workspace, need, initial_state, BH * d_k * d_v * 4) ||
             overlaps(workspace, need, final_state, BH * d_k * d_v * 4))
@@ -188,7 +205,12 @@ gdr_status gdr_chunk_fwd_ws(int64_t B, int64_t H, int64_t T, int d_k, int d_v, i
     }
     if (!launch) return GDR_OK;
     hipError_t e;
-    if (need > 0)
+    if (need > 0 && gate == GDR_GATE_CHANNEL) {
+        const hipStream_t st = static_cast<hipStream_t>(stream);
+        e = gdr::chunk_kda_ut_dispatch(BH, T, d_k, q, k, g, beta, workspace, st);
+        if (e == hipSuccess)
+            e = gdr::chunk_state_kda_dispatch(BH, T, d_k, d_v, v, initial_state, o, final_state, workspace, st);
+    } else if (need > 0)
         e = gdr::chunk_split_dispatch(BH, T, d_k, d_v, q, k, v, g, beta, initial_state, o, final_state, workspace,
                                       static_cast<hipStream_t>(stream));
     else

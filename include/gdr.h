@@ -104,9 +104,11 @@ gdr_status gdr_chunk_fwd(int64_t B, int64_t H, int64_t T, int d_k, int d_v,
 /*
  * gdr_chunk_fwd_workspace_size -- bytes of device workspace gdr_chunk_fwd_ws needs.
  *
- * Returns 0 for configurations that use no workspace (GDR_F32 I/O, GDR_GATE_CHANNEL), the
- * size in bytes otherwise (16 KiB per sequence and 64-token chunk: B*H*ceil(T/64)*16384),
- * and -1 for sizes or enums gdr_chunk_fwd would reject.
+ * Returns 0 for configurations that use no workspace (GDR_F32 I/O; GDR_GATE_CHANNEL with
+ * one sequence's workspace of 4 GiB or more, i.e. T > 4,161,728 for d_k = 128), the size in
+ * bytes otherwise, and -1 for sizes or enums gdr_chunk_fwd would reject.  Per sequence and
+ * 64-token chunk the scalar gate takes 16 KiB (B*H*ceil(T/64)*16384) and the per-channel gate
+ * 16384 + 388 d_k bytes (66048 for d_k = 128, 41216 for d_k = 64).
  */
 int64_t gdr_chunk_fwd_workspace_size(int64_t B, int64_t H, int64_t T, int d_k, int d_v,
                                      int io_dtype, int gate);
@@ -114,14 +116,15 @@ int64_t gdr_chunk_fwd_workspace_size(int64_t B, int64_t H, int64_t T, int d_k, i
 /*
  * gdr_chunk_fwd_ws -- gdr_chunk_fwd with a caller-provided device workspace.
  *
- * Same inputs, outputs, numerics and errors as gdr_chunk_fwd.  With bf16 I/O and the scalar
- * gate it runs the per-chunk algorithm as two kernels: the first forms, for every chunk at
- * once, T = N^{-1} diag(beta) (the UT transform) and the decayed score matrix A, and writes
- * them to the workspace; the second walks the chunks in order with
- * Z = T (V - diag(e^G) K S^T).  ("Linear Attention, Visualized", section "Gated DeltaNet
- * (GDN)", "Complete per-chunk algorithm": the chunk-local quantities can be formed for all
- * chunks in parallel.)  Other configurations ignore the workspace and behave exactly like
- * gdr_chunk_fwd.
+ * Same inputs, outputs, numerics and errors as gdr_chunk_fwd.  With bf16 I/O it runs the
+ * per-chunk algorithm as two kernels: the first forms, for every chunk at once,
+ * T = N^{-1} diag(beta) (the UT transform) and the decayed score matrix A, and writes them to
+ * the workspace; the second walks the chunks in order with Z = T (V - diag(e^G) K S^T).
+ * ("Linear Attention, Visualized", section "Gated DeltaNet (GDN)", "Complete per-chunk
+ * algorithm": the chunk-local quantities can be formed for all chunks in parallel.)  With
+ * the per-channel gate (section "Kimi Delta Attention (KDA)") the first kernel also writes
+ * the decayed copies K e^G, Q e^G, K e^{G_C - G} and e^{G_C}.  Configurations whose size
+ * query returns 0 ignore the workspace and behave exactly like gdr_chunk_fwd.
  *
  *   workspace        device buffer of at least gdr_chunk_fwd_workspace_size(...) bytes, owned
  *                    by the caller; contents on entry are ignored and on return undefined; it

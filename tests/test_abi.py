@@ -95,7 +95,10 @@ def test_workspace_size(lib):
     assert n(1, 1, 65, 64, 32, 0, 0) == 2 * 16384                    # ragged tail counts as a chunk
     assert n(1, 1, 0, 128, 128, 0, 0) == 0
     assert n(2, 2, 100, 64, 64, 1, 0) == 0                           # fp32 I/O: single kernel
-    assert n(2, 2, 100, 128, 128, 0, 1) == 0                         # channel gate: single kernel
+    assert n(2, 2, 100, 128, 128, 0, 1) == 4 * 2 * 66048             # channel gate: 16384 + 388 d_k
+    assert n(1, 3, 64, 64, 64, 0, 1) == 3 * 41216
+    assert n(1, 1, 64 * 65027, 128, 32, 0, 1) == 65027 * 66048       # one sequence just below 4 GiB
+    assert n(1, 1, 64 * 65027 + 1, 128, 32, 0, 1) == 0               # beyond: the single kernel
     assert n(1, 1, 64, 96, 128, 0, 0) == -1 and n(-1, 1, 64, 128, 128, 0, 0) == -1
     assert n(1, 1, (1 << 22) + 1, 128, 128, 0, 0) == -1
     assert gdr.chunk_fwd_workspace_size(1, 2, 128, 128, 128) == 2 * 2 * 16384

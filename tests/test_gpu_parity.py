@@ -196,25 +196,48 @@ def test_chunk_workload4_full_size_sampled(path):
 @pytest.mark.parametrize("T", [1, 37, 64, 65, 200])
 @pytest.mark.parametrize("dk,dv", [(128, 128), (128, 32), (64, 64), (128, 256), (64, 96)])
 @pytest.mark.parametrize("with_s0", [False, True])
-def test_chunk_kda_small(T, dk, dv, with_s0):
+@pytest.mark.parametrize("path", sorted(PATHS))
+def test_chunk_kda_small(T, dk, dv, with_s0, path):
     w = variant(3, d_k=dk, d_v=dv)
     x = gdr_synth.make_inputs(w, B=2, H=2, T=T)
     S0 = (np.random.default_rng(T).standard_normal((2, 2, dv, dk)) * 0.05).astype(np.float32) if with_s0 else None
-    o, S = run_chunk(x, True, S0)
+    o, S = run_chunk(x, True, S0, workspace=PATHS[path])
     o_ref, S_ref = oracle.recurrent_forward(x["q"], x["k"], x["v"], x["g"], x["beta"], S0)
-    check(f"chunk kda T={T} dk={dk} dv={dv} s0={with_s0}", o, S, o_ref, S_ref, True)
+    check(f"chunk kda {path} T={T} dk={dk} dv={dv} s0={with_s0}", o, S, o_ref, S_ref, True)
 
 
 @pytest.mark.parametrize("lo,hi", [(-3.0, -0.5), (-8.0, -0.01)])
-def test_chunk_kda_strong_decay(lo, hi):
+@pytest.mark.parametrize("path", sorted(PATHS))
+def test_chunk_kda_strong_decay(lo, hi, path):
     """Per-channel log-decays far beyond the fp16 range of the in-block factors (the
     diagonal tiles take the bf16 path); mixed with weak channels so both paths meet."""
     w = variant(3, g_dist=("uniform", lo, hi))
     x = gdr_synth.make_inputs(w, B=1, H=2, T=200)
     x["g"][..., ::3] = x["g"][..., ::3] * 0.01  # every third channel decays slowly
-    o, S = run_chunk(x, True)
+    o, S = run_chunk(x, True, workspace=PATHS[path])
     o_ref, S_ref = oracle.recurrent_forward(x["q"], x["k"], x["v"], x["g"], x["beta"])
-    check(f"chunk kda strong decay U({lo},{hi})", o, S, o_ref, S_ref, True)
+    check(f"chunk kda {path} strong decay U({lo},{hi})", o, S, o_ref, S_ref, True)
+
+
+@pytest.mark.parametrize("wid", [2, 3])
+def test_chunk_full_grid_small_T(wid):
+    """B=4, H=16, d=128: 256 value tiles of 32 channels, the grid the state pass serves with two
+    consumer waves per workgroup (smaller grids take 16-channel tiles); every sequence checked."""
+    x = gdr_synth.make_inputs(gdr_synth.WORKLOADS[wid], B=4, H=16, T=150)
+    S0 = (np.random.default_rng(wid).standard_normal((4, 16, 128, 128)) * 0.02).astype(np.float32)
+    o, S = run_chunk(x, True, S0)
+    o_ref, S_ref = oracle.recurrent_forward(x["q"], x["k"], x["v"], x["g"], x["beta"], S0)
+    check(f"full grid, workload {wid} gate, T=150", o, S, o_ref, S_ref, True)
+
+
+def test_chunk_kda_split_equals_single_closely():
+    """Per-channel gate: the two-kernel path (T formed densely) and the single kernel (blockwise
+    substitution) agree within the outputs' bf16 rounding."""
+    x = gdr_synth.make_inputs(gdr_synth.WORKLOADS[3], B=1, H=3, T=777)
+    o1, S1 = run_chunk(x, True, None, workspace="auto")
+    o2, S2 = run_chunk(x, True, None, workspace=None)
+    assert err_bf16_out(host(o1), host(o2)) <= TOL_BF16
+    assert err_literal(host(S1), host(S2)) <= TOL_BF16
 
 
 def test_chunk_kda_uniform_gate_matches_scalar_gate():
@@ -229,10 +252,11 @@ def test_chunk_kda_uniform_gate_matches_scalar_gate():
     check("scalar gate", o1, S1, o_ref, S_ref, True)
 
 
-def test_chunk_workload3_full_size_sampled():
+@pytest.mark.parametrize("path", sorted(PATHS))
+def test_chunk_workload3_full_size_sampled(path):
     """B=2, H=16, T=8192, d=128 bf16, per-channel gate; 2 of the 32 sequences checked."""
-    o, S, o_ref, S_ref = _sampled_full(3, 2, 3)
-    check("workload 3 full size (2 sampled heads)", o, S, o_ref, S_ref, True)
+    o, S, o_ref, S_ref = _sampled_full(3, 2, 3, workspace=PATHS[path])
+    check(f"workload 3 full size, {path} (2 sampled heads)", o, S, o_ref, S_ref, True)
 
 
 def test_chunk_kda_carried_state_split():
