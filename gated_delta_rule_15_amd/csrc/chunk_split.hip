@@ -555,15 +555,13 @@ __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const St
             const float* F = Fb(bc);
             auto kfrag = [&](int ti, int kb) { return ld8(Kc + (16 * ti + j) * L::LDK + 32 * kb + 8 * g); };
             auto qfrag = [&](int ti, int kb) { return ld8(Qc + (16 * ti + j) * L::LDK + 32 * kb + 8 * g); };
-            // P_K = K S^T, P_Q = Q S^T (rows = tokens)
-            float4v PK[4], PQ[4];
-            half8 fa[8], fb[8];
+            // P_K = K S^T (rows = tokens), the head of the serial chain
+            float4v PK[4];
+            half8 fa[4], fb[4];
 #pragma unroll
             for (int ti = 0; ti < 4; ++ti) {
                 PK[ti] = zero4();
-                PQ[ti] = zero4();
                 fa[ti] = kfrag(ti, 0);
-                if (!KDA) fa[4 + ti] = qfrag(ti, 0);
             }
             // fragments that do not depend on the state (T, A, K^T) are loaded while the
             // first products run
@@ -608,19 +606,19 @@ __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const St
                 half8* nxt = (kb & 1) ? fa : fb;
                 if (kb + 1 < NKB) {
 #pragma unroll
-                    for (int ti = 0; ti < 4; ++ti) {
-                        nxt[ti] = kfrag(ti, kb + 1);
-                        if (!KDA) nxt[4 + ti] = qfrag(ti, kb + 1);
-                    }
+                    for (int ti = 0; ti < 4; ++ti) nxt[ti] = kfrag(ti, kb + 1);
                 }
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int ti = 0; ti < 4; ++ti) {
-                    mma16(PK[ti], cur[ti], Sb[kb]);
-                    if (!KDA) mma16(PQ[ti], cur[4 + ti], Sb[kb]);
-                }
+                for (int ti = 0; ti < 4; ++ti) mma16(PK[ti], cur[ti], Sb[kb]);
                 prefetch(kb);
                 __builtin_amdgcn_sched_barrier(0);
+            }
+            // the first block of Q fragments, for the products after Z
+            half8 qa[4], qb[4];
+            if constexpr (!KDA) {
+#pragma unroll
+                for (int ti = 0; ti < 4; ++ti) qa[ti] = qfrag(ti, 0);
             }
             float4v er[4];
             float4v ed[KDA ? NST : 1];  // KDA: e^{G_C} of the state rows
@@ -634,16 +632,12 @@ __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const St
                 eGC = F[L::FEC];
             }
             __builtin_amdgcn_sched_barrier(0);
-            // R = V - e^G P_K,  O_hist = e^G P_Q
-            float4v Rr[4], Oh[4];
+            // R = V - e^G P_K
+            float4v Rr[4];
 #pragma unroll
-            for (int ti = 0; ti < 4; ++ti) {
+            for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    Rr[ti][r] = vv[ti][r] - eg[ti][r] * PK[ti][r];
-                    Oh[ti][r] = eg[ti][r] * PQ[ti][r];
-                }
-            }
+                for (int r = 0; r < 4; ++r) Rr[ti][r] = vv[ti][r] - eg[ti][r] * PK[ti][r];
             // Z = T R (T lower triangular: block column kb only for row tiles ti >= 2 kb)
             const half8 rB[2] = {pack8(Rr[0], Rr[1]), pack8(Rr[2], Rr[3])};
             float4v Zz[4];
@@ -653,8 +647,9 @@ __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const St
 #pragma unroll
                 for (int kb = 0; kb <= (ti >> 1); ++kb, ++n) mma16(Zz[ti], tf[n], rB[kb]);
             }
-            // O = O_hist + A Z  and  S^T <- e^{G_C} S^T + K^T diag(e^{G_C - G}) Z: both groups
-            // of products are issued before any of their results is used
+            // S^T <- e^{G_C} S^T + K^T diag(e^{G_C - G}) Z first (the chain), then, off the
+            // chain, P_Q = Q S^T with the state of the chunk start (its fp16 copy Sb) and
+            // O = e^G P_Q + A Z
             const half8 zB[2] = {pack8(Zz[0], Zz[1]), pack8(Zz[2], Zz[3])};
             half8 sZ0 = zB[0], sZ1 = zB[1];
             if constexpr (!KDA) {
@@ -665,19 +660,6 @@ __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const St
                     for (int r = 0; r < 4; ++r) zs[ti][r] = er[ti][r] * Zz[ti][r];
                 sZ0 = pack8(zs[0], zs[1]);
                 sZ1 = pack8(zs[2], zs[3]);
-            } else {
-                // P_Q = (Q e^G) S^T with the state of the chunk start
-#pragma unroll
-                for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                    for (int ti = 0; ti < 4; ++ti) mma16(Oh[ti], qg[ti][kb], Sb[kb]);
-            }
-            float4v Oa[4];
-#pragma unroll
-            for (int ti = 0, n = 0; ti < 4; ++ti) {
-                Oa[ti] = Oh[ti];
-#pragma unroll
-                for (int kb = 0; kb <= (ti >> 1); ++kb, ++n) mma16(Oa[ti], af[n], zB[kb]);
             }
 #pragma unroll
             for (int t = 0; t < NST; ++t) {
@@ -686,7 +668,34 @@ __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const St
                 mma16(St[t], kt0[t], sZ0);
                 mma16(St[t], kt1[t], sZ1);
             }
+            float4v PQ[4];
+#pragma unroll
+            for (int ti = 0; ti < 4; ++ti) PQ[ti] = zero4();
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                if constexpr (KDA) {
+#pragma unroll
+                    for (int ti = 0; ti < 4; ++ti) mma16(PQ[ti], qg[ti][kb], Sb[kb]);
+                } else {
+                    half8* cur = (kb & 1) ? qb : qa;
+                    half8* nxt = (kb & 1) ? qa : qb;
+                    if (kb + 1 < NKB) {
+#pragma unroll
+                        for (int ti = 0; ti < 4; ++ti) nxt[ti] = qfrag(ti, kb + 1);
+                    }
+#pragma unroll
+                    for (int ti = 0; ti < 4; ++ti) mma16(PQ[ti], cur[ti], Sb[kb]);
+                }
+            }
             if (c + 1 < nC) issue_qg(c + 1);
+            float4v Oa[4];
+#pragma unroll
+            for (int ti = 0, n = 0; ti < 4; ++ti) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Oa[ti][r] = eg[ti][r] * PQ[ti][r];
+#pragma unroll
+                for (int kb = 0; kb <= (ti >> 1); ++kb, ++n) mma16(Oa[ti], af[n], zB[kb]);
+            }
             // O rounded to bf16 into this wave's rows of O^T (the loaders store it)
 #pragma unroll
             for (int ti = 0; ti < 4; ++ti)
