@@ -164,12 +164,12 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
     const int DV = a.dv;
     const auto rq = make_rsrc(a.q + bh * T * DK, (uint32_t)(T * DK * 2));
     const auto rk = make_rsrc(a.k + bh * T * DK, (uint32_t)(T * DK * 2));
-    const auto rv = make_rsrc(a.v + bh * T * DV, (uint32_t)(T * DV * 2));
+    const auto rv = make_rsrc(UT ? nullptr : a.v + bh * T * DV, UT ? 0u : (uint32_t)(T * DV * 2));
     const auto rg = make_rsrc(a.g + bh * T * DK, (uint32_t)(T * DK * 4));
     const auto rb = make_rsrc(GD2 ? nullptr : a.beta + bh * T, GD2 ? 0u : (uint32_t)(T * 4));
     const auto re = make_rsrc(GD2 ? a.eg + bh * T * DK : nullptr, GD2 ? (uint32_t)(T * DK * 4) : 0u);
     const auto rw = make_rsrc(GD2 ? a.wg + bh * T * DV : nullptr, GD2 ? (uint32_t)(T * DV * 4) : 0u);
-    const auto ro = make_rsrc(a.o + bh * T * DV, (uint32_t)(T * DV * 2));
+    const auto ro = make_rsrc(UT ? nullptr : a.o + bh * T * DV, UT ? 0u : (uint32_t)(T * DV * 2));
     const int dvc = dv0 + 16 * w;  // first value channel of consumer wave w (w < 2)
 
     auto trfrag = [&](const _Float16* base, int ld, int kb, int col) {

@@ -24,7 +24,8 @@
 //
 // Workspace layout, per (sequence, chunk): A^T [64][64] (row m holds A[l][m], l = 0..63), then
 // T [64][64] (row l; column m stored at position pperm(m), so one operand fragment is one
-// 16-byte read).  Upper triangles are stored as zeros.
+// 16-byte read), both fp16 with zeros in the upper triangles; then the decay factors of the
+// state pass, fp32: e^{G_l} [64], e^{G_C - G_l} [64], e^{G_C}, 15 zeros (16960 bytes).
 //
 // The per-channel gate ("Kimi Delta Attention (KDA)" section of the same page) takes the same
 // state kernel in its KDA instantiation: the UT pass (chunk_kda.hip) also writes the decayed
@@ -45,6 +46,11 @@ namespace gdr {
 struct UtTab {
     static constexpr int SG = 0, SB = 192, SCF = 272, SRF = 336, SRB = 528, NSM = 736;
 };
+
+// workspace record of one (sequence, chunk) of the scalar gate, in halfs: A^T, T, factors
+constexpr int kGdnWsFactors = 2 * kChunk * kChunk;        // offset of the fp32 factor table
+constexpr int kGdnWsNF = 144;                               // its floats
+constexpr int kGdnWsStride = kGdnWsFactors + 2 * kGdnWsNF;  // 8480 halfs = 16960 bytes
 
 struct UtArgs {
     int64_t T;
@@ -134,6 +140,12 @@ __global__ __launch_bounds__(128) void chunk_ut_kernel(const UtArgs a) {
             for (int b = 0; b < 4; ++b) ge[b] = lane_value(x, 16 * b + 15);
             const int blk = l >> 4;
             sm[S::SG + l] = x;
+            // the state pass's factors of this chunk
+            float* fw = reinterpret_cast<float*>(a.ws + (bh * a.nC + c) * kGdnWsStride + kGdnWsFactors);
+            const float GC = ge[3];
+            fw[l] = fast_exp(x);
+            fw[64 + l] = fast_exp(GC - x);
+            if (l < kGdnWsNF - 128) fw[128 + l] = l == 0 ? fast_exp(GC) : 0.0f;
             sm[S::SB + l] = bt;
             sm[S::SCF + l] = fast_exp(ge[blk] - x);
 #pragma unroll
@@ -317,7 +329,7 @@ __global__ __launch_bounds__(128) void chunk_ut_kernel(const UtArgs a) {
     lds_barrier();
 
     // ---- A^T and T to the workspace, 16-byte pieces
-    uint16_t* dst = a.ws + (bh * a.nC + c) * (2 * C * C);
+    uint16_t* dst = a.ws + (bh * a.nC + c) * kGdnWsStride;
 #pragma unroll
     for (int u = 0; u < C * C / 8 / 128; ++u) {
         const int idx = tid + 128 * u, row = idx / (C / 8), col = (idx % (C / 8)) * 8;
@@ -336,7 +348,6 @@ struct StArgs {
     const uint16_t* q;
     const uint16_t* k;
     const uint16_t* v;
-    const float* g;
     const uint16_t* ws;
     const float* S0;
     uint16_t* o;
@@ -350,8 +361,9 @@ struct StLds {
     static constexpr int LDC = C + 8;
     static constexpr int LDV = 80;     // bf16, rows (tokens) of the 32-channel V tile
     static constexpr int LDO = C + 8;  // bf16, rows of O^T
-    // factor table: [0,64) e^G   [64,128) e^{G_C - G}   [128] e^{G_C}
-    static constexpr int FEG = 0, FER = 64, FEC = 128, NF = 144;
+    // factor table (scalar gate): [0,64) e^G   [64,128) e^{G_C - G}   [128] e^{G_C}
+    // (per-channel gate: e^{G_C} [DK])
+    static constexpr int FEG = 0, FER = 64, FEC = 128, NF = kGdnWsNF;
     static constexpr int szK = C * LDK * 2;
     static constexpr int szC = C * LDC * 2;
     static constexpr int szV = C * LDV * 2;
@@ -395,11 +407,11 @@ __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const St
     const int dvc = dv0 + 16 * w;
     const int64_t T = a.T, nC = a.nC;
     const int DV = a.dv;
-    const auto rq = make_rsrc(a.q + bh * T * DK, (uint32_t)(T * DK * 2));
-    const auto rk = make_rsrc(a.k + bh * T * DK, (uint32_t)(T * DK * 2));
+    // (the per-channel gate reads no q or k: those resources are empty)
+    const auto rq = make_rsrc(KDA ? nullptr : a.q + bh * T * DK, KDA ? 0u : (uint32_t)(T * DK * 2));
+    const auto rk = make_rsrc(KDA ? nullptr : a.k + bh * T * DK, KDA ? 0u : (uint32_t)(T * DK * 2));
     const auto rv = make_rsrc(a.v + bh * T * DV, (uint32_t)(T * DV * 2));
-    const auto rg = make_rsrc(KDA ? nullptr : a.g + bh * T, KDA ? 0u : (uint32_t)(T * 4));
-    constexpr int WS = KDA ? kda_ws_stride<DK>() : 2 * C * C;  // workspace halfs per chunk
+    constexpr int WS = KDA ? kda_ws_stride<DK>() : kGdnWsStride;  // workspace halfs per chunk
     // offsets (halfs) inside a chunk's workspace record of the per-channel gate
     constexpr int WKG = 2 * C * C, WQG = WKG + C * DK, WKC = WQG + C * DK, WFE = WKC + C * DK;
     const auto rw = make_rsrc(a.ws + bh * nC * WS, (uint32_t)(nC * WS * 2));
@@ -410,15 +422,21 @@ __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const St
         return cat8(ldtr(p0), ldtr(p0 + 16 * ld));
     };
 
-    // ---- loader waves (2, 3): registers for one chunk, staged into LDS one chunk ahead
+    // ---- loader waves (the last two): two register sets, so a chunk's loads are issued two
+    // chunks before the loaders stage it into LDS (one chunk ahead of the consumers)
     const int lt = tid - 64 * NCW;  // loader thread in [0, 128)
     constexpr int NPV = NCW;        // 16-byte pieces of the V tile per loader thread
     constexpr int NPK = C * DK / 8 / 128;  // K (and Q) pieces per loader thread
     constexpr int NPW = C * C / 8 / 128;   // A^T (and T) pieces per loader thread
-    // (KDA: kr holds K e^G, qr K e^{G_C - G}, gr e^{G_C} of channel lt)
-    uint4 kr[NPK], qr[NPK], ar[NPW], tr[NPW], vr[NPV];
-    float gr = 0.0f;
-    auto issue = [&](int64_t c) {
+    // (KDA: kr holds K e^G, qr K e^{G_C - G}); fr: 16-byte pieces of the factor table, the
+    // first NFQ loader threads one each
+    constexpr int NFQ = KDA ? DK / 4 : L::NF / 4;
+    struct LdRegs {
+        uint4 kr[NPK], qr[NPK], ar[NPW], tr[NPW], vr[NPV], fr;
+    };
+    LdRegs R0, R1;
+    auto issue = [&](LdRegs& R, int64_t c) {
+        uint4 *kr = R.kr, *qr = R.qr, *ar = R.ar, *tr = R.tr, *vr = R.vr;
         const uint32_t t0 = (uint32_t)(c * C);
         const uint32_t wb = (uint32_t)(c * WS);
 #pragma unroll
@@ -444,11 +462,7 @@ __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const St
             const int idx = lt + 128 * u, row = idx / (2 * NCW), col = (idx % (2 * NCW)) * 8;
             vr[u] = bld16(rv, ((t0 + row) * DV + dv0 + col) * 2);
         }
-        if constexpr (KDA) {
-            if (lt < DK) gr = bld4(rw, (wb + WFE) * 2 + lt * 4);
-        } else {
-            if (w == NCW) gr = bld4(rg, (t0 + l) * 4);
-        }
+        if (lt < NFQ) R.fr = bld16(rw, (wb + (KDA ? WFE : kGdnWsFactors)) * 2 + lt * 16);
     };
     // o of chunk c from its O^T buffer: loader wave lw takes rows (value channels) 16 lw ..,
     // a lane reads 8 consecutive channels of one token back transposed and stores 16 bytes
@@ -466,15 +480,17 @@ __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const St
         }
     };
     // K and Q to fp16 in the registers (while the consumers' first products read LDS)
-    auto convert = [&]() {
+    auto convert = [&](LdRegs& R) {
         if constexpr (KDA) return;  // the UT pass wrote fp16
+        uint4 *kr = R.kr, *qr = R.qr;
 #pragma unroll
         for (int u = 0; u < NPK; ++u) {
             kr[u] = __builtin_bit_cast(uint4, bf16x8_to_half8(kr[u]));
             qr[u] = __builtin_bit_cast(uint4, bf16x8_to_half8(qr[u]));
         }
     };
-    auto stage = [&](int64_t c) {
+    auto stage = [&](LdRegs& R, int64_t c) {
+        const uint4 *kr = R.kr, *qr = R.qr, *ar = R.ar, *tr = R.tr, *vr = R.vr;
         const int b = (int)(c & 1);
 #pragma unroll
         for (int u = 0; u < NPK; ++u) {
@@ -493,16 +509,7 @@ __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const St
             const int idx = lt + 128 * u, row = idx / (2 * NCW), col = (idx % (2 * NCW)) * 8;
             *reinterpret_cast<uint4*>(Vb(b) + row * L::LDV + col) = vr[u];
         }
-        if constexpr (KDA) {
-            if (lt < DK) Fb(b)[lt] = gr;
-        } else if (w == NCW) {  // in-chunk cumulative log-decay (lane = token) and its factors
-            const float x = wave_inclusive_scan(gr);
-            const float GC = lane_value(x, 63);
-            float* F = Fb(b);
-            F[L::FEG + l] = fast_exp(x);
-            F[L::FER + l] = fast_exp(GC - x);
-            if (l == 0) F[L::FEC] = fast_exp(GC);
-        }
+        if (lt < NFQ) reinterpret_cast<uint4*>(Fb(b))[lt] = R.fr;
     };
 
     // ---- consumer waves (0, 1): the state S^T of 16 value channels (fp32 accumulators, rows
@@ -519,11 +526,13 @@ __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const St
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) Sb[kb] = pack8(St[2 * kb], St[2 * kb + 1]);
 
+    // chunk k's loads live in register set k mod 2
     if (!consumer && nC > 0) {
-        issue(0);
-        convert();
-        stage(0);
-        if (nC > 1) issue(1);
+        issue(R0, 0);
+        convert(R0);
+        stage(R0, 0);
+        if (nC > 1) issue(R1, 1);
+        if (nC > 2) issue(R0, 2);
     }
     lds_barrier();
 
@@ -707,16 +716,20 @@ __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const St
         lds_barrier();
     }
     } else {
-    for (int64_t c = 0; c < nC; ++c) {
-        // loaders: o of the previous chunk, the next chunk into LDS, then the loads of the one
-        // after
+    // loaders: o of the previous chunk, the next chunk (set (c+1) mod 2) into LDS, then the
+    // loads of chunk c+3 into the freed set
+    auto step = [&](LdRegs& R, int64_t c) {
         if (c > 0) store_o(c - 1);
         if (c + 1 < nC) {
-            convert();
-            stage(c + 1);
-            if (c + 2 < nC) issue(c + 2);
+            convert(R);
+            stage(R, c + 1);
+            if (c + 3 < nC) issue(R, c + 3);
         }
         lds_barrier();
+    };
+    for (int64_t c = 0; c < nC; c += 2) {
+        step(R1, c);
+        if (c + 1 < nC) step(R0, c + 1);
     }
     if (nC > 0) store_o(nC - 1);
     }
@@ -770,10 +783,10 @@ static hipError_t launch_split(const UtArgs& u, const StArgs& s, int64_t BH, hip
     return launch_state<DK, false>(s, BH, st);
 }
 
-// Bytes of workspace the two-kernel path needs: 16 KiB per (sequence, chunk).
+// Bytes of workspace the two-kernel path needs: 16960 per (sequence, chunk).
 int64_t chunk_split_workspace_bytes(int64_t BH, int64_t T) {
     const int64_t nC = (T + kChunk - 1) / kChunk;
-    return BH * nC * (2 * kChunk * kChunk) * 2;
+    return BH * nC * kGdnWsStride * 2;
 }
 
 hipError_t chunk_split_dispatch(int64_t BH, int64_t T, int dk, int dv, const void* q, const void* k, const void* v,
@@ -796,7 +809,6 @@ hipError_t chunk_split_dispatch(int64_t BH, int64_t T, int dk, int dv, const voi
     s.q = u.q;
     s.k = u.k;
     s.v = static_cast<const uint16_t*>(v);
-    s.g = g;
     s.ws = u.ws;
     s.S0 = S0;
     s.o = static_cast<uint16_t*>(o);
@@ -817,7 +829,6 @@ hipError_t chunk_state_kda_dispatch(int64_t BH, int64_t T, int dk, int dv, const
     s.q = nullptr;
     s.k = nullptr;
     s.v = static_cast<const uint16_t*>(v);
-    s.g = nullptr;
     s.ws = static_cast<const uint16_t*>(ws);
     s.S0 = S0;
     s.o = static_cast<uint16_t*>(o);

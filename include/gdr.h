@@ -107,8 +107,8 @@ gdr_status gdr_chunk_fwd(int64_t B, int64_t H, int64_t T, int d_k, int d_v,
  * Returns 0 for configurations that use no workspace (GDR_F32 I/O; GDR_GATE_CHANNEL with
  * one sequence's workspace of 4 GiB or more, i.e. T > 4,161,728 for d_k = 128), the size in
  * bytes otherwise, and -1 for sizes or enums gdr_chunk_fwd would reject.  Per sequence and
- * 64-token chunk the scalar gate takes 16 KiB (B*H*ceil(T/64)*16384) and the per-channel gate
- * 16384 + 388 d_k bytes (66048 for d_k = 128, 41216 for d_k = 64).
+ * 64-token chunk the scalar gate takes 16960 bytes (B*H*ceil(T/64)*16960) and the per-channel
+ * gate 16384 + 388 d_k bytes (66048 for d_k = 128, 41216 for d_k = 64).
  */
 int64_t gdr_chunk_fwd_workspace_size(int64_t B, int64_t H, int64_t T, int d_k, int d_v,
                                      int io_dtype, int gate);

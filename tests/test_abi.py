@@ -91,8 +91,8 @@ def test_chunk_fwd_empty_batch_is_a_noop(lib):
 
 def test_workspace_size(lib):
     n = lib.gdr_chunk_fwd_workspace_size
-    assert n(4, 16, 4096, 128, 128, 0, 0) == 64 * 64 * 16384        # 16 KiB per (sequence, chunk)
-    assert n(1, 1, 65, 64, 32, 0, 0) == 2 * 16384                    # ragged tail counts as a chunk
+    assert n(4, 16, 4096, 128, 128, 0, 0) == 64 * 64 * 16960        # A^T, T, factors per (sequence, chunk)
+    assert n(1, 1, 65, 64, 32, 0, 0) == 2 * 16960                    # ragged tail counts as a chunk
     assert n(1, 1, 0, 128, 128, 0, 0) == 0
     assert n(2, 2, 100, 64, 64, 1, 0) == 0                           # fp32 I/O: single kernel
     assert n(2, 2, 100, 128, 128, 0, 1) == 4 * 2 * 66048             # channel gate: 16384 + 388 d_k
@@ -101,7 +101,7 @@ def test_workspace_size(lib):
     assert n(1, 1, 64 * 65027 + 1, 128, 32, 0, 1) == 0               # beyond: the single kernel
     assert n(1, 1, 64, 96, 128, 0, 0) == -1 and n(-1, 1, 64, 128, 128, 0, 0) == -1
     assert n(1, 1, (1 << 22) + 1, 128, 128, 0, 0) == -1
-    assert gdr.chunk_fwd_workspace_size(1, 2, 128, 128, 128) == 2 * 2 * 16384
+    assert gdr.chunk_fwd_workspace_size(1, 2, 128, 128, 128) == 2 * 2 * 16960
 
 
 def ws(lib, B=1, H=1, T=64, dk=128, dv=128, io=0, gate=0, q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, s0=None,
@@ -113,7 +113,7 @@ def ws(lib, B=1, H=1, T=64, dk=128, dv=128, io=0, gate=0, q=FAKE, k=FAKE, v=FAKE
     (dict(B=-1), INVALID), (dict(dk=96), SHAPE), (dict(io=2), DTYPE), (dict(q=None), INVALID),
     (dict(o=FAKE), INVALID),                                    # o overlaps q
     (dict(w=None), INVALID),                                    # a workspace is required
-    (dict(nbytes=16383), INVALID),                              # one chunk needs 16 KiB
+    (dict(nbytes=16959), INVALID),                              # one chunk needs 16960 bytes
     (dict(nbytes=-1), INVALID),
     (dict(w=FAKE), INVALID),                                    # workspace overlaps q
     (dict(w=FAKE2), INVALID),                                   # workspace overlaps o
