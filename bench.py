@@ -32,7 +32,7 @@ PEAK_MFMA_F16 = 2500.0  # TFLOP/s, MI355X dense fp16/bf16
 PEAK_HBM = 8000.0       # GB/s, MI355X HBM3E
 # the headline step: one gdr_chunk_fwd_ws call = the UT kernel over all chunks, then the
 # chunk-serial state kernel
-CHUNK_KERNEL = "chunk_ut_kernel<128> + chunk_state_kernel<128, false, 2>"
+CHUNK_KERNEL = "chunk_ut_kernel<128> + chunk_state_kernel<128, 0, 2>"
 CHUNK_SOURCE = os.path.join(ROOT, "gated_delta_rule_15_amd", "csrc", "chunk_split.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "chunk_split_gdn_bf16_B4_H16_T4096_traffic.json")
 COPY_BYTES = 256 << 20  # calibration copy for the HBM byte counters
@@ -299,21 +299,28 @@ def bench_gdn2(torch, gdr, gdr_synth, steps=10):
         sets[-1]["host"] = x if salt == 0 else None
     outs = [torch.empty((w.B, w.H, w.T, w.d_v), dtype=torch.bfloat16, device="cuda") for _ in sets]
     fin = [torch.empty((w.B, w.H, w.d_v, w.d_k), dtype=torch.float32, device="cuda") for _ in sets]
+    wsb = torch.empty(max(gdr.gdn2_chunk_fwd_workspace_size(w.B, w.H, w.T, w.d_k, w.d_v), 1), dtype=torch.uint8,
+                      device="cuda")
 
-    def launch(i):
+    def launch(i, ws=wsb):
         s = sets[i % 2]
-        gdr.gdn2_chunk_fwd(s["q"], s["k"], s["v"], s["g"], s["b"], s["w"], out=outs[i % 2], final_state=fin[i % 2])
+        gdr.gdn2_chunk_fwd(s["q"], s["k"], s["v"], s["g"], s["b"], s["w"], out=outs[i % 2], final_state=fin[i % 2],
+                           workspace=ws)
 
-    for i in range(2):
-        launch(i)
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for i in range(steps):
-        ev[i][0].record()
-        launch(i)
-        ev[i][1].record()
-    torch.cuda.synchronize()
-    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    def timed(ws):
+        for i in range(2):
+            launch(i, ws)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for i in range(steps):
+            ev[i][0].record()
+            launch(i, ws)
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+    ms_single = timed(None)
+    ms = timed(wsb)
     flops = chunk_flops(w.B, w.H, w.T, w.d_k, w.d_v)
     n = w.B * w.H * w.T
     nbytes = n * (2 * w.d_k + 2 * w.d_v) * 2 + n * (2 * w.d_k + w.d_v) * 4 + w.B * w.H * w.d_k * w.d_v * 4
@@ -326,7 +333,9 @@ def bench_gdn2(torch, gdr, gdr_synth, steps=10):
     torch.cuda.synchronize()
     return {"workload": "gdn2_bf16: Gated DeltaNet-2 B=2 H=16 T=8192 d_k=d_v=128 bf16, fp32 g, b [B,H,T,128], "
                         "w [B,H,T,128], zero S0",
-            "kernel": "chunk_kda_kernel<128, true, false>", "ms_per_call": round(ms, 4),
+            "kernel": "chunk_kda_kernel<128, true, true> + chunk_state_kernel<128, 2, 1>",
+            "ms_per_call": round(ms, 4),
+            "single_kernel": {"kernel": "chunk_kda_kernel<128, true, false>", "ms_per_call": round(ms_single, 4)},
             "tokens_per_s": round(w.B * w.T / (ms * 1e-3), 1),
             "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_MFMA_F16, 4),
             "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM, 4),
@@ -453,7 +462,7 @@ def main():
         b3 = chunk_bytes(w3.B, w3.H, w3.T, 128, 128, gate_per_channel=True)
         result["kda"] = {
             "workload": "per-channel gate B=2 H=16 T=8192 d=128 bf16, fp32 gate [B,H,T,128]",
-            "kernel": "chunk_kda_kernel<128, false, true> + chunk_state_kernel<128, true, 1>",
+            "kernel": "chunk_kda_kernel<128, false, true> + chunk_state_kernel<128, 1, 1>",
             "ms_per_call": round(m3, 4),
             "tokens_per_s": round(w3.B * w3.T / (m3 * 1e-3), 1),
             "mfma_frac": round(f3 / (m3 * 1e-3) / 1e12 / PEAK_MFMA_F16, 4),

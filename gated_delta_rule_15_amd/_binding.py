@@ -21,7 +21,7 @@ GDR_GATE_SCALAR, GDR_GATE_CHANNEL = 0, 1
 # every entry point include/gdr.h declares
 EXPORTED_SYMBOLS = ("gdr_version", "gdr_status_string", "gdr_chunk_fwd", "gdr_chunk_fwd_workspace_size",
                     "gdr_chunk_fwd_ws", "gdr_chunk_fwd_fused_prep", "gdr_gdp_chunk_fwd", "gdr_gdn2_chunk_fwd",
-                    "gdr_frame_fwd_workspace_size", "gdr_frame_fwd", "gdr_decode_step")
+                    "gdr_gdn2_chunk_fwd_workspace_size", "gdr_gdn2_chunk_fwd_ws", "gdr_frame_fwd_workspace_size", "gdr_frame_fwd", "gdr_decode_step")
 
 _lock = threading.Lock()
 _lib = None
@@ -59,6 +59,10 @@ def load_library():
         lib.gdr_gdp_chunk_fwd.argtypes = [i64, i64, i64, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P]
         lib.gdr_gdn2_chunk_fwd.restype = i32
         lib.gdr_gdn2_chunk_fwd.argtypes = [i64, i64, i64, i32, i32, i32, P, P, P, P, P, P, P, P, P, P]
+        lib.gdr_gdn2_chunk_fwd_workspace_size.restype = i64
+        lib.gdr_gdn2_chunk_fwd_workspace_size.argtypes = [i64, i64, i64, i32, i32]
+        lib.gdr_gdn2_chunk_fwd_ws.restype = i32
+        lib.gdr_gdn2_chunk_fwd_ws.argtypes = [i64, i64, i64, i32, i32, i32, P, P, P, P, P, P, P, P, P, P, i64, P]
         lib.gdr_frame_fwd_workspace_size.restype = i64
         lib.gdr_frame_fwd_workspace_size.argtypes = [i64, i64, i64, i32, i32, i32]
         lib.gdr_frame_fwd.restype = i32
@@ -254,14 +258,23 @@ def gdp_chunk_fwd(q, k, v, g, beta, initial_state=None, *, output_final_state=Tr
     return o, final_state
 
 
+def gdn2_chunk_fwd_workspace_size(B, H, T, d_k, d_v) -> int:
+    n = int(load_library().gdr_gdn2_chunk_fwd_workspace_size(B, H, T, d_k, d_v))
+    if n < 0:
+        raise GdrError(GDR_ERR_SHAPE, "gdr_gdn2_chunk_fwd_workspace_size")
+    return n
+
+
 def gdn2_chunk_fwd(q, k, v, g, b, w, initial_state=None, *, output_final_state=True, out=None,
-                   final_state=None, stream=None):
-    """gdr_gdn2_chunk_fwd (Gated DeltaNet-2) on torch tensors.
+                   final_state=None, stream=None, workspace="auto"):
+    """Gated DeltaNet-2 (gdr_gdn2_chunk_fwd_ws, or gdr_gdn2_chunk_fwd) on torch tensors.
 
     q, k [B,H,T,d_k]; v [B,H,T,d_v] (bf16); g [B,H,T,d_k] fp32 (per-channel log-decay);
     b [B,H,T,d_k] fp32 (erase gate); w [B,H,T,d_v] fp32 (write gate); initial_state
-    [B,H,d_v,d_k] fp32 or None.  Returns (o, final_state); final_state is None when
-    output_final_state is False.
+    [B,H,d_v,d_k] fp32 or None.  workspace: "auto" (default) allocates the two-kernel path's
+    workspace with torch; a uint8 CUDA tensor is used as that workspace; None calls the
+    single kernel.  Returns (o, final_state); final_state is None when output_final_state is
+    False.
     """
     import torch
     B, H, T, dk = q.shape
@@ -284,11 +297,26 @@ def gdn2_chunk_fwd(q, k, v, g, b, w, initial_state=None, *, output_final_state=T
         final_state = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
     if final_state is not None:
         _check(final_state, "final_state", (B, H, dv, dk), torch.float32, dev)
-    st = load_library().gdr_gdn2_chunk_fwd(B, H, T, dk, dv, io, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b),
-                                           _ptr(w), _ptr(initial_state), _ptr(o), _ptr(final_state),
-                                           _stream(stream, dev))
+    if workspace is None:
+        st = load_library().gdr_gdn2_chunk_fwd(B, H, T, dk, dv, io, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b),
+                                               _ptr(w), _ptr(initial_state), _ptr(o), _ptr(final_state),
+                                               _stream(stream, dev))
+        if st != GDR_OK:
+            raise GdrError(st, "gdr_gdn2_chunk_fwd")
+        return o, final_state
+    need = gdn2_chunk_fwd_workspace_size(B, H, T, dk, dv)
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError(f"workspace: expected 'auto', None or a tensor, got {workspace!r}")
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace: must be a contiguous tensor on the inputs' device")
+    nbytes = workspace.numel() * workspace.element_size()
+    st = load_library().gdr_gdn2_chunk_fwd_ws(B, H, T, dk, dv, io, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b),
+                                              _ptr(w), _ptr(initial_state), _ptr(o), _ptr(final_state),
+                                              _ptr(workspace), nbytes, _stream(stream, dev))
     if st != GDR_OK:
-        raise GdrError(st, "gdr_gdn2_chunk_fwd")
+        raise GdrError(st, "gdr_gdn2_chunk_fwd_ws")
     return o, final_state
 
 

@@ -168,7 +168,7 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
     const auto rg = make_rsrc(a.g + bh * T * DK, (uint32_t)(T * DK * 4));
     const auto rb = make_rsrc(GD2 ? nullptr : a.beta + bh * T, GD2 ? 0u : (uint32_t)(T * 4));
     const auto re = make_rsrc(GD2 ? a.eg + bh * T * DK : nullptr, GD2 ? (uint32_t)(T * DK * 4) : 0u);
-    const auto rw = make_rsrc(GD2 ? a.wg + bh * T * DV : nullptr, GD2 ? (uint32_t)(T * DV * 4) : 0u);
+    const auto rw = make_rsrc(GD2 && !UT ? a.wg + bh * T * DV : nullptr, GD2 && !UT ? (uint32_t)(T * DV * 4) : 0u);
     const auto ro = make_rsrc(UT ? nullptr : a.o + bh * T * DV, UT ? 0u : (uint32_t)(T * DV * 2));
     const int dvc = dv0 + 16 * w;  // first value channel of consumer wave w (w < 2)
 
@@ -220,8 +220,10 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
             const uint32_t vidx = (tc + (tid >> 2)) * DV + dv0 + (tid & 3) * 8;
             if (!UT) vp = bld16(rv, vidx * 2);
             if constexpr (GD2) {
-                wp0 = bld16(rw, vidx * 4);
-                wp1 = bld16(rw, vidx * 4 + 16);
+                if (!UT) {  // the UT pass has no V
+                    wp0 = bld16(rw, vidx * 4);
+                    wp1 = bld16(rw, vidx * 4 + 16);
+                }
             } else {
                 if (w == 0) bp = bld4(rb, (tc + l) * 4);
             }
@@ -498,8 +500,8 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
                 }
                 *reinterpret_cast<half8*>(Xd + (16 * b + jc) * L::LDX) = h0;
                 *reinterpret_cast<half8*>(Xd + (16 * b + jc) * L::LDX + 8) = h1;
-                if (UT) {  // diagonal block of T = N^{-1} diag(beta)
-                    const float bc = FB[16 * b + jc];
+                if (UT) {  // diagonal block of T = N^{-1} diag(beta) (GD2: N^{-1}, e carries the gate)
+                    const float bc = GD2 ? 1.0f : FB[16 * b + jc];
                     const int pc = pperm(16 * b + jc);
 #pragma unroll
                     for (int i = 0; i < 16; ++i) Tt[(16 * b + i) * L::LDC + pc] = (_Float16)(xd[i] * bc);
@@ -540,7 +542,7 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
                 constexpr int cb = decltype(cc)::value;
                 half4 mb[4];
                 mb[cb] = *reinterpret_cast<const half4*>(Xd + (16 * cb + j) * L::LDX + 4 * g);
-                const float bcol = FB[16 * cb + j];
+                const float bcol = GD2 ? 1.0f : FB[16 * cb + j];
                 const int pc = pperm(16 * cb + j);
 #pragma unroll
                 for (int b = cb + 1; b < 4; ++b) {
@@ -759,9 +761,10 @@ hipError_t chunk_kda_dispatch(int64_t BH, int64_t T, int dk, int dv, const void*
 
 // UT pass of the per-channel-gate two-kernel path: one group per (sequence, run of chunks), the
 // runs sized so the grid about fills the chip once (a group walks its chunks with the next
-// chunk's loads in flight).
+// chunk's loads in flight).  With an erase gate eg (Gated DeltaNet-2) the row operand is
+// eg (.) k and T = N^{-1}; beta is then unused.
 hipError_t chunk_kda_ut_dispatch(int64_t BH, int64_t T, int dk, const void* q, const void* k, const float* g,
-                                 const float* beta, void* ws, hipStream_t st) {
+                                 const float* beta, const float* eg, void* ws, hipStream_t st) {
     KdaArgs a;
     a.T = T;
     a.dv = 32;
@@ -770,8 +773,8 @@ hipError_t chunk_kda_ut_dispatch(int64_t BH, int64_t T, int dk, const void* q, c
     a.k = static_cast<const uint16_t*>(k);
     a.v = nullptr;
     a.g = g;
-    a.beta = beta;
-    a.eg = nullptr;
+    a.beta = eg ? nullptr : beta;
+    a.eg = eg;
     a.wg = nullptr;
     a.S0 = nullptr;
     a.o = nullptr;
@@ -790,6 +793,10 @@ hipError_t chunk_kda_ut_dispatch(int64_t BH, int64_t T, int dk, const void* q, c
     const int64_t cpw = (BH * nC + ncu - 1) / ncu;
     a.cpw = (int)(cpw < nC ? cpw : nC);
     const int64_t nwg = BH * ((nC + a.cpw - 1) / a.cpw);
+    if (eg) {
+        if (dk == 128) return launch_kda<128, true, true>(a, nwg, st);
+        return launch_kda<64, true, true>(a, nwg, st);
+    }
     if (dk == 128) return launch_kda<128, false, true>(a, nwg, st);
     return launch_kda<64, false, true>(a, nwg, st);
 }

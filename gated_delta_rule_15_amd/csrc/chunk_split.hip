@@ -34,6 +34,10 @@
 // S^T <- Diag(e^{G_C}) S^T + (K e^{G_C - G})^T Z.  The loaders stage K e^G in the K buffer and
 // K e^{G_C - G} in the Q buffer; the consumers read their Q e^G fragments straight from the
 // workspace, one chunk ahead, and take the Q e^G S^T products after Z, off the serial chain.
+// Gated DeltaNet-2 ("Gated DeltaNet-2, and the gate that was doing two jobs", section 2) runs
+// the same code in its own instantiation: its UT pass has put the erase gate into the row copy
+// (b (.) k) e^G and into T = N^{-1}, and the loaders stage z = w (.) v, computed and kept in
+// fp32 (the V buffer's rows hold 32 fp32 channels), in place of V.
 #include <type_traits>
 
 #include "chunk_common.h"
@@ -348,6 +352,7 @@ struct StArgs {
     const uint16_t* q;
     const uint16_t* k;
     const uint16_t* v;
+    const float* wg;  // KDA mode: write gate w [T][dv] (Gated DeltaNet-2; V becomes w (.) v), or null
     const uint16_t* ws;
     const float* S0;
     uint16_t* o;
@@ -380,10 +385,16 @@ struct StLds {
     static_assert((oQ | oA | oT | oV | oF | oOt) % 16 == 0, "alignment");
 };
 
+// Modes of the state pass: the scalar gate, the per-channel gate (KDA), and Gated DeltaNet-2
+// (the KDA pass with z = w (.) v in place of v).
+constexpr int kStGdn = 0, kStKda = 1, kStGd2 = 2;
+
 // NCW consumer waves of 16 value channels each (a value tile of 16 NCW channels) and two loader
 // waves.  NCW = 1 doubles the workgroups of a grid that would leave compute units idle.
-template <int DK, bool KDA, int NCW>
+template <int DK, int MODE, int NCW>
 __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const StArgs a) {
+    constexpr bool KDA = MODE != kStGdn;  // the UT pass wrote the decayed copies
+    constexpr bool ZW = MODE == kStGd2;   // V tile holds z = w (.) v in fp32
     using L = StLds<DK>;
     constexpr int C = kChunk;
     constexpr int NKB = DK / 32;
@@ -411,6 +422,7 @@ __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const St
     const auto rq = make_rsrc(KDA ? nullptr : a.q + bh * T * DK, KDA ? 0u : (uint32_t)(T * DK * 2));
     const auto rk = make_rsrc(KDA ? nullptr : a.k + bh * T * DK, KDA ? 0u : (uint32_t)(T * DK * 2));
     const auto rv = make_rsrc(a.v + bh * T * DV, (uint32_t)(T * DV * 2));
+    const auto rwg = make_rsrc(ZW ? a.wg + bh * T * DV : nullptr, ZW ? (uint32_t)(T * DV * 4) : 0u);
     constexpr int WS = KDA ? kda_ws_stride<DK>() : kGdnWsStride;  // workspace halfs per chunk
     // offsets (halfs) inside a chunk's workspace record of the per-channel gate
     constexpr int WKG = 2 * C * C, WQG = WKG + C * DK, WKC = WQG + C * DK, WFE = WKC + C * DK;
@@ -433,6 +445,7 @@ __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const St
     constexpr int NFQ = KDA ? DK / 4 : L::NF / 4;
     struct LdRegs {
         uint4 kr[NPK], qr[NPK], ar[NPW], tr[NPW], vr[NPV], fr;
+        uint4 wr[ZW ? 2 * NPV : 1];  // the write gate of the V pieces (Gated DeltaNet-2)
     };
     LdRegs R0, R1;
     auto issue = [&](LdRegs& R, int64_t c) {
@@ -461,6 +474,10 @@ __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const St
         for (int u = 0; u < NPV; ++u) {
             const int idx = lt + 128 * u, row = idx / (2 * NCW), col = (idx % (2 * NCW)) * 8;
             vr[u] = bld16(rv, ((t0 + row) * DV + dv0 + col) * 2);
+            if constexpr (ZW) {
+                R.wr[2 * u] = bld16(rwg, ((t0 + row) * DV + dv0 + col) * 4);
+                R.wr[2 * u + 1] = bld16(rwg, ((t0 + row) * DV + dv0 + col) * 4 + 16);
+            }
         }
         if (lt < NFQ) R.fr = bld16(rw, (wb + (KDA ? WFE : kGdnWsFactors)) * 2 + lt * 16);
     };
@@ -507,7 +524,22 @@ __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const St
 #pragma unroll
         for (int u = 0; u < NPV; ++u) {
             const int idx = lt + 128 * u, row = idx / (2 * NCW), col = (idx % (2 * NCW)) * 8;
-            *reinterpret_cast<uint4*>(Vb(b) + row * L::LDV + col) = vr[u];
+            if constexpr (ZW) {  // z = w (.) v in fp32: row `row` of the fp32 tile, 8 channels
+                const uint32_t x[4] = {vr[u].x, vr[u].y, vr[u].z, vr[u].w};
+                const uint32_t wv[8] = {R.wr[2 * u].x, R.wr[2 * u].y, R.wr[2 * u].z, R.wr[2 * u].w,
+                                        R.wr[2 * u + 1].x, R.wr[2 * u + 1].y, R.wr[2 * u + 1].z, R.wr[2 * u + 1].w};
+                float z[8];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    z[2 * e] = __uint_as_float(x[e] << 16) * __uint_as_float(wv[2 * e]);
+                    z[2 * e + 1] = __uint_as_float(x[e] & 0xffff0000u) * __uint_as_float(wv[2 * e + 1]);
+                }
+                float* vf = reinterpret_cast<float*>(Vb(b)) + row * (L::LDV / 2) + col;
+                *reinterpret_cast<float4v*>(vf) = float4v{z[0], z[1], z[2], z[3]};
+                *reinterpret_cast<float4v*>(vf + 4) = float4v{z[4], z[5], z[6], z[7]};
+            } else {
+                *reinterpret_cast<uint4*>(Vb(b) + row * L::LDV + col) = vr[u];
+            }
         }
         if (lt < NFQ) reinterpret_cast<uint4*>(Fb(b))[lt] = R.fr;
     };
@@ -553,8 +585,27 @@ __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const St
         }
     };
     if (nC > 0) issue_qg(0);
+    // Per-channel modes: warm L2 ahead of the loaders.  The 8 consumer waves of a sequence (its
+    // value tiles) each touch one 8 KiB slice of chunk c+3 (the 66 KB workspace record and the
+    // V rows), one dword per 128-byte line; the result is folded into a sink a chunk later,
+    // when the load has long returned.
+    const int treg = ((vi % a.ntiles) * NCW + w) & 7;
+    uint32_t tsink = 0, tch = 0;
+    auto touch = [&](int64_t cc) {
+        if constexpr (KDA) {
+            const uint32_t line = (uint32_t)l * 128u;
+            if (treg < 6)
+                tch = __builtin_amdgcn_raw_buffer_load_b32(rw, (uint32_t)(cc * WS) * 2 + (uint32_t)treg * 8192u + line, 0, 0);
+            else
+                tch = __builtin_amdgcn_raw_buffer_load_b32(rv, (uint32_t)(cc * C) * DV * 2 + (uint32_t)(treg & 1) * 8192u + line, 0, 0);
+        }
+    };
     for (int64_t c = 0; c < nC; ++c) {
         const int bc = (int)(c & 1);
+        if constexpr (KDA) {
+            tsink ^= tch;
+            if (c + 3 < nC) touch(c + 3);
+        }
         {
             const _Float16* Kc = Kb(bc);
             const _Float16* Qc = Qb(bc);
@@ -602,11 +653,17 @@ __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const St
 #pragma unroll
             for (int ti = 0; ti < 4; ++ti) {
                 eg[ti] = KDA ? float4v{1.0f, 1.0f, 1.0f, 1.0f} : ld4f(F + L::FEG + 16 * ti + 4 * g);
-                const uint2 vb = __builtin_bit_cast(
-                    uint2, ldtr(reinterpret_cast<const _Float16*>(Vc) + (16 * ti + 4 * g + (j >> 2)) * L::LDV +
-                                16 * w + 4 * (j & 3)));
-                vv[ti] = float4v{__uint_as_float(vb.x << 16), __uint_as_float(vb.x & 0xffff0000u),
-                                 __uint_as_float(vb.y << 16), __uint_as_float(vb.y & 0xffff0000u)};
+                if constexpr (ZW) {  // fp32 tile [token][LDV / 2]
+                    const float* vf = reinterpret_cast<const float*>(Vc) + (16 * ti + 4 * g) * (L::LDV / 2) + 16 * w + j;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) vv[ti][r] = vf[r * (L::LDV / 2)];
+                } else {
+                    const uint2 vb = __builtin_bit_cast(
+                        uint2, ldtr(reinterpret_cast<const _Float16*>(Vc) + (16 * ti + 4 * g + (j >> 2)) * L::LDV +
+                                    16 * w + 4 * (j & 3)));
+                    vv[ti] = float4v{__uint_as_float(vb.x << 16), __uint_as_float(vb.x & 0xffff0000u),
+                                     __uint_as_float(vb.y << 16), __uint_as_float(vb.y & 0xffff0000u)};
+                }
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -715,6 +772,10 @@ __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const St
         }
         lds_barrier();
     }
+    if constexpr (KDA) {
+        tsink ^= tch;
+        asm volatile("" ::"v"(tsink));  // keeps the touches
+    }
     } else {
     // loaders: o of the previous chunk, the next chunk (set (c+1) mod 2) into LDS, then the
     // loads of chunk c+3 into the freed set
@@ -741,10 +802,10 @@ __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const St
     }
 }
 
-template <int DK, bool KDA, int NCW>
+template <int DK, int MODE, int NCW>
 static hipError_t launch_state_ncw(StArgs s, int64_t BH, hipStream_t st) {
     using LS = StLds<DK>;
-    auto ks = chunk_state_kernel<DK, KDA, NCW>;
+    auto ks = chunk_state_kernel<DK, MODE, NCW>;
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(ks),
@@ -759,7 +820,7 @@ static hipError_t launch_state_ncw(StArgs s, int64_t BH, hipStream_t st) {
 
 // Value tiles of 32 channels, or of 16 when 32-channel tiles would leave compute units idle
 // (one workgroup fills a compute unit's LDS).
-template <int DK, bool KDA>
+template <int DK, int MODE>
 static hipError_t launch_state(const StArgs& s, int64_t BH, hipStream_t st) {
     static int ncu = 0;
     if (ncu == 0) {
@@ -769,8 +830,8 @@ static hipError_t launch_state(const StArgs& s, int64_t BH, hipStream_t st) {
         if (e != hipSuccess) return e;
         if (ncu < 1) ncu = 1;
     }
-    if (BH * (s.dv / 32) < ncu) return launch_state_ncw<DK, KDA, 1>(s, BH, st);
-    return launch_state_ncw<DK, KDA, 2>(s, BH, st);
+    if (BH * (s.dv / 32) < ncu) return launch_state_ncw<DK, MODE, 1>(s, BH, st);
+    return launch_state_ncw<DK, MODE, 2>(s, BH, st);
 }
 
 template <int DK>
@@ -780,7 +841,7 @@ static hipError_t launch_split(const UtArgs& u, const StArgs& s, int64_t BH, hip
     if (u.nC > 0) hipLaunchKernelGGL(ku, dim3((unsigned)(BH * u.nC)), dim3(128), LU::total, st, u);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return launch_state<DK, false>(s, BH, st);
+    return launch_state<DK, kStGdn>(s, BH, st);
 }
 
 // Bytes of workspace the two-kernel path needs: 16960 per (sequence, chunk).
@@ -809,6 +870,7 @@ hipError_t chunk_split_dispatch(int64_t BH, int64_t T, int dk, int dv, const voi
     s.q = u.q;
     s.k = u.k;
     s.v = static_cast<const uint16_t*>(v);
+    s.wg = nullptr;
     s.ws = u.ws;
     s.S0 = S0;
     s.o = static_cast<uint16_t*>(o);
@@ -819,8 +881,8 @@ hipError_t chunk_split_dispatch(int64_t BH, int64_t T, int dk, int dv, const voi
 
 // State pass of the per-channel-gate two-kernel path, over a workspace the KDA UT pass has
 // filled (chunk_kda_ut_dispatch): kda_ws_stride<dk>() halfs per (sequence, chunk).
-hipError_t chunk_state_kda_dispatch(int64_t BH, int64_t T, int dk, int dv, const void* v, const float* S0, void* o,
-                                    float* Sf, const void* ws, hipStream_t st) {
+hipError_t chunk_state_kda_dispatch(int64_t BH, int64_t T, int dk, int dv, const void* v, const float* wg,
+                                    const float* S0, void* o, float* Sf, const void* ws, hipStream_t st) {
     StArgs s;
     s.T = T;
     s.nC = (T + kChunk - 1) / kChunk;
@@ -829,12 +891,17 @@ hipError_t chunk_state_kda_dispatch(int64_t BH, int64_t T, int dk, int dv, const
     s.q = nullptr;
     s.k = nullptr;
     s.v = static_cast<const uint16_t*>(v);
+    s.wg = wg;
     s.ws = static_cast<const uint16_t*>(ws);
     s.S0 = S0;
     s.o = static_cast<uint16_t*>(o);
     s.Sf = Sf;
-    if (dk == 128) return launch_state<128, true>(s, BH, st);
-    return launch_state<64, true>(s, BH, st);
+    if (wg) {
+        if (dk == 128) return launch_state<128, kStGd2>(s, BH, st);
+        return launch_state<64, kStGd2>(s, BH, st);
+    }
+    if (dk == 128) return launch_state<128, kStKda>(s, BH, st);
+    return launch_state<64, kStKda>(s, BH, st);
 }
 
 }  // namespace gdr

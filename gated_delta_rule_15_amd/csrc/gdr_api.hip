@@ -19,10 +19,10 @@ hipError_t chunk_split_dispatch(int64_t BH, int64_t T, int dk, int dv, const voi
                                 hipStream_t st);
 int64_t chunk_split_workspace_bytes(int64_t BH, int64_t T);
 hipError_t chunk_kda_ut_dispatch(int64_t BH, int64_t T, int dk, const void* q, const void* k, const float* g,
-                                 const float* beta, void* ws, hipStream_t st);
+                                 const float* beta, const float* eg, void* ws, hipStream_t st);
 int64_t chunk_kda_ws_halfs(int dk);
-hipError_t chunk_state_kda_dispatch(int64_t BH, int64_t T, int dk, int dv, const void* v, const float* S0, void* o,
-                                    float* Sf, const void* ws, hipStream_t st);
+hipError_t chunk_state_kda_dispatch(int64_t BH, int64_t T, int dk, int dv, const void* v, const float* wg,
+                                    const float* S0, void* o, float* Sf, const void* ws, hipStream_t st);
 hipError_t chunk_fwd_pc_prep_dispatch(int64_t BH, int64_t H, int64_t T, int dk, int dv, const void* q_raw,
                                       const void* k_raw, const void* v, const float* dt, const float* A_log,
                                       const float* dt_bias, const float* beta_logit, const float* S0, void* o,
@@ -207,9 +207,10 @@ gdr_status gdr_chunk_fwd_ws(int64_t B, int64_t H, int64_t T, int d_k, int d_v, i
     hipError_t e;
     if (need > 0 && gate == GDR_GATE_CHANNEL) {
         const hipStream_t st = static_cast<hipStream_t>(stream);
-        e = gdr::chunk_kda_ut_dispatch(BH, T, d_k, q, k, g, beta, workspace, st);
+        e = gdr::chunk_kda_ut_dispatch(BH, T, d_k, q, k, g, beta, nullptr, workspace, st);
         if (e == hipSuccess)
-            e = gdr::chunk_state_kda_dispatch(BH, T, d_k, d_v, v, initial_state, o, final_state, workspace, st);
+            e = gdr::chunk_state_kda_dispatch(BH, T, d_k, d_v, v, nullptr, initial_state, o, final_state, workspace,
+                                              st);
     } else if (need > 0)
         e = gdr::chunk_split_dispatch(BH, T, d_k, d_v, q, k, v, g, beta, initial_state, o, final_state, workspace,
                                       static_cast<hipStream_t>(stream));
@@ -288,9 +289,15 @@ gdr_status gdr_chunk_fwd_fused_prep(int64_t B, int64_t H, int64_t T, int d_k, in
     return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
 }
 
-gdr_status gdr_gdn2_chunk_fwd(int64_t B, int64_t H, int64_t T, int d_k, int d_v, int io_dtype, const void* q,
-                              const void* k, const void* v, const float* g, const float* b, const float* w,
-                              const float* initial_state, void* o, float* final_state, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation shared by gdr_gdn2_chunk_fwd and gdr_gdn2_chunk_fwd_ws.
+gdr_status check_gdn2(int64_t B, int64_t H, int64_t T, int d_k, int d_v, int io_dtype, const void* q, const void* k,
+                      const void* v, const float* g, const float* b, const float* w, const float* initial_state,
+                      const void* o, const float* final_state, int64_t* BHout, bool* launch) {
+    *launch = false;
     if (B < 0 || H < 0 || T < 0) return GDR_ERR_INVALID_ARG;
     gdr_status s = check_common(d_k, d_v, io_dtype, GDR_GATE_CHANNEL);
     if (s != GDR_OK) return s;
@@ -312,12 +319,69 @@ gdr_status gdr_gdn2_chunk_fwd(int64_t B, int64_t H, int64_t T, int d_k, int d_v,
     if (final_state && initial_state && final_state != initial_state &&
         overlaps(final_state, nstate, initial_state, nstate))
         return GDR_ERR_INVALID_ARG;
+    *BHout = BH;
     if (BH == 0) return GDR_OK;
     int64_t nwg;
     if (!mul_ok(BH, d_v / 32, &nwg) || nwg > kMaxGrid) return GDR_ERR_SHAPE;
-    if (!final_state && BHT == 0) return GDR_OK;
+    *launch = final_state != nullptr || BHT > 0;
+    return GDR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdr_status gdr_gdn2_chunk_fwd(int64_t B, int64_t H, int64_t T, int d_k, int d_v, int io_dtype, const void* q,
+                              const void* k, const void* v, const float* g, const float* b, const float* w,
+                              const float* initial_state, void* o, float* final_state, void* stream) {
+    int64_t BH = 0;
+    bool launch = false;
+    gdr_status s = check_gdn2(B, H, T, d_k, d_v, io_dtype, q, k, v, g, b, w, initial_state, o, final_state, &BH,
+                              &launch);
+    if (s != GDR_OK || !launch) return s;
     hipError_t e = gdr::chunk_gdn2_dispatch(BH, T, d_k, d_v, q, k, v, g, b, w, initial_state, o, final_state,
                                             static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+}
+
+int64_t gdr_gdn2_chunk_fwd_workspace_size(int64_t B, int64_t H, int64_t T, int d_k, int d_v) {
+    return gdr_chunk_fwd_workspace_size(B, H, T, d_k, d_v, GDR_BF16, GDR_GATE_CHANNEL);
+}
+
+gdr_status gdr_gdn2_chunk_fwd_ws(int64_t B, int64_t H, int64_t T, int d_k, int d_v, int io_dtype, const void* q,
+                                 const void* k, const void* v, const float* g, const float* b, const float* w,
+                                 const float* initial_state, void* o, float* final_state, void* workspace,
+                                 int64_t workspace_bytes, void* stream) {
+    int64_t BH = 0;
+    bool launch = false;
+    gdr_status s = check_gdn2(B, H, T, d_k, d_v, io_dtype, q, k, v, g, b, w, initial_state, o, final_state, &BH,
+                              &launch);
+    if (s != GDR_OK) return s;
+    if (workspace_bytes < 0) return GDR_ERR_INVALID_ARG;
+    const int64_t need = gdr_gdn2_chunk_fwd_workspace_size(B, H, T, d_k, d_v);
+    if (need < 0) return GDR_ERR_SHAPE;
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return GDR_ERR_INVALID_ARG;
+    if (need > 0) {
+        // the workspace is written by the first kernel: it may overlap no input and no output
+        const int64_t BHT = BH * T;
+        if (overlaps(workspace, need, q, BHT * d_k * 2) || overlaps(workspace, need, k, BHT * d_k * 2) ||
+            overlaps(workspace, need, v, BHT * d_v * 2) || overlaps(workspace, need, g, BHT * d_k * 4) ||
+            overlaps(workspace, need, b, BHT * d_k * 4) || overlaps(workspace, need, w, BHT * d_v * 4) ||
+            overlaps(workspace, need, o, BHT * d_v * 2) ||
+            overlaps(workspace, need, initial_state, BH * d_k * d_v * 4) ||
+            overlaps(workspace, need, final_state, BH * d_k * d_v * 4))
+            return GDR_ERR_INVALID_ARG;
+    }
+    if (!launch) return GDR_OK;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (need > 0) {
+        e = gdr::chunk_kda_ut_dispatch(BH, T, d_k, q, k, g, nullptr, b, workspace, st);
+        if (e == hipSuccess)
+            e = gdr::chunk_state_kda_dispatch(BH, T, d_k, d_v, v, w, initial_state, o, final_state, workspace, st);
+    } else {
+        e = gdr::chunk_gdn2_dispatch(BH, T, d_k, d_v, q, k, v, g, b, w, initial_state, o, final_state, st);
+    }
     return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
 }
 

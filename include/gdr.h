@@ -241,6 +241,32 @@ gdr_status gdr_gdn2_chunk_fwd(int64_t B, int64_t H, int64_t T, int d_k, int d_v,
                               void *o, float *final_state, void *stream);
 
 /*
+ * gdr_gdn2_chunk_fwd_workspace_size -- bytes of device workspace gdr_gdn2_chunk_fwd_ws needs:
+ * gdr_chunk_fwd_workspace_size(B, H, T, d_k, d_v, GDR_BF16, GDR_GATE_CHANNEL) (0 when one
+ * sequence's workspace would reach 4 GiB, -1 for sizes gdr_gdn2_chunk_fwd would reject).
+ */
+int64_t gdr_gdn2_chunk_fwd_workspace_size(int64_t B, int64_t H, int64_t T, int d_k, int d_v);
+
+/*
+ * gdr_gdn2_chunk_fwd_ws -- gdr_gdn2_chunk_fwd with a caller-provided device workspace.
+ *
+ * Same inputs, outputs and errors as gdr_gdn2_chunk_fwd, and the per-channel-gate two-kernel
+ * path of gdr_chunk_fwd_ws: the first kernel forms, for every chunk at once, T = N^{-1} with the
+ * erase gate in N's rows, A, and the decayed copies (b (.) k) e^G, q e^G, k e^{G_C - G}; the
+ * second walks the chunks in order with Z = T (z - ((b (.) k) e^G) S^T), where z = w (.) v is
+ * formed and kept in fp32.  A size query of 0 selects the single kernel.
+ *
+ *   workspace, workspace_bytes   as for gdr_chunk_fwd_ws (must not overlap any input or output)
+ */
+gdr_status gdr_gdn2_chunk_fwd_ws(int64_t B, int64_t H, int64_t T, int d_k, int d_v,
+                                 int io_dtype,
+                                 const void *q, const void *k, const void *v,
+                                 const float *g, const float *b, const float *w,
+                                 const float *initial_state,
+                                 void *o, float *final_state,
+                                 void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
  * gdr_frame_fwd -- the frame-level implicit update (tokens in unordered frames).
  *
  * The video delta-rule post (haoyizhu.site, "video-delta-rule"), section "A Different Route":

@@ -183,6 +183,39 @@ def test_gdn2_chunk_fwd_empty_batch_is_a_noop(lib):
     assert gdn2(lib, H=0, q=None, k=None, v=None, g=None, b=None, w=None, o=None) == OK
 
 
+def gdn2_ws(lib, B=1, H=1, T=64, dk=128, dv=128, io=0, q=FAKE, k=FAKE, v=FAKE, g=FAKE, b=FAKE, w=FAKE,
+            s0=None, o=FAKE2, sf=None, ws=ctypes.c_void_p(0x50000000), nbytes=1 << 20):
+    return lib.gdr_gdn2_chunk_fwd_ws(B, H, T, dk, dv, io, q, k, v, g, b, w, s0, o, sf, ws, nbytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), INVALID), (dict(dk=96), SHAPE), (dict(io=1), UNSUP), (dict(q=None), INVALID),
+    (dict(w=None), INVALID), (dict(o=FAKE), INVALID),
+    (dict(ws=None), INVALID),                                   # a workspace is required
+    (dict(nbytes=66047), INVALID),                              # one chunk needs 66048 bytes
+    (dict(nbytes=-1), INVALID),
+    (dict(ws=FAKE), INVALID),                                   # workspace overlaps q
+    (dict(ws=FAKE2), INVALID),                                  # workspace overlaps o
+    (dict(T=1 << 22, dv=256), SHAPE),
+])
+def test_gdn2_chunk_fwd_ws_rejects(lib, kw, status):
+    assert gdn2_ws(lib, **kw) == status
+
+
+def test_gdn2_workspace_size(lib):
+    n = lib.gdr_gdn2_chunk_fwd_workspace_size
+    assert n(2, 2, 100, 128, 128) == 4 * 2 * 66048
+    assert n(1, 3, 64, 64, 64) == 3 * 41216
+    assert n(1, 1, 0, 128, 128) == 0
+    assert n(-1, 1, 64, 128, 128) == -1 and n(1, 1, 64, 96, 128) == -1
+    assert n(1, 1, 64 * 65027 + 1, 128, 32) == 0                     # beyond 4 GiB a sequence: single kernel
+
+
+def test_gdn2_ws_empty_batch_is_a_noop(lib):
+    assert gdn2_ws(lib, B=0) == OK
+    assert gdn2_ws(lib, H=0, q=None, k=None, v=None, g=None, b=None, w=None, o=None, ws=None, nbytes=0) == OK
+
+
 def prep(lib, B=1, H=1, T=64, dk=128, dv=128, io=0, q=FAKE, k=FAKE, v=FAKE, dt=FAKE, A=FAKE, bias=FAKE,
          bl=FAKE, s0=None, o=FAKE2, sf=None):
     return lib.gdr_chunk_fwd_fused_prep(B, H, T, dk, dv, io, q, k, v, dt, A, bias, bl, s0, o, sf, None)

@@ -1,4 +1,5 @@
-"""GPU parity of the Gated DeltaNet-2 forward (gdr_gdn2_chunk_fwd) against the fp64 oracle.
+"""GPU parity of the Gated DeltaNet-2 forward (gdr_gdn2_chunk_fwd_ws, the two-kernel default,
+and gdr_gdn2_chunk_fwd, the single kernel) against the fp64 oracle.
 
 Every case compares element by element with ``oracle.gdn2_forward`` (the token recurrence
 of "Gated DeltaNet-2, and the gate that was doing two jobs", section 2), except the
@@ -12,7 +13,7 @@ import pytest
 
 import gdr_synth
 import oracle
-from parity import TOL_BF16, err_bf16_out, report
+from parity import TOL_BF16, err_bf16_out, err_literal, report
 
 pytestmark = pytest.mark.gpu
 
@@ -57,6 +58,9 @@ def check(name, o, S, o_ref, S_ref):
     assert eo <= TOL_BF16 and es <= TOL_BF16, msg
 
 
+PATHS = {"split": "auto", "single": None}
+
+
 def state(seed, B, H, dv, dk, std=0.05):
     return (np.random.default_rng(seed).standard_normal((B, H, dv, dk)) * std).astype(np.float32)
 
@@ -64,27 +68,30 @@ def state(seed, B, H, dv, dk, std=0.05):
 @pytest.mark.parametrize("T", [1, 37, 64, 65, 200])
 @pytest.mark.parametrize("dk,dv", [(128, 128), (128, 32), (64, 64), (128, 256), (64, 96)])
 @pytest.mark.parametrize("with_s0", [False, True])
-def test_gdn2_small(T, dk, dv, with_s0):
+@pytest.mark.parametrize("path", sorted(PATHS))
+def test_gdn2_small(T, dk, dv, with_s0, path):
     x = gdr_synth.make_inputs(variant(d_k=dk, d_v=dv), B=2, H=2, T=T)
     S0 = state(T, 2, 2, dv, dk) if with_s0 else None
-    o, S = run(x, S0)
+    o, S = run(x, S0, workspace=PATHS[path])
     o_ref, S_ref = ref(x, S0)
-    check(f"gdn2 T={T} dk={dk} dv={dv} s0={with_s0}", o, S, o_ref, S_ref)
+    check(f"gdn2 {path} T={T} dk={dk} dv={dv} s0={with_s0}", o, S, o_ref, S_ref)
 
 
 @pytest.mark.parametrize("lo,hi", [(-3.0, -0.5), (-8.0, -0.01)])
-def test_gdn2_strong_decay(lo, hi):
+@pytest.mark.parametrize("path", sorted(PATHS))
+def test_gdn2_strong_decay(lo, hi, path):
     """Per-channel decays beyond the fp16 range of the in-block factors: the diagonal tiles
     take the bf16 path, which rebuilds e = b (.) k from the inputs."""
     x = gdr_synth.make_inputs(variant(g_dist=("uniform", lo, hi)), B=1, H=2, T=200)
     x["g"][..., ::3] = x["g"][..., ::3] * 0.01
-    o, S = run(x)
+    o, S = run(x, workspace=PATHS[path])
     o_ref, S_ref = ref(x)
-    check(f"gdn2 strong decay U({lo},{hi})", o, S, o_ref, S_ref)
+    check(f"gdn2 {path} strong decay U({lo},{hi})", o, S, o_ref, S_ref)
 
 
 @pytest.mark.parametrize("case", ["no_erase", "no_write", "full_erase", "erase_up_to_2"])
-def test_gdn2_gate_extremes(case):
+@pytest.mark.parametrize("path", sorted(PATHS))
+def test_gdn2_gate_extremes(case, path):
     x = gdr_synth.make_inputs(variant(), B=1, H=2, T=150)
     if case == "no_erase":
         x["b"][:] = 0.0
@@ -95,9 +102,9 @@ def test_gdn2_gate_extremes(case):
     else:
         x["b"] = (2.0 * x["b"]).astype(np.float32)
     S0 = state(5, 1, 2, 128, 128, std=0.5)
-    o, S = run(x, S0)
+    o, S = run(x, S0, workspace=PATHS[path])
     o_ref, S_ref = ref(x, S0)
-    check(f"gdn2 {case}", o, S, o_ref, S_ref)
+    check(f"gdn2 {path} {case}", o, S, o_ref, S_ref)
 
 
 def test_gdn2_equal_gates_match_kda():
@@ -116,18 +123,19 @@ def test_gdn2_equal_gates_match_kda():
     assert err_bf16_out(host(o2), host(o1)) <= TOL_BF16
 
 
-def test_gdn2_full_size_sampled():
+@pytest.mark.parametrize("path", sorted(PATHS))
+def test_gdn2_full_size_sampled(path):
     """B=2, H=16, T=8192, d=128 bf16; 2 of the 32 sequences checked."""
     w = gdr_synth.WORKLOADS[7]
     x = gdr_synth.make_inputs(w)
-    o, S = run(x)
+    o, S = run(x, workspace=PATHS[path])
     pick = np.array([5, 26])
     bi, hi = pick // w.H, pick % w.H
     sub = {kk: x[kk][bi, hi][None] for kk in ("q", "k", "v", "g", "b", "w")}
     o_ref, S_ref = ref(sub)
     o_s = o[torch.from_numpy(bi), torch.from_numpy(hi)][None]
     S_s = S[torch.from_numpy(bi), torch.from_numpy(hi)][None]
-    check("gdn2 full size (2 sampled heads)", o_s, S_s, o_ref, S_ref)
+    check(f"gdn2 full size, {path} (2 sampled heads)", o_s, S_s, o_ref, S_ref)
 
 
 def test_gdn2_carried_state_split():
@@ -167,3 +175,34 @@ def test_gdn2_deterministic():
     o1, S1 = run(x)
     o2, S2 = run(x)
     assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+def test_gdn2_full_grid_small_T():
+    """B=4, H=16, d=128: 256 value tiles of 32 channels, the grid the state pass serves with two
+    consumer waves per workgroup; every sequence checked."""
+    x = gdr_synth.make_inputs(variant(), B=4, H=16, T=150)
+    S0 = state(11, 4, 16, 128, 128, std=0.02)
+    o, S = run(x, S0)
+    o_ref, S_ref = ref(x, S0)
+    check("gdn2 full grid, T=150", o, S, o_ref, S_ref)
+
+
+def test_gdn2_split_equals_single_closely():
+    """The two-kernel path (T formed densely) and the single kernel (blockwise substitution)
+    agree within the outputs' bf16 rounding."""
+    x = gdr_synth.make_inputs(variant(), B=1, H=3, T=777)
+    o1, S1 = run(x, workspace="auto")
+    o2, S2 = run(x, workspace=None)
+    assert err_bf16_out(host(o1), host(o2)) <= TOL_BF16
+    assert err_literal(host(S1), host(S2)) <= TOL_BF16
+
+
+def test_gdn2_explicit_workspace_reused():
+    """A caller-owned workspace reused across calls of different sizes."""
+    need = gdr.gdn2_chunk_fwd_workspace_size(1, 2, 300, 128, 128)
+    wsb = torch.empty(need, dtype=torch.uint8, device=DEV)
+    for T in (300, 65, 129):
+        x = gdr_synth.make_inputs(variant(), B=1, H=2, T=T)
+        o, S = run(x, workspace=wsb)
+        o_ref, S_ref = ref(x)
+        check(f"gdn2 reused workspace T={T}", o, S, o_ref, S_ref)
