@@ -166,7 +166,12 @@ def bench_gdp(torch, gdr, gdr_synth, steps=10):
     bytes: q, g and o per token, k, v and beta per substep, the final state."""
     w = gdr_synth.WORKLOADS[6]
     sets = make_chunk_sets(torch, gdr_synth, w, nsets=2)
-    ms, med, _, o, S = time_chunk(torch, gdr, sets, steps, 2, fn=gdr.gdp_chunk_fwd)
+    wsb = torch.empty(max(gdr.gdp_chunk_fwd_workspace_size(w.B, w.H, w.T, w.nh, w.d_k, w.d_v), 1),
+                      dtype=torch.uint8, device="cuda")
+    ms_single, _, _, _, _ = time_chunk(torch, gdr, sets, steps, 2,
+                                       fn=lambda *a_, **kw: gdr.gdp_chunk_fwd(*a_, workspace=None, **kw))
+    ms, med, _, o, S = time_chunk(torch, gdr, sets, steps, 2,
+                                  fn=lambda *a_, **kw: gdr.gdp_chunk_fwd(*a_, workspace=wsb, **kw))
     Tv = w.T * w.nh
     flops = chunk_flops(w.B, w.H, Tv, w.d_k, w.d_v)
     nbytes = (w.B * w.H * (w.T * (2 * w.d_k + 2 * w.d_v + 4) + Tv * (2 * w.d_k + 2 * w.d_v + 4))
@@ -179,8 +184,9 @@ def bench_gdp(torch, gdr, gdr_synth, steps=10):
     qt, kt, vt, gt, bt, keep = oracle.gdp_as_virtual_gdn(sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"])
     o_ref, S_ref = oracle.recurrent_forward(qt, kt, vt, gt, bt)
     res = {"workload": "gdp_bf16: Gated Delta Product B=4 H=16 T=2048 n_h=2 d_k=d_v=128 bf16, zero S0",
-           "kernel": "chunk_fwd_pc_kernel<128, 1>", "ms_per_call": round(ms, 4),
+           "kernel": "chunk_ut_kernel<128, true> + chunk_state_kernel<128, 3, 2>", "ms_per_call": round(ms, 4),
            "ms_per_call_median": round(med, 4),
+           "single_kernel": {"kernel": "chunk_fwd_pc_kernel<128, 1>", "ms_per_call": round(ms_single, 4)},
            "tokens_per_s": round(w.B * w.T / (ms * 1e-3), 1),
            "substeps_per_s": round(w.B * Tv / (ms * 1e-3), 1),
            "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_MFMA_F16, 4),

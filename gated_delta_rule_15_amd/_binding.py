@@ -20,7 +20,7 @@ GDR_GATE_SCALAR, GDR_GATE_CHANNEL = 0, 1
 
 # every entry point include/gdr.h declares
 EXPORTED_SYMBOLS = ("gdr_version", "gdr_status_string", "gdr_chunk_fwd", "gdr_chunk_fwd_workspace_size",
-                    "gdr_chunk_fwd_ws", "gdr_chunk_fwd_fused_prep", "gdr_gdp_chunk_fwd", "gdr_gdn2_chunk_fwd",
+                    "gdr_chunk_fwd_ws", "gdr_chunk_fwd_fused_prep", "gdr_gdp_chunk_fwd", "gdr_gdp_chunk_fwd_workspace_size", "gdr_gdp_chunk_fwd_ws", "gdr_gdn2_chunk_fwd",
                     "gdr_gdn2_chunk_fwd_workspace_size", "gdr_gdn2_chunk_fwd_ws", "gdr_frame_fwd_workspace_size", "gdr_frame_fwd", "gdr_decode_step")
 
 _lock = threading.Lock()
@@ -57,6 +57,10 @@ def load_library():
         lib.gdr_chunk_fwd_fused_prep.argtypes = [i64, i64, i64, i32, i32, i32, P, P, P, P, P, P, P, P, P, P, P]
         lib.gdr_gdp_chunk_fwd.restype = i32
         lib.gdr_gdp_chunk_fwd.argtypes = [i64, i64, i64, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P]
+        lib.gdr_gdp_chunk_fwd_workspace_size.restype = i64
+        lib.gdr_gdp_chunk_fwd_workspace_size.argtypes = [i64, i64, i64, i32, i32, i32]
+        lib.gdr_gdp_chunk_fwd_ws.restype = i32
+        lib.gdr_gdp_chunk_fwd_ws.argtypes = [i64, i64, i64, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, i64, P]
         lib.gdr_gdn2_chunk_fwd.restype = i32
         lib.gdr_gdn2_chunk_fwd.argtypes = [i64, i64, i64, i32, i32, i32, P, P, P, P, P, P, P, P, P, P]
         lib.gdr_gdn2_chunk_fwd_workspace_size.restype = i64
@@ -219,12 +223,21 @@ def chunk_fwd_fused_prep(q_raw, k_raw, v, dt, A_log, dt_bias, beta_logit, initia
     return o, final_state
 
 
+def gdp_chunk_fwd_workspace_size(B, H, T, n_h, d_k, d_v) -> int:
+    n = int(load_library().gdr_gdp_chunk_fwd_workspace_size(B, H, T, n_h, d_k, d_v))
+    if n < 0:
+        raise GdrError(GDR_ERR_SHAPE, "gdr_gdp_chunk_fwd_workspace_size")
+    return n
+
+
 def gdp_chunk_fwd(q, k, v, g, beta, initial_state=None, *, output_final_state=True, out=None,
-                  final_state=None, stream=None):
-    """gdr_gdp_chunk_fwd (Gated Delta Product) on torch tensors.
+                  final_state=None, stream=None, workspace="auto"):
+    """Gated Delta Product (gdr_gdp_chunk_fwd_ws, or gdr_gdp_chunk_fwd) on torch tensors.
 
     q [B,H,T,d_k]; k [B,H,T,n_h,d_k]; v [B,H,T,n_h,d_v] (bf16); g [B,H,T] fp32 (one
     log-decay per token); beta [B,H,T,n_h] fp32; initial_state [B,H,d_v,d_k] fp32 or None.
+    workspace: "auto" (default) allocates the two-kernel path's workspace with torch; a uint8
+    CUDA tensor is used as that workspace; None calls the single kernel.
     Returns (o [B,H,T,d_v], final_state); final_state is None when output_final_state is False.
     """
     import torch
@@ -250,11 +263,26 @@ def gdp_chunk_fwd(q, k, v, g, beta, initial_state=None, *, output_final_state=Tr
         final_state = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
     if final_state is not None:
         _check(final_state, "final_state", (B, H, dv, dk), torch.float32, dev)
-    st = load_library().gdr_gdp_chunk_fwd(B, H, T, nh, dk, dv, io, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
-                                          _ptr(beta), _ptr(initial_state), _ptr(o), _ptr(final_state),
-                                          _stream(stream, dev))
+    if workspace is None:
+        st = load_library().gdr_gdp_chunk_fwd(B, H, T, nh, dk, dv, io, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                              _ptr(beta), _ptr(initial_state), _ptr(o), _ptr(final_state),
+                                              _stream(stream, dev))
+        if st != GDR_OK:
+            raise GdrError(st, "gdr_gdp_chunk_fwd")
+        return o, final_state
+    need = gdp_chunk_fwd_workspace_size(B, H, T, nh, dk, dv)
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError(f"workspace: expected 'auto', None or a tensor, got {workspace!r}")
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace: must be a contiguous tensor on the inputs' device")
+    nbytes = workspace.numel() * workspace.element_size()
+    st = load_library().gdr_gdp_chunk_fwd_ws(B, H, T, nh, dk, dv, io, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                             _ptr(beta), _ptr(initial_state), _ptr(o), _ptr(final_state),
+                                             _ptr(workspace), nbytes, _stream(stream, dev))
     if st != GDR_OK:
-        raise GdrError(st, "gdr_gdp_chunk_fwd")
+        raise GdrError(st, "gdr_gdp_chunk_fwd_ws")
     return o, final_state
 
 

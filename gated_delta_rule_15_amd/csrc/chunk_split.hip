@@ -57,7 +57,10 @@ constexpr int kGdnWsNF = 144;                               // its floats
 constexpr int kGdnWsStride = kGdnWsFactors + 2 * kGdnWsNF;  // 8480 halfs = 16960 bytes
 
 struct UtArgs {
-    int64_t T;
+    int64_t T;          // steps per sequence (T_real n_h virtual steps for the VIRT kernels)
+    int64_t Treal;      // rows of q and g per sequence (= T unless VIRT)
+    uint32_t nh;        // substeps per token (VIRT)
+    uint32_t nh_magic;  // ceil(2^32 / nh): m / nh = umulhi(m, nh_magic) for m < 2^23
     int64_t nC;
     const uint16_t* q;
     const uint16_t* k;
@@ -87,7 +90,10 @@ struct UtLds {
     static_assert((oSm | oNd | oXd | oAt | oTt) % 16 == 0, "alignment");
 };
 
-template <int DK>
+// VIRT: Gated Delta Product over its virtual steps ("Linear Attention, Visualized", "GDP as GDN
+// over a virtual sequence"): step m = n_h t + j reads q_t only when j = n_h - 1 and g_t only
+// when j = 0; other steps read past the end of the real-token buffer, which returns zero.
+template <int DK, bool VIRT>
 __global__ __launch_bounds__(128) void chunk_ut_kernel(const UtArgs a) {
     using L = UtLds<DK>;
     using S = UtTab;
@@ -107,11 +113,13 @@ __global__ __launch_bounds__(128) void chunk_ut_kernel(const UtArgs a) {
     const int64_t bh = blockIdx.x / a.nC;
     const int64_t c = blockIdx.x - bh * a.nC;
     const int64_t T = a.T;
+    const int64_t Tr = VIRT ? a.Treal : T;
     const uint32_t t0 = (uint32_t)(c * C);
-    const auto rq = make_rsrc(a.q + bh * T * DK, (uint32_t)(T * DK * 2));
+    const auto rq = make_rsrc(a.q + bh * Tr * DK, (uint32_t)(Tr * DK * 2));
     const auto rk = make_rsrc(a.k + bh * T * DK, (uint32_t)(T * DK * 2));
-    const auto rg = make_rsrc(a.g + bh * T, (uint32_t)(T * 4));
+    const auto rg = make_rsrc(a.g + bh * Tr, (uint32_t)(Tr * 4));
     const auto rb = make_rsrc(a.beta + bh * T, (uint32_t)(T * 4));
+    auto vtok = [&](uint32_t m) { return __umulhi(m, a.nh_magic); };
 
     // ---- K and Q of the chunk into LDS (fp16, natural channel order); past the sequence end
     // the loads return zeros, i.e. identity tokens
@@ -122,12 +130,22 @@ __global__ __launch_bounds__(128) void chunk_ut_kernel(const UtArgs a) {
         for (int u = 0; u < NP; ++u) {
             const int idx = tid + 128 * u, row = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
             const uint32_t off = ((t0 + row) * DK + col) * 2;
+            uint32_t offq = off;
+            if constexpr (VIRT) {
+                const uint32_t m = t0 + row, tr = vtok(m);
+                offq = m - tr * a.nh == a.nh - 1 ? (tr * DK + col) * 2 : (uint32_t)(Tr * DK * 2);
+            }
             kr[u] = bld16(rk, off);
-            qr[u] = bld16(rq, off);
+            qr[u] = bld16(rq, offq);
         }
         float gl = 0.0f, bt = 0.0f;
         if (w == 0) {
-            gl = bld4(rg, (t0 + l) * 4);
+            uint32_t offg = (t0 + l) * 4;
+            if constexpr (VIRT) {
+                const uint32_t m = t0 + l, tr = vtok(m);
+                offg = m - tr * a.nh == 0 ? tr * 4 : (uint32_t)(Tr * 4);
+            }
+            gl = bld4(rg, offg);
             bt = bld4(rb, (t0 + l) * 4);
         }
 #pragma unroll
@@ -345,7 +363,10 @@ __global__ __launch_bounds__(128) void chunk_ut_kernel(const UtArgs a) {
 // ============================================================================ state pass
 
 struct StArgs {
-    int64_t T;
+    int64_t T;          // steps per sequence (virtual steps for the GDP mode)
+    int64_t Treal;      // rows of q and o per sequence (= T unless GDP)
+    uint32_t nh;        // GDP: substeps per token
+    uint32_t nh_magic;  // GDP: ceil(2^32 / nh)
     int64_t nC;
     int dv;
     int ntiles;  // d_v / (16 NCW)
@@ -385,16 +406,18 @@ struct StLds {
     static_assert((oQ | oA | oT | oV | oF | oOt) % 16 == 0, "alignment");
 };
 
-// Modes of the state pass: the scalar gate, the per-channel gate (KDA), and Gated DeltaNet-2
-// (the KDA pass with z = w (.) v in place of v).
-constexpr int kStGdn = 0, kStKda = 1, kStGd2 = 2;
+// Modes of the state pass: the scalar gate, the per-channel gate (KDA), Gated DeltaNet-2
+// (the KDA pass with z = w (.) v in place of v), and the Gated Delta Product (the scalar-gate
+// pass over virtual steps: q read and o written on the last substep of a token only).
+constexpr int kStGdn = 0, kStKda = 1, kStGd2 = 2, kStGdp = 3;
 
 // NCW consumer waves of 16 value channels each (a value tile of 16 NCW channels) and two loader
 // waves.  NCW = 1 doubles the workgroups of a grid that would leave compute units idle.
 template <int DK, int MODE, int NCW>
 __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const StArgs a) {
-    constexpr bool KDA = MODE != kStGdn;  // the UT pass wrote the decayed copies
-    constexpr bool ZW = MODE == kStGd2;   // V tile holds z = w (.) v in fp32
+    constexpr bool KDA = MODE == kStKda || MODE == kStGd2;  // the UT pass wrote the decayed copies
+    constexpr bool ZW = MODE == kStGd2;                     // V tile holds z = w (.) v in fp32
+    constexpr bool VIRT = MODE == kStGdp;                   // GDP virtual steps
     using L = StLds<DK>;
     constexpr int C = kChunk;
     constexpr int NKB = DK / 32;
@@ -419,7 +442,8 @@ __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const St
     const int64_t T = a.T, nC = a.nC;
     const int DV = a.dv;
     // (the per-channel gate reads no q or k: those resources are empty)
-    const auto rq = make_rsrc(KDA ? nullptr : a.q + bh * T * DK, KDA ? 0u : (uint32_t)(T * DK * 2));
+    const int64_t Tr = VIRT ? a.Treal : T;  // rows of q and o
+    const auto rq = make_rsrc(KDA ? nullptr : a.q + bh * Tr * DK, KDA ? 0u : (uint32_t)(Tr * DK * 2));
     const auto rk = make_rsrc(KDA ? nullptr : a.k + bh * T * DK, KDA ? 0u : (uint32_t)(T * DK * 2));
     const auto rv = make_rsrc(a.v + bh * T * DV, (uint32_t)(T * DV * 2));
     const auto rwg = make_rsrc(ZW ? a.wg + bh * T * DV : nullptr, ZW ? (uint32_t)(T * DV * 4) : 0u);
@@ -427,7 +451,8 @@ __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const St
     // offsets (halfs) inside a chunk's workspace record of the per-channel gate
     constexpr int WKG = 2 * C * C, WQG = WKG + C * DK, WKC = WQG + C * DK, WFE = WKC + C * DK;
     const auto rw = make_rsrc(a.ws + bh * nC * WS, (uint32_t)(nC * WS * 2));
-    const auto ro = make_rsrc(a.o + bh * T * DV, (uint32_t)(T * DV * 2));
+    const auto ro = make_rsrc(a.o + bh * Tr * DV, (uint32_t)(Tr * DV * 2));
+    auto vtok = [&](uint32_t m) { return __umulhi(m, a.nh_magic); };
 
     auto trfrag = [&](const _Float16* base, int ld, int kb, int col) {
         const _Float16* p0 = base + (32 * kb + 4 * g + (j >> 2)) * ld + col;
@@ -460,8 +485,13 @@ __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const St
                 qr[u] = bld16(rw, (wb + WKC + idx * 8) * 2);
             } else {
                 const uint32_t off = ((t0 + row) * DK + col) * 2;
+                uint32_t offq = off;
+                if constexpr (VIRT) {  // q_t on the last substep of token t, zero elsewhere
+                    const uint32_t m = t0 + row, tr = vtok(m);
+                    offq = m - tr * a.nh == a.nh - 1 ? (tr * DK + col) * 2 : (uint32_t)(Tr * DK * 2);
+                }
                 kr[u] = bld16(rk, off);
-                qr[u] = bld16(rq, off);
+                qr[u] = bld16(rq, offq);
             }
         }
 #pragma unroll
@@ -493,7 +523,12 @@ __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const St
             const _Float16* rp = Ot + (d + (j >> 2)) * L::LDO + tb + 4 * (j & 3);
             const uint2 lo = __builtin_bit_cast(uint2, ldtr(rp));
             const uint2 hi = __builtin_bit_cast(uint2, ldtr(rp + 4 * L::LDO));
-            bst16(ro, ((uint32_t)(c * C + tb + j) * DV + dv0 + d) * 2, uint4{lo.x, lo.y, hi.x, hi.y});
+            uint32_t offo = ((uint32_t)(c * C + tb + j) * DV + dv0 + d) * 2;
+            if constexpr (VIRT) {  // only the last substep of a token has an output
+                const uint32_t m = (uint32_t)(c * C + tb + j), tr = vtok(m);
+                offo = m - tr * a.nh == a.nh - 1 ? (tr * DV + dv0 + d) * 2 : (uint32_t)(Tr * DV * 2);
+            }
+            bst16(ro, offo, uint4{lo.x, lo.y, hi.x, hi.y});
         }
     };
     // K and Q to fp16 in the registers (while the consumers' first products read LDS)
@@ -834,14 +869,14 @@ static hipError_t launch_state(const StArgs& s, int64_t BH, hipStream_t st) {
     return launch_state_ncw<DK, MODE, 2>(s, BH, st);
 }
 
-template <int DK>
+template <int DK, bool VIRT>
 static hipError_t launch_split(const UtArgs& u, const StArgs& s, int64_t BH, hipStream_t st) {
     using LU = UtLds<DK>;
-    auto ku = chunk_ut_kernel<DK>;
+    auto ku = chunk_ut_kernel<DK, VIRT>;
     if (u.nC > 0) hipLaunchKernelGGL(ku, dim3((unsigned)(BH * u.nC)), dim3(128), LU::total, st, u);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return launch_state<DK, kStGdn>(s, BH, st);
+    return launch_state<DK, VIRT ? kStGdp : kStGdn>(s, BH, st);
 }
 
 // Bytes of workspace the two-kernel path needs: 16960 per (sequence, chunk).
@@ -850,12 +885,19 @@ int64_t chunk_split_workspace_bytes(int64_t BH, int64_t T) {
     return BH * nC * kGdnWsStride * 2;
 }
 
-hipError_t chunk_split_dispatch(int64_t BH, int64_t T, int dk, int dv, const void* q, const void* k, const void* v,
-                                const float* g, const float* beta, const float* S0, void* o, float* Sf, void* ws,
-                                hipStream_t st) {
-    const int64_t nC = (T + kChunk - 1) / kChunk;
+// T counts real tokens; nh > 1 runs a Gated Delta Product over the T nh virtual steps (k, v,
+// beta hold T nh rows per sequence; q, g, o hold T).  The workspace covers the virtual steps.
+hipError_t chunk_split_dispatch(int64_t BH, int64_t T, int nh, int dk, int dv, const void* q, const void* k,
+                                const void* v, const float* g, const float* beta, const float* S0, void* o, float* Sf,
+                                void* ws, hipStream_t st) {
+    const int64_t Tv = T * nh;
+    const int64_t nC = (Tv + kChunk - 1) / kChunk;
+    const uint32_t magic = nh > 1 ? (uint32_t)(((uint64_t(1) << 32) + nh - 1) / nh) : 0u;
     UtArgs u;
-    u.T = T;
+    u.T = Tv;
+    u.Treal = T;
+    u.nh = (uint32_t)nh;
+    u.nh_magic = magic;
     u.nC = nC;
     u.q = static_cast<const uint16_t*>(q);
     u.k = static_cast<const uint16_t*>(k);
@@ -863,7 +905,10 @@ hipError_t chunk_split_dispatch(int64_t BH, int64_t T, int dk, int dv, const voi
     u.beta = beta;
     u.ws = static_cast<uint16_t*>(ws);
     StArgs s;
-    s.T = T;
+    s.T = Tv;
+    s.Treal = T;
+    s.nh = (uint32_t)nh;
+    s.nh_magic = magic;
     s.nC = nC;
     s.dv = dv;
     s.ntiles = dv / 32;
@@ -875,8 +920,12 @@ hipError_t chunk_split_dispatch(int64_t BH, int64_t T, int dk, int dv, const voi
     s.S0 = S0;
     s.o = static_cast<uint16_t*>(o);
     s.Sf = Sf;
-    if (dk == 128) return launch_split<128>(u, s, BH, st);
-    return launch_split<64>(u, s, BH, st);
+    if (nh > 1) {
+        if (dk == 128) return launch_split<128, true>(u, s, BH, st);
+        return launch_split<64, true>(u, s, BH, st);
+    }
+    if (dk == 128) return launch_split<128, false>(u, s, BH, st);
+    return launch_split<64, false>(u, s, BH, st);
 }
 
 // State pass of the per-channel-gate two-kernel path, over a workspace the KDA UT pass has
@@ -885,6 +934,9 @@ hipError_t chunk_state_kda_dispatch(int64_t BH, int64_t T, int dk, int dv, const
                                     const float* S0, void* o, float* Sf, const void* ws, hipStream_t st) {
     StArgs s;
     s.T = T;
+    s.Treal = T;
+    s.nh = 1;
+    s.nh_magic = 0u;
     s.nC = (T + kChunk - 1) / kChunk;
     s.dv = dv;
     s.ntiles = dv / 32;

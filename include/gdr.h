@@ -208,6 +208,30 @@ gdr_status gdr_gdp_chunk_fwd(int64_t B, int64_t H, int64_t T, int n_h, int d_k, 
                              void *o, float *final_state, void *stream);
 
 /*
+ * gdr_gdp_chunk_fwd_workspace_size -- bytes of device workspace gdr_gdp_chunk_fwd_ws needs:
+ * the scalar gate's 16960 bytes per sequence and 64 virtual steps,
+ * B*H*ceil(T*n_h/64)*16960; -1 for sizes gdr_gdp_chunk_fwd would reject.
+ */
+int64_t gdr_gdp_chunk_fwd_workspace_size(int64_t B, int64_t H, int64_t T, int n_h, int d_k, int d_v);
+
+/*
+ * gdr_gdp_chunk_fwd_ws -- gdr_gdp_chunk_fwd with a caller-provided device workspace.
+ *
+ * Same inputs, outputs and errors as gdr_gdp_chunk_fwd.  Runs the two-kernel path of
+ * gdr_chunk_fwd_ws over the T * n_h virtual steps: the UT kernel reads q_t on the last
+ * substep of a token and g_t on its first, the state kernel writes o_t on the last substep.
+ *
+ *   workspace, workspace_bytes   as for gdr_chunk_fwd_ws (must not overlap any input or output)
+ */
+gdr_status gdr_gdp_chunk_fwd_ws(int64_t B, int64_t H, int64_t T, int n_h, int d_k, int d_v,
+                                int io_dtype,
+                                const void *q, const void *k, const void *v,
+                                const float *g, const float *beta,
+                                const float *initial_state,
+                                void *o, float *final_state,
+                                void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
  * gdr_gdn2_chunk_fwd -- chunkwise forward pass of Gated DeltaNet-2.
  *
  * "Gated DeltaNet-2, and the gate that was doing two jobs" (aigenapps.com), section 2: the

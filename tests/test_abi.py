@@ -154,6 +154,37 @@ def test_gdp_chunk_fwd_empty_batch_is_a_noop(lib):
     assert gdp(lib, H=0, q=None, k=None, v=None, g=None, beta=None, o=None) == OK
 
 
+def gdp_ws(lib, B=1, H=1, T=64, nh=2, dk=128, dv=128, io=0, q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE,
+           s0=None, o=FAKE2, sf=None, ws=ctypes.c_void_p(0x50000000), nbytes=1 << 20):
+    return lib.gdr_gdp_chunk_fwd_ws(B, H, T, nh, dk, dv, io, q, k, v, g, beta, s0, o, sf, ws, nbytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), INVALID), (dict(nh=0), INVALID), (dict(nh=17), SHAPE), (dict(dk=96), SHAPE),
+    (dict(io=1), UNSUP), (dict(q=None), INVALID), (dict(o=FAKE), INVALID),
+    (dict(ws=None), INVALID),                                   # a workspace is required
+    (dict(nbytes=2 * 16960 - 1), INVALID),                      # 128 virtual steps: two records
+    (dict(nbytes=-1), INVALID),
+    (dict(ws=FAKE), INVALID), (dict(ws=FAKE2), INVALID),        # workspace overlaps q / o
+    (dict(T=1 << 21, nh=3), SHAPE),                             # T n_h beyond 2^22
+])
+def test_gdp_chunk_fwd_ws_rejects(lib, kw, status):
+    assert gdp_ws(lib, **kw) == status
+
+
+def test_gdp_workspace_size(lib):
+    n = lib.gdr_gdp_chunk_fwd_workspace_size
+    assert n(4, 16, 2048, 2, 128, 128) == 64 * 64 * 16960
+    assert n(1, 1, 33, 2, 64, 64) == 2 * 16960                      # 66 virtual steps: two chunks
+    assert n(1, 1, 0, 2, 128, 128) == 0
+    assert n(1, 1, 64, 0, 128, 128) == -1 and n(1, 1, 64, 17, 128, 128) == -1
+
+
+def test_gdp_ws_empty_batch_is_a_noop(lib):
+    assert gdp_ws(lib, B=0) == OK
+    assert gdp_ws(lib, H=0, q=None, k=None, v=None, g=None, beta=None, o=None, ws=None, nbytes=0) == OK
+
+
 def test_gdp_partial_state_overlap_rejected(lib):
     s = ctypes.c_void_p(0x30000000)
     assert gdp(lib, s0=s, sf=ctypes.c_void_p(0x30000000 + 4)) == INVALID

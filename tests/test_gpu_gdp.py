@@ -55,6 +55,9 @@ def check(name, o, S, o_ref, S_ref):
     assert eo <= TOL_BF16 and es <= TOL_BF16, msg
 
 
+PATHS = {"split": "auto", "single": None}
+
+
 def state(seed, B, H, dv, dk, std=0.05):
     return (np.random.default_rng(seed).standard_normal((B, H, dv, dk)) * std).astype(np.float32)
 
@@ -63,56 +66,62 @@ def state(seed, B, H, dv, dk, std=0.05):
 @pytest.mark.parametrize("nh", [2, 3, 4])
 @pytest.mark.parametrize("dk,dv", [(128, 128), (64, 96)])
 @pytest.mark.parametrize("with_s0", [False, True])
-def test_gdp_small(T, nh, dk, dv, with_s0):
+@pytest.mark.parametrize("path", sorted(PATHS))
+def test_gdp_small(T, nh, dk, dv, with_s0, path):
     w = variant(nh=nh, d_k=dk, d_v=dv)
     x = gdr_synth.make_inputs(w, B=2, H=2, T=T)
     S0 = state(T + nh, 2, 2, dv, dk) if with_s0 else None
-    o, S = run_gdp(x, S0)
+    o, S = run_gdp(x, S0, workspace=PATHS[path])
     o_ref, S_ref = oracle.gdp_forward(x["q"], x["k"], x["v"], x["g"], x["beta"], S0)
-    check(f"gdp T={T} nh={nh} dk={dk} dv={dv} s0={with_s0}", o, S, o_ref, S_ref)
+    check(f"gdp {path} T={T} nh={nh} dk={dk} dv={dv} s0={with_s0}", o, S, o_ref, S_ref)
 
 
 @pytest.mark.parametrize("nh,T", [(5, 30), (16, 9), (7, 64)])
-def test_gdp_many_substeps(nh, T):
+@pytest.mark.parametrize("path", sorted(PATHS))
+def test_gdp_many_substeps(nh, T, path):
     w = variant(nh=nh)
     x = gdr_synth.make_inputs(w, B=1, H=2, T=T)
     S0 = state(nh, 1, 2, 128, 128)
-    o, S = run_gdp(x, S0)
+    o, S = run_gdp(x, S0, workspace=PATHS[path])
     o_ref, S_ref = oracle.gdp_forward(x["q"], x["k"], x["v"], x["g"], x["beta"], S0)
-    check(f"gdp nh={nh} T={T}", o, S, o_ref, S_ref)
+    check(f"gdp {path} nh={nh} T={T}", o, S, o_ref, S_ref)
 
 
-def test_gdp_equals_chunk_fwd_on_the_virtual_sequence():
-    """The GDP kernel reads q, g and writes o through the substep mapping; fed the expanded
-    virtual sequence, the single-kernel chunked forward (the same kernel body) must give the
-    same bits."""
+@pytest.mark.parametrize("path", sorted(PATHS))
+def test_gdp_equals_chunk_fwd_on_the_virtual_sequence(path):
+    """The GDP kernels read q, g and write o through the substep mapping; fed the expanded
+    virtual sequence, the chunked forward on the same path (the same kernel bodies) must give
+    the same bits."""
     w = variant(nh=3)
     x = gdr_synth.make_inputs(w, B=2, H=3, T=150)
     S0 = state(3, 2, 3, 128, 128)
-    o, S = run_gdp(x, S0)
+    o, S = run_gdp(x, S0, workspace=PATHS[path])
     qt, kt, vt, gt, bt, keep = oracle.gdp_as_virtual_gdn(x["q"], x["k"], x["v"], x["g"], x["beta"])
-    ov, Sv = gdr.chunk_fwd(dev(qt, True), dev(kt, True), dev(vt, True), dev(gt), dev(bt), dev(S0), workspace=None)
+    ov, Sv = gdr.chunk_fwd(dev(qt, True), dev(kt, True), dev(vt, True), dev(gt), dev(bt), dev(S0),
+                           workspace=PATHS[path])
     torch.cuda.synchronize()
     assert torch.equal(o, ov[:, :, torch.from_numpy(keep).to(DEV)])
     assert torch.equal(S, Sv)
 
 
-def test_gdp_one_substep_is_chunk_fwd():
+@pytest.mark.parametrize("path", sorted(PATHS))
+def test_gdp_one_substep_is_chunk_fwd(path):
     w = variant(nh=1)
     x = gdr_synth.make_inputs(w, B=1, H=4, T=200)
     o, S = gdr.gdp_chunk_fwd(dev(x["q"], True), dev(x["k"][:, :, :, None], True), dev(x["v"][:, :, :, None], True),
-                             dev(x["g"]), dev(x["beta"][:, :, :, None]))
+                             dev(x["g"]), dev(x["beta"][:, :, :, None]), workspace=PATHS[path])
     o2, S2 = gdr.chunk_fwd(dev(x["q"], True), dev(x["k"], True), dev(x["v"], True), dev(x["g"]), dev(x["beta"]),
-                           workspace=None)
+                           workspace=PATHS[path])
     torch.cuda.synchronize()
     assert torch.equal(o, o2) and torch.equal(S, S2)
 
 
-def test_gdp_full_size_sampled():
+@pytest.mark.parametrize("path", sorted(PATHS))
+def test_gdp_full_size_sampled(path):
     """B=4, H=16, T=2048, n_h=2, d=128 bf16 (4096 substeps per sequence); 6 of 64 sequences."""
     w = gdr_synth.WORKLOADS[6]
     x = gdr_synth.make_inputs(w)
-    o, S = run_gdp(x)
+    o, S = run_gdp(x, workspace=PATHS[path])
     rng = np.random.default_rng(6)
     pick = np.sort(rng.choice(w.B * w.H, size=6, replace=False))
     bi, hi = pick // w.H, pick % w.H
@@ -121,7 +130,7 @@ def test_gdp_full_size_sampled():
     o_ref, S_ref = oracle.recurrent_forward(qt, kt, vt, gt, bt)
     o_s = o[torch.from_numpy(bi), torch.from_numpy(hi)][None]
     S_s = S[torch.from_numpy(bi), torch.from_numpy(hi)][None]
-    check("gdp full size (6 sampled heads)", o_s, S_s, o_ref[:, :, keep], S_ref)
+    check(f"gdp full size, {path} (6 sampled heads)", o_s, S_s, o_ref[:, :, keep], S_ref)
 
 
 def test_gdp_carried_state_split():
@@ -152,3 +161,14 @@ def test_gdp_deterministic():
     o1, S1 = run_gdp(x)
     o2, S2 = run_gdp(x)
     assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+def test_gdp_explicit_workspace_reused():
+    """A caller-owned workspace reused across calls of different sizes."""
+    need = gdr.gdp_chunk_fwd_workspace_size(1, 2, 120, 3, 128, 128)
+    wsb = torch.empty(need, dtype=torch.uint8, device=DEV)
+    for T, nh in ((120, 3), (43, 2), (9, 16)):
+        x = gdr_synth.make_inputs(variant(nh=nh), B=1, H=2, T=T)
+        o, S = run_gdp(x, workspace=wsb)
+        o_ref, S_ref = oracle.gdp_forward(x["q"], x["k"], x["v"], x["g"], x["beta"])
+        check(f"gdp reused workspace T={T} nh={nh}", o, S, o_ref, S_ref)
