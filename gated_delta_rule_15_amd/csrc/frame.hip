@@ -103,33 +103,59 @@ __global__ __launch_bounds__(256, 1) void frame_gram_kernel(const FrArgs a) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) accC[s][t] = zero4();
 
-    // ---- G and C over the frame's tokens, 64 at a time
-    for (int64_t t0 = t_beg; t0 < t_end; t0 += 64) {
-        // stage sqrt(gamma) k and sqrt(gamma) v (fp16); tokens outside the frame are zeros
-        constexpr int PK = 64 * DK / 8, PV = 64 * DV / 8;
-        for (int idx = tid; idx < PK + PV; idx += 256) {
-            const bool isk = idx < PK;
-            const int id2 = isk ? idx : idx - PK;
-            const int D = isk ? DK : DV;
-            const int row = id2 / (D / 8), col = (id2 % (D / 8)) * 8;
-            const int64_t tok = t0 + row;
-            uint4 u = uint4{0u, 0u, 0u, 0u};
-            float sg = 0.0f;
-            if (tok < t_end) {
-                u = isk ? bld16(rk, (uint32_t)((tok * DK + col) * 2)) : bld16(rv, (uint32_t)((tok * DV + col) * 2));
-                sg = sqrtf(bld4(rgm, (uint32_t)(tok * 4)));
-            }
-            const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
-            half8 h;
+    // ---- G and C over the frame's tokens, 64 at a time.  Thread tid stages the 16-byte pieces
+    // (row, col) with row = tid / R + (256 / R) i of K (R = DK / 8 pieces per row) and of V
+    // (R = DV / 8); the next block's pieces and their rows' gamma are loaded into registers
+    // while the current block's products run.  Tokens outside the frame read past the buffer
+    // end, which returns zeros.
+    constexpr int RK = DK / 8, RV = DV / 8, NPK = 64 * RK / 256, NPV = 64 * RV / 256;
+    uint4 kp[NPK], vp[NPV];
+    float gk[NPK], gv[NPV];
+    auto load_block = [&](int64_t t0) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                h[2 * e] = (_Float16)(sg * __uint_as_float(wv[e] << 16));
-                h[2 * e + 1] = (_Float16)(sg * __uint_as_float(wv[e] & 0xffff0000u));
-            }
-            _Float16* dst = isk ? Kp + row * L::LDK + col : Vp + row * L::LDV + col;
-            *reinterpret_cast<half8*>(dst) = h;
+        for (int i = 0; i < NPK; ++i) {
+            const int row = tid / RK + (256 / RK) * i, col = (tid % RK) * 8;
+            const int64_t tok = t0 + row;
+            const bool in = tok < t_end;
+            kp[i] = bld16(rk, in ? (uint32_t)((tok * DK + col) * 2) : (uint32_t)(T * DK * 2));
+            gk[i] = bld4(rgm, in ? (uint32_t)(tok * 4) : (uint32_t)(T * 4));
         }
+#pragma unroll
+        for (int i = 0; i < NPV; ++i) {
+            const int row = tid / RV + (256 / RV) * i, col = (tid % RV) * 8;
+            const int64_t tok = t0 + row;
+            const bool in = tok < t_end;
+            vp[i] = bld16(rv, in ? (uint32_t)((tok * DV + col) * 2) : (uint32_t)(T * DV * 2));
+            gv[i] = bld4(rgm, in ? (uint32_t)(tok * 4) : (uint32_t)(T * 4));
+        }
+    };
+    auto scaled = [](const uint4& u, float sg) {
+        const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
+        half8 h;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            h[2 * e] = (_Float16)(sg * __uint_as_float(wv[e] << 16));
+            h[2 * e + 1] = (_Float16)(sg * __uint_as_float(wv[e] & 0xffff0000u));
+        }
+        return h;
+    };
+    auto stage_block = [&]() {
+#pragma unroll
+        for (int i = 0; i < NPK; ++i) {
+            const int row = tid / RK + (256 / RK) * i, col = (tid % RK) * 8;
+            *reinterpret_cast<half8*>(Kp + row * L::LDK + col) = scaled(kp[i], sqrtf(gk[i]));
+        }
+#pragma unroll
+        for (int i = 0; i < NPV; ++i) {
+            const int row = tid / RV + (256 / RV) * i, col = (tid % RV) * 8;
+            *reinterpret_cast<half8*>(Vp + row * L::LDV + col) = scaled(vp[i], sqrtf(gv[i]));
+        }
+    };
+    if (t_beg < t_end) load_block(t_beg);
+    for (int64_t t0 = t_beg; t0 < t_end; t0 += 64) {
+        stage_block();
         lds_barrier();
+        if (t0 + 64 < t_end) load_block(t0 + 64);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             half8 kf[NT];
