@@ -12,9 +12,10 @@
 //
 //   frame_gram_kernel   one workgroup per (sequence, frame): G and C by fp16 MFMA over the
 //                       frame's tokens (operands sqrt(gamma) k and sqrt(gamma) v, fp32
-//                       accumulation), then W = (I + G)^{-1} by in-place Gauss-Jordan
-//                       elimination in fp32 registers (I + G is symmetric positive definite
-//                       with eigenvalues >= 1, so no pivoting is needed), written as a pair of
+//                       accumulation), then W = (I + G)^{-1} by blocked in-place Gauss-Jordan
+//                       elimination in fp32 (16-pivot panels in registers, the rank-16
+//                       updates on fp32 MFMA; I + G is symmetric positive definite with
+//                       eigenvalues >= 1, so no pivoting is needed), written as a pair of
 //                       fp16 matrices W = W_hi + W_lo, and C in fp32;
 //   frame_state_kernel  one workgroup per (sequence, 64 value channels), frames in order:
 //                       S_t^T = W_t (D_t S_{t-1}^T + C_t^T) on fp16 MFMA with both factors split
@@ -59,9 +60,7 @@ struct FrGramLds {
     static constexpr int oK = 0;
     static constexpr int oV = oK + 64 * LDK * 2;
     static constexpr int oA = oV + 64 * LDV * 2;
-    static constexpr int oRow = oA + DK * LDA * 4;   // pivot row, two buffers
-    static constexpr int oCol = oRow + 2 * DK * 4;   // pivot column, two buffers
-    static constexpr int total = oCol + 2 * DK * 4;
+    static constexpr int total = oA + DK * LDA * 4;
     static_assert(total <= 160 * 1024, "LDS budget");
 };
 
@@ -74,8 +73,6 @@ __global__ __launch_bounds__(256, 1) void frame_gram_kernel(const FrArgs a) {
     _Float16* Kp = reinterpret_cast<_Float16*>(smem + L::oK);
     _Float16* Vp = reinterpret_cast<_Float16*>(smem + L::oV);
     float* Am = reinterpret_cast<float*>(smem + L::oA);
-    float* rowb = reinterpret_cast<float*>(smem + L::oRow);
-    float* colb = reinterpret_cast<float*>(smem + L::oCol);
 
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, j = l & 15, g = l >> 4;
     const int64_t bh = blockIdx.x / a.F;
@@ -217,45 +214,105 @@ __global__ __launch_bounds__(256, 1) void frame_gram_kernel(const FrArgs a) {
     }
     lds_barrier();
 
-    // ---- W = (I + G)^{-1}: in-place Gauss-Jordan.  Thread t holds CPT consecutive entries of
-    // row i; for pivot p every entry off row p and column p takes x -= (A[i][p] / A[p][p]) A[p][j],
-    // row p is divided by the pivot, column p becomes -A[i][p] / A[p][p], the pivot 1 / A[p][p].
+    // ---- W = (I + G)^{-1} by blocked Gauss-Jordan elimination in place, 16 pivots per block.
+    // For pivot block K (rows and columns Kb = 16K .. 16K + 15):
+    //   1. wave 0 eliminates the 16 pivots on the panel columns Kb only (all rows, fp32
+    //      registers, two rows per lane; the pivot row reaches the other lanes by readlane).
+    //      The panel then holds P = [-A_{i,Kb} D^{-1} (rows i outside Kb); D^{-1} (rows Kb)],
+    //      D = A_{Kb,Kb};
+    //   2. every other column block j takes the same 16 pivots at once as a rank-16 product:
+    //      A_{:,j} <- [i outside Kb] A_{:,j} + P A_{Kb,j}, on fp32 MFMA (16x16x4), each wave a
+    //      share of the 16x16 tiles, all tiles read before any is written.
+    // This is the pivot-by-pivot elimination regrouped (the same operations in exact
+    // arithmetic): the panel sees its 16 pivots one by one, the rest of the matrix sees their
+    // product.  I + G is symmetric positive definite with eigenvalues >= 1, and so is every
+    // pivot block's Schur complement: no pivoting is needed.
+    constexpr int NB = DK / 16;           // pivot blocks
+    constexpr int NR = DK / 64;           // panel rows per lane of wave 0
+    constexpr int NTW = (NB * (NB - 1) + 3) / 4;  // trailing tiles per wave
+    for (int kbk = 0; kbk < NB; ++kbk) {
+        const int kc = 16 * kbk;
+        if (w == 0) {
+            float P[NR][16];
+#pragma unroll
+            for (int rr = 0; rr < NR; ++rr)
+#pragma unroll
+                for (int c = 0; c < 16; c += 4) {
+                    const float4v v4 = ld4f(Am + (l + 64 * rr) * L::LDA + kc + c);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) P[rr][c + e] = v4[e];
+                }
+#pragma unroll
+            for (int pp = 0; pp < 16; ++pp) {
+                const int p = kc + pp, pl = p & 63, prr = p >> 6;  // pivot row: lane pl, register row prr
+                // the pivot row from lane pl's register row prr (uniform: a scalar branch, so only
+                // that row is read)
+                float rowp[16];
+#pragma unroll
+                for (int rr = 0; rr < NR; ++rr) {
+                    if (prr == rr) {
+#pragma unroll
+                        for (int c = 0; c < 16; ++c)
+                            rowp[c] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(P[rr][c]), pl));
+                    }
+                }
+                const float rp = 1.0f / rowp[pp];
+#pragma unroll
+                for (int rr = 0; rr < NR; ++rr) {
+                    const bool prow = l + 64 * rr == p;
+                    const float f = P[rr][pp];
+                    const float keep = prow ? 0.0f : 1.0f;
+                    const float cf = prow ? rp : -f * rp;
+#pragma unroll
+                    for (int c = 0; c < 16; ++c) P[rr][c] = fmaf(rowp[c], cf, P[rr][c] * keep);
+                    P[rr][pp] = prow ? rp : -f * rp;
+                }
+            }
+#pragma unroll
+            for (int rr = 0; rr < NR; ++rr)
+#pragma unroll
+                for (int c = 0; c < 16; c += 4)
+                    *reinterpret_cast<float4v*>(Am + (l + 64 * rr) * L::LDA + kc + c) =
+                        float4v{P[rr][c], P[rr][c + 1], P[rr][c + 2], P[rr][c + 3]};
+        }
+        lds_barrier();
+        // tiles (ib, jb), jb != kbk, numbered n = ib (NB - 1) + (jb - [jb > kbk]); wave w
+        // takes n = w, w + 4, ...
+        float4v acc[NTW];
+#pragma unroll
+        for (int t = 0; t < NTW; ++t) {
+            const int n = w + 4 * t;
+            if (n < NB * (NB - 1)) {
+                const int ib = n / (NB - 1), jr = n % (NB - 1), jb = jr + (jr >= kbk ? 1 : 0);
+                float4v a4 = zero4();
+                if (ib != kbk) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) a4[r] = Am[(16 * ib + 4 * g + r) * L::LDA + 16 * jb + j];
+                }
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float av = Am[(16 * ib + j) * L::LDA + kc + 4 * q + g];   // P[16 ib + j][4q + g]
+                    const float bv = Am[(kc + 4 * q + g) * L::LDA + 16 * jb + j];   // A[Kb + 4q + g][16 jb + j]
+                    a4 = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, a4, 0, 0, 0);
+                }
+                acc[t] = a4;
+            }
+        }
+        lds_barrier();
+#pragma unroll
+        for (int t = 0; t < NTW; ++t) {
+            const int n = w + 4 * t;
+            if (n < NB * (NB - 1)) {
+                const int ib = n / (NB - 1), jr = n % (NB - 1), jb = jr + (jr >= kbk ? 1 : 0);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Am[(16 * ib + 4 * g + r) * L::LDA + 16 * jb + j] = acc[t][r];
+            }
+        }
+        lds_barrier();
+    }
+    // W as W_hi + W_lo (fp16 each), rows natural: thread t writes CPT entries of row t / TPR
     constexpr int TPR = 256 / DK, CPT = DK / TPR;
     const int ri = tid / TPR, c0 = (tid % TPR) * CPT;
-    float x[CPT];
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) x[c] = Am[ri * L::LDA + c0 + c];
-    for (int pb = 0; pb < TPR; ++pb) {
-        const bool owns_col = c0 == pb * CPT;
-        // fully unrolled, so that x[pp] is a register and not a scratch access
-#pragma clang loop unroll(full)
-        for (int pp = 0; pp < CPT; ++pp) {
-            const int p = pb * CPT + pp;
-            float* rb = rowb + (p & 1) * DK;
-            float* cb = colb + (p & 1) * DK;
-            if (owns_col) cb[ri] = x[pp];
-            if (ri == p) {
-#pragma unroll
-                for (int c = 0; c < CPT; c += 4)
-                    *reinterpret_cast<float4v*>(rb + c0 + c) = float4v{x[c], x[c + 1], x[c + 2], x[c + 3]};
-            }
-            lds_barrier();
-            const float rp = 1.0f / rb[p];
-            const float fac = cb[ri] * rp;
-            const bool prow = ri == p;
-            // row p: x = A[p][j] / piv; other rows: x -= fac * A[p][j]
-            const float keep = prow ? 0.0f : 1.0f;
-            const float cf = prow ? rp : -fac;
-#pragma unroll
-            for (int c = 0; c < CPT; c += 4) {
-                const float4v rv4 = *reinterpret_cast<const float4v*>(rb + c0 + c);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) x[c + e] = fmaf(rv4[e], cf, x[c + e] * keep);
-            }
-            if (owns_col) x[pp] = prow ? rp : -fac;
-        }
-    }
-    // W as W_hi + W_lo (fp16 each), rows natural
     uint16_t* wh = a.Wh + fi * (int64_t)(DK * DK) + ri * DK + c0;
     uint16_t* wl = a.Wl + fi * (int64_t)(DK * DK) + ri * DK + c0;
 #pragma unroll
@@ -263,8 +320,9 @@ __global__ __launch_bounds__(256, 1) void frame_gram_kernel(const FrArgs a) {
         half8 hh, hl;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            hh[e] = (_Float16)x[c + e];
-            hl[e] = (_Float16)(x[c + e] - (float)hh[e]);
+            const float xv = Am[ri * L::LDA + c0 + c + e];
+            hh[e] = (_Float16)xv;
+            hl[e] = (_Float16)(xv - (float)hh[e]);
         }
         *reinterpret_cast<half8*>(wh + c) = hh;
         *reinterpret_cast<half8*>(wl + c) = hl;
