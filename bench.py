@@ -211,27 +211,34 @@ def bench_prep(torch, gdr, gdr_synth, steps=20):
         sets.append({kk: to_dev(torch, r[kk], kk in ("q_raw", "k_raw", "v")) for kk in r})
     outs = [torch.empty((w.B, w.H, w.T, w.d_v), dtype=torch.bfloat16, device="cuda") for _ in sets]
     fin = [torch.empty((w.B, w.H, w.d_v, w.d_k), dtype=torch.float32, device="cuda") for _ in sets]
+    wsb = torch.empty(max(gdr.chunk_fwd_fused_prep_workspace_size(w.B, w.H, w.T, w.d_k, w.d_v), 1),
+                      dtype=torch.uint8, device="cuda")
 
-    def launch(i):
+    def launch(i, ws):
         s = sets[i % 2]
         gdr.chunk_fwd_fused_prep(s["q_raw"], s["k_raw"], s["v"], s["dt"], s["A_log"], s["dt_bias"], s["beta_logit"],
-                                 out=outs[i % 2], final_state=fin[i % 2])
+                                 out=outs[i % 2], final_state=fin[i % 2], workspace=ws)
 
-    for i in range(2):
-        launch(i)
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for i in range(steps):
-        ev[i][0].record()
-        launch(i)
-        ev[i][1].record()
-    torch.cuda.synchronize()
-    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    def timed(ws):
+        for i in range(2):
+            launch(i, ws)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for i in range(steps):
+            ev[i][0].record()
+            launch(i, ws)
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+    ms_single = timed(None)
+    ms = timed(wsb)
     n = w.B * w.H * w.T
     separate_pass = n * w.d_k * 2 * 2 * 2 + n * 4 * 4   # q, k read and written (bf16); dt, logit read, g, beta written
     flops = chunk_flops(w.B, w.H, w.T, w.d_k, w.d_v)
     return {"workload": "gdn_bf16_train from raw projections: B=4 H=16 T=4096 d=128, per-head A_log, dt_bias",
-            "kernel": "chunk_fwd_pc_kernel<128, 2>", "ms_per_call": round(ms, 4),
+            "kernel": "chunk_ut_kernel<128, 2> + chunk_state_kernel<128, 4, 2>", "ms_per_call": round(ms, 4),
+            "single_kernel": {"kernel": "chunk_fwd_pc_kernel<128, 2>", "ms_per_call": round(ms_single, 4)},
             "tokens_per_s": round(w.B * w.T / (ms * 1e-3), 1),
             "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_MFMA_F16, 4),
             "separate_prep_pass_hbm_floor_ms": round(separate_pass / (PEAK_HBM * 1e9) * 1e3, 4)}

@@ -12,8 +12,9 @@ library is loaded on first use and its absence is an error: there is no CPU
 fallback.
 """
 from ._binding import (EXPORTED_SYMBOLS, LIBRARY_PATH, GdrError, chunk_fwd, chunk_fwd_fused_prep,
+                       chunk_fwd_fused_prep_workspace_size,
                        chunk_fwd_workspace_size, decode_step, frame_fwd, frame_fwd_workspace_size, gdn2_chunk_fwd,
                        gdn2_chunk_fwd_workspace_size, gdp_chunk_fwd, gdp_chunk_fwd_workspace_size, load_library, status_string, version)
 
-__all__ = ["chunk_fwd", "chunk_fwd_workspace_size", "chunk_fwd_fused_prep", "frame_fwd", "frame_fwd_workspace_size", "gdp_chunk_fwd", "gdp_chunk_fwd_workspace_size", "gdn2_chunk_fwd", "gdn2_chunk_fwd_workspace_size", "decode_step", "GdrError", "load_library", "version", "status_string",
+__all__ = ["chunk_fwd", "chunk_fwd_workspace_size", "chunk_fwd_fused_prep", "chunk_fwd_fused_prep_workspace_size", "frame_fwd", "frame_fwd_workspace_size", "gdp_chunk_fwd", "gdp_chunk_fwd_workspace_size", "gdn2_chunk_fwd", "gdn2_chunk_fwd_workspace_size", "decode_step", "GdrError", "load_library", "version", "status_string",
            "LIBRARY_PATH", "EXPORTED_SYMBOLS"]

@@ -20,7 +20,8 @@ GDR_GATE_SCALAR, GDR_GATE_CHANNEL = 0, 1
 
 # every entry point include/gdr.h declares
 EXPORTED_SYMBOLS = ("gdr_version", "gdr_status_string", "gdr_chunk_fwd", "gdr_chunk_fwd_workspace_size",
-                    "gdr_chunk_fwd_ws", "gdr_chunk_fwd_fused_prep", "gdr_gdp_chunk_fwd", "gdr_gdp_chunk_fwd_workspace_size", "gdr_gdp_chunk_fwd_ws", "gdr_gdn2_chunk_fwd",
+                    "gdr_chunk_fwd_ws", "gdr_chunk_fwd_fused_prep",
+                    "gdr_chunk_fwd_fused_prep_workspace_size", "gdr_chunk_fwd_fused_prep_ws", "gdr_gdp_chunk_fwd", "gdr_gdp_chunk_fwd_workspace_size", "gdr_gdp_chunk_fwd_ws", "gdr_gdn2_chunk_fwd",
                     "gdr_gdn2_chunk_fwd_workspace_size", "gdr_gdn2_chunk_fwd_ws", "gdr_frame_fwd_workspace_size", "gdr_frame_fwd", "gdr_decode_step")
 
 _lock = threading.Lock()
@@ -55,6 +56,11 @@ def load_library():
         lib.gdr_chunk_fwd_ws.argtypes = [i64, i64, i64, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, i64, P]
         lib.gdr_chunk_fwd_fused_prep.restype = i32
         lib.gdr_chunk_fwd_fused_prep.argtypes = [i64, i64, i64, i32, i32, i32, P, P, P, P, P, P, P, P, P, P, P]
+        lib.gdr_chunk_fwd_fused_prep_workspace_size.restype = i64
+        lib.gdr_chunk_fwd_fused_prep_workspace_size.argtypes = [i64, i64, i64, i32, i32]
+        lib.gdr_chunk_fwd_fused_prep_ws.restype = i32
+        lib.gdr_chunk_fwd_fused_prep_ws.argtypes = [i64, i64, i64, i32, i32, i32, P, P, P, P, P, P, P, P, P, P, P,
+                                                    i64, P]
         lib.gdr_gdp_chunk_fwd.restype = i32
         lib.gdr_gdp_chunk_fwd.argtypes = [i64, i64, i64, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P]
         lib.gdr_gdp_chunk_fwd_workspace_size.restype = i64
@@ -183,14 +189,23 @@ def chunk_fwd(q, k, v, g, beta, initial_state=None, *, output_final_state=True, 
     return o, final_state
 
 
+def chunk_fwd_fused_prep_workspace_size(B, H, T, d_k, d_v) -> int:
+    n = int(load_library().gdr_chunk_fwd_fused_prep_workspace_size(B, H, T, d_k, d_v))
+    if n < 0:
+        raise GdrError(GDR_ERR_SHAPE, "gdr_chunk_fwd_fused_prep_workspace_size")
+    return n
+
+
 def chunk_fwd_fused_prep(q_raw, k_raw, v, dt, A_log, dt_bias, beta_logit, initial_state=None, *,
-                         output_final_state=True, out=None, final_state=None, stream=None):
-    """gdr_chunk_fwd_fused_prep on torch tensors: the scalar-gate chunked forward from raw
-    projections (q, k normalised, beta = sigmoid(beta_logit), g = -exp(A_log) softplus(dt +
-    dt_bias) inside the kernel).
+                         output_final_state=True, out=None, final_state=None, stream=None, workspace="auto"):
+    """The scalar-gate chunked forward from raw projections (q, k normalised, beta =
+    sigmoid(beta_logit), g = -exp(A_log) softplus(dt + dt_bias) inside the kernels):
+    gdr_chunk_fwd_fused_prep_ws, or gdr_chunk_fwd_fused_prep with workspace=None.
 
     q_raw, k_raw [B,H,T,d_k], v [B,H,T,d_v] (bf16); dt, beta_logit [B,H,T] fp32;
-    A_log, dt_bias [H] fp32; initial_state [B,H,d_v,d_k] fp32 or None.
+    A_log, dt_bias [H] fp32; initial_state [B,H,d_v,d_k] fp32 or None.  workspace: "auto"
+    (default) allocates the two-kernel path's workspace with torch; a uint8 CUDA tensor is used
+    as that workspace; None calls the single kernel.
     Returns (o, final_state); final_state is None when output_final_state is False.
     """
     import torch
@@ -215,11 +230,28 @@ def chunk_fwd_fused_prep(q_raw, k_raw, v, dt, A_log, dt_bias, beta_logit, initia
         final_state = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
     if final_state is not None:
         _check(final_state, "final_state", (B, H, dv, dk), torch.float32, dev)
-    st = load_library().gdr_chunk_fwd_fused_prep(B, H, T, dk, dv, io, _ptr(q_raw), _ptr(k_raw), _ptr(v), _ptr(dt),
-                                                 _ptr(A_log), _ptr(dt_bias), _ptr(beta_logit), _ptr(initial_state),
-                                                 _ptr(o), _ptr(final_state), _stream(stream, dev))
+    if workspace is None:
+        st = load_library().gdr_chunk_fwd_fused_prep(B, H, T, dk, dv, io, _ptr(q_raw), _ptr(k_raw), _ptr(v),
+                                                     _ptr(dt), _ptr(A_log), _ptr(dt_bias), _ptr(beta_logit),
+                                                     _ptr(initial_state), _ptr(o), _ptr(final_state),
+                                                     _stream(stream, dev))
+        if st != GDR_OK:
+            raise GdrError(st, "gdr_chunk_fwd_fused_prep")
+        return o, final_state
+    need = chunk_fwd_fused_prep_workspace_size(B, H, T, dk, dv)
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError(f"workspace: expected 'auto', None or a tensor, got {workspace!r}")
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace: must be a contiguous tensor on the inputs' device")
+    nbytes = workspace.numel() * workspace.element_size()
+    st = load_library().gdr_chunk_fwd_fused_prep_ws(B, H, T, dk, dv, io, _ptr(q_raw), _ptr(k_raw), _ptr(v), _ptr(dt),
+                                                    _ptr(A_log), _ptr(dt_bias), _ptr(beta_logit),
+                                                    _ptr(initial_state), _ptr(o), _ptr(final_state), _ptr(workspace),
+                                                    nbytes, _stream(stream, dev))
     if st != GDR_OK:
-        raise GdrError(st, "gdr_chunk_fwd_fused_prep")
+        raise GdrError(st, "gdr_chunk_fwd_fused_prep_ws")
     return o, final_state
 
 

@@ -67,6 +67,33 @@ __device__ __forceinline__ half8 bf16x8_to_half8(const uint4& u) {
     }
     return h;
 }
+// One 16-byte piece (8 bf16) of a row of DK values whose DK / 8 pieces sit in consecutive
+// lanes of one 16-lane DPP row: the row's inverse L2 norm 1 / max(||x||, 1e-6) (returned in
+// inv, the same in every lane of the row) and the piece divided by the norm, in fp16.
+// quad_perm xor 1 and xor 2, row_half_mirror (and row_mirror for 16 lanes) leave the row's
+// sum of squares in every lane.  Every lane of the wave must take part.
+template <int DK>
+__device__ __forceinline__ half8 unit_rows(const uint4& u, float& inv) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    float x[8], ss = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        x[2 * e] = __uint_as_float(w[e] << 16);
+        x[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
+    ss += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(ss), 0xB1, 0xf, 0xf, false));
+    ss += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(ss), 0x4E, 0xf, 0xf, false));
+    ss += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(ss), 0x141, 0xf, 0xf, false));
+    if constexpr (DK == 128)
+        ss += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(ss), 0x140, 0xf, 0xf, false));
+    inv = __builtin_amdgcn_rsqf(fmaxf(ss, 1e-12f));
+    half8 h;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) h[e] = (_Float16)(x[e] * inv);
+    return h;
+}
 // 8 bf16 (one uint4) -> 8 fp16 written as two 4-element groups at permuted positions.
 __device__ __forceinline__ void stage8(_Float16* row, int m0, const uint4& u) {
     const uint32_t w[4] = {u.x, u.y, u.z, u.w};

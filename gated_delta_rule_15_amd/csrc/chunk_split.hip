@@ -55,8 +55,17 @@ struct UtTab {
 constexpr int kGdnWsFactors = 2 * kChunk * kChunk;        // offset of the fp32 factor table
 constexpr int kGdnWsNF = 144;                               // its floats
 constexpr int kGdnWsStride = kGdnWsFactors + 2 * kGdnWsNF;  // 8480 halfs = 16960 bytes
+// fused input preparation: the record also holds the chunk's normalised k and q rows (fp16,
+// [64][DK] each), so that the state pass copies them without converting (49728 bytes for
+// DK = 128, 33344 for DK = 64)
+constexpr int kPrepWsK = kGdnWsStride;
+template <int DK>
+constexpr int prep_ws_stride() { return kPrepWsK + 2 * kChunk * DK; }
 
 struct UtArgs {
+    int H;              // PREP: heads (bh mod H is the head of the gate parameters)
+    const float* A_log; // PREP: [H]
+    const float* dt_bias;  // PREP: [H]
     int64_t T;          // steps per sequence (T_real n_h virtual steps for the VIRT kernels)
     int64_t Treal;      // rows of q and g per sequence (= T unless VIRT)
     uint32_t nh;        // substeps per token (VIRT)
@@ -90,11 +99,19 @@ struct UtLds {
     static_assert((oSm | oNd | oXd | oAt | oTt) % 16 == 0, "alignment");
 };
 
+// Instantiations: plain, VIRT and PREP.
 // VIRT: Gated Delta Product over its virtual steps ("Linear Attention, Visualized", "GDP as GDN
 // over a virtual sequence"): step m = n_h t + j reads q_t only when j = n_h - 1 and g_t only
 // when j = 0; other steps read past the end of the real-token buffer, which returns zero.
-template <int DK, bool VIRT>
+// PREP: the inputs from raw projections (same page, "Optional: Constructing the decay gate",
+// and the unit-norm convention of keys and queries): q = q_raw / max(||q_raw||, 1e-6), k
+// likewise, beta = sigmoid(beta_logit), g = -e^{A_log[h]} softplus(dt + dt_bias[h]); the
+// inverse norms go to the workspace for the state pass.
+constexpr int kUtPlain = 0, kUtVirt = 1, kUtPrep = 2;
+template <int DK, int UM>
 __global__ __launch_bounds__(128) void chunk_ut_kernel(const UtArgs a) {
+    constexpr bool VIRT = UM == kUtVirt, PREP = UM == kUtPrep;
+    constexpr int WSS = PREP ? prep_ws_stride<DK>() : kGdnWsStride;  // workspace halfs per chunk
     using L = UtLds<DK>;
     using S = UtTab;
     constexpr int C = kChunk;
@@ -147,12 +164,31 @@ __global__ __launch_bounds__(128) void chunk_ut_kernel(const UtArgs a) {
             }
             gl = bld4(rg, offg);
             bt = bld4(rb, (t0 + l) * 4);
+            if constexpr (PREP) {  // past the sequence end: identity tokens (g = 0, beta = 0)
+                const bool live = (int64_t)(t0 + l) < T;
+                const int h = (int)(bh % a.H);
+                const float lam = fast_exp(a.A_log[h]), z = gl + a.dt_bias[h];
+                // softplus(z) = max(z, 0) + log(1 + e^{-|z|})
+                gl = live ? -lam * (fmaxf(z, 0.0f) + __logf(1.0f + fast_exp(-fabsf(z)))) : 0.0f;
+                bt = live ? 1.0f / (1.0f + fast_exp(-bt)) : 0.0f;
+            }
         }
+        uint16_t* kqw = a.ws + (bh * a.nC + c) * WSS + kPrepWsK;  // PREP: normalised k, then q
 #pragma unroll
         for (int u = 0; u < NP; ++u) {
             const int idx = tid + 128 * u, row = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
-            *reinterpret_cast<half8*>(Kb + row * L::LDK + col) = bf16x8_to_half8(kr[u]);
-            *reinterpret_cast<half8*>(Qb + row * L::LDK + col) = bf16x8_to_half8(qr[u]);
+            if constexpr (PREP) {
+                // one row spans DK / 8 consecutive lanes: a DPP sum inside each 16-lane row
+                float ik, iq;
+                const half8 hk = unit_rows<DK>(kr[u], ik), hq = unit_rows<DK>(qr[u], iq);
+                *reinterpret_cast<half8*>(Kb + row * L::LDK + col) = hk;
+                *reinterpret_cast<half8*>(Qb + row * L::LDK + col) = hq;
+                *reinterpret_cast<half8*>(kqw + idx * 8) = hk;
+                *reinterpret_cast<half8*>(kqw + C * DK + idx * 8) = hq;
+            } else {
+                *reinterpret_cast<half8*>(Kb + row * L::LDK + col) = bf16x8_to_half8(kr[u]);
+                *reinterpret_cast<half8*>(Qb + row * L::LDK + col) = bf16x8_to_half8(qr[u]);
+            }
         }
         // in-chunk cumulative log-decay and the factor table (wave 0, lane = token)
         if (w == 0) {
@@ -163,7 +199,7 @@ __global__ __launch_bounds__(128) void chunk_ut_kernel(const UtArgs a) {
             const int blk = l >> 4;
             sm[S::SG + l] = x;
             // the state pass's factors of this chunk
-            float* fw = reinterpret_cast<float*>(a.ws + (bh * a.nC + c) * kGdnWsStride + kGdnWsFactors);
+            float* fw = reinterpret_cast<float*>(a.ws + (bh * a.nC + c) * WSS + kGdnWsFactors);
             const float GC = ge[3];
             fw[l] = fast_exp(x);
             fw[64 + l] = fast_exp(GC - x);
@@ -351,7 +387,7 @@ __global__ __launch_bounds__(128) void chunk_ut_kernel(const UtArgs a) {
     lds_barrier();
 
     // ---- A^T and T to the workspace, 16-byte pieces
-    uint16_t* dst = a.ws + (bh * a.nC + c) * kGdnWsStride;
+    uint16_t* dst = a.ws + (bh * a.nC + c) * WSS;
 #pragma unroll
     for (int u = 0; u < C * C / 8 / 128; ++u) {
         const int idx = tid + 128 * u, row = idx / (C / 8), col = (idx % (C / 8)) * 8;
@@ -408,8 +444,10 @@ struct StLds {
 
 // Modes of the state pass: the scalar gate, the per-channel gate (KDA), Gated DeltaNet-2
 // (the KDA pass with z = w (.) v in place of v), and the Gated Delta Product (the scalar-gate
-// pass over virtual steps: q read and o written on the last substep of a token only).
-constexpr int kStGdn = 0, kStKda = 1, kStGd2 = 2, kStGdp = 3;
+// pass over virtual steps: q read and o written on the last substep of a token only), and the
+// fused input preparation (the scalar-gate pass over raw q and k, each row scaled by the
+// inverse norm the UT pass wrote).
+constexpr int kStGdn = 0, kStKda = 1, kStGd2 = 2, kStGdp = 3, kStPrep = 4;
 
 // NCW consumer waves of 16 value channels each (a value tile of 16 NCW channels) and two loader
 // waves.  NCW = 1 doubles the workgroups of a grid that would leave compute units idle.
@@ -418,6 +456,7 @@ __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const St
     constexpr bool KDA = MODE == kStKda || MODE == kStGd2;  // the UT pass wrote the decayed copies
     constexpr bool ZW = MODE == kStGd2;                     // V tile holds z = w (.) v in fp32
     constexpr bool VIRT = MODE == kStGdp;                   // GDP virtual steps
+    constexpr bool PREP = MODE == kStPrep;                  // normalised q, k from the workspace
     using L = StLds<DK>;
     constexpr int C = kChunk;
     constexpr int NKB = DK / 32;
@@ -447,7 +486,7 @@ __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const St
     const auto rk = make_rsrc(KDA ? nullptr : a.k + bh * T * DK, KDA ? 0u : (uint32_t)(T * DK * 2));
     const auto rv = make_rsrc(a.v + bh * T * DV, (uint32_t)(T * DV * 2));
     const auto rwg = make_rsrc(ZW ? a.wg + bh * T * DV : nullptr, ZW ? (uint32_t)(T * DV * 4) : 0u);
-    constexpr int WS = KDA ? kda_ws_stride<DK>() : kGdnWsStride;  // workspace halfs per chunk
+    constexpr int WS = KDA ? kda_ws_stride<DK>() : PREP ? prep_ws_stride<DK>() : kGdnWsStride;  // halfs per chunk
     // offsets (halfs) inside a chunk's workspace record of the per-channel gate
     constexpr int WKG = 2 * C * C, WQG = WKG + C * DK, WKC = WQG + C * DK, WFE = WKC + C * DK;
     const auto rw = make_rsrc(a.ws + bh * nC * WS, (uint32_t)(nC * WS * 2));
@@ -483,6 +522,9 @@ __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const St
             if constexpr (KDA) {
                 kr[u] = bld16(rw, (wb + WKG + idx * 8) * 2);
                 qr[u] = bld16(rw, (wb + WKC + idx * 8) * 2);
+            } else if constexpr (PREP) {  // normalised fp16 rows written by the UT pass
+                kr[u] = bld16(rw, (wb + kPrepWsK + idx * 8) * 2);
+                qr[u] = bld16(rw, (wb + kPrepWsK + C * DK + idx * 8) * 2);
             } else {
                 const uint32_t off = ((t0 + row) * DK + col) * 2;
                 uint32_t offq = off;
@@ -533,7 +575,7 @@ __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const St
     };
     // K and Q to fp16 in the registers (while the consumers' first products read LDS)
     auto convert = [&](LdRegs& R) {
-        if constexpr (KDA) return;  // the UT pass wrote fp16
+        if constexpr (KDA || PREP) return;  // the UT pass wrote fp16
         uint4 *kr = R.kr, *qr = R.qr;
 #pragma unroll
         for (int u = 0; u < NPK; ++u) {
@@ -869,14 +911,14 @@ static hipError_t launch_state(const StArgs& s, int64_t BH, hipStream_t st) {
     return launch_state_ncw<DK, MODE, 2>(s, BH, st);
 }
 
-template <int DK, bool VIRT>
+template <int DK, int UM>
 static hipError_t launch_split(const UtArgs& u, const StArgs& s, int64_t BH, hipStream_t st) {
     using LU = UtLds<DK>;
-    auto ku = chunk_ut_kernel<DK, VIRT>;
+    auto ku = chunk_ut_kernel<DK, UM>;
     if (u.nC > 0) hipLaunchKernelGGL(ku, dim3((unsigned)(BH * u.nC)), dim3(128), LU::total, st, u);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return launch_state<DK, VIRT ? kStGdp : kStGdn>(s, BH, st);
+    return launch_state<DK, UM == kUtVirt ? kStGdp : UM == kUtPrep ? kStPrep : kStGdn>(s, BH, st);
 }
 
 // Bytes of workspace the two-kernel path needs: 16960 per (sequence, chunk).
@@ -894,6 +936,9 @@ hipError_t chunk_split_dispatch(int64_t BH, int64_t T, int nh, int dk, int dv, c
     const int64_t nC = (Tv + kChunk - 1) / kChunk;
     const uint32_t magic = nh > 1 ? (uint32_t)(((uint64_t(1) << 32) + nh - 1) / nh) : 0u;
     UtArgs u;
+    u.H = 1;
+    u.A_log = nullptr;
+    u.dt_bias = nullptr;
     u.T = Tv;
     u.Treal = T;
     u.nh = (uint32_t)nh;
@@ -921,11 +966,59 @@ hipError_t chunk_split_dispatch(int64_t BH, int64_t T, int nh, int dk, int dv, c
     s.o = static_cast<uint16_t*>(o);
     s.Sf = Sf;
     if (nh > 1) {
-        if (dk == 128) return launch_split<128, true>(u, s, BH, st);
-        return launch_split<64, true>(u, s, BH, st);
+        if (dk == 128) return launch_split<128, kUtVirt>(u, s, BH, st);
+        return launch_split<64, kUtVirt>(u, s, BH, st);
     }
-    if (dk == 128) return launch_split<128, false>(u, s, BH, st);
-    return launch_split<64, false>(u, s, BH, st);
+    if (dk == 128) return launch_split<128, kUtPlain>(u, s, BH, st);
+    return launch_split<64, kUtPlain>(u, s, BH, st);
+}
+
+// Bytes of workspace of the two-kernel path with fused input preparation, per (sequence,
+// chunk): 49728 for dk = 128, 33344 for dk = 64.
+int64_t chunk_split_prep_workspace_bytes(int64_t BH, int64_t T, int dk) {
+    const int64_t nC = (T + kChunk - 1) / kChunk;
+    return BH * nC * (dk == 128 ? prep_ws_stride<128>() : prep_ws_stride<64>()) * 2;
+}
+
+// Gated DeltaNet from raw projections on the two-kernel path: q_raw, k_raw [BH][T][dk] bf16,
+// dt and beta_logit [BH][T], A_log and dt_bias [H] (bh mod H is the head).
+hipError_t chunk_split_prep_dispatch(int64_t BH, int64_t H, int64_t T, int dk, int dv, const void* q_raw,
+                                     const void* k_raw, const void* v, const float* dt, const float* A_log,
+                                     const float* dt_bias, const float* beta_logit, const float* S0, void* o,
+                                     float* Sf, void* ws, hipStream_t st) {
+    const int64_t nC = (T + kChunk - 1) / kChunk;
+    UtArgs u;
+    u.H = (int)H;
+    u.A_log = A_log;
+    u.dt_bias = dt_bias;
+    u.T = T;
+    u.Treal = T;
+    u.nh = 1;
+    u.nh_magic = 0u;
+    u.nC = nC;
+    u.q = static_cast<const uint16_t*>(q_raw);
+    u.k = static_cast<const uint16_t*>(k_raw);
+    u.g = dt;
+    u.beta = beta_logit;
+    u.ws = static_cast<uint16_t*>(ws);
+    StArgs s;
+    s.T = T;
+    s.Treal = T;
+    s.nh = 1;
+    s.nh_magic = 0u;
+    s.nC = nC;
+    s.dv = dv;
+    s.ntiles = dv / 32;
+    s.q = u.q;
+    s.k = u.k;
+    s.v = static_cast<const uint16_t*>(v);
+    s.wg = nullptr;
+    s.ws = u.ws;
+    s.S0 = S0;
+    s.o = static_cast<uint16_t*>(o);
+    s.Sf = Sf;
+    if (dk == 128) return launch_split<128, kUtPrep>(u, s, BH, st);
+    return launch_split<64, kUtPrep>(u, s, BH, st);
 }
 
 // State pass of the per-channel-gate two-kernel path, over a workspace the KDA UT pass has

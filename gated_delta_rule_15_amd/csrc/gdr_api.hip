@@ -18,6 +18,11 @@ hipError_t chunk_split_dispatch(int64_t BH, int64_t T, int nh, int dk, int dv, c
                                 const void* v, const float* g, const float* beta, const float* S0, void* o, float* Sf,
                                 void* ws, hipStream_t st);
 int64_t chunk_split_workspace_bytes(int64_t BH, int64_t T);
+int64_t chunk_split_prep_workspace_bytes(int64_t BH, int64_t T, int dk);
+hipError_t chunk_split_prep_dispatch(int64_t BH, int64_t H, int64_t T, int dk, int dv, const void* q_raw,
+                                     const void* k_raw, const void* v, const float* dt, const float* A_log,
+                                     const float* dt_bias, const float* beta_logit, const float* S0, void* o,
+                                     float* Sf, void* ws, hipStream_t st);
 hipError_t chunk_kda_ut_dispatch(int64_t BH, int64_t T, int dk, const void* q, const void* k, const float* g,
                                  const float* beta, const float* eg, void* ws, hipStream_t st);
 int64_t chunk_kda_ws_halfs(int dk);
@@ -318,10 +323,16 @@ gdr_status gdr_gdp_chunk_fwd_ws(int64_t B, int64_t H, int64_t T, int n_h, int d_
     return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
 }
 
-gdr_status gdr_chunk_fwd_fused_prep(int64_t B, int64_t H, int64_t T, int d_k, int d_v, int io_dtype,
-                                    const void* q_raw, const void* k_raw, const void* v, const float* dt,
-                                    const float* A_log, const float* dt_bias, const float* beta_logit,
-                                    const float* initial_state, void* o, float* final_state, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation shared by gdr_chunk_fwd_fused_prep and gdr_chunk_fwd_fused_prep_ws.
+gdr_status check_prep(int64_t B, int64_t H, int64_t T, int d_k, int d_v, int io_dtype, const void* q_raw,
+                      const void* k_raw, const void* v, const float* dt, const float* A_log, const float* dt_bias,
+                      const float* beta_logit, const float* initial_state, const void* o, const float* final_state,
+                      int64_t* BHout, bool* launch) {
+    *launch = false;
     if (B < 0 || H < 0 || T < 0) return GDR_ERR_INVALID_ARG;
     gdr_status s = check_common(d_k, d_v, io_dtype, GDR_GATE_SCALAR);
     if (s != GDR_OK) return s;
@@ -343,13 +354,75 @@ gdr_status gdr_chunk_fwd_fused_prep(int64_t B, int64_t H, int64_t T, int d_k, in
     if (final_state && initial_state && final_state != initial_state &&
         overlaps(final_state, nstate, initial_state, nstate))
         return GDR_ERR_INVALID_ARG;
+    *BHout = BH;
     if (BH == 0) return GDR_OK;
     int64_t nwg;
     if (!mul_ok(BH, d_v / 32, &nwg) || nwg > kMaxGrid) return GDR_ERR_SHAPE;
-    if (!final_state && BHT == 0) return GDR_OK;
+    *launch = final_state != nullptr || BHT > 0;
+    return GDR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdr_status gdr_chunk_fwd_fused_prep(int64_t B, int64_t H, int64_t T, int d_k, int d_v, int io_dtype,
+                                    const void* q_raw, const void* k_raw, const void* v, const float* dt,
+                                    const float* A_log, const float* dt_bias, const float* beta_logit,
+                                    const float* initial_state, void* o, float* final_state, void* stream) {
+    int64_t BH = 0;
+    bool launch = false;
+    gdr_status s = check_prep(B, H, T, d_k, d_v, io_dtype, q_raw, k_raw, v, dt, A_log, dt_bias, beta_logit,
+                              initial_state, o, final_state, &BH, &launch);
+    if (s != GDR_OK || !launch) return s;
     hipError_t e = gdr::chunk_fwd_pc_prep_dispatch(BH, H, T, d_k, d_v, q_raw, k_raw, v, dt, A_log, dt_bias,
                                                    beta_logit, initial_state, o, final_state,
                                                    static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+}
+
+int64_t gdr_chunk_fwd_fused_prep_workspace_size(int64_t B, int64_t H, int64_t T, int d_k, int d_v) {
+    if (B < 0 || H < 0 || T < 0 || T > kMaxT) return -1;
+    if (check_common(d_k, d_v, GDR_BF16, GDR_GATE_SCALAR) != GDR_OK) return -1;
+    int64_t BH, x;
+    if (!mul_ok(B, H, &BH) || !mul_ok(BH, T + kChunkLen, &x) || !mul_ok(x, 4 * kChunkLen, &x)) return -1;
+    return gdr::chunk_split_prep_workspace_bytes(BH, T, d_k);
+}
+
+gdr_status gdr_chunk_fwd_fused_prep_ws(int64_t B, int64_t H, int64_t T, int d_k, int d_v, int io_dtype,
+                                       const void* q_raw, const void* k_raw, const void* v, const float* dt,
+                                       const float* A_log, const float* dt_bias, const float* beta_logit,
+                                       const float* initial_state, void* o, float* final_state, void* workspace,
+                                       int64_t workspace_bytes, void* stream) {
+    int64_t BH = 0;
+    bool launch = false;
+    gdr_status s = check_prep(B, H, T, d_k, d_v, io_dtype, q_raw, k_raw, v, dt, A_log, dt_bias, beta_logit,
+                              initial_state, o, final_state, &BH, &launch);
+    if (s != GDR_OK) return s;
+    if (workspace_bytes < 0) return GDR_ERR_INVALID_ARG;
+    const int64_t need = gdr_chunk_fwd_fused_prep_workspace_size(B, H, T, d_k, d_v);
+    if (need < 0) return GDR_ERR_SHAPE;
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return GDR_ERR_INVALID_ARG;
+    if (need > 0) {
+        // the workspace is written by the first kernel: it may overlap no input and no output
+        const int64_t BHT = BH * T;
+        if (overlaps(workspace, need, q_raw, BHT * d_k * 2) || overlaps(workspace, need, k_raw, BHT * d_k * 2) ||
+            overlaps(workspace, need, v, BHT * d_v * 2) || overlaps(workspace, need, dt, BHT * 4) ||
+            overlaps(workspace, need, beta_logit, BHT * 4) || overlaps(workspace, need, A_log, H * 4) ||
+            overlaps(workspace, need, dt_bias, H * 4) || overlaps(workspace, need, o, BHT * d_v * 2) ||
+            overlaps(workspace, need, initial_state, BH * d_k * d_v * 4) ||
+            overlaps(workspace, need, final_state, BH * d_k * d_v * 4))
+            return GDR_ERR_INVALID_ARG;
+    }
+    if (!launch) return GDR_OK;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (need > 0)
+        e = gdr::chunk_split_prep_dispatch(BH, H, T, d_k, d_v, q_raw, k_raw, v, dt, A_log, dt_bias, beta_logit,
+                                           initial_state, o, final_state, workspace, st);
+    else
+        e = gdr::chunk_fwd_pc_prep_dispatch(BH, H, T, d_k, d_v, q_raw, k_raw, v, dt, A_log, dt_bias, beta_logit,
+                                            initial_state, o, final_state, st);
     return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
 }
 

@@ -176,6 +176,34 @@ gdr_status gdr_chunk_fwd_fused_prep(int64_t B, int64_t H, int64_t T, int d_k, in
                                     void *o, float *final_state, void *stream);
 
 /*
+ * gdr_chunk_fwd_fused_prep_workspace_size -- bytes of device workspace
+ * gdr_chunk_fwd_fused_prep_ws needs, per sequence and 64-token chunk, 16960 + 256 d_k bytes
+ * (49728 for d_k = 128, 33344 for d_k = 64); -1 for sizes gdr_chunk_fwd_fused_prep would
+ * reject.
+ */
+int64_t gdr_chunk_fwd_fused_prep_workspace_size(int64_t B, int64_t H, int64_t T, int d_k, int d_v);
+
+/*
+ * gdr_chunk_fwd_fused_prep_ws -- gdr_chunk_fwd_fused_prep with a caller-provided workspace.
+ *
+ * Same inputs, outputs and errors as gdr_chunk_fwd_fused_prep, on the two-kernel path of
+ * gdr_chunk_fwd_ws: the UT kernel normalises q and k (q / max(||q||, 1e-6), in fp32 before the
+ * fp16 rounding), forms beta and g from their raw inputs, and writes, besides T, A and the
+ * decay factors, the normalised q and k rows in fp16; the state kernel reads those instead of
+ * the raw inputs.
+ *
+ *   workspace, workspace_bytes   as for gdr_chunk_fwd_ws (must not overlap any input or output)
+ */
+gdr_status gdr_chunk_fwd_fused_prep_ws(int64_t B, int64_t H, int64_t T, int d_k, int d_v,
+                                       int io_dtype,
+                                       const void *q_raw, const void *k_raw, const void *v,
+                                       const float *dt, const float *A_log, const float *dt_bias,
+                                       const float *beta_logit,
+                                       const float *initial_state,
+                                       void *o, float *final_state,
+                                       void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
  * gdr_gdp_chunk_fwd -- chunkwise forward pass of the Gated Delta Product.
  *
  * "Linear Attention, Visualized", section "Gated Delta Product (GDP)": each token t carries

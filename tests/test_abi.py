@@ -265,6 +265,32 @@ def test_fused_prep_rejects(lib, kw, status):
     assert prep(lib, **kw) == status
 
 
+def prep_ws(lib, B=1, H=1, T=64, dk=128, dv=128, io=0, q=FAKE, k=FAKE, v=FAKE, dt=FAKE, A=FAKE, bias=FAKE,
+            bl=FAKE, s0=None, o=FAKE2, sf=None, ws=ctypes.c_void_p(0x50000000), nbytes=1 << 20):
+    return lib.gdr_chunk_fwd_fused_prep_ws(B, H, T, dk, dv, io, q, k, v, dt, A, bias, bl, s0, o, sf, ws, nbytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), INVALID), (dict(dk=32), SHAPE), (dict(io=1), UNSUP), (dict(A=None), INVALID),
+    (dict(o=FAKE), INVALID),
+    (dict(ws=None), INVALID),                                   # a workspace is required
+    (dict(nbytes=49727), INVALID),                              # one chunk needs 49728 bytes
+    (dict(nbytes=-1), INVALID),
+    (dict(ws=FAKE), INVALID), (dict(ws=FAKE2), INVALID),        # workspace overlaps q_raw / o
+    (dict(T=(1 << 22) + 1), SHAPE),
+])
+def test_fused_prep_ws_rejects(lib, kw, status):
+    assert prep_ws(lib, **kw) == status
+
+
+def test_fused_prep_workspace_size(lib):
+    n = lib.gdr_chunk_fwd_fused_prep_workspace_size
+    assert n(4, 16, 4096, 128, 128) == 64 * 64 * 49728
+    assert n(1, 2, 65, 64, 64) == 2 * 2 * 33344
+    assert n(1, 1, 0, 128, 128) == 0
+    assert n(-1, 1, 64, 128, 128) == -1 and n(1, 1, 64, 96, 128) == -1
+
+
 def test_fused_prep_empty_batch_is_a_noop(lib):
     assert prep(lib, B=0) == OK
     assert prep(lib, T=0, q=None, k=None, v=None, dt=None, bl=None, o=None) == OK

@@ -11,7 +11,7 @@ import pytest
 
 import gdr_synth
 import oracle
-from parity import TOL_BF16, err_bf16_out, report
+from parity import TOL_BF16, err_bf16_out, err_literal, report
 
 pytestmark = pytest.mark.gpu
 
@@ -57,6 +57,9 @@ def check(name, o, S, o_ref, S_ref):
     assert eo <= TOL_BF16 and es <= TOL_BF16, msg
 
 
+PATHS = {"split": "auto", "single": None}
+
+
 def state(seed, B, H, dv, dk, std=0.05):
     return (np.random.default_rng(seed).standard_normal((B, H, dv, dk)) * std).astype(np.float32)
 
@@ -64,12 +67,13 @@ def state(seed, B, H, dv, dk, std=0.05):
 @pytest.mark.parametrize("T", [1, 37, 64, 65, 200])
 @pytest.mark.parametrize("dk,dv", [(128, 128), (128, 32), (64, 64), (64, 96)])
 @pytest.mark.parametrize("with_s0", [False, True])
-def test_prep_small(T, dk, dv, with_s0):
+@pytest.mark.parametrize("path", sorted(PATHS))
+def test_prep_small(T, dk, dv, with_s0, path):
     r = gdr_synth.make_raw_inputs(variant(d_k=dk, d_v=dv), B=2, H=3, T=T, head_params="varied")
     S0 = state(T, 2, 3, dv, dk) if with_s0 else None
-    o, S = run(r, S0)
+    o, S = run(r, S0, workspace=PATHS[path])
     o_ref, S_ref = ref(r, S0)
-    check(f"fused prep T={T} dk={dk} dv={dv} s0={with_s0}", o, S, o_ref, S_ref)
+    check(f"fused prep {path} T={T} dk={dk} dv={dv} s0={with_s0}", o, S, o_ref, S_ref)
 
 
 def test_prep_matches_unfused_path():
@@ -87,7 +91,8 @@ def test_prep_matches_unfused_path():
     assert err_bf16_out(host(o), host(o2)) <= TOL_BF16
 
 
-def test_prep_zero_and_large_raw_vectors():
+@pytest.mark.parametrize("path", sorted(PATHS))
+def test_prep_zero_and_large_raw_vectors(path):
     """Zero raw q / k rows give zero vectors (as the oracle's eps rule); raw magnitudes of
     10^3 normalise exactly like unit-scale ones."""
     r = gdr_synth.make_raw_inputs(variant(), B=1, H=2, T=130, head_params="varied")
@@ -97,16 +102,17 @@ def test_prep_zero_and_large_raw_vectors():
     r["q_raw"][0, 0, 20:30] *= 1e-3
     r["k_raw"] = gdr_synth.round_to_bf16(r["k_raw"])
     r["q_raw"] = gdr_synth.round_to_bf16(r["q_raw"])
-    o, S = run(r)
+    o, S = run(r, workspace=PATHS[path])
     o_ref, S_ref = ref(r)
-    check("fused prep, zero and scaled rows", o, S, o_ref, S_ref)
+    check(f"fused prep {path}, zero and scaled rows", o, S, o_ref, S_ref)
 
 
-def test_prep_full_size_sampled():
+@pytest.mark.parametrize("path", sorted(PATHS))
+def test_prep_full_size_sampled(path):
     """B=4, H=16, T=4096, d=128 from raw projections; 4 of the 64 sequences checked."""
     w = gdr_synth.WORKLOADS[2]
     r = gdr_synth.make_raw_inputs(w, head_params="varied")
-    o, S = run(r)
+    o, S = run(r, workspace=PATHS[path])
     pick = np.array([3, 22, 41, 60])
     bi, hi = pick // w.H, pick % w.H
     sub = {kk: r[kk][bi, hi][None] for kk in ("q_raw", "k_raw", "v", "dt", "beta_logit")}
@@ -115,7 +121,7 @@ def test_prep_full_size_sampled():
     o_ref, S_ref = oracle.recurrent_forward(q, k, sub["v"], g, beta)
     o_s = o[torch.from_numpy(bi), torch.from_numpy(hi)][None]
     S_s = S[torch.from_numpy(bi), torch.from_numpy(hi)][None]
-    check("fused prep full size (4 sampled heads)", o_s, S_s, o_ref, S_ref)
+    check(f"fused prep full size, {path} (4 sampled heads)", o_s, S_s, o_ref, S_ref)
 
 
 def test_prep_carried_state_split():
@@ -138,3 +144,21 @@ def test_prep_empty_sequence_copies_state():
     S0 = state(4, 1, 2, 128, 128)
     o, S = run(r, S0)
     assert o.numel() == 0 and torch.equal(S.cpu(), torch.from_numpy(S0))
+
+
+def test_prep_split_equals_single_closely():
+    """The two paths normalise with the same arithmetic (one inverse norm per row, applied in
+    fp32 before the fp16 rounding) and agree within the outputs' bf16 rounding."""
+    r = gdr_synth.make_raw_inputs(variant(), B=2, H=3, T=333, head_params="varied")
+    o1, S1 = run(r, workspace="auto")
+    o2, S2 = run(r, workspace=None)
+    assert err_bf16_out(host(o1), host(o2)) <= TOL_BF16
+    assert err_literal(host(S1), host(S2)) <= TOL_BF16
+
+
+def test_prep_full_grid_small_T():
+    """B=4, H=16: the grid the state pass serves with two consumer waves per workgroup."""
+    r = gdr_synth.make_raw_inputs(variant(), B=4, H=16, T=150, head_params="varied")
+    o, S = run(r)
+    o_ref, S_ref = ref(r)
+    check("fused prep full grid, T=150", o, S, o_ref, S_ref)
