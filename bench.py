@@ -153,11 +153,25 @@ def bench_decode(torch, gdr, gdr_synth, steps=64):
     ms = np.array([a.elapsed_time(b) for a, b in ev])
     nbytes = decode_bytes(w.B, w.H, w.d_k, w.d_v)
     gbs = nbytes / (ms.mean() * 1e-3) / 1e9
+    # context: a device copy of the same state (read once, written once), torch's copy kernel
+    dst = torch.empty_like(state)
+    for _ in range(3):
+        dst.copy_(state)
+    torch.cuda.synchronize()
+    evc = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+    for a_, b_ in evc:
+        a_.record()
+        dst.copy_(state)
+        b_.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * state.numel() * 4 / (float(np.mean([a_.elapsed_time(b_) for a_, b_ in evc])) * 1e-3) / 1e9
     return {"workload": "decode N=256 H=32 d=128 bf16, 64 steps, 512 MiB fp32 state",
             "us_per_step_mean": round(float(ms.mean()) * 1e3, 2), "us_per_step_median": round(float(np.median(ms)) * 1e3, 2),
             "tokens_per_s": round(w.B / (ms.mean() * 1e-3), 1),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM, "unit": "GB/s",
-                         "frac": round(gbs / PEAK_HBM, 4), "traffic": None, "bytes_per_step": nbytes}}
+                         "frac": round(gbs / PEAK_HBM, 4), "traffic": None, "bytes_per_step": nbytes},
+            "copy_of_the_state_gbs": round(copy_gbs, 1),
+            "frac_of_copy_rate": round(gbs / copy_gbs, 4)}
 
 
 def bench_gdp(torch, gdr, gdr_synth, steps=10):

@@ -329,3 +329,36 @@ def test_prefill_then_decode_handoff():
         torch.cuda.synchronize()
         assert err_bf16_out(host(od), o_ref) <= TOL_BF16
     assert err_literal(host(S), ref) <= TOL_BF16
+
+
+# ----------------------------------------------------------------------------- full grid, d_k = 64
+@pytest.mark.parametrize("mode", ["gdn", "kda", "gdn2", "gdp", "prep"])
+def test_two_kernel_modes_full_grid_dk64(mode):
+    """B=4, H=16, d_k=64, d_v=128: 256 value tiles of 32 channels, so every two-kernel mode runs
+    its two-consumer-wave state kernel at d_k = 64; every sequence checked against the oracle."""
+    B, H, T = 4, 16, 100
+    if mode in ("gdn", "kda"):
+        x = gdr_synth.make_inputs(variant(2 if mode == "gdn" else 3, d_k=64, d_v=128), B=B, H=H, T=T)
+        o, S = run_chunk(x, True)
+        o_ref, S_ref = oracle.recurrent_forward(x["q"], x["k"], x["v"], x["g"], x["beta"])
+    elif mode == "gdn2":
+        x = gdr_synth.make_inputs(variant(7, d_k=64, d_v=128), B=B, H=H, T=T)
+        o, S = gdr.gdn2_chunk_fwd(dev(x["q"], True), dev(x["k"], True), dev(x["v"], True), dev(x["g"]), dev(x["b"]),
+                                  dev(x["w"]))
+        torch.cuda.synchronize()
+        o_ref, S_ref = oracle.gdn2_forward(x["q"], x["k"], x["v"], x["g"], x["b"], x["w"])
+    elif mode == "gdp":
+        x = gdr_synth.make_inputs(variant(6, d_k=64, d_v=128, nh=2), B=B, H=H, T=T // 2)
+        o, S = gdr.gdp_chunk_fwd(dev(x["q"], True), dev(x["k"], True), dev(x["v"], True), dev(x["g"]),
+                                 dev(x["beta"]))
+        torch.cuda.synchronize()
+        o_ref, S_ref = oracle.gdp_forward(x["q"], x["k"], x["v"], x["g"], x["beta"])
+    else:
+        r = gdr_synth.make_raw_inputs(variant(2, d_k=64, d_v=128), B=B, H=H, T=T, head_params="varied")
+        o, S = gdr.chunk_fwd_fused_prep(dev(r["q_raw"], True), dev(r["k_raw"], True), dev(r["v"], True),
+                                        dev(r["dt"]), dev(r["A_log"]), dev(r["dt_bias"]), dev(r["beta_logit"]))
+        torch.cuda.synchronize()
+        q, k, g, beta = oracle.prepare_inputs(r["q_raw"], r["k_raw"], r["dt"], r["A_log"], r["dt_bias"],
+                                              r["beta_logit"])
+        o_ref, S_ref = oracle.recurrent_forward(q, k, r["v"], g, beta)
+    check(f"{mode} full grid d_k=64", o, S, o_ref, S_ref, True)
