@@ -551,7 +551,9 @@ __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const St
                 R.wr[2 * u + 1] = bld16(rwg, ((t0 + row) * DV + dv0 + col) * 4 + 16);
             }
         }
-        if (lt < NFQ) R.fr = bld16(rw, (wb + (KDA ? WFE : kGdnWsFactors)) * 2 + lt * 16);
+        // every loader lane loads (lanes past the table read past the buffer end: zeros), so
+        // that no branch hides a load from the compiler's count of loads in flight
+        R.fr = bld16(rw, lt < NFQ ? (wb + (KDA ? WFE : kGdnWsFactors)) * 2 + lt * 16 : (uint32_t)(nC * WS * 2));
     };
     // o of chunk c from its O^T buffer: loader wave lw takes rows (value channels) 16 lw ..,
     // a lane reads 8 consecutive channels of one token back transposed and stores 16 bytes
@@ -635,13 +637,16 @@ __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const St
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) Sb[kb] = pack8(St[2 * kb], St[2 * kb + 1]);
 
-    // chunk k's loads live in register set k mod 2
+    // Chunk k's loads live in register set k mod 2.  Loads of chunks past the end are issued
+    // anyway (they read past the buffers' ends, which returns zeros, and are staged into a
+    // buffer no consumer reads): with no branch around them the compiler can count the loads
+    // in flight exactly, and waits for one set while the other stays in flight.
     if (!consumer && nC > 0) {
         issue(R0, 0);
         convert(R0);
         stage(R0, 0);
-        if (nC > 1) issue(R1, 1);
-        if (nC > 2) issue(R0, 2);
+        issue(R1, 1);
+        issue(R0, 2);
     }
     lds_barrier();
 
@@ -681,7 +686,7 @@ __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const St
         const int bc = (int)(c & 1);
         if constexpr (KDA) {
             tsink ^= tch;
-            if (c + 3 < nC) touch(c + 3);
+            touch(c + 3);
         }
         {
             const _Float16* Kc = Kb(bc);
@@ -830,7 +835,7 @@ __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const St
                     for (int ti = 0; ti < 4; ++ti) mma16(PQ[ti], cur[ti], Sb[kb]);
                 }
             }
-            if (c + 1 < nC) issue_qg(c + 1);
+            issue_qg(c + 1);  // past the end: zeros, unused (no branch: see the loaders)
             float4v Oa[4];
 #pragma unroll
             for (int ti = 0, n = 0; ti < 4; ++ti) {
@@ -854,21 +859,27 @@ __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const St
         asm volatile("" ::"v"(tsink));  // keeps the touches
     }
     } else {
-    // loaders: o of the previous chunk, the next chunk (set (c+1) mod 2) into LDS, then the
-    // loads of chunk c+3 into the freed set
+    // loaders, step c (one per chunk, as the consumers' barriers): o of chunk c-1, chunk c+1
+    // (set (c+1) mod 2) into LDS, then the loads of chunk c+3 into the freed set
     auto step = [&](LdRegs& R, int64_t c) {
-        if (c > 0) store_o(c - 1);
-        if (c + 1 < nC) {
-            convert(R);
-            stage(R, c + 1);
-            if (c + 3 < nC) issue(R, c + 3);
-        }
+        store_o(c - 1);
+        convert(R);
+        stage(R, c + 1);
+        issue(R, c + 3);
         lds_barrier();
     };
-    for (int64_t c = 0; c < nC; c += 2) {
-        step(R1, c);
-        if (c + 1 < nC) step(R0, c + 1);
+    if (nC > 0) {  // step 0 has no o to store
+        convert(R1);
+        stage(R1, 1);
+        issue(R1, 3);
+        lds_barrier();
     }
+    int64_t c = 1;
+    for (; c + 1 < nC; c += 2) {
+        step(R0, c);
+        step(R1, c + 1);
+    }
+    if (c < nC) step(R0, c);
     if (nC > 0) store_o(nC - 1);
     }
 
