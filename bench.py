@@ -32,7 +32,7 @@ PEAK_MFMA_F16 = 2500.0  # TFLOP/s, MI355X dense fp16/bf16
 PEAK_HBM = 8000.0       # GB/s, MI355X HBM3E
 # the headline step: one gdr_chunk_fwd_ws call = the UT kernel over all chunks, then the
 # chunk-serial state kernel
-CHUNK_KERNEL = "chunk_ut_kernel<128> + chunk_state_kernel<128, 0, 2>"
+CHUNK_KERNEL = "chunk_ut_kernel<128, 0> + chunk_state_kernel<128, 0, 2>"
 CHUNK_SOURCE = os.path.join(ROOT, "gated_delta_rule_15_amd", "csrc", "chunk_split.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "chunk_split_gdn_bf16_B4_H16_T4096_traffic.json")
 COPY_BYTES = 256 << 20  # calibration copy for the HBM byte counters
@@ -198,7 +198,7 @@ def bench_gdp(torch, gdr, gdr_synth, steps=10):
     qt, kt, vt, gt, bt, keep = oracle.gdp_as_virtual_gdn(sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"])
     o_ref, S_ref = oracle.recurrent_forward(qt, kt, vt, gt, bt)
     res = {"workload": "gdp_bf16: Gated Delta Product B=4 H=16 T=2048 n_h=2 d_k=d_v=128 bf16, zero S0",
-           "kernel": "chunk_ut_kernel<128, true> + chunk_state_kernel<128, 3, 2>", "ms_per_call": round(ms, 4),
+           "kernel": "chunk_ut_kernel<128, 1> + chunk_state_kernel<128, 3, 2>", "ms_per_call": round(ms, 4),
            "ms_per_call_median": round(med, 4),
            "single_kernel": {"kernel": "chunk_fwd_pc_kernel<128, 1>", "ms_per_call": round(ms_single, 4)},
            "tokens_per_s": round(w.B * w.T / (ms * 1e-3), 1),
