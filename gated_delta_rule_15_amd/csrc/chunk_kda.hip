@@ -86,7 +86,19 @@ struct KdaLds {
     static constexpr int LDG = DK + 4;   // floats, rows of the block-local cumulative log-decay
     static constexpr int szK = C * LDK * 2;
     static constexpr int szC = C * LDC * 2;
-    static constexpr int oKr = 0;                     // K e^{G - G_start(blk)}, then K e^G
+    // The per-chunk tables come first: the Gram stage reads them every few instructions, and
+    // below 64 KiB an LDS address folds into the instruction's 16-bit offset instead of taking
+    // a register of its own.  Tables are fp32 in natural channel order unless noted.
+    static constexpr int oFB = 0;                     // beta [C]
+    static constexpr int oFDl = oFB + C * 4;          // Delta_b = G_loc(15) of block b [4][DK]
+    static constexpr int oFE = oFDl + 4 * DK * 4;     // e^{G_C} [DK]
+    static constexpr int oHD = oFE + DK * 4;          // fp16: d-factors [3][DK]
+    static constexpr int oHMR = oHD + 3 * DK * 2;     // fp16: e^{-G_loc(8)} [4][DK]
+    static constexpr int oHMC = oHMR + 4 * DK * 2;    // fp16: e^{G_loc(8) - Delta_b} [4][DK]
+    static constexpr int oHP = oHMC + 4 * DK * 2;     // fp16: e^{G_start(b)} [4][DK]
+    static constexpr int oHS = oHP + 4 * DK * 2;      // fp16: e^{G_C - G_end(b)} [4][DK]
+    static constexpr int oFlag = oHS + 4 * DK * 2;    // int [4]: block needs the bf16 diagonal path
+    static constexpr int oKr = oFlag + 16;            // K e^{G - G_start(blk)}, then K e^G
     static constexpr int oQr = oKr + szK;             // Q e^{G - G_start(blk)}, then Q e^G
     static constexpr int oKc = oQr + szK;             // K e^{G_end(blk) - G}, then K e^{G_C - G}
     static constexpr int oAt = oKc + szK;             // A^T
@@ -96,19 +108,9 @@ struct KdaLds {
     static constexpr int oGl = oNd + 4 * 16 * LDN * 4;  // block-local cumulative log-decay [C][LDG]
     static constexpr int oVt = oGl + C * LDG * 4;     // V^T fp32 [32][LDV]
     static constexpr int oOt = oVt + 32 * LDV * 4;    // O^T bf16 [32][LDO]
-    // per-chunk tables (fp32 natural channel order unless noted)
-    static constexpr int oFB = oOt + 32 * LDO * 2;    // beta [C]
-    static constexpr int oFDl = oFB + C * 4;          // Delta_b = G_loc(15) of block b [4][DK]
-    static constexpr int oFE = oFDl + 4 * DK * 4;     // e^{G_C} [DK]
-    static constexpr int oHD = oFE + DK * 4;          // fp16: d-factors [3][DK]
-    static constexpr int oHMR = oHD + 3 * DK * 2;     // fp16: e^{-G_loc(8)} [4][DK]
-    static constexpr int oHMC = oHMR + 4 * DK * 2;    // fp16: e^{G_loc(8) - Delta_b} [4][DK]
-    static constexpr int oHP = oHMC + 4 * DK * 2;     // fp16: e^{G_start(b)} [4][DK]
-    static constexpr int oHS = oHP + 4 * DK * 2;      // fp16: e^{G_C - G_end(b)} [4][DK]
-    static constexpr int oFlag = oHS + 4 * DK * 2;    // int [4]: block needs the bf16 diagonal path
-    static constexpr int total = oFlag + 16;
+    static constexpr int total = oOt + 32 * LDO * 2;
     static_assert(total <= 160 * 1024, "LDS budget of one gfx950 CU exceeded");
-    static_assert((oAt | oNt | oXd | oNd | oGl | oVt | oOt | oFB | oFDl | oFE | oHD | oHMR | oHMC |
+    static_assert((oKr | oAt | oNt | oXd | oNd | oGl | oVt | oOt | oFDl | oFE | oHD | oHMR | oHMC |
                    oHP | oHS | oFlag) % 16 == 0,
                   "alignment");
 };
@@ -150,7 +152,7 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
     _Float16* HS = reinterpret_cast<_Float16*>(smem + L::oHS);
     int* Flag = reinterpret_cast<int*>(smem + L::oFlag);
 
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, j = l & 15, g = l >> 4;
+    const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, j = l & 15, g = l >> 4;
     const int64_t T = a.T;
     const int64_t nC = (T + C - 1) / C;
     // state pass: one group per (sequence, 32 value channels) over all chunks; UT: one group per
@@ -205,14 +207,19 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
     float bp = 0.0f;
     // token t of the lane's block (g, k, q of its channel pair); t = 0 also brings V, beta.
     // Past the sequence end the loads return zeros (identity tokens).
+    // The token's element offset is formed as a wave-uniform value the compiler cannot split, so
+    // the address is one add to the lane's channel offset, not one of 16 registers held
+    // through the loop.
     auto issue_tok = [&](int64_t c, int t) {
-        const uint32_t t0 = (uint32_t)(c * C) + 16 * w;
-        const uint2 u = bld8(rg, ((t0 + t) * DK + ch2) * 4);
+        uint32_t tb = ((uint32_t)(c * C) + 16 * w + t) * DK;
+        asm volatile("" : "+s"(tb));
+        const uint32_t e = tb + ch2;
+        const uint2 u = bld8(rg, e * 4);
         gp[t] = float2{__uint_as_float(u.x), __uint_as_float(u.y)};
-        kp[t] = __builtin_amdgcn_raw_buffer_load_b32(rk, ((t0 + t) * DK + ch2) * 2, 0, 0);
-        qp[t] = __builtin_amdgcn_raw_buffer_load_b32(rq, ((t0 + t) * DK + ch2) * 2, 0, 0);
+        kp[t] = __builtin_amdgcn_raw_buffer_load_b32(rk, e * 2, 0, 0);
+        qp[t] = __builtin_amdgcn_raw_buffer_load_b32(rq, e * 2, 0, 0);
         if constexpr (GD2) {
-            const uint2 ue = bld8(re, ((t0 + t) * DK + ch2) * 4);
+            const uint2 ue = bld8(re, e * 4);
             ep[t] = float2{__uint_as_float(ue.x), __uint_as_float(ue.y)};
         }
         if (t == 0) {
@@ -225,7 +232,7 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
                     wp1 = bld16(rw, vidx * 4 + 16);
                 }
             } else {
-                if (w == 0) bp = bld4(rb, (tc + l) * 4);
+                bp = bld4(rb, (tc + l) * 4);  // every wave: a load under a branch costs a full wait
             }
         }
     };
@@ -386,9 +393,10 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
         // The next chunk's loads are issued between this stage's MFMAs (a token of the block
         // per step), so the memory queue drains while the matrix pipe works.
         const int64_t cn = c + 1 < c_last ? c + 1 : c;  // reloading the last chunk is harmless
-        auto gram_kda = [&](auto hc, auto qc) {
+        auto gram_kda = [&](auto hc, auto qc, auto bc) {
             constexpr int h = decltype(hc)::value;
             constexpr bool isQ = decltype(qc)::value;
+            constexpr bool BF = decltype(bc)::value;  // some diagonal block of the wave needs bf16
             const _Float16* Rs = isQ ? Qr : Kr;
             constexpr int NT = 5;
             constexpr int ti_[2][NT] = {{0, 1, 1, 2, 3}, {2, 2, 3, 3, 3}};
@@ -401,6 +409,51 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
             int fl[4];
 #pragma unroll
             for (int b = 0; b < 4; ++b) fl[b] = __builtin_amdgcn_readfirstlane(Flag[b]);
+            if constexpr (!BF) {
+                // every diagonal tile on fp16: the operands of reduction block kb + 1 are read
+                // from LDS while the MFMAs of block kb run (two register sets), and their factors
+                // applied after them
+                half8 oa[2][NT], ob[2][NT], fa[2][NT], fb[2][NT];
+                auto read_kb = [&](int kb, half8* ra, half8* rb, half8* ha, half8* hb) {
+#pragma unroll
+                    for (int t = 0; t < NT; ++t) {
+                        const int ti = ti_[h][t], tj = tj_[h][t], cf = cf_[h][t];
+                        ra[t] = rfrag(Rs, ti, kb);
+                        rb[t] = rfrag(Kc, tj, kb);
+                        if (cf == 3) {
+                            ha[t] = hfrag(HMR, ti, kb);
+                            hb[t] = hfrag(HMC, ti, kb);
+                        } else if (cf >= 0) {
+                            hb[t] = hfrag(HD, cf, kb);
+                        }
+                    }
+                };
+                auto scale_kb = [&](half8* ra, half8* rb, const half8* ha, const half8* hb) {
+#pragma unroll
+                    for (int t = 0; t < NT; ++t) {
+                        const int cf = cf_[h][t];
+                        if (cf == 3) ra[t] = hmul8(ra[t], ha[t]);
+                        if (cf >= 0) rb[t] = hmul8(rb[t], hb[t]);
+                    }
+                };
+                read_kb(0, oa[0], ob[0], fa[0], fb[0]);
+                scale_kb(oa[0], ob[0], fa[0], fb[0]);
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) {
+                    const int cur = kb & 1, nxt = cur ^ 1;
+                    if (kb + 1 < NKB) read_kb(kb + 1, oa[nxt], ob[nxt], fa[nxt], fb[nxt]);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int t = 0; t < NT; ++t) {
+                        mma16(acc[t], oa[cur][t], ob[cur][t]);
+                        if (t < 16 / NKB) issue_tok(cn, kb * (16 / NKB) + t);
+                    }
+#pragma unroll
+                    for (int u = NT; u < 16 / NKB; ++u) issue_tok(cn, kb * (16 / NKB) + u);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (kb + 1 < NKB) scale_kb(oa[nxt], ob[nxt], fa[nxt], fb[nxt]);
+                }
+            } else {
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
@@ -409,7 +462,7 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
                     const half8 A = rfrag(Rs, ti, kb);
                     half8 B = rfrag(Kc, tj, kb);
                     if (cf == 3) {
-                        if (fl[ti]) {
+                        if (BF && fl[ti]) {
                             mma16_bf16(acc[t], diag_bf16(isQ ? rq : rk, c, ti, kb, true, GD2 && !isQ),
                                        diag_bf16(rk, c, ti, kb, false, false));
                         } else {
@@ -423,6 +476,7 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
                 }
 #pragma unroll
                 for (int u = NT; u < 16 / NKB; ++u) issue_tok(cn, kb * (16 / NKB) + u);
+            }
             }
             // epilogue: beta of the row for N (not for GD2: e carries the gate), causal masks
 #pragma unroll
@@ -454,24 +508,29 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
                 }
             }
         };
-        if (w == 0) gram_kda(std::integral_constant<int, 0>{}, std::false_type{});
-        else if (w == 1) gram_kda(std::integral_constant<int, 1>{}, std::false_type{});
-        else if (w == 2) gram_kda(std::integral_constant<int, 0>{}, std::true_type{});
-        else gram_kda(std::integral_constant<int, 1>{}, std::true_type{});
+        // UT: the test for the bf16 diagonal path is taken once per wave, so the usual all-fp16
+        // case runs as straight-line code (a branch inside the loop serialises its LDS reads).
+        // The state pass keeps the per-block test (two copies of the loop exceed its registers).
+        auto gram_wave = [&](auto hc, auto qc) {
+            constexpr int h = decltype(hc)::value;
+            if (!UT || __builtin_amdgcn_readfirstlane(Flag[2 * h] | Flag[2 * h + 1]))
+                gram_kda(hc, qc, std::true_type{});
+            else
+                gram_kda(hc, qc, std::false_type{});
+        };
+        if (w == 0) gram_wave(std::integral_constant<int, 0>{}, std::false_type{});
+        else if (w == 1) gram_wave(std::integral_constant<int, 1>{}, std::false_type{});
+        else if (w == 2) gram_wave(std::integral_constant<int, 0>{}, std::true_type{});
+        else gram_wave(std::integral_constant<int, 1>{}, std::true_type{});
         lds_barrier();
 
-        // UT: T is staged where the block-local log-decay was (dead after the Gram tiles)
-        _Float16* Tt = reinterpret_cast<_Float16*>(smem + L::oGl);
-        if (UT) {
-            for (int i = tid; i < C * L::LDC / 8; i += 256)
-                reinterpret_cast<uint4*>(Tt)[i] = uint4{0u, 0u, 0u, 0u};
-            lds_barrier();
-        }
-        // ============ S4: diagonal inverses (waves 0-1, two blocks each); the copies are
-        // rescaled in place for the state pass (waves 2-3) ============
-        if (w < 2) {
-            // column-oriented forward substitution: lane (block, jc) builds column jc of
-            // X_bb = N_bb^{-1}; stored as X_bb^T (row jc = column jc)
+        // Diagonal inverses (waves 0-1, two blocks each): column-oriented forward substitution,
+        // lane (block, jc) builds column jc of X_bb = N_bb^{-1}, stored as X_bb^T (row jc =
+        // column jc).  The UT pass also writes the diagonal block of T = N^{-1} diag(beta)
+        // (GD2: N^{-1}, e carries the gate) to Tt, which takes the place of V^T and O^T (unused
+        // there).
+        _Float16* Tt = reinterpret_cast<_Float16*>(smem + L::oVt);
+        auto diag_inverse = [&]() {
             const int b = 2 * w + ((l >> 4) & 1), jc = j;
             const float* nb = Nd + b * 16 * L::LDN;
             float4v nr[15][4];
@@ -500,35 +559,39 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
                 }
                 *reinterpret_cast<half8*>(Xd + (16 * b + jc) * L::LDX) = h0;
                 *reinterpret_cast<half8*>(Xd + (16 * b + jc) * L::LDX + 8) = h1;
-                if (UT) {  // diagonal block of T = N^{-1} diag(beta) (GD2: N^{-1}, e carries the gate)
+                if constexpr (UT) {
                     const float bc = GD2 ? 1.0f : FB[16 * b + jc];
                     const int pc = pperm(16 * b + jc);
 #pragma unroll
                     for (int i = 0; i < 16; ++i) Tt[(16 * b + i) * L::LDC + pc] = (_Float16)(xd[i] * bc);
                 }
             }
-        }
-        {
-            // Kr -> K e^G, Qr -> Q e^G (factor e^{G_start(blk)}), Kc -> K e^{G_C - G}
-            // (factor e^{G_C - G_end(blk)}); 16-byte groups of the rows.  Waves 2-3 take the
-            // first three quarters, waves 0-1 (after their inverses) the last quarter.
-            constexpr int NG = C * (DK / 8);  // 16-byte groups per copy
-            const int i0 = w >= 2 ? tid - 128 : 3 * NG / 4 + tid;
-            const int i1 = w >= 2 ? 3 * NG / 4 : NG;
-            for (int i = i0; i < i1; i += 128) {
-                const int row = i / (DK / 8), col = (i % (DK / 8)) * 8, blk = row >> 4;
-                const half8 fp = ld8(HP + blk * DK + col), fs = ld8(HS + blk * DK + col);
-                half8* pk = reinterpret_cast<half8*>(Kr + row * L::LDK + col);
-                half8* pq = reinterpret_cast<half8*>(Qr + row * L::LDK + col);
-                half8* pc = reinterpret_cast<half8*>(Kc + row * L::LDK + col);
-                *pk = hmul8(*pk, fp);
-                *pq = hmul8(*pq, fp);
-                *pc = hmul8(*pc, fs);
-            }
-        }
-        lds_barrier();
+        };
 
         if constexpr (UT) {
+            // The chunk's operands go to the workspace in 16-byte pieces, spread over the last
+            // stages: waves 2-3 write K e^G and Q e^G while waves 0-1 invert the diagonal blocks,
+            // then K e^{G_C - G} while waves 0-1 form the blocks below the diagonal; all waves
+            // then write A^T, T and e^{G_C}.  The copies are rescaled on the way out (per block
+            // and channel: e^{G_start(blk)} for Kr and Qr, e^{G_C - G_end(blk)} for Kc).
+            uint16_t* dst = a.ws + (bh * nC + c) * (int64_t)kda_ws_stride<DK>();
+            constexpr int NG = C * (DK / 8);  // 16-byte pieces per copy
+            auto copy_scaled = [&](const _Float16* src, const _Float16* H, uint16_t* d) {
+#pragma unroll
+                for (int u = 0; u < NG / 128; ++u) {
+                    const int i = tid - 128 + 128 * u;
+                    const int row = i / (DK / 8), col = (i % (DK / 8)) * 8;
+                    *reinterpret_cast<half8*>(d + row * DK + col) =
+                        hmul8(ld8(src + row * L::LDK + col), ld8(H + (row >> 4) * DK + col));
+                }
+            };
+            if (w < 2) {
+                diag_inverse();
+            } else {
+                copy_scaled(Kr, HP, dst + 2 * C * C);
+                copy_scaled(Qr, HP, dst + 2 * C * C + C * DK);
+            }
+            lds_barrier();
             // blocks of N^{-1} below the diagonal, column block by column block (wave 0: column
             // 0, wave 1: columns 1 and 2): M_bc = -X_bb sum_{d=c}^{b-1} N_bd M_dc, then
             // T_bc = M_bc diag(beta_c)
@@ -563,25 +626,48 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
             } else if (w == 1) {
                 column(std::integral_constant<int, 1>{});
                 column(std::integral_constant<int, 2>{});
+            } else {
+                copy_scaled(Kc, HS, dst + 2 * C * C + 2 * C * DK);
             }
             lds_barrier();
-            // the chunk's operands to the workspace, 16-byte pieces
-            uint16_t* dst = a.ws + (bh * nC + c) * (int64_t)kda_ws_stride<DK>();
-            for (int i = tid; i < C * C / 8; i += 256) {
+            // A^T and T.  T's blocks above the diagonal are zero and are not staged: of a piece
+            // at column position col, the first four values lie in column block 2 (col / 32),
+            // the last four in the next one.
+#pragma unroll
+            for (int u = 0; u < C * C / 8 / 256; ++u) {
+                const int i = tid + 256 * u;
                 const int row = i / (C / 8), col = (i % (C / 8)) * 8;
                 *reinterpret_cast<uint4*>(dst + row * C + col) = *reinterpret_cast<const uint4*>(At + row * L::LDC + col);
-                *reinterpret_cast<uint4*>(dst + C * C + row * C + col) =
-                    *reinterpret_cast<const uint4*>(Tt + row * L::LDC + col);
-            }
-            for (int i = tid; i < C * DK / 8; i += 256) {
-                const int row = i / (DK / 8), col = (i % (DK / 8)) * 8;
-                uint16_t* d0 = dst + 2 * C * C + row * DK + col;
-                *reinterpret_cast<uint4*>(d0) = *reinterpret_cast<const uint4*>(Kr + row * L::LDK + col);
-                *reinterpret_cast<uint4*>(d0 + C * DK) = *reinterpret_cast<const uint4*>(Qr + row * L::LDK + col);
-                *reinterpret_cast<uint4*>(d0 + 2 * C * DK) = *reinterpret_cast<const uint4*>(Kc + row * L::LDK + col);
+                uint4 t = *reinterpret_cast<const uint4*>(Tt + row * L::LDC + col);
+                const int rb = row >> 4, cb = 2 * (col >> 5);
+                if (cb > rb) t.x = t.y = 0u;
+                if (cb + 1 > rb) t.z = t.w = 0u;
+                *reinterpret_cast<uint4*>(dst + C * C + row * C + col) = t;
             }
             if (tid < DK) reinterpret_cast<float*>(dst + 2 * C * C + 3 * C * DK)[tid] = FE[tid];
+            // No barrier before the next chunk: its scan and tables write nothing read here, and
+            // Tt is written again only after three more barriers.
         } else {
+        if (w < 2) diag_inverse();
+        {
+            // Kr -> K e^G, Qr -> Q e^G (factor e^{G_start(blk)}), Kc -> K e^{G_C - G}
+            // (factor e^{G_C - G_end(blk)}); 16-byte groups of the rows.  Waves 2-3 take the
+            // first three quarters, waves 0-1 (after their inverses) the last quarter.
+            constexpr int NG = C * (DK / 8);  // 16-byte groups per copy
+            const int i0 = w >= 2 ? tid - 128 : 3 * NG / 4 + tid;
+            const int i1 = w >= 2 ? 3 * NG / 4 : NG;
+            for (int i = i0; i < i1; i += 128) {
+                const int row = i / (DK / 8), col = (i % (DK / 8)) * 8, blk = row >> 4;
+                const half8 fp = ld8(HP + blk * DK + col), fs = ld8(HS + blk * DK + col);
+                half8* pk = reinterpret_cast<half8*>(Kr + row * L::LDK + col);
+                half8* pq = reinterpret_cast<half8*>(Qr + row * L::LDK + col);
+                half8* pc = reinterpret_cast<half8*>(Kc + row * L::LDK + col);
+                *pk = hmul8(*pk, fp);
+                *pq = hmul8(*pq, fp);
+                *pc = hmul8(*pc, fs);
+            }
+        }
+        lds_barrier();
         // ================= S5: state pass of chunk c (waves 0-1) =================
         if (w < 2) {
             // P_K = (K e^G) S^T, P_Q = (Q e^G) S^T
@@ -709,8 +795,8 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) Sb[kb] = pack8(St[2 * kb], St[2 * kb + 1]);
         }
-        }  // state pass
         lds_barrier();
+        }  // state pass
     }
 
     if (!UT && w < 2 && a.Sf != nullptr) {
