@@ -73,17 +73,17 @@ def chunk_transform(K: np.ndarray, g: np.ndarray, beta: np.ndarray):
     return {"T": T, "L": L, "K_left": K_left, "K_right": K_right, "lam_C": lam(1, C), "lam": lam}
 
 
-def _one_chunk(Q, K, V, g, beta, S_row):
-    """Advance S_row over one chunk; returns (O [C, d_v], S_row_next)."""
+def chunk_scores(Q: np.ndarray, K: np.ndarray, g: np.ndarray):
+    """The chunk's local score matrix and decayed queries (row convention).
+
+    A[l, m] = q_l (lam[m+1:l] (.) k_m)^T for m <= l (zero above the diagonal), and Q_left
+    with rows lam[1:l] (.) q_l.  Q, K [C, d_k]; g [C] or [C, d_k]."""
     Q = np.asarray(Q, dtype=np.float64)
-    V = np.asarray(V, dtype=np.float64)
-    C = Q.shape[0]
-    tr = chunk_transform(K, g, beta)
-    lam, T = tr["lam"], tr["T"]
     K = np.asarray(K, dtype=np.float64)
+    lam = _decay_products(np.exp(np.asarray(g, dtype=np.float64)))
+    C = Q.shape[0]
     channel = np.ndim(g) == 2
     Q_left = np.stack([lam(1, l) * Q[l - 1] for l in range(1, C + 1)])
-    # local score matrix A[l, m] = q_l (lam[m+1:l] (.) k_m)^T for m <= l
     A = np.zeros((C, C))
     for l in range(1, C + 1):
         for m in range(1, l + 1):
@@ -91,6 +91,16 @@ def _one_chunk(Q, K, V, g, beta, S_row):
                 A[l - 1, m - 1] = Q[l - 1] @ (lam(m + 1, l) * K[m - 1])
             else:
                 A[l - 1, m - 1] = lam(m + 1, l) * (Q[l - 1] @ K[m - 1])
+    return A, Q_left
+
+
+def _one_chunk(Q, K, V, g, beta, S_row):
+    """Advance S_row over one chunk; returns (O [C, d_v], S_row_next)."""
+    V = np.asarray(V, dtype=np.float64)
+    tr = chunk_transform(K, g, beta)
+    T = tr["T"]
+    channel = np.ndim(g) == 2
+    A, Q_left = chunk_scores(Q, K, g)
     U = T @ V
     W_left = T @ tr["K_left"]
     Z = U - W_left @ S_row

@@ -16,7 +16,7 @@ import numpy as np
 import pytest
 
 import oracle
-from oracle.chunked import chunk_transform, chunked_forward
+from oracle.chunked import chunk_scores, chunk_transform, chunked_forward
 
 TOL = 1e-12
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -374,6 +374,31 @@ def test_p7_wy_ut_product(gate):
     wy = lamC - tr["K_right"].T @ tr["T"] @ tr["K_left"]
     assert np.max(np.abs(Lam - wy)) < 1e-12
     assert np.max(np.abs(H - tr["K_right"].T @ tr["T"] @ V)) < 1e-12
+
+
+@pytest.mark.parametrize("gate", GATES)
+def test_chunk_quantities_closed_forms(gate):
+    """The per-chunk quantities in log space ("Gated DeltaNet (GDN)" and "Reuse GLA and GDN"
+    sections: q_left, k_left, k_right and the decay inside the local scores), written with the
+    inclusive cumulative log-decay G instead of the oracle's products of e^{g}:
+    A[l, m] = sum_c q_lc k_mc e^{G_lc - G_mc} (m <= l), q_left = e^{G} q, k_left = e^{G} k,
+    k_right = e^{G_C - G} k, lam_C = e^{G_C}."""
+    x = rand_inputs(29, B=1, H=1, T=11, dk=6, dv=3, gate=gate, unit_k=False, g_range=(-0.4, -0.01))
+    Q, K, g, beta = x["q"][0, 0], x["k"][0, 0], x["g"][0, 0], x["beta"][0, 0]
+    G = np.cumsum(g, axis=0)
+    Gc = G if gate == "channel" else G[:, None] * np.ones(K.shape[1])
+    C = K.shape[0]
+    A_ref = np.zeros((C, C))
+    for l in range(C):
+        for m in range(l + 1):
+            A_ref[l, m] = np.sum(Q[l] * K[m] * np.exp(Gc[l] - Gc[m]))
+    A, Q_left = chunk_scores(Q, K, g)
+    assert np.max(np.abs(A - A_ref)) / scale(A_ref) < TOL
+    assert np.max(np.abs(Q_left - np.exp(Gc) * Q)) / scale(Q) < TOL
+    tr = chunk_transform(K, g, beta)
+    assert np.max(np.abs(tr["K_left"] - np.exp(Gc) * K)) / scale(K) < TOL
+    assert np.max(np.abs(tr["K_right"] - np.exp(Gc[-1] - Gc) * K)) / scale(K) < TOL
+    assert np.max(np.abs(np.asarray(tr["lam_C"]) - np.exp(G[-1]))) < TOL
 
 
 @pytest.mark.parametrize("gate", GATES)
