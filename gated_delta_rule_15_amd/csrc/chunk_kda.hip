@@ -32,11 +32,13 @@
 // N^{-1} diag(beta) by blocked forward substitution (as in the scalar kernel).  Loads of
 // chunk c+1 are in flight while chunk c is processed.
 //
-// The UT instantiation runs stages S1-S4 for one chunk per workgroup, all chunks at once, adds
-// the blocks of N^{-1} below the diagonal (M_bc = -X_bb sum_{c<=d<b} N_bd M_dc) and writes, per
-// (sequence, chunk), the operands of the two-kernel state pass to a workspace: A^T and
-// T = N^{-1} diag(beta) (fp16, T's columns pperm'd), the decayed copies K e^G, Q e^G and
-// K e^{G_C - G} (fp16) and e^{G_C} per key channel (fp32).
+// The UT instantiation runs the scan, tables, Gram and diagonal inverses for a run of
+// consecutive chunks per workgroup (all runs at once), adds the blocks of N^{-1} below the
+// diagonal (M_bc = -X_bb sum_{c<=d<b} N_bd M_dc) and writes, per (sequence, chunk), the
+// operands of the two-kernel state pass to a workspace: A^T and T = N^{-1} diag(beta) (fp16,
+// T's columns pperm'd), the decayed copies K e^G, Q e^G and K e^{G_C - G} (fp16, rescaled on
+// the way out rather than in place) and e^{G_C} per key channel (fp32).  Waves 2-3 write the
+// copies while waves 0-1 form the inverses.
 //
 // Gated DeltaNet-2 ("Gated DeltaNet-2, and the gate that was doing two jobs", section 2) is
 // the GD2 instantiation.  The scalar beta is replaced by a key-side erase gate b_t and a
