@@ -263,5 +263,6 @@ def gdp_as_virtual_gdn(q, k, v, g, beta):
     return qt.reshape(B, H, T * nh, dk), kt, vt, gt.reshape(B, H, T * nh), bt, keep
 
 
-from .chunked import chunked_forward, chunk_scores, chunk_transform  # noqa: E402,F401
+from .chunked import (chunk_scores, chunk_transform, chunked_forward, gdn2_chunk_transform,  # noqa: E402,F401
+                      gdn2_chunked_forward)
 from .frame import frame_forward  # noqa: E402,F401

@@ -130,3 +130,73 @@ def chunked_forward(q, k, v, g, beta, S0=None, C: int = 64):
                 o[b, h, start:end] = O
             S_out[b, h] = S_row.T
     return o, S_out
+
+
+def gdn2_chunk_transform(K: np.ndarray, E: np.ndarray, g: np.ndarray):
+    """Per-chunk quantities of Gated DeltaNet-2 (row convention).
+
+    "Gated DeltaNet-2, and the gate that was doing two jobs" (aigenapps.com), section 2, the
+    paragraph on the chunkwise WY representation: with the channel decay normalised out of
+    the chunk, the write direction is k_l scaled by the inverse decay and the erase direction
+    e_l = b_l (.) k_l by the decay, M = tril(E~ K~^T, -1), and one triangular solve with
+    (I + M) serves both right-hand sides.  In terms of the decay products,
+    M[l, m] = e_l (lam[m+1:l] (.) k_m)^T for m < l.
+
+    K, E [C, d_k]; g [C, d_k].  Returns dict with M, T_inv = (I + M)^{-1}, E_left (rows
+    lam[1:l] (.) e_l), K_right (rows lam[l+1:C] (.) k_l), lam_C and the lam function.
+    """
+    K = np.asarray(K, dtype=np.float64)
+    E = np.asarray(E, dtype=np.float64)
+    lam = _decay_products(np.exp(np.asarray(g, dtype=np.float64)))
+    C = K.shape[0]
+    M = np.zeros((C, C))
+    for l in range(1, C + 1):
+        for m in range(1, l):
+            M[l - 1, m - 1] = E[l - 1] @ (lam(m + 1, l) * K[m - 1])
+    T_inv = forward_substitution(np.eye(C) + M, np.eye(C))
+    E_left = np.stack([lam(1, l) * E[l - 1] for l in range(1, C + 1)])
+    K_right = np.stack([lam(l + 1, C) * K[l - 1] for l in range(1, C + 1)])
+    return {"M": M, "T_inv": T_inv, "E_left": E_left, "K_right": K_right, "lam_C": lam(1, C), "lam": lam}
+
+
+def _gdn2_one_chunk(Q, K, V, g, b, w, S_row):
+    """Advance S_row (d_k x d_v) over one Gated DeltaNet-2 chunk; returns (O, S_row_next).
+
+    The erase side Y = (I + M)^{-1} E_left and the write side U_w = (I + M)^{-1} Z come from
+    one solve; the corrections are U = U_w - Y S_row; the output is the decayed read of the
+    chunk-start state plus the local scores times U, and the state moves by the chunk's
+    total decay plus K_right^T U."""
+    K = np.asarray(K, dtype=np.float64)
+    E = np.asarray(b, dtype=np.float64) * K
+    Z = np.asarray(w, dtype=np.float64) * np.asarray(V, dtype=np.float64)
+    tr = gdn2_chunk_transform(K, E, g)
+    C = K.shape[0]
+    rhs = np.concatenate([tr["E_left"], Z], axis=1)
+    sol = forward_substitution(np.eye(C) + tr["M"], rhs)
+    Y, U_w = sol[:, :K.shape[1]], sol[:, K.shape[1]:]
+    U = U_w - Y @ S_row
+    A, Q_left = chunk_scores(Q, K, g)
+    O = Q_left @ S_row + A @ U
+    S_next = tr["lam_C"][:, None] * S_row + tr["K_right"].T @ U
+    return O, S_next
+
+
+def gdn2_chunked_forward(q, k, v, g, b, w, S0=None, C: int = 64):
+    """Chunked Gated DeltaNet-2 over [B,H,T,...] inputs (the layout of oracle.gdn2_forward).
+    Returns (o [B,H,T,d_v], S_T [B,H,d_v,d_k]) in float64."""
+    q = np.asarray(q, dtype=np.float64)
+    B, H, T, dk = q.shape
+    dv = np.shape(v)[-1]
+    o = np.zeros((B, H, T, dv))
+    S_out = np.zeros((B, H, dv, dk))
+    for bb in range(B):
+        for h in range(H):
+            S_row = np.zeros((dk, dv)) if S0 is None else np.asarray(S0[bb, h], dtype=np.float64).T.copy()
+            for start in range(0, T, C):
+                end = min(start + C, T)
+                sl = slice(start, end)
+                O, S_row = _gdn2_one_chunk(q[bb, h, sl], k[bb, h, sl], v[bb, h, sl], g[bb, h, sl], b[bb, h, sl],
+                                           w[bb, h, sl], S_row)
+                o[bb, h, sl] = O
+            S_out[bb, h] = S_row.T
+    return o, S_out

@@ -8,7 +8,9 @@ directly, chunk by chunk, including a ragged last chunk:
     transform), e^{G_l}, e^{G_C - G_l} and e^{G_C};
   per-channel gate: A, T, K e^G, Q e^G, K e^{G_C - G} and e^{G_C} per key channel;
   fused input preparation: A, T and the factors of the prepared inputs, and the unit-norm
-    rows of k and q the record carries.
+    rows of k and q the record carries;
+  Gated DeltaNet-2: A, T = (I + M)^{-1} (oracle.gdn2_chunk_transform), the erase-side copy
+    (b (.) k) e^G, Q e^G, K e^{G_C - G} and e^{G_C}.
 
 Record layout per (sequence, chunk), fp16 unless noted (C = 64):
   A^T [C][C] (row m holds A[l][m]);
@@ -17,13 +19,14 @@ Record layout per (sequence, chunk), fp16 unless noted (C = 64):
   per-channel gate: K e^G, Q e^G, K e^{G_C - G} [C][d_k] each, then fp32 e^{G_C} [d_k].
 Tokens past the end of a sequence enter the kernels as identity tokens (k = q = 0, g = 0,
 beta = 0), so a ragged chunk's records hold the oracle's shorter chunk in their leading rows
-and columns and zeros elsewhere (the factors repeat e^{G_C} past the end).
+and columns and zeros elsewhere (the factors repeat e^{G_C} past the end; Gated DeltaNet-2's
+T = N^{-1} has ones on its diagonal there).
 
 Bars.  The fp32 factors: 2e-6 relative (the kernels' exponential is accurate to a few ulp).
 The fp16 matrices: max |gpu - oracle| / max |oracle| per chunk below 4e-3.  The stored value
 is rounded to fp16 (2^-11 relative), and it is formed from fp16 operands (q and k exact, the
 decay factors rounded) with fp32 accumulation: a few fp16 ulps of the largest element.
-Measured on MI355X: at most 7.6e-4 (A at d_k = 64), 3.1e-4 (T), 6.3e-4 (the copies).
+Measured on MI355X: at most 7.7e-4 (A at d_k = 64), 3.1e-4 (T), 6.3e-4 (the copies).
 """
 import dataclasses
 
@@ -87,7 +90,10 @@ def _f32(raw, byte_off, n):
     return raw[byte_off:byte_off + 4 * n].view(np.float32).astype(np.float64)
 
 
-def _check_at_t(rec, base, A_ref, T_ref, Cr, label):
+def _check_at_t(rec, base, A_ref, T_ref, Cr, label, pad_diag=0.0):
+    """A and T of one record against the oracle's leading Cr x Cr blocks.  Past the end of the
+    sequence T holds pad_diag on its diagonal and zeros elsewhere: 0 where T carries diag(beta)
+    (beta = 0 there), 1 for Gated DeltaNet-2's T = N^{-1}."""
     At = _f16(rec, base, C * C).reshape(C, C)
     Tp = _f16(rec, base + 2 * C * C, C * C).reshape(C, C)
     A = At.T
@@ -99,7 +105,9 @@ def _check_at_t(rec, base, A_ref, T_ref, Cr, label):
     # structural zeros: above the diagonal, and every row or column of a padded token
     assert np.all(np.triu(A, 1) == 0.0) and np.all(np.triu(Tm, 1) == 0.0), label
     assert np.all(A[Cr:] == 0.0) and np.all(A[:, Cr:] == 0.0), label
-    assert np.all(Tm[Cr:] == 0.0) and np.all(Tm[:, Cr:] == 0.0), label
+    pad = np.zeros((C, C))
+    pad[np.arange(Cr, C), np.arange(Cr, C)] = pad_diag
+    assert np.all(Tm[Cr:] == pad[Cr:]) and np.all(Tm[:, Cr:] == pad[:, Cr:]), label
 
 
 @pytest.mark.parametrize("T", [64, 100, 200])
@@ -196,3 +204,42 @@ def test_ut_records_fused_prep(T, dk):
                 print(f"{label}: e[{name}] {e:.2e}")
                 assert e < TOL_F16, (label, name)
                 assert np.all(got[Cr:] == 0.0), (label, name)
+
+
+@pytest.mark.parametrize("T", [64, 100])
+@pytest.mark.parametrize("dk", [128, 64])
+def test_ut_records_gdn2(T, dk):
+    """UT pass of Gated DeltaNet-2 against the oracle's chunk form (oracle.gdn2_chunk_transform):
+    A, T = (I + M)^{-1} (no beta: the erase gate sits in the row operand), the erase-side copy
+    (b (.) k) e^G in the K e^G slot, Q e^G, K e^{G_C - G} and e^{G_C}."""
+    w = dataclasses.replace(gdr_synth.WORKLOADS[7], d_k=dk, d_v=dk)
+    x = gdr_synth.make_inputs(w, B=1, H=2, T=T)
+    nbytes = gdr.gdn2_chunk_fwd_workspace_size(1, 2, T, dk, dk)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
+    gdr.gdn2_chunk_fwd(_dev(x["q"], True), _dev(x["k"], True), _dev(x["v"], True), _dev(x["g"]), _dev(x["b"]),
+                       _dev(x["w"]), workspace=ws)
+    torch.cuda.synchronize()
+    raw = ws.cpu().numpy()
+    nC = (T + C - 1) // C
+    stride = nbytes // (2 * nC)
+    for h in range(2):
+        for c in range(nC):
+            s0, s1 = c * C, min(T, (c + 1) * C)
+            Cr = s1 - s0
+            Q, K = x["q"][0, h, s0:s1], x["k"][0, h, s0:s1]
+            g, b = x["g"][0, h, s0:s1], x["b"][0, h, s0:s1]
+            tr = oracle.gdn2_chunk_transform(K, b * K, g)
+            A_ref, Q_left = oracle.chunk_scores(Q, K, g)
+            base = (h * nC + c) * stride
+            label = f"gdn2 d_k={dk} T={T} head {h} chunk {c}"
+            _check_at_t(raw, base, A_ref, tr["T_inv"], Cr, label, pad_diag=1.0)
+            off = base + 4 * C * C
+            copies = {"E e^G": tr["E_left"], "Q e^G": Q_left, "K e^(G_C-G)": tr["K_right"]}
+            for i, (name, ref) in enumerate(copies.items()):
+                got = _f16(raw, off + i * 2 * C * dk, C * dk).reshape(C, dk)
+                e = _rel(got[:Cr], ref)
+                print(f"{label}: e[{name}] {e:.2e}")
+                assert e < TOL_F16, (label, name)
+                assert np.all(got[Cr:] == 0.0), (label, name)
+            fe = _f32(raw, off + 3 * 2 * C * dk, dk)
+            assert _rel(fe, np.asarray(tr["lam_C"])) < TOL_F32, label

@@ -164,6 +164,24 @@ def test_gdn2_oracle_passes_every_pin():
     assert all(val < TOL for val in res.values()), res
 
 
+@pytest.mark.parametrize("C", [1, 3, 64])
+def test_gdn2_chunk_form_passes_every_pin(C):
+    """The chunkwise form (``oracle.gdn2_chunked_forward``: the page's WY paragraph, one
+    triangular solve for the erase and the write side) meets the same pins."""
+    res = _all_pins(lambda **x: oracle.gdn2_chunked_forward(**x, C=C))
+    assert all(val < 1e-11 for val in res.values()), res
+
+
+@pytest.mark.parametrize("C", [1, 2, 4, 16, 64, 150])
+def test_gdn2_chunk_form_equals_recurrence(C):
+    """Every chunk size gives the token recurrence; T = 150 leaves a ragged tail."""
+    x = gdn2_inputs(31, B=1, H=2, T=150, dk=8, dv=6, g_range=(-0.3, -0.001))
+    o1, S1 = oracle.gdn2_forward(**x)
+    o2, S2 = oracle.gdn2_chunked_forward(**x, C=C)
+    assert np.max(np.abs(o1 - o2)) / scale(o1) < 1e-11
+    assert np.max(np.abs(S1 - S2)) / scale(S1) < 1e-11
+
+
 def test_gdn2_empty_sequence_returns_initial_state():
     x = gdn2_inputs(11, T=0)
     o, S = oracle.gdn2_forward(**x)
