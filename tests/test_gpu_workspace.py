@@ -10,7 +10,8 @@ directly, chunk by chunk, including a ragged last chunk:
   fused input preparation: A, T and the factors of the prepared inputs, and the unit-norm
     rows of k and q the record carries;
   Gated DeltaNet-2: A, T = (I + M)^{-1} (oracle.gdn2_chunk_transform), the erase-side copy
-    (b (.) k) e^G, Q e^G, K e^{G_C - G} and e^{G_C}.
+    (b (.) k) e^G, Q e^G, K e^{G_C - G} and e^{G_C};
+  Gated Delta Product: the scalar-gate records over the virtual sequence of substeps.
 
 Record layout per (sequence, chunk), fp16 unless noted (C = 64):
   A^T [C][C] (row m holds A[l][m]);
@@ -243,3 +244,39 @@ def test_ut_records_gdn2(T, dk):
                 assert np.all(got[Cr:] == 0.0), (label, name)
             fe = _f32(raw, off + 3 * 2 * C * dk, dk)
             assert _rel(fe, np.asarray(tr["lam_C"])) < TOL_F32, label
+
+
+@pytest.mark.parametrize("T,nh", [(22, 3), (43, 3), (40, 2)])
+def test_ut_records_gdp(T, nh):
+    """UT pass of the Gated Delta Product, which runs the scalar-gate records over the virtual
+    sequence of T n_h steps: against oracle.chunk_transform / chunk_scores on the page's
+    mapping (oracle.gdp_as_virtual_gdn: decay on the first substep, q on the last)."""
+    dk = 128
+    w = dataclasses.replace(gdr_synth.WORKLOADS[6], nh=nh)
+    x = gdr_synth.make_inputs(w, B=1, H=2, T=T)
+    nbytes = gdr.gdp_chunk_fwd_workspace_size(1, 2, T, nh, dk, dk)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
+    gdr.gdp_chunk_fwd(_dev(x["q"], True), _dev(x["k"], True), _dev(x["v"], True), _dev(x["g"]), _dev(x["beta"]),
+                      workspace=ws)
+    torch.cuda.synchronize()
+    raw = ws.cpu().numpy()
+    qv, kv, _, gv, bv, _ = oracle.gdp_as_virtual_gdn(x["q"], x["k"], x["v"], x["g"], x["beta"])
+    Tv = T * nh
+    nC = (Tv + C - 1) // C
+    stride = nbytes // (2 * nC)
+    for h in range(2):
+        for c in range(nC):
+            s0, s1 = c * C, min(Tv, (c + 1) * C)
+            Cr = s1 - s0
+            Q, K = qv[0, h, s0:s1], kv[0, h, s0:s1]
+            g, beta = gv[0, h, s0:s1], bv[0, h, s0:s1]
+            tr = oracle.chunk_transform(K, g, beta)
+            A_ref, _ = oracle.chunk_scores(Q, K, g)
+            base = (h * nC + c) * stride
+            label = f"gdp n_h={nh} T={T} head {h} chunk {c}"
+            _check_at_t(raw, base, A_ref, tr["T"], Cr, label)
+            f = _f32(raw, base + 4 * C * C, 144)
+            lam = tr["lam"]
+            assert _rel(f[:Cr], np.array([lam(1, l) for l in range(1, Cr + 1)])) < TOL_F32, label
+            assert _rel(f[64:64 + Cr], np.array([lam(l + 1, Cr) for l in range(1, Cr + 1)])) < TOL_F32, label
+            assert abs(f[128] - float(tr["lam_C"])) / float(tr["lam_C"]) < TOL_F32, label
