@@ -395,13 +395,8 @@ template <int DK, typename IOT, typename OpT>
 static hipError_t launch_chunk_scalar(const ChunkArgs& a, int64_t nwg, hipStream_t st) {
     using L = ChunkLds<DK, OpT>;
     auto kern = chunk_fwd_scalar_kernel<DK, IOT, OpT>;
-    static bool attr_set = false;  // per instantiation
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, L::total);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> lds_enabled{0};  // one bit per device
+    if (const hipError_t e = enable_dynamic_lds(kern, L::total, lds_enabled); e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(256), L::total, st, a);
     return hipGetLastError();
 }

@@ -812,13 +812,8 @@ template <int DK, bool GD2, bool UT = false>
 static hipError_t launch_kda(const KdaArgs& a, int64_t nwg, hipStream_t st) {
     using L = KdaLds<DK>;
     auto kern = chunk_kda_kernel<DK, GD2, UT>;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, L::total);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> lds_enabled{0};  // one bit per device
+    if (const hipError_t e = enable_dynamic_lds(kern, L::total, lds_enabled); e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(256), L::total, st, a);
     return hipGetLastError();
 }
@@ -870,14 +865,8 @@ hipError_t chunk_kda_ut_dispatch(int64_t BH, int64_t T, int dk, const void* q, c
     a.ws = static_cast<uint16_t*>(ws);
     const int64_t nC = (T + kChunk - 1) / kChunk;
     if (BH * nC == 0) return hipSuccess;
-    static int ncu = 0;
-    if (ncu == 0) {
-        int dev = 0;
-        hipError_t e = hipGetDevice(&dev);
-        if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
-        if (e != hipSuccess) return e;
-        if (ncu < 1) ncu = 1;
-    }
+    int ncu = 1;
+    if (const hipError_t e = device_cu_count(ncu); e != hipSuccess) return e;
     const int64_t cpw = (BH * nC + ncu - 1) / ncu;
     a.cpw = (int)(cpw < nC ? cpw : nC);
     const int64_t nwg = BH * ((nC + a.cpw - 1) / a.cpw);

@@ -894,13 +894,8 @@ template <int DK, int MODE, int NCW>
 static hipError_t launch_state_ncw(StArgs s, int64_t BH, hipStream_t st) {
     using LS = StLds<DK>;
     auto ks = chunk_state_kernel<DK, MODE, NCW>;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(ks),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, LS::total);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> lds_enabled{0};  // one bit per device
+    if (const hipError_t e = enable_dynamic_lds(ks, LS::total, lds_enabled); e != hipSuccess) return e;
     s.ntiles = s.dv / (16 * NCW);
     hipLaunchKernelGGL(ks, dim3((unsigned)(BH * s.ntiles)), dim3(64 * (NCW + 2)), LS::total, st, s);
     return hipGetLastError();
@@ -910,14 +905,8 @@ static hipError_t launch_state_ncw(StArgs s, int64_t BH, hipStream_t st) {
 // (one workgroup fills a compute unit's LDS).
 template <int DK, int MODE>
 static hipError_t launch_state(const StArgs& s, int64_t BH, hipStream_t st) {
-    static int ncu = 0;
-    if (ncu == 0) {
-        int dev = 0;
-        hipError_t e = hipGetDevice(&dev);
-        if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
-        if (e != hipSuccess) return e;
-        if (ncu < 1) ncu = 1;
-    }
+    int ncu = 1;
+    if (const hipError_t e = device_cu_count(ncu); e != hipSuccess) return e;
     if (BH * (s.dv / 32) < ncu) return launch_state_ncw<DK, MODE, 1>(s, BH, st);
     return launch_state_ncw<DK, MODE, 2>(s, BH, st);
 }

@@ -518,13 +518,9 @@ template <int DK, int DV>
 static hipError_t launch_frame(const FrArgs& a, int64_t BH, hipStream_t st) {
     constexpr int lds_gram = FrGramLds<DK, DV>::total, lds_state = FrStateLds<DK>::total;
     constexpr int lds_out = FrOutLds<DV>::total;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(frame_gram_kernel<DK, DV>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, lds_gram);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> lds_enabled{0};  // one bit per device
+    if (const hipError_t e = enable_dynamic_lds(frame_gram_kernel<DK, DV>, lds_gram, lds_enabled); e != hipSuccess)
+        return e;
     if (a.F > 0) {
         hipLaunchKernelGGL((frame_gram_kernel<DK, DV>), dim3((unsigned)(BH * a.F)), dim3(256), lds_gram, st, a);
     }

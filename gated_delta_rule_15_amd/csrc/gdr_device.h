@@ -12,6 +12,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace gdr {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
@@ -22,6 +24,37 @@ typedef float float4v __attribute__((ext_vector_type(4)));
 
 constexpr int kChunk = 64;   // chunk length C
 constexpr int kWave = 64;    // CDNA wavefront
+
+// ---------------------------------------------------------------- host-side launch helpers
+// Dynamic LDS beyond the default limit is enabled per kernel and device
+// (hipFuncAttributeMaxDynamicSharedMemorySize).  `done` holds one bit per device id below 64,
+// so a launcher makes the call once per device; concurrent first calls only repeat it.
+template <typename Kern>
+inline hipError_t enable_dynamic_lds(Kern kern, int bytes, std::atomic<uint64_t>& done) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = (dev >= 0 && dev < 64) ? (uint64_t{1} << dev) : 0;
+    if (bit != 0 && (done.load(std::memory_order_acquire) & bit) != 0) return hipSuccess;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess && bit != 0) done.fetch_or(bit, std::memory_order_acq_rel);
+    return e;
+}
+
+// Compute units of the current device, cached per device id (below 64).
+inline hipError_t device_cu_count(int& ncu) {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const bool slot = dev >= 0 && dev < 64;
+    if (slot && (ncu = cache[dev].load(std::memory_order_relaxed)) > 0) return hipSuccess;
+    e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (ncu < 1) ncu = 1;
+    if (slot) cache[dev].store(ncu, std::memory_order_relaxed);
+    return hipSuccess;
+}
 
 // ---------------------------------------------------------------- scalar conversions
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {

@@ -19,8 +19,10 @@
  *
  * Conventions shared by every entry point
  *  - All tensor pointers are DEVICE pointers to contiguous row-major buffers owned by the
- *    caller.  The library allocates nothing and keeps no state between calls; the one entry
- *    point that needs scratch memory (gdr_chunk_fwd_ws) takes it from the caller.
+ *    caller.  The library allocates no device memory: the entry points that need scratch
+ *    memory (the *_ws variants and gdr_frame_fwd) take it from the caller.  Between calls it
+ *    keeps only per-device launch settings, made on first use on each device: the dynamic
+ *    LDS limit of its kernels and the device's compute-unit count.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only enqueue work and
  *    return; faults during execution surface at the caller's next synchronisation.
  *  - Every argument is validated on the host before anything is enqueued.  On any error the
