@@ -279,6 +279,41 @@ def test_chunk_deterministic():
     assert torch.equal(o1, o2) and torch.equal(S1, S2)
 
 
+def test_concurrent_calls_on_separate_streams():
+    """Calls from several host threads, each on its own stream with its own buffers and
+    workspace, give the results of the same calls made one after another (the library keeps
+    no state between calls beyond per-device launch settings)."""
+    import threading
+    cases = [(2, 300, "scalar"), (3, 200, "channel"), (2, 129, "scalar"), (3, 64, "channel")]
+    inputs = [gdr_synth.make_inputs(gdr_synth.WORKLOADS[wid], B=1, H=3, T=T, salt=i)
+              for i, (wid, T, _) in enumerate(cases)]
+    expect = [run_chunk(x, True) for x in inputs]
+    got = [None] * len(cases)
+    errors = []
+    dev_in = [{key: dev(val, key in ("q", "k", "v")) for key, val in x.items() if val is not None} for x in inputs]
+    torch.cuda.synchronize()
+
+    def worker(i):
+        try:
+            stream = torch.cuda.Stream()
+            d = dev_in[i]
+            with torch.cuda.stream(stream):
+                for _ in range(3):
+                    got[i] = gdr.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], stream=stream)
+            stream.synchronize()
+        except Exception as e:  # surfaced below
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(len(cases))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    for (o1, S1), (o2, S2) in zip(expect, got):
+        assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
 def test_chunk_final_state_may_alias_initial_state():
     x = gdr_synth.make_inputs(gdr_synth.WORKLOADS[2], B=1, H=2, T=130)
     S0 = (np.random.default_rng(1).standard_normal((1, 2, 128, 128)) * 0.05).astype(np.float32)
