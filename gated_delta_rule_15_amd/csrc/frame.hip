@@ -22,7 +22,7 @@
 //                       into high and low halves (three products: hi.hi + hi.lo + lo.hi), which
 //                       keeps the chained state at fp32-class accuracy; S_t is written in fp16
 //                       for the outputs;
-//   frame_out_kernel    one workgroup per (sequence, 64 tokens): O = Q S_t^T.
+//   frame_out_kernel    one workgroup per (sequence, 256 tokens): O = Q S_t^T.
 // The post solves the system by a Cholesky factorisation; forming the inverse once per frame
 // instead keeps the serial pass to one product per frame (the same solution in exact
 // arithmetic; I + G is well conditioned, its eigenvalues lying in [1, 1 + tr G]).
@@ -462,48 +462,62 @@ struct FrOutLds {
     static constexpr int total = 64 * LDO * 2;
 };
 
+// One group per 256 tokens of a sequence; wave w takes tokens 64 w .. 64 w + 63 of them in four
+// 16-token steps.  The frame state's operand fragments (all of S_t^T, fp16) stay in the wave's
+// registers and are reloaded only when a step enters a new frame, so each wave reads S once for
+// up to 64 tokens instead of once per 16.
 template <int DK, int DV>
 __global__ __launch_bounds__(256) void frame_out_kernel(const FrArgs a, int64_t nblk) {
     using L = FrOutLds<DV>;
-    constexpr int NKB = DK / 32, NV = DV / 16;
+    constexpr int NKB = DK / 32, NV = DV / 16, NG = 4;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     uint16_t* Ot = reinterpret_cast<uint16_t*>(smem);
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, j = l & 15, g = l >> 4;
     const int64_t bh = blockIdx.x / nblk;
     const int64_t blk = blockIdx.x - bh * nblk;
     const int64_t T = a.T;
-    const int64_t tb = blk * 64 + 16 * w;  // this wave's 16 tokens, all in one frame
     const auto rq = make_rsrc(a.q + bh * T * DK, (uint32_t)(T * DK * 2));
     const auto ro = make_rsrc(a.o + bh * T * DV, (uint32_t)(T * DV * 2));
-    const int64_t f = (tb < T ? tb : T - 1) / a.n;
-    const uint16_t* S = a.Sw + (bh * a.F + f) * (int64_t)(DV * DK);
-
-    half8 qa[NKB];
+    half8 sf[NV][NKB];
+    int64_t fcur = -1;
+    for (int gi = 0; gi < NG; ++gi) {
+        const int64_t tb = blk * 256 + 64 * w + 16 * gi;  // this step's 16 tokens, all in one frame
+        if (tb >= T) break;
+        const int64_t f = tb / a.n;
+        if (f != fcur) {
+            const uint16_t* S = a.Sw + (bh * a.F + f) * (int64_t)(DV * DK);
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-        qa[kb] = bf16x8_to_half8(bld16(rq, (uint32_t)(((tb + j) * DK + 32 * kb + 8 * g) * 2)));
+            for (int vi = 0; vi < NV; ++vi)
 #pragma unroll
-    for (int vi = 0; vi < NV; ++vi) {
-        float4v acc = zero4();
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-            const half8 sb = *reinterpret_cast<const half8*>(S + (16 * vi + j) * DK + 32 * kb + 8 * g);
-            mma16(acc, qa[kb], sb);
+                for (int kb = 0; kb < NKB; ++kb)
+                    sf[vi][kb] = *reinterpret_cast<const half8*>(S + (16 * vi + j) * DK + 32 * kb + 8 * g);
+            fcur = f;
         }
+        half8 qa[NKB];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const uint32_t b2 = pack_bf16x2(acc[r], 0.0f);
-            Ot[(16 * w + 4 * g + r) * L::LDO + 16 * vi + j] = (uint16_t)(b2 & 0xffffu);
+        for (int kb = 0; kb < NKB; ++kb)
+            qa[kb] = bf16x8_to_half8(bld16(rq, (uint32_t)(((tb + j) * DK + 32 * kb + 8 * g) * 2)));
+#pragma unroll
+        for (int vi = 0; vi < NV; ++vi) {
+            float4v acc = zero4();
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) mma16(acc, qa[kb], sf[vi][kb]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const uint32_t b2 = pack_bf16x2(acc[r], 0.0f);
+                Ot[(16 * w + 4 * g + r) * L::LDO + 16 * vi + j] = (uint16_t)(b2 & 0xffffu);
+            }
         }
-    }
-    lds_fence();
-    // this wave's 16 token rows back as 16-byte pieces
-    constexpr int PPR = DV / 8;  // pieces per row
+        lds_fence();
+        // this wave's 16 token rows back as 16-byte pieces (rows past the end are dropped)
+        constexpr int PPR = DV / 8;  // pieces per row
 #pragma unroll
-    for (int u = 0; u < 16 * PPR / 64; ++u) {
-        const int idx = l + 64 * u, row = idx / PPR, col = (idx % PPR) * 8;
-        const uint4 val = *reinterpret_cast<const uint4*>(Ot + (16 * w + row) * L::LDO + col);
-        bst16(ro, (uint32_t)(((tb + row) * DV + col) * 2), val);
+        for (int u = 0; u < 16 * PPR / 64; ++u) {
+            const int idx = l + 64 * u, row = idx / PPR, col = (idx % PPR) * 8;
+            const uint4 val = *reinterpret_cast<const uint4*>(Ot + (16 * w + row) * L::LDO + col);
+            bst16(ro, (uint32_t)(((tb + row) * DV + col) * 2), val);
+        }
+        lds_fence();  // the next step rewrites these rows
     }
 }
 
@@ -526,7 +540,7 @@ static hipError_t launch_frame(const FrArgs& a, int64_t BH, hipStream_t st) {
     }
     hipLaunchKernelGGL((frame_state_kernel<DK, DV>), dim3((unsigned)(BH * (DV / 64))), dim3(256), lds_state, st,
                        a);
-    const int64_t nblk = (a.T + 63) / 64;
+    const int64_t nblk = (a.T + 255) / 256;
     if (nblk > 0) {
         hipLaunchKernelGGL((frame_out_kernel<DK, DV>), dim3((unsigned)(BH * nblk)), dim3(256), lds_out, st, a,
                            nblk);
