@@ -22,7 +22,7 @@
 //                       into high and low halves (three products: hi.hi + hi.lo + lo.hi), which
 //                       keeps the chained state at fp32-class accuracy; S_t is written in fp16
 //                       for the outputs;
-//   frame_out_kernel    one workgroup per (sequence, 256 tokens): O = Q S_t^T.
+//   frame_out_kernel    one workgroup per (sequence, 512 tokens): O = Q S_t^T.
 // The post solves the system by a Cholesky factorisation; forming the inverse once per frame
 // instead keeps the serial pass to one product per frame (the same solution in exact
 // arithmetic; I + G is well conditioned, its eigenvalues lying in [1, 1 + tr G]).
@@ -462,14 +462,14 @@ struct FrOutLds {
     static constexpr int total = 64 * LDO * 2;
 };
 
-// One group per 256 tokens of a sequence; wave w takes tokens 64 w .. 64 w + 63 of them in four
-// 16-token steps.  The frame state's operand fragments (all of S_t^T, fp16) stay in the wave's
-// registers and are reloaded only when a step enters a new frame, so each wave reads S once for
-// up to 64 tokens instead of once per 16.
+// One group per 512 tokens of a sequence; wave w takes tokens 128 w .. 128 w + 127 of them in
+// eight 16-token steps.  The frame state's operand fragments (all of S_t^T, fp16) stay in the
+// wave's registers and are reloaded only when a step enters a new frame, so each wave reads S
+// once for up to 128 tokens instead of once per 16.
 template <int DK, int DV>
 __global__ __launch_bounds__(256) void frame_out_kernel(const FrArgs a, int64_t nblk) {
     using L = FrOutLds<DV>;
-    constexpr int NKB = DK / 32, NV = DV / 16, NG = 4;
+    constexpr int NKB = DK / 32, NV = DV / 16, NG = 8;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     uint16_t* Ot = reinterpret_cast<uint16_t*>(smem);
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, j = l & 15, g = l >> 4;
@@ -481,7 +481,7 @@ __global__ __launch_bounds__(256) void frame_out_kernel(const FrArgs a, int64_t 
     half8 sf[NV][NKB];
     int64_t fcur = -1;
     for (int gi = 0; gi < NG; ++gi) {
-        const int64_t tb = blk * 256 + 64 * w + 16 * gi;  // this step's 16 tokens, all in one frame
+        const int64_t tb = blk * 512 + 128 * w + 16 * gi;  // this step's 16 tokens, all in one frame
         if (tb >= T) break;
         const int64_t f = tb / a.n;
         if (f != fcur) {
@@ -540,7 +540,7 @@ static hipError_t launch_frame(const FrArgs& a, int64_t BH, hipStream_t st) {
     }
     hipLaunchKernelGGL((frame_state_kernel<DK, DV>), dim3((unsigned)(BH * (DV / 64))), dim3(256), lds_state, st,
                        a);
-    const int64_t nblk = (a.T + 255) / 256;
+    const int64_t nblk = (a.T + 511) / 512;
     if (nblk > 0) {
         hipLaunchKernelGGL((frame_out_kernel<DK, DV>), dim3((unsigned)(BH * nblk)), dim3(256), lds_out, st, a,
                            nblk);
