@@ -374,8 +374,34 @@ __global__ __launch_bounds__(256, 1) void frame_state_kernel(const FrArgs a) {
         wph[u] = bld16(rwh, (uint32_t)((tid + 256 * u) * 16));
         wpl[u] = bld16(rwl, (uint32_t)((tid + 256 * u) * 16));
     }
+    // C and the frame gate of the next frame, prefetched the same way (buffer loads, no branch:
+    // past the last frame they read zeros, which are never used)
+    const int gstride = a.channel ? DK : 1;
+    const auto rc = make_rsrc(a.Cw + bh * F * (int64_t)(DV * DK), (uint32_t)(F * DV * DK * 4));
+    const auto rgf = make_rsrc(a.g + bh * F * gstride, (uint32_t)(F * gstride * 4));
+    float4v cn[NST], gn[NST];
+    auto load_cg = [&](int64_t fl) {
+#pragma unroll
+        for (int t = 0; t < NST; ++t) {
+            const int ch = pperm(16 * t + 4 * g);
+            cn[t] = __builtin_bit_cast(float4v, bld16(rc, (uint32_t)(((fl * DV + dvc + j) * DK + ch) * 4)));
+            gn[t] = __builtin_bit_cast(float4v, bld16(rgf, (uint32_t)((fl * gstride + (a.channel ? ch : 0)) * 4)));
+        }
+    };
+    load_cg(0);
     for (int64_t f = 0; f < F; ++f) {
         const int64_t fi = bh * F + f;
+        // rhs^T = D S^T + C^T (rows permuted as S^T), then the next frame's C and gate
+        float4v rh[NST];
+#pragma unroll
+        for (int t = 0; t < NST; ++t) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float d = fast_exp(a.channel ? gn[t][r] : gn[t][0]);
+                rh[t][r] = fmaf(d, St[t][r], cn[t][r]);
+            }
+        }
+        load_cg(f + 1);
         // W of this frame into LDS (the previous frame's readers are past the barrier below)
 #pragma unroll
         for (int u = 0; u < NPW; ++u) {
@@ -391,26 +417,6 @@ __global__ __launch_bounds__(256, 1) void frame_state_kernel(const FrArgs a) {
                 wph[u] = bld16(rwh, nb + (uint32_t)((tid + 256 * u) * 16));
                 wpl[u] = bld16(rwl, nb + (uint32_t)((tid + 256 * u) * 16));
             }
-        }
-        // rhs^T = D S^T + C^T (rows permuted as S^T)
-        const float* cs = a.Cw + fi * (int64_t)(DV * DK) + (int64_t)(dvc + j) * DK;
-        const float* gf = a.g + (a.channel ? fi * DK : fi);
-        float4v rh[NST];
-#pragma unroll
-        for (int t = 0; t < NST; ++t) {
-            const int ch = pperm(16 * t + 4 * g);
-            const float4v c4 = ld4f(cs + ch);
-            float4v d4;
-            if (a.channel) {
-                const float4v g4 = ld4f(gf + ch);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) d4[r] = fast_exp(g4[r]);
-            } else {
-                const float d = fast_exp(gf[0]);
-                d4 = float4v{d, d, d, d};
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) rh[t][r] = fmaf(d4[r], St[t][r], c4[r]);
         }
         // operand halves: rhs = hi + lo
         half8 bh8[NKB], bl8[NKB];
