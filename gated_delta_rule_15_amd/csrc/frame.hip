@@ -256,7 +256,7 @@ __global__ __launch_bounds__(256, 1) void frame_gram_kernel(const FrArgs a) {
                             rowp[c] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(P[rr][c]), pl));
                     }
                 }
-                const float rp = 1.0f / rowp[pp];
+                const float rp = __builtin_amdgcn_rcpf(rowp[pp]);  // 1 ulp; the pivots are >= 1 in exact arithmetic
 #pragma unroll
                 for (int rr = 0; rr < NR; ++rr) {
                     const bool prow = l + 64 * rr == p;
