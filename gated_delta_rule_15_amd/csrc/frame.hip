@@ -228,52 +228,54 @@ __global__ __launch_bounds__(256, 1) void frame_gram_kernel(const FrArgs a) {
     // product.  I + G is symmetric positive definite with eigenvalues >= 1, and so is every
     // pivot block's Schur complement: no pivoting is needed.
     constexpr int NB = DK / 16;           // pivot blocks
-    constexpr int NR = DK / 64;           // panel rows per lane of wave 0
     constexpr int NTW = (NB * (NB - 1) + 3) / 4;  // trailing tiles per wave
     for (int kbk = 0; kbk < NB; ++kbk) {
         const int kc = 16 * kbk;
+        // 1. wave 0: D^{-1} by Gauss-Jordan on the 16 x 16 pivot block alone (lane r of each
+        //    16-lane row holds row kc + r; the pivot row reaches the other lanes by readlane)
         if (w == 0) {
-            float P[NR][16];
+            const int r = l & 15;
+            float P[16];
 #pragma unroll
-            for (int rr = 0; rr < NR; ++rr)
+            for (int c = 0; c < 16; c += 4) {
+                const float4v v4 = ld4f(Am + (kc + r) * L::LDA + kc + c);
 #pragma unroll
-                for (int c = 0; c < 16; c += 4) {
-                    const float4v v4 = ld4f(Am + (l + 64 * rr) * L::LDA + kc + c);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) P[rr][c + e] = v4[e];
-                }
-#pragma unroll
-            for (int pp = 0; pp < 16; ++pp) {
-                const int p = kc + pp, pl = p & 63, prr = p >> 6;  // pivot row: lane pl, register row prr
-                // the pivot row from lane pl's register row prr (uniform: a scalar branch, so only
-                // that row is read)
-                float rowp[16];
-#pragma unroll
-                for (int rr = 0; rr < NR; ++rr) {
-                    if (prr == rr) {
-#pragma unroll
-                        for (int c = 0; c < 16; ++c)
-                            rowp[c] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(P[rr][c]), pl));
-                    }
-                }
-                const float rp = __builtin_amdgcn_rcpf(rowp[pp]);  // 1 ulp; the pivots are >= 1 in exact arithmetic
-#pragma unroll
-                for (int rr = 0; rr < NR; ++rr) {
-                    const bool prow = l + 64 * rr == p;
-                    const float f = P[rr][pp];
-                    const float keep = prow ? 0.0f : 1.0f;
-                    const float cf = prow ? rp : -f * rp;
-#pragma unroll
-                    for (int c = 0; c < 16; ++c) P[rr][c] = fmaf(rowp[c], cf, P[rr][c] * keep);
-                    P[rr][pp] = prow ? rp : -f * rp;
-                }
+                for (int e = 0; e < 4; ++e) P[c + e] = v4[e];
             }
 #pragma unroll
-            for (int rr = 0; rr < NR; ++rr)
+            for (int pp = 0; pp < 16; ++pp) {
+                float rowp[16];
+#pragma unroll
+                for (int c = 0; c < 16; ++c) rowp[c] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(P[c]), pp));
+                const float rp = __builtin_amdgcn_rcpf(rowp[pp]);  // 1 ulp; the pivots are >= 1 in exact arithmetic
+                const bool prow = r == pp;
+                const float f = P[pp];
+                const float keep = prow ? 0.0f : 1.0f;
+                const float cf = prow ? rp : -f * rp;
+#pragma unroll
+                for (int c = 0; c < 16; ++c) P[c] = fmaf(rowp[c], cf, P[c] * keep);
+                P[pp] = prow ? rp : -f * rp;
+            }
+            if (l < 16) {
 #pragma unroll
                 for (int c = 0; c < 16; c += 4)
-                    *reinterpret_cast<float4v*>(Am + (l + 64 * rr) * L::LDA + kc + c) =
-                        float4v{P[rr][c], P[rr][c + 1], P[rr][c + 2], P[rr][c + 3]};
+                    *reinterpret_cast<float4v*>(Am + (kc + r) * L::LDA + kc + c) = float4v{P[c], P[c + 1], P[c + 2], P[c + 3]};
+            }
+        }
+        lds_barrier();
+        // 2. the panel's other rows, -A_{i,Kb} D^{-1}, one 16 x 16 tile per row block on fp32
+        //    MFMA (each wave reads its tiles before it writes them; D^{-1} is only read)
+        for (int t = w; t < NB - 1; t += 4) {
+            const int ib = t + (t >= kbk ? 1 : 0);
+            float4v a4 = zero4();
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float av = Am[(16 * ib + j) * L::LDA + kc + 4 * q + g];  // A[16 ib + j][Kb + 4q + g]
+                const float bv = Am[(kc + 4 * q + g) * L::LDA + kc + j];       // D^{-1}[4q + g][j]
+                a4 = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, a4, 0, 0, 0);
+            }
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) Am[(16 * ib + 4 * g + r4) * L::LDA + kc + j] = -a4[r4];
         }
         lds_barrier();
         // tiles (ib, jb), jb != kbk, numbered n = ib (NB - 1) + (jb - [jb > kbk]); wave w
