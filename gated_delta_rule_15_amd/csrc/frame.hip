@@ -17,7 +17,7 @@
 //                       updates on fp32 MFMA; I + G is symmetric positive definite with
 //                       eigenvalues >= 1, so no pivoting is needed), written as a pair of
 //                       fp16 matrices W = W_hi + W_lo, and C in fp32;
-//   frame_state_kernel  one workgroup per (sequence, 64 value channels), frames in order:
+//   frame_state_kernel  one workgroup per (sequence, 32 value channels), frames in order:
 //                       S_t^T = W_t (D_t S_{t-1}^T + C_t^T) on fp16 MFMA with both factors split
 //                       into high and low halves (three products: hi.hi + hi.lo + lo.hi), which
 //                       keeps the chained state at fp32-class accuracy; S_t is written in fp16
@@ -341,19 +341,20 @@ struct FrStateLds {
     static constexpr int total = oWl + DK * LDW * 2;
 };
 
-template <int DK, int DV>
-__global__ __launch_bounds__(256, 1) void frame_state_kernel(const FrArgs a) {
+template <int DK, int DV, int NWV>
+__global__ __launch_bounds__(64 * NWV, 1) void frame_state_kernel(const FrArgs a) {
     using L = FrStateLds<DK>;
     constexpr int NKB = DK / 32, NST = DK / 16;
-    constexpr int NPW = DK * DK / 8 / 256;  // 16-byte pieces of one W matrix per thread
+    constexpr int NTH = 64 * NWV;           // threads: NWV waves of 16 value channels
+    constexpr int NPW = DK * DK / 8 / NTH;  // 16-byte pieces of one W matrix per thread
     extern __shared__ __attribute__((aligned(16))) char smem[];
     _Float16* Whs = reinterpret_cast<_Float16*>(smem + L::oWh);
     _Float16* Wls = reinterpret_cast<_Float16*>(smem + L::oWl);
 
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, j = l & 15, g = l >> 4;
-    constexpr int NDT = DV / 64;  // workgroups per sequence
+    constexpr int NDT = DV / (16 * NWV);  // workgroups per sequence
     const int64_t bh = blockIdx.x / NDT;
-    const int dvc = (int)(blockIdx.x % NDT) * 64 + 16 * w;  // this wave's first value channel
+    const int dvc = (int)(blockIdx.x % NDT) * (16 * NWV) + 16 * w;  // this wave's first value channel
     const int64_t F = a.F;
 
     // S^T of 16 value channels, rows permuted by pperm (row P holds key channel pperm(P))
@@ -373,8 +374,8 @@ __global__ __launch_bounds__(256, 1) void frame_state_kernel(const FrArgs a) {
     uint4 wph[NPW], wpl[NPW];
 #pragma unroll
     for (int u = 0; u < NPW; ++u) {
-        wph[u] = bld16(rwh, (uint32_t)((tid + 256 * u) * 16));
-        wpl[u] = bld16(rwl, (uint32_t)((tid + 256 * u) * 16));
+        wph[u] = bld16(rwh, (uint32_t)((tid + NTH * u) * 16));
+        wpl[u] = bld16(rwl, (uint32_t)((tid + NTH * u) * 16));
     }
     // C and the frame gate of the next frame, prefetched the same way (buffer loads, no branch:
     // past the last frame they read zeros, which are never used)
@@ -412,7 +413,7 @@ __global__ __launch_bounds__(256, 1) void frame_state_kernel(const FrArgs a) {
         // W of this frame into LDS (the previous frame's readers are past the barrier below)
 #pragma unroll
         for (int u = 0; u < NPW; ++u) {
-            const int idx = tid + 256 * u, row = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
+            const int idx = tid + NTH * u, row = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
             *reinterpret_cast<uint4*>(Whs + row * L::LDW + col) = wph[u];
             *reinterpret_cast<uint4*>(Wls + row * L::LDW + col) = wpl[u];
         }
@@ -421,8 +422,8 @@ __global__ __launch_bounds__(256, 1) void frame_state_kernel(const FrArgs a) {
             const uint32_t nb = (uint32_t)((f + 1) * DK * DK * 2);  // past the end: zeros, unused
 #pragma unroll
             for (int u = 0; u < NPW; ++u) {
-                wph[u] = bld16(rwh, nb + (uint32_t)((tid + 256 * u) * 16));
-                wpl[u] = bld16(rwl, nb + (uint32_t)((tid + 256 * u) * 16));
+                wph[u] = bld16(rwh, nb + (uint32_t)((tid + NTH * u) * 16));
+                wpl[u] = bld16(rwl, nb + (uint32_t)((tid + NTH * u) * 16));
             }
         }
         // operand halves: rhs = hi + lo
@@ -551,7 +552,9 @@ static hipError_t launch_frame(const FrArgs& a, int64_t BH, hipStream_t st) {
     if (a.F > 0) {
         hipLaunchKernelGGL((frame_gram_kernel<DK, DV>), dim3((unsigned)(BH * a.F)), dim3(256), lds_gram, st, a);
     }
-    hipLaunchKernelGGL((frame_state_kernel<DK, DV>), dim3((unsigned)(BH * (DV / 64))), dim3(256), lds_state, st,
+    constexpr int kStateWaves = 2;  // value-channel tiles of 32: more groups, each reading W once
+    hipLaunchKernelGGL((frame_state_kernel<DK, DV, kStateWaves>), dim3((unsigned)(BH * (DV / (16 * kStateWaves)))),
+                       dim3(64 * kStateWaves), lds_state, st,
                        a);
     const int64_t nblk = (a.T + 511) / 512;
     if (nblk > 0) {
