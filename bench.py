@@ -303,7 +303,7 @@ def bench_frame(torch, gdr, gdr_synth, steps=10):
     torch.cuda.synchronize()
     return {"workload": "frame_bf16: frame-level implicit update B=1 H=16 T=16384 (16 frames x 1024 tokens) "
                         "d_k=d_v=128 bf16, per-channel frame gate",
-            "kernels": "frame_gram_kernel<128,128> + frame_state_kernel<128,128> + frame_out_kernel<128,128>",
+            "kernels": "frame_gram_kernel<128,128> + frame_state_kernel<128,128,2> + frame_out_kernel<128,128>",
             "ms_per_call": round(ms, 4), "tokens_per_s": round(wf["B"] * wf["T"] / (ms * 1e-3), 1),
             "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_MFMA_F16, 4),
             "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM, 4),
