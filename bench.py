@@ -30,7 +30,7 @@ sys.path.insert(0, os.path.join(ROOT, "tests"))
 
 PEAK_MFMA_F16 = 2500.0  # TFLOP/s, MI355X dense fp16/bf16
 PEAK_HBM = 8000.0       # GB/s, MI355X HBM3E
-# the headline step: one gdr_chunk_fwd_ws call = the UT kernel over all chunks, then the
+# the headline step: one gdr_chunk_fwd call = the UT kernel over all chunks, then the
 # chunk-serial state kernel
 CHUNK_KERNEL = "chunk_ut_kernel<128, 0> + chunk_state_kernel<128, 0, 2>"
 CHUNK_SOURCE = os.path.join(ROOT, "gated_delta_rule_15_amd", "csrc", "chunk_split.hip")
@@ -182,8 +182,6 @@ def bench_gdp(torch, gdr, gdr_synth, steps=10):
     sets = make_chunk_sets(torch, gdr_synth, w, nsets=2)
     wsb = torch.empty(max(gdr.gdp_chunk_fwd_workspace_size(w.B, w.H, w.T, w.nh, w.d_k, w.d_v), 1),
                       dtype=torch.uint8, device="cuda")
-    ms_single, _, _, _, _ = time_chunk(torch, gdr, sets, steps, 2,
-                                       fn=lambda *a_, **kw: gdr.gdp_chunk_fwd(*a_, workspace=None, **kw))
     ms, med, _, o, S = time_chunk(torch, gdr, sets, steps, 2,
                                   fn=lambda *a_, **kw: gdr.gdp_chunk_fwd(*a_, workspace=wsb, **kw))
     Tv = w.T * w.nh
@@ -200,7 +198,6 @@ def bench_gdp(torch, gdr, gdr_synth, steps=10):
     res = {"workload": "gdp_bf16: Gated Delta Product B=4 H=16 T=2048 n_h=2 d_k=d_v=128 bf16, zero S0",
            "kernel": "chunk_ut_kernel<128, 1> + chunk_state_kernel<128, 3, 2>", "ms_per_call": round(ms, 4),
            "ms_per_call_median": round(med, 4),
-           "single_kernel": {"kernel": "chunk_fwd_pc_kernel<128, 1>", "ms_per_call": round(ms_single, 4)},
            "tokens_per_s": round(w.B * w.T / (ms * 1e-3), 1),
            "substeps_per_s": round(w.B * Tv / (ms * 1e-3), 1),
            "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_MFMA_F16, 4),
@@ -245,14 +242,12 @@ def bench_prep(torch, gdr, gdr_synth, steps=20):
         torch.cuda.synchronize()
         return float(np.mean([a.elapsed_time(b) for a, b in ev]))
 
-    ms_single = timed(None)
     ms = timed(wsb)
     n = w.B * w.H * w.T
     separate_pass = n * w.d_k * 2 * 2 * 2 + n * 4 * 4   # q, k read and written (bf16); dt, logit read, g, beta written
     flops = chunk_flops(w.B, w.H, w.T, w.d_k, w.d_v)
     return {"workload": "gdn_bf16_train from raw projections: B=4 H=16 T=4096 d=128, per-head A_log, dt_bias",
             "kernel": "chunk_ut_kernel<128, 2> + chunk_state_kernel<128, 4, 2>", "ms_per_call": round(ms, 4),
-            "single_kernel": {"kernel": "chunk_fwd_pc_kernel<128, 2>", "ms_per_call": round(ms_single, 4)},
             "tokens_per_s": round(w.B * w.T / (ms * 1e-3), 1),
             "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_MFMA_F16, 4),
             "separate_prep_pass_hbm_floor_ms": round(separate_pass / (PEAK_HBM * 1e9) * 1e3, 4)}
@@ -346,7 +341,6 @@ def bench_gdn2(torch, gdr, gdr_synth, steps=10):
         torch.cuda.synchronize()
         return float(np.mean([a.elapsed_time(b) for a, b in ev]))
 
-    ms_single = timed(None)
     ms = timed(wsb)
     flops = chunk_flops(w.B, w.H, w.T, w.d_k, w.d_v)
     n = w.B * w.H * w.T
@@ -360,9 +354,8 @@ def bench_gdn2(torch, gdr, gdr_synth, steps=10):
     torch.cuda.synchronize()
     return {"workload": "gdn2_bf16: Gated DeltaNet-2 B=2 H=16 T=8192 d_k=d_v=128 bf16, fp32 g, b [B,H,T,128], "
                         "w [B,H,T,128], zero S0",
-            "kernel": "chunk_kda_kernel<128, true, true> + chunk_state_kernel<128, 2, 1>",
+            "kernel": "chunk_kda_kernel<128, true> + chunk_state_kernel<128, 2, 1>",
             "ms_per_call": round(ms, 4),
-            "single_kernel": {"kernel": "chunk_kda_kernel<128, true, false>", "ms_per_call": round(ms_single, 4)},
             "tokens_per_s": round(w.B * w.T / (ms * 1e-3), 1),
             "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_MFMA_F16, 4),
             "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM, 4),
@@ -459,17 +452,12 @@ def main():
                      "frac": round(tflops / PEAK_MFMA_F16, 4), "traffic": measured_traffic(),
                      "flops_per_launch": flops, "kernel": CHUNK_KERNEL,
                      "ms_per_launch_mean": round(ms_mean, 5), "ms_per_launch_median": round(ms_med, 5),
-                     "note": "one launch = one gdr_chunk_fwd_ws call (both kernels), HIP events around it"},
+                     "note": "one launch = one gdr_chunk_fwd call (both kernels), HIP events around it"},
         "roofline_hbm": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM, 4), "bytes_per_launch": nbytes},
         "wall_s_timed_region": round(wall, 4),
     }
     result["parity_sampled"] = sampled_parity(gdr_synth, w, sets[0]["host"], o, S)
-    # the single-kernel path (gdr_chunk_fwd, no workspace) on the same inputs
-    m1, _, _, _, _ = time_chunk(torch, gdr, sets, 20, 3,
-                                fn=lambda *a_, **kw: gdr.chunk_fwd(*a_, workspace=None, **kw))
-    result["single_kernel"] = {"kernel": "chunk_fwd_pc_kernel<128, 0>", "ms_per_launch_mean": round(m1, 5),
-                               "mfma_frac": round(flops / (m1 * 1e-3) / 1e12 / PEAK_MFMA_F16, 4)}
     if not args.no_extra:
         result["decode"] = bench_decode(torch, gdr, gdr_synth)
         w4 = gdr_synth.WORKLOADS[4]
@@ -483,18 +471,15 @@ def main():
         w3 = gdr_synth.WORKLOADS[3]
         sets3 = make_chunk_sets(torch, gdr_synth, w3, nsets=2)
         m3, _, _, _, _ = time_chunk(torch, gdr, sets3, 10, 2)
-        m3s, _, _, _, _ = time_chunk(torch, gdr, sets3, 10, 2,
-                                     fn=lambda *a_, **kw: gdr.chunk_fwd(*a_, workspace=None, **kw))
         f3 = chunk_flops(w3.B, w3.H, w3.T, 128, 128)
         b3 = chunk_bytes(w3.B, w3.H, w3.T, 128, 128, gate_per_channel=True)
         result["kda"] = {
             "workload": "per-channel gate B=2 H=16 T=8192 d=128 bf16, fp32 gate [B,H,T,128]",
-            "kernel": "chunk_kda_kernel<128, false, true> + chunk_state_kernel<128, 1, 1>",
+            "kernel": "chunk_kda_kernel<128, false> + chunk_state_kernel<128, 1, 1>",
             "ms_per_call": round(m3, 4),
             "tokens_per_s": round(w3.B * w3.T / (m3 * 1e-3), 1),
             "mfma_frac": round(f3 / (m3 * 1e-3) / 1e12 / PEAK_MFMA_F16, 4),
-            "hbm_frac": round(b3 / (m3 * 1e-3) / 1e9 / PEAK_HBM, 4),
-            "single_kernel": {"kernel": "chunk_kda_kernel<128, false, false>", "ms_per_call": round(m3s, 4)}}
+            "hbm_frac": round(b3 / (m3 * 1e-3) / 1e9 / PEAK_HBM, 4)}
         del sets3
         result["gdp"] = bench_gdp(torch, gdr, gdr_synth)
         result["gdn2"] = bench_gdn2(torch, gdr, gdr_synth)

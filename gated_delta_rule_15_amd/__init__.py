@@ -1,8 +1,9 @@
 """libgdr: the gated delta rule on AMD Instinct MI355X (gfx950).
 
 Python face of the C ABI in include/gdr.h.  ``chunk_fwd`` runs the chunkwise
-forward pass and returns (o, final_state) (by default on the two-kernel path with a
-torch-allocated workspace); ``chunk_fwd_fused_prep`` runs it from raw
+forward pass and returns (o, final_state) (the UT kernel over all chunks, then the
+chunk-serial state kernel; the workspace is the caller's tensor or one allocated with
+torch); ``chunk_fwd_fused_prep`` runs it from raw
 projections (normalisation and gates fused in); ``gdp_chunk_fwd`` is the same pass
 for the Gated Delta Product (n_h key/value/beta substeps per token) and
 ``gdn2_chunk_fwd`` for Gated DeltaNet-2 (separate erase and write gates);

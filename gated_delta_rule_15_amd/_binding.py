@@ -1,11 +1,16 @@
 """ctypes binding of libgdr (include/gdr.h): argument marshalling only.
 
-PyTorch provides device memory and the current HIP stream; every step of the
-computation runs in the library's HIP kernels.  There is no fallback: if the
-library is missing or a call fails, an exception is raised.
+PyTorch provides device memory and the HIP stream; every step of the computation runs in the
+library's HIP kernels.  There is no fallback: if the library is missing or a call fails, an
+exception is raised.
+
+Buffers the binding allocates (outputs, and the workspace when none is passed) are allocated
+while the call's stream is torch's current stream, so torch's caching allocator orders their
+reuse after the kernels enqueued on that stream.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import threading
@@ -14,15 +19,20 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIBRARY_PATH = os.path.join(_PKG, "libgdr.so")
 
 GDR_OK = 0
+GDR_ERR_INVALID_ARG = 1
 GDR_ERR_SHAPE = 2
+GDR_ERR_DTYPE = 3
+GDR_ERR_UNSUPPORTED = 4
+GDR_ERR_WORKSPACE = 5
+GDR_ERR_HIP = 6
 GDR_BF16, GDR_F32 = 0, 1
 GDR_GATE_SCALAR, GDR_GATE_CHANNEL = 0, 1
 
 # every entry point include/gdr.h declares
-EXPORTED_SYMBOLS = ("gdr_version", "gdr_status_string", "gdr_chunk_fwd", "gdr_chunk_fwd_workspace_size",
-                    "gdr_chunk_fwd_ws", "gdr_chunk_fwd_fused_prep",
-                    "gdr_chunk_fwd_fused_prep_workspace_size", "gdr_chunk_fwd_fused_prep_ws", "gdr_gdp_chunk_fwd", "gdr_gdp_chunk_fwd_workspace_size", "gdr_gdp_chunk_fwd_ws", "gdr_gdn2_chunk_fwd",
-                    "gdr_gdn2_chunk_fwd_workspace_size", "gdr_gdn2_chunk_fwd_ws", "gdr_frame_fwd_workspace_size", "gdr_frame_fwd", "gdr_decode_step")
+EXPORTED_SYMBOLS = ("gdr_version", "gdr_status_string", "gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd",
+                    "gdr_chunk_fwd_fused_prep_workspace_size", "gdr_chunk_fwd_fused_prep",
+                    "gdr_gdp_chunk_fwd_workspace_size", "gdr_gdp_chunk_fwd", "gdr_gdn2_chunk_fwd_workspace_size",
+                    "gdr_gdn2_chunk_fwd", "gdr_frame_fwd_workspace_size", "gdr_frame_fwd", "gdr_decode_step")
 
 _lock = threading.Lock()
 _lib = None
@@ -44,41 +54,25 @@ def load_library():
             raise OSError(f"{LIBRARY_PATH} not found: build it first (python -c 'import __graft_entry__ as g; g.build()')")
         lib = ctypes.CDLL(LIBRARY_PATH)
         i64, i32, P = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
-        lib.gdr_version.restype = i32
-        lib.gdr_version.argtypes = []
-        lib.gdr_status_string.restype = ctypes.c_char_p
-        lib.gdr_status_string.argtypes = [i32]
-        lib.gdr_chunk_fwd.restype = i32
-        lib.gdr_chunk_fwd.argtypes = [i64, i64, i64, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P]
-        lib.gdr_chunk_fwd_workspace_size.restype = i64
-        lib.gdr_chunk_fwd_workspace_size.argtypes = [i64, i64, i64, i32, i32, i32, i32]
-        lib.gdr_chunk_fwd_ws.restype = i32
-        lib.gdr_chunk_fwd_ws.argtypes = [i64, i64, i64, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, i64, P]
-        lib.gdr_chunk_fwd_fused_prep.restype = i32
-        lib.gdr_chunk_fwd_fused_prep.argtypes = [i64, i64, i64, i32, i32, i32, P, P, P, P, P, P, P, P, P, P, P]
-        lib.gdr_chunk_fwd_fused_prep_workspace_size.restype = i64
-        lib.gdr_chunk_fwd_fused_prep_workspace_size.argtypes = [i64, i64, i64, i32, i32]
-        lib.gdr_chunk_fwd_fused_prep_ws.restype = i32
-        lib.gdr_chunk_fwd_fused_prep_ws.argtypes = [i64, i64, i64, i32, i32, i32, P, P, P, P, P, P, P, P, P, P, P,
-                                                    i64, P]
-        lib.gdr_gdp_chunk_fwd.restype = i32
-        lib.gdr_gdp_chunk_fwd.argtypes = [i64, i64, i64, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P]
-        lib.gdr_gdp_chunk_fwd_workspace_size.restype = i64
-        lib.gdr_gdp_chunk_fwd_workspace_size.argtypes = [i64, i64, i64, i32, i32, i32]
-        lib.gdr_gdp_chunk_fwd_ws.restype = i32
-        lib.gdr_gdp_chunk_fwd_ws.argtypes = [i64, i64, i64, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, i64, P]
-        lib.gdr_gdn2_chunk_fwd.restype = i32
-        lib.gdr_gdn2_chunk_fwd.argtypes = [i64, i64, i64, i32, i32, i32, P, P, P, P, P, P, P, P, P, P]
-        lib.gdr_gdn2_chunk_fwd_workspace_size.restype = i64
-        lib.gdr_gdn2_chunk_fwd_workspace_size.argtypes = [i64, i64, i64, i32, i32]
-        lib.gdr_gdn2_chunk_fwd_ws.restype = i32
-        lib.gdr_gdn2_chunk_fwd_ws.argtypes = [i64, i64, i64, i32, i32, i32, P, P, P, P, P, P, P, P, P, P, i64, P]
-        lib.gdr_frame_fwd_workspace_size.restype = i64
-        lib.gdr_frame_fwd_workspace_size.argtypes = [i64, i64, i64, i32, i32, i32]
-        lib.gdr_frame_fwd.restype = i32
-        lib.gdr_frame_fwd.argtypes = [i64, i64, i64, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, i64, P]
-        lib.gdr_decode_step.restype = i32
-        lib.gdr_decode_step.argtypes = [i64, i64, i32, i32, i32, i32, P, P, P, P, P, P, P, P]
+        sigs = {
+            "gdr_version": (i32, []),
+            "gdr_status_string": (ctypes.c_char_p, [i32]),
+            "gdr_chunk_fwd_workspace_size": (i64, [i64, i64, i64, i32, i32, i32, i32]),
+            "gdr_chunk_fwd": (i32, [i64, i64, i64, i32, i32, i32, i32] + [P] * 9 + [i64, P]),
+            "gdr_chunk_fwd_fused_prep_workspace_size": (i64, [i64, i64, i64, i32, i32]),
+            "gdr_chunk_fwd_fused_prep": (i32, [i64, i64, i64, i32, i32, i32] + [P] * 11 + [i64, P]),
+            "gdr_gdp_chunk_fwd_workspace_size": (i64, [i64, i64, i64, i32, i32, i32]),
+            "gdr_gdp_chunk_fwd": (i32, [i64, i64, i64, i32, i32, i32, i32] + [P] * 9 + [i64, P]),
+            "gdr_gdn2_chunk_fwd_workspace_size": (i64, [i64, i64, i64, i32, i32]),
+            "gdr_gdn2_chunk_fwd": (i32, [i64, i64, i64, i32, i32, i32] + [P] * 10 + [i64, P]),
+            "gdr_frame_fwd_workspace_size": (i64, [i64, i64, i64, i32, i32, i32]),
+            "gdr_frame_fwd": (i32, [i64, i64, i64, i32, i32, i32, i32, i32] + [P] * 9 + [i64, P]),
+            "gdr_decode_step": (i32, [i64, i64, i32, i32, i32, i32] + [P] * 8),
+        }
+        for name, (res, args) in sigs.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
         _lib = lib
         return lib
 
@@ -101,6 +95,12 @@ def _stream(stream, device):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _on(stream):
+    """Context in which allocations belong to the call's stream (torch's current one if None)."""
+    import torch
+    return contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
+
+
 def _io_dtype(t):
     import torch
     if t.dtype == torch.bfloat16:
@@ -121,23 +121,52 @@ def _check(t, name, shape, dtype, device):
         raise ValueError(f"{name}: must be contiguous")
 
 
-def chunk_fwd_workspace_size(B, H, T, d_k, d_v, io_dtype=GDR_BF16, gate=GDR_GATE_SCALAR) -> int:
-    """gdr_chunk_fwd_workspace_size: bytes of workspace the two-kernel path needs (0: none)."""
-    n = int(load_library().gdr_chunk_fwd_workspace_size(B, H, T, d_k, d_v, io_dtype, gate))
+def _size(n, where):
+    n = int(n)
     if n < 0:
-        raise GdrError(GDR_ERR_SHAPE, "gdr_chunk_fwd_workspace_size")
+        raise GdrError(GDR_ERR_SHAPE, where)
     return n
 
 
+def _outputs(o_shape, io_torch_dtype, S_shape, dev, out, final_state, output_final_state, stream):
+    import torch
+    with _on(stream):
+        o = torch.empty(o_shape, dtype=io_torch_dtype, device=dev) if out is None else out
+        if output_final_state and final_state is None:
+            final_state = torch.empty(S_shape, dtype=torch.float32, device=dev)
+    _check(o, "out", o_shape, io_torch_dtype, dev)
+    if final_state is not None:
+        _check(final_state, "final_state", S_shape, torch.float32, dev)
+    return o, final_state
+
+
+def _workspace(workspace, need, dev, stream):
+    """The caller's uint8 workspace tensor, or (None) one allocated on the call's stream."""
+    import torch
+    if workspace is None:
+        if need == 0:
+            return None, 0
+        with _on(stream):
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace: must be a contiguous tensor on the inputs' device")
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def chunk_fwd_workspace_size(B, H, T, d_k, d_v, io_dtype=GDR_BF16, gate=GDR_GATE_SCALAR) -> int:
+    """gdr_chunk_fwd_workspace_size: bytes of workspace gdr_chunk_fwd needs (0: none)."""
+    return _size(load_library().gdr_chunk_fwd_workspace_size(B, H, T, d_k, d_v, io_dtype, gate),
+                 "gdr_chunk_fwd_workspace_size")
+
+
 def chunk_fwd(q, k, v, g, beta, initial_state=None, *, output_final_state=True, out=None,
-              final_state=None, stream=None, workspace="auto"):
-    """The chunked forward on torch tensors.
+              final_state=None, stream=None, workspace=None):
+    """gdr_chunk_fwd on torch tensors.
 
     q, k [B,H,T,d_k]; v [B,H,T,d_v] (bf16 or fp32); g [B,H,T] or [B,H,T,d_k] fp32
     (log-decay); beta [B,H,T] fp32; initial_state [B,H,d_v,d_k] fp32 or None.
-    workspace: "auto" (default) allocates the two-kernel path's workspace with torch and
-    calls gdr_chunk_fwd_ws; a uint8 CUDA tensor is used as that workspace; None calls
-    gdr_chunk_fwd (one kernel, no workspace).
+    workspace: a uint8 CUDA tensor of at least chunk_fwd_workspace_size(...) bytes, or None
+    (allocated with torch on the call's stream).
     Returns (o, final_state); final_state is None when output_final_state is False.
     """
     import torch
@@ -160,52 +189,31 @@ def chunk_fwd(q, k, v, g, beta, initial_state=None, *, output_final_state=True, 
     _check(beta, "beta", (B, H, T), torch.float32, dev)
     if initial_state is not None:
         _check(initial_state, "initial_state", (B, H, dv, dk), torch.float32, dev)
-    o = torch.empty((B, H, T, dv), dtype=q.dtype, device=dev) if out is None else out
-    _check(o, "out", (B, H, T, dv), q.dtype, dev)
-    if output_final_state and final_state is None:
-        final_state = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
-    if final_state is not None:
-        _check(final_state, "final_state", (B, H, dv, dk), torch.float32, dev)
-    if workspace is None:
-        st = load_library().gdr_chunk_fwd(B, H, T, dk, dv, io, gate, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
-                                          _ptr(beta), _ptr(initial_state), _ptr(o), _ptr(final_state),
-                                          _stream(stream, dev))
-        if st != GDR_OK:
-            raise GdrError(st, "gdr_chunk_fwd")
-        return o, final_state
+    o, final_state = _outputs((B, H, T, dv), q.dtype, (B, H, dv, dk), dev, out, final_state, output_final_state,
+                              stream)
     need = chunk_fwd_workspace_size(B, H, T, dk, dv, io, gate)
-    if isinstance(workspace, str):
-        if workspace != "auto":
-            raise ValueError(f"workspace: expected 'auto', None or a tensor, got {workspace!r}")
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    if workspace.device != dev or not workspace.is_contiguous():
-        raise ValueError("workspace: must be a contiguous tensor on the inputs' device")
-    nbytes = workspace.numel() * workspace.element_size()
-    st = load_library().gdr_chunk_fwd_ws(B, H, T, dk, dv, io, gate, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                                         _ptr(initial_state), _ptr(o), _ptr(final_state), _ptr(workspace), nbytes,
-                                         _stream(stream, dev))
+    ws, nbytes = _workspace(workspace, need, dev, stream)
+    st = load_library().gdr_chunk_fwd(B, H, T, dk, dv, io, gate, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                      _ptr(initial_state), _ptr(o), _ptr(final_state), _ptr(ws), nbytes,
+                                      _stream(stream, dev))
     if st != GDR_OK:
-        raise GdrError(st, "gdr_chunk_fwd_ws")
+        raise GdrError(st, "gdr_chunk_fwd")
     return o, final_state
 
 
 def chunk_fwd_fused_prep_workspace_size(B, H, T, d_k, d_v) -> int:
-    n = int(load_library().gdr_chunk_fwd_fused_prep_workspace_size(B, H, T, d_k, d_v))
-    if n < 0:
-        raise GdrError(GDR_ERR_SHAPE, "gdr_chunk_fwd_fused_prep_workspace_size")
-    return n
+    return _size(load_library().gdr_chunk_fwd_fused_prep_workspace_size(B, H, T, d_k, d_v),
+                 "gdr_chunk_fwd_fused_prep_workspace_size")
 
 
 def chunk_fwd_fused_prep(q_raw, k_raw, v, dt, A_log, dt_bias, beta_logit, initial_state=None, *,
-                         output_final_state=True, out=None, final_state=None, stream=None, workspace="auto"):
-    """The scalar-gate chunked forward from raw projections (q, k normalised, beta =
-    sigmoid(beta_logit), g = -exp(A_log) softplus(dt + dt_bias) inside the kernels):
-    gdr_chunk_fwd_fused_prep_ws, or gdr_chunk_fwd_fused_prep with workspace=None.
+                         output_final_state=True, out=None, final_state=None, stream=None, workspace=None):
+    """gdr_chunk_fwd_fused_prep: the scalar-gate chunked forward from raw projections (q, k
+    normalised, beta = sigmoid(beta_logit), g = -exp(A_log) softplus(dt + dt_bias) inside the
+    kernels).
 
     q_raw, k_raw [B,H,T,d_k], v [B,H,T,d_v] (bf16); dt, beta_logit [B,H,T] fp32;
-    A_log, dt_bias [H] fp32; initial_state [B,H,d_v,d_k] fp32 or None.  workspace: "auto"
-    (default) allocates the two-kernel path's workspace with torch; a uint8 CUDA tensor is used
-    as that workspace; None calls the single kernel.
+    A_log, dt_bias [H] fp32; initial_state [B,H,d_v,d_k] fp32 or None; workspace as chunk_fwd.
     Returns (o, final_state); final_state is None when output_final_state is False.
     """
     import torch
@@ -224,52 +232,29 @@ def chunk_fwd_fused_prep(q_raw, k_raw, v, dt, A_log, dt_bias, beta_logit, initia
     _check(dt_bias, "dt_bias", (H,), torch.float32, dev)
     if initial_state is not None:
         _check(initial_state, "initial_state", (B, H, dv, dk), torch.float32, dev)
-    o = torch.empty((B, H, T, dv), dtype=q_raw.dtype, device=dev) if out is None else out
-    _check(o, "out", (B, H, T, dv), q_raw.dtype, dev)
-    if output_final_state and final_state is None:
-        final_state = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
-    if final_state is not None:
-        _check(final_state, "final_state", (B, H, dv, dk), torch.float32, dev)
-    if workspace is None:
-        st = load_library().gdr_chunk_fwd_fused_prep(B, H, T, dk, dv, io, _ptr(q_raw), _ptr(k_raw), _ptr(v),
-                                                     _ptr(dt), _ptr(A_log), _ptr(dt_bias), _ptr(beta_logit),
-                                                     _ptr(initial_state), _ptr(o), _ptr(final_state),
-                                                     _stream(stream, dev))
-        if st != GDR_OK:
-            raise GdrError(st, "gdr_chunk_fwd_fused_prep")
-        return o, final_state
-    need = chunk_fwd_fused_prep_workspace_size(B, H, T, dk, dv)
-    if isinstance(workspace, str):
-        if workspace != "auto":
-            raise ValueError(f"workspace: expected 'auto', None or a tensor, got {workspace!r}")
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    if workspace.device != dev or not workspace.is_contiguous():
-        raise ValueError("workspace: must be a contiguous tensor on the inputs' device")
-    nbytes = workspace.numel() * workspace.element_size()
-    st = load_library().gdr_chunk_fwd_fused_prep_ws(B, H, T, dk, dv, io, _ptr(q_raw), _ptr(k_raw), _ptr(v), _ptr(dt),
-                                                    _ptr(A_log), _ptr(dt_bias), _ptr(beta_logit),
-                                                    _ptr(initial_state), _ptr(o), _ptr(final_state), _ptr(workspace),
-                                                    nbytes, _stream(stream, dev))
+    o, final_state = _outputs((B, H, T, dv), q_raw.dtype, (B, H, dv, dk), dev, out, final_state,
+                              output_final_state, stream)
+    ws, nbytes = _workspace(workspace, chunk_fwd_fused_prep_workspace_size(B, H, T, dk, dv), dev, stream)
+    st = load_library().gdr_chunk_fwd_fused_prep(B, H, T, dk, dv, io, _ptr(q_raw), _ptr(k_raw), _ptr(v), _ptr(dt),
+                                                 _ptr(A_log), _ptr(dt_bias), _ptr(beta_logit), _ptr(initial_state),
+                                                 _ptr(o), _ptr(final_state), _ptr(ws), nbytes, _stream(stream, dev))
     if st != GDR_OK:
-        raise GdrError(st, "gdr_chunk_fwd_fused_prep_ws")
+        raise GdrError(st, "gdr_chunk_fwd_fused_prep")
     return o, final_state
 
 
 def gdp_chunk_fwd_workspace_size(B, H, T, n_h, d_k, d_v) -> int:
-    n = int(load_library().gdr_gdp_chunk_fwd_workspace_size(B, H, T, n_h, d_k, d_v))
-    if n < 0:
-        raise GdrError(GDR_ERR_SHAPE, "gdr_gdp_chunk_fwd_workspace_size")
-    return n
+    return _size(load_library().gdr_gdp_chunk_fwd_workspace_size(B, H, T, n_h, d_k, d_v),
+                 "gdr_gdp_chunk_fwd_workspace_size")
 
 
 def gdp_chunk_fwd(q, k, v, g, beta, initial_state=None, *, output_final_state=True, out=None,
-                  final_state=None, stream=None, workspace="auto"):
-    """Gated Delta Product (gdr_gdp_chunk_fwd_ws, or gdr_gdp_chunk_fwd) on torch tensors.
+                  final_state=None, stream=None, workspace=None):
+    """gdr_gdp_chunk_fwd (Gated Delta Product) on torch tensors.
 
     q [B,H,T,d_k]; k [B,H,T,n_h,d_k]; v [B,H,T,n_h,d_v] (bf16); g [B,H,T] fp32 (one
-    log-decay per token); beta [B,H,T,n_h] fp32; initial_state [B,H,d_v,d_k] fp32 or None.
-    workspace: "auto" (default) allocates the two-kernel path's workspace with torch; a uint8
-    CUDA tensor is used as that workspace; None calls the single kernel.
+    log-decay per token); beta [B,H,T,n_h] fp32; initial_state [B,H,d_v,d_k] fp32 or None;
+    workspace as chunk_fwd.
     Returns (o [B,H,T,d_v], final_state); final_state is None when output_final_state is False.
     """
     import torch
@@ -289,52 +274,30 @@ def gdp_chunk_fwd(q, k, v, g, beta, initial_state=None, *, output_final_state=Tr
     _check(beta, "beta", (B, H, T, nh), torch.float32, dev)
     if initial_state is not None:
         _check(initial_state, "initial_state", (B, H, dv, dk), torch.float32, dev)
-    o = torch.empty((B, H, T, dv), dtype=q.dtype, device=dev) if out is None else out
-    _check(o, "out", (B, H, T, dv), q.dtype, dev)
-    if output_final_state and final_state is None:
-        final_state = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
-    if final_state is not None:
-        _check(final_state, "final_state", (B, H, dv, dk), torch.float32, dev)
-    if workspace is None:
-        st = load_library().gdr_gdp_chunk_fwd(B, H, T, nh, dk, dv, io, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
-                                              _ptr(beta), _ptr(initial_state), _ptr(o), _ptr(final_state),
-                                              _stream(stream, dev))
-        if st != GDR_OK:
-            raise GdrError(st, "gdr_gdp_chunk_fwd")
-        return o, final_state
-    need = gdp_chunk_fwd_workspace_size(B, H, T, nh, dk, dv)
-    if isinstance(workspace, str):
-        if workspace != "auto":
-            raise ValueError(f"workspace: expected 'auto', None or a tensor, got {workspace!r}")
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    if workspace.device != dev or not workspace.is_contiguous():
-        raise ValueError("workspace: must be a contiguous tensor on the inputs' device")
-    nbytes = workspace.numel() * workspace.element_size()
-    st = load_library().gdr_gdp_chunk_fwd_ws(B, H, T, nh, dk, dv, io, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
-                                             _ptr(beta), _ptr(initial_state), _ptr(o), _ptr(final_state),
-                                             _ptr(workspace), nbytes, _stream(stream, dev))
+    o, final_state = _outputs((B, H, T, dv), q.dtype, (B, H, dv, dk), dev, out, final_state, output_final_state,
+                              stream)
+    ws, nbytes = _workspace(workspace, gdp_chunk_fwd_workspace_size(B, H, T, nh, dk, dv), dev, stream)
+    st = load_library().gdr_gdp_chunk_fwd(B, H, T, nh, dk, dv, io, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                          _ptr(initial_state), _ptr(o), _ptr(final_state), _ptr(ws), nbytes,
+                                          _stream(stream, dev))
     if st != GDR_OK:
-        raise GdrError(st, "gdr_gdp_chunk_fwd_ws")
+        raise GdrError(st, "gdr_gdp_chunk_fwd")
     return o, final_state
 
 
 def gdn2_chunk_fwd_workspace_size(B, H, T, d_k, d_v) -> int:
-    n = int(load_library().gdr_gdn2_chunk_fwd_workspace_size(B, H, T, d_k, d_v))
-    if n < 0:
-        raise GdrError(GDR_ERR_SHAPE, "gdr_gdn2_chunk_fwd_workspace_size")
-    return n
+    return _size(load_library().gdr_gdn2_chunk_fwd_workspace_size(B, H, T, d_k, d_v),
+                 "gdr_gdn2_chunk_fwd_workspace_size")
 
 
 def gdn2_chunk_fwd(q, k, v, g, b, w, initial_state=None, *, output_final_state=True, out=None,
-                   final_state=None, stream=None, workspace="auto"):
-    """Gated DeltaNet-2 (gdr_gdn2_chunk_fwd_ws, or gdr_gdn2_chunk_fwd) on torch tensors.
+                   final_state=None, stream=None, workspace=None):
+    """gdr_gdn2_chunk_fwd (Gated DeltaNet-2) on torch tensors.
 
     q, k [B,H,T,d_k]; v [B,H,T,d_v] (bf16); g [B,H,T,d_k] fp32 (per-channel log-decay);
     b [B,H,T,d_k] fp32 (erase gate); w [B,H,T,d_v] fp32 (write gate); initial_state
-    [B,H,d_v,d_k] fp32 or None.  workspace: "auto" (default) allocates the two-kernel path's
-    workspace with torch; a uint8 CUDA tensor is used as that workspace; None calls the
-    single kernel.  Returns (o, final_state); final_state is None when output_final_state is
-    False.
+    [B,H,d_v,d_k] fp32 or None; workspace as chunk_fwd.
+    Returns (o, final_state); final_state is None when output_final_state is False.
     """
     import torch
     B, H, T, dk = q.shape
@@ -351,40 +314,20 @@ def gdn2_chunk_fwd(q, k, v, g, b, w, initial_state=None, *, output_final_state=T
     _check(w, "w", (B, H, T, dv), torch.float32, dev)
     if initial_state is not None:
         _check(initial_state, "initial_state", (B, H, dv, dk), torch.float32, dev)
-    o = torch.empty((B, H, T, dv), dtype=q.dtype, device=dev) if out is None else out
-    _check(o, "out", (B, H, T, dv), q.dtype, dev)
-    if output_final_state and final_state is None:
-        final_state = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
-    if final_state is not None:
-        _check(final_state, "final_state", (B, H, dv, dk), torch.float32, dev)
-    if workspace is None:
-        st = load_library().gdr_gdn2_chunk_fwd(B, H, T, dk, dv, io, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b),
-                                               _ptr(w), _ptr(initial_state), _ptr(o), _ptr(final_state),
-                                               _stream(stream, dev))
-        if st != GDR_OK:
-            raise GdrError(st, "gdr_gdn2_chunk_fwd")
-        return o, final_state
-    need = gdn2_chunk_fwd_workspace_size(B, H, T, dk, dv)
-    if isinstance(workspace, str):
-        if workspace != "auto":
-            raise ValueError(f"workspace: expected 'auto', None or a tensor, got {workspace!r}")
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    if workspace.device != dev or not workspace.is_contiguous():
-        raise ValueError("workspace: must be a contiguous tensor on the inputs' device")
-    nbytes = workspace.numel() * workspace.element_size()
-    st = load_library().gdr_gdn2_chunk_fwd_ws(B, H, T, dk, dv, io, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b),
-                                              _ptr(w), _ptr(initial_state), _ptr(o), _ptr(final_state),
-                                              _ptr(workspace), nbytes, _stream(stream, dev))
+    o, final_state = _outputs((B, H, T, dv), q.dtype, (B, H, dv, dk), dev, out, final_state, output_final_state,
+                              stream)
+    ws, nbytes = _workspace(workspace, gdn2_chunk_fwd_workspace_size(B, H, T, dk, dv), dev, stream)
+    st = load_library().gdr_gdn2_chunk_fwd(B, H, T, dk, dv, io, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), _ptr(w),
+                                           _ptr(initial_state), _ptr(o), _ptr(final_state), _ptr(ws), nbytes,
+                                           _stream(stream, dev))
     if st != GDR_OK:
-        raise GdrError(st, "gdr_gdn2_chunk_fwd_ws")
+        raise GdrError(st, "gdr_gdn2_chunk_fwd")
     return o, final_state
 
 
 def frame_fwd_workspace_size(B, H, T, frame_len, d_k, d_v) -> int:
-    n = int(load_library().gdr_frame_fwd_workspace_size(B, H, T, frame_len, d_k, d_v))
-    if n < 0:
-        raise GdrError(GDR_ERR_SHAPE, "gdr_frame_fwd_workspace_size")
-    return n
+    return _size(load_library().gdr_frame_fwd_workspace_size(B, H, T, frame_len, d_k, d_v),
+                 "gdr_frame_fwd_workspace_size")
 
 
 def frame_fwd(q, k, v, gamma, g, frame_len, initial_state=None, *, output_final_state=True, out=None,
@@ -393,7 +336,7 @@ def frame_fwd(q, k, v, gamma, g, frame_len, initial_state=None, *, output_final_
 
     q, k [B,H,T,d_k]; v [B,H,T,d_v] (bf16); gamma [B,H,T] fp32; g [B,H,F] or [B,H,F,d_k]
     fp32 (log forget gate per frame, F = ceil(T / frame_len)); initial_state [B,H,d_v,d_k]
-    fp32 or None; workspace: a uint8 CUDA tensor or None (allocated with torch).
+    fp32 or None; workspace as chunk_fwd.
     Returns (o, final_state); final_state is None when output_final_state is False.
     """
     import torch
@@ -416,19 +359,12 @@ def frame_fwd(q, k, v, gamma, g, frame_len, initial_state=None, *, output_final_
     _check(g, "g", tuple(g.shape), torch.float32, dev)
     if initial_state is not None:
         _check(initial_state, "initial_state", (B, H, dv, dk), torch.float32, dev)
-    o = torch.empty((B, H, T, dv), dtype=q.dtype, device=dev) if out is None else out
-    _check(o, "out", (B, H, T, dv), q.dtype, dev)
-    if output_final_state and final_state is None:
-        final_state = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
-    if final_state is not None:
-        _check(final_state, "final_state", (B, H, dv, dk), torch.float32, dev)
-    if workspace is None:
-        workspace = torch.empty(max(frame_fwd_workspace_size(B, H, T, frame_len, dk, dv), 1), dtype=torch.uint8,
-                                device=dev)
-    nbytes = workspace.numel() * workspace.element_size()
+    o, final_state = _outputs((B, H, T, dv), q.dtype, (B, H, dv, dk), dev, out, final_state, output_final_state,
+                              stream)
+    ws, nbytes = _workspace(workspace, frame_fwd_workspace_size(B, H, T, frame_len, dk, dv), dev, stream)
     st = load_library().gdr_frame_fwd(B, H, T, frame_len, dk, dv, io, gate, _ptr(q), _ptr(k), _ptr(v), _ptr(gamma),
-                                      _ptr(g), _ptr(initial_state), _ptr(o), _ptr(final_state), _ptr(workspace),
-                                      nbytes, _stream(stream, dev))
+                                      _ptr(g), _ptr(initial_state), _ptr(o), _ptr(final_state), _ptr(ws), nbytes,
+                                      _stream(stream, dev))
     if st != GDR_OK:
         raise GdrError(st, "gdr_frame_fwd")
     return o, final_state
@@ -457,7 +393,8 @@ def decode_step(q, k, v, g, beta, state, *, out=None, stream=None):
     _check(g, "g", tuple(g.shape), torch.float32, dev)
     _check(beta, "beta", (N, H), torch.float32, dev)
     _check(state, "state", (N, H, dv, dk), torch.float32, dev)
-    o = torch.empty((N, H, dv), dtype=q.dtype, device=dev) if out is None else out
+    with _on(stream):
+        o = torch.empty((N, H, dv), dtype=q.dtype, device=dev) if out is None else out
     _check(o, "out", (N, H, dv), q.dtype, dev)
     st = load_library().gdr_decode_step(N, H, dk, dv, io, gate, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                         _ptr(state), _ptr(o), _stream(stream, dev))

@@ -128,6 +128,29 @@ __device__ __forceinline__ float wave_inclusive_scan(float x) {
     x = dpp_add(x, __builtin_amdgcn_update_dpp(0, b, 0x143, 0xc, 0xf, false));  // row_bcast:31
     return x;
 }
+// Largest |x| over a lane's registers (NaN entries are ignored by max).
+template <int N>
+__device__ __forceinline__ float max_abs(const float4v (&x)[N]) {
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) m = fmaxf(m, fabsf(x[i][r]));
+    return m;
+}
+// Largest value over the 64 lanes, the same in every lane: a DPP reduction inside each 16-lane
+// row (quad_perm xor 1 and xor 2, row_half_mirror, row_mirror), then the four row results.
+__device__ __forceinline__ float wave_max_abs(float m) {
+    m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0xB1, 0xf, 0xf, false)));
+    m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x4E, 0xf, 0xf, false)));
+    m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x141, 0xf, 0xf, false)));
+    m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x140, 0xf, 0xf, false)));
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
 __device__ __forceinline__ float lane_value(float x, int lane) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
 }

@@ -401,10 +401,10 @@ static hipError_t launch_chunk_scalar(const ChunkArgs& a, int64_t nwg, hipStream
     return hipGetLastError();
 }
 
-hipError_t chunk_fwd_dispatch(int64_t BH, int64_t T, int dk, int dv, bool bf16, bool channel,
-                              const void* q, const void* k, const void* v, const float* g, const float* beta,
-                              const float* S0, void* o, float* Sf, hipStream_t st) {
-    (void)channel;
+// fp32 I/O, scalar gate, d_k = 64 (the only fp32 configuration the C ABI accepts).
+hipError_t chunk_fwd_f32_dispatch(int64_t BH, int64_t T, int dv, const void* q, const void* k, const void* v,
+                                  const float* g, const float* beta, const float* S0, void* o, float* Sf,
+                                  hipStream_t st) {
     ChunkArgs a;
     a.T = T;
     a.dv = dv;
@@ -417,10 +417,7 @@ hipError_t chunk_fwd_dispatch(int64_t BH, int64_t T, int dk, int dv, bool bf16, 
     a.S0 = S0;
     a.o = o;
     a.Sf = Sf;
-    const int64_t nwg = BH * a.ntiles;
-    (void)bf16;  // bf16 I/O runs in chunk_fwd_pc.hip
-    (void)dk;    // fp32 I/O: d_k = 64 (checked by the caller)
-    return launch_chunk_scalar<64, float, float>(a, nwg, st);
+    return launch_chunk_scalar<64, float, float>(a, BH * a.ntiles, st);
 }
 
 }  // namespace gdr

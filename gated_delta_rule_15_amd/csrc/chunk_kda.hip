@@ -1,5 +1,6 @@
-// chunk_kda.hip -- chunked forward of the gated delta rule with a per-channel gate
-// (KDA-style), bf16 I/O, fp16 MFMA operands, fp32 accumulation and state, gfx950.
+// chunk_kda.hip -- UT pass of the chunked forward with a per-channel gate (KDA-style) and of
+// Gated DeltaNet-2, bf16 inputs, fp16 MFMA operands, fp32 accumulation, gfx950.  The state
+// pass that follows it is chunk_state_kernel (chunk_split.hip) in its per-channel modes.
 //
 // "Linear Attention, Visualized", sections "Kimi Delta Attention (KDA)" and "Reuse GLA and
 // GDN": the decay a_t is a vector over the key channels and acts on S before the delta
@@ -11,7 +12,9 @@
 //   R = V - (K (.) e^G) S^T,   Z = T R,   O = (Q (.) e^G) S^T + A Z
 //   S^T <- Diag(e^{G_C}) S^T + (K (.) e^{G_C - G})^T Z
 //
-// The decay sits inside the channel sum, so the Gram products take it on their operands:
+// Everything but the last three lines depends on the chunk alone; this kernel forms it for all
+// chunks at once.  The decay sits inside the channel sum, so the Gram products take it on their
+// operands:
 //   off-diagonal 16x16 tiles (row block bi > column block bj), reference = end of block bj:
 //     row operand  K_l e^{G_l - G_start(bi)}            ("Kr", <= 1, one copy of K and Q)
 //     column       K_m e^{G_end(bj) - G_m}              ("Kc", <= 1)
@@ -19,26 +22,18 @@
 //   diagonal tiles, reference = token 8 of the block: Kr and Kc times e^{-G_loc(8)} and
 //     e^{G_loc(8) - G_loc(15)}, per channel (G_loc = cumulative log-decay from the block
 //     start).  Those factors exceed 1 by up to e^{8|g|}.  While every |G_loc(t) - G_loc(8)|
-//     (t = -1..15, G_loc(-1) = 0) stays within 6 the fp16 path is exact to fp16 rounding;
-//     a block beyond that forms its diagonal operands afresh from the bf16 inputs in fp32
-//     (e^{G_loc(l) - G_loc(8)} k_l, e^{G_loc(8) - G_loc(m)} k_m) and multiplies them on bf16
-//     MFMA, whose exponent range covers any decay the fp32 gate can express.
-// After the Gram products the copies are rescaled in place to K (.) e^G, Q (.) e^G and
-// K (.) e^{G_C - G} for the state pass (per-block, per-channel factors <= 1).
+//     (t = -1..15, G_loc(-1) = 0) stays within 6 the fp16 path is exact to fp16 rounding.
+//     A block beyond that ("flagged") is formed afresh from the bf16 inputs with every factor
+//     of the form e^{G_i - G_j}, i >= j, so at most 1 whatever the decay (see diag_exact).
 //
-// One workgroup (four waves) per (batch*head, 32-wide d_v tile) walks the chunks in order;
-// each chunk runs stage by stage with all waves: scan, staging, Gram, the inverses of the
-// four 16x16 diagonal blocks of N, then the state pass on waves 0-1, which applies
-// N^{-1} diag(beta) by blocked forward substitution (as in the scalar kernel).  Loads of
-// chunk c+1 are in flight while chunk c is processed.
-//
-// The UT instantiation runs the scan, tables, Gram and diagonal inverses for a run of
-// consecutive chunks per workgroup (all runs at once), adds the blocks of N^{-1} below the
-// diagonal (M_bc = -X_bb sum_{c<=d<b} N_bd M_dc) and writes, per (sequence, chunk), the
-// operands of the two-kernel state pass to a workspace: A^T and T = N^{-1} diag(beta) (fp16,
-// T's columns pperm'd), the decayed copies K e^G, Q e^G and K e^{G_C - G} (fp16, rescaled on
-// the way out rather than in place) and e^{G_C} per key channel (fp32).  Waves 2-3 write the
-// copies while waves 0-1 form the inverses.
+// One workgroup (four waves) per (sequence, run of consecutive chunks), all runs at once; each
+// chunk runs stage by stage with all waves: scan, staging, Gram, the inverses of the four 16x16
+// diagonal blocks of N, the blocks of N^{-1} below the diagonal
+// (M_bc = -X_bb sum_{c<=d<b} N_bd M_dc), and the copy-out.  Loads of the next chunk are in
+// flight while a chunk is processed.  Per (sequence, chunk) the workspace receives the operands
+// of the state pass: A^T and T = N^{-1} diag(beta) (fp16, T's columns pperm'd), the decayed
+// copies K e^G, Q e^G and K e^{G_C - G} (fp16, rescaled on the way out) and e^{G_C} per key
+// channel (fp32).  Waves 2-3 write the copies while waves 0-1 form the inverses.
 //
 // Gated DeltaNet-2 ("Gated DeltaNet-2, and the gate that was doing two jobs", section 2) is
 // the GD2 instantiation.  The scalar beta is replaced by a key-side erase gate b_t and a
@@ -47,32 +42,23 @@
 //   L[l][m] = sum_c e_lc k_mc e^{G_lc - G_mc} (m < l),   N = I + L,   Z = N^{-1} R,
 //   R = Z_in - (E (.) e^G) S^T   (Z_in the rows z_l),
 // and O, A and the state update unchanged: only the row operand of N and of the prediction
-// product changes from beta k to e, and the right-hand side from beta v to z.  So the "Kr"
-// copy holds E e^{G - G_start(blk)} (then E e^G), V^T holds z, and beta is not used.
+// product changes from beta k to e, and the right-hand side from beta v to z (formed by the
+// state pass).  So the "Kr" copy holds E e^{G - G_start(blk)} (then E e^G), and beta is not used.
 #include <type_traits>
 
 #include "chunk_common.h"
 
 namespace gdr {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-
 struct KdaArgs {
     int64_t T;
-    int dv;
-    int ntiles;  // d_v / 32
     const uint16_t* q;
     const uint16_t* k;
-    const uint16_t* v;
     const float* g;  // [.., T, DK]
     const float* beta;
     const float* eg;  // erase gate b [.., T, DK] (GD2)
-    const float* wg;  // write gate w [.., T, d_v] (GD2)
-    const float* S0;
-    uint16_t* o;
-    float* Sf;
-    uint16_t* ws;     // UT: workspace, kda_ws_stride<DK>() halfs per (sequence, chunk)
-    int cpw;          // UT: chunks per workgroup
+    uint16_t* ws;     // kda_ws_stride<DK>() halfs per (sequence, chunk)
+    int cpw;          // chunks per workgroup
 };
 
 template <int DK>
@@ -82,9 +68,7 @@ struct KdaLds {
                                          // free for fragment and transposing reads)
     static constexpr int LDX = 16 + 8;   // halfs, rows of a 16x16 fp16 block
     static constexpr int LDC = C + 8;    // halfs, rows of C-wide fp16 matrices
-    static constexpr int LDV = C + 4;    // floats, rows of V^T
     static constexpr int LDN = 16 + 4;   // floats, rows of a 16x16 fp32 block
-    static constexpr int LDO = C + 8;    // bf16, rows of O^T
     static constexpr int LDG = DK + 4;   // floats, rows of the block-local cumulative log-decay
     static constexpr int szK = C * LDK * 2;
     static constexpr int szC = C * LDC * 2;
@@ -99,27 +83,23 @@ struct KdaLds {
     static constexpr int oHMC = oHMR + 4 * DK * 2;    // fp16: e^{G_loc(8) - Delta_b} [4][DK]
     static constexpr int oHP = oHMC + 4 * DK * 2;     // fp16: e^{G_start(b)} [4][DK]
     static constexpr int oHS = oHP + 4 * DK * 2;      // fp16: e^{G_C - G_end(b)} [4][DK]
-    static constexpr int oFlag = oHS + 4 * DK * 2;    // int [4]: block needs the bf16 diagonal path
-    static constexpr int oKr = oFlag + 16;            // K e^{G - G_start(blk)}, then K e^G
-    static constexpr int oQr = oKr + szK;             // Q e^{G - G_start(blk)}, then Q e^G
-    static constexpr int oKc = oQr + szK;             // K e^{G_end(blk) - G}, then K e^{G_C - G}
+    static constexpr int oFlag = oHS + 4 * DK * 2;    // int [4]: block takes the exact diagonal path
+    static constexpr int oKr = oFlag + 16;            // K e^{G - G_start(blk)}
+    static constexpr int oQr = oKr + szK;             // Q e^{G - G_start(blk)}
+    static constexpr int oKc = oQr + szK;             // K e^{G_end(blk) - G}
     static constexpr int oAt = oKc + szK;             // A^T
     static constexpr int oNt = oAt + szC;             // off-diagonal blocks of N^T (fp16)
     static constexpr int oXd = oNt + szC;             // X_bb^T, diagonal blocks of N^{-1} (fp16)
     static constexpr int oNd = oXd + 4 * 16 * LDX * 2;  // diagonal blocks of N^T (fp32)
     static constexpr int oGl = oNd + 4 * 16 * LDN * 4;  // block-local cumulative log-decay [C][LDG]
-    static constexpr int oVt = oGl + C * LDG * 4;     // V^T fp32 [32][LDV]
-    static constexpr int oOt = oVt + 32 * LDV * 4;    // O^T bf16 [32][LDO]
-    static constexpr int total = oOt + 32 * LDO * 2;
+    static constexpr int oTt = oGl + C * LDG * 4;     // T, staged for the copy-out
+    static constexpr int total = oTt + szC;
     static_assert(total <= 160 * 1024, "LDS budget of one gfx950 CU exceeded");
-    static_assert((oKr | oAt | oNt | oXd | oNd | oGl | oVt | oOt | oFDl | oFE | oHD | oHMR | oHMC |
+    static_assert((oKr | oAt | oNt | oXd | oNd | oGl | oTt | oFDl | oFE | oHD | oHMR | oHMC |
                    oHP | oHS | oFlag) % 16 == 0,
                   "alignment");
 };
 
-__device__ __forceinline__ void mma16_bf16(float4v& acc, const bf16x8& a, const bf16x8& b) {
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
-}
 __device__ __forceinline__ half8 hmul8(const half8& a, const half8& b) { return a * b; }
 __device__ __forceinline__ uint2 bld8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
@@ -127,12 +107,11 @@ __device__ __forceinline__ uint2 bld8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return uint2{v[0], v[1]};
 }
 
-template <int DK, bool GD2, bool UT>
+template <int DK, bool GD2>
 __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
     using L = KdaLds<DK>;
     constexpr int C = kChunk;
     constexpr int NKB = DK / 32;
-    constexpr int NST = DK / 16;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     _Float16* Kr = reinterpret_cast<_Float16*>(smem + L::oKr);
     _Float16* Qr = reinterpret_cast<_Float16*>(smem + L::oQr);
@@ -140,10 +119,9 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
     _Float16* At = reinterpret_cast<_Float16*>(smem + L::oAt);
     _Float16* Nt = reinterpret_cast<_Float16*>(smem + L::oNt);
     _Float16* Xd = reinterpret_cast<_Float16*>(smem + L::oXd);
+    _Float16* Tt = reinterpret_cast<_Float16*>(smem + L::oTt);
     float* Nd = reinterpret_cast<float*>(smem + L::oNd);
     float* Gl = reinterpret_cast<float*>(smem + L::oGl);
-    float* Vt = reinterpret_cast<float*>(smem + L::oVt);
-    _Float16* Ot = reinterpret_cast<_Float16*>(smem + L::oOt);  // bf16 bit patterns
     float* FB = reinterpret_cast<float*>(smem + L::oFB);
     float* FDl = reinterpret_cast<float*>(smem + L::oFDl);
     float* FE = reinterpret_cast<float*>(smem + L::oFE);
@@ -157,46 +135,20 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
     const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, j = l & 15, g = l >> 4;
     const int64_t T = a.T;
     const int64_t nC = (T + C - 1) / C;
-    // state pass: one group per (sequence, 32 value channels) over all chunks; UT: one group per
-    // (sequence, run of cpw consecutive chunks)
-    const int64_t runs = UT ? (nC + a.cpw - 1) / a.cpw : 1;
-    const int vi = UT ? 0 : xcd_major_index(blockIdx.x, gridDim.x);
-    const int64_t bh = UT ? blockIdx.x / runs : vi / a.ntiles;
-    const int64_t c_first = UT ? (blockIdx.x - bh * runs) * a.cpw : 0;
-    const int64_t c_last = UT ? (c_first + a.cpw < nC ? c_first + a.cpw : nC) : nC;
-    const int dv0 = (vi % a.ntiles) * 32;
-    const int DV = a.dv;
+    // one group per (sequence, run of cpw consecutive chunks)
+    const int64_t runs = (nC + a.cpw - 1) / a.cpw;
+    const int64_t bh = blockIdx.x / runs;
+    const int64_t c_first = (blockIdx.x - bh * runs) * a.cpw;
+    const int64_t c_last = c_first + a.cpw < nC ? c_first + a.cpw : nC;
     const auto rq = make_rsrc(a.q + bh * T * DK, (uint32_t)(T * DK * 2));
     const auto rk = make_rsrc(a.k + bh * T * DK, (uint32_t)(T * DK * 2));
-    const auto rv = make_rsrc(UT ? nullptr : a.v + bh * T * DV, UT ? 0u : (uint32_t)(T * DV * 2));
     const auto rg = make_rsrc(a.g + bh * T * DK, (uint32_t)(T * DK * 4));
     const auto rb = make_rsrc(GD2 ? nullptr : a.beta + bh * T, GD2 ? 0u : (uint32_t)(T * 4));
     const auto re = make_rsrc(GD2 ? a.eg + bh * T * DK : nullptr, GD2 ? (uint32_t)(T * DK * 4) : 0u);
-    const auto rw = make_rsrc(GD2 && !UT ? a.wg + bh * T * DV : nullptr, GD2 && !UT ? (uint32_t)(T * DV * 4) : 0u);
-    const auto ro = make_rsrc(UT ? nullptr : a.o + bh * T * DV, UT ? 0u : (uint32_t)(T * DV * 2));
-    const int dvc = dv0 + 16 * w;  // first value channel of consumer wave w (w < 2)
-
-    auto trfrag = [&](const _Float16* base, int ld, int kb, int col) {
-        const _Float16* p0 = base + (32 * kb + 4 * g + (j >> 2)) * ld + col;
-        return cat8(ldtr(p0), ldtr(p0 + 16 * ld));
-    };
 
     // structural zeros of the triangular operands (never written afterwards)
     for (int i = tid; i < (L::oGl - L::oAt) / 16; i += 256)
         reinterpret_cast<uint4*>(smem + L::oAt)[i] = uint4{0u, 0u, 0u, 0u};
-
-    // ---- state of consumer waves 0-1: S^T tiles (fp32) and their fp16 operand copy
-    float4v St[NST];
-    half8 Sb[NKB];
-#pragma unroll
-    for (int t = 0; t < NST; ++t) St[t] = zero4();
-    if (w < 2 && a.S0 != nullptr) {
-        const float* s0 = a.S0 + bh * (int64_t)DV * DK + (int64_t)(dvc + j) * DK;
-#pragma unroll
-        for (int t = 0; t < NST; ++t) St[t] = ld4f(s0 + pperm(16 * t + 4 * g));
-    }
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) Sb[kb] = pack8(St[2 * kb], St[2 * kb + 1]);
 
     // ---- prefetch registers for one chunk, in the layout of the scan: wave w holds the
     // 16-token block w, lane l the channel pair ch2 = 2 (l mod DK/2) (for DK = 64 the upper
@@ -205,9 +157,8 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
     const bool own = 2 * l < DK;
     float2 gp[16], ep[16];  // ep: erase gate b (GD2)
     uint32_t kp[16], qp[16];
-    uint4 vp, wp0, wp1;     // wp: write gate w of the lane's 8 V values (GD2)
     float bp = 0.0f;
-    // token t of the lane's block (g, k, q of its channel pair); t = 0 also brings V, beta.
+    // token t of the lane's block (g, k, q of its channel pair); t = 0 also brings beta.
     // Past the sequence end the loads return zeros (identity tokens).
     // The token's element offset is formed as a wave-uniform value the compiler cannot split, so
     // the address is one add to the lane's channel offset, not one of 16 registers held
@@ -223,19 +174,8 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
         if constexpr (GD2) {
             const uint2 ue = bld8(re, e * 4);
             ep[t] = float2{__uint_as_float(ue.x), __uint_as_float(ue.y)};
-        }
-        if (t == 0) {
-            const uint32_t tc = (uint32_t)(c * C);
-            const uint32_t vidx = (tc + (tid >> 2)) * DV + dv0 + (tid & 3) * 8;
-            if (!UT) vp = bld16(rv, vidx * 2);
-            if constexpr (GD2) {
-                if (!UT) {  // the UT pass has no V
-                    wp0 = bld16(rw, vidx * 4);
-                    wp1 = bld16(rw, vidx * 4 + 16);
-                }
-            } else {
-                bp = bld4(rb, (tc + l) * 4);  // every wave: a load under a branch costs a full wait
-            }
+        } else if (t == 0) {
+            bp = bld4(rb, ((uint32_t)(c * C) + l) * 4);  // every wave: a load under a branch costs a full wait
         }
     };
     auto issue = [&](int64_t c) {
@@ -246,35 +186,67 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
     // Operand fragments (row j of tile ti, reduction block kb) of the Gram products.
     auto rfrag = [&](const _Float16* M, int ti, int kb) { return ld8(M + (16 * ti + j) * L::LDK + 32 * kb + 8 * g); };
     auto hfrag = [&](const _Float16* H, int row, int kb) { return ld8(H + row * DK + 32 * kb + 8 * g); };
-    // Diagonal-tile operand of block b built afresh in fp32 from the bf16 input (lane row or
-    // column j = token 16b + j; the fragment's channels are 32kb + 8g .. +7):
-    // x e^{G_loc(tok) - G_loc(8)} for the row side, x e^{G_loc(8) - G_loc(tok)} for the
-    // column side, rounded to bf16.  With gate set (GD2, row side of N) x is b (.) k.
-    auto diag_bf16 = [&](const __amdgpu_buffer_rsrc_t& rs, int64_t c, int b, int kb, bool row_side, bool gate) {
-        const int tok = 16 * b + j, ch = 32 * kb + 8 * g;
-        const uint32_t gidx = (uint32_t)(c * C + tok) * DK + ch;
-        const uint4 u = bld16(rs, gidx * 2);
-        const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
-        float gb[8];
+
+    // Diagonal 16x16 tile of block b of a flagged block, formed without any factor above 1:
+    // entry (l, m) = sum_c x_lc k_mc e^{G_lc - G_mc} (x = q, k, or e = b (.) k with `gate`).
+    // For l != m let h be the highest bit in which the block-local indices l' and m' differ; for
+    // m' < l' the reference token r = l' with the bits below h cleared satisfies m' < r <= l',
+    // so e^{G_l - G_m} = e^{G_l - G_r} e^{G_r - G_m} with both factors <= 1 for a decaying gate.
+    // Level h multiplies the row operand x_l e^{G_l - G_r(l')} (rows with bit h set, others 0) by
+    // the column operand k_m e^{G_r(m') - G_m} (columns with bit h clear, r(m') = m' with bit h
+    // set and the bits below cleared); its entries are right exactly where h is the highest
+    // differing bit, and each entry takes its value from that level (the diagonal from an
+    // unscaled product).  Five fp16 products per reduction block instead of one; only blocks
+    // whose in-block decay spread exceeds the fp16 path's range come here.
+    auto diag_exact = [&](const __amdgpu_buffer_rsrc_t& rs, int64_t c, int b, bool gate) {
+        const int tok = 16 * b + j;
+        float4v out = zero4();
+        // level 4 is the unscaled product that supplies the diagonal; levels and reduction
+        // blocks stay rolled loops, so this rare path keeps few registers live
+#pragma nounroll
+        for (int lev = 0; lev < 5; ++lev) {
+            const bool rowlive = lev == 4 || ((j >> lev) & 1), collive = lev == 4 || !((j >> lev) & 1);
+            const int rr = lev == 4 ? tok : 16 * b + ((j >> lev) << lev);        // row reference token
+            const int rc = lev == 4 ? tok : 16 * b + (((j >> lev) | 1) << lev);  // column reference token
+            float4v acc = zero4();
+#pragma nounroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                const int ch = 32 * kb + 8 * g;
+                const uint32_t gidx = (uint32_t)(c * C + tok) * DK + ch;
+                const uint4 ur = bld16(rs, gidx * 2), uk = bld16(rk, gidx * 2);
+                const uint32_t xr[4] = {ur.x, ur.y, ur.z, ur.w}, xk[4] = {uk.x, uk.y, uk.z, uk.w};
+                float gb[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) gb[e] = 1.0f;
-        if (gate) {
-            const uint4 b0 = bld16(re, gidx * 4), b1 = bld16(re, gidx * 4 + 16);
-            const uint32_t bw[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+                for (int e = 0; e < 8; ++e) gb[e] = 1.0f;
+                if (gate) {
+                    const uint4 b0 = bld16(re, gidx * 4), b1 = bld16(re, gidx * 4 + 16);
+                    const uint32_t bw[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
 #pragma unroll
-            for (int e = 0; e < 8; ++e) gb[e] = __uint_as_float(bw[e]);
+                    for (int e = 0; e < 8; ++e) gb[e] = __uint_as_float(bw[e]);
+                }
+                const float* pt = Gl + tok * L::LDG + ch;
+                const float* pr = Gl + rr * L::LDG + ch;
+                const float* pc = Gl + rc * L::LDG + ch;
+                half8 ra, cb;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float x = gb[e] * __uint_as_float(e & 1 ? (xr[e >> 1] & 0xffff0000u) : (xr[e >> 1] << 16));
+                    const float kv = __uint_as_float(e & 1 ? (xk[e >> 1] & 0xffff0000u) : (xk[e >> 1] << 16));
+                    ra[e] = rowlive ? (_Float16)(x * fast_exp(pt[e] - pr[e])) : (_Float16)0.0f;
+                    cb[e] = collive ? (_Float16)(kv * fast_exp(pc[e] - pt[e])) : (_Float16)0.0f;
+                }
+                mma16(acc, ra, cb);
+            }
+            // element (row 4g + r, column j) of the tile takes the level of its highest
+            // differing bit
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int d = (4 * g + r) ^ j;
+                const int hb = d == 0 ? 4 : d >= 8 ? 3 : d >= 4 ? 2 : d >= 2 ? 1 : 0;
+                out[r] = hb == lev ? acc[r] : out[r];
+            }
         }
-        const float* gt = Gl + tok * L::LDG + ch;
-        const float* gm = Gl + (16 * b + 8) * L::LDG + ch;
-        const float4v t0 = ld4f(gt), t1 = ld4f(gt + 4), m0 = ld4f(gm), m1 = ld4f(gm + 4);
-        bf16x8 r;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float te = e < 4 ? t0[e] : t1[e - 4], me = e < 4 ? m0[e] : m1[e - 4];
-            const float x = __uint_as_float(e & 1 ? (wv[e >> 1] & 0xffff0000u) : (wv[e >> 1] << 16));
-            r[e] = (__bf16)(gb[e] * x * fast_exp(row_side ? te - me : me - te));
-        }
-        return r;
+        return out;
     };
 
     lds_barrier();
@@ -342,22 +314,6 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
             const bool any_unsafe = __any(unsafe);
             if (l == 0) Flag[w] = any_unsafe ? 1 : 0;
             if (!GD2 && w == 0) FB[l] = bp;
-            // V^T tile, fp32 [channel][token] (GD2: z = w (.) v); the UT pass has no V
-            if (!UT) {
-            const int row = tid >> 2, col = (tid & 3) * 8;
-            const uint32_t ww[4] = {vp.x, vp.y, vp.z, vp.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                float v0 = __uint_as_float(ww[e] << 16), v1 = __uint_as_float(ww[e] & 0xffff0000u);
-                if constexpr (GD2) {
-                    const uint32_t wgt[8] = {wp0.x, wp0.y, wp0.z, wp0.w, wp1.x, wp1.y, wp1.z, wp1.w};
-                    v0 *= __uint_as_float(wgt[2 * e]);
-                    v1 *= __uint_as_float(wgt[2 * e + 1]);
-                }
-                Vt[(col + 2 * e) * L::LDV + row] = v0;
-                Vt[(col + 2 * e + 1) * L::LDV + row] = v1;
-            }
-            }
         }
         lds_barrier();
 
@@ -398,7 +354,7 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
         auto gram_kda = [&](auto hc, auto qc, auto bc) {
             constexpr int h = decltype(hc)::value;
             constexpr bool isQ = decltype(qc)::value;
-            constexpr bool BF = decltype(bc)::value;  // some diagonal block of the wave needs bf16
+            constexpr bool BF = decltype(bc)::value;  // some diagonal block of the wave is flagged
             const _Float16* Rs = isQ ? Qr : Kr;
             constexpr int NT = 5;
             constexpr int ti_[2][NT] = {{0, 1, 1, 2, 3}, {2, 2, 3, 3, 3}};
@@ -407,10 +363,6 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
             float4v acc[NT];
 #pragma unroll
             for (int t = 0; t < NT; ++t) acc[t] = zero4();
-            // the bf16 path of a diagonal block is chosen per block for the whole wave
-            int fl[4];
-#pragma unroll
-            for (int b = 0; b < 4; ++b) fl[b] = __builtin_amdgcn_readfirstlane(Flag[b]);
             if constexpr (!BF) {
                 // every diagonal tile on fp16: the operands of reduction block kb + 1 are read
                 // from LDS while the MFMAs of block kb run (two register sets), and their factors
@@ -456,29 +408,41 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
                     if (kb + 1 < NKB) scale_kb(oa[nxt], ob[nxt], fa[nxt], fb[nxt]);
                 }
             } else {
+                // flagged diagonal blocks are chosen per block for the whole wave
+                int fl[4];
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
+                for (int b = 0; b < 4; ++b) fl[b] = __builtin_amdgcn_readfirstlane(Flag[b]);
 #pragma unroll
-                for (int t = 0; t < NT; ++t) {
-                    const int ti = ti_[h][t], tj = tj_[h][t], cf = cf_[h][t];
-                    const half8 A = rfrag(Rs, ti, kb);
-                    half8 B = rfrag(Kc, tj, kb);
-                    if (cf == 3) {
-                        if (BF && fl[ti]) {
-                            mma16_bf16(acc[t], diag_bf16(isQ ? rq : rk, c, ti, kb, true, GD2 && !isQ),
-                                       diag_bf16(rk, c, ti, kb, false, false));
-                        } else {
-                            mma16(acc[t], hmul8(A, hfrag(HMR, ti, kb)), hmul8(B, hfrag(HMC, ti, kb)));
+                for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+                    for (int t = 0; t < NT; ++t) {
+                        const int ti = ti_[h][t], tj = tj_[h][t], cf = cf_[h][t];
+                        if (!(cf == 3 && fl[ti])) {
+                            half8 A = rfrag(Rs, ti, kb), B = rfrag(Kc, tj, kb);
+                            if (cf == 3) {
+                                A = hmul8(A, hfrag(HMR, ti, kb));
+                                B = hmul8(B, hfrag(HMC, ti, kb));
+                            } else if (cf >= 0) {
+                                B = hmul8(B, hfrag(HD, cf, kb));
+                            }
+                            mma16(acc[t], A, B);
                         }
-                    } else {
-                        if (cf >= 0) B = hmul8(B, hfrag(HD, cf, kb));
-                        mma16(acc[t], A, B);
+                        if (t < 16 / NKB) issue_tok(cn, kb * (16 / NKB) + t);
                     }
-                    if (t < 16 / NKB) issue_tok(cn, kb * (16 / NKB) + t);
-                }
 #pragma unroll
-                for (int u = NT; u < 16 / NKB; ++u) issue_tok(cn, kb * (16 / NKB) + u);
-            }
+                    for (int u = NT; u < 16 / NKB; ++u) issue_tok(cn, kb * (16 / NKB) + u);
+                }
+                // the wave's two diagonal blocks 2h, 2h + 1 (one inlined copy of the exact path)
+#pragma nounroll
+                for (int d = 0; d < 2; ++d) {
+                    const int b = 2 * h + d;
+                    if (fl[b]) {
+                        const float4v x = diag_exact(isQ ? rq : rk, c, b, GD2 && !isQ);
+#pragma unroll
+                        for (int t = 0; t < NT; ++t)
+                            if (cf_[h][t] == 3) acc[t] = ti_[h][t] == b ? x : acc[t];
+                    }
+                }
             }
             // epilogue: beta of the row for N (not for GD2: e carries the gate), causal masks
 #pragma unroll
@@ -510,12 +474,11 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
                 }
             }
         };
-        // UT: the test for the bf16 diagonal path is taken once per wave, so the usual all-fp16
+        // The test for the exact diagonal path is taken once per wave, so the usual all-fp16
         // case runs as straight-line code (a branch inside the loop serialises its LDS reads).
-        // The state pass keeps the per-block test (two copies of the loop exceed its registers).
         auto gram_wave = [&](auto hc, auto qc) {
             constexpr int h = decltype(hc)::value;
-            if (!UT || __builtin_amdgcn_readfirstlane(Flag[2 * h] | Flag[2 * h + 1]))
+            if (__builtin_amdgcn_readfirstlane(Flag[2 * h] | Flag[2 * h + 1]))
                 gram_kda(hc, qc, std::true_type{});
             else
                 gram_kda(hc, qc, std::false_type{});
@@ -528,10 +491,8 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
 
         // Diagonal inverses (waves 0-1, two blocks each): column-oriented forward substitution,
         // lane (block, jc) builds column jc of X_bb = N_bb^{-1}, stored as X_bb^T (row jc =
-        // column jc).  The UT pass also writes the diagonal block of T = N^{-1} diag(beta)
-        // (GD2: N^{-1}, e carries the gate) to Tt, which takes the place of V^T and O^T (unused
-        // there).
-        _Float16* Tt = reinterpret_cast<_Float16*>(smem + L::oVt);
+        // column jc), and the diagonal block of T = N^{-1} diag(beta) (GD2: N^{-1}, e carries
+        // the gate) into Tt.
         auto diag_inverse = [&]() {
             const int b = 2 * w + ((l >> 4) & 1), jc = j;
             const float* nb = Nd + b * 16 * L::LDN;
@@ -561,285 +522,102 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
                 }
                 *reinterpret_cast<half8*>(Xd + (16 * b + jc) * L::LDX) = h0;
                 *reinterpret_cast<half8*>(Xd + (16 * b + jc) * L::LDX + 8) = h1;
-                if constexpr (UT) {
-                    const float bc = GD2 ? 1.0f : FB[16 * b + jc];
-                    const int pc = pperm(16 * b + jc);
+                const float bc = GD2 ? 1.0f : FB[16 * b + jc];
+                const int pc = pperm(16 * b + jc);
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) Tt[(16 * b + i) * L::LDC + pc] = (_Float16)(xd[i] * bc);
-                }
+                for (int i = 0; i < 16; ++i) Tt[(16 * b + i) * L::LDC + pc] = (_Float16)(xd[i] * bc);
             }
         };
 
-        if constexpr (UT) {
-            // The chunk's operands go to the workspace in 16-byte pieces, spread over the last
-            // stages: waves 2-3 write K e^G and Q e^G while waves 0-1 invert the diagonal blocks,
-            // then K e^{G_C - G} while waves 0-1 form the blocks below the diagonal; all waves
-            // then write A^T, T and e^{G_C}.  The copies are rescaled on the way out (per block
-            // and channel: e^{G_start(blk)} for Kr and Qr, e^{G_C - G_end(blk)} for Kc).
-            uint16_t* dst = a.ws + (bh * nC + c) * (int64_t)kda_ws_stride<DK>();
-            constexpr int NG = C * (DK / 8);  // 16-byte pieces per copy
-            auto copy_scaled = [&](const _Float16* src, const _Float16* H, uint16_t* d) {
+        // The chunk's operands go to the workspace in 16-byte pieces, spread over the last
+        // stages: waves 2-3 write K e^G and Q e^G while waves 0-1 invert the diagonal blocks,
+        // then K e^{G_C - G} while waves 0-1 form the blocks below the diagonal; all waves
+        // then write A^T, T and e^{G_C}.  The copies are rescaled on the way out (per block
+        // and channel: e^{G_start(blk)} for Kr and Qr, e^{G_C - G_end(blk)} for Kc).
+        uint16_t* dst = a.ws + (bh * nC + c) * (int64_t)kda_ws_stride<DK>();
+        constexpr int NG = C * (DK / 8);  // 16-byte pieces per copy
+        auto copy_scaled = [&](const _Float16* src, const _Float16* H, uint16_t* d) {
 #pragma unroll
-                for (int u = 0; u < NG / 128; ++u) {
-                    const int i = tid - 128 + 128 * u;
-                    const int row = i / (DK / 8), col = (i % (DK / 8)) * 8;
-                    *reinterpret_cast<half8*>(d + row * DK + col) =
-                        hmul8(ld8(src + row * L::LDK + col), ld8(H + (row >> 4) * DK + col));
-                }
-            };
-            if (w < 2) {
-                diag_inverse();
-            } else {
-                copy_scaled(Kr, HP, dst + 2 * C * C);
-                copy_scaled(Qr, HP, dst + 2 * C * C + C * DK);
+            for (int u = 0; u < NG / 128; ++u) {
+                const int i = tid - 128 + 128 * u;
+                const int row = i / (DK / 8), col = (i % (DK / 8)) * 8;
+                *reinterpret_cast<half8*>(d + row * DK + col) =
+                    hmul8(ld8(src + row * L::LDK + col), ld8(H + (row >> 4) * DK + col));
             }
-            lds_barrier();
-            // blocks of N^{-1} below the diagonal, column block by column block (wave 0: column
-            // 0, wave 1: columns 1 and 2): M_bc = -X_bb sum_{d=c}^{b-1} N_bd M_dc, then
-            // T_bc = M_bc diag(beta_c)
-            auto mma16k16 = [](float4v& acc4, const half4& a4, const half4& b4) {
-                acc4 = __builtin_amdgcn_mfma_f32_16x16x16f16(a4, b4, acc4, 0, 0, 0);
-            };
-            auto h4 = [](const float4v& x) { return half4{(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3]}; };
-            auto xA = [&](int b) { return ldtr(Xd + (16 * b + 4 * g + (j >> 2)) * L::LDX + 4 * (j & 3)); };
-            auto nA = [&](int b, int d) { return ldtr(Nt + (16 * d + 4 * g + (j >> 2)) * L::LDC + 16 * b + 4 * (j & 3)); };
-            auto column = [&](auto cc) {
-                constexpr int cb = decltype(cc)::value;
-                half4 mb[4];
-                mb[cb] = *reinterpret_cast<const half4*>(Xd + (16 * cb + j) * L::LDX + 4 * g);
-                const float bcol = GD2 ? 1.0f : FB[16 * cb + j];
-                const int pc = pperm(16 * cb + j);
-#pragma unroll
-                for (int b = cb + 1; b < 4; ++b) {
-                    float4v y = zero4();
-#pragma unroll
-                    for (int d = cb; d < b; ++d) mma16k16(y, nA(b, d), mb[d]);
-                    float4v m = zero4();
-                    mma16k16(m, xA(b), h4(y));
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) m[r] = -m[r];
-                    mb[b] = h4(m);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) Tt[(16 * b + 4 * g + r) * L::LDC + pc] = (_Float16)(m[r] * bcol);
-                }
-            };
-            if (w == 0) {
-                column(std::integral_constant<int, 0>{});
-            } else if (w == 1) {
-                column(std::integral_constant<int, 1>{});
-                column(std::integral_constant<int, 2>{});
-            } else {
-                copy_scaled(Kc, HS, dst + 2 * C * C + 2 * C * DK);
-            }
-            lds_barrier();
-            // A^T and T.  T's blocks above the diagonal are zero and are not staged: of a piece
-            // at column position col, the first four values lie in column block 2 (col / 32),
-            // the last four in the next one.
-#pragma unroll
-            for (int u = 0; u < C * C / 8 / 256; ++u) {
-                const int i = tid + 256 * u;
-                const int row = i / (C / 8), col = (i % (C / 8)) * 8;
-                *reinterpret_cast<uint4*>(dst + row * C + col) = *reinterpret_cast<const uint4*>(At + row * L::LDC + col);
-                uint4 t = *reinterpret_cast<const uint4*>(Tt + row * L::LDC + col);
-                const int rb = row >> 4, cb = 2 * (col >> 5);
-                if (cb > rb) t.x = t.y = 0u;
-                if (cb + 1 > rb) t.z = t.w = 0u;
-                *reinterpret_cast<uint4*>(dst + C * C + row * C + col) = t;
-            }
-            if (tid < DK) reinterpret_cast<float*>(dst + 2 * C * C + 3 * C * DK)[tid] = FE[tid];
-            // No barrier before the next chunk: its scan and tables write nothing read here, and
-            // Tt is written again only after three more barriers.
-        } else {
-        if (w < 2) diag_inverse();
-        {
-            // Kr -> K e^G, Qr -> Q e^G (factor e^{G_start(blk)}), Kc -> K e^{G_C - G}
-            // (factor e^{G_C - G_end(blk)}); 16-byte groups of the rows.  Waves 2-3 take the
-            // first three quarters, waves 0-1 (after their inverses) the last quarter.
-            constexpr int NG = C * (DK / 8);  // 16-byte groups per copy
-            const int i0 = w >= 2 ? tid - 128 : 3 * NG / 4 + tid;
-            const int i1 = w >= 2 ? 3 * NG / 4 : NG;
-            for (int i = i0; i < i1; i += 128) {
-                const int row = i / (DK / 8), col = (i % (DK / 8)) * 8, blk = row >> 4;
-                const half8 fp = ld8(HP + blk * DK + col), fs = ld8(HS + blk * DK + col);
-                half8* pk = reinterpret_cast<half8*>(Kr + row * L::LDK + col);
-                half8* pq = reinterpret_cast<half8*>(Qr + row * L::LDK + col);
-                half8* pc = reinterpret_cast<half8*>(Kc + row * L::LDK + col);
-                *pk = hmul8(*pk, fp);
-                *pq = hmul8(*pq, fp);
-                *pc = hmul8(*pc, fs);
-            }
-        }
-        lds_barrier();
-        // ================= S5: state pass of chunk c (waves 0-1) =================
+        };
         if (w < 2) {
-            // P_K = (K e^G) S^T, P_Q = (Q e^G) S^T
-            float4v PK[4], PQ[4];
-#pragma unroll
-            for (int ti = 0; ti < 4; ++ti) {
-                PK[ti] = zero4();
-                PQ[ti] = zero4();
-            }
-            half8 fa[8], fb[8];
-#pragma unroll
-            for (int ti = 0; ti < 4; ++ti) {
-                fa[ti] = rfrag(Kr, ti, 0);
-                fa[4 + ti] = rfrag(Qr, ti, 0);
-            }
-            float4v vv[4], bt[4];
-#pragma unroll
-            for (int ti = 0; ti < 4; ++ti) {
-                vv[ti] = ld4f(Vt + (16 * w + j) * L::LDV + 16 * ti + 4 * g);
-                bt[ti] = GD2 ? float4v{1.0f, 1.0f, 1.0f, 1.0f} : ld4f(FB + 16 * ti + 4 * g);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
-                half8* cur = (kb & 1) ? fb : fa;
-                half8* nxt = (kb & 1) ? fa : fb;
-                if (kb + 1 < NKB) {
-#pragma unroll
-                    for (int ti = 0; ti < 4; ++ti) {
-                        nxt[ti] = rfrag(Kr, ti, kb + 1);
-                        nxt[4 + ti] = rfrag(Qr, ti, kb + 1);
-                    }
-                }
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int ti = 0; ti < 4; ++ti) {
-                    mma16(PK[ti], cur[ti], Sb[kb]);
-                    mma16(PQ[ti], cur[4 + ti], Sb[kb]);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            // operands of the block substitution and of A Z
-            half4 xf[4];
-#pragma unroll
-            for (int b = 0; b < 4; ++b) xf[b] = ldtr(Xd + (16 * b + 4 * g + (j >> 2)) * L::LDX + 4 * (j & 3));
-            const half4 n10 = ldtr(Nt + (4 * g + (j >> 2)) * L::LDC + 16 + 4 * (j & 3));
-            const half8 n2x = trfrag(Nt, L::LDC, 0, 32 + 4 * (j & 3));
-            const half8 n3x = trfrag(Nt, L::LDC, 0, 48 + 4 * (j & 3));
-            const half4 n32 = ldtr(Nt + (32 + 4 * g + (j >> 2)) * L::LDC + 48 + 4 * (j & 3));
-            half8 af[6];
-#pragma unroll
-            for (int ti = 0, n = 0; ti < 4; ++ti) {
-#pragma unroll
-                for (int kb = 0; kb <= (ti >> 1); ++kb, ++n) af[n] = trfrag(At, L::LDC, kb, 16 * ti + 4 * (j & 3));
-            }
-            float4v ed[NST];
-#pragma unroll
-            for (int t = 0; t < NST; ++t) ed[t] = ld4f(FE + pperm(16 * t + 4 * g));
-            __builtin_amdgcn_sched_barrier(0);
-            // R' = diag(beta) (V - P_K) (GD2: z - P_E);  Z = N^{-1} R' by blocked forward substitution
-            float4v Rb[4];
-#pragma unroll
-            for (int ti = 0; ti < 4; ++ti)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) Rb[ti][r] = bt[ti][r] * (vv[ti][r] - PK[ti][r]);
-            auto mma16k16 = [](float4v& acc, const half4& a4, const half4& b4) {
-                acc = __builtin_amdgcn_mfma_f32_16x16x16f16(a4, b4, acc, 0, 0, 0);
-            };
-            auto h4 = [](const float4v& x) { return half4{(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3]}; };
-            auto sub4 = [](float4v a4, const float4v& b4) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) a4[r] -= b4[r];
-                return a4;
-            };
-            float4v Zz[4], y;
-            Zz[0] = zero4();
-            mma16k16(Zz[0], xf[0], h4(Rb[0]));
-            y = zero4();
-            mma16k16(y, n10, h4(Zz[0]));
-            Zz[1] = zero4();
-            mma16k16(Zz[1], xf[1], h4(sub4(Rb[1], y)));
-            const half8 z01 = pack8(Zz[0], Zz[1]);
-            y = zero4();
-            mma16(y, n2x, z01);
-            Zz[2] = zero4();
-            mma16k16(Zz[2], xf[2], h4(sub4(Rb[2], y)));
-            y = zero4();
-            mma16(y, n3x, z01);
-            mma16k16(y, n32, h4(Zz[2]));
-            Zz[3] = zero4();
-            mma16k16(Zz[3], xf[3], h4(sub4(Rb[3], y)));
-            auto ktfrag = [&](int t, int kb) { return trfrag(Kc, L::LDK, kb, pperm(16 * t + 4 * (j & 3))); };
-            half8 kt0[NST], kt1[NST];
-#pragma unroll
-            for (int t = 0; t < NST; ++t) {
-                kt0[t] = ktfrag(t, 0);
-                kt1[t] = ktfrag(t, 1);
-            }
-            const half8 zB[2] = {z01, pack8(Zz[2], Zz[3])};
-#pragma unroll
-            for (int ti = 0, n = 0; ti < 4; ++ti) {
-                float4v acc = PQ[ti];
-#pragma unroll
-                for (int kb = 0; kb <= (ti >> 1); ++kb, ++n) mma16(acc, af[n], zB[kb]);
-                *reinterpret_cast<uint2*>(Ot + (16 * w + j) * L::LDO + 16 * ti + 4 * g) =
-                    uint2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
-            }
-            lds_fence();
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-                const int tb = 32 * s2 + 16 * (g >> 1), d = 16 * w + 8 * (g & 1);
-                const _Float16* rp = Ot + (d + (j >> 2)) * L::LDO + tb + 4 * (j & 3);
-                const uint2 lo = __builtin_bit_cast(uint2, ldtr(rp));
-                const uint2 hi = __builtin_bit_cast(uint2, ldtr(rp + 4 * L::LDO));
-                bst16(ro, ((uint32_t)(c * C + tb + j) * DV + dv0 + d) * 2, uint4{lo.x, lo.y, hi.x, hi.y});
-            }
-            // S^T <- Diag(e^{G_C}) S^T + (K e^{G_C - G})^T Z
-#pragma unroll
-            for (int t = 0; t < NST; ++t) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) St[t][r] *= ed[t][r];
-                mma16(St[t], kt0[t], zB[0]);
-                mma16(St[t], kt1[t], zB[1]);
-            }
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) Sb[kb] = pack8(St[2 * kb], St[2 * kb + 1]);
+            diag_inverse();
+        } else {
+            copy_scaled(Kr, HP, dst + 2 * C * C);
+            copy_scaled(Qr, HP, dst + 2 * C * C + C * DK);
         }
         lds_barrier();
-        }  // state pass
-    }
-
-    if (!UT && w < 2 && a.Sf != nullptr) {
-        float* sf = a.Sf + bh * (int64_t)DV * DK + (int64_t)(dvc + j) * DK;
+        // blocks of N^{-1} below the diagonal, column block by column block (wave 0: column
+        // 0, wave 1: columns 1 and 2): M_bc = -X_bb sum_{d=c}^{b-1} N_bd M_dc, then
+        // T_bc = M_bc diag(beta_c)
+        auto mma16k16 = [](float4v& acc4, const half4& a4, const half4& b4) {
+            acc4 = __builtin_amdgcn_mfma_f32_16x16x16f16(a4, b4, acc4, 0, 0, 0);
+        };
+        auto h4 = [](const float4v& x) { return half4{(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3]}; };
+        auto xA = [&](int b) { return ldtr(Xd + (16 * b + 4 * g + (j >> 2)) * L::LDX + 4 * (j & 3)); };
+        auto nA = [&](int b, int d) { return ldtr(Nt + (16 * d + 4 * g + (j >> 2)) * L::LDC + 16 * b + 4 * (j & 3)); };
+        auto column = [&](auto cc) {
+            constexpr int cb = decltype(cc)::value;
+            half4 mb[4];
+            mb[cb] = *reinterpret_cast<const half4*>(Xd + (16 * cb + j) * L::LDX + 4 * g);
+            const float bcol = GD2 ? 1.0f : FB[16 * cb + j];
+            const int pc = pperm(16 * cb + j);
 #pragma unroll
-        for (int t = 0; t < NST; ++t) *reinterpret_cast<float4v*>(sf + pperm(16 * t + 4 * g)) = St[t];
+            for (int b = cb + 1; b < 4; ++b) {
+                float4v y = zero4();
+#pragma unroll
+                for (int d = cb; d < b; ++d) mma16k16(y, nA(b, d), mb[d]);
+                float4v m = zero4();
+                mma16k16(m, xA(b), h4(y));
+#pragma unroll
+                for (int r = 0; r < 4; ++r) m[r] = -m[r];
+                mb[b] = h4(m);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Tt[(16 * b + 4 * g + r) * L::LDC + pc] = (_Float16)(m[r] * bcol);
+            }
+        };
+        if (w == 0) {
+            column(std::integral_constant<int, 0>{});
+        } else if (w == 1) {
+            column(std::integral_constant<int, 1>{});
+            column(std::integral_constant<int, 2>{});
+        } else {
+            copy_scaled(Kc, HS, dst + 2 * C * C + 2 * C * DK);
+        }
+        lds_barrier();
+        // A^T and T.  T's blocks above the diagonal are zero and are not staged: of a piece
+        // at column position col, the first four values lie in column block 2 (col / 32),
+        // the last four in the next one.
+#pragma unroll
+        for (int u = 0; u < C * C / 8 / 256; ++u) {
+            const int i = tid + 256 * u;
+            const int row = i / (C / 8), col = (i % (C / 8)) * 8;
+            *reinterpret_cast<uint4*>(dst + row * C + col) = *reinterpret_cast<const uint4*>(At + row * L::LDC + col);
+            uint4 t = *reinterpret_cast<const uint4*>(Tt + row * L::LDC + col);
+            const int rb = row >> 4, cb = 2 * (col >> 5);
+            if (cb > rb) t.x = t.y = 0u;
+            if (cb + 1 > rb) t.z = t.w = 0u;
+            *reinterpret_cast<uint4*>(dst + C * C + row * C + col) = t;
+        }
+        if (tid < DK) reinterpret_cast<float*>(dst + 2 * C * C + 3 * C * DK)[tid] = FE[tid];
+        // No barrier before the next chunk: its scan and tables write nothing read here, and
+        // Tt is written again only after three more barriers.
     }
 }
 
-template <int DK, bool GD2, bool UT = false>
+template <int DK, bool GD2>
 static hipError_t launch_kda(const KdaArgs& a, int64_t nwg, hipStream_t st) {
     using L = KdaLds<DK>;
-    auto kern = chunk_kda_kernel<DK, GD2, UT>;
+    auto kern = chunk_kda_kernel<DK, GD2>;
     static std::atomic<uint64_t> lds_enabled{0};  // one bit per device
     if (const hipError_t e = enable_dynamic_lds(kern, L::total, lds_enabled); e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(256), L::total, st, a);
     return hipGetLastError();
-}
-
-hipError_t chunk_kda_dispatch(int64_t BH, int64_t T, int dk, int dv, const void* q, const void* k, const void* v,
-                              const float* g, const float* beta, const float* S0, void* o, float* Sf,
-                              hipStream_t st) {
-    KdaArgs a;
-    a.T = T;
-    a.dv = dv;
-    a.ntiles = dv / 32;
-    a.q = static_cast<const uint16_t*>(q);
-    a.k = static_cast<const uint16_t*>(k);
-    a.v = static_cast<const uint16_t*>(v);
-    a.g = g;
-    a.beta = beta;
-    a.eg = nullptr;
-    a.wg = nullptr;
-    a.S0 = S0;
-    a.o = static_cast<uint16_t*>(o);
-    a.Sf = Sf;
-    a.ws = nullptr;
-    a.cpw = 1;
-    const int64_t nwg = BH * a.ntiles;
-    if (dk == 128) return launch_kda<128, false>(a, nwg, st);
-    return launch_kda<64, false>(a, nwg, st);
 }
 
 // UT pass of the per-channel-gate two-kernel path: one group per (sequence, run of chunks), the
@@ -850,18 +628,11 @@ hipError_t chunk_kda_ut_dispatch(int64_t BH, int64_t T, int dk, const void* q, c
                                  const float* beta, const float* eg, void* ws, hipStream_t st) {
     KdaArgs a;
     a.T = T;
-    a.dv = 32;
-    a.ntiles = 1;
     a.q = static_cast<const uint16_t*>(q);
     a.k = static_cast<const uint16_t*>(k);
-    a.v = nullptr;
     a.g = g;
     a.beta = eg ? nullptr : beta;
     a.eg = eg;
-    a.wg = nullptr;
-    a.S0 = nullptr;
-    a.o = nullptr;
-    a.Sf = nullptr;
     a.ws = static_cast<uint16_t*>(ws);
     const int64_t nC = (T + kChunk - 1) / kChunk;
     if (BH * nC == 0) return hipSuccess;
@@ -871,39 +642,13 @@ hipError_t chunk_kda_ut_dispatch(int64_t BH, int64_t T, int dk, const void* q, c
     a.cpw = (int)(cpw < nC ? cpw : nC);
     const int64_t nwg = BH * ((nC + a.cpw - 1) / a.cpw);
     if (eg) {
-        if (dk == 128) return launch_kda<128, true, true>(a, nwg, st);
-        return launch_kda<64, true, true>(a, nwg, st);
+        if (dk == 128) return launch_kda<128, true>(a, nwg, st);
+        return launch_kda<64, true>(a, nwg, st);
     }
-    if (dk == 128) return launch_kda<128, false, true>(a, nwg, st);
-    return launch_kda<64, false, true>(a, nwg, st);
+    if (dk == 128) return launch_kda<128, false>(a, nwg, st);
+    return launch_kda<64, false>(a, nwg, st);
 }
 
 int64_t chunk_kda_ws_halfs(int dk) { return dk == 128 ? kda_ws_stride<128>() : kda_ws_stride<64>(); }
-
-// Gated DeltaNet-2: per-channel log-decay g [.., T, dk], erase gate b [.., T, dk], write gate
-// w [.., T, dv], all fp32.
-hipError_t chunk_gdn2_dispatch(int64_t BH, int64_t T, int dk, int dv, const void* q, const void* k, const void* v,
-                               const float* g, const float* b, const float* w, const float* S0, void* o, float* Sf,
-                               hipStream_t st) {
-    KdaArgs a;
-    a.T = T;
-    a.dv = dv;
-    a.ntiles = dv / 32;
-    a.q = static_cast<const uint16_t*>(q);
-    a.k = static_cast<const uint16_t*>(k);
-    a.v = static_cast<const uint16_t*>(v);
-    a.g = g;
-    a.beta = nullptr;
-    a.eg = b;
-    a.wg = w;
-    a.S0 = S0;
-    a.o = static_cast<uint16_t*>(o);
-    a.Sf = Sf;
-    a.ws = nullptr;
-    a.cpw = 1;
-    const int64_t nwg = BH * a.ntiles;
-    if (dk == 128) return launch_kda<128, true>(a, nwg, st);
-    return launch_kda<64, true>(a, nwg, st);
-}
 
 }  // namespace gdr

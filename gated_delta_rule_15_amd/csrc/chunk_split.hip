@@ -636,6 +636,15 @@ __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const St
     }
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) Sb[kb] = pack8(St[2 * kb], St[2 * kb + 1]);
+    // Operand range: the consumers hold S, R and Z multiplied by 2^sexp (one exponent per wave,
+    // the same for all of its value channels).  Every step is linear in (V, S), so the scaled
+    // quantities obey the same recurrence exactly; only the fp16 roundings see the scale, which
+    // keeps max(|S|, |V|) 2^sexp inside [2^-3, 2^6] (rescaled to [2^3, 2^4) when it leaves it):
+    // fp16's 11-bit mantissa then holds the values that matter, and no operand (|R| and |Z| stay
+    // within a small multiple of that bound) reaches the fp16 maximum.  o and the final state
+    // are divided by 2^sexp on the way out.
+    int sexp = 0;
+    float smax = consumer ? wave_max_abs(max_abs(St)) : 0.0f;  // max |S| 2^sexp over the wave
 
     // Chunk k's loads live in register set k mod 2.  Loads of chunks past the end are issued
     // anyway (they read past the buffers' ends, which returns zeros, and are staged into a
@@ -747,6 +756,7 @@ __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const St
                                      __uint_as_float(vb.y << 16), __uint_as_float(vb.y & 0xffff0000u)};
                 }
             }
+            const float vmax = wave_max_abs(max_abs(vv));  // max |V| of the chunk (unscaled)
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
@@ -780,12 +790,32 @@ __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const St
                 eGC = F[L::FEC];
             }
             __builtin_amdgcn_sched_barrier(0);
-            // R = V - e^G P_K
+            // the operand scale of this chunk: rescale S (and P_K, computed from it) when the
+            // chunk's V or the state leave the range (a wave-uniform, rare branch)
+            float pqs = 1.0f;  // P_Q is computed below from the unrescaled copy Sb
+            {
+                const float M = fmaxf(smax, vmax * __builtin_ldexpf(1.0f, sexp));
+                if ((M > 64.0f || (M < 0.125f && M > 0.0f)) && M <= 3.0e38f) {
+                    const int e2 = min(max(sexp + 4 - __builtin_amdgcn_frexp_expf(M), -100), 100);
+                    pqs = __builtin_ldexpf(1.0f, e2 - sexp);
+#pragma unroll
+                    for (int t = 0; t < NST; ++t)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) St[t][r] *= pqs;
+#pragma unroll
+                    for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) PK[ti][r] *= pqs;
+                    sexp = e2;
+                }
+            }
+            const float vsc = __builtin_ldexpf(1.0f, sexp), osc = __builtin_ldexpf(1.0f, -sexp);
+            // R = V - e^G P_K (scaled)
             float4v Rr[4];
 #pragma unroll
             for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) Rr[ti][r] = vv[ti][r] - eg[ti][r] * PK[ti][r];
+                for (int r = 0; r < 4; ++r) Rr[ti][r] = vv[ti][r] * vsc - eg[ti][r] * PK[ti][r];
             // Z = T R (T lower triangular: block column kb only for row tiles ti >= 2 kb)
             const half8 rB[2] = {pack8(Rr[0], Rr[1]), pack8(Rr[2], Rr[3])};
             float4v Zz[4];
@@ -840,17 +870,18 @@ __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const St
 #pragma unroll
             for (int ti = 0, n = 0; ti < 4; ++ti) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) Oa[ti][r] = eg[ti][r] * PQ[ti][r];
+                for (int r = 0; r < 4; ++r) Oa[ti][r] = eg[ti][r] * pqs * PQ[ti][r];
 #pragma unroll
                 for (int kb = 0; kb <= (ti >> 1); ++kb, ++n) mma16(Oa[ti], af[n], zB[kb]);
             }
-            // O rounded to bf16 into this wave's rows of O^T (the loaders store it)
+            // O unscaled and rounded to bf16 into this wave's rows of O^T (the loaders store it)
 #pragma unroll
             for (int ti = 0; ti < 4; ++ti)
                 *reinterpret_cast<uint2*>(Ob(bc) + (16 * w + j) * L::LDO + 16 * ti + 4 * g) =
-                    uint2{pack_bf16x2(Oa[ti][0], Oa[ti][1]), pack_bf16x2(Oa[ti][2], Oa[ti][3])};
+                    uint2{pack_bf16x2(Oa[ti][0] * osc, Oa[ti][1] * osc), pack_bf16x2(Oa[ti][2] * osc, Oa[ti][3] * osc)};
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) Sb[kb] = pack8(St[2 * kb], St[2 * kb + 1]);
+            smax = wave_max_abs(max_abs(St));
         }
         lds_barrier();
     }
@@ -885,8 +916,14 @@ __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const St
 
     if (consumer && a.Sf != nullptr) {
         float* sf = a.Sf + bh * (int64_t)DV * DK + (int64_t)(dvc + j) * DK;
+        const float osc = __builtin_ldexpf(1.0f, -sexp);
 #pragma unroll
-        for (int t = 0; t < NST; ++t) *reinterpret_cast<float4v*>(sf + pperm(16 * t + 4 * g)) = St[t];
+        for (int t = 0; t < NST; ++t) {
+            float4v x = St[t];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) x[r] *= osc;
+            *reinterpret_cast<float4v*>(sf + pperm(16 * t + 4 * g)) = x;
+        }
     }
 }
 

@@ -19,24 +19,44 @@
  *
  * Conventions shared by every entry point
  *  - All tensor pointers are DEVICE pointers to contiguous row-major buffers owned by the
- *    caller.  The library allocates no device memory: the entry points that need scratch
- *    memory (the *_ws variants and gdr_frame_fwd) take it from the caller.  Between calls it
- *    keeps only per-device launch settings, made on first use on each device: the dynamic
- *    LDS limit of its kernels and the device's compute-unit count.
+ *    caller.  The library allocates no device memory: the chunked entry points and
+ *    gdr_frame_fwd take their scratch memory (the "workspace") from the caller, sized by the
+ *    matching *_workspace_size query.  Between calls the library keeps only per-device launch
+ *    settings, made on first use on each device: the dynamic LDS limit of its kernels and the
+ *    device's compute-unit count.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only enqueue work and
  *    return; faults during execution surface at the caller's next synchronisation.
  *  - Every argument is validated on the host before anything is enqueued.  On any error the
  *    call returns a non-zero gdr_status and enqueues nothing.
+ *  - Workspace: a device buffer of at least the queried size; its contents on entry are
+ *    ignored and on return undefined; it may overlap no input or output.  A NULL, short or
+ *    overlapping workspace returns GDR_ERR_WORKSPACE (a query result of 0 means none is
+ *    needed and the argument is ignored).  Calls that share a workspace must be ordered on one
+ *    stream.
  *  - io_dtype applies to q, k, v and o (GDR_BF16 or GDR_F32); g, beta and the state are
  *    always float32.
  *  - Supported sizes: d_k in {64, 128}; d_v a multiple of 32 in [32, 256].  With
  *    io_dtype = GDR_F32 the chunked forward supports d_k = 64 and the scalar gate only
  *    (GDR_ERR_UNSUPPORTED otherwise); decode supports every combination.
- *  - Numerics: bf16 inputs are widened exactly; the chunked forward multiplies on fp16 MFMA
- *    (inputs with |x| >= 65504 overflow there) with fp32 accumulation, holds the state in
- *    fp32, and rounds o to bf16 (RNE) once at the end.  The fp32-I/O forward and the
- *    decode step compute in fp32 throughout.
- */
+ *  - Numerics of the bf16 chunked forward: bf16 inputs are widened exactly; products run on
+ *    fp16 MFMA with fp32 accumulation; the state is held in fp32 and rounded to an fp16
+ *    operand copy once per 64-token chunk.  The state, the chunk's values and the terms
+ *    derived from them (R, Z) are carried with a power-of-two scale chosen per chunk and per
+ *    16 value channels, so their fp16 roundings do not depend on the overall scale of v and
+ *    the initial state: the result scales exactly with (v, initial_state) while both stay
+ *    inside fp32's range.  q, k and the gates enter fp16 operands unscaled, so |q|, |k|
+ *    (and |k| times a per-channel decay factor) must stay below 65504.  o is rounded to bf16
+ *    (RNE) once at the end.  The fp32-I/O forward and the decode step compute in fp32
+ *    throughout.
+ *  - Gates: the pages' gates decay, g <= 0 (0 < a <= 1), and the chunked kernels rely on it
+ *    only for range: every decay factor they form is e^{G_i - G_j} with the later token i,
+ *    at most 1.  A positive g is accepted and computed, but those factors then grow like
+ *    e^{64 g} across a chunk (fp16 overflow past g of about 0.17 per token on average).
+ *    beta (and the Gated DeltaNet-2 gates) are not clamped; the recurrence itself is
+ *    contractive for unit keys with beta in [0, 2].
+ *  - Non-finite inputs propagate: a NaN or infinity in one sequence's inputs affects that
+ *    sequence's outputs and final state only.
+  */
 #ifndef GDR_H
 #define GDR_H
 
@@ -52,7 +72,8 @@ typedef enum gdr_status {
     GDR_ERR_SHAPE = 2,       /* a size outside the supported range                        */
     GDR_ERR_DTYPE = 3,       /* io_dtype is not GDR_BF16 or GDR_F32                       */
     GDR_ERR_UNSUPPORTED = 4, /* valid but not implemented combination                     */
-    GDR_ERR_HIP = 5          /* the HIP runtime rejected a launch                         */
+    GDR_ERR_WORKSPACE = 5,   /* workspace NULL, smaller than required, or overlapping a buffer */
+    GDR_ERR_HIP = 6          /* the HIP runtime rejected a launch                         */
 } gdr_status;
 
 typedef enum gdr_dtype { GDR_BF16 = 0, GDR_F32 = 1 } gdr_dtype;
@@ -69,13 +90,32 @@ int gdr_version(void);
 const char *gdr_status_string(int status);
 
 /*
+ * gdr_chunk_fwd_workspace_size -- bytes of device workspace gdr_chunk_fwd needs.
+ *
+ * Per sequence and 64-token chunk the scalar gate takes 16960 bytes
+ * (B*H*ceil(T/64)*16960) and the per-channel gate 16384 + 388 d_k bytes (66048 for d_k = 128,
+ * 41216 for d_k = 64).  Returns 0 for GDR_F32 I/O (one kernel, no workspace), and -1 for sizes
+ * or enums gdr_chunk_fwd would reject.
+ */
+int64_t gdr_chunk_fwd_workspace_size(int64_t B, int64_t H, int64_t T, int d_k, int d_v,
+                                     int io_dtype, int gate);
+
+/*
  * gdr_chunk_fwd -- chunkwise-parallel forward pass over whole sequences.
  *
  * Computes, for each of the B*H independent (batch, head) sequences, every output o_t of
  * the recurrence above and the final state S_T, with the per-chunk algorithm of
  * "Linear Attention, Visualized", section "Gated DeltaNet (GDN)", "Complete per-chunk
- * algorithm" (scalar gate) and section "Reuse GLA and GDN" (channel gate), chunk size 64:
- * the UT transform (I + B L) T = B inside each chunk, then the chunk-serial state pass.
+ * algorithm" (scalar gate) and section "Reuse GLA and GDN" (channel gate), chunk size 64.
+ * The page notes that the chunk-local quantities can be formed for all chunks in parallel
+ * before the boundary pass threads the state through them; with bf16 I/O the call runs as
+ * two kernels that do exactly that: the first forms, for every chunk at once,
+ * T = N^{-1} diag(beta) (the UT transform, N = I + diag(beta) (Gam (.) K K^T)_strict) and the
+ * decayed score matrix A, and writes them to the workspace; the second walks the chunks in
+ * order with Z = T (V - diag(e^G) K S^T), O = diag(e^G) Q S^T + A Z and the state update.
+ * With the per-channel gate (section "Kimi Delta Attention (KDA)") the first kernel also
+ * writes the decayed copies K e^G, Q e^G, K e^{G_C - G} and e^{G_C}.  GDR_F32 I/O runs one
+ * kernel with fp32 operands and needs no workspace.
  *
  *   q, k           [B, H, T, d_k]  io_dtype
  *   v              [B, H, T, d_v]  io_dtype
@@ -85,71 +125,44 @@ const char *gdr_status_string(int status);
  *   o              [B, H, T, d_v]  io_dtype, written (must not alias an input)
  *   final_state    [B, H, d_v, d_k] float32, written, or NULL to skip; may alias
  *                  initial_state exactly (each state tile is read before it is written)
+ *   workspace      device buffer of at least gdr_chunk_fwd_workspace_size(...) bytes
+ *                  (see the conventions above; GDR_ERR_WORKSPACE if missing or short)
+ *   workspace_bytes  its size in bytes
  *
  * T may be any value in [0, 2^22] (a ragged last chunk is handled exactly; T = 0 copies
  * the initial state, or zeros, to final_state); a longer sequence returns GDR_ERR_SHAPE
- * (split it and carry the state).  B*H*T*max(d_k, d_v) must fit in int64.
+ * (split it and carry the state).  The per-channel gate addresses one sequence's workspace
+ * with 32-bit offsets: T above 4,161,728 (d_k = 128) returns GDR_ERR_SHAPE.
+ * B*H*T*max(d_k, d_v) must fit in int64.
  *
  * Per-channel gate: bf16 I/O only (GDR_ERR_UNSUPPORTED for GDR_F32).  Inside each 16-token
- * block the decay is factored through the block's 9th token; the fast path covers a
- * log-decay spread of up to 6 from that token in every channel, a wider block is
- * recomputed on a bf16 path that holds while every per-token log-decay is >= -10 (a
- * decay factor of at least 4.5e-5 per token).
+ * block the decay is factored through the block's 9th token while every channel's
+ * log-decay stays within 6 of that token's; a wider block forms its diagonal 16x16 Gram tiles
+ * afresh from the bf16 inputs with every factor of the form e^{G_i - G_j} (i the later token),
+ * so any decay the fp32 gate can express is covered.
  */
 gdr_status gdr_chunk_fwd(int64_t B, int64_t H, int64_t T, int d_k, int d_v,
                          int io_dtype, int gate,
                          const void *q, const void *k, const void *v,
                          const float *g, const float *beta,
                          const float *initial_state,
-                         void *o, float *final_state, void *stream);
+                         void *o, float *final_state,
+                         void *workspace, int64_t workspace_bytes, void *stream);
 
 /*
- * gdr_chunk_fwd_workspace_size -- bytes of device workspace gdr_chunk_fwd_ws needs.
- *
- * Returns 0 for configurations that use no workspace (GDR_F32 I/O; GDR_GATE_CHANNEL with
- * one sequence's workspace of 4 GiB or more, i.e. T > 4,161,728 for d_k = 128), the size in
- * bytes otherwise, and -1 for sizes or enums gdr_chunk_fwd would reject.  Per sequence and
- * 64-token chunk the scalar gate takes 16960 bytes (B*H*ceil(T/64)*16960) and the per-channel
- * gate 16384 + 388 d_k bytes (66048 for d_k = 128, 41216 for d_k = 64).
+ * gdr_chunk_fwd_fused_prep_workspace_size -- bytes of device workspace
+ * gdr_chunk_fwd_fused_prep needs, per sequence and 64-token chunk, 16960 + 256 d_k bytes
+ * (49728 for d_k = 128, 33344 for d_k = 64); -1 for sizes gdr_chunk_fwd_fused_prep would
+ * reject.
  */
-int64_t gdr_chunk_fwd_workspace_size(int64_t B, int64_t H, int64_t T, int d_k, int d_v,
-                                     int io_dtype, int gate);
-
-/*
- * gdr_chunk_fwd_ws -- gdr_chunk_fwd with a caller-provided device workspace.
- *
- * Same inputs, outputs, numerics and errors as gdr_chunk_fwd.  With bf16 I/O it runs the
- * per-chunk algorithm as two kernels: the first forms, for every chunk at once,
- * T = N^{-1} diag(beta) (the UT transform) and the decayed score matrix A, and writes them to
- * the workspace; the second walks the chunks in order with Z = T (V - diag(e^G) K S^T).
- * ("Linear Attention, Visualized", section "Gated DeltaNet (GDN)", "Complete per-chunk
- * algorithm": the chunk-local quantities can be formed for all chunks in parallel.)  With
- * the per-channel gate (section "Kimi Delta Attention (KDA)") the first kernel also writes
- * the decayed copies K e^G, Q e^G, K e^{G_C - G} and e^{G_C}.  Configurations whose size
- * query returns 0 ignore the workspace and behave exactly like gdr_chunk_fwd.
- *
- *   workspace        device buffer of at least gdr_chunk_fwd_workspace_size(...) bytes, owned
- *                    by the caller; contents on entry are ignored and on return undefined; it
- *                    must not overlap any input or output (GDR_ERR_INVALID_ARG)
- *   workspace_bytes  its size; smaller than required (or a NULL workspace when one is
- *                    required) returns GDR_ERR_INVALID_ARG
- *
- * Calls that share a workspace must be ordered on one stream.
- */
-gdr_status gdr_chunk_fwd_ws(int64_t B, int64_t H, int64_t T, int d_k, int d_v,
-                            int io_dtype, int gate,
-                            const void *q, const void *k, const void *v,
-                            const float *g, const float *beta,
-                            const float *initial_state,
-                            void *o, float *final_state,
-                            void *workspace, int64_t workspace_bytes, void *stream);
+int64_t gdr_chunk_fwd_fused_prep_workspace_size(int64_t B, int64_t H, int64_t T, int d_k, int d_v);
 
 /*
  * gdr_chunk_fwd_fused_prep -- gdr_chunk_fwd (scalar gate) from raw projections, with the
- * input preparation fused into the chunk kernel.
+ * input preparation fused into the chunk kernels.
  *
  * Forms, per token and head, the inputs the recurrence assumes and runs the chunked forward
- * on them without writing them out:
+ * on them without writing q, k, g or beta out:
  *   q = q_raw / max(||q_raw||_2, 1e-6),  k = k_raw / max(||k_raw||_2, 1e-6)   (over d_k; the
  *       pages take keys L2-normalised by convention, and queries are treated the same way)
  *   beta = 1 / (1 + exp(-beta_logit))                                        (0 < beta < 1)
@@ -157,12 +170,15 @@ gdr_status gdr_chunk_fwd_ws(int64_t B, int64_t H, int64_t T, int d_k, int d_v,
  * The gate is Mamba-2's construction ("Linear Attention, Visualized", section "Mamba-2:
  * input-dependent scalar decay", "Optional: Constructing the decay gate"): a decay rate
  * lambda = e^{A_log} per head times a positive step Delta_t = softplus(dt_t + b_Delta).
+ * The first kernel normalises q and k (in fp32 before the fp16 rounding), forms beta and g,
+ * and writes, besides T, A and the decay factors, the normalised q and k rows in fp16; the
+ * state kernel reads those instead of the raw inputs.
  *
  *   q_raw, k_raw     [B, H, T, d_k]  bf16 (not normalised)
  *   v                [B, H, T, d_v]  bf16
  *   dt, beta_logit   [B, H, T]       float32
  *   A_log, dt_bias   [H]             float32, one per head
- *   initial_state, o, final_state    as gdr_chunk_fwd
+ *   initial_state, o, final_state, workspace, workspace_bytes   as gdr_chunk_fwd
  *
  * Equivalent to computing q, k, g, beta as above and calling gdr_chunk_fwd with
  * GDR_GATE_SCALAR, except that q and k enter the fp16 MFMA operands unrounded to bf16.
@@ -175,35 +191,15 @@ gdr_status gdr_chunk_fwd_fused_prep(int64_t B, int64_t H, int64_t T, int d_k, in
                                     const float *dt, const float *A_log, const float *dt_bias,
                                     const float *beta_logit,
                                     const float *initial_state,
-                                    void *o, float *final_state, void *stream);
+                                    void *o, float *final_state,
+                                    void *workspace, int64_t workspace_bytes, void *stream);
 
 /*
- * gdr_chunk_fwd_fused_prep_workspace_size -- bytes of device workspace
- * gdr_chunk_fwd_fused_prep_ws needs, per sequence and 64-token chunk, 16960 + 256 d_k bytes
- * (49728 for d_k = 128, 33344 for d_k = 64); -1 for sizes gdr_chunk_fwd_fused_prep would
- * reject.
+ * gdr_gdp_chunk_fwd_workspace_size -- bytes of device workspace gdr_gdp_chunk_fwd needs:
+ * the scalar gate's 16960 bytes per sequence and 64 virtual steps,
+ * B*H*ceil(T*n_h/64)*16960; -1 for sizes gdr_gdp_chunk_fwd would reject.
  */
-int64_t gdr_chunk_fwd_fused_prep_workspace_size(int64_t B, int64_t H, int64_t T, int d_k, int d_v);
-
-/*
- * gdr_chunk_fwd_fused_prep_ws -- gdr_chunk_fwd_fused_prep with a caller-provided workspace.
- *
- * Same inputs, outputs and errors as gdr_chunk_fwd_fused_prep, on the two-kernel path of
- * gdr_chunk_fwd_ws: the UT kernel normalises q and k (q / max(||q||, 1e-6), in fp32 before the
- * fp16 rounding), forms beta and g from their raw inputs, and writes, besides T, A and the
- * decay factors, the normalised q and k rows in fp16; the state kernel reads those instead of
- * the raw inputs.
- *
- *   workspace, workspace_bytes   as for gdr_chunk_fwd_ws (must not overlap any input or output)
- */
-gdr_status gdr_chunk_fwd_fused_prep_ws(int64_t B, int64_t H, int64_t T, int d_k, int d_v,
-                                       int io_dtype,
-                                       const void *q_raw, const void *k_raw, const void *v,
-                                       const float *dt, const float *A_log, const float *dt_bias,
-                                       const float *beta_logit,
-                                       const float *initial_state,
-                                       void *o, float *final_state,
-                                       void *workspace, int64_t workspace_bytes, void *stream);
+int64_t gdr_gdp_chunk_fwd_workspace_size(int64_t B, int64_t H, int64_t T, int n_h, int d_k, int d_v);
 
 /*
  * gdr_gdp_chunk_fwd -- chunkwise forward pass of the Gated Delta Product.
@@ -215,7 +211,9 @@ gdr_status gdr_chunk_fwd_fused_prep_ws(int64_t B, int64_t H, int64_t T, int d_k,
  * and o_t = S q_t is read after the last one.  Computed, as that page's section "GDP as GDN
  * over a virtual sequence" describes, by the scalar-gate chunked forward of gdr_chunk_fwd run
  * over the T * n_h substeps in order (decay on each token's first substep, query and output
- * on its last), with the same numerics.  n_h = 1 is exactly gdr_chunk_fwd.
+ * on its last), with the same numerics: the first kernel reads q_t on the last substep of a
+ * token and g_t on its first, the state kernel writes o_t on the last substep.  n_h = 1 is
+ * exactly gdr_chunk_fwd.
  *
  *   q              [B, H, T, d_k]         bf16
  *   k              [B, H, T, n_h, d_k]    bf16
@@ -225,6 +223,7 @@ gdr_status gdr_chunk_fwd_fused_prep_ws(int64_t B, int64_t H, int64_t T, int d_k,
  *   initial_state  [B, H, d_v, d_k] float32, or NULL for a zero state
  *   o              [B, H, T, d_v]         bf16, written (must not alias an input)
  *   final_state    [B, H, d_v, d_k] float32, written, or NULL; may alias initial_state exactly
+ *   workspace, workspace_bytes   as gdr_chunk_fwd
  *
  * n_h in [1, 16] (n_h < 1: GDR_ERR_INVALID_ARG, n_h > 16: GDR_ERR_SHAPE); T * n_h <= 2^22
  * (GDR_ERR_SHAPE otherwise); io_dtype must be GDR_BF16 (GDR_F32 returns
@@ -235,31 +234,15 @@ gdr_status gdr_gdp_chunk_fwd(int64_t B, int64_t H, int64_t T, int n_h, int d_k, 
                              const void *q, const void *k, const void *v,
                              const float *g, const float *beta,
                              const float *initial_state,
-                             void *o, float *final_state, void *stream);
+                             void *o, float *final_state,
+                             void *workspace, int64_t workspace_bytes, void *stream);
 
 /*
- * gdr_gdp_chunk_fwd_workspace_size -- bytes of device workspace gdr_gdp_chunk_fwd_ws needs:
- * the scalar gate's 16960 bytes per sequence and 64 virtual steps,
- * B*H*ceil(T*n_h/64)*16960; -1 for sizes gdr_gdp_chunk_fwd would reject.
+ * gdr_gdn2_chunk_fwd_workspace_size -- bytes of device workspace gdr_gdn2_chunk_fwd needs:
+ * gdr_chunk_fwd_workspace_size(B, H, T, d_k, d_v, GDR_BF16, GDR_GATE_CHANNEL) (-1 for sizes
+ * gdr_gdn2_chunk_fwd would reject).
  */
-int64_t gdr_gdp_chunk_fwd_workspace_size(int64_t B, int64_t H, int64_t T, int n_h, int d_k, int d_v);
-
-/*
- * gdr_gdp_chunk_fwd_ws -- gdr_gdp_chunk_fwd with a caller-provided device workspace.
- *
- * Same inputs, outputs and errors as gdr_gdp_chunk_fwd.  Runs the two-kernel path of
- * gdr_chunk_fwd_ws over the T * n_h virtual steps: the UT kernel reads q_t on the last
- * substep of a token and g_t on its first, the state kernel writes o_t on the last substep.
- *
- *   workspace, workspace_bytes   as for gdr_chunk_fwd_ws (must not overlap any input or output)
- */
-gdr_status gdr_gdp_chunk_fwd_ws(int64_t B, int64_t H, int64_t T, int n_h, int d_k, int d_v,
-                                int io_dtype,
-                                const void *q, const void *k, const void *v,
-                                const float *g, const float *beta,
-                                const float *initial_state,
-                                void *o, float *final_state,
-                                void *workspace, int64_t workspace_bytes, void *stream);
+int64_t gdr_gdn2_chunk_fwd_workspace_size(int64_t B, int64_t H, int64_t T, int d_k, int d_v);
 
 /*
  * gdr_gdn2_chunk_fwd -- chunkwise forward pass of Gated DeltaNet-2.
@@ -271,8 +254,11 @@ gdr_status gdr_gdp_chunk_fwd_ws(int64_t B, int64_t H, int64_t T, int n_h, int d_
  *     S_t = S_{t-1} Diag(a_t) (I - e_t k_t^T) + z_t k_t^T,     o_t = S_t q_t
  * (the page's P_t = (I - k_t e_t^T) D_t P_{t-1} + k_t z_t^T for P = S^T): the decayed state is
  * read along e_t and the correction z_t - S Diag(a_t) e_t is written along k_t.  b = w = beta
- * on every channel is exactly gdr_chunk_fwd with GDR_GATE_CHANNEL.  Computed by the
- * per-channel-gate chunk kernel with the same numerics and the same decay range limits.
+ * on every channel is exactly gdr_chunk_fwd with GDR_GATE_CHANNEL.  Runs the per-channel-gate
+ * two-kernel path: the first kernel forms, for every chunk at once, T = N^{-1} with the erase
+ * gate in N's rows, A, and the decayed copies (b (.) k) e^G, q e^G, k e^{G_C - G}; the second
+ * walks the chunks in order with Z = T (z - ((b (.) k) e^G) S^T), where z = w (.) v is formed
+ * and kept in fp32.  Same numerics and decay coverage as the per-channel gate.
  *
  *   q, k           [B, H, T, d_k]  bf16
  *   v              [B, H, T, d_v]  bf16
@@ -282,43 +268,19 @@ gdr_status gdr_gdp_chunk_fwd_ws(int64_t B, int64_t H, int64_t T, int n_h, int d_
  *   initial_state  [B, H, d_v, d_k] float32, or NULL for a zero state
  *   o              [B, H, T, d_v]  bf16, written (must not alias an input)
  *   final_state    [B, H, d_v, d_k] float32, written, or NULL; may alias initial_state exactly
+ *   workspace, workspace_bytes   as gdr_chunk_fwd
  *
  * io_dtype must be GDR_BF16 (GDR_F32 returns GDR_ERR_UNSUPPORTED).  (T + 64) * d_v <= 2^30
- * (the fp32 write gate's 32-bit offsets; GDR_ERR_SHAPE otherwise).  Sizes, the rest of the T
- * range and every other error as for gdr_chunk_fwd.
+ * (the fp32 write gate's 32-bit offsets) and the per-channel gate's T limit, GDR_ERR_SHAPE
+ * otherwise.  Sizes, the rest of the T range and every other error as for gdr_chunk_fwd.
  */
 gdr_status gdr_gdn2_chunk_fwd(int64_t B, int64_t H, int64_t T, int d_k, int d_v,
                               int io_dtype,
                               const void *q, const void *k, const void *v,
                               const float *g, const float *b, const float *w,
                               const float *initial_state,
-                              void *o, float *final_state, void *stream);
-
-/*
- * gdr_gdn2_chunk_fwd_workspace_size -- bytes of device workspace gdr_gdn2_chunk_fwd_ws needs:
- * gdr_chunk_fwd_workspace_size(B, H, T, d_k, d_v, GDR_BF16, GDR_GATE_CHANNEL) (0 when one
- * sequence's workspace would reach 4 GiB, -1 for sizes gdr_gdn2_chunk_fwd would reject).
- */
-int64_t gdr_gdn2_chunk_fwd_workspace_size(int64_t B, int64_t H, int64_t T, int d_k, int d_v);
-
-/*
- * gdr_gdn2_chunk_fwd_ws -- gdr_gdn2_chunk_fwd with a caller-provided device workspace.
- *
- * Same inputs, outputs and errors as gdr_gdn2_chunk_fwd, and the per-channel-gate two-kernel
- * path of gdr_chunk_fwd_ws: the first kernel forms, for every chunk at once, T = N^{-1} with the
- * erase gate in N's rows, A, and the decayed copies (b (.) k) e^G, q e^G, k e^{G_C - G}; the
- * second walks the chunks in order with Z = T (z - ((b (.) k) e^G) S^T), where z = w (.) v is
- * formed and kept in fp32.  A size query of 0 selects the single kernel.
- *
- *   workspace, workspace_bytes   as for gdr_chunk_fwd_ws (must not overlap any input or output)
- */
-gdr_status gdr_gdn2_chunk_fwd_ws(int64_t B, int64_t H, int64_t T, int d_k, int d_v,
-                                 int io_dtype,
-                                 const void *q, const void *k, const void *v,
-                                 const float *g, const float *b, const float *w,
-                                 const float *initial_state,
-                                 void *o, float *final_state,
-                                 void *workspace, int64_t workspace_bytes, void *stream);
+                              void *o, float *final_state,
+                              void *workspace, int64_t workspace_bytes, void *stream);
 
 /*
  * gdr_frame_fwd -- the frame-level implicit update (tokens in unordered frames).
@@ -345,8 +307,10 @@ gdr_status gdr_gdn2_chunk_fwd_ws(int64_t B, int64_t H, int64_t T, int d_k, int d
  *                  frame's state in fp16), owned by the caller, overlapping nothing else
  *
  * Supported: bf16 I/O, d_k and d_v in {64, 128} (GDR_ERR_UNSUPPORTED otherwise); frame_len a
- * positive multiple of 16 and (ceil(T / frame_len) + 1) * d_k * d_k * 2 <= 2^31
- * (GDR_ERR_SHAPE otherwise); T in [0, 2^22].  Numerics: G and C from fp16 MFMA operands
+ * positive multiple of 16 and (ceil(T / frame_len) + 1) * d_v * d_k * 4 < 2^32 (the state
+ * pass addresses one sequence's per-frame records with 32-bit offsets; GDR_ERR_SHAPE
+ * otherwise); T in [0, 2^22].  A NULL, short or overlapping workspace returns
+ * GDR_ERR_WORKSPACE.  Numerics: G and C from fp16 MFMA operands
  * sqrt(gamma) k, sqrt(gamma) v with fp32 accumulation; (I + G)^{-1} by Gauss-Jordan
  * elimination in fp32; the state chained in fp32 with split-fp16 products; o from an fp16
  * copy of each frame's state, rounded to bf16.

@@ -13,9 +13,10 @@ from gated_delta_rule_15_amd import _binding as B
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "gdr.h")
 
-OK, INVALID, SHAPE, DTYPE, UNSUP = 0, 1, 2, 3, 4
+OK, INVALID, SHAPE, DTYPE, UNSUP, WSERR, HIPERR = 0, 1, 2, 3, 4, 5, 6
 FAKE = ctypes.c_void_p(0x10000)        # never dereferenced: every call below fails validation
 FAKE2 = ctypes.c_void_p(0x20000000)
+WS = ctypes.c_void_p(0x50000000)      # a fake workspace that overlaps no other fake buffer
 
 
 @pytest.fixture(scope="module")
@@ -44,15 +45,16 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert gdr.version() == 100
-    for s in range(6):
-        assert gdr.status_string(s)
+    assert gdr.version() == 200
+    for s in range(7):
+        assert gdr.status_string(s) and "unknown" not in gdr.status_string(s)
+    assert "workspace" in gdr.status_string(WSERR)
     assert "unknown" in gdr.status_string(99)
 
 
 def chunk(lib, B=1, H=1, T=64, dk=128, dv=128, io=0, gate=0, q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE,
-          s0=None, o=FAKE2, sf=None):
-    return lib.gdr_chunk_fwd(B, H, T, dk, dv, io, gate, q, k, v, g, beta, s0, o, sf, None)
+          s0=None, o=FAKE2, sf=None, ws=WS, nbytes=1 << 20):
+    return lib.gdr_chunk_fwd(B, H, T, dk, dv, io, gate, q, k, v, g, beta, s0, o, sf, ws, nbytes, None)
 
 
 def decode(lib, N=1, H=1, dk=128, dv=128, io=0, gate=0, q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, S=FAKE2,
@@ -71,6 +73,13 @@ def decode(lib, N=1, H=1, dk=128, dv=128, io=0, gate=0, q=FAKE, k=FAKE, v=FAKE, 
     (dict(io=1, dk=64, dv=64, gate=1), UNSUP),                 # per-channel gate needs bf16 I/O
     (dict(B=1 << 40, H=1 << 30), SHAPE),                       # size overflow
     (dict(T=(1 << 22) + 1), SHAPE),                            # 32-bit per-sequence offsets
+    (dict(T=64 * 65027 + 1, dv=32, gate=1), SHAPE),            # channel-gate workspace of a sequence >= 4 GiB
+    (dict(ws=None), WSERR),                                    # a workspace is required
+    (dict(nbytes=16959), WSERR),                               # one chunk needs 16960 bytes
+    (dict(nbytes=-1), WSERR),
+    (dict(ws=FAKE), WSERR),                                    # workspace overlaps q
+    (dict(ws=FAKE2), WSERR),                                   # workspace overlaps o
+    (dict(gate=1, nbytes=66047), WSERR),                       # channel gate: 66048 bytes per chunk
 ])
 def test_chunk_fwd_rejects(lib, kw, status):
     assert chunk(lib, **kw) == status
@@ -86,7 +95,15 @@ def test_chunk_fwd_state_aliasing_rules(lib):
 
 def test_chunk_fwd_empty_batch_is_a_noop(lib):
     assert chunk(lib, B=0) == OK
-    assert chunk(lib, H=0, q=None, k=None, v=None, g=None, beta=None, o=None) == OK
+    assert chunk(lib, H=0, q=None, k=None, v=None, g=None, beta=None, o=None, ws=None, nbytes=0) == OK
+    assert chunk(lib, T=0, q=None, k=None, v=None, g=None, beta=None, o=None, ws=None, nbytes=0) == OK
+
+
+def test_chunk_fwd_f32_needs_no_workspace(lib):
+    # fp32 I/O queries 0 bytes; the workspace argument is then ignored (validation passes and the
+    # call would launch, so only the no-op shape is called here)
+    assert lib.gdr_chunk_fwd_workspace_size(1, 1, 64, 64, 64, 1, 0) == 0
+    assert chunk(lib, B=0, io=1, dk=64, dv=64, ws=None, nbytes=0) == OK
 
 
 def test_workspace_size(lib):
@@ -94,44 +111,20 @@ def test_workspace_size(lib):
     assert n(4, 16, 4096, 128, 128, 0, 0) == 64 * 64 * 16960        # A^T, T, factors per (sequence, chunk)
     assert n(1, 1, 65, 64, 32, 0, 0) == 2 * 16960                    # ragged tail counts as a chunk
     assert n(1, 1, 0, 128, 128, 0, 0) == 0
-    assert n(2, 2, 100, 64, 64, 1, 0) == 0                           # fp32 I/O: single kernel
+    assert n(2, 2, 100, 64, 64, 1, 0) == 0                           # fp32 I/O: one kernel, no workspace
+    assert n(2, 2, 100, 128, 64, 1, 0) == -1                         # fp32 I/O is d_k = 64 only
     assert n(2, 2, 100, 128, 128, 0, 1) == 4 * 2 * 66048             # channel gate: 16384 + 388 d_k
     assert n(1, 3, 64, 64, 64, 0, 1) == 3 * 41216
     assert n(1, 1, 64 * 65027, 128, 32, 0, 1) == 65027 * 66048       # one sequence just below 4 GiB
-    assert n(1, 1, 64 * 65027 + 1, 128, 32, 0, 1) == 0               # beyond: the single kernel
+    assert n(1, 1, 64 * 65027 + 1, 128, 32, 0, 1) == -1              # beyond: rejected
     assert n(1, 1, 64, 96, 128, 0, 0) == -1 and n(-1, 1, 64, 128, 128, 0, 0) == -1
     assert n(1, 1, (1 << 22) + 1, 128, 128, 0, 0) == -1
     assert gdr.chunk_fwd_workspace_size(1, 2, 128, 128, 128) == 2 * 2 * 16960
 
 
-def ws(lib, B=1, H=1, T=64, dk=128, dv=128, io=0, gate=0, q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, s0=None,
-       o=FAKE2, sf=None, w=ctypes.c_void_p(0x50000000), nbytes=1 << 20):
-    return lib.gdr_chunk_fwd_ws(B, H, T, dk, dv, io, gate, q, k, v, g, beta, s0, o, sf, w, nbytes, None)
-
-
-@pytest.mark.parametrize("kw,status", [
-    (dict(B=-1), INVALID), (dict(dk=96), SHAPE), (dict(io=2), DTYPE), (dict(q=None), INVALID),
-    (dict(o=FAKE), INVALID),                                    # o overlaps q
-    (dict(w=None), INVALID),                                    # a workspace is required
-    (dict(nbytes=16959), INVALID),                              # one chunk needs 16960 bytes
-    (dict(nbytes=-1), INVALID),
-    (dict(w=FAKE), INVALID),                                    # workspace overlaps q
-    (dict(w=FAKE2), INVALID),                                   # workspace overlaps o
-    (dict(T=(1 << 22) + 1), SHAPE),
-    (dict(io=1, dk=128), UNSUP),
-])
-def test_chunk_fwd_ws_rejects(lib, kw, status):
-    assert ws(lib, **kw) == status
-
-
-def test_chunk_fwd_ws_noops(lib):
-    assert ws(lib, B=0) == OK
-    assert ws(lib, T=0, q=None, k=None, v=None, g=None, beta=None, o=None, w=None, nbytes=0) == OK
-
-
 def gdp(lib, B=1, H=1, T=64, nh=2, dk=128, dv=128, io=0, q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE,
-        s0=None, o=FAKE2, sf=None):
-    return lib.gdr_gdp_chunk_fwd(B, H, T, nh, dk, dv, io, q, k, v, g, beta, s0, o, sf, None)
+        s0=None, o=FAKE2, sf=None, ws=WS, nbytes=1 << 20):
+    return lib.gdr_gdp_chunk_fwd(B, H, T, nh, dk, dv, io, q, k, v, g, beta, s0, o, sf, ws, nbytes, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -144,6 +137,10 @@ def gdp(lib, B=1, H=1, T=64, nh=2, dk=128, dv=128, io=0, q=FAKE, k=FAKE, v=FAKE,
     (dict(T=1 << 21, nh=3), SHAPE),                             # T * n_h above 2^22
     (dict(T=(1 << 22) + 1, nh=1), SHAPE),
     (dict(B=1 << 40, H=1 << 30), SHAPE),                        # size overflow
+    (dict(ws=None), WSERR),                                     # a workspace is required
+    (dict(nbytes=2 * 16960 - 1), WSERR),                        # 128 virtual steps: two records
+    (dict(nbytes=-1), WSERR),
+    (dict(ws=FAKE), WSERR), (dict(ws=FAKE2), WSERR),            # workspace overlaps q / o
 ])
 def test_gdp_chunk_fwd_rejects(lib, kw, status):
     assert gdp(lib, **kw) == status
@@ -151,25 +148,7 @@ def test_gdp_chunk_fwd_rejects(lib, kw, status):
 
 def test_gdp_chunk_fwd_empty_batch_is_a_noop(lib):
     assert gdp(lib, B=0) == OK
-    assert gdp(lib, H=0, q=None, k=None, v=None, g=None, beta=None, o=None) == OK
-
-
-def gdp_ws(lib, B=1, H=1, T=64, nh=2, dk=128, dv=128, io=0, q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE,
-           s0=None, o=FAKE2, sf=None, ws=ctypes.c_void_p(0x50000000), nbytes=1 << 20):
-    return lib.gdr_gdp_chunk_fwd_ws(B, H, T, nh, dk, dv, io, q, k, v, g, beta, s0, o, sf, ws, nbytes, None)
-
-
-@pytest.mark.parametrize("kw,status", [
-    (dict(B=-1), INVALID), (dict(nh=0), INVALID), (dict(nh=17), SHAPE), (dict(dk=96), SHAPE),
-    (dict(io=1), UNSUP), (dict(q=None), INVALID), (dict(o=FAKE), INVALID),
-    (dict(ws=None), INVALID),                                   # a workspace is required
-    (dict(nbytes=2 * 16960 - 1), INVALID),                      # 128 virtual steps: two records
-    (dict(nbytes=-1), INVALID),
-    (dict(ws=FAKE), INVALID), (dict(ws=FAKE2), INVALID),        # workspace overlaps q / o
-    (dict(T=1 << 21, nh=3), SHAPE),                             # T n_h beyond 2^22
-])
-def test_gdp_chunk_fwd_ws_rejects(lib, kw, status):
-    assert gdp_ws(lib, **kw) == status
+    assert gdp(lib, H=0, q=None, k=None, v=None, g=None, beta=None, o=None, ws=None, nbytes=0) == OK
 
 
 def test_gdp_workspace_size(lib):
@@ -180,19 +159,14 @@ def test_gdp_workspace_size(lib):
     assert n(1, 1, 64, 0, 128, 128) == -1 and n(1, 1, 64, 17, 128, 128) == -1
 
 
-def test_gdp_ws_empty_batch_is_a_noop(lib):
-    assert gdp_ws(lib, B=0) == OK
-    assert gdp_ws(lib, H=0, q=None, k=None, v=None, g=None, beta=None, o=None, ws=None, nbytes=0) == OK
-
-
 def test_gdp_partial_state_overlap_rejected(lib):
     s = ctypes.c_void_p(0x30000000)
     assert gdp(lib, s0=s, sf=ctypes.c_void_p(0x30000000 + 4)) == INVALID
 
 
 def gdn2(lib, B=1, H=1, T=64, dk=128, dv=128, io=0, q=FAKE, k=FAKE, v=FAKE, g=FAKE, b=FAKE, w=FAKE,
-         s0=None, o=FAKE2, sf=None):
-    return lib.gdr_gdn2_chunk_fwd(B, H, T, dk, dv, io, q, k, v, g, b, w, s0, o, sf, None)
+         s0=None, o=FAKE2, sf=None, ws=WS, nbytes=1 << 20):
+    return lib.gdr_gdn2_chunk_fwd(B, H, T, dk, dv, io, q, k, v, g, b, w, s0, o, sf, ws, nbytes, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -204,6 +178,10 @@ def gdn2(lib, B=1, H=1, T=64, dk=128, dv=128, io=0, q=FAKE, k=FAKE, v=FAKE, g=FA
     (dict(T=(1 << 22) + 1), SHAPE),
     (dict(T=1 << 22, dv=256), SHAPE),                           # fp32 write gate past 32-bit offsets
     (dict(B=1 << 40, H=1 << 30), SHAPE),
+    (dict(ws=None), WSERR),                                     # a workspace is required
+    (dict(nbytes=66047), WSERR),                                # one chunk needs 66048 bytes
+    (dict(nbytes=-1), WSERR),
+    (dict(ws=FAKE), WSERR), (dict(ws=FAKE2), WSERR),            # workspace overlaps q / o
 ])
 def test_gdn2_chunk_fwd_rejects(lib, kw, status):
     assert gdn2(lib, **kw) == status
@@ -211,26 +189,7 @@ def test_gdn2_chunk_fwd_rejects(lib, kw, status):
 
 def test_gdn2_chunk_fwd_empty_batch_is_a_noop(lib):
     assert gdn2(lib, B=0) == OK
-    assert gdn2(lib, H=0, q=None, k=None, v=None, g=None, b=None, w=None, o=None) == OK
-
-
-def gdn2_ws(lib, B=1, H=1, T=64, dk=128, dv=128, io=0, q=FAKE, k=FAKE, v=FAKE, g=FAKE, b=FAKE, w=FAKE,
-            s0=None, o=FAKE2, sf=None, ws=ctypes.c_void_p(0x50000000), nbytes=1 << 20):
-    return lib.gdr_gdn2_chunk_fwd_ws(B, H, T, dk, dv, io, q, k, v, g, b, w, s0, o, sf, ws, nbytes, None)
-
-
-@pytest.mark.parametrize("kw,status", [
-    (dict(B=-1), INVALID), (dict(dk=96), SHAPE), (dict(io=1), UNSUP), (dict(q=None), INVALID),
-    (dict(w=None), INVALID), (dict(o=FAKE), INVALID),
-    (dict(ws=None), INVALID),                                   # a workspace is required
-    (dict(nbytes=66047), INVALID),                              # one chunk needs 66048 bytes
-    (dict(nbytes=-1), INVALID),
-    (dict(ws=FAKE), INVALID),                                   # workspace overlaps q
-    (dict(ws=FAKE2), INVALID),                                  # workspace overlaps o
-    (dict(T=1 << 22, dv=256), SHAPE),
-])
-def test_gdn2_chunk_fwd_ws_rejects(lib, kw, status):
-    assert gdn2_ws(lib, **kw) == status
+    assert gdn2(lib, H=0, q=None, k=None, v=None, g=None, b=None, w=None, o=None, ws=None, nbytes=0) == OK
 
 
 def test_gdn2_workspace_size(lib):
@@ -239,17 +198,12 @@ def test_gdn2_workspace_size(lib):
     assert n(1, 3, 64, 64, 64) == 3 * 41216
     assert n(1, 1, 0, 128, 128) == 0
     assert n(-1, 1, 64, 128, 128) == -1 and n(1, 1, 64, 96, 128) == -1
-    assert n(1, 1, 64 * 65027 + 1, 128, 32) == 0                     # beyond 4 GiB a sequence: single kernel
-
-
-def test_gdn2_ws_empty_batch_is_a_noop(lib):
-    assert gdn2_ws(lib, B=0) == OK
-    assert gdn2_ws(lib, H=0, q=None, k=None, v=None, g=None, b=None, w=None, o=None, ws=None, nbytes=0) == OK
+    assert n(1, 1, 64 * 65027 + 1, 128, 32) == -1                    # beyond 4 GiB a sequence: rejected
 
 
 def prep(lib, B=1, H=1, T=64, dk=128, dv=128, io=0, q=FAKE, k=FAKE, v=FAKE, dt=FAKE, A=FAKE, bias=FAKE,
-         bl=FAKE, s0=None, o=FAKE2, sf=None):
-    return lib.gdr_chunk_fwd_fused_prep(B, H, T, dk, dv, io, q, k, v, dt, A, bias, bl, s0, o, sf, None)
+         bl=FAKE, s0=None, o=FAKE2, sf=None, ws=WS, nbytes=1 << 20):
+    return lib.gdr_chunk_fwd_fused_prep(B, H, T, dk, dv, io, q, k, v, dt, A, bias, bl, s0, o, sf, ws, nbytes, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -260,27 +214,13 @@ def prep(lib, B=1, H=1, T=64, dk=128, dv=128, io=0, q=FAKE, k=FAKE, v=FAKE, dt=F
     (dict(o=FAKE), INVALID),                                    # o overlaps q_raw
     (dict(T=(1 << 22) + 1), SHAPE),
     (dict(B=1 << 40, H=1 << 30), SHAPE),
+    (dict(ws=None), WSERR),                                     # a workspace is required
+    (dict(nbytes=49727), WSERR),                                # one chunk needs 49728 bytes
+    (dict(nbytes=-1), WSERR),
+    (dict(ws=FAKE), WSERR), (dict(ws=FAKE2), WSERR),            # workspace overlaps q_raw / o
 ])
 def test_fused_prep_rejects(lib, kw, status):
     assert prep(lib, **kw) == status
-
-
-def prep_ws(lib, B=1, H=1, T=64, dk=128, dv=128, io=0, q=FAKE, k=FAKE, v=FAKE, dt=FAKE, A=FAKE, bias=FAKE,
-            bl=FAKE, s0=None, o=FAKE2, sf=None, ws=ctypes.c_void_p(0x50000000), nbytes=1 << 20):
-    return lib.gdr_chunk_fwd_fused_prep_ws(B, H, T, dk, dv, io, q, k, v, dt, A, bias, bl, s0, o, sf, ws, nbytes, None)
-
-
-@pytest.mark.parametrize("kw,status", [
-    (dict(B=-1), INVALID), (dict(dk=32), SHAPE), (dict(io=1), UNSUP), (dict(A=None), INVALID),
-    (dict(o=FAKE), INVALID),
-    (dict(ws=None), INVALID),                                   # a workspace is required
-    (dict(nbytes=49727), INVALID),                              # one chunk needs 49728 bytes
-    (dict(nbytes=-1), INVALID),
-    (dict(ws=FAKE), INVALID), (dict(ws=FAKE2), INVALID),        # workspace overlaps q_raw / o
-    (dict(T=(1 << 22) + 1), SHAPE),
-])
-def test_fused_prep_ws_rejects(lib, kw, status):
-    assert prep_ws(lib, **kw) == status
 
 
 def test_fused_prep_workspace_size(lib):
@@ -293,7 +233,7 @@ def test_fused_prep_workspace_size(lib):
 
 def test_fused_prep_empty_batch_is_a_noop(lib):
     assert prep(lib, B=0) == OK
-    assert prep(lib, T=0, q=None, k=None, v=None, dt=None, bl=None, o=None) == OK
+    assert prep(lib, T=0, q=None, k=None, v=None, dt=None, bl=None, o=None, ws=None, nbytes=0) == OK
 
 
 def frame(lib, B=1, H=1, T=64, n=16, dk=128, dv=128, io=0, gate=0, q=FAKE, k=FAKE, v=FAKE, gm=FAKE, g=FAKE,
@@ -305,9 +245,11 @@ def frame(lib, B=1, H=1, T=64, n=16, dk=128, dv=128, io=0, gate=0, q=FAKE, k=FAK
     (dict(B=-1), INVALID), (dict(n=0), INVALID), (dict(n=24), SHAPE), (dict(dk=96), SHAPE),
     (dict(dv=32), UNSUP), (dict(dv=256), UNSUP), (dict(io=1, dk=64, dv=64), UNSUP), (dict(io=3), DTYPE),
     (dict(gate=2), INVALID), (dict(q=None), INVALID), (dict(gm=None), INVALID), (dict(g=None), INVALID),
-    (dict(o=FAKE), INVALID), (dict(w=None), INVALID), (dict(nbytes=100), INVALID), (dict(w=FAKE), INVALID),
+    (dict(o=FAKE), INVALID), (dict(w=None), WSERR), (dict(nbytes=100), WSERR), (dict(w=FAKE), WSERR),
+    (dict(nbytes=-1), WSERR),
     (dict(T=(1 << 22) + 1), SHAPE),
-    (dict(T=1 << 22, n=16), SHAPE),                             # frames' W past 32-bit offsets
+    (dict(T=1 << 22, n=16), SHAPE),                             # frames' records past 32-bit offsets
+    (dict(T=16 * 131071, n=16, dk=64, dv=128), SHAPE),          # C of one sequence reaches 4 GiB
 ])
 def test_frame_fwd_rejects(lib, kw, status):
     assert frame(lib, **kw) == status
@@ -319,6 +261,10 @@ def test_frame_workspace_size(lib):
     assert n(1, 2, 1000, 256, 128, 128) == 2 * 4 * per
     assert n(1, 1, 0, 16, 64, 64) == 0
     assert n(1, 1, 64, 24, 128, 128) == -1 and n(1, 1, 64, 16, 128, 32) == -1
+    # one sequence's fp32 C records are addressed with 32-bit offsets (a frame past the end
+    # included): d_k = 64, d_v = 128, frame_len = 16 fits up to 131070 frames
+    assert n(1, 1, 16 * 131070, 16, 64, 128) > 0
+    assert n(1, 1, 16 * 131071, 16, 64, 128) == -1
     assert frame(lib, B=0) == OK
 
 

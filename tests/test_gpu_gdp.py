@@ -55,7 +55,6 @@ def check(name, o, S, o_ref, S_ref):
     assert eo <= TOL_BF16 and es <= TOL_BF16, msg
 
 
-PATHS = {"split": "auto", "single": None}
 
 
 def state(seed, B, H, dv, dk, std=0.05):
@@ -66,62 +65,55 @@ def state(seed, B, H, dv, dk, std=0.05):
 @pytest.mark.parametrize("nh", [2, 3, 4])
 @pytest.mark.parametrize("dk,dv", [(128, 128), (64, 96)])
 @pytest.mark.parametrize("with_s0", [False, True])
-@pytest.mark.parametrize("path", sorted(PATHS))
-def test_gdp_small(T, nh, dk, dv, with_s0, path):
+def test_gdp_small(T, nh, dk, dv, with_s0):
     w = variant(nh=nh, d_k=dk, d_v=dv)
     x = gdr_synth.make_inputs(w, B=2, H=2, T=T)
     S0 = state(T + nh, 2, 2, dv, dk) if with_s0 else None
-    o, S = run_gdp(x, S0, workspace=PATHS[path])
+    o, S = run_gdp(x, S0)
     o_ref, S_ref = oracle.gdp_forward(x["q"], x["k"], x["v"], x["g"], x["beta"], S0)
-    check(f"gdp {path} T={T} nh={nh} dk={dk} dv={dv} s0={with_s0}", o, S, o_ref, S_ref)
+    check(f"gdp T={T} nh={nh} dk={dk} dv={dv} s0={with_s0}", o, S, o_ref, S_ref)
 
 
 @pytest.mark.parametrize("nh,T", [(5, 30), (16, 9), (7, 64)])
-@pytest.mark.parametrize("path", sorted(PATHS))
-def test_gdp_many_substeps(nh, T, path):
+def test_gdp_many_substeps(nh, T):
     w = variant(nh=nh)
     x = gdr_synth.make_inputs(w, B=1, H=2, T=T)
     S0 = state(nh, 1, 2, 128, 128)
-    o, S = run_gdp(x, S0, workspace=PATHS[path])
+    o, S = run_gdp(x, S0)
     o_ref, S_ref = oracle.gdp_forward(x["q"], x["k"], x["v"], x["g"], x["beta"], S0)
-    check(f"gdp {path} nh={nh} T={T}", o, S, o_ref, S_ref)
+    check(f"gdp nh={nh} T={T}", o, S, o_ref, S_ref)
 
 
-@pytest.mark.parametrize("path", sorted(PATHS))
-def test_gdp_equals_chunk_fwd_on_the_virtual_sequence(path):
+def test_gdp_equals_chunk_fwd_on_the_virtual_sequence():
     """The GDP kernels read q, g and write o through the substep mapping; fed the expanded
     virtual sequence, the chunked forward on the same path (the same kernel bodies) must give
     the same bits."""
     w = variant(nh=3)
     x = gdr_synth.make_inputs(w, B=2, H=3, T=150)
     S0 = state(3, 2, 3, 128, 128)
-    o, S = run_gdp(x, S0, workspace=PATHS[path])
+    o, S = run_gdp(x, S0)
     qt, kt, vt, gt, bt, keep = oracle.gdp_as_virtual_gdn(x["q"], x["k"], x["v"], x["g"], x["beta"])
-    ov, Sv = gdr.chunk_fwd(dev(qt, True), dev(kt, True), dev(vt, True), dev(gt), dev(bt), dev(S0),
-                           workspace=PATHS[path])
+    ov, Sv = gdr.chunk_fwd(dev(qt, True), dev(kt, True), dev(vt, True), dev(gt), dev(bt), dev(S0))
     torch.cuda.synchronize()
     assert torch.equal(o, ov[:, :, torch.from_numpy(keep).to(DEV)])
     assert torch.equal(S, Sv)
 
 
-@pytest.mark.parametrize("path", sorted(PATHS))
-def test_gdp_one_substep_is_chunk_fwd(path):
+def test_gdp_one_substep_is_chunk_fwd():
     w = variant(nh=1)
     x = gdr_synth.make_inputs(w, B=1, H=4, T=200)
     o, S = gdr.gdp_chunk_fwd(dev(x["q"], True), dev(x["k"][:, :, :, None], True), dev(x["v"][:, :, :, None], True),
-                             dev(x["g"]), dev(x["beta"][:, :, :, None]), workspace=PATHS[path])
-    o2, S2 = gdr.chunk_fwd(dev(x["q"], True), dev(x["k"], True), dev(x["v"], True), dev(x["g"]), dev(x["beta"]),
-                           workspace=PATHS[path])
+                             dev(x["g"]), dev(x["beta"][:, :, :, None]))
+    o2, S2 = gdr.chunk_fwd(dev(x["q"], True), dev(x["k"], True), dev(x["v"], True), dev(x["g"]), dev(x["beta"]))
     torch.cuda.synchronize()
     assert torch.equal(o, o2) and torch.equal(S, S2)
 
 
-@pytest.mark.parametrize("path", sorted(PATHS))
-def test_gdp_full_size_sampled(path):
+def test_gdp_full_size_sampled():
     """B=4, H=16, T=2048, n_h=2, d=128 bf16 (4096 substeps per sequence); 6 of 64 sequences."""
     w = gdr_synth.WORKLOADS[6]
     x = gdr_synth.make_inputs(w)
-    o, S = run_gdp(x, workspace=PATHS[path])
+    o, S = run_gdp(x)
     rng = np.random.default_rng(6)
     pick = np.sort(rng.choice(w.B * w.H, size=6, replace=False))
     bi, hi = pick // w.H, pick % w.H
@@ -130,7 +122,7 @@ def test_gdp_full_size_sampled(path):
     o_ref, S_ref = oracle.recurrent_forward(qt, kt, vt, gt, bt)
     o_s = o[torch.from_numpy(bi), torch.from_numpy(hi)][None]
     S_s = S[torch.from_numpy(bi), torch.from_numpy(hi)][None]
-    check(f"gdp full size, {path} (6 sampled heads)", o_s, S_s, o_ref[:, :, keep], S_ref)
+    check(f"gdp full size, (6 sampled heads)", o_s, S_s, o_ref[:, :, keep], S_ref)
 
 
 def test_gdp_carried_state_split():

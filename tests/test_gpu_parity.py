@@ -104,33 +104,20 @@ def test_decode_full_size_64_steps_sampled():
 
 
 # ----------------------------------------------------------------------------- chunk_fwd
-# "split": gdr_chunk_fwd_ws (UT kernel for all chunks, then the state pass); "single":
-# gdr_chunk_fwd (one producer/consumer kernel)
-PATHS = {"split": "auto", "single": None}
 
 
 @pytest.mark.parametrize("T", [1, 37, 64, 65, 200])
 @pytest.mark.parametrize("dk,dv", [(128, 128), (128, 32), (64, 64), (128, 256), (64, 96)])
 @pytest.mark.parametrize("with_s0", [False, True])
-@pytest.mark.parametrize("path", sorted(PATHS))
-def test_chunk_small_bf16(T, dk, dv, with_s0, path):
+def test_chunk_small_bf16(T, dk, dv, with_s0):
     w = variant(2, d_k=dk, d_v=dv)
     x = gdr_synth.make_inputs(w, B=2, H=2, T=T)
     S0 = (np.random.default_rng(T).standard_normal((2, 2, dv, dk)) * 0.05).astype(np.float32) if with_s0 else None
-    o, S = run_chunk(x, True, S0, workspace=PATHS[path])
+    o, S = run_chunk(x, True, S0)
     o_ref, S_ref = oracle.recurrent_forward(x["q"], x["k"], x["v"], x["g"], x["beta"], S0)
-    check(f"chunk bf16 {path} T={T} dk={dk} dv={dv} s0={with_s0}", o, S, o_ref, S_ref, True)
+    check(f"chunk bf16 T={T} dk={dk} dv={dv} s0={with_s0}", o, S, o_ref, S_ref, True)
 
 
-def test_chunk_split_equals_single_closely():
-    """The two paths compute the same algebra with different roundings (T formed densely in
-    the split path, blockwise substitution in the single kernel): they agree within the
-    outputs' bf16 rounding."""
-    x = gdr_synth.make_inputs(gdr_synth.WORKLOADS[2], B=2, H=4, T=333)
-    o1, S1 = run_chunk(x, True, None, workspace="auto")
-    o2, S2 = run_chunk(x, True, None, workspace=None)
-    assert err_bf16_out(host(o1), host(o2)) <= TOL_BF16
-    assert err_literal(host(S1), host(S2)) <= TOL_BF16
 
 
 def test_chunk_split_explicit_workspace_reused():
@@ -142,7 +129,7 @@ def test_chunk_split_explicit_workspace_reused():
         x = gdr_synth.make_inputs(gdr_synth.WORKLOADS[2], B=2, H=2, T=T, salt=T)
         o, S = run_chunk(x, True, None, workspace=wsb)
         o_ref, S_ref = oracle.recurrent_forward(x["q"], x["k"], x["v"], x["g"], x["beta"])
-        check(f"chunk split, reused workspace T={T}", o, S, o_ref, S_ref, True)
+        check(f"chunk, reused workspace T={T}", o, S, o_ref, S_ref, True)
 
 
 @pytest.mark.parametrize("T", [1, 63, 100, 256])
@@ -178,45 +165,41 @@ def _sampled_full(wid, nsample, seed, **kw):
     return o_s, S_s, o_ref, S_ref
 
 
-@pytest.mark.parametrize("path", sorted(PATHS))
-def test_chunk_workload2_full_size_sampled(path):
+def test_chunk_workload2_full_size_sampled():
     """B=4, H=16, T=4096, d=128 bf16; 8 of the 64 sequences checked."""
-    o, S, o_ref, S_ref = _sampled_full(2, 8, 2, workspace=PATHS[path])
-    check(f"workload 2 full size, {path} (8 sampled heads)", o, S, o_ref, S_ref, True)
+    o, S, o_ref, S_ref = _sampled_full(2, 8, 2)
+    check("workload 2 full size (8 sampled heads)", o, S, o_ref, S_ref, True)
 
 
-@pytest.mark.parametrize("path", sorted(PATHS))
-def test_chunk_workload4_full_size_sampled(path):
+def test_chunk_workload4_full_size_sampled():
     """B=1, H=32, T=65536, d=128 bf16 with a carried initial state; 2 heads checked."""
-    o, S, o_ref, S_ref = _sampled_full(4, 2, 4, workspace=PATHS[path])
-    check(f"workload 4 full size, {path} (2 sampled heads)", o, S, o_ref, S_ref, True)
+    o, S, o_ref, S_ref = _sampled_full(4, 2, 4)
+    check("workload 4 full size (2 sampled heads)", o, S, o_ref, S_ref, True)
 
 
 # ----------------------------------------------------------------------------- chunk_fwd, per-channel gate
 @pytest.mark.parametrize("T", [1, 37, 64, 65, 200])
 @pytest.mark.parametrize("dk,dv", [(128, 128), (128, 32), (64, 64), (128, 256), (64, 96)])
 @pytest.mark.parametrize("with_s0", [False, True])
-@pytest.mark.parametrize("path", sorted(PATHS))
-def test_chunk_kda_small(T, dk, dv, with_s0, path):
+def test_chunk_kda_small(T, dk, dv, with_s0):
     w = variant(3, d_k=dk, d_v=dv)
     x = gdr_synth.make_inputs(w, B=2, H=2, T=T)
     S0 = (np.random.default_rng(T).standard_normal((2, 2, dv, dk)) * 0.05).astype(np.float32) if with_s0 else None
-    o, S = run_chunk(x, True, S0, workspace=PATHS[path])
+    o, S = run_chunk(x, True, S0)
     o_ref, S_ref = oracle.recurrent_forward(x["q"], x["k"], x["v"], x["g"], x["beta"], S0)
-    check(f"chunk kda {path} T={T} dk={dk} dv={dv} s0={with_s0}", o, S, o_ref, S_ref, True)
+    check(f"chunk kda T={T} dk={dk} dv={dv} s0={with_s0}", o, S, o_ref, S_ref, True)
 
 
 @pytest.mark.parametrize("lo,hi", [(-3.0, -0.5), (-8.0, -0.01)])
-@pytest.mark.parametrize("path", sorted(PATHS))
-def test_chunk_kda_strong_decay(lo, hi, path):
+def test_chunk_kda_strong_decay(lo, hi):
     """Per-channel log-decays far beyond the fp16 range of the in-block factors (the
-    diagonal tiles take the bf16 path); mixed with weak channels so both paths meet."""
+    diagonal tiles take the exact path); mixed with weak channels so both paths meet."""
     w = variant(3, g_dist=("uniform", lo, hi))
     x = gdr_synth.make_inputs(w, B=1, H=2, T=200)
     x["g"][..., ::3] = x["g"][..., ::3] * 0.01  # every third channel decays slowly
-    o, S = run_chunk(x, True, workspace=PATHS[path])
+    o, S = run_chunk(x, True)
     o_ref, S_ref = oracle.recurrent_forward(x["q"], x["k"], x["v"], x["g"], x["beta"])
-    check(f"chunk kda {path} strong decay U({lo},{hi})", o, S, o_ref, S_ref, True)
+    check(f"chunk kda strong decay U({lo},{hi})", o, S, o_ref, S_ref, True)
 
 
 @pytest.mark.parametrize("wid", [2, 3])
@@ -230,14 +213,6 @@ def test_chunk_full_grid_small_T(wid):
     check(f"full grid, workload {wid} gate, T=150", o, S, o_ref, S_ref, True)
 
 
-def test_chunk_kda_split_equals_single_closely():
-    """Per-channel gate: the two-kernel path (T formed densely) and the single kernel (blockwise
-    substitution) agree within the outputs' bf16 rounding."""
-    x = gdr_synth.make_inputs(gdr_synth.WORKLOADS[3], B=1, H=3, T=777)
-    o1, S1 = run_chunk(x, True, None, workspace="auto")
-    o2, S2 = run_chunk(x, True, None, workspace=None)
-    assert err_bf16_out(host(o1), host(o2)) <= TOL_BF16
-    assert err_literal(host(S1), host(S2)) <= TOL_BF16
 
 
 def test_chunk_kda_uniform_gate_matches_scalar_gate():
@@ -252,11 +227,10 @@ def test_chunk_kda_uniform_gate_matches_scalar_gate():
     check("scalar gate", o1, S1, o_ref, S_ref, True)
 
 
-@pytest.mark.parametrize("path", sorted(PATHS))
-def test_chunk_workload3_full_size_sampled(path):
+def test_chunk_workload3_full_size_sampled():
     """B=2, H=16, T=8192, d=128 bf16, per-channel gate; 2 of the 32 sequences checked."""
-    o, S, o_ref, S_ref = _sampled_full(3, 2, 3, workspace=PATHS[path])
-    check(f"workload 3 full size, {path} (2 sampled heads)", o, S, o_ref, S_ref, True)
+    o, S, o_ref, S_ref = _sampled_full(3, 2, 3)
+    check("workload 3 full size (2 sampled heads)", o, S, o_ref, S_ref, True)
 
 
 def test_chunk_kda_carried_state_split():
