@@ -642,9 +642,10 @@ __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const St
     // keeps max(|S|, |V|) 2^sexp inside [2^-3, 2^6] (rescaled to [2^3, 2^4) when it leaves it):
     // fp16's 11-bit mantissa then holds the values that matter, and no operand (|R| and |Z| stay
     // within a small multiple of that bound) reaches the fp16 maximum.  o and the final state
-    // are divided by 2^sexp on the way out.
+    // are divided by 2^sexp on the way out.  The test is lane-local plus a ballot; only a
+    // rescale (rare) reduces across the wave.
     int sexp = 0;
-    float smax = consumer ? wave_max_abs(max_abs(St)) : 0.0f;  // max |S| 2^sexp over the wave
+    float ls = max_abs(St);  // this lane's largest |S| 2^sexp
 
     // Chunk k's loads live in register set k mod 2.  Loads of chunks past the end are issued
     // anyway (they read past the buffers' ends, which returns zeros, and are staged into a
@@ -756,7 +757,7 @@ __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const St
                                      __uint_as_float(vb.y << 16), __uint_as_float(vb.y & 0xffff0000u)};
                 }
             }
-            const float vmax = wave_max_abs(max_abs(vv));  // max |V| of the chunk (unscaled)
+            const float lv = max_abs(vv);  // this lane's largest |V| of the chunk (unscaled)
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
@@ -790,23 +791,29 @@ __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const St
                 eGC = F[L::FEC];
             }
             __builtin_amdgcn_sched_barrier(0);
-            // the operand scale of this chunk: rescale S (and P_K, computed from it) when the
-            // chunk's V or the state leave the range (a wave-uniform, rare branch)
-            float pqs = 1.0f;  // P_Q is computed below from the unrescaled copy Sb
+            // the operand scale of this chunk: when the chunk's V or the state leave the range
+            // (a wave-uniform, rare branch), rescale S, repack its operand copy and redo P_K
             {
-                const float M = fmaxf(smax, vmax * __builtin_ldexpf(1.0f, sexp));
-                if ((M > 64.0f || (M < 0.125f && M > 0.0f)) && M <= 3.0e38f) {
+                const float lm = fmaxf(ls, lv * __builtin_ldexpf(1.0f, sexp));
+                if (__any(lm > 64.0f) || __all(lm < 0.125f)) {
+                    const float M = wave_max_abs(lm);
                     const int e2 = min(max(sexp + 4 - __builtin_amdgcn_frexp_expf(M), -100), 100);
-                    pqs = __builtin_ldexpf(1.0f, e2 - sexp);
+                    if (M > 0.0f && M <= 3.0e38f && e2 != sexp) {
+                        const float rho = __builtin_ldexpf(1.0f, e2 - sexp);
 #pragma unroll
-                    for (int t = 0; t < NST; ++t)
+                        for (int t = 0; t < NST; ++t)
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) St[t][r] *= pqs;
+                            for (int r = 0; r < 4; ++r) St[t][r] *= rho;
 #pragma unroll
-                    for (int ti = 0; ti < 4; ++ti)
+                        for (int kb = 0; kb < NKB; ++kb) Sb[kb] = pack8(St[2 * kb], St[2 * kb + 1]);
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) PK[ti][r] *= pqs;
-                    sexp = e2;
+                        for (int ti = 0; ti < 4; ++ti) PK[ti] = zero4();
+#pragma unroll
+                        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                            for (int ti = 0; ti < 4; ++ti) mma16(PK[ti], kfrag(ti, kb), Sb[kb]);
+                        sexp = e2;
+                    }
                 }
             }
             const float vsc = __builtin_ldexpf(1.0f, sexp), osc = __builtin_ldexpf(1.0f, -sexp);
@@ -870,7 +877,7 @@ __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const St
 #pragma unroll
             for (int ti = 0, n = 0; ti < 4; ++ti) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) Oa[ti][r] = eg[ti][r] * pqs * PQ[ti][r];
+                for (int r = 0; r < 4; ++r) Oa[ti][r] = eg[ti][r] * PQ[ti][r];
 #pragma unroll
                 for (int kb = 0; kb <= (ti >> 1); ++kb, ++n) mma16(Oa[ti], af[n], zB[kb]);
             }
@@ -881,7 +888,7 @@ __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const St
                     uint2{pack_bf16x2(Oa[ti][0] * osc, Oa[ti][1] * osc), pack_bf16x2(Oa[ti][2] * osc, Oa[ti][3] * osc)};
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) Sb[kb] = pack8(St[2 * kb], St[2 * kb + 1]);
-            smax = wave_max_abs(max_abs(St));
+            ls = max_abs(St);
         }
         lds_barrier();
     }

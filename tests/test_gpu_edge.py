@@ -71,6 +71,14 @@ def check(name, o, S, o_ref, S_ref):
     assert eo <= TOL_BF16 and es <= TOL_BF16, msg
 
 
+def err_one_ulp(x, ref):
+    """max_i (|x_i - ref_i| - 2^-7 max(|x_i|, |ref_i|))_+ / RMS(ref): two bf16 results charged only
+    beyond one bf16 unit in the last place (two roundings of nearly equal values may differ by
+    one)."""
+    d = np.abs(x - ref) - 2.0 ** -7 * np.maximum(np.abs(x), np.abs(ref))
+    return float(np.max(np.maximum(d, 0.0))) / max(float(np.sqrt(np.mean(ref ** 2))), 1e-30)
+
+
 def s0(seed, B, H, dv, dk, std=0.05):
     return (np.random.default_rng(seed).standard_normal((B, H, dv, dk)) * std).astype(np.float32)
 
@@ -155,7 +163,8 @@ SCALES = [2.0 ** -14, 2.0 ** 12]
 def test_scale_of_values_and_state(wid, scale):
     """(o, S_T) is linear in (v, S0): scaling both by a power of two scales the result
     exactly.  Checked against the oracle on the scaled inputs, and against the GPU's own
-    unscaled result."""
+    unscaled result (the kernels' fp16 operands then differ by a power of two, so the two
+    results agree to fp32 rounding before o's bf16 rounding)."""
     w = gdr_synth.WORKLOADS[wid]
     x = gdr_synth.make_inputs(w, B=1, H=2, T=300)
     S0 = s0(5, 1, 2, 128, 128, std=0.3)
@@ -166,7 +175,7 @@ def test_scale_of_values_and_state(wid, scale):
     o2, S2 = run(xs, S0s)
     o_ref, S_ref = oracle.recurrent_forward(xs["q"], xs["k"], xs["v"], xs["g"], xs["beta"], S0s)
     check(f"workload {wid} gate, v and S0 times {scale:g}", o2, S2, o_ref, S_ref)
-    assert err_bf16_out(host(o2) / scale, host(o1)) <= 1e-3
+    assert err_one_ulp(host(o2) / scale, host(o1)) <= 1e-3
     assert err_literal(host(S2) / scale, host(S1)) <= 1e-3
 
 
