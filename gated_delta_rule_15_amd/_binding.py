@@ -30,6 +30,7 @@ GDR_GATE_SCALAR, GDR_GATE_CHANNEL = 0, 1
 
 # every entry point include/gdr.h declares
 EXPORTED_SYMBOLS = ("gdr_version", "gdr_status_string", "gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd",
+                    "gdr_chunk_fwd_noalloc",
                     "gdr_chunk_fwd_fused_prep_workspace_size", "gdr_chunk_fwd_fused_prep",
                     "gdr_gdp_chunk_fwd_workspace_size", "gdr_gdp_chunk_fwd", "gdr_gdn2_chunk_fwd_workspace_size",
                     "gdr_gdn2_chunk_fwd", "gdr_frame_fwd_workspace_size", "gdr_frame_fwd", "gdr_decode_step")
@@ -59,6 +60,7 @@ def load_library():
             "gdr_status_string": (ctypes.c_char_p, [i32]),
             "gdr_chunk_fwd_workspace_size": (i64, [i64, i64, i64, i32, i32, i32, i32]),
             "gdr_chunk_fwd": (i32, [i64, i64, i64, i32, i32, i32, i32] + [P] * 9 + [i64, P]),
+            "gdr_chunk_fwd_noalloc": (i32, [i64, i64, i64, i32, i32, i32, i32] + [P] * 9),
             "gdr_chunk_fwd_fused_prep_workspace_size": (i64, [i64, i64, i64, i32, i32]),
             "gdr_chunk_fwd_fused_prep": (i32, [i64, i64, i64, i32, i32, i32] + [P] * 11 + [i64, P]),
             "gdr_gdp_chunk_fwd_workspace_size": (i64, [i64, i64, i64, i32, i32, i32]),
@@ -199,6 +201,49 @@ def chunk_fwd(q, k, v, g, beta, initial_state=None, *, output_final_state=True, 
     if st != GDR_OK:
         raise GdrError(st, "gdr_chunk_fwd")
     return o, final_state
+
+
+# the size of gdr_chunk_fwd_noalloc's built-in workspace (GDR_CHUNK_FWD_NOALLOC_WORKSPACE_BYTES)
+NOALLOC_WORKSPACE_BYTES = 96 << 20
+
+
+def chunk_fwd_noalloc(q, k, v, g, beta, initial_state, out, final_state, *, stream=None):
+    """gdr_chunk_fwd_noalloc on torch tensors: chunk_fwd with the library's built-in workspace.
+
+    Same tensors as chunk_fwd; the outputs ``out`` and ``final_state`` (or None to skip the
+    state) are the caller's, so the call allocates nothing.  Raises GdrError with
+    GDR_ERR_WORKSPACE when the configuration needs more than NOALLOC_WORKSPACE_BYTES.  Calls on
+    one GPU share the built-in workspace: overlapping calls (other streams or threads) race.
+    """
+    import torch
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("chunk_fwd_noalloc needs GPU tensors")
+    io = _io_dtype(q)
+    _check(q, "q", (B, H, T, dk), q.dtype, dev)
+    _check(k, "k", (B, H, T, dk), q.dtype, dev)
+    _check(v, "v", (B, H, T, dv), q.dtype, dev)
+    if g.shape == (B, H, T):
+        gate = GDR_GATE_SCALAR
+    elif g.shape == (B, H, T, dk):
+        gate = GDR_GATE_CHANNEL
+    else:
+        raise ValueError(f"g: expected [B,H,T] or [B,H,T,d_k], got {tuple(g.shape)}")
+    _check(g, "g", tuple(g.shape), torch.float32, dev)
+    _check(beta, "beta", (B, H, T), torch.float32, dev)
+    if initial_state is not None:
+        _check(initial_state, "initial_state", (B, H, dv, dk), torch.float32, dev)
+    _check(out, "out", (B, H, T, dv), q.dtype, dev)
+    if final_state is not None:
+        _check(final_state, "final_state", (B, H, dv, dk), torch.float32, dev)
+    st = load_library().gdr_chunk_fwd_noalloc(B, H, T, dk, dv, io, gate, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                              _ptr(beta), _ptr(initial_state), _ptr(out), _ptr(final_state),
+                                              _stream(stream, dev))
+    if st != GDR_OK:
+        raise GdrError(st, "gdr_chunk_fwd_noalloc")
+    return out, final_state
 
 
 def chunk_fwd_fused_prep_workspace_size(B, H, T, d_k, d_v) -> int:

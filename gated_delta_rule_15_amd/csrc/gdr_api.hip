@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "gdr.h"
 
 namespace gdr {
@@ -154,6 +156,23 @@ gdr_status check_chunk(int64_t B, int64_t H, int64_t T, int d_k, int d_v, int io
     return GDR_OK;
 }
 
+// The kernels of gdr_chunk_fwd on validated arguments and a workspace of the required size.
+gdr_status enqueue_chunk(int64_t BH, int64_t T, int d_k, int d_v, int io_dtype, int gate, const void* q, const void* k,
+                         const void* v, const float* g, const float* beta, const float* initial_state, void* o,
+                         float* final_state, void* workspace, hipStream_t st) {
+    if (io_dtype == GDR_F32)  // fp32 operands throughout, one kernel
+        return from_hip(gdr::chunk_fwd_f32_dispatch(BH, T, d_v, q, k, v, g, beta, initial_state, o, final_state, st));
+    if (gate == GDR_GATE_CHANNEL) {
+        hipError_t e = gdr::chunk_kda_ut_dispatch(BH, T, d_k, q, k, g, beta, nullptr, workspace, st);
+        if (e == hipSuccess)
+            e = gdr::chunk_state_kda_dispatch(BH, T, d_k, d_v, v, nullptr, initial_state, o, final_state, workspace,
+                                              st);
+        return from_hip(e);
+    }
+    return from_hip(gdr::chunk_split_dispatch(BH, T, 1, d_k, d_v, q, k, v, g, beta, initial_state, o, final_state,
+                                              workspace, st));
+}
+
 }  // namespace
 
 extern "C" {
@@ -188,18 +207,8 @@ gdr_status gdr_chunk_fwd(int64_t B, int64_t H, int64_t T, int d_k, int d_v, int 
                          {initial_state, BH * d_k * d_v * 4}, {final_state, BH * d_k * d_v * 4}};
     s = check_workspace(workspace, workspace_bytes, need, bufs, 8);
     if (s != GDR_OK || !launch) return s;
-    const hipStream_t st = static_cast<hipStream_t>(stream);
-    if (io_dtype == GDR_F32)  // fp32 operands throughout, one kernel
-        return from_hip(gdr::chunk_fwd_f32_dispatch(BH, T, d_v, q, k, v, g, beta, initial_state, o, final_state, st));
-    if (gate == GDR_GATE_CHANNEL) {
-        hipError_t e = gdr::chunk_kda_ut_dispatch(BH, T, d_k, q, k, g, beta, nullptr, workspace, st);
-        if (e == hipSuccess)
-            e = gdr::chunk_state_kda_dispatch(BH, T, d_k, d_v, v, nullptr, initial_state, o, final_state, workspace,
-                                              st);
-        return from_hip(e);
-    }
-    return from_hip(gdr::chunk_split_dispatch(BH, T, 1, d_k, d_v, q, k, v, g, beta, initial_state, o, final_state,
-                                              workspace, st));
+    return enqueue_chunk(BH, T, d_k, d_v, io_dtype, gate, q, k, v, g, beta, initial_state, o, final_state, workspace,
+                         static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"
@@ -467,6 +476,63 @@ gdr_status gdr_decode_step(int64_t N, int64_t H, int d_k, int d_v, int io_dtype,
     if (NH > kMaxGrid) return GDR_ERR_SHAPE;
     return from_hip(gdr::decode_dispatch(NH, d_k, d_v, io_dtype == GDR_BF16, gate == GDR_GATE_CHANNEL, q, k, v, g,
                                          beta, state, o, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------------------------
+// gdr_chunk_fwd_noalloc: gdr_chunk_fwd with the library's own device workspace, for callers that
+// cannot allocate.  The workspace is this file-scope array: every GPU the library runs on holds
+// one copy, from module load until the process ends.  Host code never uses the array's name
+// as an address (on the host it only names the symbol); the device address of each GPU's copy
+// comes from hipGetSymbolAddress, taken once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[GDR_CHUNK_FWD_NOALLOC_WORKSPACE_BYTES];
+
+namespace {
+
+std::atomic<void*> g_scratch[64];  // device address of `scratch`, per device id below 64
+
+hipError_t scratch_address(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const bool slot = dev >= 0 && dev < 64;
+    if (slot) {
+        void* p = g_scratch[dev].load(std::memory_order_acquire);
+        if (p != nullptr) {
+            *out = p;
+            return hipSuccess;
+        }
+    }
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    if (slot) g_scratch[dev].store(p, std::memory_order_release);  // concurrent first calls store the same value
+    *out = p;
+    return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdr_status gdr_chunk_fwd_noalloc(int64_t B, int64_t H, int64_t T, int d_k, int d_v, int io_dtype, int gate,
+                                 const void* q, const void* k, const void* v, const float* g, const float* beta,
+                                 const float* initial_state, void* o, float* final_state, void* stream) {
+    int64_t BH = 0;
+    bool launch = false;
+    gdr_status s = check_chunk(B, H, T, d_k, d_v, io_dtype, gate, q, k, v, g, beta, initial_state, o, final_state,
+                               &BH, &launch);
+    if (s != GDR_OK) return s;
+    const int64_t need = gdr_chunk_fwd_workspace_size(B, H, T, d_k, d_v, io_dtype, gate);
+    if (need < 0) return GDR_ERR_SHAPE;
+    if (need > (int64_t)GDR_CHUNK_FWD_NOALLOC_WORKSPACE_BYTES) return GDR_ERR_WORKSPACE;
+    if (!launch) return GDR_OK;
+    void* ws = nullptr;
+    if (need > 0 && scratch_address(&ws) != hipSuccess) return GDR_ERR_HIP;
+    return enqueue_chunk(BH, T, d_k, d_v, io_dtype, gate, q, k, v, g, beta, initial_state, o, final_state, ws,
+                         static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

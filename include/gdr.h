@@ -150,6 +150,30 @@ gdr_status gdr_chunk_fwd(int64_t B, int64_t H, int64_t T, int d_k, int d_v,
                          void *workspace, int64_t workspace_bytes, void *stream);
 
 /*
+ * gdr_chunk_fwd_noalloc -- gdr_chunk_fwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * Same inputs, outputs, numerics and errors as gdr_chunk_fwd, without the workspace arguments:
+ * the workspace is a device array inside the library, GDR_CHUNK_FWD_NOALLOC_WORKSPACE_BYTES
+ * (96 MiB) on every GPU the library runs on, held from the library's load on that GPU until the
+ * process ends.  The call allocates nothing (no hipMalloc, no library allocation).  A
+ * configuration whose gdr_chunk_fwd_workspace_size exceeds that returns GDR_ERR_WORKSPACE
+ * (the B=4, H=16, T=4096, d_k=d_v=128 scalar-gate shape needs 66.25 MiB and fits).
+ *
+ * All calls on one GPU share that GPU's array, which keeps the last call's contents (the
+ * kernels need no particular contents on entry).  Calls that overlap on one GPU -- on
+ * different streams, or from different threads without ordering -- race on the array and
+ * give undefined results; order them on one stream.
+ */
+#define GDR_CHUNK_FWD_NOALLOC_WORKSPACE_BYTES (96u << 20)
+gdr_status gdr_chunk_fwd_noalloc(int64_t B, int64_t H, int64_t T, int d_k, int d_v,
+                                 int io_dtype, int gate,
+                                 const void *q, const void *k, const void *v,
+                                 const float *g, const float *beta,
+                                 const float *initial_state,
+                                 void *o, float *final_state, void *stream);
+
+/*
  * gdr_chunk_fwd_fused_prep_workspace_size -- bytes of device workspace
  * gdr_chunk_fwd_fused_prep needs, per sequence and 64-token chunk, 16960 + 256 d_k bytes
  * (49728 for d_k = 128, 33344 for d_k = 64); -1 for sizes gdr_chunk_fwd_fused_prep would

@@ -106,6 +106,31 @@ def test_chunk_fwd_f32_needs_no_workspace(lib):
     assert chunk(lib, B=0, io=1, dk=64, dv=64, ws=None, nbytes=0) == OK
 
 
+def noalloc(lib, B=1, H=1, T=64, dk=128, dv=128, io=0, gate=0, q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE,
+            s0=None, o=FAKE2, sf=None):
+    return lib.gdr_chunk_fwd_noalloc(B, H, T, dk, dv, io, gate, q, k, v, g, beta, s0, o, sf, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), INVALID), (dict(dk=96), SHAPE), (dict(io=2), DTYPE), (dict(q=None), INVALID),
+    (dict(o=FAKE), INVALID), (dict(io=1, dk=128), UNSUP), (dict(T=(1 << 22) + 1), SHAPE),
+    (dict(B=8, H=16, T=4096), WSERR),                          # 132.5 MiB of records: beyond the 96 MiB built in
+    (dict(B=1, H=16, T=8192, gate=1), WSERR),                  # channel gate: 16 x 128 x 66048 bytes
+])
+def test_chunk_fwd_noalloc_rejects(lib, kw, status):
+    assert noalloc(lib, **kw) == status
+
+
+def test_chunk_fwd_noalloc_limit(lib):
+    n = lib.gdr_chunk_fwd_workspace_size
+    assert n(4, 16, 4096, 128, 128, 0, 0) <= B.NOALLOC_WORKSPACE_BYTES   # the B=4 H=16 T=4096 shape fits
+    assert n(8, 16, 4096, 128, 128, 0, 0) > B.NOALLOC_WORKSPACE_BYTES
+    text = open(HEADER).read()
+    assert re.search(r"#define GDR_CHUNK_FWD_NOALLOC_WORKSPACE_BYTES \(96u << 20\)", text)
+    assert B.NOALLOC_WORKSPACE_BYTES == 96 << 20
+    assert noalloc(lib, B=0) == OK and noalloc(lib, T=0, q=None, k=None, v=None, g=None, beta=None, o=None) == OK
+
+
 def test_workspace_size(lib):
     n = lib.gdr_chunk_fwd_workspace_size
     assert n(4, 16, 4096, 128, 128, 0, 0) == 64 * 64 * 16960        # A^T, T, factors per (sequence, chunk)
