@@ -8,7 +8,9 @@ the long-context workload (B=1, H=32, T=65536, carried state), the per-channel-g
 headline workload from raw projections with the input preparation fused in.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extra]
-    python bench.py --pmc-run      # kernels only, for rocprofv3 counter passes
+    python bench.py --pmc-run WORKLOAD   # one workload's kernels only, for rocprofv3 counter
+                                         # passes: headline, decode, kda, long (and a 256 MiB
+                                         # device copy that calibrates the byte counters)
 
 Prints ONE JSON line.  Inputs are seeded synthetic tensors (gdr_synth) resident in HBM
 before timing starts; two input sets alternate so the 256 MB last-level cache cannot
@@ -33,26 +35,37 @@ PEAK_HBM = 8000.0       # GB/s, MI355X HBM3E
 # the headline step: one gdr_chunk_fwd call = the UT kernel over all chunks, then the
 # chunk-serial state kernel
 CHUNK_KERNEL = "chunk_ut_kernel<128, 0> + chunk_state_kernel<128, 0, 2>"
-CHUNK_SOURCE = os.path.join(ROOT, "gated_delta_rule_15_amd", "csrc", "chunk_split.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "chunk_split_gdn_bf16_B4_H16_T4096_traffic.json")
+CSRC = os.path.join(ROOT, "gated_delta_rule_15_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+# rocprofv3 counter summaries (HBM bytes per call), each tied to the sources it measured
+TRAFFIC = {
+    "headline": ("chunk_split_gdn_bf16_B4_H16_T4096_traffic.json", ("chunk_split.hip", "chunk_common.h", "gdr_device.h")),
+    "kda": ("chunk_kda_B2_H16_T8192_traffic.json", ("chunk_kda.hip", "chunk_split.hip", "chunk_common.h", "gdr_device.h")),
+    "long": ("chunk_split_long_B1_H32_T65536_traffic.json", ("chunk_split.hip", "chunk_common.h", "gdr_device.h")),
+    "decode": ("decode_N256_H32_d128_traffic.json", ("decode.hip", "gdr_device.h")),
+}
 COPY_BYTES = 256 << 20  # calibration copy for the HBM byte counters
 
 
-def source_digest(path):
+def source_digest(files):
     import hashlib
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per launch of the chunk kernel from the committed counter summary, or None
-    when the summary is missing or was taken on a different kernel source."""
+def measured_traffic(workload):
+    """HBM bytes per call from the committed counter summary of ``workload``, or None when the
+    summary is missing or was taken on different kernel sources."""
+    name, files = TRAFFIC[workload]
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(os.path.join(PROFILES, name)) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("source_sha256_16") != source_digest(CHUNK_SOURCE):
+    if rec.get("source_sha256_16") != source_digest(files):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -169,7 +182,8 @@ def bench_decode(torch, gdr, gdr_synth, steps=64):
             "us_per_step_mean": round(float(ms.mean()) * 1e3, 2), "us_per_step_median": round(float(np.median(ms)) * 1e3, 2),
             "tokens_per_s": round(w.B / (ms.mean() * 1e-3), 1),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM, "unit": "GB/s",
-                         "frac": round(gbs / PEAK_HBM, 4), "traffic": None, "bytes_per_step": nbytes},
+                         "frac": round(gbs / PEAK_HBM, 4), "traffic": measured_traffic("decode"),
+                         "bytes_per_step": nbytes},
             "copy_of_the_state_gbs": round(copy_gbs, 1),
             "frac_of_copy_rate": round(gbs / copy_gbs, 4)}
 
@@ -399,8 +413,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="headline workload only")
-    ap.add_argument("--pmc-run", action="store_true",
-                    help="launch the headline chunk kernel --steps times and one 256 MiB device copy, print nothing")
+    ap.add_argument("--pmc-run", choices=("headline", "decode", "kda", "long"), default=None,
+                    help="launch one workload's kernels --steps times and one 256 MiB device copy, print nothing")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path shards by "
@@ -413,17 +427,22 @@ def main():
 
     gdr.load_library()
     w = gdr_synth.WORKLOADS[2]
-    sets = make_chunk_sets(torch, gdr_synth, w)
     if args.pmc_run:
-        # Counter passes: the headline step's kernels on the headline workload, then a plain
-        # copy of known size whose FETCH_SIZE / WRITE_SIZE calibrate the counters' byte units.
-        time_chunk(torch, gdr, sets, args.steps, 0)
+        # Counter passes: one workload's kernels, then a plain copy of known size whose
+        # FETCH_SIZE / WRITE_SIZE calibrate the counters' byte units.
+        if args.pmc_run == "decode":
+            bench_decode(torch, gdr, gdr_synth, steps=args.steps)
+        else:
+            wid = {"headline": 2, "kda": 3, "long": 4}[args.pmc_run]
+            time_chunk(torch, gdr, make_chunk_sets(torch, gdr_synth, gdr_synth.WORKLOADS[wid],
+                                                   nsets=1 if wid == 4 else 2), args.steps, 0)
         src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
         dst.copy_(src)
         torch.cuda.synchronize()
         return
+    sets = make_chunk_sets(torch, gdr_synth, w)
     ms_mean, ms_med, wall, o, S = time_chunk(torch, gdr, sets, args.steps, args.warmup)
     flops = chunk_flops(w.B, w.H, w.T, w.d_k, w.d_v)
     nbytes = chunk_bytes(w.B, w.H, w.T, w.d_k, w.d_v)
@@ -449,7 +468,7 @@ def main():
                    "B": w.B, "H": w.H, "T": w.T, "d_k": w.d_k, "d_v": w.d_v, "chunk": 64, "gate": "scalar",
                    "compute": "f16 MFMA operands, f32 accumulation and state"},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_MFMA_F16, "unit": "TFLOP/s",
-                     "frac": round(tflops / PEAK_MFMA_F16, 4), "traffic": measured_traffic(),
+                     "frac": round(tflops / PEAK_MFMA_F16, 4), "traffic": measured_traffic("headline"),
                      "flops_per_launch": flops, "kernel": CHUNK_KERNEL,
                      "ms_per_launch_mean": round(ms_mean, 5), "ms_per_launch_median": round(ms_med, 5),
                      "note": "one launch = one gdr_chunk_fwd call (both kernels), HIP events around it"},
@@ -466,7 +485,8 @@ def main():
         result["long_context"] = {
             "workload": "B=1 H=32 T=65536 d=128 bf16, S0 ~ 0.02 N(0,1)",
             "ms_per_call": round(m4, 4), "tokens_per_s": round(w4.B * w4.T / (m4 * 1e-3), 1),
-            "mfma_frac": round(chunk_flops(w4.B, w4.H, w4.T, 128, 128) / (m4 * 1e-3) / 1e12 / PEAK_MFMA_F16, 4)}
+            "mfma_frac": round(chunk_flops(w4.B, w4.H, w4.T, 128, 128) / (m4 * 1e-3) / 1e12 / PEAK_MFMA_F16, 4),
+            "traffic": measured_traffic("long")}
         del sets4
         w3 = gdr_synth.WORKLOADS[3]
         sets3 = make_chunk_sets(torch, gdr_synth, w3, nsets=2)
@@ -479,7 +499,7 @@ def main():
             "ms_per_call": round(m3, 4),
             "tokens_per_s": round(w3.B * w3.T / (m3 * 1e-3), 1),
             "mfma_frac": round(f3 / (m3 * 1e-3) / 1e12 / PEAK_MFMA_F16, 4),
-            "hbm_frac": round(b3 / (m3 * 1e-3) / 1e9 / PEAK_HBM, 4)}
+            "hbm_frac": round(b3 / (m3 * 1e-3) / 1e9 / PEAK_HBM, 4), "traffic": measured_traffic("kda")}
         del sets3
         result["gdp"] = bench_gdp(torch, gdr, gdr_synth)
         result["gdn2"] = bench_gdn2(torch, gdr, gdr_synth)
