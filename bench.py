@@ -100,9 +100,26 @@ def to_dev(torch, a, bf16=False):
     return t.to(torch.bfloat16) if bf16 else t
 
 
+def region_ms(torch, launch, steps, warmup=2):
+    """Mean milliseconds per call of launch(i), i = 0..steps-1: HIP events on the launch stream
+    around the calls, enqueued back to back after `warmup` untimed calls."""
+    for i in range(warmup):
+        launch(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        launch(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return float(e0.elapsed_time(e1) / steps)
+
+
 def time_chunk(torch, gdr, sets, steps, warmup, fn=None):
-    """Per-launch HIP-event durations of chunk_fwd (or ``fn``, same signature), alternating
-    input sets."""
+    """Launch durations of chunk_fwd (or ``fn``, same signature), alternating input sets: HIP
+    events on the launch stream around the ``steps`` calls, enqueued back to back (an event
+    pair around every call would add its own packets between the calls); returns the mean per
+    call, the wall clock of the region, and the last outputs."""
     outs = [torch.empty(s["o_shape"], dtype=torch.bfloat16, device="cuda") for s in sets]
     fin = [torch.empty(s["S_shape"], dtype=torch.float32, device="cuda") for s in sets]
     if fn is None:  # the chunked forward with a workspace allocated once, outside the timing
@@ -120,16 +137,16 @@ def time_chunk(torch, gdr, sets, steps, warmup, fn=None):
     for i in range(warmup):
         launch(i)
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    e0.record()
     for i in range(steps):
-        ev[i][0].record()
         launch(i)
-        ev[i][1].record()
+    e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = [a.elapsed_time(b) for a, b in ev]
-    return float(np.mean(ms)), float(np.median(ms)), wall, outs[0], fin[0]
+    ms = e0.elapsed_time(e1) / steps
+    return float(ms), wall, outs[(steps - 1) % len(sets)], fin[(steps - 1) % len(sets)]
 
 
 def make_chunk_sets(torch, gdr_synth, w, nsets=2):
@@ -152,35 +169,20 @@ def bench_decode(torch, gdr, gdr_synth, steps=64):
         d = gdr_synth.make_decode_inputs(w, s)
         inp.append({k: to_dev(torch, v, k in ("q", "k", "v")) for k, v in d.items()})
     out = torch.empty((w.B, w.H, w.d_v), dtype=torch.bfloat16, device="cuda")
-    for s in range(3):  # warm-up (advances the state; it is synthetic)
-        d = inp[s]
+
+    def step(s):  # fresh inputs every step; the state advances in place (it is synthetic)
+        d = inp[s % steps]
         gdr.decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], state, out=out)
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for s in range(steps):
-        d = inp[s]
-        ev[s][0].record()
-        gdr.decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], state, out=out)
-        ev[s][1].record()
-    torch.cuda.synchronize()
-    ms = np.array([a.elapsed_time(b) for a, b in ev])
+
+    ms_mean = region_ms(torch, step, steps, warmup=3)
     nbytes = decode_bytes(w.B, w.H, w.d_k, w.d_v)
-    gbs = nbytes / (ms.mean() * 1e-3) / 1e9
+    gbs = nbytes / (ms_mean * 1e-3) / 1e9
     # context: a device copy of the same state (read once, written once), torch's copy kernel
     dst = torch.empty_like(state)
-    for _ in range(3):
-        dst.copy_(state)
-    torch.cuda.synchronize()
-    evc = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
-    for a_, b_ in evc:
-        a_.record()
-        dst.copy_(state)
-        b_.record()
-    torch.cuda.synchronize()
-    copy_gbs = 2 * state.numel() * 4 / (float(np.mean([a_.elapsed_time(b_) for a_, b_ in evc])) * 1e-3) / 1e9
+    copy_gbs = 2 * state.numel() * 4 / (region_ms(torch, lambda i: dst.copy_(state), 20, warmup=3) * 1e-3) / 1e9
     return {"workload": "decode N=256 H=32 d=128 bf16, 64 steps, 512 MiB fp32 state",
-            "us_per_step_mean": round(float(ms.mean()) * 1e3, 2), "us_per_step_median": round(float(np.median(ms)) * 1e3, 2),
-            "tokens_per_s": round(w.B / (ms.mean() * 1e-3), 1),
+            "us_per_step_mean": round(ms_mean * 1e3, 2),
+            "tokens_per_s": round(w.B / (ms_mean * 1e-3), 1),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM, 4), "traffic": measured_traffic("decode"),
                          "bytes_per_step": nbytes},
@@ -196,8 +198,8 @@ def bench_gdp(torch, gdr, gdr_synth, steps=10):
     sets = make_chunk_sets(torch, gdr_synth, w, nsets=2)
     wsb = torch.empty(max(gdr.gdp_chunk_fwd_workspace_size(w.B, w.H, w.T, w.nh, w.d_k, w.d_v), 1),
                       dtype=torch.uint8, device="cuda")
-    ms, med, _, o, S = time_chunk(torch, gdr, sets, steps, 2,
-                                  fn=lambda *a_, **kw: gdr.gdp_chunk_fwd(*a_, workspace=wsb, **kw))
+    ms, _, o, S = time_chunk(torch, gdr, sets, steps, 2,
+                             fn=lambda *a_, **kw: gdr.gdp_chunk_fwd(*a_, workspace=wsb, **kw))
     Tv = w.T * w.nh
     flops = chunk_flops(w.B, w.H, Tv, w.d_k, w.d_v)
     nbytes = (w.B * w.H * (w.T * (2 * w.d_k + 2 * w.d_v + 4) + Tv * (2 * w.d_k + 2 * w.d_v + 4))
@@ -211,7 +213,6 @@ def bench_gdp(torch, gdr, gdr_synth, steps=10):
     o_ref, S_ref = oracle.recurrent_forward(qt, kt, vt, gt, bt)
     res = {"workload": "gdp_bf16: Gated Delta Product B=4 H=16 T=2048 n_h=2 d_k=d_v=128 bf16, zero S0",
            "kernel": "chunk_ut_kernel<128, 1> + chunk_state_kernel<128, 3, 2>", "ms_per_call": round(ms, 4),
-           "ms_per_call_median": round(med, 4),
            "tokens_per_s": round(w.B * w.T / (ms * 1e-3), 1),
            "substeps_per_s": round(w.B * Tv / (ms * 1e-3), 1),
            "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_MFMA_F16, 4),
@@ -244,19 +245,7 @@ def bench_prep(torch, gdr, gdr_synth, steps=20):
         gdr.chunk_fwd_fused_prep(s["q_raw"], s["k_raw"], s["v"], s["dt"], s["A_log"], s["dt_bias"], s["beta_logit"],
                                  out=outs[i % 2], final_state=fin[i % 2], workspace=ws)
 
-    def timed(ws):
-        for i in range(2):
-            launch(i, ws)
-        torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-        for i in range(steps):
-            ev[i][0].record()
-            launch(i, ws)
-            ev[i][1].record()
-        torch.cuda.synchronize()
-        return float(np.mean([a.elapsed_time(b) for a, b in ev]))
-
-    ms = timed(wsb)
+    ms = region_ms(torch, lambda i: launch(i, wsb), steps)
     n = w.B * w.H * w.T
     separate_pass = n * w.d_k * 2 * 2 * 2 + n * 4 * 4   # q, k read and written (bf16); dt, logit read, g, beta written
     flops = chunk_flops(w.B, w.H, w.T, w.d_k, w.d_v)
@@ -290,16 +279,7 @@ def bench_frame(torch, gdr, gdr_synth, steps=10):
         gdr.frame_fwd(s_["q"], s_["k"], s_["v"], s_["gamma"], s_["g"], n, out=outs[i % 2], final_state=fin[i % 2],
                       workspace=wsb)
 
-    for i in range(2):
-        launch(i)
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for i in range(steps):
-        ev[i][0].record()
-        launch(i)
-        ev[i][1].record()
-    torch.cuda.synchronize()
-    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    ms = region_ms(torch, launch, steps)
     F = wf["T"] // n
     per = n * dk * dk + 2 * n * dk * dv + 2 * dk ** 3 + 2 * dk * dk * dv + 2 * n * dk * dv
     flops = wf["B"] * wf["H"] * F * per
@@ -343,19 +323,7 @@ def bench_gdn2(torch, gdr, gdr_synth, steps=10):
         gdr.gdn2_chunk_fwd(s["q"], s["k"], s["v"], s["g"], s["b"], s["w"], out=outs[i % 2], final_state=fin[i % 2],
                            workspace=ws)
 
-    def timed(ws):
-        for i in range(2):
-            launch(i, ws)
-        torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-        for i in range(steps):
-            ev[i][0].record()
-            launch(i, ws)
-            ev[i][1].record()
-        torch.cuda.synchronize()
-        return float(np.mean([a.elapsed_time(b) for a, b in ev]))
-
-    ms = timed(wsb)
+    ms = region_ms(torch, lambda i: launch(i, wsb), steps)
     flops = chunk_flops(w.B, w.H, w.T, w.d_k, w.d_v)
     n = w.B * w.H * w.T
     nbytes = n * (2 * w.d_k + 2 * w.d_v) * 2 + n * (2 * w.d_k + w.d_v) * 4 + w.B * w.H * w.d_k * w.d_v * 4
@@ -443,7 +411,7 @@ def main():
         torch.cuda.synchronize()
         return
     sets = make_chunk_sets(torch, gdr_synth, w)
-    ms_mean, ms_med, wall, o, S = time_chunk(torch, gdr, sets, args.steps, args.warmup)
+    ms_mean, wall, o, S = time_chunk(torch, gdr, sets, args.steps, args.warmup)
     flops = chunk_flops(w.B, w.H, w.T, w.d_k, w.d_v)
     nbytes = chunk_bytes(w.B, w.H, w.T, w.d_k, w.d_v)
     tflops = flops / (ms_mean * 1e-3) / 1e12
@@ -470,8 +438,9 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_MFMA_F16, "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_MFMA_F16, 4), "traffic": measured_traffic("headline"),
                      "flops_per_launch": flops, "kernel": CHUNK_KERNEL,
-                     "ms_per_launch_mean": round(ms_mean, 5), "ms_per_launch_median": round(ms_med, 5),
-                     "note": "one launch = one gdr_chunk_fwd call (both kernels), HIP events around it"},
+                     "ms_per_launch_mean": round(ms_mean, 5),
+                     "note": "one launch = one gdr_chunk_fwd call (both kernels); HIP events on the launch "
+                             "stream around the timed calls, enqueued back to back"},
         "roofline_hbm": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM, 4), "bytes_per_launch": nbytes},
         "wall_s_timed_region": round(wall, 4),
@@ -481,7 +450,7 @@ def main():
         result["decode"] = bench_decode(torch, gdr, gdr_synth)
         w4 = gdr_synth.WORKLOADS[4]
         sets4 = make_chunk_sets(torch, gdr_synth, w4, nsets=1)
-        m4, _, _, _, _ = time_chunk(torch, gdr, sets4, 5, 1)
+        m4, _, _, _ = time_chunk(torch, gdr, sets4, 5, 1)
         result["long_context"] = {
             "workload": "B=1 H=32 T=65536 d=128 bf16, S0 ~ 0.02 N(0,1)",
             "ms_per_call": round(m4, 4), "tokens_per_s": round(w4.B * w4.T / (m4 * 1e-3), 1),
@@ -490,7 +459,7 @@ def main():
         del sets4
         w3 = gdr_synth.WORKLOADS[3]
         sets3 = make_chunk_sets(torch, gdr_synth, w3, nsets=2)
-        m3, _, _, _, _ = time_chunk(torch, gdr, sets3, 10, 2)
+        m3, _, _, _ = time_chunk(torch, gdr, sets3, 10, 2)
         f3 = chunk_flops(w3.B, w3.H, w3.T, 128, 128)
         b3 = chunk_bytes(w3.B, w3.H, w3.T, 128, 128, gate_per_channel=True)
         result["kda"] = {

@@ -11,11 +11,36 @@
 
 namespace gdr {
 
+// The chunk's triangular matrices are stored without their all-zero 32x32 block: A^T (row m
+// holds A[l][m], nonzero for l >= m) keeps rows 0..31 at full width and rows 32..63 at columns
+// 32..63; T (lower triangular) keeps rows 0..31 at columns 0..31 and rows 32..63 at full width.
+// Each is 384 pieces of 8 halfs (3072 halfs), stored in piece order.
+constexpr int kTriHalfs = 3 * kChunk * kChunk / 4;
+constexpr int kTriPieces = kTriHalfs / 8;
+__device__ __forceinline__ void at_piece(int idx, int& row, int& col) {
+    if (idx < 256) {
+        row = idx >> 3;
+        col = (idx & 7) * 8;
+    } else {
+        row = 32 + ((idx - 256) >> 2);
+        col = 32 + ((idx - 256) & 3) * 8;
+    }
+}
+__device__ __forceinline__ void t_piece(int idx, int& row, int& col) {
+    if (idx < 128) {
+        row = idx >> 2;
+        col = (idx & 3) * 8;
+    } else {
+        row = 32 + ((idx - 128) >> 3);
+        col = ((idx - 128) & 7) * 8;
+    }
+}
+
 // Workspace of the per-channel-gate two-kernel path, per (sequence, chunk), in halfs:
-// A^T [C][C], T [C][C] (columns pperm'd), K e^G [C][DK], Q e^G [C][DK], K e^{G_C - G} [C][DK]
+// A^T and T (compact, T's columns pperm'd), K e^G [C][DK], Q e^G [C][DK], K e^{G_C - G} [C][DK]
 // (fp16), then e^{G_C} [DK] (fp32, natural channel order).
 template <int DK>
-constexpr int kda_ws_stride() { return 2 * kChunk * kChunk + 3 * kChunk * DK + 2 * DK; }
+constexpr int kda_ws_stride() { return 2 * kTriHalfs + 3 * kChunk * DK + 2 * DK; }
 
 // position of logical index m inside its row under the 32-block permutation
 __device__ __forceinline__ int pperm(int m) {

@@ -548,8 +548,8 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
         if (w < 2) {
             diag_inverse();
         } else {
-            copy_scaled(Kr, HP, dst + 2 * C * C);
-            copy_scaled(Qr, HP, dst + 2 * C * C + C * DK);
+            copy_scaled(Kr, HP, dst + 2 * kTriHalfs);
+            copy_scaled(Qr, HP, dst + 2 * kTriHalfs + C * DK);
         }
         lds_barrier();
         // blocks of N^{-1} below the diagonal, column block by column block (wave 0: column
@@ -587,24 +587,24 @@ __global__ __launch_bounds__(256, 1) void chunk_kda_kernel(const KdaArgs a) {
             column(std::integral_constant<int, 1>{});
             column(std::integral_constant<int, 2>{});
         } else {
-            copy_scaled(Kc, HS, dst + 2 * C * C + 2 * C * DK);
+            copy_scaled(Kc, HS, dst + 2 * kTriHalfs + 2 * C * DK);
         }
         lds_barrier();
-        // A^T and T.  T's blocks above the diagonal are zero and are not staged: of a piece
-        // at column position col, the first four values lie in column block 2 (col / 32),
-        // the last four in the next one.
-#pragma unroll
-        for (int u = 0; u < C * C / 8 / 256; ++u) {
-            const int i = tid + 256 * u;
-            const int row = i / (C / 8), col = (i % (C / 8)) * 8;
-            *reinterpret_cast<uint4*>(dst + row * C + col) = *reinterpret_cast<const uint4*>(At + row * L::LDC + col);
+        // A^T and T without their all-zero 32x32 blocks.  T's 16x16 blocks above the diagonal
+        // are zero and are not staged: of a piece at column position col, the first four values
+        // lie in 16-block column 2 (col / 32), the last four in the next one.
+        for (int idx = tid; idx < kTriPieces; idx += 256) {
+            int ra, ca, row, col;
+            at_piece(idx, ra, ca);
+            t_piece(idx, row, col);
+            *reinterpret_cast<uint4*>(dst + idx * 8) = *reinterpret_cast<const uint4*>(At + ra * L::LDC + ca);
             uint4 t = *reinterpret_cast<const uint4*>(Tt + row * L::LDC + col);
             const int rb = row >> 4, cb = 2 * (col >> 5);
             if (cb > rb) t.x = t.y = 0u;
             if (cb + 1 > rb) t.z = t.w = 0u;
-            *reinterpret_cast<uint4*>(dst + C * C + row * C + col) = t;
+            *reinterpret_cast<uint4*>(dst + kTriHalfs + idx * 8) = t;
         }
-        if (tid < DK) reinterpret_cast<float*>(dst + 2 * C * C + 3 * C * DK)[tid] = FE[tid];
+        if (tid < DK) reinterpret_cast<float*>(dst + 2 * kTriHalfs + 3 * C * DK)[tid] = FE[tid];
         // No barrier before the next chunk: its scan and tables write nothing read here, and
         // Tt is written again only after three more barriers.
     }

@@ -22,10 +22,11 @@
 // once per chunk instead of once per value-channel tile.  The price is the workspace traffic
 // (T and A written once and read by every value-channel tile) and a second read of K and Q.
 //
-// Workspace layout, per (sequence, chunk): A^T [64][64] (row m holds A[l][m], l = 0..63), then
-// T [64][64] (row l; column m stored at position pperm(m), so one operand fragment is one
-// 16-byte read), both fp16 with zeros in the upper triangles; then the decay factors of the
-// state pass, fp32: e^{G_l} [64], e^{G_C - G_l} [64], e^{G_C}, 15 zeros (16960 bytes).
+// Workspace layout, per (sequence, chunk): A^T (row m holds A[l][m], l = 0..63), then T (row l;
+// column m stored at position pperm(m), so one operand fragment is one 16-byte read), both fp16
+// with zeros in the upper 16x16 blocks of their diagonal 32x32 blocks and their all-zero 32x32
+// block left out (3072 halfs each, see at_piece / t_piece); then the decay factors of the state
+// pass, fp32: e^{G_l} [64], e^{G_C - G_l} [64], e^{G_C}, 15 zeros (12864 bytes).
 //
 // The per-channel gate ("Kimi Delta Attention (KDA)" section of the same page) takes the same
 // state kernel in its KDA instantiation: the UT pass (chunk_kda.hip) also writes the decayed
@@ -52,12 +53,12 @@ struct UtTab {
 };
 
 // workspace record of one (sequence, chunk) of the scalar gate, in halfs: A^T, T, factors
-constexpr int kGdnWsFactors = 2 * kChunk * kChunk;        // offset of the fp32 factor table
+constexpr int kGdnWsFactors = 2 * kTriHalfs;               // offset of the fp32 factor table
 constexpr int kGdnWsNF = 144;                               // its floats
-constexpr int kGdnWsStride = kGdnWsFactors + 2 * kGdnWsNF;  // 8480 halfs = 16960 bytes
+constexpr int kGdnWsStride = kGdnWsFactors + 2 * kGdnWsNF;  // 6432 halfs = 12864 bytes
 // fused input preparation: the record also holds the chunk's normalised k and q rows (fp16,
-// [64][DK] each), so that the state pass copies them without converting (49728 bytes for
-// DK = 128, 33344 for DK = 64)
+// [64][DK] each), so that the state pass copies them without converting (45632 bytes for
+// DK = 128, 29248 for DK = 64)
 constexpr int kPrepWsK = kGdnWsStride;
 template <int DK>
 constexpr int prep_ws_stride() { return kPrepWsK + 2 * kChunk * DK; }
@@ -386,13 +387,16 @@ __global__ __launch_bounds__(128) void chunk_ut_kernel(const UtArgs a) {
     }
     lds_barrier();
 
-    // ---- A^T and T to the workspace, 16-byte pieces
+    // ---- A^T and T to the workspace, 16-byte pieces, without their all-zero 32x32 blocks
     uint16_t* dst = a.ws + (bh * a.nC + c) * WSS;
 #pragma unroll
-    for (int u = 0; u < C * C / 8 / 128; ++u) {
-        const int idx = tid + 128 * u, row = idx / (C / 8), col = (idx % (C / 8)) * 8;
-        *reinterpret_cast<uint4*>(dst + row * C + col) = *reinterpret_cast<const uint4*>(At + row * L::LDC + col);
-        *reinterpret_cast<uint4*>(dst + C * C + row * C + col) = *reinterpret_cast<const uint4*>(Tt + row * L::LDC + col);
+    for (int u = 0; u < kTriPieces / 128; ++u) {
+        const int idx = tid + 128 * u;
+        int ra, ca, rt, ct;
+        at_piece(idx, ra, ca);
+        t_piece(idx, rt, ct);
+        *reinterpret_cast<uint4*>(dst + idx * 8) = *reinterpret_cast<const uint4*>(At + ra * L::LDC + ca);
+        *reinterpret_cast<uint4*>(dst + kTriHalfs + idx * 8) = *reinterpret_cast<const uint4*>(Tt + rt * L::LDC + ct);
     }
 }
 
@@ -488,7 +492,7 @@ __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const St
     const auto rwg = make_rsrc(ZW ? a.wg + bh * T * DV : nullptr, ZW ? (uint32_t)(T * DV * 4) : 0u);
     constexpr int WS = KDA ? kda_ws_stride<DK>() : PREP ? prep_ws_stride<DK>() : kGdnWsStride;  // halfs per chunk
     // offsets (halfs) inside a chunk's workspace record of the per-channel gate
-    constexpr int WKG = 2 * C * C, WQG = WKG + C * DK, WKC = WQG + C * DK, WFE = WKC + C * DK;
+    constexpr int WKG = 2 * kTriHalfs, WQG = WKG + C * DK, WKC = WQG + C * DK, WFE = WKC + C * DK;
     const auto rw = make_rsrc(a.ws + bh * nC * WS, (uint32_t)(nC * WS * 2));
     const auto ro = make_rsrc(a.o + bh * Tr * DV, (uint32_t)(Tr * DV * 2));
     auto vtok = [&](uint32_t m) { return __umulhi(m, a.nh_magic); };
@@ -503,7 +507,7 @@ __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const St
     const int lt = tid - 64 * NCW;  // loader thread in [0, 128)
     constexpr int NPV = NCW;        // 16-byte pieces of the V tile per loader thread
     constexpr int NPK = C * DK / 8 / 128;  // K (and Q) pieces per loader thread
-    constexpr int NPW = C * C / 8 / 128;   // A^T (and T) pieces per loader thread
+    constexpr int NPW = kTriPieces / 128;  // A^T (and T) pieces per loader thread
     // (KDA: kr holds K e^G, qr K e^{G_C - G}); fr: 16-byte pieces of the factor table, the
     // first NFQ loader threads one each
     constexpr int NFQ = KDA ? DK / 4 : L::NF / 4;
@@ -540,7 +544,7 @@ __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const St
         for (int u = 0; u < NPW; ++u) {
             const int idx = lt + 128 * u;
             ar[u] = bld16(rw, (wb + idx * 8) * 2);
-            tr[u] = bld16(rw, (wb + C * C + idx * 8) * 2);
+            tr[u] = bld16(rw, (wb + kTriHalfs + idx * 8) * 2);
         }
 #pragma unroll
         for (int u = 0; u < NPV; ++u) {
@@ -595,10 +599,13 @@ __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const St
             *reinterpret_cast<uint4*>(Qb(b) + row * L::LDK + col) = qr[u];
         }
 #pragma unroll
-        for (int u = 0; u < NPW; ++u) {
-            const int idx = lt + 128 * u, row = idx / (C / 8), col = (idx % (C / 8)) * 8;
-            *reinterpret_cast<uint4*>(Ab(b) + row * L::LDC + col) = ar[u];
-            *reinterpret_cast<uint4*>(Tb(b) + row * L::LDC + col) = tr[u];
+        for (int u = 0; u < NPW; ++u) {  // the all-zero 32x32 blocks are never read: not staged
+            const int idx = lt + 128 * u;
+            int ra, ca, rt, ct;
+            at_piece(idx, ra, ca);
+            t_piece(idx, rt, ct);
+            *reinterpret_cast<uint4*>(Ab(b) + ra * L::LDC + ca) = ar[u];
+            *reinterpret_cast<uint4*>(Tb(b) + rt * L::LDC + ct) = tr[u];
         }
 #pragma unroll
         for (int u = 0; u < NPV; ++u) {

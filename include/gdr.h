@@ -92,9 +92,9 @@ const char *gdr_status_string(int status);
 /*
  * gdr_chunk_fwd_workspace_size -- bytes of device workspace gdr_chunk_fwd needs.
  *
- * Per sequence and 64-token chunk the scalar gate takes 16960 bytes
- * (B*H*ceil(T/64)*16960) and the per-channel gate 16384 + 388 d_k bytes (66048 for d_k = 128,
- * 41216 for d_k = 64).  Returns 0 for GDR_F32 I/O (one kernel, no workspace), and -1 for sizes
+ * Per sequence and 64-token chunk the scalar gate takes 12864 bytes
+ * (B*H*ceil(T/64)*12864) and the per-channel gate 12288 + 388 d_k bytes (61952 for d_k = 128,
+ * 37120 for d_k = 64).  Returns 0 for GDR_F32 I/O (one kernel, no workspace), and -1 for sizes
  * or enums gdr_chunk_fwd would reject.
  */
 int64_t gdr_chunk_fwd_workspace_size(int64_t B, int64_t H, int64_t T, int d_k, int d_v,
@@ -131,8 +131,7 @@ int64_t gdr_chunk_fwd_workspace_size(int64_t B, int64_t H, int64_t T, int d_k, i
  *
  * T may be any value in [0, 2^22] (a ragged last chunk is handled exactly; T = 0 copies
  * the initial state, or zeros, to final_state); a longer sequence returns GDR_ERR_SHAPE
- * (split it and carry the state).  The per-channel gate addresses one sequence's workspace
- * with 32-bit offsets: T above 4,161,728 (d_k = 128) returns GDR_ERR_SHAPE.
+ * (split it and carry the state).
  * B*H*T*max(d_k, d_v) must fit in int64.
  *
  * Per-channel gate: bf16 I/O only (GDR_ERR_UNSUPPORTED for GDR_F32).  Inside each 16-token
@@ -158,7 +157,7 @@ gdr_status gdr_chunk_fwd(int64_t B, int64_t H, int64_t T, int d_k, int d_v,
  * (96 MiB) on every GPU the library runs on, held from the library's load on that GPU until the
  * process ends.  The call allocates nothing (no hipMalloc, no library allocation).  A
  * configuration whose gdr_chunk_fwd_workspace_size exceeds that returns GDR_ERR_WORKSPACE
- * (the B=4, H=16, T=4096, d_k=d_v=128 scalar-gate shape needs 66.25 MiB and fits).
+ * (the B=4, H=16, T=4096, d_k=d_v=128 scalar-gate shape needs 50.25 MiB and fits).
  *
  * All calls on one GPU share that GPU's array, which keeps the last call's contents (the
  * kernels need no particular contents on entry).  Calls that overlap on one GPU -- on
@@ -175,8 +174,8 @@ gdr_status gdr_chunk_fwd_noalloc(int64_t B, int64_t H, int64_t T, int d_k, int d
 
 /*
  * gdr_chunk_fwd_fused_prep_workspace_size -- bytes of device workspace
- * gdr_chunk_fwd_fused_prep needs, per sequence and 64-token chunk, 16960 + 256 d_k bytes
- * (49728 for d_k = 128, 33344 for d_k = 64); -1 for sizes gdr_chunk_fwd_fused_prep would
+ * gdr_chunk_fwd_fused_prep needs, per sequence and 64-token chunk, 12864 + 256 d_k bytes
+ * (45632 for d_k = 128, 29248 for d_k = 64); -1 for sizes gdr_chunk_fwd_fused_prep would
  * reject.
  */
 int64_t gdr_chunk_fwd_fused_prep_workspace_size(int64_t B, int64_t H, int64_t T, int d_k, int d_v);
@@ -220,8 +219,8 @@ gdr_status gdr_chunk_fwd_fused_prep(int64_t B, int64_t H, int64_t T, int d_k, in
 
 /*
  * gdr_gdp_chunk_fwd_workspace_size -- bytes of device workspace gdr_gdp_chunk_fwd needs:
- * the scalar gate's 16960 bytes per sequence and 64 virtual steps,
- * B*H*ceil(T*n_h/64)*16960; -1 for sizes gdr_gdp_chunk_fwd would reject.
+ * the scalar gate's 12864 bytes per sequence and 64 virtual steps,
+ * B*H*ceil(T*n_h/64)*12864; -1 for sizes gdr_gdp_chunk_fwd would reject.
  */
 int64_t gdr_gdp_chunk_fwd_workspace_size(int64_t B, int64_t H, int64_t T, int n_h, int d_k, int d_v);
 
@@ -295,8 +294,7 @@ int64_t gdr_gdn2_chunk_fwd_workspace_size(int64_t B, int64_t H, int64_t T, int d
  *   workspace, workspace_bytes   as gdr_chunk_fwd
  *
  * io_dtype must be GDR_BF16 (GDR_F32 returns GDR_ERR_UNSUPPORTED).  (T + 64) * d_v <= 2^30
- * (the fp32 write gate's 32-bit offsets) and the per-channel gate's T limit, GDR_ERR_SHAPE
- * otherwise.  Sizes, the rest of the T range and every other error as for gdr_chunk_fwd.
+ * (the fp32 write gate's 32-bit offsets), GDR_ERR_SHAPE otherwise.  Sizes, the rest of the T range and every other error as for gdr_chunk_fwd.
  */
 gdr_status gdr_gdn2_chunk_fwd(int64_t B, int64_t H, int64_t T, int d_k, int d_v,
                               int io_dtype,

@@ -73,13 +73,12 @@ def decode(lib, N=1, H=1, dk=128, dv=128, io=0, gate=0, q=FAKE, k=FAKE, v=FAKE, 
     (dict(io=1, dk=64, dv=64, gate=1), UNSUP),                 # per-channel gate needs bf16 I/O
     (dict(B=1 << 40, H=1 << 30), SHAPE),                       # size overflow
     (dict(T=(1 << 22) + 1), SHAPE),                            # 32-bit per-sequence offsets
-    (dict(T=64 * 65027 + 1, dv=32, gate=1), SHAPE),            # channel-gate workspace of a sequence >= 4 GiB
     (dict(ws=None), WSERR),                                    # a workspace is required
-    (dict(nbytes=16959), WSERR),                               # one chunk needs 16960 bytes
+    (dict(nbytes=12863), WSERR),                               # one chunk needs 12864 bytes
     (dict(nbytes=-1), WSERR),
     (dict(ws=FAKE), WSERR),                                    # workspace overlaps q
     (dict(ws=FAKE2), WSERR),                                   # workspace overlaps o
-    (dict(gate=1, nbytes=66047), WSERR),                       # channel gate: 66048 bytes per chunk
+    (dict(gate=1, nbytes=61951), WSERR),                       # channel gate: 61952 bytes per chunk
 ])
 def test_chunk_fwd_rejects(lib, kw, status):
     assert chunk(lib, **kw) == status
@@ -115,7 +114,7 @@ def noalloc(lib, B=1, H=1, T=64, dk=128, dv=128, io=0, gate=0, q=FAKE, k=FAKE, v
     (dict(B=-1), INVALID), (dict(dk=96), SHAPE), (dict(io=2), DTYPE), (dict(q=None), INVALID),
     (dict(o=FAKE), INVALID), (dict(io=1, dk=128), UNSUP), (dict(T=(1 << 22) + 1), SHAPE),
     (dict(B=8, H=16, T=4096), WSERR),                          # 132.5 MiB of records: beyond the 96 MiB built in
-    (dict(B=1, H=16, T=8192, gate=1), WSERR),                  # channel gate: 16 x 128 x 66048 bytes
+    (dict(B=1, H=16, T=8192, gate=1), WSERR),                  # channel gate: 16 x 128 x 61952 bytes
 ])
 def test_chunk_fwd_noalloc_rejects(lib, kw, status):
     assert noalloc(lib, **kw) == status
@@ -133,18 +132,17 @@ def test_chunk_fwd_noalloc_limit(lib):
 
 def test_workspace_size(lib):
     n = lib.gdr_chunk_fwd_workspace_size
-    assert n(4, 16, 4096, 128, 128, 0, 0) == 64 * 64 * 16960        # A^T, T, factors per (sequence, chunk)
-    assert n(1, 1, 65, 64, 32, 0, 0) == 2 * 16960                    # ragged tail counts as a chunk
+    assert n(4, 16, 4096, 128, 128, 0, 0) == 64 * 64 * 12864        # A^T, T, factors per (sequence, chunk)
+    assert n(1, 1, 65, 64, 32, 0, 0) == 2 * 12864                    # ragged tail counts as a chunk
     assert n(1, 1, 0, 128, 128, 0, 0) == 0
     assert n(2, 2, 100, 64, 64, 1, 0) == 0                           # fp32 I/O: one kernel, no workspace
     assert n(2, 2, 100, 128, 64, 1, 0) == -1                         # fp32 I/O is d_k = 64 only
-    assert n(2, 2, 100, 128, 128, 0, 1) == 4 * 2 * 66048             # channel gate: 16384 + 388 d_k
-    assert n(1, 3, 64, 64, 64, 0, 1) == 3 * 41216
-    assert n(1, 1, 64 * 65027, 128, 32, 0, 1) == 65027 * 66048       # one sequence just below 4 GiB
-    assert n(1, 1, 64 * 65027 + 1, 128, 32, 0, 1) == -1              # beyond: rejected
+    assert n(2, 2, 100, 128, 128, 0, 1) == 4 * 2 * 61952             # channel gate: 12288 + 388 d_k
+    assert n(1, 3, 64, 64, 64, 0, 1) == 3 * 37120
+    assert n(1, 1, 1 << 22, 128, 32, 0, 1) == 65536 * 61952          # longest sequence: below 4 GiB
     assert n(1, 1, 64, 96, 128, 0, 0) == -1 and n(-1, 1, 64, 128, 128, 0, 0) == -1
     assert n(1, 1, (1 << 22) + 1, 128, 128, 0, 0) == -1
-    assert gdr.chunk_fwd_workspace_size(1, 2, 128, 128, 128) == 2 * 2 * 16960
+    assert gdr.chunk_fwd_workspace_size(1, 2, 128, 128, 128) == 2 * 2 * 12864
 
 
 def gdp(lib, B=1, H=1, T=64, nh=2, dk=128, dv=128, io=0, q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE,
@@ -163,7 +161,7 @@ def gdp(lib, B=1, H=1, T=64, nh=2, dk=128, dv=128, io=0, q=FAKE, k=FAKE, v=FAKE,
     (dict(T=(1 << 22) + 1, nh=1), SHAPE),
     (dict(B=1 << 40, H=1 << 30), SHAPE),                        # size overflow
     (dict(ws=None), WSERR),                                     # a workspace is required
-    (dict(nbytes=2 * 16960 - 1), WSERR),                        # 128 virtual steps: two records
+    (dict(nbytes=2 * 12864 - 1), WSERR),                        # 128 virtual steps: two records
     (dict(nbytes=-1), WSERR),
     (dict(ws=FAKE), WSERR), (dict(ws=FAKE2), WSERR),            # workspace overlaps q / o
 ])
@@ -178,8 +176,8 @@ def test_gdp_chunk_fwd_empty_batch_is_a_noop(lib):
 
 def test_gdp_workspace_size(lib):
     n = lib.gdr_gdp_chunk_fwd_workspace_size
-    assert n(4, 16, 2048, 2, 128, 128) == 64 * 64 * 16960
-    assert n(1, 1, 33, 2, 64, 64) == 2 * 16960                      # 66 virtual steps: two chunks
+    assert n(4, 16, 2048, 2, 128, 128) == 64 * 64 * 12864
+    assert n(1, 1, 33, 2, 64, 64) == 2 * 12864                      # 66 virtual steps: two chunks
     assert n(1, 1, 0, 2, 128, 128) == 0
     assert n(1, 1, 64, 0, 128, 128) == -1 and n(1, 1, 64, 17, 128, 128) == -1
 
@@ -204,7 +202,7 @@ def gdn2(lib, B=1, H=1, T=64, dk=128, dv=128, io=0, q=FAKE, k=FAKE, v=FAKE, g=FA
     (dict(T=1 << 22, dv=256), SHAPE),                           # fp32 write gate past 32-bit offsets
     (dict(B=1 << 40, H=1 << 30), SHAPE),
     (dict(ws=None), WSERR),                                     # a workspace is required
-    (dict(nbytes=66047), WSERR),                                # one chunk needs 66048 bytes
+    (dict(nbytes=61951), WSERR),                                # one chunk needs 61952 bytes
     (dict(nbytes=-1), WSERR),
     (dict(ws=FAKE), WSERR), (dict(ws=FAKE2), WSERR),            # workspace overlaps q / o
 ])
@@ -219,11 +217,11 @@ def test_gdn2_chunk_fwd_empty_batch_is_a_noop(lib):
 
 def test_gdn2_workspace_size(lib):
     n = lib.gdr_gdn2_chunk_fwd_workspace_size
-    assert n(2, 2, 100, 128, 128) == 4 * 2 * 66048
-    assert n(1, 3, 64, 64, 64) == 3 * 41216
+    assert n(2, 2, 100, 128, 128) == 4 * 2 * 61952
+    assert n(1, 3, 64, 64, 64) == 3 * 37120
     assert n(1, 1, 0, 128, 128) == 0
     assert n(-1, 1, 64, 128, 128) == -1 and n(1, 1, 64, 96, 128) == -1
-    assert n(1, 1, 64 * 65027 + 1, 128, 32) == -1                    # beyond 4 GiB a sequence: rejected
+    assert n(1, 1, 1 << 22, 128, 32) == 65536 * 61952                # longest sequence: below 4 GiB
 
 
 def prep(lib, B=1, H=1, T=64, dk=128, dv=128, io=0, q=FAKE, k=FAKE, v=FAKE, dt=FAKE, A=FAKE, bias=FAKE,
@@ -240,7 +238,7 @@ def prep(lib, B=1, H=1, T=64, dk=128, dv=128, io=0, q=FAKE, k=FAKE, v=FAKE, dt=F
     (dict(T=(1 << 22) + 1), SHAPE),
     (dict(B=1 << 40, H=1 << 30), SHAPE),
     (dict(ws=None), WSERR),                                     # a workspace is required
-    (dict(nbytes=49727), WSERR),                                # one chunk needs 49728 bytes
+    (dict(nbytes=45631), WSERR),                                # one chunk needs 45632 bytes
     (dict(nbytes=-1), WSERR),
     (dict(ws=FAKE), WSERR), (dict(ws=FAKE2), WSERR),            # workspace overlaps q_raw / o
 ])
@@ -250,8 +248,8 @@ def test_fused_prep_rejects(lib, kw, status):
 
 def test_fused_prep_workspace_size(lib):
     n = lib.gdr_chunk_fwd_fused_prep_workspace_size
-    assert n(4, 16, 4096, 128, 128) == 64 * 64 * 49728
-    assert n(1, 2, 65, 64, 64) == 2 * 2 * 33344
+    assert n(4, 16, 4096, 128, 128) == 64 * 64 * 45632
+    assert n(1, 2, 65, 64, 64) == 2 * 2 * 29248
     assert n(1, 1, 0, 128, 128) == 0
     assert n(-1, 1, 64, 128, 128) == -1 and n(1, 1, 64, 96, 128) == -1
 

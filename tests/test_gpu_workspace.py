@@ -14,8 +14,11 @@ directly, chunk by chunk, including a ragged last chunk:
   Gated Delta Product: the scalar-gate records over the virtual sequence of substeps.
 
 Record layout per (sequence, chunk), fp16 unless noted (C = 64):
-  A^T [C][C] (row m holds A[l][m]);
-  T [C][C], column m of each row stored at position pperm(m) inside its 32-column block;
+  A^T (row m holds A[l][m]) without its all-zero 32x32 block (rows 32.., columns ..31): rows
+    0..31 at full width, then rows 32..63 at columns 32..63, in 8-half pieces (3072 halfs);
+  T, column m of each row stored at position pperm(m) inside its 32-column block, without its
+    all-zero block (rows ..31, columns 32..): rows 0..31 at columns 0..31, then rows 32..63
+    at full width (3072 halfs);
   scalar gate: fp32 e^{G_l} [C], e^{G_C - G_l} [C], e^{G_C}, 15 zeros;
   per-channel gate: K e^G, Q e^G, K e^{G_C - G} [C][d_k] each, then fp32 e^{G_C} [d_k].
 Tokens past the end of a sequence enter the kernels as identity tokens (k = q = 0, g = 0,
@@ -91,12 +94,30 @@ def _f32(raw, byte_off, n):
     return raw[byte_off:byte_off + 4 * n].view(np.float32).astype(np.float64)
 
 
+TRI = 3 * C * C // 4          # halfs of one compact triangular matrix
+FACTORS = 4 * TRI              # byte offset of the fp32 factor table (and of the KDA copies)
+GDN_RECORD = FACTORS + 4 * 144  # bytes of the scalar gate's record
+
+
+def _expand(flat, upper_zero):
+    """A compact triangular matrix back to C x C, its left-out 32x32 block zero.  upper_zero:
+    the block left out is rows 0..31 x columns 32..63 (T), else rows 32..63 x columns 0..31 (A^T)."""
+    M = np.zeros((C, C))
+    if upper_zero:
+        M[:32, :32] = flat[:1024].reshape(32, 32)
+        M[32:, :] = flat[1024:].reshape(32, 64)
+    else:
+        M[:32, :] = flat[:2048].reshape(32, 64)
+        M[32:, 32:] = flat[2048:].reshape(32, 32)
+    return M
+
+
 def _check_at_t(rec, base, A_ref, T_ref, Cr, label, pad_diag=0.0):
     """A and T of one record against the oracle's leading Cr x Cr blocks.  Past the end of the
     sequence T holds pad_diag on its diagonal and zeros elsewhere: 0 where T carries diag(beta)
     (beta = 0 there), 1 for Gated DeltaNet-2's T = N^{-1}."""
-    At = _f16(rec, base, C * C).reshape(C, C)
-    Tp = _f16(rec, base + 2 * C * C, C * C).reshape(C, C)
+    At = _expand(_f16(rec, base, TRI), upper_zero=False)
+    Tp = _expand(_f16(rec, base + 2 * TRI, TRI), upper_zero=True)
     A = At.T
     Tm = Tp[:, PPERM]  # logical column m from its stored position
     eA = _rel(A[:Cr, :Cr], A_ref)
@@ -127,7 +148,7 @@ def test_ut_records_scalar_gate(T, dk):
             base = (h * nC + c) * stride
             label = f"scalar d_k={dk} T={T} head {h} chunk {c}"
             _check_at_t(raw, base, A_ref, tr["T"], Cr, label)
-            f = _f32(raw, base + 4 * C * C, 144)
+            f = _f32(raw, base + FACTORS, 144)
             lam = tr["lam"]
             eg = np.array([lam(1, l) for l in range(1, Cr + 1)])
             er = np.array([lam(l + 1, Cr) for l in range(1, Cr + 1)])
@@ -157,7 +178,7 @@ def test_ut_records_channel_gate(T, dk):
             base = (h * nC + c) * stride
             label = f"channel d_k={dk} T={T} head {h} chunk {c}"
             _check_at_t(raw, base, A_ref, tr["T"], Cr, label)
-            off = base + 4 * C * C
+            off = base + FACTORS
             copies = {"K e^G": tr["K_left"], "Q e^G": Q_left, "K e^(G_C-G)": tr["K_right"]}
             for i, (name, ref) in enumerate(copies.items()):
                 got = _f16(raw, off + i * 2 * C * dk, C * dk).reshape(C, dk)
@@ -174,7 +195,7 @@ def test_ut_records_channel_gate(T, dk):
 def test_ut_records_fused_prep(T, dk):
     """UT pass with the fused input preparation: A, T and the factors of the prepared inputs,
     and the unit-norm fp16 rows of k and q that the record carries after the factor table
-    (at byte 16960: k [C][d_k], then q)."""
+    (after the scalar-gate record: k [C][d_k], then q)."""
     w = dataclasses.replace(gdr_synth.WORKLOADS[2], d_k=dk, d_v=dk)
     r = gdr_synth.make_raw_inputs(w, B=1, H=2, T=T, head_params="varied")
     nbytes = gdr.chunk_fwd_fused_prep_workspace_size(1, 2, T, dk, dk)
@@ -197,10 +218,10 @@ def test_ut_records_fused_prep(T, dk):
             base = (h * nC + c) * stride
             label = f"prep d_k={dk} T={T} head {h} chunk {c}"
             _check_at_t(raw, base, A_ref, tr["T"], Cr, label)
-            f = _f32(raw, base + 4 * C * C, 144)
+            f = _f32(raw, base + FACTORS, 144)
             assert abs(f[128] - float(tr["lam_C"])) / float(tr["lam_C"]) < TOL_F32, label
             for i, (name, ref) in enumerate((("k", K), ("q", Q))):
-                got = _f16(raw, base + 16960 + i * 2 * C * dk, C * dk).reshape(C, dk)
+                got = _f16(raw, base + GDN_RECORD + i * 2 * C * dk, C * dk).reshape(C, dk)
                 e = _rel(got[:Cr], ref)
                 print(f"{label}: e[{name}] {e:.2e}")
                 assert e < TOL_F16, (label, name)
@@ -234,7 +255,7 @@ def test_ut_records_gdn2(T, dk):
             base = (h * nC + c) * stride
             label = f"gdn2 d_k={dk} T={T} head {h} chunk {c}"
             _check_at_t(raw, base, A_ref, tr["T_inv"], Cr, label, pad_diag=1.0)
-            off = base + 4 * C * C
+            off = base + FACTORS
             copies = {"E e^G": tr["E_left"], "Q e^G": Q_left, "K e^(G_C-G)": tr["K_right"]}
             for i, (name, ref) in enumerate(copies.items()):
                 got = _f16(raw, off + i * 2 * C * dk, C * dk).reshape(C, dk)
@@ -275,7 +296,7 @@ def test_ut_records_gdp(T, nh):
             base = (h * nC + c) * stride
             label = f"gdp n_h={nh} T={T} head {h} chunk {c}"
             _check_at_t(raw, base, A_ref, tr["T"], Cr, label)
-            f = _f32(raw, base + 4 * C * C, 144)
+            f = _f32(raw, base + FACTORS, 144)
             lam = tr["lam"]
             assert _rel(f[:Cr], np.array([lam(1, l) for l in range(1, Cr + 1)])) < TOL_F32, label
             assert _rel(f[64:64 + Cr], np.array([lam(l + 1, Cr) for l in range(1, Cr + 1)])) < TOL_F32, label
