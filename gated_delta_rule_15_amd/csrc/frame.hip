@@ -48,6 +48,7 @@ struct FrArgs {
     uint16_t* Wl;
     float* Cw;
     uint16_t* Sw;
+    int* Ew;         // per (sequence, frame, 16 value channels): the power of two Sw is scaled by
 };
 
 // ============================================================================ Gram + inverse
@@ -341,7 +342,7 @@ struct FrStateLds {
     static constexpr int total = oWl + DK * LDW * 2;
 };
 
-template <int DK, int DV, int NWV>
+template <int DK, int DV, int NWV, bool CH>
 __global__ __launch_bounds__(64 * NWV, 1) void frame_state_kernel(const FrArgs a) {
     using L = FrStateLds<DK>;
     constexpr int NKB = DK / 32, NST = DK / 16;
@@ -378,23 +379,20 @@ __global__ __launch_bounds__(64 * NWV, 1) void frame_state_kernel(const FrArgs a
         wpl[u] = bld16(rwl, (uint32_t)((tid + NTH * u) * 16));
     }
     // C and the frame gate of the next frame, prefetched the same way (buffer loads, no branch:
-    // past the last frame they read zeros, which are never used)
-    const int gstride = a.channel ? DK : 1;
+    // past the last frame they read zeros, which are never used).  The scalar gate is one dword
+    // per frame.
+    constexpr int gstride = CH ? DK : 1;
     const auto rc = make_rsrc(a.Cw + bh * F * (int64_t)(DV * DK), (uint32_t)(F * DV * DK * 4));
     const auto rgf = make_rsrc(a.g + bh * F * gstride, (uint32_t)(F * gstride * 4));
-    float4v cn[NST], gn[NST];
+    float4v cn[NST], gn[CH ? NST : 1];
     auto load_cg = [&](int64_t fl) {
 #pragma unroll
         for (int t = 0; t < NST; ++t) {
             const int ch = pperm(16 * t + 4 * g);
             cn[t] = __builtin_bit_cast(float4v, bld16(rc, (uint32_t)(((fl * DV + dvc + j) * DK + ch) * 4)));
-            // scalar gate: element 0 of the 16 bytes at the frame's value.  At the last frame
-            // the other three dwords lie past the buffer's end; a buffer load checks each dword
-            // against the range on its own, so element 0 is still read (the scalar-gate cases
-            // of the frame tests end every sequence on such a load).  Two loads with a select,
-            // to keep every load inside the range, cost 19 us on the frame workload.
-            gn[t] = __builtin_bit_cast(float4v, bld16(rgf, (uint32_t)((fl * gstride + (a.channel ? ch : 0)) * 4)));
+            if constexpr (CH) gn[t] = __builtin_bit_cast(float4v, bld16(rgf, (uint32_t)((fl * DK + ch) * 4)));
         }
+        if constexpr (!CH) gn[0][0] = bld4(rgf, (uint32_t)(fl * 4));
     };
     load_cg(0);
     for (int64_t f = 0; f < F; ++f) {
@@ -405,9 +403,22 @@ __global__ __launch_bounds__(64 * NWV, 1) void frame_state_kernel(const FrArgs a
         for (int t = 0; t < NST; ++t) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float d = fast_exp(a.channel ? gn[t][r] : gn[t][0]);
+                const float d = fast_exp(CH ? gn[t][r] : gn[0][0]);
                 rh[t][r] = fmaf(d, St[t][r], cn[t][r]);
             }
+        }
+        // rhs is split into fp16 halves below; a power of two per wave brings its largest
+        // magnitude near 2^12 first (C grows with the writing strength and the frame length
+        // even when the state does not), and the product is scaled back after it
+        int rexp = 0;
+        {
+            const float M = wave_max_abs(max_abs(rh));
+            if (M > 0.0f && M <= 3.0e38f) rexp = min(max(12 - __builtin_amdgcn_frexp_expf(M), -100), 100);
+            const float sc = __builtin_ldexpf(1.0f, rexp);
+#pragma unroll
+            for (int t = 0; t < NST; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) rh[t][r] *= sc;
         }
         load_cg(f + 1);
         // W of this frame into LDS (the previous frame's readers are past the barrier below)
@@ -450,14 +461,25 @@ __global__ __launch_bounds__(64 * NWV, 1) void frame_state_kernel(const FrArgs a
                 mma16(acc, ah, bl8[kb]);
                 mma16(acc, al, bh8[kb]);
             }
-            St[t] = acc;
-        }
-        // S_t in fp16, [value channel][key channel], for the outputs
-        uint16_t* sd = a.Sw + fi * (int64_t)(DV * DK) + (int64_t)(dvc + j) * DK;
+            const float isc = __builtin_ldexpf(1.0f, -rexp);
 #pragma unroll
-        for (int t = 0; t < NST; ++t) {
-            const half4 h = half4{(_Float16)St[t][0], (_Float16)St[t][1], (_Float16)St[t][2], (_Float16)St[t][3]};
-            *reinterpret_cast<half4*>(sd + pperm(16 * t + 4 * g)) = h;
+            for (int r = 0; r < 4; ++r) St[t][r] = acc[r] * isc;
+        }
+        // S_t in fp16, [value channel][key channel], for the outputs, times a power of two per
+        // wave that brings its largest magnitude near 2^12 (stored beside it for the outputs)
+        {
+            const float M = wave_max_abs(max_abs(St));
+            int sexp = 0;
+            if (M > 0.0f && M <= 3.0e38f) sexp = min(max(12 - __builtin_amdgcn_frexp_expf(M), -100), 100);
+            const float sc = __builtin_ldexpf(1.0f, sexp);
+            uint16_t* sd = a.Sw + fi * (int64_t)(DV * DK) + (int64_t)(dvc + j) * DK;
+#pragma unroll
+            for (int t = 0; t < NST; ++t) {
+                const half4 h = half4{(_Float16)(St[t][0] * sc), (_Float16)(St[t][1] * sc), (_Float16)(St[t][2] * sc),
+                                      (_Float16)(St[t][3] * sc)};
+                *reinterpret_cast<half4*>(sd + pperm(16 * t + 4 * g)) = h;
+            }
+            if (l == 0) a.Ew[fi * (DV / 16) + dvc / 16] = sexp;
         }
         lds_barrier();
     }
@@ -493,6 +515,7 @@ __global__ __launch_bounds__(256) void frame_out_kernel(const FrArgs a, int64_t 
     const auto rq = make_rsrc(a.q + bh * T * DK, (uint32_t)(T * DK * 2));
     const auto ro = make_rsrc(a.o + bh * T * DV, (uint32_t)(T * DV * 2));
     half8 sf[NV][NKB];
+    float osc[NV];  // 2^-exponent of each 16-channel group of the frame's state copy
     int64_t fcur = -1;
     for (int gi = 0; gi < NG; ++gi) {
         const int64_t tb = blk * 512 + 128 * w + 16 * gi;  // this step's 16 tokens, all in one frame
@@ -501,10 +524,12 @@ __global__ __launch_bounds__(256) void frame_out_kernel(const FrArgs a, int64_t 
         if (f != fcur) {
             const uint16_t* S = a.Sw + (bh * a.F + f) * (int64_t)(DV * DK);
 #pragma unroll
-            for (int vi = 0; vi < NV; ++vi)
+            for (int vi = 0; vi < NV; ++vi) {
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb)
                     sf[vi][kb] = *reinterpret_cast<const half8*>(S + (16 * vi + j) * DK + 32 * kb + 8 * g);
+                osc[vi] = __builtin_ldexpf(1.0f, -a.Ew[(bh * a.F + f) * NV + vi]);
+            }
             fcur = f;
         }
         half8 qa[NKB];
@@ -518,7 +543,7 @@ __global__ __launch_bounds__(256) void frame_out_kernel(const FrArgs a, int64_t 
             for (int kb = 0; kb < NKB; ++kb) mma16(acc, qa[kb], sf[vi][kb]);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const uint32_t b2 = pack_bf16x2(acc[r], 0.0f);
+                const uint32_t b2 = pack_bf16x2(acc[r] * osc[vi], 0.0f);
                 Ot[(16 * w + 4 * g + r) * L::LDO + 16 * vi + j] = (uint16_t)(b2 & 0xffffu);
             }
         }
@@ -539,7 +564,7 @@ __global__ __launch_bounds__(256) void frame_out_kernel(const FrArgs a, int64_t 
 
 int64_t frame_workspace_bytes(int64_t BH, int64_t T, int n, int dk, int dv) {
     const int64_t F = (T + n - 1) / n;
-    return BH * F * ((int64_t)dk * dk * 2 * 2 + (int64_t)dv * dk * 4 + (int64_t)dv * dk * 2);
+    return BH * F * ((int64_t)dk * dk * 2 * 2 + (int64_t)dv * dk * 4 + (int64_t)dv * dk * 2 + (int64_t)dv / 16 * 4);
 }
 
 template <int DK, int DV>
@@ -553,9 +578,12 @@ static hipError_t launch_frame(const FrArgs& a, int64_t BH, hipStream_t st) {
         hipLaunchKernelGGL((frame_gram_kernel<DK, DV>), dim3((unsigned)(BH * a.F)), dim3(256), lds_gram, st, a);
     }
     constexpr int kStateWaves = 2;  // value-channel tiles of 32: more groups, each reading W once
-    hipLaunchKernelGGL((frame_state_kernel<DK, DV, kStateWaves>), dim3((unsigned)(BH * (DV / (16 * kStateWaves)))),
-                       dim3(64 * kStateWaves), lds_state, st,
-                       a);
+    if (a.channel)
+        hipLaunchKernelGGL((frame_state_kernel<DK, DV, kStateWaves, true>), dim3((unsigned)(BH * (DV / (16 * kStateWaves)))),
+                           dim3(64 * kStateWaves), lds_state, st, a);
+    else
+        hipLaunchKernelGGL((frame_state_kernel<DK, DV, kStateWaves, false>),
+                           dim3((unsigned)(BH * (DV / (16 * kStateWaves)))), dim3(64 * kStateWaves), lds_state, st, a);
     const int64_t nblk = (a.T + 511) / 512;
     if (nblk > 0) {
         hipLaunchKernelGGL((frame_out_kernel<DK, DV>), dim3((unsigned)(BH * nblk)), dim3(256), lds_out, st, a,
@@ -586,6 +614,7 @@ hipError_t frame_dispatch(int64_t BH, int64_t T, int n, int dk, int dv, bool cha
     a.Wl = reinterpret_cast<uint16_t*>(base + nf * (int64_t)dk * dk * 2);
     a.Cw = reinterpret_cast<float*>(base + nf * (int64_t)dk * dk * 4);
     a.Sw = reinterpret_cast<uint16_t*>(base + nf * ((int64_t)dk * dk * 4 + (int64_t)dv * dk * 4));
+    a.Ew = reinterpret_cast<int*>(base + nf * ((int64_t)dk * dk * 4 + (int64_t)dv * dk * 6));
     if (dk == 128 && dv == 128) return launch_frame<128, 128>(a, BH, st);
     if (dk == 128 && dv == 64) return launch_frame<128, 64>(a, BH, st);
     if (dk == 64 && dv == 128) return launch_frame<64, 128>(a, BH, st);

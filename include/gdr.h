@@ -326,7 +326,8 @@ gdr_status gdr_gdn2_chunk_fwd(int64_t B, int64_t H, int64_t T, int d_k, int d_v,
  *   initial_state, o, final_state   as gdr_chunk_fwd
  *   workspace      device buffer of at least gdr_frame_fwd_workspace_size(...) bytes (per
  *                  sequence and frame: (I + G)^{-1} as two fp16 matrices, C in fp32 and the
- *                  frame's state in fp16), owned by the caller, overlapping nothing else
+ *                  frame's state in fp16 with one power-of-two exponent per 16 value channels),
+ *                  owned by the caller, overlapping nothing else
  *
  * Supported: bf16 I/O, d_k and d_v in {64, 128} (GDR_ERR_UNSUPPORTED otherwise); frame_len a
  * positive multiple of 16 and (ceil(T / frame_len) + 1) * d_v * d_k * 4 < 2^32 (the state
@@ -334,8 +335,11 @@ gdr_status gdr_gdn2_chunk_fwd(int64_t B, int64_t H, int64_t T, int d_k, int d_v,
  * otherwise); T in [0, 2^22].  A NULL, short or overlapping workspace returns
  * GDR_ERR_WORKSPACE.  Numerics: G and C from fp16 MFMA operands
  * sqrt(gamma) k, sqrt(gamma) v with fp32 accumulation; (I + G)^{-1} by Gauss-Jordan
- * elimination in fp32; the state chained in fp32 with split-fp16 products; o from an fp16
- * copy of each frame's state, rounded to bf16.
+ * elimination in fp32; the state chained in fp32 with split-fp16 products, the right-hand
+ * side D S + C scaled by a power of two per frame before its fp16 split; o from an fp16 copy
+ * of each frame's state (scaled by a power of two per frame and 16 value channels), rounded
+ * to bf16.  G and C must stay inside fp32's range, and sqrt(gamma) |k|, sqrt(gamma) |v| below
+ * 65504.
  */
 int64_t gdr_frame_fwd_workspace_size(int64_t B, int64_t H, int64_t T, int frame_len, int d_k,
                                      int d_v);

@@ -280,7 +280,7 @@ def test_frame_fwd_rejects(lib, kw, status):
 
 def test_frame_workspace_size(lib):
     n = lib.gdr_frame_fwd_workspace_size
-    per = 128 * 128 * 4 + 128 * 128 * 4 + 128 * 128 * 2             # W hi+lo, C, S per frame
+    per = 128 * 128 * 4 + 128 * 128 * 4 + 128 * 128 * 2 + 8 * 4     # W hi+lo, C, S, S's exponents per frame
     assert n(1, 2, 1000, 256, 128, 128) == 2 * 4 * per
     assert n(1, 1, 0, 16, 64, 64) == 0
     assert n(1, 1, 64, 24, 128, 128) == -1 and n(1, 1, 64, 16, 128, 32) == -1

@@ -118,3 +118,29 @@ def test_frame_deterministic():
     o1, S1 = run(x, 48)
     o2, S2 = run(x, 48)
     assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+@pytest.mark.parametrize("vscale", [50.0, 2.0 ** 10, 2.0 ** -14])
+def test_frame_repeated_keys_strong_writes(vscale):
+    """A static scene (the video delta-rule post, "A Different Route"): every frame repeats four
+    (key, value) pairs, with writing strengths x30.  C = V^T Gamma K then grows with the frame
+    length (about 1024 x 3.75 x |v| here) while the state stays near the values; v and S0 are
+    also scaled by 2^10 and 2^-14, which the result must follow exactly (linearity).  The
+    largest sqrt(gamma) |v| stays below fp16's 65504, the documented limit of the Gram kernel's
+    operands."""
+    n, T = 1024, 3072
+    x = gdr_synth.make_frame_inputs(B=1, H=2, T=T, frame_len=n, channel=True, s0_std=0.05, salt=7)
+    rng = np.random.default_rng(11)
+    keys = rng.standard_normal((1, 2, 4, 128)).astype(np.float32)
+    keys /= np.linalg.norm(keys, axis=-1, keepdims=True)
+    vals = rng.standard_normal((1, 2, 4, 128)).astype(np.float32)
+    pick = rng.integers(0, 4, size=T)
+    x["k"] = gdr_synth.round_to_bf16(keys[:, :, pick] + 0.01 * rng.standard_normal((1, 2, T, 128)).astype(np.float32))
+    x["v"] = gdr_synth.round_to_bf16((vals[:, :, pick] + 0.1 * rng.standard_normal((1, 2, T, 128))).astype(np.float32)
+                                     * np.float32(vscale))
+    x["gamma"] = (x["gamma"] * np.float32(30.0)).astype(np.float32)
+    x["S0"] = (x["S0"] * np.float32(vscale)).astype(np.float32)
+    o, S = run(x, n)
+    o_ref, S_ref = frame_forward(x["q"], x["k"], x["v"], x["gamma"], x["g"], n, x["S0"])
+    assert torch.isfinite(o.float()).all() and torch.isfinite(S).all()
+    check(f"frame, repeated keys, gamma x30, v x {vscale:g}", o, S, o_ref, S_ref)
