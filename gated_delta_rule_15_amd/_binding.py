@@ -16,7 +16,8 @@ import os
 import threading
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIBRARY_PATH = os.path.join(_PKG, "libgdr.so")
+# GDR_LIBRARY names another build of the library (the host-sanitizer test loads one this way)
+LIBRARY_PATH = os.environ.get("GDR_LIBRARY") or os.path.join(_PKG, "libgdr.so")
 
 GDR_OK = 0
 GDR_ERR_INVALID_ARG = 1

@@ -44,7 +44,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "gdr_oracle.c")
-_LIB = os.path.join(_HERE, "libgdr_oracle.so")
+# GDR_ORACLE_LIBRARY names another build of the same source (the host-sanitizer test loads an
+# AddressSanitizer / UndefinedBehaviorSanitizer build this way); it is used as it is.
+_LIB = os.environ.get("GDR_ORACLE_LIBRARY") or os.path.join(_HERE, "libgdr_oracle.so")
 _lock = threading.Lock()
 _lib = None
 
@@ -66,7 +68,8 @@ def _load():
     global _lib
     with _lock:
         if _lib is None:
-            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            if "GDR_ORACLE_LIBRARY" not in os.environ and (
+                    not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC)):
                 build(force=True)
             lib = ctypes.CDLL(_LIB)
             P = ctypes.c_void_p
