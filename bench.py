@@ -119,7 +119,8 @@ def time_chunk(torch, gdr, sets, steps, warmup, fn=None):
     """Launch durations of chunk_fwd (or ``fn``, same signature), alternating input sets: HIP
     events on the launch stream around the ``steps`` calls, enqueued back to back (an event
     pair around every call would add its own packets between the calls); returns the mean per
-    call, the wall clock of the region, and the last outputs."""
+    call, the wall clock of the region, and the outputs of input set 0 (every call on set 0
+    writes the same buffers)."""
     outs = [torch.empty(s["o_shape"], dtype=torch.bfloat16, device="cuda") for s in sets]
     fin = [torch.empty(s["S_shape"], dtype=torch.float32, device="cuda") for s in sets]
     if fn is None:  # the chunked forward with a workspace allocated once, outside the timing
@@ -146,7 +147,7 @@ def time_chunk(torch, gdr, sets, steps, warmup, fn=None):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = e0.elapsed_time(e1) / steps
-    return float(ms), wall, outs[(steps - 1) % len(sets)], fin[(steps - 1) % len(sets)]
+    return float(ms), wall, outs[0], fin[0]
 
 
 def make_chunk_sets(torch, gdr_synth, w, nsets=2):
@@ -476,7 +477,19 @@ def main():
         result["frame"] = bench_frame(torch, gdr, gdr_synth)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(w, sets[0]["host"])
+    mark_parity(result)
     print(json.dumps(result))
+
+
+def mark_parity(d):
+    """Adds "within_bar" to every sampled-parity record: both errors within the 2e-2 bar that
+    the GPU parity tests apply to bf16 outputs and fp32 states."""
+    for v in d.values():
+        if isinstance(v, dict):
+            if "e_o" in v and "e_S" in v:
+                v["within_bar"] = bool(v["e_o"] <= 2e-2 and v["e_S"] <= 2e-2)
+            else:
+                mark_parity(v)
 
 
 if __name__ == "__main__":

@@ -12,7 +12,7 @@
 //                       the Gram tiles of K K^T and Q K^T, the four 16x16 diagonal blocks of
 //                       N^{-1} by fp32 forward substitution, the blocks below the diagonal by
 //                       16x16 MFMA products (M_bc = -X_bb sum_{c<=d<b} N_bd M_dc), and T and A
-//                       written to a workspace as fp16 (16 KiB per chunk and sequence);
+//                       written to a workspace as fp16 (12 KiB per chunk and sequence);
 //   chunk_state_kernel  one workgroup per (sequence, 32 value channels), chunks in order:
 //                       R = V - diag(e^G) K S^T,  Z = T R,  O = diag(e^G) Q S^T + A Z,
 //                       S^T <- e^{G_C} S^T + K^T diag(e^{G_C - G}) Z.
@@ -45,7 +45,7 @@
 
 namespace gdr {
 
-// per-chunk factor table of the UT kernel (floats), as the single-kernel path:
+// per-chunk factor table of the UT kernel (floats):
 //   [0,64) G   [192,256) beta   [272,336) cf[m] = e^{Gend(blk(m)) - G_m}
 //   [336,528) rf[b][l] = e^{G_l - Gend(b)}   [528,720) rb[b][l] = beta_l rf[b][l]
 struct UtTab {
