@@ -972,7 +972,7 @@ static hipError_t launch_split(const UtArgs& u, const StArgs& s, int64_t BH, hip
     return launch_state<DK, UM == kUtVirt ? kStGdp : UM == kUtPrep ? kStPrep : kStGdn>(s, BH, st);
 }
 
-// Bytes of workspace the two-kernel path needs: 16960 per (sequence, chunk).
+// Bytes of workspace the two-kernel path needs: 12864 per (sequence, chunk).
 int64_t chunk_split_workspace_bytes(int64_t BH, int64_t T) {
     const int64_t nC = (T + kChunk - 1) / kChunk;
     return BH * nC * kGdnWsStride * 2;
@@ -1025,7 +1025,7 @@ hipError_t chunk_split_dispatch(int64_t BH, int64_t T, int nh, int dk, int dv, c
 }
 
 // Bytes of workspace of the two-kernel path with fused input preparation, per (sequence,
-// chunk): 49728 for dk = 128, 33344 for dk = 64.
+// chunk): 45632 for dk = 128, 29248 for dk = 64.
 int64_t chunk_split_prep_workspace_bytes(int64_t BH, int64_t T, int dk) {
     const int64_t nC = (T + kChunk - 1) / kChunk;
     return BH * nC * (dk == 128 ? prep_ws_stride<128>() : prep_ws_stride<64>()) * 2;
