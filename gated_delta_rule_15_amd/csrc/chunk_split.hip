@@ -88,15 +88,18 @@ struct UtLds {
     static constexpr int LDX = 16 + 8;   // halfs, rows of a 16x16 fp16 block
     static constexpr int szK = C * LDK * 2;
     static constexpr int szC = C * LDC * 2;
-    // K and Q during the Gram products; afterwards the same bytes hold N^T, A^T and T
+    // K and Q during the Gram products; afterwards the same bytes hold N^T, A^T, T, the
+    // diagonal blocks of N^T (fp32) and X_bb^T (fp16), all written after the last K and Q read
     static constexpr int oK = 0, oQ = szK;
     static constexpr int oNt = 0, oAt = szC, oTt = 2 * szC;
-    static constexpr int szAlias = (2 * szK > 3 * szC ? 2 * szK : 3 * szC);
-    static constexpr int oSm = (szAlias + 15) / 16 * 16;
-    static constexpr int oNd = oSm + UtTab::NSM * 4;          // diagonal blocks of N^T (fp32)
+    static constexpr int oNd = 3 * szC;                       // diagonal blocks of N^T (fp32)
     static constexpr int oXd = oNd + 4 * 16 * LDN * 4;        // X_bb^T (fp16)
-    static constexpr int total = oXd + 4 * 16 * LDX * 2;
-    static_assert(total <= 64 * 1024, "the UT kernel is sized for several workgroups per CU");
+    static constexpr int endAfter = oXd + 4 * 16 * LDX * 2;
+    static constexpr int szAlias = (2 * szK > endAfter ? 2 * szK : endAfter);
+    static constexpr int oSm = (szAlias + 15) / 16 * 16;
+    static constexpr int total = oSm + UtTab::NSM * 4;
+    // four workgroups per CU at DK = 128 (39808 bytes each)
+    static_assert(total <= 160 * 1024 / 4, "the UT kernel is sized for four workgroups per CU");
     static_assert((oSm | oNd | oXd | oAt | oTt) % 16 == 0, "alignment");
 };
 
