@@ -433,6 +433,9 @@ struct StLds {
     // factor table (scalar gate): [0,64) e^G   [64,128) e^{G_C - G}   [128] e^{G_C}
     // (per-channel gate: e^{G_C} [DK])
     static constexpr int FEG = 0, FER = 64, FEC = 128, NF = kGdnWsNF;
+    // one 16-byte slot per loader thread, so that every loader lane stores its piece (the
+    // slots past the table receive zeros) and no branch sits in the loaders' staging
+    static constexpr int NFL = 128 * 4;
     static constexpr int szK = C * LDK * 2;
     static constexpr int szC = C * LDC * 2;
     static constexpr int szV = C * LDV * 2;
@@ -442,7 +445,7 @@ struct StLds {
     static constexpr int oT = oA + 2 * szC;
     static constexpr int oV = oT + 2 * szC;
     static constexpr int oF = oV + 2 * szV;
-    static constexpr int oOt = oF + 2 * NF * 4;  // O^T of a chunk, two buffers
+    static constexpr int oOt = oF + 2 * NFL * 4;  // O^T of a chunk, two buffers
     static constexpr int szO = 32 * LDO * 2;
     static constexpr int total = oOt + 2 * szO;
     static_assert(total <= 160 * 1024, "LDS budget of one gfx950 CU exceeded");
@@ -474,7 +477,7 @@ __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const St
     auto Ab = [&](int b) { return reinterpret_cast<_Float16*>(smem + L::oA + b * L::szC); };
     auto Tb = [&](int b) { return reinterpret_cast<_Float16*>(smem + L::oT + b * L::szC); };
     auto Vb = [&](int b) { return reinterpret_cast<uint16_t*>(smem + L::oV + b * L::szV); };
-    auto Fb = [&](int b) { return reinterpret_cast<float*>(smem + L::oF + b * L::NF * 4); };
+    auto Fb = [&](int b) { return reinterpret_cast<float*>(smem + L::oF + b * L::NFL * 4); };
     auto Ob = [&](int b) { return reinterpret_cast<_Float16*>(smem + L::oOt + b * L::szO); };  // bf16 bits
 
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, j = l & 15, g = l >> 4;
@@ -519,7 +522,11 @@ __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const St
         uint4 wr[ZW ? 2 * NPV : 1];  // the write gate of the V pieces (Gated DeltaNet-2)
     };
     LdRegs R0, R1;
-    auto issue = [&](LdRegs& R, int64_t c) {
+    // The loads of one chunk in two parts: part 0 (K, A^T, V) right after the set is staged,
+    // part 1 (Q, T, the factor table) at the start of the next step, after the o stores, so that
+    // the stores do not queue behind the whole chunk's loads in the CU's memory pipeline.
+    auto issue_part = [&](auto pc, LdRegs& R, int64_t c) {
+        constexpr int P = decltype(pc)::value;
         uint4 *kr = R.kr, *qr = R.qr, *ar = R.ar, *tr = R.tr, *vr = R.vr;
         const uint32_t t0 = (uint32_t)(c * C);
         const uint32_t wb = (uint32_t)(c * WS);
@@ -527,46 +534,56 @@ __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const St
         for (int u = 0; u < NPK; ++u) {
             const int idx = lt + 128 * u, row = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
             if constexpr (KDA) {
-                kr[u] = bld16(rw, (wb + WKG + idx * 8) * 2);
-                qr[u] = bld16(rw, (wb + WKC + idx * 8) * 2);
+                if constexpr (P == 0) kr[u] = bld16(rw, (wb + WKG + idx * 8) * 2);
+                else qr[u] = bld16(rw, (wb + WKC + idx * 8) * 2);
             } else if constexpr (PREP) {  // normalised fp16 rows written by the UT pass
-                kr[u] = bld16(rw, (wb + kPrepWsK + idx * 8) * 2);
-                qr[u] = bld16(rw, (wb + kPrepWsK + C * DK + idx * 8) * 2);
+                if constexpr (P == 0) kr[u] = bld16(rw, (wb + kPrepWsK + idx * 8) * 2);
+                else qr[u] = bld16(rw, (wb + kPrepWsK + C * DK + idx * 8) * 2);
             } else {
                 const uint32_t off = ((t0 + row) * DK + col) * 2;
-                uint32_t offq = off;
-                if constexpr (VIRT) {  // q_t on the last substep of token t, zero elsewhere
-                    const uint32_t m = t0 + row, tr = vtok(m);
-                    offq = m - tr * a.nh == a.nh - 1 ? (tr * DK + col) * 2 : (uint32_t)(Tr * DK * 2);
+                if constexpr (P == 0) {
+                    kr[u] = bld16(rk, off);
+                } else {
+                    uint32_t offq = off;
+                    if constexpr (VIRT) {  // q_t on the last substep of token t, zero elsewhere
+                        const uint32_t m = t0 + row, tr = vtok(m);
+                        offq = m - tr * a.nh == a.nh - 1 ? (tr * DK + col) * 2 : (uint32_t)(Tr * DK * 2);
+                    }
+                    qr[u] = bld16(rq, offq);
                 }
-                kr[u] = bld16(rk, off);
-                qr[u] = bld16(rq, offq);
             }
         }
 #pragma unroll
         for (int u = 0; u < NPW; ++u) {
             const int idx = lt + 128 * u;
-            ar[u] = bld16(rw, (wb + idx * 8) * 2);
-            tr[u] = bld16(rw, (wb + kTriHalfs + idx * 8) * 2);
+            if constexpr (P == 0) ar[u] = bld16(rw, (wb + idx * 8) * 2);
+            else tr[u] = bld16(rw, (wb + kTriHalfs + idx * 8) * 2);
         }
+        if constexpr (P == 0) {
 #pragma unroll
-        for (int u = 0; u < NPV; ++u) {
-            const int idx = lt + 128 * u, row = idx / (2 * NCW), col = (idx % (2 * NCW)) * 8;
-            vr[u] = bld16(rv, ((t0 + row) * DV + dv0 + col) * 2);
-            if constexpr (ZW) {
-                R.wr[2 * u] = bld16(rwg, ((t0 + row) * DV + dv0 + col) * 4);
-                R.wr[2 * u + 1] = bld16(rwg, ((t0 + row) * DV + dv0 + col) * 4 + 16);
+            for (int u = 0; u < NPV; ++u) {
+                const int idx = lt + 128 * u, row = idx / (2 * NCW), col = (idx % (2 * NCW)) * 8;
+                vr[u] = bld16(rv, ((t0 + row) * DV + dv0 + col) * 2);
+                if constexpr (ZW) {
+                    R.wr[2 * u] = bld16(rwg, ((t0 + row) * DV + dv0 + col) * 4);
+                    R.wr[2 * u + 1] = bld16(rwg, ((t0 + row) * DV + dv0 + col) * 4 + 16);
+                }
             }
+        } else {
+            // every loader lane loads (lanes past the table read past the buffer end: zeros), so
+            // that no branch hides a load from the compiler's count of loads in flight
+            R.fr = bld16(rw, lt < NFQ ? (wb + (KDA ? WFE : kGdnWsFactors)) * 2 + lt * 16 : (uint32_t)(nC * WS * 2));
         }
-        // every loader lane loads (lanes past the table read past the buffer end: zeros), so
-        // that no branch hides a load from the compiler's count of loads in flight
-        R.fr = bld16(rw, lt < NFQ ? (wb + (KDA ? WFE : kGdnWsFactors)) * 2 + lt * 16 : (uint32_t)(nC * WS * 2));
+    };
+    auto issue = [&](LdRegs& R, int64_t c) {
+        issue_part(std::integral_constant<int, 0>{}, R, c);
+        issue_part(std::integral_constant<int, 1>{}, R, c);
     };
     // o of chunk c from its O^T buffer: loader wave lw takes rows (value channels) 16 lw ..,
     // a lane reads 8 consecutive channels of one token back transposed and stores 16 bytes
     auto store_o = [&](int64_t c) {
         const int lw = w - NCW;
-        if (lw >= NCW) return;
+        if (NCW == 1 && lw >= NCW) return;  // 16-channel tiles: the second loader wave has no rows
         const _Float16* Ot = Ob((int)(c & 1));
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
@@ -630,7 +647,7 @@ __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const St
                 *reinterpret_cast<uint4*>(Vb(b) + row * L::LDV + col) = vr[u];
             }
         }
-        if (lt < NFQ) reinterpret_cast<uint4*>(Fb(b))[lt] = R.fr;
+        reinterpret_cast<uint4*>(Fb(b))[lt] = R.fr;
     };
 
     // ---- consumer waves (0, 1): the state S^T of 16 value channels (fp32 accumulators, rows
@@ -907,27 +924,29 @@ __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const St
         asm volatile("" ::"v"(tsink));  // keeps the touches
     }
     } else {
-    // loaders, step c (one per chunk, as the consumers' barriers): o of chunk c-1, chunk c+1
-    // (set (c+1) mod 2) into LDS, then the loads of chunk c+3 into the freed set
-    auto step = [&](LdRegs& R, int64_t c) {
+    // loaders, step c (one per chunk, as the consumers' barriers): o of chunk c-1, part 1 of
+    // chunk c+2 (into the other set), chunk c+1 (set (c+1) mod 2) into LDS, then part 0 of
+    // chunk c+3 into the freed set
+    auto step = [&](LdRegs& R, LdRegs& Ro, int64_t c) {
         store_o(c - 1);
+        issue_part(std::integral_constant<int, 1>{}, Ro, c + 2);  // the rest of chunk c+2
         convert(R);
         stage(R, c + 1);
-        issue(R, c + 3);
+        issue_part(std::integral_constant<int, 0>{}, R, c + 3);
         lds_barrier();
     };
-    if (nC > 0) {  // step 0 has no o to store
+    if (nC > 0) {  // step 0 has no o to store (chunk 2 went out whole)
         convert(R1);
         stage(R1, 1);
-        issue(R1, 3);
+        issue_part(std::integral_constant<int, 0>{}, R1, 3);
         lds_barrier();
     }
     int64_t c = 1;
     for (; c + 1 < nC; c += 2) {
-        step(R0, c);
-        step(R1, c + 1);
+        step(R0, R1, c);
+        step(R1, R0, c + 1);
     }
-    if (c < nC) step(R0, c);
+    if (c < nC) step(R0, R1, c);
     if (nC > 0) store_o(nC - 1);
     }
 
