@@ -26,7 +26,10 @@
 // column m stored at position pperm(m), so one operand fragment is one 16-byte read), both fp16
 // with zeros in the upper 16x16 blocks of their diagonal 32x32 blocks and their all-zero 32x32
 // block left out (3072 halfs each, see at_piece / t_piece); then the decay factors of the state
-// pass, fp32: e^{G_l} [64], e^{G_C - G_l} [64], e^{G_C}, 15 zeros (12864 bytes).
+// pass, fp32: e^{G_l} [64], e^{G_C - G_l} [64], e^{G_C}, 15 zeros (12864 bytes).  With the fused
+// input preparation the state pass reads the raw q and k rows and takes their inverse norms in
+// its per-token factors: e^{G_l}/||k_l||, e^{G_C - G_l}/||k_l||, e^{G_C}, 15 zeros and
+// e^{G_l}/||q_l|| (13120 bytes); only the UT pass needs the normalised rows themselves.
 //
 // The per-channel gate ("Kimi Delta Attention (KDA)" section of the same page) takes the same
 // state kernel in its KDA instantiation: the UT pass (chunk_kda.hip) also writes the decayed
@@ -46,22 +49,21 @@
 namespace gdr {
 
 // per-chunk factor table of the UT kernel (floats):
-//   [0,64) G   [192,256) beta   [272,336) cf[m] = e^{Gend(blk(m)) - G_m}
-//   [336,528) rf[b][l] = e^{G_l - Gend(b)}   [528,720) rb[b][l] = beta_l rf[b][l]
+//   [0,64) G   [64,128) 1/||k_l||, [128,192) 1/||q_l|| (fused preparation)   [192,256) beta
+//   [272,336) cf[m] = e^{Gend(blk(m)) - G_m}   [336,528) rf[b][l] = e^{G_l - Gend(b)}
+//   [528,720) rb[b][l] = beta_l rf[b][l]
 struct UtTab {
-    static constexpr int SG = 0, SB = 192, SCF = 272, SRF = 336, SRB = 528, NSM = 736;
+    static constexpr int SG = 0, SIK = 64, SIQ = 128, SB = 192, SCF = 272, SRF = 336, SRB = 528, NSM = 736;
 };
 
 // workspace record of one (sequence, chunk) of the scalar gate, in halfs: A^T, T, factors
 constexpr int kGdnWsFactors = 2 * kTriHalfs;               // offset of the fp32 factor table
 constexpr int kGdnWsNF = 144;                               // its floats
 constexpr int kGdnWsStride = kGdnWsFactors + 2 * kGdnWsNF;  // 6432 halfs = 12864 bytes
-// fused input preparation: the record also holds the chunk's normalised k and q rows (fp16,
-// [64][DK] each), so that the state pass copies them without converting (45632 bytes for
-// DK = 128, 29248 for DK = 64)
-constexpr int kPrepWsK = kGdnWsStride;
-template <int DK>
-constexpr int prep_ws_stride() { return kPrepWsK + 2 * kChunk * DK; }
+// fused input preparation: the factor table holds e^G/||k|| [64], e^{G_C - G}/||k|| [64],
+// e^{G_C}, 15 zeros, e^G/||q|| [64] (13120 bytes per record for either DK)
+constexpr int kPrepNF = 208;
+constexpr int kPrepWsStride = kGdnWsFactors + 2 * kPrepNF;
 
 struct UtArgs {
     int H;              // PREP: heads (bh mod H is the head of the gate parameters)
@@ -110,12 +112,12 @@ struct UtLds {
 // PREP: the inputs from raw projections (same page, "Optional: Constructing the decay gate",
 // and the unit-norm convention of keys and queries): q = q_raw / max(||q_raw||, 1e-6), k
 // likewise, beta = sigmoid(beta_logit), g = -e^{A_log[h]} softplus(dt + dt_bias[h]); the
-// inverse norms go to the workspace for the state pass.
+// inverse norms go into the state pass's per-token factors.
 constexpr int kUtPlain = 0, kUtVirt = 1, kUtPrep = 2;
 template <int DK, int UM>
 __global__ __launch_bounds__(128) void chunk_ut_kernel(const UtArgs a) {
     constexpr bool VIRT = UM == kUtVirt, PREP = UM == kUtPrep;
-    constexpr int WSS = PREP ? prep_ws_stride<DK>() : kGdnWsStride;  // workspace halfs per chunk
+    constexpr int WSS = PREP ? kPrepWsStride : kGdnWsStride;  // workspace halfs per chunk
     using L = UtLds<DK>;
     using S = UtTab;
     constexpr int C = kChunk;
@@ -177,7 +179,6 @@ __global__ __launch_bounds__(128) void chunk_ut_kernel(const UtArgs a) {
                 bt = live ? 1.0f / (1.0f + fast_exp(-bt)) : 0.0f;
             }
         }
-        uint16_t* kqw = a.ws + (bh * a.nC + c) * WSS + kPrepWsK;  // PREP: normalised k, then q
 #pragma unroll
         for (int u = 0; u < NP; ++u) {
             const int idx = tid + 128 * u, row = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
@@ -187,8 +188,10 @@ __global__ __launch_bounds__(128) void chunk_ut_kernel(const UtArgs a) {
                 const half8 hk = unit_rows<DK>(kr[u], ik), hq = unit_rows<DK>(qr[u], iq);
                 *reinterpret_cast<half8*>(Kb + row * L::LDK + col) = hk;
                 *reinterpret_cast<half8*>(Qb + row * L::LDK + col) = hq;
-                *reinterpret_cast<half8*>(kqw + idx * 8) = hk;
-                *reinterpret_cast<half8*>(kqw + C * DK + idx * 8) = hq;
+                if (col == 0) {
+                    sm[S::SIK + row] = ik;
+                    sm[S::SIQ + row] = iq;
+                }
             } else {
                 *reinterpret_cast<half8*>(Kb + row * L::LDK + col) = bf16x8_to_half8(kr[u]);
                 *reinterpret_cast<half8*>(Qb + row * L::LDK + col) = bf16x8_to_half8(qr[u]);
@@ -202,12 +205,14 @@ __global__ __launch_bounds__(128) void chunk_ut_kernel(const UtArgs a) {
             for (int b = 0; b < 4; ++b) ge[b] = lane_value(x, 16 * b + 15);
             const int blk = l >> 4;
             sm[S::SG + l] = x;
-            // the state pass's factors of this chunk
-            float* fw = reinterpret_cast<float*>(a.ws + (bh * a.nC + c) * WSS + kGdnWsFactors);
+            // the state pass's factors of this chunk (PREP: after the barrier, with the norms)
             const float GC = ge[3];
-            fw[l] = fast_exp(x);
-            fw[64 + l] = fast_exp(GC - x);
-            if (l < kGdnWsNF - 128) fw[128 + l] = l == 0 ? fast_exp(GC) : 0.0f;
+            if constexpr (!PREP) {
+                float* fw = reinterpret_cast<float*>(a.ws + (bh * a.nC + c) * WSS + kGdnWsFactors);
+                fw[l] = fast_exp(x);
+                fw[64 + l] = fast_exp(GC - x);
+                if (l < kGdnWsNF - 128) fw[128 + l] = l == 0 ? fast_exp(GC) : 0.0f;
+            }
             sm[S::SB + l] = bt;
             sm[S::SCF + l] = fast_exp(ge[blk] - x);
 #pragma unroll
@@ -219,6 +224,17 @@ __global__ __launch_bounds__(128) void chunk_ut_kernel(const UtArgs a) {
         }
     }
     lds_barrier();
+    if constexpr (PREP) {  // per-token factors with the inverse norms of the raw rows
+        if (w == 0) {
+            float* fw = reinterpret_cast<float*>(a.ws + (bh * a.nC + c) * WSS + kGdnWsFactors);
+            const float x = sm[S::SG + l], GC = sm[S::SG + C - 1];
+            const float ik = sm[S::SIK + l], eg = fast_exp(x);
+            fw[l] = eg * ik;
+            fw[64 + l] = fast_exp(GC - x) * ik;
+            if (l < 16) fw[128 + l] = l == 0 ? fast_exp(GC) : 0.0f;
+            fw[144 + l] = eg * sm[S::SIQ + l];
+        }
+    }
 
     // ---- Gram tiles.  Wave 0 forms KK {00,10,11,20,21,30,31} and QK {00,10,11}; wave 1 forms
     // KK {22,32,33} and QK {20,21,22,30,31,32,33}.  Off the diagonal the decay is factorised
@@ -432,7 +448,7 @@ struct StLds {
     static constexpr int LDO = C + 8;  // bf16, rows of O^T
     // factor table (scalar gate): [0,64) e^G   [64,128) e^{G_C - G}   [128] e^{G_C}
     // (per-channel gate: e^{G_C} [DK])
-    static constexpr int FEG = 0, FER = 64, FEC = 128, NF = kGdnWsNF;
+    static constexpr int FEG = 0, FER = 64, FEC = 128, FEQ = 144, NF = kGdnWsNF;
     // one 16-byte slot per loader thread, so that every loader lane stores its piece (the
     // slots past the table receive zeros) and no branch sits in the loaders' staging
     static constexpr int NFL = 128 * 4;
@@ -466,7 +482,7 @@ __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const St
     constexpr bool KDA = MODE == kStKda || MODE == kStGd2;  // the UT pass wrote the decayed copies
     constexpr bool ZW = MODE == kStGd2;                     // V tile holds z = w (.) v in fp32
     constexpr bool VIRT = MODE == kStGdp;                   // GDP virtual steps
-    constexpr bool PREP = MODE == kStPrep;                  // normalised q, k from the workspace
+    constexpr bool PREP = MODE == kStPrep;                  // raw q, k; inverse norms in the factors
     using L = StLds<DK>;
     constexpr int C = kChunk;
     constexpr int NKB = DK / 32;
@@ -496,7 +512,7 @@ __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const St
     const auto rk = make_rsrc(KDA ? nullptr : a.k + bh * T * DK, KDA ? 0u : (uint32_t)(T * DK * 2));
     const auto rv = make_rsrc(a.v + bh * T * DV, (uint32_t)(T * DV * 2));
     const auto rwg = make_rsrc(ZW ? a.wg + bh * T * DV : nullptr, ZW ? (uint32_t)(T * DV * 4) : 0u);
-    constexpr int WS = KDA ? kda_ws_stride<DK>() : PREP ? prep_ws_stride<DK>() : kGdnWsStride;  // halfs per chunk
+    constexpr int WS = KDA ? kda_ws_stride<DK>() : PREP ? kPrepWsStride : kGdnWsStride;  // halfs per chunk
     // offsets (halfs) inside a chunk's workspace record of the per-channel gate
     constexpr int WKG = 2 * kTriHalfs, WQG = WKG + C * DK, WKC = WQG + C * DK, WFE = WKC + C * DK;
     const auto rw = make_rsrc(a.ws + bh * nC * WS, (uint32_t)(nC * WS * 2));
@@ -516,7 +532,7 @@ __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const St
     constexpr int NPW = kTriPieces / 128;  // A^T (and T) pieces per loader thread
     // (KDA: kr holds K e^G, qr K e^{G_C - G}); fr: 16-byte pieces of the factor table, the
     // first NFQ loader threads one each
-    constexpr int NFQ = KDA ? DK / 4 : L::NF / 4;
+    constexpr int NFQ = KDA ? DK / 4 : PREP ? kPrepNF / 4 : L::NF / 4;
     struct LdRegs {
         uint4 kr[NPK], qr[NPK], ar[NPW], tr[NPW], vr[NPV], fr;
         uint4 wr[ZW ? 2 * NPV : 1];  // the write gate of the V pieces (Gated DeltaNet-2)
@@ -536,9 +552,6 @@ __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const St
             if constexpr (KDA) {
                 if constexpr (P == 0) kr[u] = bld16(rw, (wb + WKG + idx * 8) * 2);
                 else qr[u] = bld16(rw, (wb + WKC + idx * 8) * 2);
-            } else if constexpr (PREP) {  // normalised fp16 rows written by the UT pass
-                if constexpr (P == 0) kr[u] = bld16(rw, (wb + kPrepWsK + idx * 8) * 2);
-                else qr[u] = bld16(rw, (wb + kPrepWsK + C * DK + idx * 8) * 2);
             } else {
                 const uint32_t off = ((t0 + row) * DK + col) * 2;
                 if constexpr (P == 0) {
@@ -601,7 +614,7 @@ __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const St
     };
     // K and Q to fp16 in the registers (while the consumers' first products read LDS)
     auto convert = [&](LdRegs& R) {
-        if constexpr (KDA || PREP) return;  // the UT pass wrote fp16
+        if constexpr (KDA) return;  // the UT pass wrote fp16
         uint4 *kr = R.kr, *qr = R.qr;
 #pragma unroll
         for (int u = 0; u < NPK; ++u) {
@@ -900,6 +913,10 @@ __global__ __launch_bounds__(64 * (NCW + 2), 1) void chunk_state_kernel(const St
                 }
             }
             issue_qg(c + 1);  // past the end: zeros, unused (no branch: see the loaders)
+            if constexpr (PREP) {  // the output's factor carries 1/||q|| instead of 1/||k||
+#pragma unroll
+                for (int ti = 0; ti < 4; ++ti) eg[ti] = ld4f(F + L::FEQ + 16 * ti + 4 * g);
+            }
             float4v Oa[4];
 #pragma unroll
             for (int ti = 0, n = 0; ti < 4; ++ti) {
@@ -1046,11 +1063,12 @@ hipError_t chunk_split_dispatch(int64_t BH, int64_t T, int nh, int dk, int dv, c
     return launch_split<64, kUtPlain>(u, s, BH, st);
 }
 
-// Bytes of workspace of the two-kernel path with fused input preparation, per (sequence,
-// chunk): 45632 for dk = 128, 29248 for dk = 64.
+// Bytes of workspace of the two-kernel path with fused input preparation: 13120 per (sequence,
+// chunk) for either dk.
 int64_t chunk_split_prep_workspace_bytes(int64_t BH, int64_t T, int dk) {
+    (void)dk;
     const int64_t nC = (T + kChunk - 1) / kChunk;
-    return BH * nC * (dk == 128 ? prep_ws_stride<128>() : prep_ws_stride<64>()) * 2;
+    return BH * nC * kPrepWsStride * 2;
 }
 
 // Gated DeltaNet from raw projections on the two-kernel path: q_raw, k_raw [BH][T][dk] bf16,

@@ -174,9 +174,8 @@ gdr_status gdr_chunk_fwd_noalloc(int64_t B, int64_t H, int64_t T, int d_k, int d
 
 /*
  * gdr_chunk_fwd_fused_prep_workspace_size -- bytes of device workspace
- * gdr_chunk_fwd_fused_prep needs, per sequence and 64-token chunk, 12864 + 256 d_k bytes
- * (45632 for d_k = 128, 29248 for d_k = 64); -1 for sizes gdr_chunk_fwd_fused_prep would
- * reject.
+ * gdr_chunk_fwd_fused_prep needs, per sequence and 64-token chunk, 13120 bytes (either d_k);
+ * -1 for sizes gdr_chunk_fwd_fused_prep would reject.
  */
 int64_t gdr_chunk_fwd_fused_prep_workspace_size(int64_t B, int64_t H, int64_t T, int d_k, int d_v);
 
@@ -193,9 +192,11 @@ int64_t gdr_chunk_fwd_fused_prep_workspace_size(int64_t B, int64_t H, int64_t T,
  * The gate is Mamba-2's construction ("Linear Attention, Visualized", section "Mamba-2:
  * input-dependent scalar decay", "Optional: Constructing the decay gate"): a decay rate
  * lambda = e^{A_log} per head times a positive step Delta_t = softplus(dt_t + b_Delta).
- * The first kernel normalises q and k (in fp32 before the fp16 rounding), forms beta and g,
- * and writes, besides T, A and the decay factors, the normalised q and k rows in fp16; the
- * state kernel reads those instead of the raw inputs.
+ * The first kernel normalises q and k (in fp32 before the fp16 rounding) for the chunk-local
+ * products, forms beta and g, and writes T, A and the per-token factors of the state pass
+ * with the inverse norms folded in (e^G / ||k||, e^{G_C - G} / ||k||, e^G / ||q||).  The
+ * state kernel reads the raw q and k rows: every product it forms with them is scaled per
+ * token, so the normalisation is exact there and no normalised row is ever written.
  *
  *   q_raw, k_raw     [B, H, T, d_k]  bf16 (not normalised)
  *   v                [B, H, T, d_v]  bf16
@@ -204,7 +205,10 @@ int64_t gdr_chunk_fwd_fused_prep_workspace_size(int64_t B, int64_t H, int64_t T,
  *   initial_state, o, final_state, workspace, workspace_bytes   as gdr_chunk_fwd
  *
  * Equivalent to computing q, k, g, beta as above and calling gdr_chunk_fwd with
- * GDR_GATE_SCALAR, except that q and k enter the fp16 MFMA operands unrounded to bf16.
+ * GDR_GATE_SCALAR, except that q and k are not rounded to bf16 after the normalisation.
+ * Range: the raw rows enter the state kernel's fp16 operands unscaled, so every element of
+ * q_raw and k_raw must stay below 65504 in magnitude; rows whose elements all fall below
+ * 6.1e-5 (fp16's smallest normal) lose accuracy there.
  * io_dtype must be GDR_BF16 (GDR_F32 returns GDR_ERR_UNSUPPORTED).  Sizes, T range and every
  * other error as for gdr_chunk_fwd.
  */

@@ -238,7 +238,7 @@ def prep(lib, B=1, H=1, T=64, dk=128, dv=128, io=0, q=FAKE, k=FAKE, v=FAKE, dt=F
     (dict(T=(1 << 22) + 1), SHAPE),
     (dict(B=1 << 40, H=1 << 30), SHAPE),
     (dict(ws=None), WSERR),                                     # a workspace is required
-    (dict(nbytes=45631), WSERR),                                # one chunk needs 45632 bytes
+    (dict(nbytes=13119), WSERR),                                # one chunk needs 13120 bytes
     (dict(nbytes=-1), WSERR),
     (dict(ws=FAKE), WSERR), (dict(ws=FAKE2), WSERR),            # workspace overlaps q_raw / o
 ])
@@ -248,8 +248,8 @@ def test_fused_prep_rejects(lib, kw, status):
 
 def test_fused_prep_workspace_size(lib):
     n = lib.gdr_chunk_fwd_fused_prep_workspace_size
-    assert n(4, 16, 4096, 128, 128) == 64 * 64 * 45632
-    assert n(1, 2, 65, 64, 64) == 2 * 2 * 29248
+    assert n(4, 16, 4096, 128, 128) == 64 * 64 * 13120
+    assert n(1, 2, 65, 64, 64) == 2 * 2 * 13120
     assert n(1, 1, 0, 128, 128) == 0
     assert n(-1, 1, 64, 128, 128) == -1 and n(1, 1, 64, 96, 128) == -1
 

@@ -7,8 +7,8 @@ directly, chunk by chunk, including a ragged last chunk:
   scalar gate: A (the local scores), T = (I + diag(beta) L)^{-1} diag(beta) (the UT
     transform), e^{G_l}, e^{G_C - G_l} and e^{G_C};
   per-channel gate: A, T, K e^G, Q e^G, K e^{G_C - G} and e^{G_C} per key channel;
-  fused input preparation: A, T and the factors of the prepared inputs, and the unit-norm
-    rows of k and q the record carries;
+  fused input preparation: A, T and the per-token factors with the raw rows' inverse norms
+    folded in;
   Gated DeltaNet-2: A, T = (I + M)^{-1} (oracle.gdn2_chunk_transform), the erase-side copy
     (b (.) k) e^G, Q e^G, K e^{G_C - G} and e^{G_C};
   Gated Delta Product: the scalar-gate records over the virtual sequence of substeps.
@@ -20,6 +20,8 @@ Record layout per (sequence, chunk), fp16 unless noted (C = 64):
     all-zero block (rows ..31, columns 32..): rows 0..31 at columns 0..31, then rows 32..63
     at full width (3072 halfs);
   scalar gate: fp32 e^{G_l} [C], e^{G_C - G_l} [C], e^{G_C}, 15 zeros;
+  fused preparation: fp32 e^{G_l}/||k_l|| [C], e^{G_C - G_l}/||k_l|| [C], e^{G_C}, 15 zeros,
+    e^{G_l}/||q_l|| [C];
   per-channel gate: K e^G, Q e^G, K e^{G_C - G} [C][d_k] each, then fp32 e^{G_C} [d_k].
 Tokens past the end of a sequence enter the kernels as identity tokens (k = q = 0, g = 0,
 beta = 0), so a ragged chunk's records hold the oracle's shorter chunk in their leading rows
@@ -96,7 +98,6 @@ def _f32(raw, byte_off, n):
 
 TRI = 3 * C * C // 4          # halfs of one compact triangular matrix
 FACTORS = 4 * TRI              # byte offset of the fp32 factor table (and of the KDA copies)
-GDN_RECORD = FACTORS + 4 * 144  # bytes of the scalar gate's record
 
 
 def _expand(flat, upper_zero):
@@ -193,9 +194,10 @@ def test_ut_records_channel_gate(T, dk):
 @pytest.mark.parametrize("T", [64, 100])
 @pytest.mark.parametrize("dk", [128, 64])
 def test_ut_records_fused_prep(T, dk):
-    """UT pass with the fused input preparation: A, T and the factors of the prepared inputs,
-    and the unit-norm fp16 rows of k and q that the record carries after the factor table
-    (after the scalar-gate record: k [C][d_k], then q)."""
+    """UT pass with the fused input preparation: A and T of the prepared inputs, and the state
+    pass's per-token factors with the inverse norms of the raw rows folded in: e^{G_l}/||k_l||,
+    e^{G_C - G_l}/||k_l||, e^{G_C} and e^{G_l}/||q_l|| (the state pass multiplies the raw rows'
+    products by them)."""
     w = dataclasses.replace(gdr_synth.WORKLOADS[2], d_k=dk, d_v=dk)
     r = gdr_synth.make_raw_inputs(w, B=1, H=2, T=T, head_params="varied")
     nbytes = gdr.chunk_fwd_fused_prep_workspace_size(1, 2, T, dk, dk)
@@ -207,6 +209,8 @@ def test_ut_records_fused_prep(T, dk):
     nC = (T + C - 1) // C
     stride = nbytes // (2 * nC)
     q, k, g, beta = oracle.prepare_inputs(r["q_raw"], r["k_raw"], r["dt"], r["A_log"], r["dt_bias"], r["beta_logit"])
+    # the normalisation's inverse norms, 1 / max(||x_raw||, 1e-6), of the rows the kernel read
+    inv = {n: 1.0 / np.maximum(np.linalg.norm(np.asarray(r[n], np.float64), axis=-1), 1e-6) for n in ("q_raw", "k_raw")}
     for h in range(2):
         for c in range(nC):
             s0, s1 = c * C, min(T, (c + 1) * C)
@@ -218,14 +222,21 @@ def test_ut_records_fused_prep(T, dk):
             base = (h * nC + c) * stride
             label = f"prep d_k={dk} T={T} head {h} chunk {c}"
             _check_at_t(raw, base, A_ref, tr["T"], Cr, label)
-            f = _f32(raw, base + FACTORS, 144)
-            assert abs(f[128] - float(tr["lam_C"])) / float(tr["lam_C"]) < TOL_F32, label
-            for i, (name, ref) in enumerate((("k", K), ("q", Q))):
-                got = _f16(raw, base + GDN_RECORD + i * 2 * C * dk, C * dk).reshape(C, dk)
-                e = _rel(got[:Cr], ref)
-                print(f"{label}: e[{name}] {e:.2e}")
-                assert e < TOL_F16, (label, name)
-                assert np.all(got[Cr:] == 0.0), (label, name)
+            f = _f32(raw, base + FACTORS, 208)
+            lam = tr["lam"]
+            eg = np.array([lam(1, l) for l in range(1, Cr + 1)])
+            er = np.array([lam(l + 1, Cr) for l in range(1, Cr + 1)])
+            lamC = float(tr["lam_C"])
+            ik, iq = inv["k_raw"][0, h, s0:s1], inv["q_raw"][0, h, s0:s1]
+            assert _rel(f[:Cr], eg * ik) < TOL_F32, label
+            assert _rel(f[64:64 + Cr], er * ik) < TOL_F32, label
+            assert abs(f[128] - lamC) / lamC < TOL_F32, label
+            assert np.all(f[129:144] == 0.0), label
+            assert _rel(f[144:144 + Cr], eg * iq) < TOL_F32, label
+            # past the end the rows are zero (inverse norm 1e6): the factors only ever multiply
+            # products with those zero rows
+            assert np.all(np.abs(f[Cr:64] - 1e6 * lamC) <= 1e-5 * 1e6 * lamC), label
+            assert np.all(np.abs(f[144 + Cr:208] - 1e6 * lamC) <= 1e-5 * 1e6 * lamC), label
 
 
 @pytest.mark.parametrize("T", [64, 100])
