@@ -300,9 +300,25 @@ __global__ __launch_bounds__(128) void chunk_ut_kernel(const UtArgs a) {
         }
     }
     lds_barrier();  // every read of K and Q is done: their bytes become N^T, A^T and T
-    for (int i = tid; i < 3 * L::szC / 16; i += 128)
-        reinterpret_cast<uint4*>(smem + L::oNt)[i] = uint4{0u, 0u, 0u, 0u};
-    lds_barrier();
+    // Zeros where the record holds them and no later write lands: the 16x16 blocks of A^T
+    // below the block diagonal inside the stored region (rows 16-31 x columns 0-15, rows 48-63
+    // x columns 32-47), and the upper blocks of T's stored diagonal 32x32 blocks (rows 0-15
+    // and 32-47 of their 32 stored columns; the inverses overwrite the diagonal 16x16 blocks
+    // inside those rows later).  Every other element of A^T and T that the copy-out reads is
+    // written by this epilogue, the inverses or the blocks below the diagonal; N^T is read
+    // below its block diagonal only.  None of these stores meets another write before the
+    // next barrier.
+    for (int i = tid; i < 192; i += 128) {
+        _Float16* z;
+        if (i < 64) {
+            const int r = i < 32 ? 16 + (i >> 1) : 48 + ((i - 32) >> 1), cz = (i < 32 ? 0 : 32) + (i & 1) * 8;
+            z = At + r * L::LDC + cz;
+        } else {
+            const int k = i - 64, hi = k >> 6, kk = k & 63;
+            z = Tt + (32 * hi + (kk >> 2)) * L::LDC + 32 * hi + (kk & 3) * 8;
+        }
+        *reinterpret_cast<uint4*>(z) = uint4{0u, 0u, 0u, 0u};
+    }
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
         const int ti = ti_[P][t], tj = tj_[P][t];
