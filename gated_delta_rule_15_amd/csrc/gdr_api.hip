@@ -96,6 +96,14 @@ gdr_status check_aliasing(const void* o, int64_t obytes, const Span* ins, int ni
 
 gdr_status from_hip(hipError_t e) { return e == hipSuccess ? GDR_OK : GDR_ERR_HIP; }
 
+// Both grids of a chunked call fit a launch: the state pass's B*H*d_v/16 groups (at most) and
+// the UT pass's B*H*ceil(steps/64) (one group per chunk).
+bool grids_ok(int64_t BH, int d_v, int64_t steps) {
+    int64_t a = 0, b = 0;
+    return mul_ok(BH, d_v / 16, &a) && a <= kMaxGrid && mul_ok(BH, (steps + kChunkLen - 1) / kChunkLen, &b) &&
+           b <= kMaxGrid;
+}
+
 // Per-channel workspace bytes of one sequence: the state kernel addresses them with 32-bit
 // offsets, so they must stay below 4 GiB.
 int64_t kda_ws_bytes_per_seq(int64_t T, int d_k) {
@@ -150,8 +158,7 @@ gdr_status check_chunk(int64_t B, int64_t H, int64_t T, int d_k, int d_v, int io
     if (io_dtype == GDR_F32 && (d_k != 64 || gate == GDR_GATE_CHANNEL)) return GDR_ERR_UNSUPPORTED;
     *BHout = BH;
     if (BH == 0) return GDR_OK;
-    int64_t nwg;
-    if (!mul_ok(BH, d_v / 16, &nwg) || nwg > kMaxGrid) return GDR_ERR_SHAPE;
+    if (!grids_ok(BH, d_v, T)) return GDR_ERR_SHAPE;
     *launch = final_state != nullptr || BHT > 0;
     return GDR_OK;
 }
@@ -238,8 +245,7 @@ gdr_status check_gdp(int64_t B, int64_t H, int64_t T, int n_h, int d_k, int d_v,
     if (s != GDR_OK) return s;
     *BHout = BH;
     if (BH == 0) return GDR_OK;
-    int64_t nwg;
-    if (!mul_ok(BH, d_v / 16, &nwg) || nwg > kMaxGrid) return GDR_ERR_SHAPE;
+    if (!grids_ok(BH, d_v, T * n_h)) return GDR_ERR_SHAPE;
     *launch = final_state != nullptr || BHT > 0;
     return GDR_OK;
 }
@@ -305,8 +311,7 @@ gdr_status check_prep(int64_t B, int64_t H, int64_t T, int d_k, int d_v, int io_
     if (s != GDR_OK) return s;
     *BHout = BH;
     if (BH == 0) return GDR_OK;
-    int64_t nwg;
-    if (!mul_ok(BH, d_v / 16, &nwg) || nwg > kMaxGrid) return GDR_ERR_SHAPE;
+    if (!grids_ok(BH, d_v, T)) return GDR_ERR_SHAPE;
     *launch = final_state != nullptr || BHT > 0;
     return GDR_OK;
 }
@@ -374,8 +379,7 @@ gdr_status check_gdn2(int64_t B, int64_t H, int64_t T, int d_k, int d_v, int io_
     if (s != GDR_OK) return s;
     *BHout = BH;
     if (BH == 0) return GDR_OK;
-    int64_t nwg;
-    if (!mul_ok(BH, d_v / 16, &nwg) || nwg > kMaxGrid) return GDR_ERR_SHAPE;
+    if (!grids_ok(BH, d_v, T)) return GDR_ERR_SHAPE;
     *launch = final_state != nullptr || BHT > 0;
     return GDR_OK;
 }

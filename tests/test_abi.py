@@ -330,3 +330,15 @@ def test_python_binding_refuses_cpu_tensors(lib):
     with pytest.raises(ValueError):
         gdr.decode_step(x[:, :, 0], x[:, :, 0], x[:, :, 0], torch.zeros(1, 1), torch.zeros(1, 1),
                         torch.zeros(1, 1, 64, 64))
+
+
+def test_chunked_grids_stay_within_one_launch(lib):
+    """B*H*ceil(T/64) UT groups beyond one launch's grid limit return GDR_ERR_SHAPE (never a
+    truncated grid), for every chunked entry point; the buffers sit 2^52 bytes apart so that no
+    overlap check fires first."""
+    P = [ctypes.c_void_p(i << 52) for i in range(1, 10)]
+    B, T = 1 << 20, 1 << 22  # 2^21 state groups at d_v = 32, but 2^36 UT groups
+    assert lib.gdr_chunk_fwd(B, 1, T, 128, 32, 0, 0, *P[:5], None, P[5], None, P[6], 1 << 20, None) == SHAPE
+    assert lib.gdr_gdn2_chunk_fwd(B, 1, T, 128, 32, 0, *P[:6], None, P[6], None, P[7], 1 << 20, None) == SHAPE
+    assert lib.gdr_chunk_fwd_fused_prep(B, 1, T, 128, 32, 0, *P[:7], None, P[7], None, P[8], 1 << 20, None) == SHAPE
+    assert lib.gdr_gdp_chunk_fwd(B, 1, T // 2, 2, 128, 32, 0, *P[:5], None, P[5], None, P[6], 1 << 20, None) == SHAPE
