@@ -43,6 +43,11 @@ TRAFFIC = {
     "kda": ("chunk_kda_B2_H16_T8192_traffic.json", ("chunk_kda.hip", "chunk_split.hip", "chunk_common.h", "gdr_device.h")),
     "long": ("chunk_split_long_B1_H32_T65536_traffic.json", ("chunk_split.hip", "chunk_common.h", "gdr_device.h")),
     "decode": ("decode_N256_H32_d128_traffic.json", ("decode.hip", "gdr_device.h")),
+    "gdp": ("chunk_split_gdp_B4_H16_T2048_nh2_traffic.json", ("chunk_split.hip", "chunk_common.h", "gdr_device.h")),
+    "gdn2": ("chunk_kda_gdn2_B2_H16_T8192_traffic.json",
+             ("chunk_kda.hip", "chunk_split.hip", "chunk_common.h", "gdr_device.h")),
+    "prep": ("chunk_split_prep_B4_H16_T4096_traffic.json", ("chunk_split.hip", "chunk_common.h", "gdr_device.h")),
+    "frame": ("frame_B1_H16_T16384_n1024_traffic.json", ("frame.hip", "chunk_common.h", "gdr_device.h")),
 }
 COPY_BYTES = 256 << 20  # calibration copy for the HBM byte counters
 
@@ -191,7 +196,7 @@ def bench_decode(torch, gdr, gdr_synth, steps=64):
             "frac_of_copy_rate": round(gbs / copy_gbs, 4)}
 
 
-def bench_gdp(torch, gdr, gdr_synth, steps=10):
+def bench_gdp(torch, gdr, gdr_synth, steps=10, parity=True):
     """Gated Delta Product forward on B=4, H=16, T=2048, n_h=2, d=128 (4096 substeps per
     sequence).  Algorithmic work is that of the chunked GDN over the T n_h virtual steps;
     bytes: q, g and o per token, k, v and beta per substep, the final state."""
@@ -205,6 +210,8 @@ def bench_gdp(torch, gdr, gdr_synth, steps=10):
     flops = chunk_flops(w.B, w.H, Tv, w.d_k, w.d_v)
     nbytes = (w.B * w.H * (w.T * (2 * w.d_k + 2 * w.d_v + 4) + Tv * (2 * w.d_k + 2 * w.d_v + 4))
               + w.B * w.H * w.d_k * w.d_v * 4)
+    if not parity:
+        return {"ms_per_call": round(ms, 4)}
     # parity on one sampled sequence (GDN over the virtual sequence, the CPU-pinned oracle route)
     import oracle
     from parity import err_bf16_out, err_literal
@@ -218,7 +225,7 @@ def bench_gdp(torch, gdr, gdr_synth, steps=10):
            "substeps_per_s": round(w.B * Tv / (ms * 1e-3), 1),
            "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_MFMA_F16, 4),
            "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM, 4),
-           "flops_per_launch": flops, "bytes_per_launch": nbytes,
+           "flops_per_launch": flops, "bytes_per_launch": nbytes, "traffic": measured_traffic("gdp"),
            "parity_sampled": {"heads_checked": 1,
                               "e_o": round(err_bf16_out(o[:1, :1].float().cpu().numpy().astype(np.float64),
                                                         o_ref[:, :, keep]), 6),
@@ -254,10 +261,11 @@ def bench_prep(torch, gdr, gdr_synth, steps=20):
             "kernel": "chunk_ut_kernel<128, 2> + chunk_state_kernel<128, 4, 2>", "ms_per_call": round(ms, 4),
             "tokens_per_s": round(w.B * w.T / (ms * 1e-3), 1),
             "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_MFMA_F16, 4),
+            "traffic": measured_traffic("prep"),
             "separate_prep_pass_hbm_floor_ms": round(separate_pass / (PEAK_HBM * 1e9) * 1e3, 4)}
 
 
-def bench_frame(torch, gdr, gdr_synth, steps=10):
+def bench_frame(torch, gdr, gdr_synth, steps=10, parity=True):
     """Frame-level implicit update on B=1, H=16, T=16384 as 16 frames of 1024 tokens, d=128,
     per-channel frame gate.  Algorithmic flops per (frame, head): the lower triangle of
     G = K^T Gamma K (n d_k^2), C = V^T Gamma K (2 n d_k d_v), the inverse of I + G (2 d_k^3),
@@ -285,6 +293,8 @@ def bench_frame(torch, gdr, gdr_synth, steps=10):
     per = n * dk * dk + 2 * n * dk * dv + 2 * dk ** 3 + 2 * dk * dk * dv + 2 * n * dk * dv
     flops = wf["B"] * wf["H"] * F * per
     nbytes = wf["B"] * wf["H"] * wf["T"] * ((2 * dk + 2 * dv) * 2 + 4) + wf["B"] * wf["H"] * F * dk * 4
+    if not parity:
+        return {"ms_per_call": round(ms, 4)}
     from oracle.frame import frame_forward
     from parity import err_bf16_out, err_literal
     sub = {kk: (None if host[kk] is None else host[kk][:, :1]) for kk in host}
@@ -297,14 +307,14 @@ def bench_frame(torch, gdr, gdr_synth, steps=10):
             "ms_per_call": round(ms, 4), "tokens_per_s": round(wf["B"] * wf["T"] / (ms * 1e-3), 1),
             "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_MFMA_F16, 4),
             "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM, 4),
-            "flops_per_launch": flops, "bytes_per_launch": nbytes,
+            "flops_per_launch": flops, "bytes_per_launch": nbytes, "traffic": measured_traffic("frame"),
             "parity_sampled": {"heads_checked": 1,
                                "e_o": round(err_bf16_out(outs[0][:, :1].float().cpu().numpy().astype(np.float64),
                                                          o_ref), 6),
                                "e_S": round(err_literal(fin[0][:, :1].cpu().numpy().astype(np.float64), S_ref), 6)}}
 
 
-def bench_gdn2(torch, gdr, gdr_synth, steps=10):
+def bench_gdn2(torch, gdr, gdr_synth, steps=10, parity=True):
     """Gated DeltaNet-2 forward on B=2, H=16, T=8192, d=128 (per-channel decay, erase gate b,
     write gate w).  Algorithmic flops as the chunked forward; bytes: q, k, v, o in bf16, g and
     b [T, d_k] and w [T, d_v] in fp32, the final state."""
@@ -328,6 +338,8 @@ def bench_gdn2(torch, gdr, gdr_synth, steps=10):
     flops = chunk_flops(w.B, w.H, w.T, w.d_k, w.d_v)
     n = w.B * w.H * w.T
     nbytes = n * (2 * w.d_k + 2 * w.d_v) * 2 + n * (2 * w.d_k + w.d_v) * 4 + w.B * w.H * w.d_k * w.d_v * 4
+    if not parity:
+        return {"ms_per_call": round(ms, 4)}
     import oracle
     from parity import err_bf16_out, err_literal
     x = sets[0]["host"]
@@ -342,7 +354,7 @@ def bench_gdn2(torch, gdr, gdr_synth, steps=10):
             "tokens_per_s": round(w.B * w.T / (ms * 1e-3), 1),
             "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_MFMA_F16, 4),
             "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM, 4),
-            "flops_per_launch": flops, "bytes_per_launch": nbytes,
+            "flops_per_launch": flops, "bytes_per_launch": nbytes, "traffic": measured_traffic("gdn2"),
             "parity_sampled": {"heads_checked": 1,
                                "e_o": round(err_bf16_out(outs[0][:1, :1].float().cpu().numpy().astype(np.float64),
                                                          o_ref), 6),
@@ -382,7 +394,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="headline workload only")
-    ap.add_argument("--pmc-run", choices=("headline", "decode", "kda", "long"), default=None,
+    ap.add_argument("--pmc-run", choices=("headline", "decode", "kda", "long", "gdp", "gdn2", "prep", "frame"),
+                    default=None,
                     help="launch one workload's kernels --steps times and one 256 MiB device copy, print nothing")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -401,6 +414,11 @@ def main():
         # FETCH_SIZE / WRITE_SIZE calibrate the counters' byte units.
         if args.pmc_run == "decode":
             bench_decode(torch, gdr, gdr_synth, steps=args.steps)
+        elif args.pmc_run in ("gdp", "gdn2", "frame"):
+            {"gdp": bench_gdp, "gdn2": bench_gdn2, "frame": bench_frame}[args.pmc_run](
+                torch, gdr, gdr_synth, steps=args.steps, parity=False)
+        elif args.pmc_run == "prep":
+            bench_prep(torch, gdr, gdr_synth, steps=args.steps)
         else:
             wid = {"headline": 2, "kda": 3, "long": 4}[args.pmc_run]
             time_chunk(torch, gdr, make_chunk_sets(torch, gdr_synth, gdr_synth.WORKLOADS[wid],

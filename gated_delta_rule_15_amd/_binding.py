@@ -104,6 +104,14 @@ def _on(stream):
     return contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
 
 
+def _launch(dev, fn, *args):
+    """fn(*args) with the tensors' device current: the library resolves its per-device launch
+    settings (and gdr_chunk_fwd_noalloc's built-in workspace) through the current device."""
+    import torch
+    with torch.cuda.device(dev):
+        return fn(*args)
+
+
 def _io_dtype(t):
     import torch
     if t.dtype == torch.bfloat16:
@@ -196,7 +204,7 @@ def chunk_fwd(q, k, v, g, beta, initial_state=None, *, output_final_state=True, 
                               stream)
     need = chunk_fwd_workspace_size(B, H, T, dk, dv, io, gate)
     ws, nbytes = _workspace(workspace, need, dev, stream)
-    st = load_library().gdr_chunk_fwd(B, H, T, dk, dv, io, gate, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+    st = _launch(dev, load_library().gdr_chunk_fwd, B, H, T, dk, dv, io, gate, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                       _ptr(initial_state), _ptr(o), _ptr(final_state), _ptr(ws), nbytes,
                                       _stream(stream, dev))
     if st != GDR_OK:
@@ -239,7 +247,7 @@ def chunk_fwd_noalloc(q, k, v, g, beta, initial_state, out, final_state, *, stre
     _check(out, "out", (B, H, T, dv), q.dtype, dev)
     if final_state is not None:
         _check(final_state, "final_state", (B, H, dv, dk), torch.float32, dev)
-    st = load_library().gdr_chunk_fwd_noalloc(B, H, T, dk, dv, io, gate, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+    st = _launch(dev, load_library().gdr_chunk_fwd_noalloc, B, H, T, dk, dv, io, gate, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
                                               _ptr(beta), _ptr(initial_state), _ptr(out), _ptr(final_state),
                                               _stream(stream, dev))
     if st != GDR_OK:
@@ -281,7 +289,7 @@ def chunk_fwd_fused_prep(q_raw, k_raw, v, dt, A_log, dt_bias, beta_logit, initia
     o, final_state = _outputs((B, H, T, dv), q_raw.dtype, (B, H, dv, dk), dev, out, final_state,
                               output_final_state, stream)
     ws, nbytes = _workspace(workspace, chunk_fwd_fused_prep_workspace_size(B, H, T, dk, dv), dev, stream)
-    st = load_library().gdr_chunk_fwd_fused_prep(B, H, T, dk, dv, io, _ptr(q_raw), _ptr(k_raw), _ptr(v), _ptr(dt),
+    st = _launch(dev, load_library().gdr_chunk_fwd_fused_prep, B, H, T, dk, dv, io, _ptr(q_raw), _ptr(k_raw), _ptr(v), _ptr(dt),
                                                  _ptr(A_log), _ptr(dt_bias), _ptr(beta_logit), _ptr(initial_state),
                                                  _ptr(o), _ptr(final_state), _ptr(ws), nbytes, _stream(stream, dev))
     if st != GDR_OK:
@@ -323,7 +331,7 @@ def gdp_chunk_fwd(q, k, v, g, beta, initial_state=None, *, output_final_state=Tr
     o, final_state = _outputs((B, H, T, dv), q.dtype, (B, H, dv, dk), dev, out, final_state, output_final_state,
                               stream)
     ws, nbytes = _workspace(workspace, gdp_chunk_fwd_workspace_size(B, H, T, nh, dk, dv), dev, stream)
-    st = load_library().gdr_gdp_chunk_fwd(B, H, T, nh, dk, dv, io, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+    st = _launch(dev, load_library().gdr_gdp_chunk_fwd, B, H, T, nh, dk, dv, io, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                           _ptr(initial_state), _ptr(o), _ptr(final_state), _ptr(ws), nbytes,
                                           _stream(stream, dev))
     if st != GDR_OK:
@@ -363,7 +371,7 @@ def gdn2_chunk_fwd(q, k, v, g, b, w, initial_state=None, *, output_final_state=T
     o, final_state = _outputs((B, H, T, dv), q.dtype, (B, H, dv, dk), dev, out, final_state, output_final_state,
                               stream)
     ws, nbytes = _workspace(workspace, gdn2_chunk_fwd_workspace_size(B, H, T, dk, dv), dev, stream)
-    st = load_library().gdr_gdn2_chunk_fwd(B, H, T, dk, dv, io, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), _ptr(w),
+    st = _launch(dev, load_library().gdr_gdn2_chunk_fwd, B, H, T, dk, dv, io, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), _ptr(w),
                                            _ptr(initial_state), _ptr(o), _ptr(final_state), _ptr(ws), nbytes,
                                            _stream(stream, dev))
     if st != GDR_OK:
@@ -408,7 +416,7 @@ def frame_fwd(q, k, v, gamma, g, frame_len, initial_state=None, *, output_final_
     o, final_state = _outputs((B, H, T, dv), q.dtype, (B, H, dv, dk), dev, out, final_state, output_final_state,
                               stream)
     ws, nbytes = _workspace(workspace, frame_fwd_workspace_size(B, H, T, frame_len, dk, dv), dev, stream)
-    st = load_library().gdr_frame_fwd(B, H, T, frame_len, dk, dv, io, gate, _ptr(q), _ptr(k), _ptr(v), _ptr(gamma),
+    st = _launch(dev, load_library().gdr_frame_fwd, B, H, T, frame_len, dk, dv, io, gate, _ptr(q), _ptr(k), _ptr(v), _ptr(gamma),
                                       _ptr(g), _ptr(initial_state), _ptr(o), _ptr(final_state), _ptr(ws), nbytes,
                                       _stream(stream, dev))
     if st != GDR_OK:
@@ -442,7 +450,7 @@ def decode_step(q, k, v, g, beta, state, *, out=None, stream=None):
     with _on(stream):
         o = torch.empty((N, H, dv), dtype=q.dtype, device=dev) if out is None else out
     _check(o, "out", (N, H, dv), q.dtype, dev)
-    st = load_library().gdr_decode_step(N, H, dk, dv, io, gate, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+    st = _launch(dev, load_library().gdr_decode_step, N, H, dk, dv, io, gate, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                         _ptr(state), _ptr(o), _stream(stream, dev))
     if st != GDR_OK:
         raise GdrError(st, "gdr_decode_step")
