@@ -103,28 +103,31 @@ __global__ __launch_bounds__(256, 1) void frame_gram_kernel(const FrArgs a) {
 
     // ---- G and C over the frame's tokens, 64 at a time.  Thread tid stages the 16-byte pieces
     // (row, col) with row = tid / R + (256 / R) i of K (R = DK / 8 pieces per row) and of V
-    // (R = DV / 8); the next block's pieces and their rows' gamma are loaded into registers
-    // while the current block's products run.  Tokens outside the frame read past the buffer
-    // end, which returns zeros.
+    // (R = DV / 8); a block's pieces and their rows' gamma are loaded into registers two blocks
+    // before it is staged.  Tokens outside the frame read past the buffer end, which returns
+    // zeros.
     constexpr int RK = DK / 8, RV = DV / 8, NPK = 64 * RK / 256, NPV = 64 * RV / 256;
-    uint4 kp[NPK], vp[NPV];
-    float gk[NPK], gv[NPV];
-    auto load_block = [&](int64_t t0) {
+    struct Blk {
+        uint4 kp[NPK], vp[NPV];
+        float gk[NPK], gv[NPV];
+    };
+    Blk B0, B1;  // blocks alternate between the two register sets
+    auto load_block = [&](Blk& B, int64_t t0) {
 #pragma unroll
         for (int i = 0; i < NPK; ++i) {
             const int row = tid / RK + (256 / RK) * i, col = (tid % RK) * 8;
             const int64_t tok = t0 + row;
             const bool in = tok < t_end;
-            kp[i] = bld16(rk, in ? (uint32_t)((tok * DK + col) * 2) : (uint32_t)(T * DK * 2));
-            gk[i] = bld4(rgm, in ? (uint32_t)(tok * 4) : (uint32_t)(T * 4));
+            B.kp[i] = bld16(rk, in ? (uint32_t)((tok * DK + col) * 2) : (uint32_t)(T * DK * 2));
+            B.gk[i] = bld4(rgm, in ? (uint32_t)(tok * 4) : (uint32_t)(T * 4));
         }
 #pragma unroll
         for (int i = 0; i < NPV; ++i) {
             const int row = tid / RV + (256 / RV) * i, col = (tid % RV) * 8;
             const int64_t tok = t0 + row;
             const bool in = tok < t_end;
-            vp[i] = bld16(rv, in ? (uint32_t)((tok * DV + col) * 2) : (uint32_t)(T * DV * 2));
-            gv[i] = bld4(rgm, in ? (uint32_t)(tok * 4) : (uint32_t)(T * 4));
+            B.vp[i] = bld16(rv, in ? (uint32_t)((tok * DV + col) * 2) : (uint32_t)(T * DV * 2));
+            B.gv[i] = bld4(rgm, in ? (uint32_t)(tok * 4) : (uint32_t)(T * 4));
         }
     };
     auto scaled = [](const uint4& u, float sg) {
@@ -137,23 +140,25 @@ __global__ __launch_bounds__(256, 1) void frame_gram_kernel(const FrArgs a) {
         }
         return h;
     };
-    auto stage_block = [&]() {
+    auto stage_block = [&](const Blk& B) {
 #pragma unroll
         for (int i = 0; i < NPK; ++i) {
             const int row = tid / RK + (256 / RK) * i, col = (tid % RK) * 8;
-            *reinterpret_cast<half8*>(Kp + row * L::LDK + col) = scaled(kp[i], sqrtf(gk[i]));
+            *reinterpret_cast<half8*>(Kp + row * L::LDK + col) = scaled(B.kp[i], sqrtf(B.gk[i]));
         }
 #pragma unroll
         for (int i = 0; i < NPV; ++i) {
             const int row = tid / RV + (256 / RV) * i, col = (tid % RV) * 8;
-            *reinterpret_cast<half8*>(Vp + row * L::LDV + col) = scaled(vp[i], sqrtf(gv[i]));
+            *reinterpret_cast<half8*>(Vp + row * L::LDV + col) = scaled(B.vp[i], sqrtf(B.gv[i]));
         }
     };
-    if (t_beg < t_end) load_block(t_beg);
-    for (int64_t t0 = t_beg; t0 < t_end; t0 += 64) {
-        stage_block();
+    // one block: stage it, refill its register set with the block two ahead (past the frame:
+    // zeros, no memory traffic, and no branch, so that the other set's loads stay in flight),
+    // then the products
+    auto block = [&](Blk& B, int64_t t0) {
+        stage_block(B);
         lds_barrier();
-        if (t0 + 64 < t_end) load_block(t0 + 64);
+        load_block(B, t0 + 128);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             half8 kf[NT];
@@ -180,7 +185,15 @@ __global__ __launch_bounds__(256, 1) void frame_gram_kernel(const FrArgs a) {
             }
         }
         lds_barrier();
+    };
+    load_block(B0, t_beg);
+    load_block(B1, t_beg + 64);
+    int64_t t0 = t_beg;
+    for (; t0 + 64 < t_end; t0 += 128) {
+        block(B0, t0);
+        block(B1, t0 + 64);
     }
+    if (t0 < t_end) block(B0, t0);
 
     // ---- I + G into LDS (both triangles), C to the workspace
     const int64_t fi = bh * a.F + f;
@@ -217,23 +230,26 @@ __global__ __launch_bounds__(256, 1) void frame_gram_kernel(const FrArgs a) {
 
     // ---- W = (I + G)^{-1} by blocked Gauss-Jordan elimination in place, 16 pivots per block.
     // For pivot block K (rows and columns Kb = 16K .. 16K + 15):
-    //   1. wave 0 eliminates the 16 pivots on the panel columns Kb only (all rows, fp32
-    //      registers, two rows per lane; the pivot row reaches the other lanes by readlane).
-    //      The panel then holds P = [-A_{i,Kb} D^{-1} (rows i outside Kb); D^{-1} (rows Kb)],
-    //      D = A_{Kb,Kb};
-    //   2. every other column block j takes the same 16 pivots at once as a rank-16 product:
-    //      A_{:,j} <- [i outside Kb] A_{:,j} + P A_{Kb,j}, on fp32 MFMA (16x16x4), each wave a
-    //      share of the 16x16 tiles, all tiles read before any is written.
+    //   1. wave 0 inverts the 16 x 16 pivot tile D = A_{Kb,Kb} alone (fp32 registers, lane r of
+    //      each 16-lane row holds row r; the pivot row reaches the other lanes by readlane);
+    //   2. the panel: the other rows of column block K become P_i = -A_{i,Kb} D^{-1} (fp32
+    //      MFMA, 16x16x4);
+    //   3. every other column block j takes the 16 pivots at once as a rank-16 product,
+    //      A_ij <- A_ij + P_i A_{Kb,j} (i != K) and A_{Kb,j} <- D^{-1} A_{Kb,j}, every tile read
+    //      before any is written.
     // This is the pivot-by-pivot elimination regrouped (the same operations in exact
     // arithmetic): the panel sees its 16 pivots one by one, the rest of the matrix sees their
     // product.  I + G is symmetric positive definite with eigenvalues >= 1, and so is every
-    // pivot block's Schur complement: no pivoting is needed.
-    constexpr int NB = DK / 16;           // pivot blocks
-    constexpr int NTW = (NB * (NB - 1) + 3) / 4;  // trailing tiles per wave
+    // pivot block's Schur complement: no pivoting is needed.  Steps 2 and 3 are split by row
+    // blocks: wave w owns row blocks w, w + 4, .. and forms their panel tiles and then their
+    // trailing tiles, so that a row's P_i fragments are read once for its tiles and the row
+    // block K fragments once for all of a wave's rows, and no barrier separates the panel from
+    // the update (a wave reads only its own rows of column block K).
+    constexpr int NB = DK / 16;          // pivot blocks
+    constexpr int NRW = (NB + 3) / 4;    // row blocks per wave
     for (int kbk = 0; kbk < NB; ++kbk) {
         const int kc = 16 * kbk;
-        // 1. wave 0: D^{-1} by Gauss-Jordan on the 16 x 16 pivot block alone (lane r of each
-        //    16-lane row holds row kc + r; the pivot row reaches the other lanes by readlane)
+        // 1. wave 0: D^{-1}
         if (w == 0) {
             const int r = l & 15;
             float P[16];
@@ -264,51 +280,66 @@ __global__ __launch_bounds__(256, 1) void frame_gram_kernel(const FrArgs a) {
             }
         }
         lds_barrier();
-        // 2. the panel's other rows, -A_{i,Kb} D^{-1}, one 16 x 16 tile per row block on fp32
-        //    MFMA (each wave reads its tiles before it writes them; D^{-1} is only read)
-        for (int t = w; t < NB - 1; t += 4) {
-            const int ib = t + (t >= kbk ? 1 : 0);
-            float4v a4 = zero4();
+        // 2. this wave's panel tiles (row blocks ib = w + 4u other than K), written in place
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float av = Am[(16 * ib + j) * L::LDA + kc + 4 * q + g];  // A[16 ib + j][Kb + 4q + g]
-                const float bv = Am[(kc + 4 * q + g) * L::LDA + kc + j];       // D^{-1}[4q + g][j]
-                a4 = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, a4, 0, 0, 0);
-            }
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) Am[(16 * ib + 4 * g + r4) * L::LDA + kc + j] = -a4[r4];
-        }
-        lds_barrier();
-        // tiles (ib, jb), jb != kbk, numbered n = ib (NB - 1) + (jb - [jb > kbk]); wave w
-        // takes n = w, w + 4, ...
-        float4v acc[NTW];
-#pragma unroll
-        for (int t = 0; t < NTW; ++t) {
-            const int n = w + 4 * t;
-            if (n < NB * (NB - 1)) {
-                const int ib = n / (NB - 1), jr = n % (NB - 1), jb = jr + (jr >= kbk ? 1 : 0);
+        for (int u = 0; u < NRW; ++u) {
+            const int ib = w + 4 * u;
+            if (ib < NB && ib != kbk) {
                 float4v a4 = zero4();
-                if (ib != kbk) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) a4[r] = Am[(16 * ib + 4 * g + r) * L::LDA + 16 * jb + j];
-                }
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const float av = Am[(16 * ib + j) * L::LDA + kc + 4 * q + g];   // P[16 ib + j][4q + g]
-                    const float bv = Am[(kc + 4 * q + g) * L::LDA + 16 * jb + j];   // A[Kb + 4q + g][16 jb + j]
+                    const float av = Am[(16 * ib + j) * L::LDA + kc + 4 * q + g];  // A[16 ib + j][Kb + 4q + g]
+                    const float bv = Am[(kc + 4 * q + g) * L::LDA + kc + j];       // D^{-1}[4q + g][j]
                     a4 = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, a4, 0, 0, 0);
                 }
-                acc[t] = a4;
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) Am[(16 * ib + 4 * g + r4) * L::LDA + kc + j] = -a4[r4];
+            }
+        }
+        lds_fence();  // this wave's panel stores before it reads them back as operands
+        // 3. this wave's trailing tiles: P fragments of its rows (row block K: D^{-1}), then
+        //    each column block jb != K with its row block K fragments
+        float pa[NRW][4];
+#pragma unroll
+        for (int u = 0; u < NRW; ++u) {
+            const int ib = w + 4 * u;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                pa[u][q] = ib < NB ? Am[(16 * ib + j) * L::LDA + kc + 4 * q + g] : 0.0f;  // P[16 ib + j][4q + g]
+        }
+        float4v acc[NRW][NB - 1];
+#pragma unroll
+        for (int jr = 0; jr < NB - 1; ++jr) {
+            const int jb = jr + (jr >= kbk ? 1 : 0);
+            float pb[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) pb[q] = Am[(kc + 4 * q + g) * L::LDA + 16 * jb + j];  // A[Kb + 4q + g][16 jb + j]
+#pragma unroll
+            for (int u = 0; u < NRW; ++u) {
+                const int ib = w + 4 * u;
+                if (ib < NB) {
+                    float4v a4 = zero4();
+                    if (ib != kbk) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) a4[r] = Am[(16 * ib + 4 * g + r) * L::LDA + 16 * jb + j];
+                    }
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) a4 = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[u][q], pb[q], a4, 0, 0, 0);
+                    acc[u][jr] = a4;
+                }
             }
         }
         lds_barrier();
 #pragma unroll
-        for (int t = 0; t < NTW; ++t) {
-            const int n = w + 4 * t;
-            if (n < NB * (NB - 1)) {
-                const int ib = n / (NB - 1), jr = n % (NB - 1), jb = jr + (jr >= kbk ? 1 : 0);
+        for (int u = 0; u < NRW; ++u) {
+            const int ib = w + 4 * u;
+            if (ib < NB) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) Am[(16 * ib + 4 * g + r) * L::LDA + 16 * jb + j] = acc[t][r];
+                for (int jr = 0; jr < NB - 1; ++jr) {
+                    const int jb = jr + (jr >= kbk ? 1 : 0);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) Am[(16 * ib + 4 * g + r) * L::LDA + 16 * jb + j] = acc[u][jr][r];
+                }
             }
         }
         lds_barrier();
