@@ -230,8 +230,8 @@ __global__ __launch_bounds__(256, 1) void frame_gram_kernel(const FrArgs a) {
 
     // ---- W = (I + G)^{-1} by blocked Gauss-Jordan elimination in place, 16 pivots per block.
     // For pivot block K (rows and columns Kb = 16K .. 16K + 15):
-    //   1. wave 0 inverts the 16 x 16 pivot tile D = A_{Kb,Kb} alone (fp32 registers, lane r of
-    //      each 16-lane row holds row r; the pivot row reaches the other lanes by readlane);
+    //   1. wave 0 inverts the 16 x 16 pivot tile D = A_{Kb,Kb} alone by Gauss-Jordan (fp32
+    //      registers, four entries per lane);
     //   2. the panel: the other rows of column block K become P_i = -A_{i,Kb} D^{-1} (fp32
     //      MFMA, 16x16x4);
     //   3. every other column block j takes the 16 pivots at once as a rank-16 product,
@@ -249,35 +249,30 @@ __global__ __launch_bounds__(256, 1) void frame_gram_kernel(const FrArgs a) {
     constexpr int NRW = (NB + 3) / 4;    // row blocks per wave
     for (int kbk = 0; kbk < NB; ++kbk) {
         const int kc = 16 * kbk;
-        // 1. wave 0: D^{-1}
+        // 1. wave 0: D^{-1}.  Lane (r, cg) = (l % 16, l / 16) holds row r, columns 4cg .. 4cg + 3;
+        //    for pivot p it fetches row p's four entries of its columns and its own row's
+        //    column-p entry from the lanes that hold them (ds_bpermute), the pivot by readlane
         if (w == 0) {
-            const int r = l & 15;
-            float P[16];
-#pragma unroll
-            for (int c = 0; c < 16; c += 4) {
-                const float4v v4 = ld4f(Am + (kc + r) * L::LDA + kc + c);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) P[c + e] = v4[e];
-            }
+            const int r = l & 15, cg = l >> 4;
+            float4v x = ld4f(Am + (kc + r) * L::LDA + kc + 4 * cg);
 #pragma unroll
             for (int pp = 0; pp < 16; ++pp) {
-                float rowp[16];
+                const int src_p = (16 * cg + pp) * 4;               // row pp, this column group
+                const int src_f = (16 * (pp >> 2) + r) * 4;         // row r, column pp
+                float rowp[4];
 #pragma unroll
-                for (int c = 0; c < 16; ++c) rowp[c] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(P[c]), pp));
-                const float rp = __builtin_amdgcn_rcpf(rowp[pp]);  // 1 ulp; the pivots are >= 1 in exact arithmetic
+                for (int e = 0; e < 4; ++e) rowp[e] = __int_as_float(__builtin_amdgcn_ds_bpermute(src_p, __float_as_int(x[e])));
+                const float f = __int_as_float(__builtin_amdgcn_ds_bpermute(src_f, __float_as_int(x[pp & 3])));
+                const float dp = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x[pp & 3]), 16 * (pp >> 2) + pp));
+                const float rp = __builtin_amdgcn_rcpf(dp);  // 1 ulp; the pivots are >= 1 in exact arithmetic
                 const bool prow = r == pp;
-                const float f = P[pp];
                 const float keep = prow ? 0.0f : 1.0f;
                 const float cf = prow ? rp : -f * rp;
 #pragma unroll
-                for (int c = 0; c < 16; ++c) P[c] = fmaf(rowp[c], cf, P[c] * keep);
-                P[pp] = prow ? rp : -f * rp;
+                for (int e = 0; e < 4; ++e) x[e] = fmaf(rowp[e], cf, x[e] * keep);
+                if (cg == (pp >> 2)) x[pp & 3] = prow ? rp : -f * rp;
             }
-            if (l < 16) {
-#pragma unroll
-                for (int c = 0; c < 16; c += 4)
-                    *reinterpret_cast<float4v*>(Am + (kc + r) * L::LDA + kc + c) = float4v{P[c], P[c + 1], P[c + 2], P[c + 3]};
-            }
+            *reinterpret_cast<float4v*>(Am + (kc + r) * L::LDA + kc + 4 * cg) = x;
         }
         lds_barrier();
         // 2. this wave's panel tiles (row blocks ib = w + 4u other than K), written in place
