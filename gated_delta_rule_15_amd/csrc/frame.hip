@@ -58,9 +58,10 @@ struct FrGramLds {
     static constexpr int LDK = DK + 16;   // halfs, token rows of sqrt(gamma) k
     static constexpr int LDV = DV + 16;   // halfs, token rows of sqrt(gamma) v
     static constexpr int LDA = DK + 4;    // floats, rows of I + G
-    static constexpr int oK = 0;
-    static constexpr int oV = oK + 64 * LDK * 2;
-    static constexpr int oA = oV + 64 * LDV * 2;
+    static constexpr int szK = 64 * LDK * 2, szV = 64 * LDV * 2;
+    static constexpr int oK = 0;                // two buffers each
+    static constexpr int oV = oK + 2 * szK;
+    static constexpr int oA = oV + 2 * szV;
     static constexpr int total = oA + DK * LDA * 4;
     static_assert(total <= 160 * 1024, "LDS budget");
 };
@@ -71,8 +72,8 @@ __global__ __launch_bounds__(256, 1) void frame_gram_kernel(const FrArgs a) {
     constexpr int NT = DK / 16, NV = DV / 16;
     constexpr int NSG = (NT + 3) / 4, NSC = (NV + 3) / 4;  // row tiles per wave
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    _Float16* Kp = reinterpret_cast<_Float16*>(smem + L::oK);
-    _Float16* Vp = reinterpret_cast<_Float16*>(smem + L::oV);
+    auto Kbuf = [&](int b) { return reinterpret_cast<_Float16*>(smem + L::oK + b * L::szK); };
+    auto Vbuf = [&](int b) { return reinterpret_cast<_Float16*>(smem + L::oV + b * L::szV); };
     float* Am = reinterpret_cast<float*>(smem + L::oA);
 
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, j = l & 15, g = l >> 4;
@@ -140,7 +141,7 @@ __global__ __launch_bounds__(256, 1) void frame_gram_kernel(const FrArgs a) {
         }
         return h;
     };
-    auto stage_block = [&](const Blk& B) {
+    auto stage_block = [&](const Blk& B, _Float16* Kp, _Float16* Vp) {
 #pragma unroll
         for (int i = 0; i < NPK; ++i) {
             const int row = tid / RK + (256 / RK) * i, col = (tid % RK) * 8;
@@ -152,13 +153,8 @@ __global__ __launch_bounds__(256, 1) void frame_gram_kernel(const FrArgs a) {
             *reinterpret_cast<half8*>(Vp + row * L::LDV + col) = scaled(B.vp[i], sqrtf(B.gv[i]));
         }
     };
-    // one block: stage it, refill its register set with the block two ahead (past the frame:
-    // zeros, no memory traffic, and no branch, so that the other set's loads stay in flight),
-    // then the products
-    auto block = [&](Blk& B, int64_t t0) {
-        stage_block(B);
-        lds_barrier();
-        load_block(B, t0 + 128);
+    // the products of one staged block
+    auto products = [&](const _Float16* Kp, const _Float16* Vp) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             half8 kf[NT];
@@ -184,16 +180,28 @@ __global__ __launch_bounds__(256, 1) void frame_gram_kernel(const FrArgs a) {
                 }
             }
         }
+    };
+    // one step: stage the next block (register set Bn) into LDS buffer bn, refill Bn with the
+    // block three ahead (past the frame: zeros, no memory traffic, and no branch, so that the
+    // other set's loads stay in flight), then the products of the block in buffer 1 - bn.  One
+    // barrier per block: the buffer being staged was last read by the step before.
+    auto step = [&](Blk& Bn, int bn, int64_t t_refill) {
+        stage_block(Bn, Kbuf(bn), Vbuf(bn));
+        load_block(Bn, t_refill);
+        products(Kbuf(1 - bn), Vbuf(1 - bn));
         lds_barrier();
     };
     load_block(B0, t_beg);
     load_block(B1, t_beg + 64);
+    stage_block(B0, Kbuf(0), Vbuf(0));
+    load_block(B0, t_beg + 128);
+    lds_barrier();
     int64_t t0 = t_beg;
     for (; t0 + 64 < t_end; t0 += 128) {
-        block(B0, t0);
-        block(B1, t0 + 64);
+        step(B1, 1, t0 + 192);  // products of the block at t0 (buffer 0)
+        step(B0, 0, t0 + 256);  // products of the block at t0 + 64 (buffer 1)
     }
-    if (t0 < t_end) block(B0, t0);
+    if (t0 < t_end) step(B1, 1, t0 + 192);
 
     // ---- I + G into LDS (both triangles), C to the workspace
     const int64_t fi = bh * a.F + f;
@@ -339,22 +347,24 @@ __global__ __launch_bounds__(256, 1) void frame_gram_kernel(const FrArgs a) {
         }
         lds_barrier();
     }
-    // W as W_hi + W_lo (fp16 each), rows natural: thread t writes CPT entries of row t / TPR
-    constexpr int TPR = 256 / DK, CPT = DK / TPR;
-    const int ri = tid / TPR, c0 = (tid % TPR) * CPT;
-    uint16_t* wh = a.Wh + fi * (int64_t)(DK * DK) + ri * DK + c0;
-    uint16_t* wl = a.Wl + fi * (int64_t)(DK * DK) + ri * DK + c0;
+    // W as W_hi + W_lo (fp16 each), rows natural, in pieces of 8 columns: consecutive threads
+    // take consecutive pieces of a row (conflict-free LDS reads, 16-byte stores)
+    constexpr int PPR = DK / 8, NPW = DK * PPR / 256;
+    uint16_t* wh = a.Wh + fi * (int64_t)(DK * DK);
+    uint16_t* wl = a.Wl + fi * (int64_t)(DK * DK);
 #pragma unroll
-    for (int c = 0; c < CPT; c += 8) {
+    for (int u = 0; u < NPW; ++u) {
+        const int idx = tid + 256 * u, row = idx / PPR, col = (idx % PPR) * 8;
+        const float4v x0 = ld4f(Am + row * L::LDA + col), x1 = ld4f(Am + row * L::LDA + col + 4);
         half8 hh, hl;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float xv = Am[ri * L::LDA + c0 + c + e];
+            const float xv = e < 4 ? x0[e] : x1[e - 4];
             hh[e] = (_Float16)xv;
             hl[e] = (_Float16)(xv - (float)hh[e]);
         }
-        *reinterpret_cast<half8*>(wh + c) = hh;
-        *reinterpret_cast<half8*>(wl + c) = hl;
+        *reinterpret_cast<half8*>(wh + row * DK + col) = hh;
+        *reinterpret_cast<half8*>(wl + row * DK + col) = hl;
     }
 }
 
