@@ -465,14 +465,6 @@ __global__ __launch_bounds__(64 * NWV, 1) void frame_state_kernel(const FrArgs a
             *reinterpret_cast<uint4*>(Wls + row * L::LDW + col) = wpl[u];
         }
         lds_barrier();
-        {
-            const uint32_t nb = (uint32_t)((f + 1) * DK * DK * 2);  // past the end: zeros, unused
-#pragma unroll
-            for (int u = 0; u < NPW; ++u) {
-                wph[u] = bld16(rwh, nb + (uint32_t)((tid + NTH * u) * 16));
-                wpl[u] = bld16(rwl, nb + (uint32_t)((tid + NTH * u) * 16));
-            }
-        }
         // operand halves: rhs = hi + lo
         half8 bh8[NKB], bl8[NKB];
 #pragma unroll
@@ -484,22 +476,41 @@ __global__ __launch_bounds__(64 * NWV, 1) void frame_state_kernel(const FrArgs a
                 bl8[kb][e] = (_Float16)(full - (float)bh8[kb][e]);
             }
         }
-        // S^T = W rhs^T: row tile t uses W rows pperm(16 t + j), 8 consecutive key channels
+        // S^T = W rhs^T: row tile t uses W rows pperm(16 t + j), 8 consecutive key channels.  Two
+        // tiles at a time, so that two accumulation chains interleave; after each pair the
+        // registers W was staged from take the next frame's W pieces a few at a time (past the
+        // end: zeros, unused), so that their issue overlaps the products.
+        static_assert(NST % 2 == 0 && NPW % (NST / 2) == 0, "W pieces per tile pair");
+        constexpr int LPP = NPW / (NST / 2);
+        const uint32_t nb = (uint32_t)((f + 1) * DK * DK * 2);
+        const float isc = __builtin_ldexpf(1.0f, -rexp);
 #pragma unroll
-        for (int t = 0; t < NST; ++t) {
-            float4v acc = zero4();
-            const int wr = pperm(16 * t + j);
+        for (int t = 0; t < NST; t += 2) {
+            float4v acc0 = zero4(), acc1 = zero4();
+            const int wr0 = pperm(16 * t + j), wr1 = pperm(16 * (t + 1) + j);
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
-                const half8 ah = ld8(Whs + wr * L::LDW + 32 * kb + 8 * g);
-                const half8 al = ld8(Wls + wr * L::LDW + 32 * kb + 8 * g);
-                mma16(acc, ah, bh8[kb]);
-                mma16(acc, ah, bl8[kb]);
-                mma16(acc, al, bh8[kb]);
+                const half8 ah0 = ld8(Whs + wr0 * L::LDW + 32 * kb + 8 * g);
+                const half8 al0 = ld8(Wls + wr0 * L::LDW + 32 * kb + 8 * g);
+                const half8 ah1 = ld8(Whs + wr1 * L::LDW + 32 * kb + 8 * g);
+                const half8 al1 = ld8(Wls + wr1 * L::LDW + 32 * kb + 8 * g);
+                mma16(acc0, ah0, bh8[kb]);
+                mma16(acc1, ah1, bh8[kb]);
+                mma16(acc0, ah0, bl8[kb]);
+                mma16(acc1, ah1, bl8[kb]);
+                mma16(acc0, al0, bh8[kb]);
+                mma16(acc1, al1, bh8[kb]);
             }
-            const float isc = __builtin_ldexpf(1.0f, -rexp);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) St[t][r] = acc[r] * isc;
+            for (int r = 0; r < 4; ++r) {
+                St[t][r] = acc0[r] * isc;
+                St[t + 1][r] = acc1[r] * isc;
+            }
+#pragma unroll
+            for (int u = (t / 2) * LPP; u < (t / 2 + 1) * LPP; ++u) {
+                wph[u] = bld16(rwh, nb + (uint32_t)((tid + NTH * u) * 16));
+                wpl[u] = bld16(rwl, nb + (uint32_t)((tid + NTH * u) * 16));
+            }
         }
         // S_t in fp16, [value channel][key channel], for the outputs, times a power of two per
         // wave that brings its largest magnitude near 2^12 (stored beside it for the outputs)
