@@ -254,7 +254,8 @@ __global__ __launch_bounds__(256, 1) void frame_gram_kernel(const FrArgs a) {
     // block K fragments once for all of a wave's rows, and no barrier separates the panel from
     // the update (a wave reads only its own rows of column block K).
     constexpr int NB = DK / 16;          // pivot blocks
-    constexpr int NRW = (NB + 3) / 4;    // row blocks per wave
+    constexpr int NRW = NB / 4;          // row blocks per wave
+    static_assert(NB % 4 == 0, "every wave owns whole row blocks");
     for (int kbk = 0; kbk < NB; ++kbk) {
         const int kc = 16 * kbk;
         // 1. wave 0: D^{-1}.  Lane (r, cg) = (l % 16, l / 16) holds row r, columns 4cg .. 4cg + 3;
@@ -287,7 +288,7 @@ __global__ __launch_bounds__(256, 1) void frame_gram_kernel(const FrArgs a) {
 #pragma unroll
         for (int u = 0; u < NRW; ++u) {
             const int ib = w + 4 * u;
-            if (ib < NB && ib != kbk) {
+            if (ib != kbk) {
                 float4v a4 = zero4();
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
@@ -307,9 +308,10 @@ __global__ __launch_bounds__(256, 1) void frame_gram_kernel(const FrArgs a) {
         for (int u = 0; u < NRW; ++u) {
             const int ib = w + 4 * u;
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                pa[u][q] = ib < NB ? Am[(16 * ib + j) * L::LDA + kc + 4 * q + g] : 0.0f;  // P[16 ib + j][4q + g]
+            for (int q = 0; q < 4; ++q) pa[u][q] = Am[(16 * ib + j) * L::LDA + kc + 4 * q + g];  // P[16 ib + j][4q + g]
         }
+        // (no branch in the loop, so that the next column's loads can go out under the current
+        // column's products: row block K loads its old tile too and starts from zero instead)
         float4v acc[NRW][NB - 1];
 #pragma unroll
         for (int jr = 0; jr < NB - 1; ++jr) {
@@ -320,29 +322,26 @@ __global__ __launch_bounds__(256, 1) void frame_gram_kernel(const FrArgs a) {
 #pragma unroll
             for (int u = 0; u < NRW; ++u) {
                 const int ib = w + 4 * u;
-                if (ib < NB) {
-                    float4v a4 = zero4();
-                    if (ib != kbk) {
+                float4v a4;
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) a4[r] = Am[(16 * ib + 4 * g + r) * L::LDA + 16 * jb + j];
-                    }
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) a4 = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[u][q], pb[q], a4, 0, 0, 0);
-                    acc[u][jr] = a4;
+                for (int r = 0; r < 4; ++r) {
+                    const float old = Am[(16 * ib + 4 * g + r) * L::LDA + 16 * jb + j];
+                    a4[r] = ib != kbk ? old : 0.0f;
                 }
+#pragma unroll
+                for (int q = 0; q < 4; ++q) a4 = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[u][q], pb[q], a4, 0, 0, 0);
+                acc[u][jr] = a4;
             }
         }
         lds_barrier();
 #pragma unroll
         for (int u = 0; u < NRW; ++u) {
             const int ib = w + 4 * u;
-            if (ib < NB) {
 #pragma unroll
-                for (int jr = 0; jr < NB - 1; ++jr) {
-                    const int jb = jr + (jr >= kbk ? 1 : 0);
+            for (int jr = 0; jr < NB - 1; ++jr) {
+                const int jb = jr + (jr >= kbk ? 1 : 0);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) Am[(16 * ib + 4 * g + r) * L::LDA + 16 * jb + j] = acc[u][jr][r];
-                }
+                for (int r = 0; r < 4; ++r) Am[(16 * ib + 4 * g + r) * L::LDA + 16 * jb + j] = acc[u][jr][r];
             }
         }
         lds_barrier();
