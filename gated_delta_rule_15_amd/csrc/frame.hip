@@ -13,10 +13,10 @@
 //   frame_gram_kernel   one workgroup per (sequence, frame): G and C by fp16 MFMA over the
 //                       frame's tokens (operands sqrt(gamma) k and sqrt(gamma) v, fp32
 //                       accumulation), then W = (I + G)^{-1} by blocked in-place Gauss-Jordan
-//                       elimination in fp32 (16-pivot panels in registers, the rank-16
-//                       updates on fp32 MFMA; I + G is symmetric positive definite with
-//                       eigenvalues >= 1, so no pivoting is needed), written as a pair of
-//                       fp16 matrices W = W_hi + W_lo, and C in fp32;
+//                       elimination in fp32 (16 x 16 pivot blocks inverted in registers, the
+//                       panels and rank-16 updates on fp32 MFMA; I + G is symmetric positive
+//                       definite with eigenvalues >= 1, so no pivoting is needed), written as a
+//                       pair of fp16 matrices W = W_hi + W_lo, and C in fp32;
 //   frame_state_kernel  one workgroup per (sequence, 32 value channels), frames in order:
 //                       S_t^T = W_t (D_t S_{t-1}^T + C_t^T) on fp16 MFMA with both factors split
 //                       into high and low halves (three products: hi.hi + hi.lo + lo.hi), which
@@ -25,7 +25,7 @@
 //   frame_out_kernel    one workgroup per (sequence, 512 tokens): O = Q S_t^T.
 // The post solves the system by a Cholesky factorisation; forming the inverse once per frame
 // instead keeps the serial pass to one product per frame (the same solution in exact
-// arithmetic; I + G is well conditioned, its eigenvalues lying in [1, 1 + tr G]).
+// arithmetic; I + G is never singular, its eigenvalues lying in [1, 1 + tr G]).
 #include "chunk_common.h"
 
 namespace gdr {
