@@ -104,13 +104,13 @@ __global__ __launch_bounds__(256, 1) void frame_gram_kernel(const FrArgs a) {
 
     // ---- G and C over the frame's tokens, 64 at a time.  Thread tid stages the 16-byte pieces
     // (row, col) with row = tid / R + (256 / R) i of K (R = DK / 8 pieces per row) and of V
-    // (R = DV / 8); a block's pieces and their rows' gamma are loaded into registers two blocks
-    // before it is staged.  Tokens outside the frame read past the buffer end, which returns
-    // zeros.
+    // (R = DV / 8); a block's pieces, and in each wave the gamma of the block's 64 tokens (one
+    // per lane), are loaded into registers two blocks before it is staged.  Tokens outside the
+    // frame read past the buffer end, which returns zeros.
     constexpr int RK = DK / 8, RV = DV / 8, NPK = 64 * RK / 256, NPV = 64 * RV / 256;
     struct Blk {
         uint4 kp[NPK], vp[NPV];
-        float gk[NPK], gv[NPV];
+        float gm;  // gamma of the block's token l (every wave loads the block's 64)
     };
     Blk B0, B1;  // blocks alternate between the two register sets
     auto load_block = [&](Blk& B, int64_t t0) {
@@ -120,7 +120,6 @@ __global__ __launch_bounds__(256, 1) void frame_gram_kernel(const FrArgs a) {
             const int64_t tok = t0 + row;
             const bool in = tok < t_end;
             B.kp[i] = bld16(rk, in ? (uint32_t)((tok * DK + col) * 2) : (uint32_t)(T * DK * 2));
-            B.gk[i] = bld4(rgm, in ? (uint32_t)(tok * 4) : (uint32_t)(T * 4));
         }
 #pragma unroll
         for (int i = 0; i < NPV; ++i) {
@@ -128,8 +127,8 @@ __global__ __launch_bounds__(256, 1) void frame_gram_kernel(const FrArgs a) {
             const int64_t tok = t0 + row;
             const bool in = tok < t_end;
             B.vp[i] = bld16(rv, in ? (uint32_t)((tok * DV + col) * 2) : (uint32_t)(T * DV * 2));
-            B.gv[i] = bld4(rgm, in ? (uint32_t)(tok * 4) : (uint32_t)(T * 4));
         }
+        B.gm = bld4(rgm, t0 + l < t_end ? (uint32_t)((t0 + l) * 4) : (uint32_t)(T * 4));
     };
     auto scaled = [](const uint4& u, float sg) {
         const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
@@ -141,16 +140,20 @@ __global__ __launch_bounds__(256, 1) void frame_gram_kernel(const FrArgs a) {
         }
         return h;
     };
+    // a row's sqrt(gamma) comes from the lane that loaded its gamma (ds_bpermute)
     auto stage_block = [&](const Blk& B, _Float16* Kp, _Float16* Vp) {
+        const int sgl = __float_as_int(sqrtf(B.gm));
 #pragma unroll
         for (int i = 0; i < NPK; ++i) {
             const int row = tid / RK + (256 / RK) * i, col = (tid % RK) * 8;
-            *reinterpret_cast<half8*>(Kp + row * L::LDK + col) = scaled(B.kp[i], sqrtf(B.gk[i]));
+            const float sg = __int_as_float(__builtin_amdgcn_ds_bpermute(row * 4, sgl));
+            *reinterpret_cast<half8*>(Kp + row * L::LDK + col) = scaled(B.kp[i], sg);
         }
 #pragma unroll
         for (int i = 0; i < NPV; ++i) {
             const int row = tid / RV + (256 / RV) * i, col = (tid % RV) * 8;
-            *reinterpret_cast<half8*>(Vp + row * L::LDV + col) = scaled(B.vp[i], sqrtf(B.gv[i]));
+            const float sg = __int_as_float(__builtin_amdgcn_ds_bpermute(row * 4, sgl));
+            *reinterpret_cast<half8*>(Vp + row * L::LDV + col) = scaled(B.vp[i], sg);
         }
     };
     // the products of one staged block
