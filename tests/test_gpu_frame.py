@@ -66,6 +66,41 @@ def test_frame_writing_strength_scales(scale):
     check(f"frame gamma x{scale}", o, S, o_ref, S_ref)
 
 
+def test_frame_zero_writes_pure_decay():
+    """gamma = 0: G = C = 0 and W = I, so each frame only decays the state, S_t = S_{t-1} D_t.
+    Against the oracle, and S_T against the closed form S0 diag(exp(sum of the frame gates)),
+    ragged last frame included."""
+    n, T = 64, 200
+    x = gdr_synth.make_frame_inputs(B=1, H=2, T=T, frame_len=n, channel=True, s0_std=0.3)
+    x["gamma"] = np.zeros_like(x["gamma"])
+    o, S = run(x, n)
+    o_ref, S_ref = frame_forward(x["q"], x["k"], x["v"], x["gamma"], x["g"], n, x["S0"])
+    check("frame gamma = 0", o, S, o_ref, S_ref)
+    closed = x["S0"].astype(np.float64) * np.exp(x["g"].astype(np.float64).sum(axis=2))[:, :, None, :]
+    assert err_literal(host(S), closed) <= 1e-4
+
+
+def test_frame_steep_channel_decays():
+    """Per-channel log gates in U(-30, -10): the old state all but vanishes at every frame, so
+    S_t is about C_t (I + G_t)^{-1}; the products of tiny decays must not lose the fresh part."""
+    n, T = 64, 320
+    x = gdr_synth.make_frame_inputs(B=1, H=2, T=T, frame_len=n, channel=True, s0_std=0.05, salt=3)
+    r = np.random.default_rng(5)
+    x["g"] = r.uniform(-30.0, -10.0, size=x["g"].shape).astype(np.float32)
+    o, S = run(x, n)
+    o_ref, S_ref = frame_forward(x["q"], x["k"], x["v"], x["gamma"], x["g"], n, x["S0"])
+    check("frame steep per-channel decays", o, S, o_ref, S_ref)
+
+
+def test_frame_single_ragged_frame():
+    """One frame longer than the sequence (frame_len 160, T = 150): every query reads the
+    state after all 150 writes, through a partly filled last token block."""
+    x = gdr_synth.make_frame_inputs(B=1, H=2, T=150, frame_len=160, channel=False, s0_std=0.05, salt=4)
+    o, S = run(x, 160)
+    o_ref, S_ref = frame_forward(x["q"], x["k"], x["v"], x["gamma"], x["g"], 160, x["S0"])
+    check("frame single ragged frame", o, S, o_ref, S_ref)
+
+
 def test_frame_permutation_invariance():
     """Tokens permuted inside their frames: outputs permuted alike, final state unchanged
     (up to the fp32 summation order of G and C)."""
