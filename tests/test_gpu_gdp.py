@@ -84,6 +84,26 @@ def test_gdp_many_substeps(nh, T):
     check(f"gdp nh={nh} T={T}", o, S, o_ref, S_ref)
 
 
+@pytest.mark.parametrize("kind", ["reflections", "identity", "mixed"])
+def test_gdp_special_substeps(kind):
+    """beta = 2 with unit keys makes every substep a Householder reflection I - 2 k k^T (a swap
+    of two coordinates for k = (e_a - e_b)/sqrt(2), "A Swap Is a Reflection"); beta = 0 makes
+    it the identity (only the decay acts); mixed takes 0, 2 and the drawn values in turn."""
+    w = variant(nh=3)
+    x = gdr_synth.make_inputs(w, B=1, H=2, T=70)
+    if kind == "reflections":
+        x["beta"][:] = 2.0
+    elif kind == "identity":
+        x["beta"][:] = 0.0
+    else:
+        x["beta"][..., 0] = 0.0
+        x["beta"][..., 1] = 2.0
+    S0 = state(11, 1, 2, 128, 128, std=0.2)
+    o, S = run_gdp(x, S0)
+    o_ref, S_ref = oracle.gdp_forward(x["q"], x["k"], x["v"], x["g"], x["beta"], S0)
+    check(f"gdp {kind} substeps", o, S, o_ref, S_ref)
+
+
 def test_gdp_equals_chunk_fwd_on_the_virtual_sequence():
     """The GDP kernels read q, g and write o through the substep mapping; fed the expanded
     virtual sequence, the chunked forward on the same path (the same kernel bodies) must give
