@@ -77,6 +77,32 @@ def test_decode_small(dk, dv, io, gate):
     assert es <= TOL_F32, es   # the state is fp32 in both I/O modes
 
 
+@pytest.mark.parametrize("kind", ["identity", "exact_write", "reflection"])
+def test_decode_special_values(kind):
+    """g = 0 and beta = 0 (the identity: the state must come back bit for bit), beta = 1 (the
+    exact write of v along k) and beta = 2 (a reflection, "A Swap Is a Reflection"), three
+    steps each against the oracle."""
+    w = variant(5)
+    N, H, steps = 3, 2, 3
+    st = gdr_synth.make_decode_state(w, N=N, H=H)
+    state = dev(st)
+    ref = st.astype(np.float64)
+    for s in range(steps):
+        d = gdr_synth.make_decode_inputs(w, s, N=N, H=H)
+        if kind == "identity":
+            d["g"][:] = 0.0
+            d["beta"][:] = 0.0
+        else:
+            d["beta"][:] = 1.0 if kind == "exact_write" else 2.0
+        o = gdr.decode_step(dev(d["q"], True), dev(d["k"], True), dev(d["v"], True), dev(d["g"]), dev(d["beta"]), state)
+        o_ref, ref = oracle.decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], ref)
+        torch.cuda.synchronize()
+        assert err_bf16_out(host(o), o_ref) <= TOL_BF16, (kind, s)
+    assert err_literal(host(state), ref) <= TOL_F32
+    if kind == "identity":
+        assert torch.equal(state.cpu(), torch.from_numpy(st))
+
+
 def test_decode_full_size_64_steps_sampled():
     """256 sequences x 32 heads, d = 128, 64 fresh-input steps on a 512 MiB state;
     48 sampled (sequence, head) states checked at every step against the oracle."""
