@@ -104,6 +104,23 @@ def test_prep_zero_and_large_raw_vectors():
     check(f"fused prep, zero and scaled rows", o, S, o_ref, S_ref)
 
 
+def test_prep_extreme_gate_parameters():
+    """Raw gate inputs far outside the configs': dt of +-40 (softplus of 40, a decay of e^-40
+    per token, and softplus of -40, no decay at all), saturated beta logits (+-40, so beta is
+    1 or about 4e-18) and a head with lambda = e^3; the preparation's softplus and logistic
+    map must stay finite and match the oracle's."""
+    r = gdr_synth.make_raw_inputs(variant(), B=1, H=2, T=200, head_params="varied")
+    r["dt"][0, 0, 10:40] = 40.0
+    r["dt"][0, 1, 50:120] = -40.0
+    r["beta_logit"][0, 0, 60:90] = 40.0
+    r["beta_logit"][0, 1, 130:160] = -40.0
+    r["A_log"][1] = 3.0
+    o, S = run(r)
+    o_ref, S_ref = ref(r)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(S).all()
+    check("fused prep, extreme gate parameters", o, S, o_ref, S_ref)
+
+
 def test_prep_full_size_sampled():
     """B=4, H=16, T=4096, d=128 from raw projections; 4 of the 64 sequences checked."""
     w = gdr_synth.WORKLOADS[2]
